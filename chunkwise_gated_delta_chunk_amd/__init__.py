@@ -1,0 +1,258 @@
+"""Python binding of liblinattn.so: the MI355X varlen chunkwise gated-delta-rule
+prefill forward (GDN and KDA) and its device-side chunk metadata.
+
+Argument marshalling only: tensors are checked for dtype, device, shape and
+contiguity, their device pointers and the current HIP stream are handed to
+the C ABI (include/linattn.h), and outputs the caller did not provide are
+allocated with torch.  Every step of the computation runs in the library's
+gfx950 kernels; if the library is missing or a call fails, an exception is
+raised -- there is no other path.
+
+Layouts (token-major varlen packing, batch 1): q, k [T_max, H, d_k];
+v [T_max, H, d_v]; g [T_max, H] (GDN) or [T_max, H, d_k] (KDA); beta
+[T_max, H]; cu_seqlens int32 [N_max + 1]; h0 / ht [N_max, H, d_k, d_v] fp32;
+o [T_max, H, d_v] fp32.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "LinAttnError", "lib", "nt_max", "build_chunk_meta", "workspace_bytes",
+    "gdn_chunk_fwd", "kda_chunk_fwd", "chunk_fwd_stages", "dv_split_for",
+    "STAGE_MAP", "STAGE_REDUCE", "META_BAD_START", "META_NOT_MONOTONE",
+    "META_OVER_CAPACITY", "LIB_PATH",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinattn.so")
+
+LA_BF16, LA_F32 = 0, 1
+STAGE_MAP, STAGE_REDUCE = 1, 2
+META_BAD_START, META_NOT_MONOTONE, META_OVER_CAPACITY = 1, 2, 4
+
+
+class LinAttnError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__(f"{what}: {_status_string(status)} (status {status})")
+
+
+class ChunkFwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("T_max", ctypes.c_int32), ("N_max", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("BT", ctypes.c_int32),
+        ("qkv_dtype", ctypes.c_int32), ("dv_split", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
+        ("cu_seqlens", ctypes.c_void_p), ("chunk_indices", ctypes.c_void_p),
+        ("chunk_offsets", ctypes.c_void_p), ("h0", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("ht", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                              "(or python chunkwise_gated_delta_chunk_amd/build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        L.la_nt_max.restype = ctypes.c_int64
+        L.la_nt_max.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
+        L.build_chunk_meta.restype = ctypes.c_int
+        L.build_chunk_meta.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
+                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
+                                       ctypes.c_void_p, ctypes.c_void_p]
+        P = ctypes.POINTER(ChunkFwdArgs)
+        L.la_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
+        L.la_chunk_fwd_workspace_bytes.argtypes = [P, ctypes.c_int]
+        for f in (L.gdn_chunk_fwd, L.kda_chunk_fwd):
+            f.restype = ctypes.c_int
+            f.argtypes = [P, ctypes.c_void_p]
+        L.la_chunk_fwd_stages.restype = ctypes.c_int
+        L.la_chunk_fwd_stages.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.la_chunk_fwd_dv_split.restype = ctypes.c_int32
+        L.la_chunk_fwd_dv_split.argtypes = [P]
+        L.la_status_string.restype = ctypes.c_char_p
+        L.la_status_string.argtypes = [ctypes.c_int]
+        _lib = L
+    return _lib
+
+
+def _status_string(s):
+    try:
+        return lib().la_status_string(int(s)).decode()
+    except Exception:  # pragma: no cover - message only
+        return "?"
+
+
+def _stream(stream):
+    if stream is None:
+        return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    if isinstance(stream, torch.cuda.Stream):
+        return ctypes.c_void_p(stream.cuda_stream)
+    return ctypes.c_void_p(int(stream))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _need(t, name, dtype=None, shape=None, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def nt_max(T_max, N_max, BT=64):
+    """ceil(T_max/BT) + N_max - 1 (-1 for invalid arguments)."""
+    return int(lib().la_nt_max(int(T_max), int(N_max), int(BT)))
+
+
+def build_chunk_meta(cu_seqlens, T_max, BT=64, *, chunk_indices=None, chunk_offsets=None,
+                     status=None, stream=None):
+    """Device-side chunk metadata from cu_seqlens [N_max+1] int32.
+
+    Returns (chunk_indices [NT_max, 2], chunk_offsets [N_max+1], status [1]),
+    all int32 on cu_seqlens' device; pass preallocated tensors for capture.
+    """
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    N_max = cu_seqlens.numel() - 1
+    NT = nt_max(T_max, N_max, BT)
+    dev = cu_seqlens.device
+    if chunk_indices is None:
+        chunk_indices = torch.empty((max(NT, 0), 2), dtype=torch.int32, device=dev)
+    if chunk_offsets is None:
+        chunk_offsets = torch.empty((N_max + 1,), dtype=torch.int32, device=dev)
+    if status is None:
+        status = torch.empty((1,), dtype=torch.int32, device=dev)
+    _need(chunk_indices, "chunk_indices", torch.int32, (NT, 2), dev)
+    _need(chunk_offsets, "chunk_offsets", torch.int32, (N_max + 1,), dev)
+    _need(status, "status", torch.int32, (1,), dev)
+    rc = lib().build_chunk_meta(_ptr(cu_seqlens), N_max, int(T_max), int(BT),
+                                _ptr(chunk_indices), _ptr(chunk_offsets), _ptr(status),
+                                _stream(stream))
+    if rc != 0:
+        raise LinAttnError(rc, "build_chunk_meta")
+    return chunk_indices, chunk_offsets, status
+
+
+def _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, dv_split=0, BT=64):
+    a = ChunkFwdArgs()
+    a.T_max, a.N_max, a.H, a.d_k, a.d_v, a.BT = T_max, N_max, H, d_k, d_v, BT
+    a.qkv_dtype = LA_BF16 if qkv_dtype == torch.bfloat16 else LA_F32
+    a.dv_split = dv_split
+    return a
+
+
+def workspace_bytes(T_max, N_max, H, d_k, d_v, qkv_dtype, kda=False, BT=64):
+    a = _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, BT=BT)
+    return int(lib().la_chunk_fwd_workspace_bytes(ctypes.byref(a), int(kda)))
+
+
+def dv_split_for(T_max, N_max, H, d_k, d_v, qkv_dtype, dv_split=0):
+    a = _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, dv_split)
+    return int(lib().la_chunk_fwd_dv_split(ctypes.byref(a)))
+
+
+def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0, o, ht,
+             output_final_state, workspace, scale, dv_split):
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"q must be bfloat16 or float32, got {q.dtype}")
+    if q.dim() != 3:
+        raise ValueError("q must be [T_max, H, d_k]")
+    T_max, H, d_k = q.shape
+    d_v = v.shape[-1]
+    dev = q.device
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (T_max, H, d_k), dev)
+    _need(v, "v", q.dtype, (T_max, H, d_v), dev)
+    _need(g, "g", torch.float32, (T_max, H, d_k) if kda else (T_max, H), dev)
+    _need(beta, "beta", torch.float32, (T_max, H), dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+    N_max = cu_seqlens.numel() - 1
+    NT = nt_max(T_max, N_max)
+    _need(chunk_indices, "chunk_indices", torch.int32, (NT, 2), dev)
+    _need(chunk_offsets, "chunk_offsets", torch.int32, (N_max + 1,), dev)
+    st_shape = (N_max, H, d_k, d_v)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, st_shape, dev)
+    if o is None:
+        o = torch.empty((T_max, H, d_v), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, (T_max, H, d_v), dev)
+    if ht is None and output_final_state:
+        ht = torch.empty(st_shape, dtype=torch.float32, device=dev)
+    if ht is not None:
+        _need(ht, "ht", torch.float32, st_shape, dev)
+    a = _shape_args(T_max, N_max, H, d_k, d_v, q.dtype, dv_split)
+    need = int(lib().la_chunk_fwd_workspace_bytes(ctypes.byref(a), int(kda)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    a.scale = float(scale)
+    a.q, a.k, a.v, a.g, a.beta = (t.data_ptr() for t in (q, k, v, g, beta))
+    a.cu_seqlens = cu_seqlens.data_ptr()
+    a.chunk_indices = chunk_indices.data_ptr()
+    a.chunk_offsets = chunk_offsets.data_ptr()
+    a.h0 = None if h0 is None else h0.data_ptr()
+    a.o = o.data_ptr()
+    a.ht = None if ht is None else ht.data_ptr()
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel()
+    return a, o, ht, workspace
+
+
+def _call(name, kda, stages, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, *,
+          h0=None, o=None, ht=None, output_final_state=True, workspace=None, scale=1.0,
+          dv_split=0, stream=None):
+    a, o, ht, workspace = _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices,
+                                   chunk_offsets, h0, o, ht, output_final_state, workspace,
+                                   scale, dv_split)
+    L = lib()
+    s = _stream(stream)
+    if stages is None:
+        f = L.kda_chunk_fwd if kda else L.gdn_chunk_fwd
+        rc = f(ctypes.byref(a), s)
+    else:
+        rc = L.la_chunk_fwd_stages(ctypes.byref(a), int(kda), int(stages), s)
+    if rc != 0:
+        raise LinAttnError(rc, name)
+    return o, ht
+
+
+def gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, **kw):
+    """GDN chunk forward (scalar log-decay g [T_max, H]); returns (o, ht)."""
+    return _call("gdn_chunk_fwd", False, None, q, k, v, g, beta, cu_seqlens, chunk_indices,
+                 chunk_offsets, **kw)
+
+
+def kda_chunk_fwd(q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, **kw):
+    """KDA chunk forward (per-key-channel log-decay g [T_max, H, d_k]); returns (o, ht)."""
+    return _call("kda_chunk_fwd", True, None, q, k, v, g, beta, cu_seqlens, chunk_indices,
+                 chunk_offsets, **kw)
+
+
+def chunk_fwd_stages(kda, stages, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets,
+                     **kw):
+    """Run STAGE_MAP and/or STAGE_REDUCE of the forward (la_chunk_fwd_stages)."""
+    return _call("la_chunk_fwd_stages", bool(kda), stages, q, k, v, g, beta, cu_seqlens,
+                 chunk_indices, chunk_offsets, **kw)

@@ -1,0 +1,177 @@
+// Host side of the C ABI declared in include/linattn.h: argument checks (all
+// before anything is enqueued), workspace sizing, split choice and launches.
+// No allocation, no synchronisation, no state kept between calls.
+#include "../../include/linattn.h"
+
+#include <hip/hip_runtime.h>
+
+#include "kernels.h"
+
+namespace {
+
+constexpr int kBTSupported = 64;
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// shape checks shared by the workspace query and the forward calls
+int check_shape(const la_chunk_fwd_args *a) {
+  if (a->T_max < 1 || a->N_max < 1 || a->H < 1) return LA_ERR_SHAPE;
+  if (a->T_max > 0x7fffffff - 2 * kBTSupported) return LA_ERR_SHAPE;
+  if (a->qkv_dtype != LA_BF16 && a->qkv_dtype != LA_F32) return LA_ERR_DTYPE;
+  if (a->BT != kBTSupported) return LA_ERR_UNSUPPORTED;
+  if (a->d_k != a->d_v) return LA_ERR_UNSUPPORTED;
+  if (a->qkv_dtype == LA_BF16 && a->d_k != 64 && a->d_k != 128) return LA_ERR_UNSUPPORTED;
+  if (a->qkv_dtype == LA_F32 && a->d_k != 64) return LA_ERR_UNSUPPORTED;
+  const int s = a->dv_split;
+  if (s != 0 && s != 1 && s != 2 && s != 4 && s != 8) return LA_ERR_UNSUPPORTED;
+  if (s != 0 && a->d_v / s < 16) return LA_ERR_UNSUPPORTED;
+  // every (token, head) index and (slot, head) workspace index stays in size_t
+  const int64_t nt = la_nt_max(a->T_max, a->N_max, a->BT);
+  if (nt < 1 || nt > 0x7fffffff) return LA_ERR_SHAPE;
+  if ((int64_t)a->N_max * a->H > 0x7fffffff / 8) return LA_ERR_SHAPE;
+  return LA_OK;
+}
+
+int split_for(const la_chunk_fwd_args *a) {
+  if (a->dv_split) return a->dv_split;
+  // enough workgroups to cover the CUs about twice over, down to 16 columns
+  const int64_t units = (int64_t)a->N_max * a->H;
+  int s = 1;
+  while (units * s < 512 && a->d_v / (2 * s) >= 16 && s < 8) s *= 2;
+  return s;
+}
+
+size_t elem_bytes(const la_chunk_fwd_args *a) { return a->qkv_dtype == LA_BF16 ? 2 : 4; }
+
+size_t ws_bytes(const la_chunk_fwd_args *a) {
+  const size_t per = (size_t)a->BT * a->BT * elem_bytes(a);  // one BT x BT matrix
+  const size_t half = (size_t)la_nt_max(a->T_max, a->N_max, a->BT) * a->H * per;
+  return 2 * half;  // Tn then M
+}
+
+int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
+  if (!a) return LA_ERR_NULL;
+  if (stages < 1 || stages > 3) return LA_ERR_UNSUPPORTED;
+  const int sc = check_shape(a);
+  if (sc != LA_OK) return sc;
+  if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->cu_seqlens || !a->chunk_indices ||
+      !a->chunk_offsets || !a->o)
+    return LA_ERR_NULL;
+  if (!a->workspace) return LA_ERR_WORKSPACE;
+  if (a->workspace_bytes < ws_bytes(a)) return LA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(a->workspace) % 256 != 0) return LA_ERR_WORKSPACE;
+  if (a->h0 && a->ht && a->h0 != a->ht) {
+    const size_t sb = (size_t)a->N_max * a->H * a->d_k * a->d_v * sizeof(float);
+    if (overlaps(a->h0, sb, a->ht, sb)) return LA_ERR_ALIAS;
+  }
+  // 16-byte vector loads of q/k rows and of workspace rows
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->k);
+  if (mis % 16 != 0) return LA_ERR_SHAPE;
+
+  const bool bf = a->qkv_dtype == LA_BF16;
+  const size_t half = ws_bytes(a) / 2;
+  char *ws = static_cast<char *>(a->workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (stages & LA_STAGE_MAP) {
+    la::MapParams mp{};
+    mp.q = a->q;
+    mp.k = a->k;
+    mp.g = a->g;
+    mp.beta = a->beta;
+    mp.cu_seqlens = a->cu_seqlens;
+    mp.chunk_indices = a->chunk_indices;
+    mp.H = a->H;
+    mp.NT_max = (int)la_nt_max(a->T_max, a->N_max, a->BT);
+    mp.Tn_raw = ws;
+    mp.M_raw = ws + half;
+    if (la::launch_chunk_map(mp, kda, bf, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
+  }
+  if (stages & LA_STAGE_REDUCE) {
+    la::ReduceParams rp{};
+    rp.q = a->q;
+    rp.k = a->k;
+    rp.v = a->v;
+    rp.g = a->g;
+    rp.beta = a->beta;
+    rp.cu_seqlens = a->cu_seqlens;
+    rp.chunk_offsets = a->chunk_offsets;
+    rp.h0 = a->h0;
+    rp.o = a->o;
+    rp.ht = a->ht;
+    rp.Tn_raw = ws;
+    rp.M_raw = ws + half;
+    rp.H = a->H;
+    rp.N_max = a->N_max;
+    rp.S = split_for(a);
+    rp.scale = a->scale;
+    if (la::launch_chunk_reduce(rp, kda, bf, a->d_k, a->d_v / rp.S, st) != hipSuccess)
+      return LA_ERR_HIP;
+  }
+  return LA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t la_nt_max(int64_t T_max, int64_t N_max, int32_t BT) {
+  if (T_max < 1 || N_max < 1 || BT < 1) return -1;
+  return (T_max + BT - 1) / BT + N_max - 1;
+}
+
+int build_chunk_meta(const int32_t *cu_seqlens, int32_t N_max, int32_t T_max, int32_t BT,
+                     int32_t *chunk_indices, int32_t *chunk_offsets, int32_t *status,
+                     void *stream) {
+  if (!cu_seqlens || !chunk_indices || !chunk_offsets) return LA_ERR_NULL;
+  if (N_max < 1 || N_max > LA_MAX_N || T_max < 1 || T_max > 0x7fffffff - 2 * kBTSupported)
+    return LA_ERR_SHAPE;
+  if (BT != kBTSupported) return LA_ERR_UNSUPPORTED;
+  const int64_t nt = la_nt_max(T_max, N_max, BT);
+  if (nt > 0x7fffffff / 2) return LA_ERR_SHAPE;
+  if (la::launch_chunk_meta(cu_seqlens, N_max, T_max, BT, (int)nt, chunk_indices, chunk_offsets,
+                            status, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LA_ERR_HIP;
+  return LA_OK;
+}
+
+size_t la_chunk_fwd_workspace_bytes(const la_chunk_fwd_args *a, int is_kda) {
+  (void)is_kda;  // GDN and KDA keep the same per-chunk matrices
+  if (!a || check_shape(a) != LA_OK) return 0;
+  return ws_bytes(a);
+}
+
+int gdn_chunk_fwd(const la_chunk_fwd_args *a, void *stream) {
+  return forward(a, false, LA_STAGE_MAP | LA_STAGE_REDUCE, stream);
+}
+
+int kda_chunk_fwd(const la_chunk_fwd_args *a, void *stream) {
+  return forward(a, true, LA_STAGE_MAP | LA_STAGE_REDUCE, stream);
+}
+
+int la_chunk_fwd_stages(const la_chunk_fwd_args *a, int is_kda, int stages, void *stream) {
+  return forward(a, is_kda != 0, stages, stream);
+}
+
+int32_t la_chunk_fwd_dv_split(const la_chunk_fwd_args *a) {
+  if (!a || check_shape(a) != LA_OK) return 0;
+  return split_for(a);
+}
+
+const char *la_status_string(int status) {
+  switch (status) {
+    case LA_OK: return "ok";
+    case LA_ERR_NULL: return "a required pointer is NULL";
+    case LA_ERR_SHAPE: return "shape out of range or misaligned input";
+    case LA_ERR_DTYPE: return "unsupported dtype";
+    case LA_ERR_UNSUPPORTED: return "unsupported BT, head dim or dv_split";
+    case LA_ERR_WORKSPACE: return "workspace missing, misaligned or too small";
+    case LA_ERR_ALIAS: return "ht partially overlaps h0";
+    case LA_ERR_HIP: return "HIP launch failed";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

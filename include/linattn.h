@@ -1,0 +1,170 @@
+/*
+ * linattn.h -- C ABI of the MI355X (gfx950) varlen chunkwise gated-delta-rule
+ * prefill forward (GDN: scalar per-head decay; KDA: per-key-channel decay).
+ *
+ * The operation.  For each sequence n of a varlen batch and each head h, the
+ * per-head recurrent state ("Empowering Hybrid Attention Models on NPUs",
+ * section 2.1) evolves token by token as
+ *     S_t = S_{t-1} Diag(alpha_t) (I - beta_t k_t k_t^T) + beta_t v_t k_t^T,
+ *     o_t = scale * S_t q_t,        alpha_t = exp(g_t),
+ * where g_t is a log-decay: one value per (token, head) for GDN, one per
+ * (token, head, key channel) for KDA.  The library stores the state
+ * transposed, H = S^T, as a d_k x d_v fp32 block.  It is evaluated chunkwise
+ * with BT-token chunks as Map-Reduce-Map (same paper, section 2.1): a
+ * chunk-parallel map (gate cumsum, masked K K^T / Q K^T, triangular inverse)
+ * and a sequential reduce over each sequence's chunks that carries the state
+ * and forms the outputs -- the pipeline "gate / chunk cumsum -> forward intra
+ * -> recompute_w_u -> forward h -> forward o" of the FLA graph-capture RFC
+ * ("[RFC] Add Graph Capture Support for FLA Prefill and Training Paths on
+ * Ascend NPUs", section "Step 3").
+ *
+ * Fixed-capacity execution (same RFC, sections "Fixed-capacity execution",
+ * "Device-side metadata", "Static buffer contract", "API proposal").  A bucket
+ * is (T_max, N_max, BT) with NT_max = ceil(T_max/BT) + N_max - 1 chunk slots.
+ * cu_seqlens has the fixed shape [N_max+1]; build_chunk_meta turns it into
+ * chunk_indices [NT_max][2] (unused slots hold the sentinel {-1, 0}) and
+ * chunk_offsets [N_max+1] on the device, and every kernel grid is sized from
+ * (T_max, N_max, H) only, so one capture of the calls in a hipGraph replays
+ * any layout written into the same cu_seqlens buffer.
+ *
+ * Conventions for every entry point:
+ *  - All array pointers are DEVICE pointers owned by the caller.  The library
+ *    allocates nothing, caches nothing, creates no stream or graph and never
+ *    synchronises; calls are asynchronous on `stream` (a hipStream_t; NULL is
+ *    the null stream) and may be captured into a hipGraph.
+ *  - Arguments that can be checked on the host are checked before anything is
+ *    enqueued; a failed check returns a negative la_status and enqueues
+ *    nothing.  There is no fallback path.
+ *  - Layouts are row-major, token-major varlen packing (batch 1):
+ *    q, k [T_max][H][d_k]; v, o [T_max][H][d_v]; g [T_max][H] (GDN) or
+ *    [T_max][H][d_k] (KDA); beta [T_max][H]; h0, ht [N_max][H][d_k][d_v].
+ */
+#ifndef LINATTN_H
+#define LINATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LA_OK = 0,
+    LA_ERR_NULL = -1,        /* a required pointer is NULL                      */
+    LA_ERR_SHAPE = -2,       /* T_max, N_max or H out of range                  */
+    LA_ERR_DTYPE = -3,       /* unknown or unsupported dtype code               */
+    LA_ERR_UNSUPPORTED = -4, /* BT, d_k/d_v combination not built               */
+    LA_ERR_WORKSPACE = -5,   /* workspace NULL or smaller than required         */
+    LA_ERR_ALIAS = -6,       /* ht overlaps h0 without being identical          */
+    LA_ERR_HIP = -7          /* a HIP launch failed (hipGetLastError)           */
+} la_status;
+
+typedef enum { LA_BF16 = 0, LA_F32 = 1 } la_dtype;
+
+/* Device status bits written by build_chunk_meta (0 = valid cu_seqlens). */
+#define LA_META_BAD_START 1     /* cu_seqlens[0] != 0                           */
+#define LA_META_NOT_MONOTONE 2  /* cu_seqlens[n+1] < cu_seqlens[n] for some n   */
+#define LA_META_OVER_CAPACITY 4 /* cu_seqlens[N_max] > T_max                    */
+
+/* Largest N_max build_chunk_meta accepts (its offsets scan lives in LDS). */
+#define LA_MAX_N 8192
+
+/* Chunk capacity of a bucket: ceil(T_max/BT) + N_max - 1, or -1 if any
+ * argument is < 1 (FLA RFC, section "Fixed-capacity execution"). */
+int64_t la_nt_max(int64_t T_max, int64_t N_max, int32_t BT);
+
+/*
+ * Device-side metadata (FLA RFC, sections "Fixed-capacity execution" and
+ * "Device-side metadata").  Reads cu_seqlens[N_max+1] (int32) on the device
+ * and writes
+ *   chunk_offsets[n]    = sum_{m<n} ceil((cu[m+1]-cu[m]) / BT)   (int32, N_max+1)
+ *   chunk_indices[j]    = {n, i_t} for j = chunk_offsets[n] + i_t,
+ *                         {-1, 0}  for j >= chunk_offsets[N_max] (int32, NT_max x 2)
+ *   *status             = OR of LA_META_* bits (int32; status may be NULL).
+ * Slots are sequence-major then chunk-minor; zero-length sequences own none.
+ * If cu_seqlens is invalid (status != 0) every slot is the sentinel and every
+ * offset is 0, so the forward calls then write nothing.  One launch of one
+ * workgroup; capturable.
+ * Host errors: LA_ERR_NULL (cu_seqlens, chunk_indices or chunk_offsets NULL),
+ * LA_ERR_SHAPE (N_max < 1, N_max > LA_MAX_N, T_max < 1),
+ * LA_ERR_UNSUPPORTED (BT not 64), LA_ERR_HIP.
+ */
+int build_chunk_meta(const int32_t *cu_seqlens, int32_t N_max, int32_t T_max,
+                     int32_t BT, int32_t *chunk_indices,
+                     int32_t *chunk_offsets, int32_t *status, void *stream);
+
+/* Arguments of the forward calls.  Sizes describe the bucket (capacity); the
+ * actual layout comes from cu_seqlens on the device. */
+typedef struct {
+    int32_t T_max, N_max, H;   /* bucket capacity and head count (>= 1)          */
+    int32_t d_k, d_v;          /* head dims: d_k == d_v; 64 or 128 (bf16),       */
+                               /* 64 (fp32 inputs)                               */
+    int32_t BT;                /* chunk size: 64                                 */
+    int32_t qkv_dtype;         /* LA_BF16 or LA_F32: dtype of q, k, v            */
+    int32_t dv_split;          /* state column slices per (seq, head): 0 = auto, */
+                               /* else 1, 2, 4 or 8 (d_v / dv_split >= 16)       */
+    float scale;               /* o = scale * S q                                */
+    const void *q, *k, *v;     /* [T_max][H][d_k] / [T_max][H][d_v], qkv_dtype   */
+    const float *g;            /* log-decay: GDN [T_max][H]; KDA [T_max][H][d_k] */
+    const float *beta;         /* [T_max][H]                                     */
+    const int32_t *cu_seqlens; /* [N_max+1]                                      */
+    const int32_t *chunk_indices; /* [NT_max][2], from build_chunk_meta          */
+    const int32_t *chunk_offsets; /* [N_max+1], from build_chunk_meta            */
+    const float *h0;           /* [N_max][H][d_k][d_v] or NULL (zero state)      */
+    float *o;                  /* [T_max][H][d_v] fp32 output                    */
+    float *ht;                 /* [N_max][H][d_k][d_v] or NULL; may equal h0     */
+    void *workspace;           /* >= la_chunk_fwd_workspace_bytes(...) bytes,    */
+    size_t workspace_bytes;    /* 256-byte aligned                               */
+} la_chunk_fwd_args;
+
+/*
+ * Workspace the forward needs for this shape (only T_max, N_max, H, d_k, d_v,
+ * BT and qkv_dtype are read); 0 if the shape is invalid.  The workspace holds,
+ * per chunk slot and head, the chunk-local matrices of the map stage
+ * (T = A^-1 diag(beta) with its diagonal removed, and the masked decayed
+ * Q K^T), each BT x BT in fp16 (bf16 inputs) or fp32 (fp32 inputs); its
+ * content between calls is unspecified.
+ */
+size_t la_chunk_fwd_workspace_bytes(const la_chunk_fwd_args *shape, int is_kda);
+
+/*
+ * GDN / KDA chunk forward.  For every non-empty sequence n and head h:
+ * o rows cu[n]..cu[n+1]-1 of head h and ht[n][h] (if ht != NULL) are written;
+ * o rows >= cu[N_max], sentinel slots and zero-length sequences are never
+ * written.  h0 == NULL means a zero initial state.  ht may be the same
+ * pointer as h0 (in-place state update); a partial overlap is LA_ERR_ALIAS.
+ * Matrix products run on MFMA: bf16 inputs in fp16 operands with fp32
+ * accumulation (inputs and intermediates must stay within fp16 range,
+ * |x| < 65504; g <= 0 is assumed for KDA), fp32 inputs in fp32 operands.
+ * The metadata must come from build_chunk_meta on the same cu_seqlens, T_max,
+ * N_max and BT.
+ * Host errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_UNSUPPORTED,
+ * LA_ERR_WORKSPACE, LA_ERR_ALIAS, LA_ERR_HIP.
+ */
+int gdn_chunk_fwd(const la_chunk_fwd_args *a, void *stream);
+int kda_chunk_fwd(const la_chunk_fwd_args *a, void *stream);
+
+/*
+ * The forward split into its two launches, for callers that time or overlap
+ * them: stages = LA_STAGE_MAP runs the chunk-parallel map into the workspace,
+ * LA_STAGE_REDUCE runs the sequential reduce + output from it, and
+ * LA_STAGE_MAP | LA_STAGE_REDUCE equals gdn_chunk_fwd / kda_chunk_fwd.
+ * A reduce must follow a map of the same arguments on the same workspace.
+ */
+#define LA_STAGE_MAP 1
+#define LA_STAGE_REDUCE 2
+int la_chunk_fwd_stages(const la_chunk_fwd_args *a, int is_kda, int stages,
+                        void *stream);
+
+/* The dv_split the forward uses for these arguments (after "auto"). */
+int32_t la_chunk_fwd_dv_split(const la_chunk_fwd_args *a);
+
+/* Static text for a la_status value. */
+const char *la_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LINATTN_H */

@@ -1,0 +1,73 @@
+"""Shared helpers for the GPU parity tests: move seeded inputs to the device,
+run the library, run the oracle on the same values, compare."""
+
+import numpy as np
+import torch
+
+import chunkwise_gated_delta_chunk_amd as la
+from oracle import recurrence
+
+# max relative error gates: bf16 inputs (fp16 MFMA operands, fp32 accumulation)
+# and fp32 inputs (fp32 MFMA)
+TOL = {"bf16": 2e-3, "f32": 1e-4}
+
+
+def rel_err(x, ref, mask=None):
+    """max |x - ref| / max |ref| over the valid elements (mask over leading dims)."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if mask is not None:
+        x, ref = x[mask], ref[mask]
+    if ref.size == 0:
+        return 0.0
+    return float(np.abs(x - ref).max() / max(np.abs(ref).max(), 1e-30))
+
+
+def to_dev(inp, device="cuda"):
+    tdt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    d = {}
+    for key in ("q", "k", "v"):
+        d[key] = torch.from_numpy(inp[key]).to(device=device, dtype=tdt).contiguous()
+    for key in ("g", "beta"):
+        d[key] = torch.from_numpy(inp[key]).to(device=device).contiguous()
+    d["cu_seqlens"] = torch.from_numpy(inp["cu_seqlens"].astype(np.int32)).to(device)
+    d["h0"] = None if inp["h0"] is None else torch.from_numpy(inp["h0"]).to(device).contiguous()
+    return d
+
+
+def run_gpu(inp, *, dv_split=0, scale=1.0, device="cuda", with_state=True, o=None, ht=None,
+            h0=None, stream=None):
+    d = to_dev(inp, device)
+    T = inp["q"].shape[0]
+    ci, co, st = la.build_chunk_meta(d["cu_seqlens"], T, stream=stream)
+    fwd = la.kda_chunk_fwd if inp["kda"] else la.gdn_chunk_fwd
+    o, ht = fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], ci, co,
+                h0=d["h0"] if h0 is None else h0, o=o, ht=ht, output_final_state=with_state,
+                scale=scale, dv_split=dv_split, stream=stream)
+    torch.cuda.synchronize()
+    return o, ht, (ci, co, st)
+
+
+def run_oracle(inp, *, scale=1.0, heads=None):
+    """Oracle on the same input values; ``heads`` restricts to a head subset."""
+    sel = slice(None) if heads is None else list(heads)
+    q, k, v, g, b = (inp[x][:, sel] for x in ("q", "k", "v", "g", "beta"))
+    h0 = None if inp["h0"] is None else inp["h0"][:, sel]
+    return recurrence.gated_delta_fwd(q, k, v, g, b, inp["cu_seqlens"], h0, scale,
+                                      kda=inp["kda"])
+
+
+def compare(inp, o, ht, o_ref, ht_ref, heads=None, tol=None):
+    """rel errors of o over covered rows and of ht over non-empty sequences."""
+    tol = TOL[inp["dtype"]] if tol is None else tol
+    sel = slice(None) if heads is None else list(heads)
+    cu = inp["cu_seqlens"]
+    rows = slice(0, int(cu[-1]))
+    o_np = o.float().cpu().numpy()[rows][:, sel]
+    eo = rel_err(o_np, o_ref[rows])
+    eh = 0.0
+    if ht is not None and ht_ref is not None:
+        nonempty = np.diff(cu.astype(np.int64)) > 0
+        h_np = ht.cpu().numpy()[:, sel]
+        eh = rel_err(h_np[nonempty], ht_ref[nonempty])
+    return eo, eh, tol

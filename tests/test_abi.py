@@ -1,0 +1,124 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/linattn.h declares, and rejects bad arguments on the host before
+anything is enqueued (every case below fails a host check, so no launch is
+attempted)."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import chunkwise_gated_delta_chunk_amd as la
+from oracle import meta_ref
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "linattn.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[A-Za-z_][\w\s\*]*?\b([A-Za-z_]\w*)\s*\(",
+                                 text, flags=re.M)) - {"defined"})
+
+
+def test_exports_every_declared_function():
+    names = declared_functions()
+    assert {"build_chunk_meta", "gdn_chunk_fwd", "kda_chunk_fwd", "la_nt_max",
+            "la_chunk_fwd_workspace_bytes", "la_status_string"} <= set(names)
+    L = ctypes.CDLL(la.LIB_PATH)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+@pytest.mark.parametrize("T,N,BT", [(16384, 64, 64), (8192, 8, 64), (1, 1, 64), (65, 3, 32),
+                                    (0, 3, 64), (5, 0, 64)])
+def test_nt_max_matches_formula(T, N, BT):
+    want = meta_ref.nt_max(T, N, BT) if T >= 1 and N >= 1 else -1
+    assert la.nt_max(T, N, BT) == want
+
+
+def test_status_strings():
+    for s in range(0, -8, -1):
+        assert la.lib().la_status_string(s)
+    assert la.lib().la_status_string(99) == b"unknown status"
+
+
+def _args(**kw):
+    a = la.ChunkFwdArgs()
+    a.T_max, a.N_max, a.H, a.d_k, a.d_v, a.BT, a.qkv_dtype = 256, 2, 2, 64, 64, 64, 0
+    a.scale = 1.0
+    fake = 0x100000  # 256-aligned, never dereferenced: every case fails before launch
+    for f in ("q", "k", "v", "g", "beta", "cu_seqlens", "chunk_indices", "chunk_offsets", "o",
+              "workspace"):
+        setattr(a, f, fake)
+    a.workspace_bytes = 1 << 30
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+BAD = [
+    ("null q", dict(q=None), -1),
+    ("null o", dict(o=None), -1),
+    ("null metadata", dict(chunk_offsets=None), -1),
+    ("T_max 0", dict(T_max=0), -2),
+    ("N_max 0", dict(N_max=0), -2),
+    ("H 0", dict(H=0), -2),
+    ("dtype 7", dict(qkv_dtype=7), -3),
+    ("BT 32", dict(BT=32), -4),
+    ("d 96", dict(d_k=96, d_v=96), -4),
+    ("d_k != d_v", dict(d_v=128), -4),
+    ("fp32 d 128", dict(qkv_dtype=1, d_k=128, d_v=128), -4),
+    ("dv_split 3", dict(dv_split=3), -4),
+    ("dv_split too fine", dict(dv_split=8), -4),
+    ("no workspace", dict(workspace=None), -5),
+    ("workspace small", dict(workspace_bytes=100), -5),
+    ("workspace misaligned", dict(workspace=0x100010), -5),
+    ("q misaligned", dict(q=0x100008), -2),
+    ("ht partly over h0", dict(h0=0x200000, ht=0x200000 + 4096), -6),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BAD, ids=[b[0] for b in BAD])
+def test_forward_rejects_on_host(name, kw, code):
+    a = _args(**kw)
+    L = la.lib()
+    assert L.gdn_chunk_fwd(ctypes.byref(a), None) == code
+    assert L.kda_chunk_fwd(ctypes.byref(a), None) == code
+    assert L.la_chunk_fwd_stages(ctypes.byref(a), 0, 3, None) == code
+
+
+def test_forward_null_args_and_bad_stages():
+    L = la.lib()
+    assert L.gdn_chunk_fwd(None, None) == -1
+    a = _args(workspace_bytes=100)
+    assert L.la_chunk_fwd_stages(ctypes.byref(a), 0, 0, None) == -4
+    assert L.la_chunk_fwd_stages(ctypes.byref(a), 0, 4, None) == -4
+
+
+def test_meta_rejects_on_host():
+    L = la.lib()
+    p = ctypes.c_void_p(0x100000)
+    assert L.build_chunk_meta(None, 2, 256, 64, p, p, None, None) == -1
+    assert L.build_chunk_meta(p, 2, 256, 64, None, p, None, None) == -1
+    assert L.build_chunk_meta(p, 0, 256, 64, p, p, None, None) == -2
+    assert L.build_chunk_meta(p, 8193, 256, 64, p, p, None, None) == -2
+    assert L.build_chunk_meta(p, 2, 0, 64, p, p, None, None) == -2
+    assert L.build_chunk_meta(p, 2, 256, 32, p, p, None, None) == -4
+
+
+def test_workspace_size_and_split():
+    import torch
+    for (T, N, H, d, dt, esz) in [(8192, 8, 16, 128, torch.bfloat16, 2),
+                                  (256, 1, 2, 64, torch.float32, 4),
+                                  (16384, 64, 32, 128, torch.bfloat16, 2)]:
+        want = 2 * meta_ref.nt_max(T, N, 64) * H * 64 * 64 * esz
+        assert la.workspace_bytes(T, N, H, d, d, dt) == want
+        assert la.workspace_bytes(T, N, H, d, d, dt, kda=True) == want
+    assert la.workspace_bytes(0, 1, 1, 64, 64, torch.bfloat16) == 0
+    assert la.dv_split_for(8192, 8, 16, 128, 128, torch.bfloat16) == 4
+    assert la.dv_split_for(4096, 1, 16, 128, 128, torch.bfloat16) == 8
+    assert la.dv_split_for(16384, 64, 32, 128, 128, torch.bfloat16) == 1
+    assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32) == 4
+    assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32, dv_split=2) == 2

@@ -1,0 +1,257 @@
+"""GPU parity: the HIP path through the C ABI against the fp64 oracle.
+
+Bar: max relative error (max |x - ref| / max |ref| over valid elements)
+<= 2e-3 for bf16 inputs and <= 1e-4 for fp32 inputs, for o (rows of real
+tokens) and ht (non-empty sequences); metadata bit-exact; padding rows,
+sentinel slots and empty sequences never written.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import chunkwise_gated_delta_chunk_amd as la
+from oracle import chunkwise_ref, meta_ref
+from synth import config, make_inputs
+from tests.helpers import TOL, compare, rel_err, run_gpu, run_oracle, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+# ------------------------------------------------------------- metadata ---
+def _meta_case(cu, N_max, T_max):
+    cu_t = torch.tensor(cu, dtype=torch.int32, device="cuda")
+    ci, co, st = la.build_chunk_meta(cu_t, T_max)
+    torch.cuda.synchronize()
+    ref_i, ref_o, ref_s = meta_ref.chunk_meta(cu, N_max, T_max, 64)
+    assert np.array_equal(ci.cpu().numpy(), ref_i)
+    assert np.array_equal(co.cpu().numpy(), ref_o)
+    assert int(st.item()) == ref_s
+
+
+def test_meta_golden_cases():
+    import json, os
+    cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "meta_cases.json")))
+    for c in cases["cases"]:
+        if c["BT"] != 64:
+            continue
+        _say("meta case", c["name"])
+        _meta_case(c["cu"], c["N_max"], c["T_max"])
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_meta_random_layouts(seed):
+    from synth import bucket_layout
+    rng = np.random.default_rng(100 + seed)
+    for _ in range(10):
+        T_max = int(rng.integers(1, 20000))
+        N_max = int(rng.integers(1, 300))
+        cu = bucket_layout(rng, T_max, N_max)
+        _meta_case(cu.tolist(), N_max, T_max)
+
+
+def test_meta_large_n_and_capacity():
+    _meta_case([0] + [1] * 8191 + [16384], 8192, 16384)   # N_max = LA_MAX_N
+    rng = np.random.default_rng(7)
+    from synth import bucket_layout
+    cu = bucket_layout(rng, 16384, 64)
+    _meta_case(cu.tolist(), 64, 16384)
+
+
+# ---------------------------------------------------------------- fp32 ---
+def test_config0_fp32():
+    inp = config(0)
+    o, ht, _ = run_gpu(inp)
+    o_ref, ht_ref = run_oracle(inp)
+    eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref)
+    _say(f"config0 o {eo:.2e} ht {eh:.2e}")
+    assert eo <= TOL["f32"] and eh <= TOL["f32"]
+
+
+# ------------------------------------------------------ small bf16 GDN/KDA ---
+SMALL_CU = [0, 1, 64, 64, 200, 333, 460]   # one-token, exact chunk, empty, tails
+
+
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("split", [1, 2, 4])
+def test_small_bf16(kda, d, split):
+    if d // split < 16:
+        pytest.skip("slice narrower than 16")
+    inp = make_inputs(SMALL_CU[-1], 3, d, d, kda=kda, dtype="bf16", seed=20 + d + split,
+                      cu_seqlens=SMALL_CU, h0_std=0.1)
+    o, ht, _ = run_gpu(inp, dv_split=split)
+    o_ref, ht_ref = run_oracle(inp)
+    eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref)
+    _say(f"small kda={kda} d={d} split={split}: o {eo:.2e} ht {eh:.2e}")
+    assert eo <= tol and eh <= tol
+
+
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+def test_small_fp32(kda):
+    inp = make_inputs(SMALL_CU[-1], 2, 64, 64, kda=kda, dtype="f32", seed=31,
+                      cu_seqlens=SMALL_CU, h0_std=0.1)
+    for split in (1, 4):
+        o, ht, _ = run_gpu(inp, dv_split=split, scale=0.5)
+        o_ref, ht_ref = run_oracle(inp, scale=0.5)
+        eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref)
+        _say(f"fp32 kda={kda} split={split}: o {eo:.2e} ht {eh:.2e}")
+        assert eo <= tol and eh <= tol
+
+
+# ---------------------------------------------------------- map stage ---
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+def test_map_stage_matrices(kda):
+    """T (diagonal removed) and M in the workspace against the chunkwise reference."""
+    cu = [0, 64, 100, 230]
+    inp = make_inputs(230, 2, 128, 128, kda=kda, dtype="bf16", seed=41, cu_seqlens=cu)
+    d = to_dev(inp)
+    ci, co, _ = la.build_chunk_meta(d["cu_seqlens"], 230)
+    nbytes = la.workspace_bytes(230, 3, 2, 128, 128, torch.bfloat16, kda)
+    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    la.chunk_fwd_stages(kda, la.STAGE_MAP, d["q"], d["k"], d["v"], d["g"], d["beta"],
+                        d["cu_seqlens"], ci, co, workspace=ws)
+    torch.cuda.synchronize()
+    NT = la.nt_max(230, 3)
+    half = ws[: nbytes // 2].view(torch.float16).view(NT, 2, 64, 64).float().cpu().numpy()
+    mm = ws[nbytes // 2:].view(torch.float16).view(NT, 2, 64, 64).float().cpu().numpy()
+    _, _, inter = chunkwise_ref.chunk_forward(inp["q"], inp["k"], inp["v"], inp["g"],
+                                              inp["beta"], cu, None, kda=kda, keep=True)
+    for (slot, h), it in inter.items():
+        C = it["T"].shape[0]
+        Tref = it["T"] - np.diag(np.diag(it["T"]))
+        et = rel_err(half[slot, h, :C, :C], Tref)
+        em = rel_err(mm[slot, h, :C, :C], it["M"])
+        assert et < 2e-3 and em < 2e-3, (slot, h, et, em)
+        # tail rows/columns and the upper triangle are exactly zero
+        assert not half[slot, h, C:, :].any() and not half[slot, h, :, C:].any()
+        assert not np.triu(half[slot, h], 0).any()
+        assert not np.triu(mm[slot, h], 1).any()
+
+
+# --------------------------------------------------- workloads at size ---
+def test_config1_full():
+    inp = config(1)
+    _say("config1 cu", inp["cu_seqlens"].tolist())
+    o, ht, _ = run_gpu(inp)
+    o_ref, ht_ref = run_oracle(inp)
+    eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref)
+    _say(f"config1 o {eo:.2e} ht {eh:.2e}")
+    assert eo <= tol and eh <= tol
+
+
+def test_config2_kda_full():
+    inp = config(2)
+    o, ht, _ = run_gpu(inp)
+    o_ref, ht_ref = run_oracle(inp)
+    eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref)
+    _say(f"config2 o {eo:.2e} ht {eh:.2e}")
+    assert eo <= tol and eh <= tol
+
+
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+def test_config4_short(kda):
+    inp = config(4, kda=kda, T=2048)
+    o, ht, _ = run_gpu(inp)
+    o_ref, ht_ref = run_oracle(inp)
+    eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref)
+    _say(f"config4 T=2048 kda={kda} o {eo:.2e} ht {eh:.2e}")
+    assert eo <= tol and eh <= tol
+
+
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+def test_config4_long_sampled_heads(kda):
+    """T=65536, one sequence: oracle on two of the ten heads."""
+    inp = config(4, kda=kda)
+    o, ht, _ = run_gpu(inp)
+    heads = [0, 7]
+    o_ref, ht_ref = run_oracle(inp, heads=heads)
+    eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref, heads=heads)
+    _say(f"config4 T=65536 kda={kda} heads {heads}: o {eo:.2e} ht {eh:.2e}")
+    assert eo <= tol and eh <= tol
+
+
+@pytest.mark.parametrize("replay", [0, 1])
+def test_config3_layouts_sampled_heads(replay):
+    inp = config(3, replay=replay)
+    cu = inp["cu_seqlens"]
+    _say(f"config3 replay {replay}: N={int((np.diff(cu) > 0).sum())} total={int(cu[-1])}")
+    o, ht, _ = run_gpu(inp)
+    heads = [replay, 31 - replay]
+    o_ref, ht_ref = run_oracle(inp, heads=heads)
+    eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref, heads=heads)
+    _say(f"config3 o {eo:.2e} ht {eh:.2e}")
+    assert eo <= tol and eh <= tol
+
+
+# ------------------------------------------------------ write contract ---
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+def test_padding_and_empty_slots_untouched(kda):
+    """Padding rows hold NaN and canaries: no leak into results, no writes."""
+    T_max, cu = 700, [0, 130, 130, 300, 300, 300]     # rows 300.. are padding
+    inp = make_inputs(T_max, 2, 128, 128, kda=kda, dtype="bf16", seed=51, cu_seqlens=cu,
+                      h0_std=0.1)
+    for key in ("q", "k", "v", "g"):
+        inp[key][300:] = np.nan
+    inp["beta"][300:] = np.nan
+    o = torch.full((T_max, 2, 128), 123.0, device="cuda")
+    ht = torch.full((5, 2, 128, 128), -7.0, device="cuda")
+    o, ht, _ = run_gpu(inp, o=o, ht=ht)
+    o_np, ht_np = o.cpu().numpy(), ht.cpu().numpy()
+    assert (o_np[300:] == 123.0).all()
+    for n in (1, 3, 4):                                 # empty sequences
+        assert (ht_np[n] == -7.0).all()
+    assert np.isfinite(o_np[:300]).all() and np.isfinite(ht_np[[0, 2]]).all()
+    clean = dict(inp, q=inp["q"][:300], k=inp["k"][:300], v=inp["v"][:300], g=inp["g"][:300],
+                 beta=inp["beta"][:300])
+    o_ref, ht_ref = run_oracle(clean)
+    eo = rel_err(o_np[:300], o_ref[:300])
+    eh = rel_err(ht_np[[0, 2]], ht_ref[[0, 2]])
+    assert eo <= 2e-3 and eh <= 2e-3
+
+
+def test_invalid_cu_writes_nothing():
+    inp = make_inputs(256, 2, 64, 64, kda=False, dtype="bf16", seed=52, cu_seqlens=[0, 200, 100])
+    d = to_dev(inp)
+    ci, co, st = la.build_chunk_meta(d["cu_seqlens"], 256)
+    o = torch.full((256, 2, 64), 5.0, device="cuda")
+    ht = torch.full((2, 2, 64, 64), 6.0, device="cuda")
+    la.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], ci, co, o=o, ht=ht)
+    torch.cuda.synchronize()
+    assert int(st.item()) == la.META_NOT_MONOTONE
+    assert (o == 5.0).all() and (ht == 6.0).all()
+
+
+def test_in_place_state_and_determinism():
+    inp = make_inputs(300, 2, 128, 128, kda=False, dtype="bf16", seed=53,
+                      cu_seqlens=[0, 100, 300], h0_std=0.1)
+    o1, ht1, _ = run_gpu(inp)
+    o2, ht2, _ = run_gpu(inp)
+    assert torch.equal(o1, o2) and torch.equal(ht1, ht2)      # bitwise repeatable
+    d = to_dev(inp)
+    state = d["h0"].clone()
+    ci, co, _ = la.build_chunk_meta(d["cu_seqlens"], 300)
+    o3, ht3 = la.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], ci, co,
+                               h0=state, ht=state)
+    torch.cuda.synchronize()
+    assert ht3.data_ptr() == state.data_ptr()
+    assert torch.equal(o3, o1) and torch.equal(state, ht1)
+
+
+def test_no_initial_state_equals_zero_state():
+    inp = make_inputs(200, 2, 64, 64, kda=True, dtype="bf16", seed=54, cu_seqlens=[0, 70, 200])
+    o1, ht1, _ = run_gpu(inp)
+    z = torch.zeros((2, 2, 64, 64), device="cuda")
+    o2, ht2, _ = run_gpu(inp, h0=z)
+    assert torch.equal(o1, o2) and torch.equal(ht1, ht2)
+
+
+def test_scale_is_linear():
+    inp = make_inputs(200, 2, 64, 64, kda=False, dtype="bf16", seed=55, cu_seqlens=[0, 200])
+    o1, ht1, _ = run_gpu(inp, scale=1.0)
+    o2, ht2, _ = run_gpu(inp, scale=0.125)
+    assert torch.equal(o1 * 0.125, o2) and torch.equal(ht1, ht2)
