@@ -1,0 +1,287 @@
+"""Benchmark of the varlen chunkwise gated-delta-rule prefill forward on one MI355X.
+
+One step = the whole hot path over one batch: device chunk metadata
+(build_chunk_meta), the chunk-parallel map and the sequential reduce + output,
+captured once in a HIP graph and replayed (the fixed-capacity graph-replay mode
+of the FLA graph-capture RFC, section "Performance evaluation").  Inputs are
+seeded synthetic tensors already resident in HBM.
+
+Prints ONE JSON line.  ``value`` is tokens/s of graph replays; ``roofline``
+describes the dominant kernel (average duration measured live with HIP events
+on the launch stream); ``cpu_baseline`` is the fp64 oracle timed on this
+host's cores.  ``--gpus N`` with N > 1 exits: this build runs on one GPU.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+
+WORKLOADS = {
+    "c1": (1, None, "GDN varlen prefill: bf16 q/k/v, fp32 g/beta/state, H=16, d_k=d_v=128, "
+                    "BT=64, T=8192 cut into 8 sequences by 7 uniform cut points, "
+                    "h0~N(0,0.1), seed 1"),
+    "c2": (2, None, "KDA: bf16, one sequence T=4096, H=16, d_k=d_v=128, BT=64, zero state, seed 2"),
+    "c4g": (4, False, "GDN: bf16, one sequence T=65536, H=10, d=128, BT=64, zero state, seed 4"),
+    "c4k": (4, True, "KDA: bf16, one sequence T=65536, H=10, d=128, BT=64, zero state, seed 4"),
+    "c4g_short": (4, False, "GDN: bf16, one sequence T=2048, H=10, d=128, zero state, seed 4"),
+    "c4k_short": (4, True, "KDA: bf16, one sequence T=2048, H=10, d=128, zero state, seed 4"),
+}
+
+KERNEL_SOURCES = ["la_device.h", "kernels.h", "chunk_map.hip", "chunk_reduce.hip", "meta.hip"]
+
+
+def kernel_source_hash(name):
+    h = hashlib.sha256()
+    for f in ["la_device.h", "kernels.h", name]:
+        with open(os.path.join(ROOT, "chunkwise_gated_delta_chunk_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def alg_bytes(inp, kind):
+    """Algorithmic HBM bytes of one launch ('Measurement')."""
+    T = int(inp["cu_seqlens"][-1])
+    H, dk, dv = inp["H"], inp["dk"], inp["dv"]
+    s_qkv = 2 if inp["dtype"] == "bf16" else 4
+    s_g = 4 * dk if inp["kda"] else 4
+    lens = np.diff(inp["cu_seqlens"].astype(np.int64))
+    nonempty = int((lens > 0).sum())
+    chunks = int((-(-lens // 64)).sum())
+    state = nonempty * H * dk * dv * 4 * ((inp["h0"] is not None) + 1)
+    mats = chunks * H * 2 * 64 * 64 * s_qkv          # Tn and M, one write + one read
+    if kind == "op":
+        return T * H * ((2 * dk + dv) * s_qkv + s_g + 4 + 4 * dv) + state
+    if kind == "map":
+        return T * H * (2 * dk * s_qkv + s_g + 4) + mats
+    if kind == "reduce":
+        return T * H * ((2 * dk + dv) * s_qkv + s_g + 4 + 4 * dv) + mats + state
+    raise ValueError(kind)
+
+
+def alg_flops(inp):
+    """Dense chunk GEMM flops + 2/3 C^3 for the inverse, per chunk-head (C=64)."""
+    lens = np.diff(inp["cu_seqlens"].astype(np.int64))
+    chunks = int((-(-lens // 64)).sum())
+    C, dk, dv = 64, inp["dk"], inp["dv"]
+    per = (2 * C * C * dk * 3 + 2 * C * C * dv + 3 * 2 * C * dk * dv + 2 * C * C * dv
+           + 2 * C ** 3 / 3)
+    return chunks * inp["H"] * per
+
+
+def load_traffic(kernel_kind, workload):
+    """HBM traffic of the dominant kernel from the committed counter summary, if
+    it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel_kind}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = "chunk_reduce.hip" if kernel_kind == "reduce" else "chunk_map.hip"
+    if rec.get("kernel_src_sha") != kernel_source_hash(src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, budget_s=12.0):
+    """Time the fp64 oracle (as it stands) on this host: whole workload, repeated
+    until ~budget_s of wall time or 3 runs."""
+    from oracle import recurrence
+    T = int(inp["cu_seqlens"][-1])
+    units = int((np.diff(inp["cu_seqlens"]) > 0).sum()) * inp["H"]
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    omp = int(os.environ.get("OMP_NUM_THREADS", cores))
+    threads = max(1, min(cores, omp, units))
+    times = []
+    t_all = time.perf_counter()
+    while len(times) < 3 and (time.perf_counter() - t_all) < budget_s:
+        t0 = time.perf_counter()
+        recurrence.gated_delta_fwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"],
+                                   inp["cu_seqlens"], inp["h0"], kda=inp["kda"],
+                                   nthreads=threads)
+        times.append(time.perf_counter() - t0)
+    t = float(np.median(times))
+    return {"value": T / t, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"whole workload ({T} tokens x {inp['H']} heads), median of "
+                      f"{len(times)} run(s) of the fp64 token recurrence, {threads} OpenMP "
+                      f"threads of {cores} host cores"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="c1", choices=sorted(WORKLOADS))
+    ap.add_argument("--dv-split", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(see DESIGN.md, 'More than one GPU').", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import chunkwise_gated_delta_chunk_amd as la
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        n = args.copy_calibration * (1 << 20) // 4
+        src = torch.randn(n, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n * 4, "bytes_written": n * 4,
+                          "launches": 3}))
+        return
+
+    cfg, kda, desc = WORKLOADS[args.workload]
+    T_arg = 2048 if args.workload.endswith("_short") else None
+    inp = synth.config(cfg, kda=kda, T=T_arg) if cfg == 4 else synth.config(cfg)
+    T = inp["q"].shape[0]
+    H, dk, dv = inp["H"], inp["dk"], inp["dv"]
+    tdt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    q = torch.from_numpy(inp["q"]).to(dev, tdt)
+    k = torch.from_numpy(inp["k"]).to(dev, tdt)
+    v = torch.from_numpy(inp["v"]).to(dev, tdt)
+    g = torch.from_numpy(inp["g"]).to(dev)
+    beta = torch.from_numpy(inp["beta"]).to(dev)
+    cu = torch.from_numpy(inp["cu_seqlens"].astype(np.int32)).to(dev)
+    N = cu.numel() - 1
+    h0 = None if inp["h0"] is None else torch.from_numpy(inp["h0"]).to(dev)
+    NT = la.nt_max(T, N)
+    ci = torch.empty((NT, 2), dtype=torch.int32, device=dev)
+    co = torch.empty((N + 1,), dtype=torch.int32, device=dev)
+    st = torch.empty((1,), dtype=torch.int32, device=dev)
+    o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
+    ht = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    ws = torch.empty((la.workspace_bytes(T, N, H, dk, dv, tdt, bool(inp["kda"])),),
+                     dtype=torch.uint8, device=dev)
+    fwd_kw = dict(h0=h0, o=o, ht=ht, workspace=ws, dv_split=args.dv_split)
+    split = la.dv_split_for(T, N, H, dk, dv, tdt, args.dv_split)
+    is_kda = bool(inp["kda"])
+    fwd = la.kda_chunk_fwd if is_kda else la.gdn_chunk_fwd
+
+    def step():
+        la.build_chunk_meta(cu, T, chunk_indices=ci, chunk_offsets=co, status=st)
+        fwd(q, k, v, g, beta, cu, ci, co, **fwd_kw)
+
+    # ---- eager warmup + per-kernel HIP-event timing on the launch stream
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        e = evs[i]
+        e[0].record()
+        la.build_chunk_meta(cu, T, chunk_indices=ci, chunk_offsets=co, status=st)
+        e[1].record()
+        la.chunk_fwd_stages(is_kda, la.STAGE_MAP, q, k, v, g, beta, cu, ci, co, **fwd_kw)
+        e[2].record()
+        la.chunk_fwd_stages(is_kda, la.STAGE_REDUCE, q, k, v, g, beta, cu, ci, co, **fwd_kw)
+        e[3].record()
+    torch.cuda.synchronize()
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])  # ms
+    t_meta, t_map, t_red = (float(x) for x in per.mean(axis=0))
+    eager_o = o.clone()
+    eager_ht = ht.clone()
+
+    # eager whole-step timing (no events between kernels)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    # ---- graph capture of one step, replay timing
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    tc = time.perf_counter()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    capture_ms = (time.perf_counter() - tc) * 1e3
+    for _ in range(args.warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+    graph_eq = bool(torch.equal(o, eager_o) and torch.equal(ht, eager_ht))
+
+    tokens = int(inp["cu_seqlens"][-1])
+    value = tokens * args.steps / elapsed
+
+    kernels = {"meta": t_meta, "map": t_map, "reduce": t_red}
+    dom = "reduce" if t_red >= t_map else "map"
+    dom_ms = kernels[dom]
+    ab = alg_bytes(inp, dom)
+    achieved = ab / (dom_ms * 1e-3) / 1e9
+    traffic = load_traffic(dom, args.workload)
+    op_bytes = alg_bytes(inp, "op")
+    op_flops = alg_flops(inp)
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": f"chunk_reduce_kernel (d_v split {split})" if dom == "reduce"
+            else "chunk_map_kernel",
+            "alg_bytes_per_launch": ab, "avg_launch_ms": round(dom_ms, 5)}
+
+    out = {
+        "metric": "GDN/KDA chunk-fwd tokens/s (H=16,d=128,8K varlen); % of HBM/MFMA roofline",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 inputs; fp16 MFMA operands, fp32 accumulation and state"
+        if inp["dtype"] == "bf16" else "fp32",
+        "data": "synthetic (seeded, resident in HBM)",
+        "config": {"workload": desc, "mode": "graph-replay of meta+map+reduce",
+                   "tokens": tokens, "heads": H, "d": dk, "sequences": N, "nt_max": NT,
+                   "dv_split": split},
+        "roofline": roof,
+        "op_roofline": {
+            "alg_bytes": op_bytes, "alg_flops": op_flops,
+            "hbm_frac": round(op_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(op_flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+        "kernels_ms": {k2: round(v2, 5) for k2, v2 in kernels.items()},
+        "eager_ms_per_step": round(eager_ms, 5), "capture_ms": round(capture_ms, 3),
+        "graph_equals_eager": graph_eq,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -16,6 +16,9 @@ FLAGS = [
     "-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
     # packed fp32 ops disabled for all device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # private arrays stay in registers or scratch, never in LDS: the kernels
+    # size their LDS themselves
+    "-mllvm", "-disable-promote-alloca-to-lds",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-warning-option",
 ]
 

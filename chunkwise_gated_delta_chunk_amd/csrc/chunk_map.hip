@@ -5,15 +5,25 @@
 //   A    = I + strict_lower(beta_r (K K^T)_rs exp(G_r - G_s))
 //   M    = lower_incl((Q K^T)_rs exp(G_r - G_s))
 //   T    = A^-1 diag(beta)
-// and writes T with its diagonal removed (the diagonal is beta, which the
-// reduce applies exactly in fp32) and M to the workspace, fp16 for bf16 inputs
-// (fp32 for fp32 inputs).  These are the state-independent "forward intra"
-// pieces of the GDN pipeline in the FLA graph-capture RFC ("[RFC] Add Graph
-// Capture Support for FLA Prefill and Training Paths on Ascend NPUs", section
-// "Step 3"), and the shared-input products K K^T, Q K^T grouped ahead of the
-// inversion as "Empowering Hybrid Attention Models on NPUs" (section 5)
-// suggests, with A^-1 kept apart from W = A^-1 K: the reduce applies T to
-// (V - K H) instead of materialising W.
+// These are the state-independent "forward intra" pieces of the GDN pipeline
+// in the FLA graph-capture RFC ("[RFC] Add Graph Capture Support for FLA
+// Prefill and Training Paths on Ascend NPUs", section "Step 3"), with the
+// shared-input products K K^T, Q K^T grouped ahead of the inversion as
+// "Empowering Hybrid Attention Models on NPUs" (section 5) suggests, and
+// A^-1 kept apart from W = A^-1 K: the reduce applies T to (V - K H) instead
+// of materialising W.
+//
+// Written to the workspace for the reduce, per (slot, head):
+//   Tn  = T with its diagonal (beta) removed -- the reduce applies beta in fp32
+//   M
+//   vec = [exp(G_r) | exp(G_C - G_r) | beta_r | per-key-row state decay]
+// T and M are stored in the workspace element type (fp16 for bf16 inputs,
+// fp32 for fp32 inputs) with their columns in the reduce's chained k order
+// (kpos), ready to be MFMA A operands.
+//
+// A^-1 is formed by 16x16 blocks: the four diagonal blocks by forward
+// substitution (one lane per column), then block row i of column block j as
+// X_ij = -X_ii sum_{k=j}^{i-1} L_ik X_kj on fp32 MFMA, one block per wave.
 //
 // Sentinel slots exit before any pointer arithmetic (RFC, section
 // "Fixed-capacity execution").  Rows >= C of K, Q, beta and g read as zero, so
@@ -23,7 +33,10 @@
 // (K K^T)_rs -> sum_i k_ri k_si exp(G_ri - G_si).  Off-diagonal 16-row blocks
 // (R > S) factor it through the first row b of block R,
 // k_ri exp(G_ri - G_bi) * k_si exp(G_bi - G_si), both factors <= 1 when g <= 0;
-// the four diagonal 16x16 blocks are summed elementwise in fp32.
+// the four diagonal 16x16 blocks are summed elementwise in fp32.  The KDA map
+// also writes the decayed operands the reduce needs, K*exp(G) and Q*exp(G)
+// (key index in chained order) and (K*exp(G_C - G))^T (chunk rows in chained
+// order), and exp(G_C) as the state decay, so the reduce does no gate work.
 #include "la_device.h"
 #include "kernels.h"
 
@@ -31,9 +44,13 @@ namespace la {
 
 namespace {
 
-// (R, S) 16x16 tile pairs of the lower block triangle of a 64x64 matrix
-__constant__ int8_t kTileR[10] = {0, 1, 1, 2, 2, 2, 3, 3, 3, 3};
-__constant__ int8_t kTileS[10] = {0, 0, 1, 0, 1, 2, 0, 1, 2, 3};
+// (R, S) of the p-th 16x16 tile of the lower block triangle of a 64x64 matrix,
+// p = 0..9 in row order: R = 0,1,1,2,2,2,3,3,3,3 and S = 0,0,1,0,1,2,0,1,2,3,
+// packed two bits per entry
+__device__ __forceinline__ int tile_r(int p) { return (0xFFA94 >> (2 * p)) & 3; }
+__device__ __forceinline__ int tile_s(int p) { return (0xE4910 >> (2 * p)) & 3; }
+
+using F32 = Op<float>;
 
 template <bool KDA, typename In, int DK>
 __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
@@ -42,19 +59,26 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   constexpr int LDK = DK + O::PAD;   // K / Q row stride (elements)
   constexpr int LDL = kBT + 4;       // fp32 64x64 stride
   constexpr int KSTEP = 4 * O::KPL;  // k per MFMA
-
-  __shared__ __attribute__((aligned(16))) T sK[kBT * LDK];
-  __shared__ __attribute__((aligned(16))) T sQ[kBT * LDK];
-  __shared__ float sL[kBT * LDL];     // strict lower part of A
-  __shared__ float sX[kBT * LDL];     // A^-1
-  __shared__ float sY[3 * 256];       // block products during the inverse
+  constexpr int KQ_BYTES = 2 * kBT * LDK * (int)sizeof(T);
+  constexpr int LX_BYTES = 2 * kBT * LDL * (int)sizeof(float);
+  constexpr int VECN = 192 + DK;
+  // GDN: K and Q are dead once the products are formed, and A / A^-1 take
+  // their bytes.  KDA keeps both (K and Q are read until M is complete).
+  constexpr int AREA = KDA ? KQ_BYTES : (KQ_BYTES > LX_BYTES ? KQ_BYTES : LX_BYTES);
+  __shared__ __attribute__((aligned(16))) char sArea[AREA];
+  __shared__ __attribute__((aligned(16))) char sLXk[KDA ? LX_BYTES : 16];
+  __shared__ float sY[4][16 * 17];    // per-wave 16x16 scratch
   __shared__ float sB[kBT];
   __shared__ float sg[kBT];
   // KDA: per-channel cumulative gate and the decayed operands of one block row
   __shared__ float sG[KDA ? kBT * DK : 1];
-  __shared__ __attribute__((aligned(16))) T sKr[KDA ? 16 * LDK : 1];  // rows of block R (K)
-  __shared__ __attribute__((aligned(16))) T sQr[KDA ? 16 * LDK : 1];  // rows of block R (Q)
-  __shared__ __attribute__((aligned(16))) T sKs[KDA ? 48 * LDK : 1];  // rows 0..16R-1 (K)
+  __shared__ __attribute__((aligned(16))) T sKr[KDA ? 16 * LDK : 1];
+  __shared__ __attribute__((aligned(16))) T sQr[KDA ? 16 * LDK : 1];
+  __shared__ __attribute__((aligned(16))) T sKs[KDA ? 48 * LDK : 1];
+  T *sK = reinterpret_cast<T *>(sArea);
+  T *sQ = sK + kBT * LDK;
+  float *sL = KDA ? reinterpret_cast<float *>(sLXk) : reinterpret_cast<float *>(sArea);
+  float *sX = sL + kBT * LDL;
 
   const int slot = blockIdx.x;
   const int h = blockIdx.y;
@@ -67,26 +91,71 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   const int C = min(kBT, eos - r0);
   const int H = p.H;
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int lr = lane & 15, lg = lane >> 4;
+  const size_t unit = (size_t)slot * H + h;
+  T *Tws = static_cast<T *>(p.Tn_raw) + unit * (kBT * kBT);
+  T *Mws = static_cast<T *>(p.M_raw) + unit * (kBT * kBT);
+  float *vec = p.vec + unit * VECN;
 
-  // ---- stage K, Q (rows >= C zero), beta, g
+  // ---- stage K, Q (rows >= C zero), beta, g.  All global loads are issued
+  // first (masked, raw bytes) and converted afterwards, so they overlap.
   {
-    constexpr int VEC = 16 / sizeof(In);  // 16-byte global loads
+    constexpr int VEC = 16 / sizeof(In);  // elements per 16-byte load
     constexpr int PER_ROW = DK / VEC;
+    constexpr int NIT = kBT * PER_ROW / kThreads;
+    static_assert(kBT * PER_ROW % kThreads == 0, "staging split");
     const In *q = static_cast<const In *>(p.q);
     const In *k = static_cast<const In *>(p.k);
-    for (int idx = tid; idx < kBT * PER_ROW; idx += kThreads) {
+    uint4 kraw[NIT], qraw[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = tid + it * kThreads;
       const int r = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
-      T kv[VEC], qv[VEC];
+      kraw[it] = uint4{0, 0, 0, 0};
+      qraw[it] = uint4{0, 0, 0, 0};
       if (r < C) {
         const size_t off = ((size_t)(r0 + r) * H + h) * DK + c;
+        kraw[it] = *reinterpret_cast<const uint4 *>(k + off);
+        qraw[it] = *reinterpret_cast<const uint4 *>(q + off);
+      }
+    }
+    float bval = 0.f, gval = 0.f;
+    if (tid < C) {
+      bval = p.beta[(size_t)(r0 + tid) * H + h];
+      if (!KDA) gval = p.g[(size_t)(r0 + tid) * H + h];
+    }
+    constexpr int GIT = KDA ? kBT * DK / 4 / kThreads : 1;  // float4 gate loads per thread
+    float4 graw[GIT];
+    if constexpr (KDA) {
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) {
-          kv[e] = (T)O::load(k + off + e);
-          qv[e] = (T)O::load(q + off + e);
+      for (int it = 0; it < GIT; ++it) {
+        const int idx = tid + it * kThreads;
+        const int r = idx / (DK / 4), c = (idx % (DK / 4)) * 4;
+        graw[it] = float4{0.f, 0.f, 0.f, 0.f};
+        if (r < C) graw[it] = *reinterpret_cast<const float4 *>(p.g + ((size_t)(r0 + r) * H + h) * DK + c);
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int idx = tid + it * kThreads;
+      const int r = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
+      T kv[VEC], qv[VEC];
+      const uint32_t kw[4] = {kraw[it].x, kraw[it].y, kraw[it].z, kraw[it].w};
+      const uint32_t qw[4] = {qraw[it].x, qraw[it].y, qraw[it].z, qraw[it].w};
+      if constexpr (VEC == 8) {  // bf16 -> fp16
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kv[2 * e] = (T)__uint_as_float(kw[e] << 16);
+          kv[2 * e + 1] = (T)__uint_as_float(kw[e] & 0xffff0000u);
+          qv[2 * e] = (T)__uint_as_float(qw[e] << 16);
+          qv[2 * e + 1] = (T)__uint_as_float(qw[e] & 0xffff0000u);
         }
-      } else {
+      } else {  // fp32
 #pragma unroll
-        for (int e = 0; e < VEC; ++e) kv[e] = qv[e] = (T)0.f;
+        for (int e = 0; e < 4; ++e) {
+          kv[e] = (T)__uint_as_float(kw[e]);
+          qv[e] = (T)__uint_as_float(qw[e]);
+        }
       }
 #pragma unroll
       for (int e = 0; e < VEC; ++e) {
@@ -95,28 +164,31 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
       }
     }
     if (tid < kBT) {
-      const bool ok = tid < C;
-      sB[tid] = ok ? p.beta[(size_t)(r0 + tid) * H + h] : 0.f;
-      if (!KDA) sg[tid] = ok ? p.g[(size_t)(r0 + tid) * H + h] : 0.f;
+      sB[tid] = bval;
+      sg[tid] = gval;
     }
     if constexpr (KDA) {
-      // per-channel inclusive cumsum down the rows (sequential per channel)
-      for (int c = tid; c < DK; c += kThreads) {
-        float run = 0.f;
-        for (int r = 0; r < kBT; ++r) {
-          if (r < C) run += p.g[((size_t)(r0 + r) * H + h) * DK + c];
-          sG[r * DK + c] = run;
-        }
+#pragma unroll
+      for (int it = 0; it < GIT; ++it) {
+        const int idx = tid + it * kThreads;
+        *reinterpret_cast<float4 *>(sG + idx * 4) = graw[it];
       }
     }
   }
   __syncthreads();
 
-  // ---- masked products A (strict lower, fp32 in LDS) and M (to workspace)
-  T *Mws = static_cast<T *>(p.M_raw) + ((size_t)slot * H + h) * (kBT * kBT);
-  T *Tws = static_cast<T *>(p.Tn_raw) + ((size_t)slot * H + h) * (kBT * kBT);
+  // M tile (R, S) from an accumulator -> workspace, columns in chained order
+  auto store_m = [&](int R, int S, const f32x4 &c, bool mask) {
+    const int s = 16 * S + lr;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * R + lg * 4 + e;
+      Mws[r * kBT + kpos<O>(s)] = (T)((!mask || s <= r) ? c[e] : 0.f);
+    }
+  };
 
   if constexpr (!KDA) {
+    // ---- masked products: A (strict lower, fp32 -> sL) and M (-> workspace)
     const float G = wave_inclusive_scan(sg[lane]);  // lane r holds G_r
     // 10 lower tiles of K K^T then 10 of Q K^T: 5 per wave, wave w takes w + 4i
     f32x4 a5[5];
@@ -124,39 +196,92 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
     for (int i = 0; i < 5; ++i) {
       const int t = w + 4 * i;
       const int pr = t % 10;
-      const int R = kTileR[pr], S = kTileS[pr];
+      const int R = tile_r(pr), S = tile_s(pr);
       const T *src = t < 10 ? sK : sQ;
       f32x4 c = zero4();
 #pragma unroll
-      for (int k0 = 0; k0 < DK; k0 += KSTEP) {
+      for (int k0 = 0; k0 < DK; k0 += KSTEP)
         c = O::mfma(frag_lds<O>(src, LDK, 16 * R, k0, lane), frag_lds<O>(sK, LDK, 16 * S, k0, lane),
                     c);
-      }
       a5[i] = c;
     }
+    __syncthreads();  // K / Q are dead: their bytes now hold A and A^-1
+    const float GC = __shfl(G, kBT - 1, 64);
 #pragma unroll
     for (int i = 0; i < 5; ++i) {
       const int t = w + 4 * i;
       const int pr = t % 10;
-      const int R = kTileR[pr], S = kTileS[pr];
-      const int s = 16 * S + (lane & 15);
+      const int R = tile_r(pr), S = tile_s(pr);
+      const int s = 16 * S + lr;
       const float Gs = __shfl(G, s, 64);
+      f32x4 v;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int r = 16 * R + (lane >> 4) * 4 + e;
-        const float Gr = __shfl(G, r, 64);
-        if (t < 10) {
-          sL[r * LDL + s] = s < r ? sB[r] * a5[i][e] * __expf(Gr - Gs) : 0.f;
-        } else {
-          Mws[r * kBT + s] = (T)(s <= r ? a5[i][e] * __expf(Gr - Gs) : 0.f);
+        const int r = 16 * R + lg * 4 + e;
+        v[e] = a5[i][e] * __expf(__shfl(G, r, 64) - Gs);
+      }
+      if (t < 10) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * R + lg * 4 + e;
+          sL[r * LDL + s] = s < r ? sB[r] * v[e] : 0.f;
         }
+      } else {
+        store_m(R, S, v, true);
       }
     }
+    if (w == 0) {
+      vec[lane] = __expf(G);
+      vec[64 + lane] = __expf(GC - G);
+      vec[128 + lane] = sB[lane];
+      const float gC = __expf(GC);
+      for (int d = lane; d < DK; d += 64) vec[192 + d] = gC;
+    }
   } else {
-    // KDA off-diagonal blocks: for block row R, reference row b = 16R
+    // per-channel inclusive cumsum: SEG row segments per channel, then the
+    // totals of earlier segments are added
+    {
+      constexpr int SEG = kThreads / DK, RPS = kBT / SEG;
+      const int c = tid % DK, sgi = tid / DK;
+      float run = 0.f;
+      for (int r = sgi * RPS; r < (sgi + 1) * RPS; ++r) {
+        run += sG[r * DK + c];
+        sG[r * DK + c] = run;
+      }
+      __syncthreads();
+      float off = 0.f;
+      for (int s2 = 0; s2 < sgi; ++s2) off += sG[((s2 + 1) * RPS - 1) * DK + c];
+      __syncthreads();
+      if (sgi > 0)
+        for (int r = sgi * RPS; r < (sgi + 1) * RPS; ++r) sG[r * DK + c] += off;
+      __syncthreads();
+    }
+    // decayed operands for the reduce, in chained order
+    {
+      T *Kd = static_cast<T *>(p.Kd_raw) + unit * (kBT * DK);
+      T *Qd = static_cast<T *>(p.Qd_raw) + unit * (kBT * DK);
+      T *Kbt = static_cast<T *>(p.Kbt_raw) + unit * (kBT * DK);
+      for (int idx = tid; idx < kBT * DK; idx += kThreads) {
+        const int r = idx / DK, c = idx % DK;
+        const float f = __expf(sG[r * DK + c]);
+        Kd[r * DK + kpos<O>(c)] = (T)((float)sK[r * LDK + c] * f);
+        Qd[r * DK + kpos<O>(c)] = (T)((float)sQ[r * LDK + c] * f);
+      }
+      for (int idx = tid; idx < kBT * DK; idx += kThreads) {
+        const int c = idx / kBT, r = idx % kBT;
+        const float f = __expf(sG[(kBT - 1) * DK + c] - sG[r * DK + c]);
+        Kbt[c * kBT + kpos<O>(r)] = (T)((float)sK[r * LDK + c] * f);
+      }
+      if (tid < kBT) {
+        vec[tid] = 1.f;
+        vec[64 + tid] = 1.f;
+        vec[128 + tid] = sB[tid];
+      }
+      for (int d = tid; d < DK; d += kThreads) vec[192 + d] = __expf(sG[(kBT - 1) * DK + d]);
+    }
+    // off-diagonal blocks: for block row R, reference row b = 16R
     for (int R = 1; R < 4; ++R) {
       const int b = 16 * R;
-      // r-side rows of block R and s-side rows 0..b-1, decayed through row b
       for (int idx = tid; idx < (16 + b) * DK; idx += kThreads) {
         const int r = idx / DK, c = idx % DK;
         const float Gb = sG[b * DK + c];
@@ -172,8 +297,7 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
         }
       }
       __syncthreads();
-      // tiles (R, S) for S < R: A part and M part -> 2R tiles over 4 waves
-      for (int t = w; t < 2 * R; t += 4) {
+      for (int t = w; t < 2 * R; t += 4) {  // tiles (R, S), S < R: A part then M part
         const int S = t % R;
         const bool isM = t >= R;
         const T *src = isM ? sQr : sKr;
@@ -182,12 +306,15 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
         for (int k0 = 0; k0 < DK; k0 += KSTEP)
           c = O::mfma(frag_lds<O>(src, LDK, 0, k0, lane), frag_lds<O>(sKs, LDK, 16 * S, k0, lane),
                       c);
-        const int s = 16 * S + (lane & 15);
+        if (isM) {
+          store_m(R, S, c, false);
+        } else {
+          const int s = 16 * S + lr;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = b + (lane >> 4) * 4 + e;
-          if (isM) Mws[r * kBT + s] = (T)c[e];
-          else sL[r * LDL + s] = sB[r] * c[e];
+          for (int e = 0; e < 4; ++e) {
+            const int r = b + lg * 4 + e;
+            sL[r * LDL + s] = sB[r] * c[e];
+          }
         }
       }
       __syncthreads();
@@ -205,7 +332,7 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
         }
       }
       sL[r * LDL + s] = s < r ? sB[r] * a : 0.f;
-      Mws[r * kBT + s] = (T)m;
+      Mws[r * kBT + kpos<O>(s)] = (T)m;
     }
   }
   // upper block triangle of M is zero (the reduce reads whole k-steps)
@@ -213,21 +340,29 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
     const int u = idx >> 8;  // (R, S) with S > R
     const int R = u < 3 ? 0 : (u < 5 ? 1 : 2);
     const int S = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
-    Mws[(16 * R + ((idx >> 4) & 15)) * kBT + 16 * S + (idx & 15)] = (T)0.f;
+    Mws[(16 * R + ((idx >> 4) & 15)) * kBT + kpos<O>(16 * S + (idx & 15))] = (T)0.f;
   }
   __syncthreads();
 
-  // ---- X = (I + L)^-1 by blocks: diagonal 16x16 blocks by forward
-  // substitution (one lane per column), then block rows below the diagonal.
+  // ---- X = (I + L)^-1: diagonal blocks by forward substitution, lane = column
   if (w == 0) {
     const int blk = lane >> 4, c = lane & 15;
     const float *Lb = sL + (16 * blk) * LDL + 16 * blk;
     float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+      float lrow[16];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const float4 v = *reinterpret_cast<const float4 *>(Lb + r * LDL + 4 * q4);
+        lrow[4 * q4] = v.x;
+        lrow[4 * q4 + 1] = v.y;
+        lrow[4 * q4 + 2] = v.z;
+        lrow[4 * q4 + 3] = v.w;
+      }
       float acc = (r == c) ? 1.f : 0.f;
 #pragma unroll
-      for (int s = 0; s < r; ++s) acc -= Lb[r * LDL + s] * x[s];
+      for (int s = 0; s < r; ++s) acc -= lrow[s] * x[s];
       x[r] = acc;
     }
     float *Xb = sX + (16 * blk) * LDL + 16 * blk;
@@ -235,30 +370,50 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
     for (int r = 0; r < 16; ++r) Xb[r * LDL + c] = x[r];
   }
   __syncthreads();
-  // X_ij = -X_ii * sum_{s in [16j, 16i)} L[16i + r][s] X[s][16j + c], by i - j
+  // block rows below the diagonal: X_ij = -X_ii sum_{k=j}^{i-1} L_ik X_kj, by i - j
 #pragma unroll
   for (int dist = 1; dist < 4; ++dist) {
-    const int nblk = 4 - dist;  // pairs (j + dist, j), j = 0..nblk-1
-    for (int idx = tid; idx < nblk * 256; idx += kThreads) {
-      const int j = idx >> 8, i = j + dist, r = (idx >> 4) & 15, c = idx & 15;
-      float acc = 0.f;
-      for (int s = 16 * j; s < 16 * i; ++s) acc += sL[(16 * i + r) * LDL + s] * sX[s * LDL + 16 * j + c];
-      sY[idx] = acc;
-    }
-    __syncthreads();
-    for (int idx = tid; idx < nblk * 256; idx += kThreads) {
-      const int j = idx >> 8, i = j + dist, r = (idx >> 4) & 15, c = idx & 15;
-      float acc = 0.f;
+    const int j = w, i = w + dist;
+    if (i < 4) {
+      f32x4 y = zero4();
+      for (int kb = j; kb < i; ++kb) {
 #pragma unroll
-      for (int s = 0; s < 16; ++s) acc += sX[(16 * i + r) * LDL + 16 * i + s] * sY[j * 256 + s * 16 + c];
-      sX[(16 * i + r) * LDL + 16 * j + c] = -acc;
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+          const float a = sL[(16 * i + lr) * LDL + 16 * kb + k0 + lg];
+          const float bb = sX[(16 * kb + k0 + lg) * LDL + 16 * j + lr];
+          y = F32::mfma(a, bb, y);
+        }
+      }
+      float *Y = sY[w];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Y[(lg * 4 + e) * 17 + lr] = y[e];
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      f32x4 x = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < 16; k0 += 4) {
+        const float a = sX[(16 * i + lr) * LDL + 16 * i + k0 + lg];
+        const float bb = Y[(k0 + lg) * 17 + lr];
+        x = F32::mfma(a, bb, x);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sX[(16 * i + lg * 4 + e) * LDL + 16 * j + lr] = -x[e];
     }
     __syncthreads();
   }
-  // ---- T = X diag(beta), strict lower part only
-  for (int idx = tid; idx < kBT * kBT; idx += kThreads) {
-    const int r = idx >> 6, s = idx & 63;
-    Tws[idx] = (T)(s < r ? sX[r * LDL + s] * sB[s] : 0.f);
+  // ---- Tn = X diag(beta), strict lower part, 16-byte stores in chained order
+  {
+    constexpr int CH = 16 / sizeof(T);  // elements per 16-byte store
+    for (int idx = tid; idx < kBT * kBT / CH; idx += kThreads) {
+      const int r = idx / (kBT / CH), p0 = (idx % (kBT / CH)) * CH;
+      T v[CH];
+#pragma unroll
+      for (int e = 0; e < CH; ++e) {
+        const int s = kidx<O>(p0 + e);
+        v[e] = (T)(s < r ? sX[r * LDL + s] * sB[s] : 0.f);
+      }
+      *reinterpret_cast<uint4 *>(Tws + r * kBT + p0) = *reinterpret_cast<const uint4 *>(v);
+    }
   }
 }
 

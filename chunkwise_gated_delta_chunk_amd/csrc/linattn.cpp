@@ -25,9 +25,10 @@ int check_shape(const la_chunk_fwd_args *a) {
   if (a->d_k != a->d_v) return LA_ERR_UNSUPPORTED;
   if (a->qkv_dtype == LA_BF16 && a->d_k != 64 && a->d_k != 128) return LA_ERR_UNSUPPORTED;
   if (a->qkv_dtype == LA_F32 && a->d_k != 64) return LA_ERR_UNSUPPORTED;
+  // dv_split: 0 (auto) or a power of two leaving 32, 64 or 128 columns
   const int s = a->dv_split;
-  if (s != 0 && s != 1 && s != 2 && s != 4 && s != 8) return LA_ERR_UNSUPPORTED;
-  if (s != 0 && a->d_v / s < 16) return LA_ERR_UNSUPPORTED;
+  if (s != 0 && s != 1 && s != 2 && s != 4) return LA_ERR_UNSUPPORTED;
+  if (s != 0 && a->d_v / s < 32) return LA_ERR_UNSUPPORTED;
   // every (token, head) index and (slot, head) workspace index stays in size_t
   const int64_t nt = la_nt_max(a->T_max, a->N_max, a->BT);
   if (nt < 1 || nt > 0x7fffffff) return LA_ERR_SHAPE;
@@ -37,20 +38,41 @@ int check_shape(const la_chunk_fwd_args *a) {
 
 int split_for(const la_chunk_fwd_args *a) {
   if (a->dv_split) return a->dv_split;
-  // enough workgroups to cover the CUs about twice over, down to 16 columns
-  const int64_t units = (int64_t)a->N_max * a->H;
-  int s = 1;
-  while (units * s < 512 && a->d_v / (2 * s) >= 16 && s < 8) s *= 2;
-  return s;
+  // four waves of 16 state columns per workgroup
+  return a->d_v / 64;
 }
 
 size_t elem_bytes(const la_chunk_fwd_args *a) { return a->qkv_dtype == LA_BF16 ? 2 : 4; }
 
-size_t ws_bytes(const la_chunk_fwd_args *a) {
-  const size_t per = (size_t)a->BT * a->BT * elem_bytes(a);  // one BT x BT matrix
-  const size_t half = (size_t)la_nt_max(a->T_max, a->N_max, a->BT) * a->H * per;
-  return 2 * half;  // Tn then M
+// Workspace layout, per chunk slot and head (element size e = 2 for bf16
+// inputs, 4 for fp32), each region contiguous over (slot, head):
+// Tn [BT][BT], M [BT][BT], vec [192 + d_k] fp32; KDA adds Kd [BT][d_k],
+// Qd [BT][d_k] and Kbt [d_k][BT].
+struct WsLayout {
+  size_t tn, m, vec, kd, qd, kbt, total;
+};
+
+size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+WsLayout ws_layout(const la_chunk_fwd_args *a, bool kda) {
+  const size_t cells = (size_t)la_nt_max(a->T_max, a->N_max, a->BT) * a->H;
+  const size_t e = elem_bytes(a);
+  WsLayout L{};
+  L.tn = 0;
+  L.m = round256(cells * a->BT * a->BT * e);
+  L.vec = L.m + round256(cells * a->BT * a->BT * e);
+  L.total = L.vec + round256(cells * (size_t)(192 + a->d_k) * sizeof(float));
+  if (kda) {
+    const size_t op = round256(cells * a->BT * a->d_k * e);
+    L.kd = L.total;
+    L.qd = L.kd + op;
+    L.kbt = L.qd + op;
+    L.total = L.kbt + op;
+  }
+  return L;
 }
+
+size_t ws_bytes(const la_chunk_fwd_args *a, bool kda) { return ws_layout(a, kda).total; }
 
 int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
   if (!a) return LA_ERR_NULL;
@@ -61,7 +83,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
       !a->chunk_offsets || !a->o)
     return LA_ERR_NULL;
   if (!a->workspace) return LA_ERR_WORKSPACE;
-  if (a->workspace_bytes < ws_bytes(a)) return LA_ERR_WORKSPACE;
+  if (a->workspace_bytes < ws_bytes(a, kda)) return LA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(a->workspace) % 256 != 0) return LA_ERR_WORKSPACE;
   if (a->h0 && a->ht && a->h0 != a->ht) {
     const size_t sb = (size_t)a->N_max * a->H * a->d_k * a->d_v * sizeof(float);
@@ -72,7 +94,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
   if (mis % 16 != 0) return LA_ERR_SHAPE;
 
   const bool bf = a->qkv_dtype == LA_BF16;
-  const size_t half = ws_bytes(a) / 2;
+  const WsLayout L = ws_layout(a, kda);
   char *ws = static_cast<char *>(a->workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (stages & LA_STAGE_MAP) {
@@ -85,8 +107,14 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     mp.chunk_indices = a->chunk_indices;
     mp.H = a->H;
     mp.NT_max = (int)la_nt_max(a->T_max, a->N_max, a->BT);
-    mp.Tn_raw = ws;
-    mp.M_raw = ws + half;
+    mp.Tn_raw = ws + L.tn;
+    mp.M_raw = ws + L.m;
+    mp.vec = reinterpret_cast<float *>(ws + L.vec);
+    if (kda) {
+      mp.Kd_raw = ws + L.kd;
+      mp.Qd_raw = ws + L.qd;
+      mp.Kbt_raw = ws + L.kbt;
+    }
     if (la::launch_chunk_map(mp, kda, bf, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
   }
   if (stages & LA_STAGE_REDUCE) {
@@ -94,15 +122,19 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     rp.q = a->q;
     rp.k = a->k;
     rp.v = a->v;
-    rp.g = a->g;
-    rp.beta = a->beta;
     rp.cu_seqlens = a->cu_seqlens;
     rp.chunk_offsets = a->chunk_offsets;
     rp.h0 = a->h0;
     rp.o = a->o;
     rp.ht = a->ht;
-    rp.Tn_raw = ws;
-    rp.M_raw = ws + half;
+    rp.Tn_raw = ws + L.tn;
+    rp.M_raw = ws + L.m;
+    rp.vec = reinterpret_cast<const float *>(ws + L.vec);
+    if (kda) {
+      rp.Kd_raw = ws + L.kd;
+      rp.Qd_raw = ws + L.qd;
+      rp.Kbt_raw = ws + L.kbt;
+    }
     rp.H = a->H;
     rp.N_max = a->N_max;
     rp.S = split_for(a);
@@ -138,9 +170,8 @@ int build_chunk_meta(const int32_t *cu_seqlens, int32_t N_max, int32_t T_max, in
 }
 
 size_t la_chunk_fwd_workspace_bytes(const la_chunk_fwd_args *a, int is_kda) {
-  (void)is_kda;  // GDN and KDA keep the same per-chunk matrices
   if (!a || check_shape(a) != LA_OK) return 0;
-  return ws_bytes(a);
+  return ws_bytes(a, is_kda != 0);
 }
 
 int gdn_chunk_fwd(const la_chunk_fwd_args *a, void *stream) {

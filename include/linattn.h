@@ -103,7 +103,7 @@ typedef struct {
     int32_t BT;                /* chunk size: 64                                 */
     int32_t qkv_dtype;         /* LA_BF16 or LA_F32: dtype of q, k, v            */
     int32_t dv_split;          /* state column slices per (seq, head): 0 = auto, */
-                               /* else 1, 2, 4 or 8 (d_v / dv_split >= 16)       */
+                               /* else 1, 2 or 4 with d_v / dv_split >= 32       */
     float scale;               /* o = scale * S q                                */
     const void *q, *k, *v;     /* [T_max][H][d_k] / [T_max][H][d_v], qkv_dtype   */
     const float *g;            /* log-decay: GDN [T_max][H]; KDA [T_max][H][d_k] */
@@ -120,11 +120,21 @@ typedef struct {
 
 /*
  * Workspace the forward needs for this shape (only T_max, N_max, H, d_k, d_v,
- * BT and qkv_dtype are read); 0 if the shape is invalid.  The workspace holds,
- * per chunk slot and head, the chunk-local matrices of the map stage
- * (T = A^-1 diag(beta) with its diagonal removed, and the masked decayed
- * Q K^T), each BT x BT in fp16 (bf16 inputs) or fp32 (fp32 inputs); its
- * content between calls is unspecified.
+ * BT and qkv_dtype are read); 0 if the shape is invalid.  The workspace holds
+ * the map stage's results for the reduce.  With e = 2 (bf16 inputs: fp16
+ * values) or 4 (fp32 inputs) and cells = NT_max * H, in this order, each
+ * region indexed [slot][head] and starting on a 256-byte boundary:
+ *   Tn  cells x [BT][BT]  T = A^-1 diag(beta) with its diagonal removed
+ *   M   cells x [BT][BT]  masked decayed Q K^T (lower triangle incl. diagonal)
+ *   vec cells x [192 + d_k] fp32: exp(G_r), exp(G_C - G_r), beta_r (BT each),
+ *                         then the state decay of each key row
+ * and for KDA also
+ *   Kd  cells x [BT][d_k] K * exp(G);   Qd cells x [BT][d_k] Q * exp(G)
+ *   Kbt cells x [d_k][BT] (K * exp(G_C - G))^T
+ * where G is the chunk-local cumulative gate and G_C its last row.  For e = 2
+ * the column index of each row is stored permuted inside every 32-column
+ * block (the MFMA operand order of the reduce).  Content between calls is
+ * unspecified.
  */
 size_t la_chunk_fwd_workspace_bytes(const la_chunk_fwd_args *shape, int is_kda);
 

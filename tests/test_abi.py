@@ -71,7 +71,8 @@ BAD = [
     ("d_k != d_v", dict(d_v=128), -4),
     ("fp32 d 128", dict(qkv_dtype=1, d_k=128, d_v=128), -4),
     ("dv_split 3", dict(dv_split=3), -4),
-    ("dv_split too fine", dict(dv_split=8), -4),
+    ("dv_split 8", dict(dv_split=8), -4),
+    ("dv_split too fine", dict(dv_split=4), -4),
     ("no workspace", dict(workspace=None), -5),
     ("workspace small", dict(workspace_bytes=100), -5),
     ("workspace misaligned", dict(workspace=0x100010), -5),
@@ -113,12 +114,14 @@ def test_workspace_size_and_split():
     for (T, N, H, d, dt, esz) in [(8192, 8, 16, 128, torch.bfloat16, 2),
                                   (256, 1, 2, 64, torch.float32, 4),
                                   (16384, 64, 32, 128, torch.bfloat16, 2)]:
-        want = 2 * meta_ref.nt_max(T, N, 64) * H * 64 * 64 * esz
+        cells = meta_ref.nt_max(T, N, 64) * H
+        r256 = lambda x: (x + 255) // 256 * 256
+        want = 2 * r256(cells * 64 * 64 * esz) + r256(cells * (192 + d) * 4)
         assert la.workspace_bytes(T, N, H, d, d, dt) == want
-        assert la.workspace_bytes(T, N, H, d, d, dt, kda=True) == want
+        want_kda = want + 3 * r256(cells * 64 * d * esz)
+        assert la.workspace_bytes(T, N, H, d, d, dt, kda=True) == want_kda
     assert la.workspace_bytes(0, 1, 1, 64, 64, torch.bfloat16) == 0
-    assert la.dv_split_for(8192, 8, 16, 128, 128, torch.bfloat16) == 4
-    assert la.dv_split_for(4096, 1, 16, 128, 128, torch.bfloat16) == 8
-    assert la.dv_split_for(16384, 64, 32, 128, 128, torch.bfloat16) == 1
-    assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32) == 4
+    assert la.dv_split_for(8192, 8, 16, 128, 128, torch.bfloat16) == 2
+    assert la.dv_split_for(16384, 64, 32, 128, 128, torch.bfloat16) == 2
+    assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32) == 1
     assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32, dv_split=2) == 2

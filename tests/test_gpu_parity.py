@@ -80,8 +80,8 @@ SMALL_CU = [0, 1, 64, 64, 200, 333, 460]   # one-token, exact chunk, empty, tail
 @pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("split", [1, 2, 4])
 def test_small_bf16(kda, d, split):
-    if d // split < 16:
-        pytest.skip("slice narrower than 16")
+    if d // split < 32:
+        pytest.skip("slice narrower than 32 columns")
     inp = make_inputs(SMALL_CU[-1], 3, d, d, kda=kda, dtype="bf16", seed=20 + d + split,
                       cu_seqlens=SMALL_CU, h0_std=0.1)
     o, ht, _ = run_gpu(inp, dv_split=split)
@@ -95,7 +95,7 @@ def test_small_bf16(kda, d, split):
 def test_small_fp32(kda):
     inp = make_inputs(SMALL_CU[-1], 2, 64, 64, kda=kda, dtype="f32", seed=31,
                       cu_seqlens=SMALL_CU, h0_std=0.1)
-    for split in (1, 4):
+    for split in (1, 2):
         o, ht, _ = run_gpu(inp, dv_split=split, scale=0.5)
         o_ref, ht_ref = run_oracle(inp, scale=0.5)
         eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref)
@@ -104,33 +104,79 @@ def test_small_fp32(kda):
 
 
 # ---------------------------------------------------------- map stage ---
+def kpos(k):
+    """Stored position of logical column k in fp16 workspace rows: the MFMA
+    operand order of the reduce, a permutation inside each 32-column block."""
+    return (k & ~31) + 8 * ((k & 15) >> 2) + (k & 3) + 4 * ((k & 31) >> 4)
+
+
+def r256(x):
+    return (x + 255) // 256 * 256
+
+
 @pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
 def test_map_stage_matrices(kda):
-    """T (diagonal removed) and M in the workspace against the chunkwise reference."""
+    """Map-stage workspace against the chunkwise reference: T without its
+    diagonal, M, the row vectors and (KDA) the decayed operands."""
     cu = [0, 64, 100, 230]
-    inp = make_inputs(230, 2, 128, 128, kda=kda, dtype="bf16", seed=41, cu_seqlens=cu)
-    d = to_dev(inp)
-    ci, co, _ = la.build_chunk_meta(d["cu_seqlens"], 230)
-    nbytes = la.workspace_bytes(230, 3, 2, 128, 128, torch.bfloat16, kda)
+    d = 128
+    inp = make_inputs(230, 2, d, d, kda=kda, dtype="bf16", seed=41, cu_seqlens=cu)
+    dv = to_dev(inp)
+    ci, co, _ = la.build_chunk_meta(dv["cu_seqlens"], 230)
+    nbytes = la.workspace_bytes(230, 3, 2, d, d, torch.bfloat16, kda)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
-    la.chunk_fwd_stages(kda, la.STAGE_MAP, d["q"], d["k"], d["v"], d["g"], d["beta"],
-                        d["cu_seqlens"], ci, co, workspace=ws)
+    la.chunk_fwd_stages(kda, la.STAGE_MAP, dv["q"], dv["k"], dv["v"], dv["g"], dv["beta"],
+                        dv["cu_seqlens"], ci, co, workspace=ws)
     torch.cuda.synchronize()
     NT = la.nt_max(230, 3)
-    half = ws[: nbytes // 2].view(torch.float16).view(NT, 2, 64, 64).float().cpu().numpy()
-    mm = ws[nbytes // 2:].view(torch.float16).view(NT, 2, 64, 64).float().cpu().numpy()
+    cells = NT * 2
+    mat = cells * 64 * 64 * 2
+    off_m, off_v = r256(mat), 2 * r256(mat)
+    vecn = 192 + d
+    off_kd = off_v + r256(cells * vecn * 4)
+    op = cells * 64 * d * 2
+    cols64 = [kpos(k) for k in range(64)]
+    colsd = [kpos(k) for k in range(d)]
+    tn = ws[:mat].view(torch.float16).view(NT, 2, 64, 64).float().cpu().numpy()[..., cols64]
+    mm = ws[off_m:off_m + mat].view(torch.float16).view(NT, 2, 64, 64).float().cpu().numpy()[..., cols64]
+    vec = ws[off_v:off_v + cells * vecn * 4].view(torch.float32).view(NT, 2, vecn).cpu().numpy()
+    if kda:
+        kd = ws[off_kd:off_kd + op].view(torch.float16).view(NT, 2, 64, d).float().cpu().numpy()[..., colsd]
+        qd = ws[off_kd + r256(op):off_kd + r256(op) + op].view(torch.float16).view(NT, 2, 64, d)
+        qd = qd.float().cpu().numpy()[..., colsd]
+        o3 = off_kd + 2 * r256(op)
+        kbt = ws[o3:o3 + op].view(torch.float16).view(NT, 2, d, 64).float().cpu().numpy()[..., cols64]
     _, _, inter = chunkwise_ref.chunk_forward(inp["q"], inp["k"], inp["v"], inp["g"],
                                               inp["beta"], cu, None, kda=kda, keep=True)
-    for (slot, h), it in inter.items():
-        C = it["T"].shape[0]
-        Tref = it["T"] - np.diag(np.diag(it["T"]))
-        et = rel_err(half[slot, h, :C, :C], Tref)
-        em = rel_err(mm[slot, h, :C, :C], it["M"])
-        assert et < 2e-3 and em < 2e-3, (slot, h, et, em)
-        # tail rows/columns and the upper triangle are exactly zero
-        assert not half[slot, h, C:, :].any() and not half[slot, h, :, C:].any()
-        assert not np.triu(half[slot, h], 0).any()
-        assert not np.triu(mm[slot, h], 1).any()
+    slot = 0
+    for n in range(3):
+        for c0 in range(cu[n], cu[n + 1], 64):
+            rows = slice(c0, min(c0 + 64, cu[n + 1]))
+            C = rows.stop - rows.start
+            for h in range(2):
+                it = inter[(slot, h)]
+                Tref = it["T"] - np.diag(np.diag(it["T"]))
+                assert rel_err(tn[slot, h, :C, :C], Tref) < 2e-3, (slot, h)
+                assert rel_err(mm[slot, h, :C, :C], it["M"]) < 2e-3, (slot, h)
+                # tail rows/columns and the upper triangle are exactly zero
+                assert not tn[slot, h, C:, :].any() and not tn[slot, h, :, C:].any()
+                assert not np.triu(tn[slot, h], 0).any()
+                assert not np.triu(mm[slot, h], 1).any()
+                G = it["G"]
+                Gl = G[:, 0] if G.ndim == 2 else G
+                assert rel_err(vec[slot, h, 128:128 + C], inp["beta"][rows, h]) == 0.0
+                if not kda:
+                    assert rel_err(vec[slot, h, :C], np.exp(G)) < 1e-5
+                    assert rel_err(vec[slot, h, 64:64 + C], np.exp(G[-1] - G)) < 1e-5
+                    assert rel_err(vec[slot, h, 192:192 + d], np.full(d, np.exp(G[-1]))) < 1e-5
+                else:
+                    K, Q = inp["k"][rows, h], inp["q"][rows, h]
+                    assert rel_err(kd[slot, h, :C], K * np.exp(G)) < 1e-3
+                    assert rel_err(qd[slot, h, :C], Q * np.exp(G)) < 1e-3
+                    assert rel_err(kbt[slot, h, :, :C], (K * np.exp(G[-1] - G)).T) < 1e-3
+                    assert rel_err(vec[slot, h, 192:192 + d], np.exp(G[-1])) < 1e-5
+                    assert not kd[slot, h, C:].any() and not kbt[slot, h, :, C:].any()
+            slot += 1
 
 
 # --------------------------------------------------- workloads at size ---
