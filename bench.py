@@ -55,22 +55,29 @@ def kernel_source_hash(name):
 
 
 def alg_bytes(inp, kind):
-    """Algorithmic HBM bytes of one launch ('Measurement')."""
+    """Algorithmic HBM bytes of one launch.
+
+    "op": the whole forward, T*H*[(2 d_k + d_v) s_qkv + s_g + 4 + 4 d_v] plus
+    4 d_k d_v per (non-empty sequence, head) for each of h0 / ht.
+    The kernels split these bytes by who has to touch the operation's own
+    inputs and outputs: the map reads q, k (GDN: only to form its chunk
+    matrices), g and beta; the reduce reads q, k (GDN), v and h0 and writes o
+    and ht.  Intermediates handed from map to reduce through the workspace
+    are implementation overhead and are not counted."""
     T = int(inp["cu_seqlens"][-1])
     H, dk, dv = inp["H"], inp["dk"], inp["dv"]
     s_qkv = 2 if inp["dtype"] == "bf16" else 4
     s_g = 4 * dk if inp["kda"] else 4
     lens = np.diff(inp["cu_seqlens"].astype(np.int64))
     nonempty = int((lens > 0).sum())
-    chunks = int((-(-lens // 64)).sum())
     state = nonempty * H * dk * dv * 4 * ((inp["h0"] is not None) + 1)
-    mats = chunks * H * 2 * 64 * 64 * s_qkv          # Tn and M, one write + one read
     if kind == "op":
         return T * H * ((2 * dk + dv) * s_qkv + s_g + 4 + 4 * dv) + state
     if kind == "map":
-        return T * H * (2 * dk * s_qkv + s_g + 4) + mats
+        return T * H * (2 * dk * s_qkv + s_g + 4)
     if kind == "reduce":
-        return T * H * ((2 * dk + dv) * s_qkv + s_g + 4 + 4 * dv) + mats + state
+        qk = 0 if inp["kda"] else 2 * dk * s_qkv
+        return T * H * (qk + dv * s_qkv + 4 * dv) + state
     raise ValueError(kind)
 
 
