@@ -13,13 +13,18 @@
 // A^-1 kept apart from W = A^-1 K: the reduce applies T to (V - K H) instead
 // of materialising W.
 //
-// Written to the workspace for the reduce, per (slot, head):
+// Written to the workspace for the reduce, per (slot, head), as one image
+// (image_layout in la_device.h: swizzled 16-byte pieces, ready to be copied
+// into LDS verbatim):
+//   K, Q  in the operand element type, key index in chained order
 //   Tn  = T with its diagonal (beta) removed -- the reduce applies beta in fp32
 //   M
 //   vec = [exp(G_r) | exp(G_C - G_r) | beta_r | per-key-row state decay]
-// T and M are stored in the workspace element type (fp16 for bf16 inputs,
-// fp32 for fp32 inputs) with their columns in the reduce's chained k order
-// (kpos), ready to be MFMA A operands.
+// The element type is fp16 for bf16 inputs (bf16 values are exact in fp16
+// inside its normal range) and fp32 for fp32 inputs; matrices have their
+// columns in the reduce's chained k order (kpos), ready to be MFMA A
+// operands.  fp32 GDN also writes K^T (chunk rows chained); fp16 GDN does not
+// need it, its reduce reads K^T from K with transposing LDS reads.
 //
 // A^-1 is formed by 16x16 blocks: the four diagonal blocks by forward
 // substitution (one lane per column), then block row i of column block j as
@@ -34,9 +39,9 @@
 // (R > S) factor it through the first row b of block R,
 // k_ri exp(G_ri - G_bi) * k_si exp(G_bi - G_si), both factors <= 1 when g <= 0;
 // the four diagonal 16x16 blocks are summed elementwise in fp32.  The KDA map
-// also writes the decayed operands the reduce needs, K*exp(G) and Q*exp(G)
-// (key index in chained order) and (K*exp(G_C - G))^T (chunk rows in chained
-// order), and exp(G_C) as the state decay, so the reduce does no gate work.
+// writes the decayed operands in place of K and Q, K*exp(G) and Q*exp(G), and
+// (K*exp(G_C - G))^T (chunk rows in chained order), and exp(G_C) as the state
+// decay, so the reduce does no gate work.
 #include "la_device.h"
 #include "kernels.h"
 
@@ -61,7 +66,6 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   constexpr int KSTEP = 4 * O::KPL;  // k per MFMA
   constexpr int KQ_BYTES = 2 * kBT * LDK * (int)sizeof(T);
   constexpr int LX_BYTES = 2 * kBT * LDL * (int)sizeof(float);
-  constexpr int VECN = 192 + DK;
   // GDN: K and Q are dead once the products are formed, and A / A^-1 take
   // their bytes.  KDA keeps both (K and Q are read until M is complete).
   constexpr int AREA = KDA ? KQ_BYTES : (KQ_BYTES > LX_BYTES ? KQ_BYTES : LX_BYTES);
@@ -75,6 +79,8 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   __shared__ __attribute__((aligned(16))) T sKr[KDA ? 16 * LDK : 1];
   __shared__ __attribute__((aligned(16))) T sQr[KDA ? 16 * LDK : 1];
   __shared__ __attribute__((aligned(16))) T sKs[KDA ? 48 * LDK : 1];
+  constexpr int LDM = kBT + O::PAD;  // M, natural column order, before the write-out
+  __shared__ __attribute__((aligned(16))) T sMt[kBT * LDM];
   T *sK = reinterpret_cast<T *>(sArea);
   T *sQ = sK + kBT * LDK;
   float *sL = KDA ? reinterpret_cast<float *>(sLXk) : reinterpret_cast<float *>(sArea);
@@ -92,31 +98,49 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   const int H = p.H;
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
+  constexpr int E = (int)sizeof(T);
+  constexpr ImageLayout I = image_layout(KDA, E, DK);
+  constexpr int PK = DK * E / 16, PT = kBT * E / 16;  // 16-byte pieces per row
+  constexpr int CH = 16 / E;                          // elements per piece
   const size_t unit = (size_t)slot * H + h;
-  T *Tws = static_cast<T *>(p.Tn_raw) + unit * (kBT * kBT);
-  T *Mws = static_cast<T *>(p.M_raw) + unit * (kBT * kBT);
-  float *vec = p.vec + unit * VECN;
+  char *img = static_cast<char *>(p.img) + unit * I.BYTES;
+  float *vec = reinterpret_cast<float *>(img + I.VEC);
+  // 16 bytes of v[0..CH) -> piece `piece` of row `row` of an image tile
+  auto put = [&](int region, int P, int row, int piece, const T *v) {
+    const int off = P == 16 ? tile_off<16>(row, piece) : P == 8 ? tile_off<8>(row, piece)
+                                                                 : row * 16 * P + 16 * piece;
+    *reinterpret_cast<u32x4 *>(img + region + off) = *reinterpret_cast<const u32x4 *>(v);
+  };
 
   // ---- stage K, Q (rows >= C zero), beta, g.  All global loads are issued
   // first (masked, raw bytes) and converted afterwards, so they overlap.
+  // bf16: a unit is row r, 32-element block b, half g2: input pieces
+  // 4b + g2 and 4b + 2 + g2 (8 elements each), which hold exactly the chained
+  // pieces 4b + 2 g2 (their low halves) and 4b + 2 g2 + 1 (their high halves).
+  // fp32: a unit is one 4-element piece (the chained order is the natural one).
   {
-    constexpr int VEC = 16 / sizeof(In);  // elements per 16-byte load
-    constexpr int PER_ROW = DK / VEC;
-    constexpr int NIT = kBT * PER_ROW / kThreads;
-    static_assert(kBT * PER_ROW % kThreads == 0, "staging split");
+    constexpr int VEC = 16 / sizeof(In);              // elements per 16-byte load
+    constexpr int UPR = VEC == 8 ? DK / 16 : DK / 4;  // units per row
+    constexpr int NU = kBT * UPR / kThreads;
+    constexpr int NP = VEC == 8 ? 2 : 1;              // input pieces per unit
+    static_assert(kBT * UPR % kThreads == 0, "staging split");
     const In *q = static_cast<const In *>(p.q);
     const In *k = static_cast<const In *>(p.k);
-    uint4 kraw[NIT], qraw[NIT];
+    u32x4 kraw[NU][NP], qraw[NU][NP];
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int idx = tid + it * kThreads;
-      const int r = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
-      kraw[it] = uint4{0, 0, 0, 0};
-      qraw[it] = uint4{0, 0, 0, 0};
-      if (r < C) {
-        const size_t off = ((size_t)(r0 + r) * H + h) * DK + c;
-        kraw[it] = *reinterpret_cast<const uint4 *>(k + off);
-        qraw[it] = *reinterpret_cast<const uint4 *>(q + off);
+    for (int it = 0; it < NU; ++it) {
+      const int u = tid + it * kThreads;
+      const int r = u / UPR, pi = u % UPR;
+#pragma unroll
+      for (int j = 0; j < NP; ++j) {
+        const int piece = VEC == 8 ? 4 * (pi >> 1) + (pi & 1) + 2 * j : pi;
+        kraw[it][j] = u32x4{0, 0, 0, 0};
+        qraw[it][j] = u32x4{0, 0, 0, 0};
+        if (r < C) {
+          const size_t off = ((size_t)(r0 + r) * H + h) * DK + piece * VEC;
+          kraw[it][j] = *reinterpret_cast<const u32x4 *>(k + off);
+          qraw[it][j] = *reinterpret_cast<const u32x4 *>(q + off);
+        }
       }
     }
     float bval = 0.f, gval = 0.f;
@@ -136,31 +160,57 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
       }
     }
 #pragma unroll
-    for (int it = 0; it < NIT; ++it) {
-      const int idx = tid + it * kThreads;
-      const int r = idx / PER_ROW, c = (idx % PER_ROW) * VEC;
-      T kv[VEC], qv[VEC];
-      const uint32_t kw[4] = {kraw[it].x, kraw[it].y, kraw[it].z, kraw[it].w};
-      const uint32_t qw[4] = {qraw[it].x, qraw[it].y, qraw[it].z, qraw[it].w};
-      if constexpr (VEC == 8) {  // bf16 -> fp16
+    for (int it = 0; it < NU; ++it) {
+      const int u = tid + it * kThreads;
+      const int r = u / UPR, pi = u % UPR;
+      T kv[NP][VEC], qv[NP][VEC];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kv[2 * e] = (T)__uint_as_float(kw[e] << 16);
-          kv[2 * e + 1] = (T)__uint_as_float(kw[e] & 0xffff0000u);
-          qv[2 * e] = (T)__uint_as_float(qw[e] << 16);
-          qv[2 * e + 1] = (T)__uint_as_float(qw[e] & 0xffff0000u);
-        }
-      } else {  // fp32
+      for (int j = 0; j < NP; ++j) {
+        if constexpr (VEC == 8) {  // bf16 -> fp16
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kv[e] = (T)__uint_as_float(kw[e]);
-          qv[e] = (T)__uint_as_float(qw[e]);
+          for (int e = 0; e < 4; ++e) {
+            kv[j][2 * e] = (T)__uint_as_float(kraw[it][j][e] << 16);
+            kv[j][2 * e + 1] = (T)__uint_as_float(kraw[it][j][e] & 0xffff0000u);
+            qv[j][2 * e] = (T)__uint_as_float(qraw[it][j][e] << 16);
+            qv[j][2 * e + 1] = (T)__uint_as_float(qraw[it][j][e] & 0xffff0000u);
+          }
+        } else {  // fp32
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kv[j][e] = (T)__uint_as_float(kraw[it][j][e]);
+            qv[j][e] = (T)__uint_as_float(qraw[it][j][e]);
+          }
         }
+        const int piece = VEC == 8 ? 4 * (pi >> 1) + (pi & 1) + 2 * j : pi;
+        *reinterpret_cast<u32x4 *>(sK + r * LDK + piece * VEC) = *reinterpret_cast<const u32x4 *>(kv[j]);
+        *reinterpret_cast<u32x4 *>(sQ + r * LDK + piece * VEC) = *reinterpret_cast<const u32x4 *>(qv[j]);
       }
+      if constexpr (!KDA) {  // the reduce's K and Q operands, chained order
+        if constexpr (VEC == 8) {
+          const int cp = 4 * (pi >> 1) + 2 * (pi & 1);
+          T lo[8], hi[8];
 #pragma unroll
-      for (int e = 0; e < VEC; ++e) {
-        sK[r * LDK + c + e] = kv[e];
-        sQ[r * LDK + c + e] = qv[e];
+          for (int e = 0; e < 4; ++e) {
+            lo[e] = kv[0][e];
+            lo[4 + e] = kv[1][e];
+            hi[e] = kv[0][4 + e];
+            hi[4 + e] = kv[1][4 + e];
+          }
+          put(I.K, PK, r, cp, lo);
+          put(I.K, PK, r, cp + 1, hi);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            lo[e] = qv[0][e];
+            lo[4 + e] = qv[1][e];
+            hi[e] = qv[0][4 + e];
+            hi[4 + e] = qv[1][4 + e];
+          }
+          put(I.Q, PK, r, cp, lo);
+          put(I.Q, PK, r, cp + 1, hi);
+        } else {
+          put(I.K, PK, r, pi, kv[0]);
+          put(I.Q, PK, r, pi, qv[0]);
+        }
       }
     }
     if (tid < kBT) {
@@ -176,15 +226,23 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
     }
   }
   __syncthreads();
+  if constexpr (!KDA && O::KPL == 1) {
+    // fp32 GDN: K^T for the reduce's state update (chunk rows chained = natural)
+    for (int idx = tid; idx < DK * PT; idx += kThreads) {
+      const int c = idx / PT, pc = idx % PT;
+      T v[CH];
+#pragma unroll
+      for (int e = 0; e < CH; ++e) v[e] = sK[kidx<O>(pc * CH + e) * LDK + c];
+      put(I.KT, PT, c, pc, v);
+    }
+  }
 
-  // M tile (R, S) from an accumulator -> workspace, columns in chained order
-  auto store_m = [&](int R, int S, const f32x4 &c, bool mask) {
+  // M tile (R, S) from an accumulator -> sMt (natural order; the write-out
+  // below zeroes the upper triangle)
+  auto store_m = [&](int R, int S, const f32x4 &c) {
     const int s = 16 * S + lr;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int r = 16 * R + lg * 4 + e;
-      Mws[r * kBT + kpos<O>(s)] = (T)((!mask || s <= r) ? c[e] : 0.f);
-    }
+    for (int e = 0; e < 4; ++e) sMt[(16 * R + lg * 4 + e) * LDM + s] = (T)c[e];
   };
 
   if constexpr (!KDA) {
@@ -227,7 +285,7 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
           sL[r * LDL + s] = s < r ? sB[r] * v[e] : 0.f;
         }
       } else {
-        store_m(R, S, v, true);
+        store_m(R, S, v);
       }
     }
     if (w == 0) {
@@ -258,19 +316,29 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
     }
     // decayed operands for the reduce, in chained order
     {
-      T *Kd = static_cast<T *>(p.Kd_raw) + unit * (kBT * DK);
-      T *Qd = static_cast<T *>(p.Qd_raw) + unit * (kBT * DK);
-      T *Kbt = static_cast<T *>(p.Kbt_raw) + unit * (kBT * DK);
-      for (int idx = tid; idx < kBT * DK; idx += kThreads) {
-        const int r = idx / DK, c = idx % DK;
-        const float f = __expf(sG[r * DK + c]);
-        Kd[r * DK + kpos<O>(c)] = (T)((float)sK[r * LDK + c] * f);
-        Qd[r * DK + kpos<O>(c)] = (T)((float)sQ[r * LDK + c] * f);
+      for (int idx = tid; idx < kBT * PK; idx += kThreads) {
+        const int r = idx / PK, pc = idx % PK;
+        T kv[CH], qv[CH];
+#pragma unroll
+        for (int e = 0; e < CH; ++e) {
+          const int c = kidx<O>(pc * CH + e);
+          const float f = __expf(sG[r * DK + c]);
+          kv[e] = (T)((float)sK[r * LDK + c] * f);
+          qv[e] = (T)((float)sQ[r * LDK + c] * f);
+        }
+        put(I.K, PK, r, pc, kv);
+        put(I.Q, PK, r, pc, qv);
       }
-      for (int idx = tid; idx < kBT * DK; idx += kThreads) {
-        const int c = idx / kBT, r = idx % kBT;
-        const float f = __expf(sG[(kBT - 1) * DK + c] - sG[r * DK + c]);
-        Kbt[c * kBT + kpos<O>(r)] = (T)((float)sK[r * LDK + c] * f);
+      for (int idx = tid; idx < DK * PT; idx += kThreads) {
+        const int c = idx / PT, pc = idx % PT;
+        const float GC = sG[(kBT - 1) * DK + c];
+        T v[CH];
+#pragma unroll
+        for (int e = 0; e < CH; ++e) {
+          const int r = kidx<O>(pc * CH + e);
+          v[e] = (T)((float)sK[r * LDK + c] * __expf(GC - sG[r * DK + c]));
+        }
+        put(I.KT, PT, c, pc, v);
       }
       if (tid < kBT) {
         vec[tid] = 1.f;
@@ -307,7 +375,7 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
           c = O::mfma(frag_lds<O>(src, LDK, 0, k0, lane), frag_lds<O>(sKs, LDK, 16 * S, k0, lane),
                       c);
         if (isM) {
-          store_m(R, S, c, false);
+          store_m(R, S, c);
         } else {
           const int s = 16 * S + lr;
 #pragma unroll
@@ -332,17 +400,22 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
         }
       }
       sL[r * LDL + s] = s < r ? sB[r] * a : 0.f;
-      Mws[r * kBT + kpos<O>(s)] = (T)m;
+      sMt[r * LDM + s] = (T)m;
     }
   }
-  // upper block triangle of M is zero (the reduce reads whole k-steps)
-  for (int idx = tid; idx < 6 * 256; idx += kThreads) {
-    const int u = idx >> 8;  // (R, S) with S > R
-    const int R = u < 3 ? 0 : (u < 5 ? 1 : 2);
-    const int S = u < 3 ? u + 1 : (u < 5 ? u - 1 : 3);
-    Mws[(16 * R + ((idx >> 4) & 15)) * kBT + kpos<O>(16 * S + (idx & 15))] = (T)0.f;
-  }
   __syncthreads();
+  // M -> image, chained columns, upper triangle zero (the reduce reads whole
+  // k-steps)
+  for (int idx = tid; idx < kBT * PT; idx += kThreads) {
+    const int r = idx / PT, pc = idx % PT;
+    T v[CH];
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const int s = kidx<O>(pc * CH + e);
+      v[e] = s <= r ? sMt[r * LDM + s] : (T)0.f;
+    }
+    put(I.MM, PT, r, pc, v);
+  }
 
   // ---- X = (I + L)^-1: diagonal blocks by forward substitution, lane = column
   if (w == 0) {
@@ -401,19 +474,16 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
     }
     __syncthreads();
   }
-  // ---- Tn = X diag(beta), strict lower part, 16-byte stores in chained order
-  {
-    constexpr int CH = 16 / sizeof(T);  // elements per 16-byte store
-    for (int idx = tid; idx < kBT * kBT / CH; idx += kThreads) {
-      const int r = idx / (kBT / CH), p0 = (idx % (kBT / CH)) * CH;
-      T v[CH];
+  // ---- Tn = X diag(beta), strict lower part, chained columns
+  for (int idx = tid; idx < kBT * PT; idx += kThreads) {
+    const int r = idx / PT, pc = idx % PT;
+    T v[CH];
 #pragma unroll
-      for (int e = 0; e < CH; ++e) {
-        const int s = kidx<O>(p0 + e);
-        v[e] = (T)(s < r ? sX[r * LDL + s] * sB[s] : 0.f);
-      }
-      *reinterpret_cast<uint4 *>(Tws + r * kBT + p0) = *reinterpret_cast<const uint4 *>(v);
+    for (int e = 0; e < CH; ++e) {
+      const int s = kidx<O>(pc * CH + e);
+      v[e] = (T)(s < r ? sX[r * LDL + s] * sB[s] : 0.f);
     }
+    put(I.TN, PT, r, pc, v);
   }
 }
 

@@ -141,27 +141,138 @@ __device__ __forceinline__ typename O::Frag b_frag(const f32x4 *acc, int s) {
   }
 }
 
+// ------------------------------------------------------------ tile images
+// Operand tiles live in LDS as rows of 16-byte pieces with the piece index of
+// each row XOR-swizzled, so that a tile can be copied into LDS verbatim (one
+// lane per 16 bytes, as the direct global-to-LDS loads write it) and still be
+// read without bank conflicts:
+//   - 16 consecutive rows reading the same logical piece (an A fragment) hit
+//     16 distinct pieces, i.e. all 64 banks once;
+//   - 4 consecutive rows reading 4 consecutive pieces of a 32-element block
+//     (the transposed reads of the state update, one per 16-lane group) hit
+//     16 distinct pieces.
+// P = pieces per row (16: 256-byte rows, 8: 128-byte rows; narrower rows
+// need no swizzle for these patterns).
+template <int P>
+__device__ __host__ __forceinline__ constexpr int swz(int row) {
+  if constexpr (P == 16) return ((row & 3) << 2) | ((row >> 2) & 3);
+  else if constexpr (P == 8) return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  else return 0;
+}
+// byte offset of logical piece `piece` of row `row`
+template <int P>
+__device__ __host__ __forceinline__ constexpr int tile_off(int row, int piece) {
+  return row * (16 * P) + ((piece ^ swz<P>(row)) << 4);
+}
+
+// The per-(chunk slot, head) image the map writes to the workspace and the
+// reduce copies into LDS, element type e = 2 (fp16 operands) or 4 (fp32):
+//   K   [64][d_k]  K (GDN) or K*exp(G) (KDA), key index in chained order
+//   Q   [64][d_k]  likewise Q
+//   KT  [d_k][64]  (KDA: (K*exp(G_C - G))^T; fp32 GDN: K^T), chunk rows chained;
+//                  absent for fp16 GDN, whose reduce reads K^T from K
+//   TN  [64][64]   T = A^-1 diag(beta) without its diagonal, columns chained
+//   MM  [64][64]   masked decayed Q K^T, columns chained
+//   VEC [192 + d_k] fp32: exp(G_r) | exp(G_C - G_r) | beta_r | state decay
+//                  of each key row, padded to a multiple of 1 KiB
+// every matrix swizzled as above; every region a multiple of 1 KiB.
+struct ImageLayout {
+  int K, Q, KT, TN, MM, VEC, BYTES, PK, PT;
+};
+__device__ __host__ constexpr ImageLayout image_layout(bool kda, int e, int dk) {
+  const bool has_kt = kda || e == 4;
+  ImageLayout L{};
+  L.PK = dk * e / 16;
+  L.PT = 64 * e / 16;
+  L.K = 0;
+  L.Q = L.K + 64 * dk * e;
+  L.KT = L.Q + 64 * dk * e;
+  L.TN = L.KT + (has_kt ? dk * 64 * e : 0);
+  L.MM = L.TN + 64 * 64 * e;
+  L.VEC = L.MM + 64 * 64 * e;
+  L.BYTES = L.VEC + ((192 + dk) * 4 + 1023) / 1024 * 1024;
+  return L;
+}
+
+typedef __attribute__((address_space(3))) void *lds_ptr_t;
+__device__ __forceinline__ lds_ptr_t to_lds(void *p) { return (lds_ptr_t)(p); }
+
+// Direct global-to-LDS copy of 16 bytes per lane: lane l's bytes at buffer
+// offset voff (+ soff, not range checked) land at lds + 16 l; lanes out of the
+// resource's range write zeros.  `lds` must be the same for the whole wave.
+// The builtin is emitted in the device pass only: in the host pass it would
+// keep a kernel template from getting its launch stub.
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t rsrc, void *lds, int voff,
+                                              int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, to_lds(lds), 16, voff, soff, 0, 0);
+#endif
+}
+
+// s_waitcnt immediate waiting until at most n vector memory operations of
+// this wave are outstanding (expcnt and lgkmcnt not waited for)
+__device__ __host__ constexpr int vmcnt_imm(int n) {
+  return (((n >> 4) & 3) << 14) | 0x0F70 | (n & 15);
+}
+
+// A fragment (rows m0..m0+15, k-step s) from a swizzled image tile with P
+// pieces per row, k index in chained order
+template <typename O, int P>
+__device__ __forceinline__ typename O::Frag a_frag_img(const char *tile, int m0, int s, int lane) {
+  const int lr = lane & 15, g = lane >> 4;
+  const int row = m0 + lr;
+  if constexpr (O::KPL == 1) {
+    // fp32: k = 16 (s / 4) + 4 g + (s % 4): piece 4 (s / 4) + g, word s % 4
+    return *reinterpret_cast<const float *>(tile + tile_off<P>(row, 4 * (s >> 2) + g) + 4 * (s & 3));
+  } else {
+    return *reinterpret_cast<const typename O::Frag *>(tile + tile_off<P>(row, 4 * s + g));
+  }
+}
+
 // Transposed A fragment (fp16 only): the operand M^T of a product that
-// contracts over the rows of a row-major LDS matrix M whose columns are in
-// chained order (kpos), for output rows m0..m0+15 of M^T (= columns of M) and
-// k-step s over the rows of M.  Built from two ds_read_b64_tr_b16, which in
-// each 16-lane group hand lane j element e of the 4-element row read by lane
-// 4e + j/4, entry j%4: lane j therefore reads row 32s + 4g + j/4 (+16 for the
-// upper half) at the four columns m0 + 4(j%4) .. +3, contiguous in kpos order.
-__device__ __forceinline__ half8 a_frag_tr(const _Float16 *base, int ld, int m0, int s, int lane) {
-  typedef short s16x4 __attribute__((ext_vector_type(4)));
+// contracts over the rows of an image tile M (P pieces per row) whose columns
+// are in chained order (kpos), for output rows m0..m0+15 of M^T (= columns of
+// M) and k-step s over the rows of M.  Built from two ds_read_b64_tr_b16,
+// which in each 16-lane group hand lane j element e of the 4-element row read
+// by lane 4e + j/4, entry j%4: lane j therefore reads row 32s + 4g + j/4 (+16
+// for the upper half) at the four columns m0 + 4(j%4) .. +3, contiguous in
+// kpos order.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4 ds_read_tr16(const char *p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p));
+}
+template <int P>
+__device__ __forceinline__ half8 a_frag_tr(const char *tile, int m0, int s, int lane) {
   const int j = lane & 15, g = lane >> 4;
   const int row = 32 * s + 4 * g + (j >> 2);
-  const int pos = (m0 & ~31) + 8 * (j & 3) + 4 * ((m0 & 31) >> 4);
-  const _Float16 *p0 = base + row * ld + pos;
-  const auto lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4 *)(p0));
-  const auto hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) s16x4 *)(p0 + 16 * ld));
+  const int piece = (m0 >> 5) * 4 + (j & 3);
+  const int sub = 8 * ((m0 >> 4) & 1);
+  const auto lo = ds_read_tr16(tile + tile_off<P>(row, piece) + sub);
+  const auto hi = ds_read_tr16(tile + tile_off<P>(row + 16, piece) + sub);
   // whole-vector casts: a bit cast of a single vector element is lowered as
   // element 0 by this compiler
   return __builtin_shufflevector(__builtin_bit_cast(half4, lo), __builtin_bit_cast(half4, hi), 0,
                                  1, 2, 3, 4, 5, 6, 7);
+}
+
+// The same transposed read as opaque inline assembly, for use while direct
+// global-to-LDS loads are in flight: the compiler cannot tell which LDS bytes
+// the builtin reads and would otherwise wait for every outstanding vector
+// memory operation first.  Its result is only valid after wait_lds_tied.
+__device__ __forceinline__ void ds_read_tr16_async(s16x4 &r, const char *p) {
+  const uint32_t a = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char *)p);
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
+}
+// wait until at most N LDS operations are outstanding (LDS operations
+// complete in order), tying the four registers to the wait so no use of
+// them is scheduled above it
+template <int N>
+__device__ __forceinline__ void wait_lds_tied(s16x4 &a, s16x4 &b, s16x4 &c, s16x4 &d) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
+}
+__device__ __forceinline__ half8 join_half8(s16x4 lo, s16x4 hi) {
+  return __builtin_shufflevector(__builtin_bit_cast(half4, lo), __builtin_bit_cast(half4, hi), 0, 1,
+                                 2, 3, 4, 5, 6, 7);
 }
 
 // number of k-steps over K logical indices

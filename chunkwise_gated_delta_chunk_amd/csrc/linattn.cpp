@@ -33,46 +33,24 @@ int check_shape(const la_chunk_fwd_args *a) {
   const int64_t nt = la_nt_max(a->T_max, a->N_max, a->BT);
   if (nt < 1 || nt > 0x7fffffff) return LA_ERR_SHAPE;
   if ((int64_t)a->N_max * a->H > 0x7fffffff / 8) return LA_ERR_SHAPE;
+  // byte offsets inside one chunk of v / o (64 token rows) stay in int
+  if ((int64_t)a->H * a->d_v * 4 * 64 > 0x7fffffff) return LA_ERR_SHAPE;
   return LA_OK;
 }
 
 int split_for(const la_chunk_fwd_args *a) {
   if (a->dv_split) return a->dv_split;
-  // four waves of 16 state columns per workgroup
+  // 64 state columns per workgroup
   return a->d_v / 64;
 }
 
 size_t elem_bytes(const la_chunk_fwd_args *a) { return a->qkv_dtype == LA_BF16 ? 2 : 4; }
 
-// Workspace layout, per chunk slot and head (element size e = 2 for bf16
-// inputs, 4 for fp32), each region contiguous over (slot, head):
-// Tn [BT][BT], M [BT][BT], vec [192 + d_k] fp32; KDA adds Kd [BT][d_k],
-// Qd [BT][d_k] and Kbt [d_k][BT].
-struct WsLayout {
-  size_t tn, m, vec, kd, qd, kbt, total;
-};
-
-size_t round256(size_t x) { return (x + 255) & ~(size_t)255; }
-
-WsLayout ws_layout(const la_chunk_fwd_args *a, bool kda) {
+// Workspace: one map-stage image per (chunk slot, head), image_layout bytes each
+size_t ws_bytes(const la_chunk_fwd_args *a, bool kda) {
   const size_t cells = (size_t)la_nt_max(a->T_max, a->N_max, a->BT) * a->H;
-  const size_t e = elem_bytes(a);
-  WsLayout L{};
-  L.tn = 0;
-  L.m = round256(cells * a->BT * a->BT * e);
-  L.vec = L.m + round256(cells * a->BT * a->BT * e);
-  L.total = L.vec + round256(cells * (size_t)(192 + a->d_k) * sizeof(float));
-  if (kda) {
-    const size_t op = round256(cells * a->BT * a->d_k * e);
-    L.kd = L.total;
-    L.qd = L.kd + op;
-    L.kbt = L.qd + op;
-    L.total = L.kbt + op;
-  }
-  return L;
+  return cells * (size_t)la::image_layout(kda, (int)elem_bytes(a), a->d_k).BYTES;
 }
-
-size_t ws_bytes(const la_chunk_fwd_args *a, bool kda) { return ws_layout(a, kda).total; }
 
 int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
   if (!a) return LA_ERR_NULL;
@@ -89,12 +67,12 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     const size_t sb = (size_t)a->N_max * a->H * a->d_k * a->d_v * sizeof(float);
     if (overlaps(a->h0, sb, a->ht, sb)) return LA_ERR_ALIAS;
   }
-  // 16-byte vector loads of q/k rows and of workspace rows
-  const uintptr_t mis = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->k);
+  // 16-byte vector loads of q, k and v rows
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->k) |
+                        reinterpret_cast<uintptr_t>(a->v);
   if (mis % 16 != 0) return LA_ERR_SHAPE;
 
   const bool bf = a->qkv_dtype == LA_BF16;
-  const WsLayout L = ws_layout(a, kda);
   char *ws = static_cast<char *>(a->workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (stages & LA_STAGE_MAP) {
@@ -107,34 +85,18 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     mp.chunk_indices = a->chunk_indices;
     mp.H = a->H;
     mp.NT_max = (int)la_nt_max(a->T_max, a->N_max, a->BT);
-    mp.Tn_raw = ws + L.tn;
-    mp.M_raw = ws + L.m;
-    mp.vec = reinterpret_cast<float *>(ws + L.vec);
-    if (kda) {
-      mp.Kd_raw = ws + L.kd;
-      mp.Qd_raw = ws + L.qd;
-      mp.Kbt_raw = ws + L.kbt;
-    }
+    mp.img = ws;
     if (la::launch_chunk_map(mp, kda, bf, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
   }
   if (stages & LA_STAGE_REDUCE) {
     la::ReduceParams rp{};
-    rp.q = a->q;
-    rp.k = a->k;
     rp.v = a->v;
     rp.cu_seqlens = a->cu_seqlens;
     rp.chunk_offsets = a->chunk_offsets;
     rp.h0 = a->h0;
     rp.o = a->o;
     rp.ht = a->ht;
-    rp.Tn_raw = ws + L.tn;
-    rp.M_raw = ws + L.m;
-    rp.vec = reinterpret_cast<const float *>(ws + L.vec);
-    if (kda) {
-      rp.Kd_raw = ws + L.kd;
-      rp.Qd_raw = ws + L.qd;
-      rp.Kbt_raw = ws + L.kbt;
-    }
+    rp.img = ws;
     rp.H = a->H;
     rp.N_max = a->N_max;
     rp.S = split_for(a);

@@ -71,3 +71,67 @@ def compare(inp, o, ht, o_ref, ht_ref, heads=None, tol=None):
         h_np = ht.cpu().numpy()[:, sel]
         eh = rel_err(h_np[nonempty], ht_ref[nonempty])
     return eo, eh, tol
+
+
+# ------------------------------------------------------ workspace images ---
+# Layout of the per-(chunk slot, head) map-stage image, as include/linattn.h
+# documents it: regions K, Q, [KT], TN, MM, VEC; matrices stored as rows of
+# 16-byte pieces, piece index XOR-swizzled per row, fp16 columns in the
+# chained MFMA order.
+
+def kpos(k):
+    """Stored position of logical column k in the chained fp16 order."""
+    return (k & ~31) + 8 * ((k & 15) >> 2) + (k & 3) + 4 * ((k & 31) >> 4)
+
+
+def swz(row, P):
+    if P == 16:
+        return ((row & 3) << 2) | ((row >> 2) & 3)
+    if P == 8:
+        return (((row >> 1) & 1) << 2) | ((row >> 2) & 3)
+    return 0
+
+
+def image_layout(kda, esz, d):
+    has_kt = kda or esz == 4
+    L = {"K": 0, "Q": 64 * d * esz}
+    L["KT"] = L["Q"] + 64 * d * esz
+    L["TN"] = L["KT"] + (d * 64 * esz if has_kt else 0)
+    L["MM"] = L["TN"] + 64 * 64 * esz
+    L["VEC"] = L["MM"] + 64 * 64 * esz
+    L["BYTES"] = L["VEC"] + -(-(192 + d) * 4 // 1024) * 1024
+    L["has_kt"] = has_kt
+    return L
+
+
+def untile(cell, off, rows, cols, esz):
+    """Logical [rows][cols] matrix from an image tile at byte offset ``off`` of
+    one cell (uint8 numpy array)."""
+    P = cols * esz // 16
+    ch = 16 // esz
+    r = np.arange(rows)[:, None]
+    c = np.arange(cols)[None, :]
+    pos = np.vectorize(kpos)(c) if esz == 2 else c
+    sw = np.vectorize(lambda x: swz(int(x), P))(r)
+    byte = off + r * P * 16 + (((pos // ch) ^ sw) * 16) + (pos % ch) * esz
+    dt = np.float16 if esz == 2 else np.float32
+    flat = cell.view(dt)
+    return flat[byte // esz].astype(np.float64)
+
+
+def decode_images(ws, NT, H, d, kda, esz):
+    """Every cell of a workspace (torch uint8 tensor) as dict of logical arrays."""
+    L = image_layout(kda, esz, d)
+    raw = ws[:NT * H * L["BYTES"]].cpu().numpy().reshape(NT, H, L["BYTES"])
+    out = {}
+    for slot in range(NT):
+        for h in range(H):
+            cell = np.ascontiguousarray(raw[slot, h])
+            rec = {"K": untile(cell, L["K"], 64, d, esz), "Q": untile(cell, L["Q"], 64, d, esz),
+                   "TN": untile(cell, L["TN"], 64, 64, esz),
+                   "MM": untile(cell, L["MM"], 64, 64, esz),
+                   "VEC": cell[L["VEC"]:L["VEC"] + (192 + d) * 4].view(np.float32).astype(np.float64)}
+            if L["has_kt"]:
+                rec["KT"] = untile(cell, L["KT"], d, 64, esz)
+            out[(slot, h)] = rec
+    return out

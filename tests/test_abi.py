@@ -115,11 +115,13 @@ def test_workspace_size_and_split():
                                   (256, 1, 2, 64, torch.float32, 4),
                                   (16384, 64, 32, 128, torch.bfloat16, 2)]:
         cells = meta_ref.nt_max(T, N, 64) * H
-        r256 = lambda x: (x + 255) // 256 * 256
-        want = 2 * r256(cells * 64 * 64 * esz) + r256(cells * (192 + d) * 4)
-        assert la.workspace_bytes(T, N, H, d, d, dt) == want
-        want_kda = want + 3 * r256(cells * 64 * d * esz)
-        assert la.workspace_bytes(T, N, H, d, d, dt, kda=True) == want_kda
+        # one image per cell: K, Q, [K^T: KDA or fp32], Tn, M, vec padded to 1 KiB
+        vec = -(-(192 + d) * 4 // 1024) * 1024
+        kt = 64 * d * esz
+        gdn = 2 * 64 * d * esz + (kt if esz == 4 else 0) + 2 * 64 * 64 * esz + vec
+        assert la.workspace_bytes(T, N, H, d, d, dt) == cells * gdn
+        kda = 2 * 64 * d * esz + kt + 2 * 64 * 64 * esz + vec
+        assert la.workspace_bytes(T, N, H, d, d, dt, kda=True) == cells * kda
     assert la.workspace_bytes(0, 1, 1, 64, 64, torch.bfloat16) == 0
     assert la.dv_split_for(8192, 8, 16, 128, 128, torch.bfloat16) == 2
     assert la.dv_split_for(16384, 64, 32, 128, 128, torch.bfloat16) == 2

@@ -13,7 +13,7 @@ import torch
 import chunkwise_gated_delta_chunk_amd as la
 from oracle import chunkwise_ref, meta_ref
 from synth import config, make_inputs
-from tests.helpers import TOL, compare, rel_err, run_gpu, run_oracle, to_dev
+from tests.helpers import TOL, compare, decode_images, rel_err, run_gpu, run_oracle, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -110,14 +110,11 @@ def kpos(k):
     return (k & ~31) + 8 * ((k & 15) >> 2) + (k & 3) + 4 * ((k & 31) >> 4)
 
 
-def r256(x):
-    return (x + 255) // 256 * 256
-
-
 @pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
 def test_map_stage_matrices(kda):
-    """Map-stage workspace against the chunkwise reference: T without its
-    diagonal, M, the row vectors and (KDA) the decayed operands."""
+    """Map-stage images against the chunkwise reference: T without its
+    diagonal, M, the row vectors, K and Q (GDN: exact fp16 copies) and the
+    decayed operands (KDA)."""
     cu = [0, 64, 100, 230]
     d = 128
     inp = make_inputs(230, 2, d, d, kda=kda, dtype="bf16", seed=41, cu_seqlens=cu)
@@ -129,23 +126,7 @@ def test_map_stage_matrices(kda):
                         dv["cu_seqlens"], ci, co, workspace=ws)
     torch.cuda.synchronize()
     NT = la.nt_max(230, 3)
-    cells = NT * 2
-    mat = cells * 64 * 64 * 2
-    off_m, off_v = r256(mat), 2 * r256(mat)
-    vecn = 192 + d
-    off_kd = off_v + r256(cells * vecn * 4)
-    op = cells * 64 * d * 2
-    cols64 = [kpos(k) for k in range(64)]
-    colsd = [kpos(k) for k in range(d)]
-    tn = ws[:mat].view(torch.float16).view(NT, 2, 64, 64).float().cpu().numpy()[..., cols64]
-    mm = ws[off_m:off_m + mat].view(torch.float16).view(NT, 2, 64, 64).float().cpu().numpy()[..., cols64]
-    vec = ws[off_v:off_v + cells * vecn * 4].view(torch.float32).view(NT, 2, vecn).cpu().numpy()
-    if kda:
-        kd = ws[off_kd:off_kd + op].view(torch.float16).view(NT, 2, 64, d).float().cpu().numpy()[..., colsd]
-        qd = ws[off_kd + r256(op):off_kd + r256(op) + op].view(torch.float16).view(NT, 2, 64, d)
-        qd = qd.float().cpu().numpy()[..., colsd]
-        o3 = off_kd + 2 * r256(op)
-        kbt = ws[o3:o3 + op].view(torch.float16).view(NT, 2, d, 64).float().cpu().numpy()[..., cols64]
+    img = decode_images(ws, NT, 2, d, kda, 2)
     _, _, inter = chunkwise_ref.chunk_forward(inp["q"], inp["k"], inp["v"], inp["g"],
                                               inp["beta"], cu, None, kda=kda, keep=True)
     slot = 0
@@ -155,27 +136,35 @@ def test_map_stage_matrices(kda):
             C = rows.stop - rows.start
             for h in range(2):
                 it = inter[(slot, h)]
+                im = img[(slot, h)]
+                tn, mm, vec = im["TN"], im["MM"], im["VEC"]
                 Tref = it["T"] - np.diag(np.diag(it["T"]))
-                assert rel_err(tn[slot, h, :C, :C], Tref) < 2e-3, (slot, h)
-                assert rel_err(mm[slot, h, :C, :C], it["M"]) < 2e-3, (slot, h)
+                assert rel_err(tn[:C, :C], Tref) < 2e-3, (slot, h)
+                assert rel_err(mm[:C, :C], it["M"]) < 2e-3, (slot, h)
                 # tail rows/columns and the upper triangle are exactly zero
-                assert not tn[slot, h, C:, :].any() and not tn[slot, h, :, C:].any()
-                assert not np.triu(tn[slot, h], 0).any()
-                assert not np.triu(mm[slot, h], 1).any()
+                assert not tn[C:, :].any() and not tn[:, C:].any()
+                assert not np.triu(tn, 0).any()
+                assert not np.triu(mm, 1).any()
                 G = it["G"]
-                Gl = G[:, 0] if G.ndim == 2 else G
-                assert rel_err(vec[slot, h, 128:128 + C], inp["beta"][rows, h]) == 0.0
+                assert rel_err(vec[128:128 + C], inp["beta"][rows, h]) == 0.0
+                K, Q = inp["k"][rows, h], inp["q"][rows, h]
                 if not kda:
-                    assert rel_err(vec[slot, h, :C], np.exp(G)) < 1e-5
-                    assert rel_err(vec[slot, h, 64:64 + C], np.exp(G[-1] - G)) < 1e-5
-                    assert rel_err(vec[slot, h, 192:192 + d], np.full(d, np.exp(G[-1]))) < 1e-5
+                    # bf16 values are exact in fp16 inside its normal range; below
+                    # it they round to the subnormal grid (step 2^-24)
+                    for got, ref in ((im["K"][:C], K), (im["Q"][:C], Q)):
+                        normal = np.abs(ref) >= 2.0 ** -14
+                        assert np.array_equal(got[normal], ref[normal])
+                        assert np.abs(got - ref).max() <= 2.0 ** -25
+                    assert not im["K"][C:].any() and not im["Q"][C:].any()
+                    assert rel_err(vec[:C], np.exp(G)) < 1e-5
+                    assert rel_err(vec[64:64 + C], np.exp(G[-1] - G)) < 1e-5
+                    assert rel_err(vec[192:192 + d], np.full(d, np.exp(G[-1]))) < 1e-5
                 else:
-                    K, Q = inp["k"][rows, h], inp["q"][rows, h]
-                    assert rel_err(kd[slot, h, :C], K * np.exp(G)) < 1e-3
-                    assert rel_err(qd[slot, h, :C], Q * np.exp(G)) < 1e-3
-                    assert rel_err(kbt[slot, h, :, :C], (K * np.exp(G[-1] - G)).T) < 1e-3
-                    assert rel_err(vec[slot, h, 192:192 + d], np.exp(G[-1])) < 1e-5
-                    assert not kd[slot, h, C:].any() and not kbt[slot, h, :, C:].any()
+                    assert rel_err(im["K"][:C], K * np.exp(G)) < 1e-3
+                    assert rel_err(im["Q"][:C], Q * np.exp(G)) < 1e-3
+                    assert rel_err(im["KT"][:, :C], (K * np.exp(G[-1] - G)).T) < 1e-3
+                    assert rel_err(vec[192:192 + d], np.exp(G[-1])) < 1e-5
+                    assert not im["K"][C:].any() and not im["KT"][:, C:].any()
             slot += 1
 
 
