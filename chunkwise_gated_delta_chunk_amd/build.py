@@ -19,6 +19,9 @@ FLAGS = [
     # private arrays stay in registers or scratch, never in LDS: the kernels
     # size their LDS themselves
     "-mllvm", "-disable-promote-alloca-to-lds",
+    # MFMA accumulators in ordinary VGPRs: the kernels scale and convert their
+    # accumulators with VALU instructions, which cannot read AGPRs
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall", "-Wno-unused-function", "-Wno-unknown-warning-option",
 ]
 

@@ -19,19 +19,27 @@
 // operands (K*exp(G), Q*exp(G), (K*exp(G_C - G))^T, exp(G_C)), so the row
 // factors are 1 and the state decays by diag(exp(G_C)).
 //
-// Work split: each wave owns CT 16-column state tiles for all chunk rows, so
-// the chain H -> K H -> X -> U -> H of its columns never leaves the wave, and
-// every A-operand fragment read from LDS feeds CT MFMAs (CT = 1 by default:
-// with two tiles the register pressure costs more than the saved LDS reads).  With
+// Work split: each wave owns 16 state columns for all chunk rows, so the
+// chain H -> K H -> X -> U -> H of its columns never leaves the wave.  With
 // the chained k order (see la_device.h) an accumulator tile is itself the B
 // operand of the next product, so H, X and U stay in registers.  Only the
-// shared, state-independent operands of a chunk are in LDS: the map stage's
-// image of the chunk (K, Q, [K^T], Tn, M, row vectors) and the V slice.  Both
+// shared, state-independent operands of a chunk are in LDS: the V slice and
+// the map stage's image of the chunk (K, Q, [K^T], Tn, M, row vectors).  Both
 // are copied one chunk ahead by direct global-to-LDS loads (no registers, no
 // LDS store instructions) into the other half of a double buffer: one
 // barrier per chunk, and the copy of chunk j + 1 overlaps the arithmetic of
 // chunk j.  V rows past the chunk's end read as zero through the buffer range
 // check, and output rows past it are dropped the same way.
+//
+// Instruction overhead is kept off the per-chunk path: every hot LDS address
+// is a per-lane pattern computed once plus an immediate offset (the chunk
+// loop is unrolled over the two buffers so the buffer is a constant), the
+// copy's per-lane offsets are computed once, and the memory resources
+// advance by pointer bumps.  The fp16 reads of K and Q fragments, of V and of
+// the transposed K^T fragments are opaque inline-assembly reads issued well
+// ahead of their MFMAs with waits tied to their registers: the compiler's own
+// schedule keeps only one or two LDS reads in flight, and it waits for every
+// outstanding vector memory operation before a builtin transposed read.
 //
 // Blocks are numbered so that the slices of one (sequence, head) land on the
 // same XCD (workgroup IDs are dealt round-robin over the 8 XCDs) and share
@@ -44,26 +52,31 @@ namespace la {
 
 namespace {
 
-template <bool KDA, typename In, int DK, int NW, int CT>
+template <bool KDA, typename In, int DK, int NW>
 __global__ __launch_bounds__(64 * NW) void chunk_reduce_kernel(ReduceParams p) {
   using O = Op<In>;
   constexpr int E = (int)sizeof(typename O::T);
   constexpr ImageLayout I = image_layout(KDA, E, DK);
   constexpr bool HAS_KT = KDA || O::KPL == 1;
+  constexpr bool F16 = O::KPL == 8;
   constexpr int PK = DK * E / 16, PT = kBT * E / 16;
-  constexpr int W = 16 * CT * NW;            // state columns per workgroup (CT tiles per wave)
+  constexpr int W = 16 * NW;                 // state columns per workgroup
   constexpr int DV = DK;                     // d_v == d_k
   constexpr int NKD = ksteps<O>(DK);         // k-steps over d_k
   constexpr int NKR = ksteps<O>(kBT);        // k-steps over chunk rows
   constexpr int NHT = DK / 16;               // state row tiles
   constexpr int PV = W * (int)sizeof(In) / 16;   // 16-byte pieces per V row
   constexpr int V_BYTES = kBT * W * (int)sizeof(In);
-  constexpr int STAGE = I.BYTES + V_BYTES;
+  // stage buffer: the V tile first (its reads and those of K and Q stay
+  // under the 64 KiB immediate offset), then the image
+  constexpr int IMG = V_BYTES;
+  constexpr int STAGE = V_BYTES + I.BYTES;
   constexpr int NBUF = 2 * STAGE <= 160 * 1024 ? 2 : 1;
-  constexpr int NIMG = I.BYTES / 1024, NVL = V_BYTES / 1024;
-  constexpr int STORES = 4 * CT * 4;         // o stores per wave per chunk
+  constexpr int NVL = V_BYTES / 1024, NIMG = I.BYTES / 1024, NLOAD = NVL + NIMG;
+  constexpr int LPW = (NLOAD + NW - 1) / NW;  // copy pieces per wave
+  constexpr int STORES = 4 * 4;               // o stores per wave per chunk
   static_assert(I.BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "1 KiB staging pieces");
-  static_assert(STORES < 64, "vmcnt range");
+  static_assert(!F16 || IMG + I.Q + 3 * 256 * PK + 16 <= 65536, "immediate offsets");
 
   __shared__ __attribute__((aligned(16))) char smem[NBUF * STAGE];
 
@@ -79,300 +92,323 @@ __global__ __launch_bounds__(64 * NW) void chunk_reduce_kernel(ReduceParams p) {
   const int bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
   const int lane = lane_id(), w = wave_id();
   const int lr = lane & 15, lg = lane >> 4;
-  const int cw = slice * W + 16 * CT * w;            // this wave's first state column
+  const int cw = slice * W + 16 * w;                 // this wave's first state column
   const int rs_v = H * DV * (int)sizeof(In);         // token stride of v (bytes)
   const int rs_o = H * DV * 4;                       // token stride of o (bytes)
-  const char *img_all = static_cast<const char *>(p.img);
 
   // ---------------------------------------------------------------- staging
-  // V piece q of the LDS tile (row q / PV, stored piece q % PV) comes from the
-  // global row's logical piece (stored ^ swizzle)
-  auto v_voff = [&](int q) {
-    const int row = q / PV, phys = q % PV;
-    return row * rs_v + ((phys ^ swz<PV>(row)) << 4);
-  };
-  auto issue = [&](char *buf, int jj) {
-    const int r0 = bos + (jj - j0) * kBT;
-    const int C = min(kBT, eos - r0);
-    const auto ri = buffer_rsrc(img_all + ((size_t)jj * H + h) * I.BYTES, I.BYTES);
-    for (int q = w; q < NIMG; q += NW)
-      copy16_to_lds(ri, buf + q * 1024, lane * 16, q * 1024);
-    const auto rv = buffer_rsrc(static_cast<const In *>(p.v) + ((size_t)r0 * H + h) * DV + slice * W,
-                                C * rs_v);
-    for (int q = w; q < NVL; q += NW)
-      copy16_to_lds(rv, buf + I.BYTES + q * 1024, v_voff(q * 64 + lane), 0);
+  // Piece q (1 KiB) of a stage: V pieces first, then the image.  Wave w
+  // copies pieces w, w + NW, ...; a V piece's per-lane source offset (row and
+  // swizzled column piece within the chunk) does not depend on the chunk.
+  int voff[LPW];
+#pragma unroll
+  for (int i = 0; i < LPW; ++i) {
+    const int q = w + NW * i;
+    const int e = (q < NVL ? q : 0) * 64 + lane;  // 16-byte V piece index
+    const int row = e / PV, phys = e % PV;
+    voff[i] = q < NVL ? row * rs_v + ((phys ^ swz<PV>(row)) << 4) : lane * 16;
+  }
+  const char *img_c = static_cast<const char *>(p.img) + ((size_t)j0 * H + h) * I.BYTES;
+  const size_t img_step = (size_t)H * I.BYTES;
+  const In *v_c = static_cast<const In *>(p.v) + ((size_t)bos * H + h) * DV + slice * W;
+  const size_t v_step = (size_t)kBT * H * DV;
+  // copy of the chunk whose image starts at img and whose C V rows start at vrow
+  auto copy_chunk = [&](int buf, const char *img, const In *vrow, int C) {
+    const auto ri = buffer_rsrc(img, I.BYTES);
+    const auto rv = buffer_rsrc(vrow, C * rs_v);
+    char *dst = smem + buf * STAGE;
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) {
+      const int q = w + NW * i;
+      if (q < NVL) copy16_to_lds(rv, dst + q * 1024, voff[i], 0);
+      else if (q < NLOAD) copy16_to_lds(ri, dst + q * 1024, lane * 16, (q - NVL) * 1024);
+    }
   };
 
-  // ---------------------------------------------------------- the state
-  f32x4 hacc[CT][NHT];
-  const size_t sbase = ((size_t)n * H + h) * DK * DV;
+  // ---------------------------------------------------------- LDS patterns
+  // per-lane byte addresses, one set per buffer; immediates add the rest
+  uint32_t aK[NBUF][F16 ? NKD : 1];      // A fragment, row tile 0, k-step s (K; Q at +I.Q - I.K)
+  uint32_t aT[NBUF][F16 ? NHT / 2 : 1];  // transposed K^T reads, tile pair t / 2
+  uint32_t aV[NBUF];                     // transposed V reads, row tile 0
+  const uint32_t base = lds_addr(smem);
 #pragma unroll
-  for (int ct = 0; ct < CT; ++ct)
+  for (int bf = 0; bf < NBUF; ++bf) {
+    const uint32_t b0 = base + bf * STAGE;
+    if constexpr (F16) {
+#pragma unroll
+      for (int s = 0; s < NKD; ++s) aK[bf][s] = b0 + tile_off<PK>(lr, 4 * s + lg);
+      const int row = 4 * lg + (lr >> 2);
+#pragma unroll
+      for (int u = 0; u < NHT / 2; ++u) aT[bf][u] = b0 + tile_off<PK>(row, 4 * u + (lr & 3));
+    }
+    if constexpr (sizeof(In) == 2) {
+      // lane i of a 16-lane group reads row 4 lg + i / 4 at columns
+      // 16 w + 4 (i % 4) .. +3 and receives column 16 w + i of 4 rows
+      const int row = 4 * lg + (lr >> 2);
+      const int col = 16 * w + 4 * (lr & 3);
+      aV[bf] = b0 + tile_off<PV>(row, col >> 3) + 2 * (col & 7);
+    } else {
+      aV[bf] = b0;
+    }
+  }
+
+  // ---------------------------------------------------------- the state
+  f32x4 hacc[NHT];
+  const size_t sbase = ((size_t)n * H + h) * DK * DV;
+  if (p.h0) {
 #pragma unroll
     for (int t = 0; t < NHT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        hacc[ct][t][e] =
-            p.h0 ? p.h0[sbase + (size_t)(16 * t + lg * 4 + e) * DV + cw + 16 * ct + lr] : 0.f;
+      for (int e = 0; e < 4; ++e) hacc[t][e] = p.h0[sbase + (size_t)(16 * t + lg * 4 + e) * DV + cw + lr];
+  } else {
+#pragma unroll
+    for (int t = 0; t < NHT; ++t) hacc[t] = zero4();
+  }
 
   int off_o[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) off_o[e] = (lg * 4 + e) * rs_o + (cw + lr) * 4;
-
-  // V values of rows 16R + 4 lg + e, column 16 CT w + 16 ct + lr of the block's tile
-  auto load_v = [&](const char *tV, int R, int ct) {
-    f32x4 v;
-    if constexpr (sizeof(In) == 2) {
-      // transposed read: lane i of a 16-lane group reads row 16R + 4 lg + i/4,
-      // columns c0 + 4 (i % 4) .. +3, and receives column c0 + i of 4 rows
-      const int row = 16 * R + 4 * lg + (lr >> 2);
-      const int col = 16 * CT * w + 16 * ct + 4 * (lr & 3);
-      const s16x4 raw = ds_read_tr16(tV + tile_off<PV>(row, col >> 3) + 2 * (col & 7));
-#pragma unroll
-      for (int e = 0; e < 4; ++e) v[e] = __uint_as_float((uint32_t)(uint16_t)raw[e] << 16);
-    } else {
-      const int col = 16 * CT * w + 16 * ct + lr;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = 16 * R + 4 * lg + e;
-        v[e] = *reinterpret_cast<const float *>(tV + tile_off<PV>(row, col >> 2) + 4 * (col & 3));
-      }
-    }
-    return v;
-  };
+  float *o_c = p.o + ((size_t)bos * H + h) * DV;
+  const size_t o_step = (size_t)kBT * H * DV;
 
   // ---------------------------------------------------------- one chunk
-  // The next chunk's copy (into `next`, if not null) is issued after the last
-  // LDS read that uses the transposing builtin (the V reads of X)
-  auto compute = [&](const char *buf, int jj, char *next) {
+  // buffer BUF holds chunk jj; the copy of the next chunk, if any, goes to
+  // the other buffer and is issued after the V reads
+  auto chunk = [&](auto bufc, int jj, bool first) {
+    constexpr int BUF = decltype(bufc)::value;
+    constexpr int NXT = NBUF == 2 ? 1 - BUF : 0;
     const int r0 = bos + (jj - j0) * kBT;
     const int C = min(kBT, eos - r0);
-    const char *tK = buf + I.K;
-    const char *tQ = buf + I.Q;
-    const char *tKT = buf + I.KT;
-    const char *tTN = buf + I.TN;
-    const char *tMM = buf + I.MM;
-    const float *sv = reinterpret_cast<const float *>(buf + I.VEC);
-    const char *tV = buf + I.BYTES;
+    const bool more = jj + 1 < j1;
+    const char *buf = smem + BUF * STAGE;
+    const char *tV = buf;
+    const char *tK = buf + IMG + I.K;
+    const char *tQ = buf + IMG + I.Q;
+    const char *tKT = buf + IMG + I.KT;
+    const char *tTN = buf + IMG + I.TN;
+    const char *tMM = buf + IMG + I.MM;
+    const float *sv = reinterpret_cast<const float *>(buf + IMG + I.VEC);
 
-    // K H and Q H, the state as B operand straight from its accumulators
-    typename O::Frag hb[CT][NKD];
+    // the copy of this chunk has landed: the operations issued after it are
+    // the previous chunk's STORES output stores (completion is in issue order)
+    if (first || NBUF == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(STORES));
+    __syncthreads();
+
+    // ---- K H and Q H, the state as B operand straight from its accumulators
+    typename O::Frag hb[NKD];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int s = 0; s < NKD; ++s) hb[ct][s] = b_frag<O>(hacc[ct], s);
-    f32x4 yk[CT][4], yq[CT][4];
-#pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        yk[ct][R] = zero4();
-        yq[ct][R] = zero4();
-      }
-#pragma unroll
-    for (int s = 0; s < NKD; ++s)
-#pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        const auto ak = a_frag_img<O, PK>(tK, 16 * R, s, lane);
-        const auto aq = a_frag_img<O, PK>(tQ, 16 * R, s, lane);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) {
-          yk[ct][R] = O::mfma(ak, hb[ct][s], yk[ct][R]);
-          yq[ct][R] = O::mfma(aq, hb[ct][s], yq[ct][R]);
-        }
-      }
-    // X = V - gamma (K H); V rows past the chunk's end were staged as zero
-    f32x4 gam[4], x[CT][4];
+    for (int s = 0; s < NKD; ++s) hb[s] = b_frag<O>(hacc, s);
+    f32x4 yk[4], yq[4];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
-      gam[R] = *reinterpret_cast<const f32x4 *>(sv + 16 * R + lg * 4);
+      yk[R] = zero4();
+      yq[R] = zero4();
+    }
+    if constexpr (F16) {
+      // the 8 fragments of k-step s are read two k-steps ahead
+      half8 fr[NKD][8];
+      auto read_step = [&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        static_for<4>([&](auto rc) {
+          constexpr int R = decltype(rc)::value;
+          ds_read_b128_at<IMG + I.K + R * 256 * PK>(fr[s][2 * R], aK[BUF][s]);
+          ds_read_b128_at<IMG + I.Q + R * 256 * PK>(fr[s][2 * R + 1], aK[BUF][s]);
+        });
+      };
+      read_step(std::integral_constant<int, 0>{});
+      if constexpr (NKD > 1) read_step(std::integral_constant<int, 1>{});
+      static_for<NKD>([&](auto sc) {
+        constexpr int s = decltype(sc)::value;
+        auto &f = fr[s];
+        if constexpr (s + 1 < NKD) wait_lds_tied8<8>(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+        else wait_lds_tied8<0>(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+        if constexpr (s + 2 < NKD) read_step(std::integral_constant<int, s + 2>{});
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct) {
-        const f32x4 v = load_v(tV, R, ct);
+        for (int R = 0; R < 4; ++R) {
+          yk[R] = O::mfma(f[2 * R], hb[s], yk[R]);
+          yq[R] = O::mfma(f[2 * R + 1], hb[s], yq[R]);
+        }
+      });
+    } else {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) x[ct][R][e] = v[e] - gam[R][e] * yk[ct][R][e];
+      for (int s = 0; s < NKD; ++s)
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+          const auto ak = a_frag_img<O, PK>(tK, 16 * R, s, lane);
+          const auto aq = a_frag_img<O, PK>(tQ, 16 * R, s, lane);
+          yk[R] = O::mfma(ak, hb[s], yk[R]);
+          yq[R] = O::mfma(aq, hb[s], yq[R]);
+        }
+    }
+
+    // ---- X = V - gamma (K H); V rows past the chunk's end were staged as zero
+    f32x4 gam[4], x[4];
+    if constexpr (sizeof(In) == 2) {
+      s16x4 vr[4];
+      static_for<4>([&](auto rc) {
+        constexpr int R = decltype(rc)::value;
+        ds_read_tr16_at<R * 256 * PV>(vr[R], aV[BUF]);
+      });
+      wait_lds_tied<0>(vr[0], vr[1], vr[2], vr[3]);
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        gam[R] = *reinterpret_cast<const f32x4 *>(sv + 16 * R + lg * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          x[R][e] = __uint_as_float((uint32_t)(uint16_t)vr[R][e] << 16) - gam[R][e] * yk[R][e];
+      }
+    } else {
+      const int col = 16 * w + lr;
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        gam[R] = *reinterpret_cast<const f32x4 *>(sv + 16 * R + lg * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int row = 16 * R + 4 * lg + e;
+          const float v = *reinterpret_cast<const float *>(tV + tile_off<PV>(row, col >> 2) + 4 * (col & 3));
+          x[R][e] = v - gam[R][e] * yk[R][e];
+        }
       }
     }
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    if (next) issue(next, jj + 1);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    // U = beta X + Tn X
-    typename O::Frag xb[CT][NKR];
+
+    // ---- the copy of the next chunk, ahead of this chunk's stores
+    if constexpr (NBUF == 2) {
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) copy_chunk(NXT, img_c + img_step, v_c + v_step, min(kBT, eos - r0 - kBT));
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // ---- U = beta X + Tn X
+    typename O::Frag xb[NKR];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int s = 0; s < NKR; ++s) xb[ct][s] = b_frag<O>(x[ct], s);
-    f32x4 u[CT][4], ub[CT][4];
+    for (int s = 0; s < NKR; ++s) xb[s] = b_frag<O>(x, s);
+    f32x4 u[4], ub[4];
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
       const f32x4 bet = *reinterpret_cast<const f32x4 *>(sv + 128 + 16 * R + lg * 4);
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+      for (int e = 0; e < 4; ++e) u[R][e] = bet[e] * x[R][e];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) u[ct][R][e] = bet[e] * x[ct][R][e];
-#pragma unroll
-      for (int s = 0; s < ksteps_lower<O>(R); ++s) {
-        const auto at = a_frag_img<O, PT>(tTN, 16 * R, s, lane);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) u[ct][R] = O::mfma(at, xb[ct][s], u[ct][R]);
-      }
+      for (int s = 0; s < ksteps_lower<O>(R); ++s)
+        u[R] = O::mfma(a_frag_img<O, PT>(tTN, 16 * R, s, lane), xb[s], u[R]);
       if constexpr (!KDA) {
         const f32x4 fac = *reinterpret_cast<const f32x4 *>(sv + 64 + 16 * R + lg * 4);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) ub[ct][R][e] = fac[e] * u[ct][R][e];
+        for (int e = 0; e < 4; ++e) ub[R][e] = fac[e] * u[R][e];
       }
     }
-    typename O::Frag ufr[CT][NKR], ubf[CT][NKR];
+    typename O::Frag ufr[NKR], ubf[NKR];
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-      for (int s = 0; s < NKR; ++s) {
-        ufr[ct][s] = b_frag<O>(u[ct], s);
-        if constexpr (KDA) ubf[ct][s] = ufr[ct][s];
-        else ubf[ct][s] = b_frag<O>(ub[ct], s);
-      }
-    // O = scale (gamma (Q H) + M U); rows past the chunk's end are dropped by
-    // the range check of the per-tile output resource
+    for (int s = 0; s < NKR; ++s) {
+      ufr[s] = b_frag<O>(u, s);
+      if constexpr (KDA) ubf[s] = ufr[s];
+      else ubf[s] = b_frag<O>(ub, s);
+    }
+
+    // ---- the transposed K^T reads of the update (fp16 GDN), issued ahead
+    // of the output's arithmetic
+    s16x4 tr[F16 && !HAS_KT ? NHT : 1][4];
+    if constexpr (F16 && !HAS_KT) {
+      static_assert(NKR == 2, "two k-steps over the chunk rows");
+      static_for<NHT>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        static_for<4>([&](auto qc) {
+          constexpr int q = decltype(qc)::value;  // (k-step, half) = (q / 2, q % 2)
+          constexpr int OFF = IMG + I.K + (32 * (q >> 1) + 16 * (q & 1)) * 16 * PK + 8 * (t & 1);
+          ds_read_tr16_at<OFF>(tr[t][q], aT[BUF][t >> 1]);
+        });
+      });
+    }
+
+    // ---- O = scale (gamma (Q H) + M U); rows past the chunk's end are
+    // dropped by the range check of the per-tile output resource
 #pragma unroll
     for (int R = 0; R < 4; ++R) {
-      f32x4 oa[CT];
+      f32x4 oa;
 #pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
+      for (int e = 0; e < 4; ++e) oa[e] = gam[R][e] * yq[R][e];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) oa[ct][e] = gam[R][e] * yq[ct][R][e];
+      for (int s = 0; s < ksteps_lower<O>(R); ++s)
+        oa = O::mfma(a_frag_img<O, PT>(tMM, 16 * R, s, lane), ufr[s], oa);
+      const auto ro = buffer_rsrc(o_c + (size_t)16 * R * H * DV, (C - 16 * R) * rs_o);
 #pragma unroll
-      for (int s = 0; s < ksteps_lower<O>(R); ++s) {
-        const auto am = a_frag_img<O, PT>(tMM, 16 * R, s, lane);
-#pragma unroll
-        for (int ct = 0; ct < CT; ++ct) oa[ct] = O::mfma(am, ufr[ct][s], oa[ct]);
-      }
-      const auto ro = buffer_rsrc(p.o + ((size_t)(r0 + 16 * R) * H + h) * DV, (C - 16 * R) * rs_o);
-#pragma unroll
-      for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p.scale * oa[ct][e]), ro,
-                                                off_o[e] + 64 * ct, 0, 0);
+      for (int e = 0; e < 4; ++e)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p.scale * oa[e]), ro, off_o[e], 0, 0);
     }
-    // H <- decay H + Kbar^T Ubar
+
+    // ---- H <- decay H + Kbar^T Ubar
     if constexpr (HAS_KT) {
 #pragma unroll
       for (int t = 0; t < NHT; ++t) {
         const f32x4 dec = *reinterpret_cast<const f32x4 *>(sv + 192 + 16 * t + lg * 4);
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
+        for (int e = 0; e < 4; ++e) hacc[t][e] *= dec[e];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) hacc[ct][t][e] *= dec[e];
-#pragma unroll
-        for (int s = 0; s < NKR; ++s) {
-          const auto a = a_frag_img<O, PT>(tKT, 16 * t, s, lane);
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) hacc[ct][t] = O::mfma(a, ubf[ct][s], hacc[ct][t]);
-        }
+        for (int s = 0; s < NKR; ++s)
+          hacc[t] = O::mfma(a_frag_img<O, PT>(tKT, 16 * t, s, lane), ubf[s], hacc[t]);
       }
     } else {
-      // K^T straight from K by transposed reads (fp16 GDN, NKR = 2 k-steps):
-      // tile t needs reads (s, half) = (0,lo) (0,hi) (1,lo) (1,hi); those of
-      // tile t + 1 are issued before tile t's wait
-      static_assert(NKR == 2, "two k-steps over the chunk rows");
-      const int j = lr;
-      const int roff = 4 * lg + (j >> 2);
-      auto issue_t = [&](int t, s16x4 (&r)[4]) {
-        const int piece = (t >> 1) * 4 + (j & 3);
-        const int sub = 8 * (t & 1);
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          ds_read_tr16_async(r[q], tK + tile_off<PK>(32 * (q >> 1) + 16 * (q & 1) + roff, piece) + sub);
-      };
       const float gdec = sv[192];
-      s16x4 cur[4], nxt[4];
-      issue_t(0, cur);
+      static_for<NHT>([&](auto tc) {
+        constexpr int t = decltype(tc)::value;
+        // outstanding after tile t's reads: those of the later tiles
+        constexpr int LATER = 4 * (NHT - 1 - t) < 15 ? 4 * (NHT - 1 - t) : 15;
+        wait_lds_tied<LATER>(tr[t][0], tr[t][1], tr[t][2], tr[t][3]);
 #pragma unroll
-      for (int t = 0; t < NHT; ++t) {
-        if (t + 1 < NHT) {
-          issue_t(t + 1, nxt);
-          wait_lds_tied<4>(cur[0], cur[1], cur[2], cur[3]);
-        } else {
-          wait_lds_tied<0>(cur[0], cur[1], cur[2], cur[3]);
-        }
+        for (int e = 0; e < 4; ++e) hacc[t][e] *= gdec;
 #pragma unroll
-        for (int ct = 0; ct < CT; ++ct)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) hacc[ct][t][e] *= gdec;
-#pragma unroll
-        for (int s = 0; s < NKR; ++s) {
-          const half8 a = join_half8(cur[2 * s], cur[2 * s + 1]);
-#pragma unroll
-          for (int ct = 0; ct < CT; ++ct) hacc[ct][t] = O::mfma(a, ubf[ct][s], hacc[ct][t]);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) cur[q] = nxt[q];
-      }
+        for (int s = 0; s < NKR; ++s)
+          hacc[t] = O::mfma(join_half8(tr[t][2 * s], tr[t][2 * s + 1]), ubf[s], hacc[t]);
+      });
     }
+
+    // ---- single buffer: the copy of the next chunk once every wave is done
+    if constexpr (NBUF == 1) {
+      __syncthreads();
+      if (more) copy_chunk(0, img_c + img_step, v_c + v_step, min(kBT, eos - r0 - kBT));
+    }
+    img_c += img_step;
+    v_c += v_step;
+    o_c += o_step;
   };
 
   // ---------------------------------------------------------- chunk loop
-  // Every vector memory operation of a wave inside the loop is one of its
-  // staging loads or one of its STORES output stores per chunk, and they
-  // complete in issue order: at the top of chunk jj the operations issued
-  // after chunk jj's loads are the previous chunk's stores.
-  issue(smem, j0);
-  for (int jj = j0; jj < j1; ++jj) {
-    char *cur = smem + (NBUF == 2 ? ((jj - j0) & 1) * STAGE : 0);
-    if (NBUF == 2 && jj != j0) __builtin_amdgcn_s_waitcnt(vmcnt_imm(STORES));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();  // every wave's copy of chunk jj has landed
-    if constexpr (NBUF == 2) {
-      // the copy of chunk jj + 1 is issued inside compute, before this chunk's
-      // stores (see the count above)
-      compute(cur, jj, jj + 1 < j1 ? smem + (((jj - j0) & 1) ^ 1) * STAGE : nullptr);
-    } else {
-      compute(cur, jj, nullptr);
-      __syncthreads();  // every wave is done reading the buffer
-      if (jj + 1 < j1) issue(smem, jj + 1);
-    }
+  copy_chunk(0, img_c, v_c, min(kBT, eos - bos));
+  for (int jj = j0; jj < j1; jj += 2) {
+    chunk(std::integral_constant<int, 0>{}, jj, jj == j0);
+    if (jj + 1 < j1) chunk(std::integral_constant<int, NBUF == 2 ? 1 : 0>{}, jj + 1, false);
   }
 
   // ---- final state slice
   if (p.ht) {
 #pragma unroll
-    for (int ct = 0; ct < CT; ++ct)
+    for (int t = 0; t < NHT; ++t)
 #pragma unroll
-      for (int t = 0; t < NHT; ++t)
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          p.ht[sbase + (size_t)(16 * t + lg * 4 + e) * DV + cw + 16 * ct + lr] = hacc[ct][t][e];
+      for (int e = 0; e < 4; ++e)
+        p.ht[sbase + (size_t)(16 * t + lg * 4 + e) * DV + cw + lr] = hacc[t][e];
   }
 }
 
 }  // namespace
 
-// 16-column state tiles per wave (1: four waves per 64 columns; 2: two)
-#ifndef LA_REDUCE_CT
-#define LA_REDUCE_CT 1
-#endif
-
 template <bool KDA, typename In, int DK, int NW>
 static hipError_t launch_reduce_t(const ReduceParams &p, hipStream_t st) {
-  constexpr int CT = LA_REDUCE_CT;
   const int units = p.N_max * p.H;
   const int grid = ((units + 7) / 8) * 8 * p.S;
-  hipLaunchKernelGGL((chunk_reduce_kernel<KDA, In, DK, NW, CT>), dim3(grid), dim3(64 * NW), 0, st, p);
+  hipLaunchKernelGGL((chunk_reduce_kernel<KDA, In, DK, NW>), dim3(grid), dim3(64 * NW), 0, st, p);
   return hipGetLastError();
 }
 
 template <bool KDA, typename In, int DK>
 static hipError_t launch_reduce_w(const ReduceParams &p, int W, hipStream_t st) {
-  constexpr int CT = LA_REDUCE_CT;
   switch (W) {
-    case 32: return launch_reduce_t<KDA, In, DK, 2 / CT>(p, st);
-    case 64: return launch_reduce_t<KDA, In, DK, 4 / CT>(p, st);
+    case 32: return launch_reduce_t<KDA, In, DK, 2>(p, st);
+    case 64: return launch_reduce_t<KDA, In, DK, 4>(p, st);
     case 128:
-      if constexpr (DK >= 128) return launch_reduce_t<KDA, In, DK, 8 / CT>(p, st);
+      if constexpr (DK >= 128) return launch_reduce_t<KDA, In, DK, 8>(p, st);
       return hipErrorInvalidValue;
     default: return hipErrorInvalidValue;
   }

@@ -12,6 +12,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <utility>
+
 namespace la {
 
 constexpr int kBT = 64;       // chunk length (tokens)
@@ -269,6 +271,41 @@ __device__ __forceinline__ void ds_read_tr16_async(s16x4 &r, const char *p) {
 template <int N>
 __device__ __forceinline__ void wait_lds_tied(s16x4 &a, s16x4 &b, s16x4 &c, s16x4 &d) {
   asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
+}
+template <int N, typename F>
+__device__ __forceinline__ void wait_lds_tied8(F &a, F &b, F &c, F &d, F &e, F &f, F &g, F &h) {
+  asm volatile("s_waitcnt lgkmcnt(%8)"
+               : "+v"(a), "+v"(b), "+v"(c), "+v"(d), "+v"(e), "+v"(f), "+v"(g), "+v"(h)
+               : "n"(N));
+}
+// 16-byte LDS read as opaque inline assembly (valid after a tied wait)
+__device__ __forceinline__ void ds_read_b128_async(half8 &r, const char *p) {
+  const uint32_t a = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char *)p);
+  asm volatile("ds_read_b128 %0, %1" : "=v"(r) : "v"(a));
+}
+// the same two reads at LDS byte address `a` + OFF (OFF an immediate < 64 KiB)
+template <int OFF>
+__device__ __forceinline__ void ds_read_b128_at(half8 &r, uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS immediate offset");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(a), "n"(OFF));
+}
+template <int OFF>
+__device__ __forceinline__ void ds_read_tr16_at(s16x4 &r, uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS immediate offset");
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(a), "n"(OFF));
+}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) {
+  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char *)p);
+}
+
+// compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1
+template <typename F, int... Is>
+__device__ __forceinline__ void static_for_impl(F &&f, std::integer_sequence<int, Is...>) {
+  (f(std::integral_constant<int, Is>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
 }
 __device__ __forceinline__ half8 join_half8(s16x4 lo, s16x4 hi) {
   return __builtin_shufflevector(__builtin_bit_cast(half4, lo), __builtin_bit_cast(half4, hi), 0, 1,
