@@ -26,10 +26,12 @@
 // shared, state-independent operands of a chunk are in LDS: the V slice and
 // the map stage's image of the chunk (K, Q, [K^T], Tn, M, row vectors).  Both
 // are copied one chunk ahead by direct global-to-LDS loads (no registers, no
-// LDS store instructions) into the other half of a double buffer: one
-// barrier per chunk, and the copy of chunk j + 1 overlaps the arithmetic of
-// chunk j.  V rows past the chunk's end read as zero through the buffer range
-// check, and output rows past it are dropped the same way.
+// LDS store instructions) into the other half of a double buffer, by one
+// extra wave per workgroup that does nothing else: one barrier per chunk,
+// the copy of chunk j + 1 overlaps the arithmetic of chunk j, and the
+// compute waves never block on issuing vector memory loads.  V rows past the
+// chunk's end read as zero through the buffer range check, and output rows
+// past it are dropped the same way.
 //
 // Instruction overhead is kept off the per-chunk path: every hot LDS address
 // is a per-lane pattern computed once plus an immediate offset (the chunk
@@ -53,7 +55,7 @@ namespace la {
 namespace {
 
 template <bool KDA, typename In, int DK, int NW>
-__global__ __launch_bounds__(64 * NW) void chunk_reduce_kernel(ReduceParams p) {
+__global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParams p) {
   using O = Op<In>;
   constexpr int E = (int)sizeof(typename O::T);
   constexpr ImageLayout I = image_layout(KDA, E, DK);
@@ -73,8 +75,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_reduce_kernel(ReduceParams p) {
   constexpr int STAGE = V_BYTES + I.BYTES;
   constexpr int NBUF = 2 * STAGE <= 160 * 1024 ? 2 : 1;
   constexpr int NVL = V_BYTES / 1024, NIMG = I.BYTES / 1024, NLOAD = NVL + NIMG;
-  constexpr int LPW = (NLOAD + NW - 1) / NW;  // copy pieces per wave
-  constexpr int STORES = 4 * 4;               // o stores per wave per chunk
+  (void)NLOAD;
   static_assert(I.BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "1 KiB staging pieces");
   static_assert(!F16 || IMG + I.Q + 3 * 256 * PK + 16 <= 65536, "immediate offsets");
 
@@ -91,22 +92,25 @@ __global__ __launch_bounds__(64 * NW) void chunk_reduce_kernel(ReduceParams p) {
   if (j0 == j1) return;  // empty sequence (or invalid cu_seqlens): no writes
   const int bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
   const int lane = lane_id(), w = wave_id();
+  const bool copier = w == NW;  // the extra wave only stages operands
   const int lr = lane & 15, lg = lane >> 4;
   const int cw = slice * W + 16 * w;                 // this wave's first state column
   const int rs_v = H * DV * (int)sizeof(In);         // token stride of v (bytes)
   const int rs_o = H * DV * 4;                       // token stride of o (bytes)
 
   // ---------------------------------------------------------------- staging
-  // Piece q (1 KiB) of a stage: V pieces first, then the image.  Wave w
-  // copies pieces w, w + NW, ...; a V piece's per-lane source offset (row and
-  // swizzled column piece within the chunk) does not depend on the chunk.
-  int voff[LPW];
+  // One extra wave per workgroup does all the staging: piece q (1 KiB) of a
+  // stage is V piece q for q < NVL, then image piece q - NVL.  A CU's vector
+  // memory path takes tens of cycles per piece, and a wave that issues loads
+  // blocks until they are accepted; the compute waves issue none.  A V
+  // piece's per-lane source offset (row and swizzled column piece within the
+  // chunk) does not depend on the chunk.
+  int voff[NVL];
 #pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int q = w + NW * i;
-    const int e = (q < NVL ? q : 0) * 64 + lane;  // 16-byte V piece index
+  for (int q = 0; q < NVL; ++q) {
+    const int e = q * 64 + lane;  // 16-byte V piece index
     const int row = e / PV, phys = e % PV;
-    voff[i] = q < NVL ? row * rs_v + ((phys ^ swz<PV>(row)) << 4) : lane * 16;
+    voff[q] = row * rs_v + ((phys ^ swz<PV>(row)) << 4);
   }
   const char *img_c = static_cast<const char *>(p.img) + ((size_t)j0 * H + h) * I.BYTES;
   const size_t img_step = (size_t)H * I.BYTES;
@@ -118,11 +122,9 @@ __global__ __launch_bounds__(64 * NW) void chunk_reduce_kernel(ReduceParams p) {
     const auto rv = buffer_rsrc(vrow, C * rs_v);
     char *dst = smem + buf * STAGE;
 #pragma unroll
-    for (int i = 0; i < LPW; ++i) {
-      const int q = w + NW * i;
-      if (q < NVL) copy16_to_lds(rv, dst + q * 1024, voff[i], 0);
-      else if (q < NLOAD) copy16_to_lds(ri, dst + q * 1024, lane * 16, (q - NVL) * 1024);
-    }
+    for (int q = 0; q < NVL; ++q) copy16_to_lds(rv, dst + q * 1024, voff[q], 0);
+#pragma unroll
+    for (int q = 0; q < NIMG; ++q) copy16_to_lds(ri, dst + (NVL + q) * 1024, lane * 16, q * 1024);
   };
 
   // ---------------------------------------------------------- LDS patterns
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(64 * NW) void chunk_reduce_kernel(ReduceParams p) {
   // ---------------------------------------------------------- the state
   f32x4 hacc[NHT];
   const size_t sbase = ((size_t)n * H + h) * DK * DV;
-  if (p.h0) {
+  if (p.h0 && !copier) {
 #pragma unroll
     for (int t = 0; t < NHT; ++t)
 #pragma unroll
@@ -174,12 +176,27 @@ __global__ __launch_bounds__(64 * NW) void chunk_reduce_kernel(ReduceParams p) {
   // ---------------------------------------------------------- one chunk
   // buffer BUF holds chunk jj; the copy of the next chunk, if any, goes to
   // the other buffer and is issued after the V reads
-  auto chunk = [&](auto bufc, int jj, bool first) {
+  auto chunk = [&](auto bufc, int jj) {
     constexpr int BUF = decltype(bufc)::value;
     constexpr int NXT = NBUF == 2 ? 1 - BUF : 0;
     const int r0 = bos + (jj - j0) * kBT;
     const int C = min(kBT, eos - r0);
     const bool more = jj + 1 < j1;
+    // the copier's loads of chunk jj have landed; after the barrier every
+    // compute wave is also done with chunk jj - 1, whose buffer (two
+    // buffers) the copier refills with chunk jj + 1
+    if (copier) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    __syncthreads();
+    if (copier) {
+      if (NBUF == 2 && more) copy_chunk(NXT, img_c + img_step, v_c + v_step, min(kBT, eos - r0 - kBT));
+      if constexpr (NBUF == 1) {
+        __syncthreads();  // the compute waves are done with the buffer
+        if (more) copy_chunk(0, img_c + img_step, v_c + v_step, min(kBT, eos - r0 - kBT));
+      }
+      img_c += img_step;
+      v_c += v_step;
+      return;
+    }
     const char *buf = smem + BUF * STAGE;
     const char *tV = buf;
     const char *tK = buf + IMG + I.K;
@@ -188,12 +205,6 @@ __global__ __launch_bounds__(64 * NW) void chunk_reduce_kernel(ReduceParams p) {
     const char *tTN = buf + IMG + I.TN;
     const char *tMM = buf + IMG + I.MM;
     const float *sv = reinterpret_cast<const float *>(buf + IMG + I.VEC);
-
-    // the copy of this chunk has landed: the operations issued after it are
-    // the previous chunk's STORES output stores (completion is in issue order)
-    if (first || NBUF == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(STORES));
-    __syncthreads();
 
     // ---- K H and Q H, the state as B operand straight from its accumulators
     typename O::Frag hb[NKD];
@@ -270,15 +281,6 @@ __global__ __launch_bounds__(64 * NW) void chunk_reduce_kernel(ReduceParams p) {
           x[R][e] = v - gam[R][e] * yk[R][e];
         }
       }
-    }
-
-    // ---- the copy of the next chunk, ahead of this chunk's stores
-    if constexpr (NBUF == 2) {
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-      if (more) copy_chunk(NXT, img_c + img_step, v_c + v_step, min(kBT, eos - r0 - kBT));
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
     }
 
     // ---- U = beta X + Tn X
@@ -365,25 +367,24 @@ __global__ __launch_bounds__(64 * NW) void chunk_reduce_kernel(ReduceParams p) {
       });
     }
 
-    // ---- single buffer: the copy of the next chunk once every wave is done
-    if constexpr (NBUF == 1) {
-      __syncthreads();
-      if (more) copy_chunk(0, img_c + img_step, v_c + v_step, min(kBT, eos - r0 - kBT));
-    }
+    // ---- single buffer: the copier refills it once every wave is done
+    if constexpr (NBUF == 1) __syncthreads();
+    (void)more;
+    (void)NXT;
     img_c += img_step;
     v_c += v_step;
     o_c += o_step;
   };
 
   // ---------------------------------------------------------- chunk loop
-  copy_chunk(0, img_c, v_c, min(kBT, eos - bos));
+  if (copier) copy_chunk(0, img_c, v_c, min(kBT, eos - bos));
   for (int jj = j0; jj < j1; jj += 2) {
-    chunk(std::integral_constant<int, 0>{}, jj, jj == j0);
-    if (jj + 1 < j1) chunk(std::integral_constant<int, NBUF == 2 ? 1 : 0>{}, jj + 1, false);
+    chunk(std::integral_constant<int, 0>{}, jj);
+    if (jj + 1 < j1) chunk(std::integral_constant<int, NBUF == 2 ? 1 : 0>{}, jj + 1);
   }
 
   // ---- final state slice
-  if (p.ht) {
+  if (p.ht && !copier) {
 #pragma unroll
     for (int t = 0; t < NHT; ++t)
 #pragma unroll
@@ -398,7 +399,7 @@ template <bool KDA, typename In, int DK, int NW>
 static hipError_t launch_reduce_t(const ReduceParams &p, hipStream_t st) {
   const int units = p.N_max * p.H;
   const int grid = ((units + 7) / 8) * 8 * p.S;
-  hipLaunchKernelGGL((chunk_reduce_kernel<KDA, In, DK, NW>), dim3(grid), dim3(64 * NW), 0, st, p);
+  hipLaunchKernelGGL((chunk_reduce_kernel<KDA, In, DK, NW>), dim3(grid), dim3(64 * (NW + 1)), 0, st, p);
   return hipGetLastError();
 }
 
