@@ -37,8 +37,10 @@
 // KDA (a gate vector per row): the decay sits inside the contraction,
 // (K K^T)_rs -> sum_i k_ri k_si exp(G_ri - G_si).  Off-diagonal 16-row blocks
 // (R > S) factor it through the first row b of block R,
-// k_ri exp(G_ri - G_bi) * k_si exp(G_bi - G_si), both factors <= 1 when g <= 0;
-// the four diagonal 16x16 blocks are summed elementwise in fp32.  The KDA map
+// k_ri exp(G_ri - G_bi) * k_si exp(G_bi - G_si), both factors <= 1 when g <= 0,
+// formed in registers as MFMA operands.  The four diagonal 16x16 blocks factor
+// through their own first row in fp32 (one factor grows, so a block whose
+// decay exceeds e^60 in some channel is summed elementwise).  The KDA map
 // writes the decayed operands in place of K and Q, K*exp(G) and Q*exp(G), and
 // (K*exp(G_C - G))^T (chunk rows in chained order), and exp(G_C) as the state
 // decay, so the reduce does no gate work.
@@ -74,11 +76,10 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   __shared__ float sY[4][16 * 17];    // per-wave 16x16 scratch
   __shared__ float sB[kBT];
   __shared__ float sg[kBT];
-  // KDA: per-channel cumulative gate and the decayed operands of one block row
-  __shared__ float sG[KDA ? kBT * DK : 1];
-  __shared__ __attribute__((aligned(16))) T sKr[KDA ? 16 * LDK : 1];
-  __shared__ __attribute__((aligned(16))) T sQr[KDA ? 16 * LDK : 1];
-  __shared__ __attribute__((aligned(16))) T sKs[KDA ? 48 * LDK : 1];
+  // KDA: per-channel cumulative gate (rows padded so that 16 rows at one
+  // channel hit distinct banks)
+  constexpr int GS = DK + 4;
+  __shared__ float sG[KDA ? kBT * GS : 1];
   constexpr int LDM = kBT + O::PAD;  // M, natural column order, before the write-out
   __shared__ __attribute__((aligned(16))) T sMt[kBT * LDM];
   T *sK = reinterpret_cast<T *>(sArea);
@@ -221,7 +222,7 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
 #pragma unroll
       for (int it = 0; it < GIT; ++it) {
         const int idx = tid + it * kThreads;
-        *reinterpret_cast<float4 *>(sG + idx * 4) = graw[it];
+        *reinterpret_cast<float4 *>(sG + (idx / (DK / 4)) * GS + (idx % (DK / 4)) * 4) = graw[it];
       }
     }
   }
@@ -303,15 +304,15 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
       const int c = tid % DK, sgi = tid / DK;
       float run = 0.f;
       for (int r = sgi * RPS; r < (sgi + 1) * RPS; ++r) {
-        run += sG[r * DK + c];
-        sG[r * DK + c] = run;
+        run += sG[r * GS + c];
+        sG[r * GS + c] = run;
       }
       __syncthreads();
       float off = 0.f;
-      for (int s2 = 0; s2 < sgi; ++s2) off += sG[((s2 + 1) * RPS - 1) * DK + c];
+      for (int s2 = 0; s2 < sgi; ++s2) off += sG[((s2 + 1) * RPS - 1) * GS + c];
       __syncthreads();
       if (sgi > 0)
-        for (int r = sgi * RPS; r < (sgi + 1) * RPS; ++r) sG[r * DK + c] += off;
+        for (int r = sgi * RPS; r < (sgi + 1) * RPS; ++r) sG[r * GS + c] += off;
       __syncthreads();
     }
     // decayed operands for the reduce, in chained order
@@ -322,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
 #pragma unroll
         for (int e = 0; e < CH; ++e) {
           const int c = kidx<O>(pc * CH + e);
-          const float f = __expf(sG[r * DK + c]);
+          const float f = __expf(sG[r * GS + c]);
           kv[e] = (T)((float)sK[r * LDK + c] * f);
           qv[e] = (T)((float)sQ[r * LDK + c] * f);
         }
@@ -331,12 +332,12 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
       }
       for (int idx = tid; idx < DK * PT; idx += kThreads) {
         const int c = idx / PT, pc = idx % PT;
-        const float GC = sG[(kBT - 1) * DK + c];
+        const float GC = sG[(kBT - 1) * GS + c];
         T v[CH];
 #pragma unroll
         for (int e = 0; e < CH; ++e) {
           const int r = kidx<O>(pc * CH + e);
-          v[e] = (T)((float)sK[r * LDK + c] * __expf(GC - sG[r * DK + c]));
+          v[e] = (T)((float)sK[r * LDK + c] * __expf(GC - sG[r * GS + c]));
         }
         put(I.KT, PT, c, pc, v);
       }
@@ -345,62 +346,101 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
         vec[64 + tid] = 1.f;
         vec[128 + tid] = sB[tid];
       }
-      for (int d = tid; d < DK; d += kThreads) vec[192 + d] = __expf(sG[(kBT - 1) * DK + d]);
+      for (int d = tid; d < DK; d += kThreads) vec[192 + d] = __expf(sG[(kBT - 1) * GS + d]);
     }
-    // off-diagonal blocks: for block row R, reference row b = 16R
-    for (int R = 1; R < 4; ++R) {
-      const int b = 16 * R;
-      for (int idx = tid; idx < (16 + b) * DK; idx += kThreads) {
-        const int r = idx / DK, c = idx % DK;
-        const float Gb = sG[b * DK + c];
-        if (r < 16) {
-          const int rr = b + r;
-          const float f = __expf(sG[rr * DK + c] - Gb);
-          sKr[r * LDK + c] = (T)((float)sK[rr * LDK + c] * f);
-          sQr[r * LDK + c] = (T)((float)sQ[rr * LDK + c] * f);
-        } else {
-          const int ss = r - 16;
-          const float f = __expf(Gb - sG[ss * DK + c]);
-          sKs[ss * LDK + c] = (T)((float)sK[ss * LDK + c] * f);
+    // off-diagonal 16x16 tiles (R, S), S < R, wave w taking tiles w and
+    // w + 4 of (1,0) (2,0) (2,1) (3,0) (3,1) (3,2): the decay of pair (r, s)
+    // factors through row b = 16R per channel,
+    //   k_rc e^{G_rc - G_bc} * k_sc e^{G_bc - G_sc},
+    // both factors <= 1 when g <= 0.  Each lane forms its row's KPL channels
+    // of both factors in registers (lane row r = b + lr for the A operands,
+    // s = 16S + lr for the B operand) and feeds them to the MFMAs.
+    for (int t = w; t < 6; t += 4) {
+      const int R = t < 1 ? 1 : t < 3 ? 2 : 3, S = t - R * (R - 1) / 2;
+      const int b = 16 * R, r = b + lr, s = 16 * S + lr;
+      f32x4 ca = zero4(), cm = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < DK; k0 += KSTEP) {
+        const int c = k0 + lg * O::KPL;
+        float fk[O::KPL], fq[O::KPL], hs[O::KPL];
+#pragma unroll
+        for (int e = 0; e < O::KPL; ++e) {
+          const float gb = sG[b * GS + c + e];
+          const float er = __expf(sG[r * GS + c + e] - gb);
+          const float es = __expf(gb - sG[s * GS + c + e]);
+          fk[e] = (float)sK[r * LDK + c + e] * er;
+          fq[e] = (float)sQ[r * LDK + c + e] * er;
+          hs[e] = (float)sK[s * LDK + c + e] * es;
         }
-      }
-      __syncthreads();
-      for (int t = w; t < 2 * R; t += 4) {  // tiles (R, S), S < R: A part then M part
-        const int S = t % R;
-        const bool isM = t >= R;
-        const T *src = isM ? sQr : sKr;
-        f32x4 c = zero4();
-#pragma unroll
-        for (int k0 = 0; k0 < DK; k0 += KSTEP)
-          c = O::mfma(frag_lds<O>(src, LDK, 0, k0, lane), frag_lds<O>(sKs, LDK, 16 * S, k0, lane),
-                      c);
-        if (isM) {
-          store_m(R, S, c);
+        typename O::Frag af, qf, hf;
+        if constexpr (O::KPL == 1) {
+          af = fk[0];
+          qf = fq[0];
+          hf = hs[0];
         } else {
-          const int s = 16 * S + lr;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = b + lg * 4 + e;
-            sL[r * LDL + s] = sB[r] * c[e];
+          for (int e = 0; e < O::KPL; ++e) {
+            af[e] = (T)fk[e];
+            qf[e] = (T)fq[e];
+            hf[e] = (T)hs[e];
           }
         }
+        ca = O::mfma(af, hf, ca);
+        cm = O::mfma(qf, hf, cm);
       }
-      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = b + lg * 4 + e;
+        sL[rr * LDL + s] = sB[rr] * ca[e];
+      }
+      store_m(R, S, cm);
     }
-    // diagonal blocks, elementwise in fp32: 4 blocks x 16 x 16 (r, s) pairs
-    for (int idx = tid; idx < 4 * 256; idx += kThreads) {
-      const int blk = idx >> 8, r = 16 * blk + ((idx >> 4) & 15), s = 16 * blk + (idx & 15);
-      float a = 0.f, m = 0.f;
-      if (s <= r) {
-        for (int c = 0; c < DK; ++c) {
-          const float e = __expf(sG[r * DK + c] - sG[s * DK + c]);
-          const float ks = (float)sK[s * LDK + c];
-          a += (float)sK[r * LDK + c] * ks * e;
-          m += (float)sQ[r * LDK + c] * ks * e;
+    // diagonal blocks: wave w takes block w (rows b .. b+15).  The decay of
+    // pair (r, s) factors through row b per channel,
+    //   k_rc e^{G_rc - G_bc} * k_sc e^{G_bc - G_sc},
+    // so both products are fp32 MFMAs (k = channel; lane row r supplies the
+    // A value of row r and the B value of column r).  The second factor grows
+    // with the block's decay: a block where some |G_rc - G_bc| exceeds 60 is
+    // summed elementwise instead, so no factor leaves the fp32 range.
+    {
+      const int b = 16 * w, r = b + lr;
+      f32x4 ca = zero4(), cm = zero4();
+      float span = 0.f;
+#pragma unroll 4
+      for (int c0 = 0; c0 < DK; c0 += 4) {
+        const int c = c0 + lg;
+        const float d = sG[r * GS + c] - sG[b * GS + c];
+        span = fmaxf(span, fabsf(d));
+        const float e1 = __expf(d), e2 = __expf(-d);
+        const float kr = (float)sK[r * LDK + c], qr = (float)sQ[r * LDK + c];
+        const float hs = kr * e2;
+        ca = F32::mfma(kr * e1, hs, ca);
+        cm = F32::mfma(qr * e1, hs, cm);
+      }
+      const int s = b + lr;
+      if (__ballot(span > 60.f) == 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = b + lg * 4 + e;
+          sL[rr * LDL + s] = s < rr ? sB[rr] * ca[e] : 0.f;
+          sMt[rr * LDM + s] = s <= rr ? (T)cm[e] : (T)0.f;
+        }
+      } else {
+        for (int idx = lane; idx < 256; idx += 64) {
+          const int rr = b + (idx >> 4), ss = b + (idx & 15);
+          float a = 0.f, m = 0.f;
+          if (ss <= rr) {
+            for (int c = 0; c < DK; ++c) {
+              const float e = __expf(sG[rr * GS + c] - sG[ss * GS + c]);
+              const float ks = (float)sK[ss * LDK + c];
+              a += (float)sK[rr * LDK + c] * ks * e;
+              m += (float)sQ[rr * LDK + c] * ks * e;
+            }
+          }
+          sL[rr * LDL + ss] = ss < rr ? sB[rr] * a : 0.f;
+          sMt[rr * LDM + ss] = (T)m;
         }
       }
-      sL[r * LDL + s] = s < r ? sB[r] * a : 0.f;
-      sMt[r * LDM + s] = (T)m;
     }
   }
   __syncthreads();

@@ -188,6 +188,30 @@ def test_config2_kda_full():
     assert eo <= tol and eh <= tol
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_kda_strong_channel_decay(dtype):
+    """KDA with some channels decaying hard: per-token g = -4.5 gives a
+    16-row decay of e^-67 (past the range where the map factors diagonal
+    blocks through their first row, so they are summed elementwise), g = -3.5
+    gives e^-52 (factored, with factors up to e^52).  Head 0 keeps the usual
+    gates; other channels of heads 1 and 2 too."""
+    d = 128 if dtype == "bf16" else 64
+    cu = [0, 50, 64, 200, 333]
+    inp = make_inputs(cu[-1], 3, d, d, kda=True, dtype=dtype, seed=91, cu_seqlens=cu,
+                      h0_std=0.1)
+    g = inp["g"]
+    g[:, 1, 0:8] = -4.5
+    g[:, 1, 40:41] = -20.0
+    g[:, 2, 3:11] = -3.5
+    g[100:140, 2, 20] = -3.0
+    o, ht, _ = run_gpu(inp)
+    o_ref, ht_ref = run_oracle(inp)
+    eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref)
+    _say(f"kda strong decay {dtype}: o {eo:.2e} ht {eh:.2e}")
+    assert np.isfinite(o.cpu().numpy()[:cu[-1]]).all()
+    assert eo <= tol and eh <= tol
+
+
 @pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
 def test_config4_short(kda):
     inp = config(4, kda=kda, T=2048)
