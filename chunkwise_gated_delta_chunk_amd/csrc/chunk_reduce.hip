@@ -81,13 +81,34 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
 
   __shared__ __attribute__((aligned(16))) char smem[NBUF * STAGE];
 
-  // ---- block -> (unit, slice), XCD-aware
+  // ---- block -> (unit, slice), XCD-aware: the slices of one unit share an
+  // XCD (and its L2, which then serves the image to all of them)
   const int b = blockIdx.x;
   const int xcd = b & 7, kk = b >> 3;
   const int slice = kk % p.S, unit = (kk / p.S) * 8 + xcd;
   const int H = p.H;
   if (unit >= p.N_max * H) return;
-  const int n = unit / H, h = unit % H;
+  const int rank = unit / H, h = unit % H;
+  // Units go out longest sequence first, so that when there are more
+  // workgroups than CUs the ones on the critical path start in the first
+  // round: unit u takes the sequence of rank u / H by decreasing chunk count
+  // (ties by index).  Up to 64 sequences every wave ranks them by itself,
+  // lane m holding sequence m, with no LDS and no barrier; empty sequences
+  // rank last, so their units leave at once.  Beyond 64 sequences the
+  // natural order is kept.
+  int n = rank;
+  if (p.N_max <= 64) {
+    const int m = lane_id();
+    int len = -1;
+    if (m < p.N_max) len = p.chunk_offsets[m + 1] - p.chunk_offsets[m];
+    if (rank >= __popcll(__ballot(len > 0))) return;
+    int r = 0;
+    for (int i = 0; i < p.N_max; ++i) {
+      const int li = __builtin_amdgcn_readlane(len, i);
+      r += (li > len) | ((li == len) & (i < m));
+    }
+    n = __builtin_ctzll(__ballot(r == rank));
+  }
   const int j0 = p.chunk_offsets[n], j1 = p.chunk_offsets[n + 1];
   if (j0 == j1) return;  // empty sequence (or invalid cu_seqlens): no writes
   const int bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
@@ -132,6 +153,8 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
   uint32_t aK[NBUF][F16 ? NKD : 1];      // A fragment, row tile 0, k-step s (K; Q at +I.Q - I.K)
   uint32_t aT[NBUF][F16 ? NHT / 2 : 1];  // transposed K^T reads, tile pair t / 2
   uint32_t aV[NBUF];                     // transposed V reads, row tile 0
+  uint32_t aP[NBUF][2];                  // Tn fragments, row tile 0, k-step s (M at +I.MM - I.TN)
+  uint32_t aS[NBUF];                     // row vectors, rows 4 lg .. 4 lg + 3
   const uint32_t base = lds_addr(smem);
 #pragma unroll
   for (int bf = 0; bf < NBUF; ++bf) {
@@ -142,6 +165,9 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
       const int row = 4 * lg + (lr >> 2);
 #pragma unroll
       for (int u = 0; u < NHT / 2; ++u) aT[bf][u] = b0 + tile_off<PK>(row, 4 * u + (lr & 3));
+#pragma unroll
+      for (int s = 0; s < 2; ++s) aP[bf][s] = b0 + IMG + I.TN + tile_off<PT>(lr, 4 * s + lg);
+      aS[bf] = b0 + IMG + I.VEC + 16 * lg;
     }
     if constexpr (sizeof(In) == 2) {
       // lane i of a 16-lane group reads row 4 lg + i / 4 at columns
@@ -176,27 +202,35 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
   // ---------------------------------------------------------- one chunk
   // buffer BUF holds chunk jj; the copy of the next chunk, if any, goes to
   // the other buffer and is issued after the V reads
+  // The copier and the compute waves run separate loops with the same
+  // barriers.  At the barrier opening chunk jj the copier's loads of chunk
+  // jj have landed and every compute wave is done with chunk jj - 1, whose
+  // buffer (two buffers) the copier then refills with chunk jj + 1.  Every
+  // LDS read of a compute wave is waited for inside its chunk, so that
+  // barrier needs no fence, and the compute waves' output stores stay in
+  // flight across it.
+  auto chunk_barrier = [&]() {
+    if constexpr (NBUF == 2) barrier_lds();
+    else __syncthreads();
+  };
+  auto copy_step = [&](int jj) {
+    const int r0 = bos + (jj - j0) * kBT;
+    const bool more = jj + 1 < j1;
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+    chunk_barrier();
+    if (NBUF == 2 && more) copy_chunk(1 - ((jj - j0) & 1), img_c + img_step, v_c + v_step, min(kBT, eos - r0 - kBT));
+    if constexpr (NBUF == 1) {
+      __syncthreads();  // the compute waves are done with the buffer
+      if (more) copy_chunk(0, img_c + img_step, v_c + v_step, min(kBT, eos - r0 - kBT));
+    }
+    img_c += img_step;
+    v_c += v_step;
+  };
   auto chunk = [&](auto bufc, int jj) {
     constexpr int BUF = decltype(bufc)::value;
-    constexpr int NXT = NBUF == 2 ? 1 - BUF : 0;
     const int r0 = bos + (jj - j0) * kBT;
     const int C = min(kBT, eos - r0);
-    const bool more = jj + 1 < j1;
-    // the copier's loads of chunk jj have landed; after the barrier every
-    // compute wave is also done with chunk jj - 1, whose buffer (two
-    // buffers) the copier refills with chunk jj + 1
-    if (copier) __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();
-    if (copier) {
-      if (NBUF == 2 && more) copy_chunk(NXT, img_c + img_step, v_c + v_step, min(kBT, eos - r0 - kBT));
-      if constexpr (NBUF == 1) {
-        __syncthreads();  // the compute waves are done with the buffer
-        if (more) copy_chunk(0, img_c + img_step, v_c + v_step, min(kBT, eos - r0 - kBT));
-      }
-      img_c += img_step;
-      v_c += v_step;
-      return;
-    }
+    chunk_barrier();
     const char *buf = smem + BUF * STAGE;
     const char *tV = buf;
     const char *tK = buf + IMG + I.K;
@@ -253,21 +287,123 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
         }
     }
 
-    // ---- X = V - gamma (K H); V rows past the chunk's end were staged as zero
+    // ---- X = V - gamma (K H); U = beta X + Tn X; O = scale (gamma (Q H) + M U).
+    // V rows past the chunk's end were staged as zero; output rows past it
+    // are dropped by the range check of the per-tile output resource.
     f32x4 gam[4], x[4];
-    if constexpr (sizeof(In) == 2) {
+    typename O::Frag ufr[NKR], ubf[NKR];
+    s16x4 tr[F16 && !HAS_KT ? NHT : 1][4];
+    float gdec = 0.f;
+    if constexpr (F16) {
+      // Every LDS read of these phases is issued ahead of its first use as
+      // inline assembly and waited for with its registers tied (LDS
+      // operations complete in order): V, gamma and the six Tn fragments;
+      // beta, the update factors and the state decay while X forms; the six
+      // M fragments while U's products run; the K^T reads of the update in
+      // two halves around the output.  Fragment i of Tn and M is
+      // (row tile, k-step) = (0,0) (1,0) (2,0) (2,1) (3,0) (3,1).
+      constexpr auto fR = [](int i) { return i < 2 ? i : (i + 2) / 2; };
+      constexpr auto fS = [](int i) { return i < 2 ? 0 : (i & 1); };
+      constexpr int DMM = I.MM - I.TN;
       s16x4 vr[4];
+      half8 ft[6], fm[6];
+      f32x4 bet[4], fac[4], dcv;
       static_for<4>([&](auto rc) {
         constexpr int R = decltype(rc)::value;
         ds_read_tr16_at<R * 256 * PV>(vr[R], aV[BUF]);
       });
-      wait_lds_tied<0>(vr[0], vr[1], vr[2], vr[3]);
+      static_for<4>([&](auto rc) {
+        constexpr int R = decltype(rc)::value;
+        ds_read_b128_at<64 * R>(gam[R], aS[BUF]);
+      });
+      static_for<6>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        ds_read_b128_at<fR(i) * 256 * PT>(ft[i], aP[BUF][fS(i)]);
+      });
+      wait_lds_tied<6>(vr[0], vr[1], vr[2], vr[3]);
+      wait_lds_tied4<6>(gam[0], gam[1], gam[2], gam[3]);
 #pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        gam[R] = *reinterpret_cast<const f32x4 *>(sv + 16 * R + lg * 4);
+      for (int R = 0; R < 4; ++R)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           x[R][e] = __uint_as_float((uint32_t)(uint16_t)vr[R][e] << 16) - gam[R][e] * yk[R][e];
+      static_for<4>([&](auto rc) {
+        constexpr int R = decltype(rc)::value;
+        ds_read_b128_at<512 + 64 * R>(bet[R], aS[BUF]);
+        if constexpr (!KDA) ds_read_b128_at<256 + 64 * R>(fac[R], aS[BUF]);
+      });
+      if constexpr (!HAS_KT) ds_read_b128_at<768>(dcv, aS[BUF]);
+      constexpr int AFTER_TN = (KDA ? 4 : 8) + (HAS_KT ? 0 : 1);
+      typename O::Frag xb[NKR];
+#pragma unroll
+      for (int s = 0; s < NKR; ++s) xb[s] = b_frag<O>(x, s);
+      wait_lds_tied2<AFTER_TN>(ft[0], ft[1]);
+      wait_lds_tied4<AFTER_TN>(ft[2], ft[3], ft[4], ft[5]);
+      f32x4 u[4], ub[4];
+#pragma unroll
+      for (int R = 0; R < 4; ++R) u[R] = zero4();
+      static_for<6>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        u[fR(i)] = O::mfma(ft[i], xb[fS(i)], u[fR(i)]);
+      });
+      static_for<6>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        ds_read_b128_at<DMM + fR(i) * 256 * PT>(fm[i], aP[BUF][fS(i)]);
+      });
+      wait_lds_tied4<6>(bet[0], bet[1], bet[2], bet[3]);
+      if constexpr (!KDA) wait_lds_tied4<6>(fac[0], fac[1], fac[2], fac[3]);
+      if constexpr (!HAS_KT) {
+        wait_lds_tied1<6>(dcv);
+        gdec = dcv[0];
+      }
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) u[R][e] += bet[R][e] * x[R][e];
+        if constexpr (!KDA)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ub[R][e] = fac[R][e] * u[R][e];
+      }
+#pragma unroll
+      for (int s = 0; s < NKR; ++s) {
+        ufr[s] = b_frag<O>(u, s);
+        if constexpr (KDA) ubf[s] = ufr[s];
+        else ubf[s] = b_frag<O>(ub, s);
+      }
+      wait_lds_tied2<0>(fm[0], fm[1]);
+      wait_lds_tied4<0>(fm[2], fm[3], fm[4], fm[5]);
+      // the transposed K^T reads of the update (GDN), first half
+      auto read_kt = [&](auto t0c) {
+        constexpr int T0 = decltype(t0c)::value;
+        static_for<NHT / 2>([&](auto tc) {
+          constexpr int t = T0 + decltype(tc)::value;
+          static_for<4>([&](auto qc) {
+            constexpr int q = decltype(qc)::value;  // (k-step, half) = (q / 2, q % 2)
+            constexpr int OFF = IMG + I.K + (32 * (q >> 1) + 16 * (q & 1)) * 16 * PK + 8 * (t & 1);
+            ds_read_tr16_at<OFF>(tr[t][q], aT[BUF][t >> 1]);
+          });
+        });
+      };
+      if constexpr (!HAS_KT) {
+        static_assert(NKR == 2, "two k-steps over the chunk rows");
+        read_kt(std::integral_constant<int, 0>{});
+      }
+      f32x4 oa[4];
+#pragma unroll
+      for (int R = 0; R < 4; ++R)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) oa[R][e] = gam[R][e] * yq[R][e];
+      static_for<6>([&](auto ic) {
+        constexpr int i = decltype(ic)::value;
+        oa[fR(i)] = O::mfma(fm[i], ufr[fS(i)], oa[fR(i)]);
+      });
+      if constexpr (!HAS_KT) read_kt(std::integral_constant<int, NHT / 2>{});
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        const auto ro = buffer_rsrc(o_c + (size_t)16 * R * H * DV, (C - 16 * R) * rs_o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p.scale * oa[R][e]), ro, off_o[e], 0, 0);
       }
     } else {
       const int col = 16 * w + lr;
@@ -281,64 +417,43 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
           x[R][e] = v - gam[R][e] * yk[R][e];
         }
       }
-    }
-
-    // ---- U = beta X + Tn X
-    typename O::Frag xb[NKR];
+      typename O::Frag xb[NKR];
 #pragma unroll
-    for (int s = 0; s < NKR; ++s) xb[s] = b_frag<O>(x, s);
-    f32x4 u[4], ub[4];
+      for (int s = 0; s < NKR; ++s) xb[s] = b_frag<O>(x, s);
+      f32x4 u[4], ub[4];
 #pragma unroll
-    for (int R = 0; R < 4; ++R) {
-      const f32x4 bet = *reinterpret_cast<const f32x4 *>(sv + 128 + 16 * R + lg * 4);
+      for (int R = 0; R < 4; ++R) {
+        const f32x4 bet = *reinterpret_cast<const f32x4 *>(sv + 128 + 16 * R + lg * 4);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) u[R][e] = bet[e] * x[R][e];
+        for (int e = 0; e < 4; ++e) u[R][e] = bet[e] * x[R][e];
 #pragma unroll
-      for (int s = 0; s < ksteps_lower<O>(R); ++s)
-        u[R] = O::mfma(a_frag_img<O, PT>(tTN, 16 * R, s, lane), xb[s], u[R]);
-      if constexpr (!KDA) {
-        const f32x4 fac = *reinterpret_cast<const f32x4 *>(sv + 64 + 16 * R + lg * 4);
+        for (int s = 0; s < ksteps_lower<O>(R); ++s)
+          u[R] = O::mfma(a_frag_img<O, PT>(tTN, 16 * R, s, lane), xb[s], u[R]);
+        if constexpr (!KDA) {
+          const f32x4 fac = *reinterpret_cast<const f32x4 *>(sv + 64 + 16 * R + lg * 4);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) ub[R][e] = fac[e] * u[R][e];
+          for (int e = 0; e < 4; ++e) ub[R][e] = fac[e] * u[R][e];
+        }
       }
-    }
-    typename O::Frag ufr[NKR], ubf[NKR];
 #pragma unroll
-    for (int s = 0; s < NKR; ++s) {
-      ufr[s] = b_frag<O>(u, s);
-      if constexpr (KDA) ubf[s] = ufr[s];
-      else ubf[s] = b_frag<O>(ub, s);
-    }
-
-    // ---- the transposed K^T reads of the update (fp16 GDN), issued ahead
-    // of the output's arithmetic
-    s16x4 tr[F16 && !HAS_KT ? NHT : 1][4];
-    if constexpr (F16 && !HAS_KT) {
-      static_assert(NKR == 2, "two k-steps over the chunk rows");
-      static_for<NHT>([&](auto tc) {
-        constexpr int t = decltype(tc)::value;
-        static_for<4>([&](auto qc) {
-          constexpr int q = decltype(qc)::value;  // (k-step, half) = (q / 2, q % 2)
-          constexpr int OFF = IMG + I.K + (32 * (q >> 1) + 16 * (q & 1)) * 16 * PK + 8 * (t & 1);
-          ds_read_tr16_at<OFF>(tr[t][q], aT[BUF][t >> 1]);
-        });
-      });
-    }
-
-    // ---- O = scale (gamma (Q H) + M U); rows past the chunk's end are
-    // dropped by the range check of the per-tile output resource
+      for (int s = 0; s < NKR; ++s) {
+        ufr[s] = b_frag<O>(u, s);
+        if constexpr (KDA) ubf[s] = ufr[s];
+        else ubf[s] = b_frag<O>(ub, s);
+      }
 #pragma unroll
-    for (int R = 0; R < 4; ++R) {
-      f32x4 oa;
+      for (int R = 0; R < 4; ++R) {
+        f32x4 oa;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) oa[e] = gam[R][e] * yq[R][e];
+        for (int e = 0; e < 4; ++e) oa[e] = gam[R][e] * yq[R][e];
 #pragma unroll
-      for (int s = 0; s < ksteps_lower<O>(R); ++s)
-        oa = O::mfma(a_frag_img<O, PT>(tMM, 16 * R, s, lane), ufr[s], oa);
-      const auto ro = buffer_rsrc(o_c + (size_t)16 * R * H * DV, (C - 16 * R) * rs_o);
+        for (int s = 0; s < ksteps_lower<O>(R); ++s)
+          oa = O::mfma(a_frag_img<O, PT>(tMM, 16 * R, s, lane), ufr[s], oa);
+        const auto ro = buffer_rsrc(o_c + (size_t)16 * R * H * DV, (C - 16 * R) * rs_o);
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p.scale * oa[e]), ro, off_o[e], 0, 0);
+        for (int e = 0; e < 4; ++e)
+          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p.scale * oa[e]), ro, off_o[e], 0, 0);
+      }
     }
 
     // ---- H <- decay H + Kbar^T Ubar
@@ -353,7 +468,6 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
           hacc[t] = O::mfma(a_frag_img<O, PT>(tKT, 16 * t, s, lane), ubf[s], hacc[t]);
       }
     } else {
-      const float gdec = sv[192];
       static_for<NHT>([&](auto tc) {
         constexpr int t = decltype(tc)::value;
         // outstanding after tile t's reads: those of the later tiles
@@ -369,18 +483,23 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
 
     // ---- single buffer: the copier refills it once every wave is done
     if constexpr (NBUF == 1) __syncthreads();
-    (void)more;
-    (void)NXT;
-    img_c += img_step;
-    v_c += v_step;
     o_c += o_step;
   };
 
   // ---------------------------------------------------------- chunk loop
-  if (copier) copy_chunk(0, img_c, v_c, min(kBT, eos - bos));
-  for (int jj = j0; jj < j1; jj += 2) {
+  if (copier) {
+    copy_chunk(0, img_c, v_c, min(kBT, eos - bos));
+    for (int jj = j0; jj < j1; ++jj) copy_step(jj);
+    return;
+  }
+  // two chunks per trip, one per buffer; leaving through the breaks keeps a
+  // single path into the loop header, so the state accumulators keep their
+  // registers from trip to trip
+  for (int jj = j0;;) {
     chunk(std::integral_constant<int, 0>{}, jj);
-    if (jj + 1 < j1) chunk(std::integral_constant<int, NBUF == 2 ? 1 : 0>{}, jj + 1);
+    if (++jj == j1) break;
+    chunk(std::integral_constant<int, NBUF == 2 ? 1 : 0>{}, jj);
+    if (++jj == j1) break;
   }
 
   // ---- final state slice

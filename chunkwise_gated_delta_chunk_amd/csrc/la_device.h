@@ -290,10 +290,34 @@ __device__ __forceinline__ void ds_read_b128_at(half8 &r, uint32_t a) {
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(a), "n"(OFF));
 }
 template <int OFF>
+__device__ __forceinline__ void ds_read_b128_at(f32x4 &r, uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS immediate offset");
+  asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(a), "n"(OFF));
+}
+// waits as wait_lds_tied, for other register counts and types
+template <int N, typename F>
+__device__ __forceinline__ void wait_lds_tied4(F &a, F &b, F &c, F &d) {
+  asm volatile("s_waitcnt lgkmcnt(%4)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d) : "n"(N));
+}
+template <int N, typename F>
+__device__ __forceinline__ void wait_lds_tied1(F &a) {
+  asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(a) : "n"(N));
+}
+template <int N, typename F>
+__device__ __forceinline__ void wait_lds_tied2(F &a, F &b) {
+  asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(a), "+v"(b) : "n"(N));
+}
+template <int OFF>
 __device__ __forceinline__ void ds_read_tr16_at(s16x4 &r, uint32_t a) {
   static_assert(OFF >= 0 && OFF < 65536, "DS immediate offset");
   asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(a), "n"(OFF));
 }
+// Workgroup barrier without the release fence of __syncthreads: a wave's
+// pending global stores are not waited for.  The caller orders LDS itself:
+// its own LDS reads must have been waited for, and direct-to-LDS loads that
+// others read after the barrier must have completed (vmcnt) in the issuing
+// wave.  The memory clobber keeps the compiler's memory accesses in place.
+__device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
 __device__ __forceinline__ uint32_t lds_addr(const void *p) {
   return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char *)p);
 }

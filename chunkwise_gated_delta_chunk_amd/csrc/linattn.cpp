@@ -10,6 +10,7 @@
 namespace {
 
 constexpr int kBTSupported = 64;
+constexpr int kCUs = 256;  // compute units of one MI355X
 
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
@@ -40,8 +41,13 @@ int check_shape(const la_chunk_fwd_args *a) {
 
 int split_for(const la_chunk_fwd_args *a) {
   if (a->dv_split) return a->dv_split;
-  // 64 state columns per workgroup
-  return a->d_v / 64;
+  // 64 state columns per workgroup (four compute waves); when that leaves at
+  // most one workgroup per CU, 32 columns (two compute waves), which run a
+  // chunk faster: the sequences' serial chains then bound the time, not the
+  // total work
+  const int s = a->d_v / 64 > 0 ? a->d_v / 64 : 1;
+  if ((int64_t)a->N_max * a->H * s <= kCUs && a->d_v / (2 * s) >= 32) return 2 * s;
+  return s;
 }
 
 size_t elem_bytes(const la_chunk_fwd_args *a) { return a->qkv_dtype == LA_BF16 ? 2 : 4; }

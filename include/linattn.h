@@ -103,7 +103,9 @@ typedef struct {
     int32_t BT;                /* chunk size: 64                                 */
     int32_t qkv_dtype;         /* LA_BF16 or LA_F32: dtype of q, k, v            */
     int32_t dv_split;          /* state column slices per (seq, head): 0 = auto, */
-                               /* else 1, 2 or 4 with d_v / dv_split >= 32       */
+                               /* else 1, 2 or 4 with d_v / dv_split >= 32.      */
+                               /* auto: d_v / 64 slices, twice that when         */
+                               /* N_max * H * (d_v / 64) <= 256 (the CU count)   */
     float scale;               /* o = scale * S q                                */
     const void *q, *k, *v;     /* [T_max][H][d_k] / [T_max][H][d_v], qkv_dtype   */
     const float *g;            /* log-decay: GDN [T_max][H]; KDA [T_max][H][d_k] */

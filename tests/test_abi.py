@@ -123,7 +123,12 @@ def test_workspace_size_and_split():
         kda = 2 * 64 * d * esz + kt + 2 * 64 * 64 * esz + vec
         assert la.workspace_bytes(T, N, H, d, d, dt, kda=True) == cells * kda
     assert la.workspace_bytes(0, 1, 1, 64, 64, torch.bfloat16) == 0
-    assert la.dv_split_for(8192, 8, 16, 128, 128, torch.bfloat16) == 2
+    # 64 columns per workgroup, 32 when that leaves at most one workgroup per
+    # CU (256 of them)
+    assert la.dv_split_for(8192, 8, 16, 128, 128, torch.bfloat16) == 4
+    assert la.dv_split_for(8192, 8, 17, 128, 128, torch.bfloat16) == 2
     assert la.dv_split_for(16384, 64, 32, 128, 128, torch.bfloat16) == 2
-    assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32) == 1
-    assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32, dv_split=2) == 2
+    assert la.dv_split_for(65536, 1, 10, 128, 128, torch.bfloat16) == 4
+    assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32) == 2
+    assert la.dv_split_for(4096, 512, 2, 64, 64, torch.float32) == 1
+    assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32, dv_split=1) == 1
