@@ -149,9 +149,9 @@ def bench_bucket(args, torch, la, synth, dev):
     st = torch.empty((1,), dtype=torch.int32, device=dev)
     o = torch.empty((T_max, H, d), device=dev)
     ht = torch.empty((N_max, H, d, d), device=dev)
-    ws = torch.empty((la.workspace_bytes(T_max, N_max, H, d, d, bf, False),), dtype=torch.uint8,
-                     device=dev)
-    kw = dict(o=o, ht=ht, workspace=ws, dv_split=args.dv_split)
+    ws = torch.empty((la.workspace_bytes(T_max, N_max, H, d, d, bf, False, seg_len=args.seg_len),),
+                     dtype=torch.uint8, device=dev)
+    kw = dict(o=o, ht=ht, workspace=ws, dv_split=args.dv_split, seg_len=args.seg_len)
 
     def fill(inp):
         for t, key in ((q, "q"), (k, "k"), (v, "v")):
@@ -232,6 +232,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="c1", choices=sorted(WORKLOADS))
     ap.add_argument("--dv-split", type=int, default=0)
+    ap.add_argument("--seg-len", type=int, default=0,
+                    help="chunks per segment of the reduce (0 auto, -1 one pass per sequence)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--layouts", type=int, default=20, help="bucket layouts (c3 only)")
     ap.add_argument("--copy-calibration", type=int, default=0,
@@ -285,10 +287,12 @@ def main():
     st = torch.empty((1,), dtype=torch.int32, device=dev)
     o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
     ht = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    ws = torch.empty((la.workspace_bytes(T, N, H, dk, dv, tdt, bool(inp["kda"])),),
+    ws = torch.empty((la.workspace_bytes(T, N, H, dk, dv, tdt, bool(inp["kda"]),
+                                         seg_len=args.seg_len),),
                      dtype=torch.uint8, device=dev)
-    fwd_kw = dict(h0=h0, o=o, ht=ht, workspace=ws, dv_split=args.dv_split)
-    split = la.dv_split_for(T, N, H, dk, dv, tdt, args.dv_split)
+    fwd_kw = dict(h0=h0, o=o, ht=ht, workspace=ws, dv_split=args.dv_split, seg_len=args.seg_len)
+    split = la.dv_split_for(T, N, H, dk, dv, tdt, args.dv_split, seg_len=args.seg_len)
+    seg = la.seg_len_for(T, N, H, dk, dv, tdt, seg_len=args.seg_len)
     is_kda = bool(inp["kda"])
     fwd = la.kda_chunk_fwd if is_kda else la.gdn_chunk_fwd
 
@@ -363,8 +367,10 @@ def main():
     op_flops = alg_flops(inp)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": f"chunk_reduce_kernel (d_v split {split})" if dom == "reduce"
-            else "chunk_map_kernel",
+            "kernel": (f"chunk_reduce_kernel (d_v split {split})" if seg == 0 else
+                       f"reduce stage: chunk_reduce_kernel x2 + chunk_combine_kernel "
+                       f"(segments of {seg} chunks, d_v split {split})")
+            if dom == "reduce" else "chunk_map_kernel",
             "alg_bytes_per_launch": ab, "avg_launch_ms": round(dom_ms, 5)}
 
     out = {
@@ -377,7 +383,7 @@ def main():
         "data": "synthetic (seeded, resident in HBM)",
         "config": {"workload": desc, "mode": "graph-replay of meta+map+reduce",
                    "tokens": tokens, "heads": H, "d": dk, "sequences": N, "nt_max": NT,
-                   "dv_split": split},
+                   "dv_split": split, "seg_len": seg},
         "roofline": roof,
         "op_roofline": {
             "alg_bytes": op_bytes, "alg_flops": op_flops,

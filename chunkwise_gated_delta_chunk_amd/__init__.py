@@ -23,7 +23,7 @@ import torch
 
 __all__ = [
     "LinAttnError", "lib", "nt_max", "build_chunk_meta", "workspace_bytes",
-    "gdn_chunk_fwd", "kda_chunk_fwd", "chunk_fwd_stages", "dv_split_for",
+    "gdn_chunk_fwd", "kda_chunk_fwd", "chunk_fwd_stages", "dv_split_for", "seg_len_for",
     "STAGE_MAP", "STAGE_REDUCE", "META_BAD_START", "META_NOT_MONOTONE",
     "META_OVER_CAPACITY", "LIB_PATH",
 ]
@@ -46,7 +46,7 @@ class ChunkFwdArgs(ctypes.Structure):
         ("T_max", ctypes.c_int32), ("N_max", ctypes.c_int32), ("H", ctypes.c_int32),
         ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("BT", ctypes.c_int32),
         ("qkv_dtype", ctypes.c_int32), ("dv_split", ctypes.c_int32),
-        ("scale", ctypes.c_float),
+        ("seg_len", ctypes.c_int32), ("scale", ctypes.c_float),
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
         ("cu_seqlens", ctypes.c_void_p), ("chunk_indices", ctypes.c_void_p),
@@ -83,6 +83,8 @@ def lib():
         L.la_chunk_fwd_stages.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
         L.la_chunk_fwd_dv_split.restype = ctypes.c_int32
         L.la_chunk_fwd_dv_split.argtypes = [P]
+        L.la_chunk_fwd_seg_len.restype = ctypes.c_int32
+        L.la_chunk_fwd_seg_len.argtypes = [P]
         L.la_status_string.restype = ctypes.c_char_p
         L.la_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -156,26 +158,34 @@ def build_chunk_meta(cu_seqlens, T_max, BT=64, *, chunk_indices=None, chunk_offs
     return chunk_indices, chunk_offsets, status
 
 
-def _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, dv_split=0, BT=64):
+def _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, dv_split=0, BT=64, seg_len=0):
     a = ChunkFwdArgs()
     a.T_max, a.N_max, a.H, a.d_k, a.d_v, a.BT = T_max, N_max, H, d_k, d_v, BT
     a.qkv_dtype = LA_BF16 if qkv_dtype == torch.bfloat16 else LA_F32
     a.dv_split = dv_split
+    a.seg_len = seg_len
     return a
 
 
-def workspace_bytes(T_max, N_max, H, d_k, d_v, qkv_dtype, kda=False, BT=64):
-    a = _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, BT=BT)
+def workspace_bytes(T_max, N_max, H, d_k, d_v, qkv_dtype, kda=False, BT=64, seg_len=0):
+    a = _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, BT=BT, seg_len=seg_len)
     return int(lib().la_chunk_fwd_workspace_bytes(ctypes.byref(a), int(kda)))
 
 
-def dv_split_for(T_max, N_max, H, d_k, d_v, qkv_dtype, dv_split=0):
-    a = _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, dv_split)
+def dv_split_for(T_max, N_max, H, d_k, d_v, qkv_dtype, dv_split=0, seg_len=0):
+    a = _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, dv_split, seg_len=seg_len)
     return int(lib().la_chunk_fwd_dv_split(ctypes.byref(a)))
 
 
+def seg_len_for(T_max, N_max, H, d_k, d_v, qkv_dtype, seg_len=0):
+    """Chunks per segment of the sequence-parallel reduce (0: one workgroup
+    per sequence), after "auto"; -1 for an invalid shape."""
+    a = _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, seg_len=seg_len)
+    return int(lib().la_chunk_fwd_seg_len(ctypes.byref(a)))
+
+
 def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0, o, ht,
-             output_final_state, workspace, scale, dv_split):
+             output_final_state, workspace, scale, dv_split, seg_len):
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError(f"q must be bfloat16 or float32, got {q.dtype}")
     if q.dim() != 3:
@@ -203,7 +213,7 @@ def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0
         ht = torch.empty(st_shape, dtype=torch.float32, device=dev)
     if ht is not None:
         _need(ht, "ht", torch.float32, st_shape, dev)
-    a = _shape_args(T_max, N_max, H, d_k, d_v, q.dtype, dv_split)
+    a = _shape_args(T_max, N_max, H, d_k, d_v, q.dtype, dv_split, seg_len=seg_len)
     need = int(lib().la_chunk_fwd_workspace_bytes(ctypes.byref(a), int(kda)))
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
@@ -223,10 +233,10 @@ def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0
 
 def _call(name, kda, stages, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, *,
           h0=None, o=None, ht=None, output_final_state=True, workspace=None, scale=1.0,
-          dv_split=0, stream=None):
+          dv_split=0, seg_len=0, stream=None):
     a, o, ht, workspace = _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices,
                                    chunk_offsets, h0, o, ht, output_final_state, workspace,
-                                   scale, dv_split)
+                                   scale, dv_split, seg_len)
     L = lib()
     s = _stream(stream)
     if stages is None:

@@ -81,11 +81,14 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   constexpr int GS = DK + 4;
   __shared__ float sG[KDA ? kBT * GS : 1];
   constexpr int LDM = kBT + O::PAD;  // M, natural column order, before the write-out
-  __shared__ __attribute__((aligned(16))) T sMt[kBT * LDM];
   T *sK = reinterpret_cast<T *>(sArea);
   T *sQ = sK + kBT * LDK;
   float *sL = KDA ? reinterpret_cast<float *>(sLXk) : reinterpret_cast<float *>(sArea);
   float *sX = sL + kBT * LDL;
+  // M waits for its write-out in the bytes of X, which the inverse fills
+  // only after it
+  T *sMt = reinterpret_cast<T *>(sX);
+  static_assert(kBT * LDM * sizeof(T) <= kBT * LDL * sizeof(float), "M inside X");
 
   const int slot = blockIdx.x;
   const int h = blockIdx.y;
@@ -444,24 +447,12 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
     }
   }
   __syncthreads();
-  // M -> image, chained columns, upper triangle zero (the reduce reads whole
-  // k-steps)
-  for (int idx = tid; idx < kBT * PT; idx += kThreads) {
-    const int r = idx / PT, pc = idx % PT;
-    T v[CH];
-#pragma unroll
-    for (int e = 0; e < CH; ++e) {
-      const int s = kidx<O>(pc * CH + e);
-      v[e] = s <= r ? sMt[r * LDM + s] : (T)0.f;
-    }
-    put(I.MM, PT, r, pc, v);
-  }
-
-  // ---- X = (I + L)^-1: diagonal blocks by forward substitution, lane = column
+  // ---- X = (I + L)^-1: diagonal blocks by forward substitution, lane =
+  // column; wave 0 solves them into registers while the M write-out runs
+  float xd[16];
   if (w == 0) {
     const int blk = lane >> 4, c = lane & 15;
     const float *Lb = sL + (16 * blk) * LDL + 16 * blk;
-    float x[16];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       float lrow[16];
@@ -475,12 +466,28 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
       }
       float acc = (r == c) ? 1.f : 0.f;
 #pragma unroll
-      for (int s = 0; s < r; ++s) acc -= lrow[s] * x[s];
-      x[r] = acc;
+      for (int s = 0; s < r; ++s) acc -= lrow[s] * xd[s];
+      xd[r] = acc;
     }
+  }
+  // M -> image, chained columns, upper triangle zero (the reduce reads whole
+  // k-steps)
+  for (int idx = tid; idx < kBT * PT; idx += kThreads) {
+    const int r = idx / PT, pc = idx % PT;
+    T v[CH];
+#pragma unroll
+    for (int e = 0; e < CH; ++e) {
+      const int s = kidx<O>(pc * CH + e);
+      v[e] = s <= r ? sMt[r * LDM + s] : (T)0.f;
+    }
+    put(I.MM, PT, r, pc, v);
+  }
+  __syncthreads();  // M is written out: X may take its bytes
+  if (w == 0) {
+    const int blk = lane >> 4, c = lane & 15;
     float *Xb = sX + (16 * blk) * LDL + 16 * blk;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) Xb[r * LDL + c] = x[r];
+    for (int r = 0; r < 16; ++r) Xb[r * LDL + c] = xd[r];
   }
   __syncthreads();
   // block rows below the diagonal: X_ij = -X_ii sum_{k=j}^{i-1} L_ik X_kj, by i - j

@@ -54,68 +54,64 @@ namespace la {
 
 namespace {
 
+// What one workgroup does: chunk slots [j0, j1) of sequence n, head h, state
+// columns col0 .. col0 + W - 1; the state starts from init ([d_k][d_v] fp32,
+// this (sequence or segment, head)), the identity (init_id) or zero, and ends
+// in fin (fp32) and / or pimg (fp16 hi and lo images, see the segment passes
+// below).  vzero: V reads as zero.
+struct Work {
+  int n, h, j0, j1, t0, eos, col0;
+  bool vzero, init_id;
+  const float *init;
+  float *fin;
+  _Float16 *pimg;
+};
+
+// Geometry shared by the kernel (LDS size) and its body.
 template <bool KDA, typename In, int DK, int NW>
-__global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParams p) {
+struct ReduceShape {
   using O = Op<In>;
-  constexpr int E = (int)sizeof(typename O::T);
-  constexpr ImageLayout I = image_layout(KDA, E, DK);
+  static constexpr int E = (int)sizeof(typename O::T);
+  static constexpr ImageLayout I = image_layout(KDA, E, DK);
+  static constexpr int W = 16 * NW;                       // state columns per workgroup
+  static constexpr int V_BYTES = kBT * W * (int)sizeof(In);
+  // stage buffer: the V tile first (its reads and those of K and Q stay
+  // under the 64 KiB immediate offset), then the image
+  static constexpr int IMG = V_BYTES;
+  static constexpr int STAGE = V_BYTES + I.BYTES;
+  static constexpr int NBUF = 2 * STAGE <= 160 * 1024 ? 2 : 1;
+};
+
+template <bool KDA, typename In, int DK, int NW, bool OUT>
+__device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &wk, char *smem) {
+  using O = Op<In>;
+  using SH = ReduceShape<KDA, In, DK, NW>;
+  constexpr int E = SH::E;
+  constexpr ImageLayout I = SH::I;
   constexpr bool HAS_KT = KDA || O::KPL == 1;
   constexpr bool F16 = O::KPL == 8;
   constexpr int PK = DK * E / 16, PT = kBT * E / 16;
-  constexpr int W = 16 * NW;                 // state columns per workgroup
+  constexpr int W = SH::W;                   // state columns per workgroup
   constexpr int DV = DK;                     // d_v == d_k
   constexpr int NKD = ksteps<O>(DK);         // k-steps over d_k
   constexpr int NKR = ksteps<O>(kBT);        // k-steps over chunk rows
   constexpr int NHT = DK / 16;               // state row tiles
   constexpr int PV = W * (int)sizeof(In) / 16;   // 16-byte pieces per V row
-  constexpr int V_BYTES = kBT * W * (int)sizeof(In);
-  // stage buffer: the V tile first (its reads and those of K and Q stay
-  // under the 64 KiB immediate offset), then the image
-  constexpr int IMG = V_BYTES;
-  constexpr int STAGE = V_BYTES + I.BYTES;
-  constexpr int NBUF = 2 * STAGE <= 160 * 1024 ? 2 : 1;
-  constexpr int NVL = V_BYTES / 1024, NIMG = I.BYTES / 1024, NLOAD = NVL + NIMG;
-  (void)NLOAD;
+  constexpr int V_BYTES = SH::V_BYTES;
+  constexpr int IMG = SH::IMG;
+  constexpr int STAGE = SH::STAGE;
+  constexpr int NBUF = SH::NBUF;
+  constexpr int NVL = V_BYTES / 1024, NIMG = I.BYTES / 1024;
   static_assert(I.BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "1 KiB staging pieces");
   static_assert(!F16 || IMG + I.Q + 3 * 256 * PK + 16 <= 65536, "immediate offsets");
 
-  __shared__ __attribute__((aligned(16))) char smem[NBUF * STAGE];
-
-  // ---- block -> (unit, slice), XCD-aware: the slices of one unit share an
-  // XCD (and its L2, which then serves the image to all of them)
-  const int b = blockIdx.x;
-  const int xcd = b & 7, kk = b >> 3;
-  const int slice = kk % p.S, unit = (kk / p.S) * 8 + xcd;
   const int H = p.H;
-  if (unit >= p.N_max * H) return;
-  const int rank = unit / H, h = unit % H;
-  // Units go out longest sequence first, so that when there are more
-  // workgroups than CUs the ones on the critical path start in the first
-  // round: unit u takes the sequence of rank u / H by decreasing chunk count
-  // (ties by index).  Up to 64 sequences every wave ranks them by itself,
-  // lane m holding sequence m, with no LDS and no barrier; empty sequences
-  // rank last, so their units leave at once.  Beyond 64 sequences the
-  // natural order is kept.
-  int n = rank;
-  if (p.N_max <= 64) {
-    const int m = lane_id();
-    int len = -1;
-    if (m < p.N_max) len = p.chunk_offsets[m + 1] - p.chunk_offsets[m];
-    if (rank >= __popcll(__ballot(len > 0))) return;
-    int r = 0;
-    for (int i = 0; i < p.N_max; ++i) {
-      const int li = __builtin_amdgcn_readlane(len, i);
-      r += (li > len) | ((li == len) & (i < m));
-    }
-    n = __builtin_ctzll(__ballot(r == rank));
-  }
-  const int j0 = p.chunk_offsets[n], j1 = p.chunk_offsets[n + 1];
-  if (j0 == j1) return;  // empty sequence (or invalid cu_seqlens): no writes
-  const int bos = p.cu_seqlens[n], eos = p.cu_seqlens[n + 1];
+  const int n = wk.n, h = wk.h, j0 = wk.j0, j1 = wk.j1, eos = wk.eos;
+  (void)n;
   const int lane = lane_id(), w = wave_id();
   const bool copier = w == NW;  // the extra wave only stages operands
   const int lr = lane & 15, lg = lane >> 4;
-  const int cw = slice * W + 16 * w;                 // this wave's first state column
+  const int cw = wk.col0 + 16 * w;                   // this wave's first state column
   const int rs_v = H * DV * (int)sizeof(In);         // token stride of v (bytes)
   const int rs_o = H * DV * 4;                       // token stride of o (bytes)
 
@@ -135,17 +131,23 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
   }
   const char *img_c = static_cast<const char *>(p.img) + ((size_t)j0 * H + h) * I.BYTES;
   const size_t img_step = (size_t)H * I.BYTES;
-  const In *v_c = static_cast<const In *>(p.v) + ((size_t)bos * H + h) * DV + slice * W;
+  const In *v_c = static_cast<const In *>(p.v) + ((size_t)wk.t0 * H + h) * DV + (wk.vzero ? 0 : wk.col0);
   const size_t v_step = (size_t)kBT * H * DV;
   // copy of the chunk whose image starts at img and whose C V rows start at vrow
+  // (no output: the Q and M pieces of the image are not needed; a zero V
+  // has an empty range, so its loads write zeros)
   auto copy_chunk = [&](int buf, const char *img, const In *vrow, int C) {
     const auto ri = buffer_rsrc(img, I.BYTES);
-    const auto rv = buffer_rsrc(vrow, C * rs_v);
+    const auto rv = buffer_rsrc(vrow, wk.vzero ? 0 : C * rs_v);
     char *dst = smem + buf * STAGE;
 #pragma unroll
     for (int q = 0; q < NVL; ++q) copy16_to_lds(rv, dst + q * 1024, voff[q], 0);
 #pragma unroll
-    for (int q = 0; q < NIMG; ++q) copy16_to_lds(ri, dst + (NVL + q) * 1024, lane * 16, q * 1024);
+    for (int q = 0; q < NIMG; ++q) {
+      const bool unused = !OUT && ((q * 1024 >= I.Q && q * 1024 < I.Q + kBT * DK * E) ||
+                                   (q * 1024 >= I.MM && q * 1024 < I.MM + kBT * kBT * E));
+      if (!unused) copy16_to_lds(ri, dst + (NVL + q) * 1024, lane * 16, q * 1024);
+    }
   };
 
   // ---------------------------------------------------------- LDS patterns
@@ -182,21 +184,22 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
 
   // ---------------------------------------------------------- the state
   f32x4 hacc[NHT];
-  const size_t sbase = ((size_t)n * H + h) * DK * DV;
-  if (p.h0 && !copier) {
+  if (wk.init && !copier) {
 #pragma unroll
     for (int t = 0; t < NHT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) hacc[t][e] = p.h0[sbase + (size_t)(16 * t + lg * 4 + e) * DV + cw + lr];
+      for (int e = 0; e < 4; ++e) hacc[t][e] = wk.init[(size_t)(16 * t + lg * 4 + e) * DV + cw + lr];
   } else {
 #pragma unroll
-    for (int t = 0; t < NHT; ++t) hacc[t] = zero4();
+    for (int t = 0; t < NHT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hacc[t][e] = wk.init_id && 16 * t + lg * 4 + e == cw + lr ? 1.f : 0.f;
   }
 
   int off_o[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) off_o[e] = (lg * 4 + e) * rs_o + (cw + lr) * 4;
-  float *o_c = p.o + ((size_t)bos * H + h) * DV;
+  float *o_c = p.o + ((size_t)wk.t0 * H + h) * DV;
   const size_t o_step = (size_t)kBT * H * DV;
 
   // ---------------------------------------------------------- one chunk
@@ -214,7 +217,7 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
     else __syncthreads();
   };
   auto copy_step = [&](int jj) {
-    const int r0 = bos + (jj - j0) * kBT;
+    const int r0 = wk.t0 + (jj - j0) * kBT;
     const bool more = jj + 1 < j1;
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     chunk_barrier();
@@ -228,7 +231,7 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
   };
   auto chunk = [&](auto bufc, int jj) {
     constexpr int BUF = decltype(bufc)::value;
-    const int r0 = bos + (jj - j0) * kBT;
+    const int r0 = wk.t0 + (jj - j0) * kBT;
     const int C = min(kBT, eos - r0);
     chunk_barrier();
     const char *buf = smem + BUF * STAGE;
@@ -258,7 +261,7 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
         static_for<4>([&](auto rc) {
           constexpr int R = decltype(rc)::value;
           ds_read_b128_at<IMG + I.K + R * 256 * PK>(fr[s][2 * R], aK[BUF][s]);
-          ds_read_b128_at<IMG + I.Q + R * 256 * PK>(fr[s][2 * R + 1], aK[BUF][s]);
+          if constexpr (OUT) ds_read_b128_at<IMG + I.Q + R * 256 * PK>(fr[s][2 * R + 1], aK[BUF][s]);
         });
       };
       read_step(std::integral_constant<int, 0>{});
@@ -266,13 +269,18 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
       static_for<NKD>([&](auto sc) {
         constexpr int s = decltype(sc)::value;
         auto &f = fr[s];
-        if constexpr (s + 1 < NKD) wait_lds_tied8<8>(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
-        else wait_lds_tied8<0>(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+        if constexpr (OUT) {
+          if constexpr (s + 1 < NKD) wait_lds_tied8<8>(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+          else wait_lds_tied8<0>(f[0], f[1], f[2], f[3], f[4], f[5], f[6], f[7]);
+        } else {
+          if constexpr (s + 1 < NKD) wait_lds_tied4<4>(f[0], f[2], f[4], f[6]);
+          else wait_lds_tied4<0>(f[0], f[2], f[4], f[6]);
+        }
         if constexpr (s + 2 < NKD) read_step(std::integral_constant<int, s + 2>{});
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
           yk[R] = O::mfma(f[2 * R], hb[s], yk[R]);
-          yq[R] = O::mfma(f[2 * R + 1], hb[s], yq[R]);
+          if constexpr (OUT) yq[R] = O::mfma(f[2 * R + 1], hb[s], yq[R]);
         }
       });
     } else {
@@ -280,10 +288,8 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
       for (int s = 0; s < NKD; ++s)
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
-          const auto ak = a_frag_img<O, PK>(tK, 16 * R, s, lane);
-          const auto aq = a_frag_img<O, PK>(tQ, 16 * R, s, lane);
-          yk[R] = O::mfma(ak, hb[s], yk[R]);
-          yq[R] = O::mfma(aq, hb[s], yq[R]);
+          yk[R] = O::mfma(a_frag_img<O, PK>(tK, 16 * R, s, lane), hb[s], yk[R]);
+          if constexpr (OUT) yq[R] = O::mfma(a_frag_img<O, PK>(tQ, 16 * R, s, lane), hb[s], yq[R]);
         }
     }
 
@@ -346,14 +352,16 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
         constexpr int i = decltype(ic)::value;
         u[fR(i)] = O::mfma(ft[i], xb[fS(i)], u[fR(i)]);
       });
-      static_for<6>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        ds_read_b128_at<DMM + fR(i) * 256 * PT>(fm[i], aP[BUF][fS(i)]);
-      });
-      wait_lds_tied4<6>(bet[0], bet[1], bet[2], bet[3]);
-      if constexpr (!KDA) wait_lds_tied4<6>(fac[0], fac[1], fac[2], fac[3]);
+      constexpr int NM = OUT ? 6 : 0;  // M fragments in flight
+      if constexpr (OUT)
+        static_for<6>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          ds_read_b128_at<DMM + fR(i) * 256 * PT>(fm[i], aP[BUF][fS(i)]);
+        });
+      wait_lds_tied4<NM>(bet[0], bet[1], bet[2], bet[3]);
+      if constexpr (!KDA) wait_lds_tied4<NM>(fac[0], fac[1], fac[2], fac[3]);
       if constexpr (!HAS_KT) {
-        wait_lds_tied1<6>(dcv);
+        wait_lds_tied1<NM>(dcv);
         gdec = dcv[0];
       }
 #pragma unroll
@@ -370,8 +378,10 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
         if constexpr (KDA) ubf[s] = ufr[s];
         else ubf[s] = b_frag<O>(ub, s);
       }
-      wait_lds_tied2<0>(fm[0], fm[1]);
-      wait_lds_tied4<0>(fm[2], fm[3], fm[4], fm[5]);
+      if constexpr (OUT) {
+        wait_lds_tied2<0>(fm[0], fm[1]);
+        wait_lds_tied4<0>(fm[2], fm[3], fm[4], fm[5]);
+      }
       // the transposed K^T reads of the update (GDN), first half
       auto read_kt = [&](auto t0c) {
         constexpr int T0 = decltype(t0c)::value;
@@ -388,22 +398,26 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
         static_assert(NKR == 2, "two k-steps over the chunk rows");
         read_kt(std::integral_constant<int, 0>{});
       }
-      f32x4 oa[4];
+      if constexpr (OUT) {
+        f32x4 oa[4];
 #pragma unroll
-      for (int R = 0; R < 4; ++R)
+        for (int R = 0; R < 4; ++R)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) oa[R][e] = gam[R][e] * yq[R][e];
-      static_for<6>([&](auto ic) {
-        constexpr int i = decltype(ic)::value;
-        oa[fR(i)] = O::mfma(fm[i], ufr[fS(i)], oa[fR(i)]);
-      });
-      if constexpr (!HAS_KT) read_kt(std::integral_constant<int, NHT / 2>{});
+          for (int e = 0; e < 4; ++e) oa[R][e] = gam[R][e] * yq[R][e];
+        static_for<6>([&](auto ic) {
+          constexpr int i = decltype(ic)::value;
+          oa[fR(i)] = O::mfma(fm[i], ufr[fS(i)], oa[fR(i)]);
+        });
+        if constexpr (!HAS_KT) read_kt(std::integral_constant<int, NHT / 2>{});
 #pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        const auto ro = buffer_rsrc(o_c + (size_t)16 * R * H * DV, (C - 16 * R) * rs_o);
+        for (int R = 0; R < 4; ++R) {
+          const auto ro = buffer_rsrc(o_c + (size_t)16 * R * H * DV, (C - 16 * R) * rs_o);
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p.scale * oa[R][e]), ro, off_o[e], 0, 0);
+          for (int e = 0; e < 4; ++e)
+            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p.scale * oa[R][e]), ro, off_o[e], 0, 0);
+        }
+      } else {
+        if constexpr (!HAS_KT) read_kt(std::integral_constant<int, NHT / 2>{});
       }
     } else {
       const int col = 16 * w + lr;
@@ -442,7 +456,7 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
         else ubf[s] = b_frag<O>(ub, s);
       }
 #pragma unroll
-      for (int R = 0; R < 4; ++R) {
+      for (int R = 0; R < 4 && OUT; ++R) {
         f32x4 oa;
 #pragma unroll
         for (int e = 0; e < 4; ++e) oa[e] = gam[R][e] * yq[R][e];
@@ -488,7 +502,7 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
 
   // ---------------------------------------------------------- chunk loop
   if (copier) {
-    copy_chunk(0, img_c, v_c, min(kBT, eos - bos));
+    copy_chunk(0, img_c, v_c, min(kBT, eos - wk.t0));
     for (int jj = j0; jj < j1; ++jj) copy_step(jj);
     return;
   }
@@ -502,22 +516,160 @@ __global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParam
     if (++jj == j1) break;
   }
 
-  // ---- final state slice
-  if (p.ht && !copier) {
+  // ---- final state slice: fp32, or the fp16 hi / lo images of a segment's
+  // transition (element (r, c) at the place an A fragment of a [d_k][d_k]
+  // operand with chained columns expects it: row r, column kpos(c))
+  if (wk.fin) {
 #pragma unroll
     for (int t = 0; t < NHT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        p.ht[sbase + (size_t)(16 * t + lg * 4 + e) * DV + cw + lr] = hacc[t][e];
+      for (int e = 0; e < 4; ++e) wk.fin[(size_t)(16 * t + lg * 4 + e) * DV + cw + lr] = hacc[t][e];
   }
+  if (wk.pimg) {
+    constexpr int PP = DK * 2 / 16;  // 16-byte pieces per fp16 row
+    const int kc = kpos<Op<bf16>>(cw + lr);
+#pragma unroll
+    for (int t = 0; t < NHT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * t + lg * 4 + e;
+        const int off = (tile_off<PP>(r, kc >> 3) >> 1) + (kc & 7);
+        const _Float16 hi = (_Float16)hacc[t][e];
+        wk.pimg[off] = hi;
+        wk.pimg[DK * DK + off] = (_Float16)(hacc[t][e] - (float)hi);
+      }
+  }
+}
+
+// Which work a workgroup has: 0 none, 1 with output, 2 without (the Delta and
+// P roles of the segmented first pass).
+//
+// One workgroup per sequence (seg == 0): units (sequence, head) go out
+// longest sequence first, so that when there are more workgroups than CUs
+// the ones on the critical path start in the first round: unit u takes the
+// sequence of rank u / H by decreasing chunk count (ties by index).  Up to
+// 64 sequences every wave ranks them by itself, lane m holding sequence m,
+// with no LDS and no barrier; empty sequences rank last, so their units
+// leave at once.  Beyond 64 sequences the natural order is kept.
+//
+// Segmented (seg = L > 0, N_max <= 64): sequence n's chunks form
+// ceil(chunks / L) segments of L chunks, numbered after those of sequences
+// m < n.  The state entering segment s + 1 is an affine function of the one
+// entering s, H_{s+1} = P_s H_s + D_s, with P_s the segment's transition
+// (the state it leaves from the identity with V = 0) and D_s the state it
+// leaves from zero.  Pass 1: segment 0 runs with output from the initial
+// state and leaves its state in hin of segment 1 (or in ht); middle segments
+// compute D_s (d_v slices) and P_s (d_k slices, fp16 hi / lo images).  The
+// combine kernel then walks H_{s+1} = P_s H_s + D_s.  Pass 2: segments s >= 1
+// run with output from hin, the last one leaving ht.
+template <int DK, int W>
+__device__ __forceinline__ int decode_work(const ReduceParams &p, Work &wk) {
+  const int b = blockIdx.x;
+  const int xcd = b & 7, kk = b >> 3;
+  const int H = p.H;
+  const int SS = p.pass == 1 ? p.S + p.SP : p.S;  // slices per unit
+  const int slice = kk % SS, unit = (kk / SS) * 8 + xcd;
+  const int m = lane_id();
+  const size_t mat = (size_t)DK * DK;
+  wk.vzero = false;
+  wk.init_id = false;
+  wk.init = nullptr;
+  wk.fin = nullptr;
+  wk.pimg = nullptr;
+  wk.col0 = slice * W;
+  if (p.seg == 0) {
+    if (unit >= p.N_max * H) return 0;
+    const int rank = unit / H;
+    wk.h = unit % H;
+    int n = rank;
+    if (p.N_max <= 64) {
+      int len = -1;
+      if (m < p.N_max) len = p.chunk_offsets[m + 1] - p.chunk_offsets[m];
+      if (rank >= __popcll(__ballot(len > 0))) return 0;
+      int r = 0;
+      for (int i = 0; i < p.N_max; ++i) {
+        const int li = __builtin_amdgcn_readlane(len, i);
+        r += (li > len) | ((li == len) & (i < m));
+      }
+      n = __builtin_ctzll(__ballot(r == rank));
+    }
+    wk.n = n;
+    wk.j0 = p.chunk_offsets[n];
+    wk.j1 = p.chunk_offsets[n + 1];
+    if (wk.j0 == wk.j1) return 0;  // empty sequence (or invalid cu_seqlens): no writes
+    wk.t0 = p.cu_seqlens[n];
+    wk.eos = p.cu_seqlens[n + 1];
+    const size_t sb = ((size_t)n * H + wk.h) * mat;
+    if (p.h0) wk.init = p.h0 + sb;
+    if (p.ht) wk.fin = p.ht + sb;
+    return 1;
+  }
+  if (unit >= p.NS_max * H) return 0;
+  const int sig = unit / H;
+  wk.h = unit % H;
+  // the segment slot's sequence: lane i holds sequence i's segment count
+  int ns = 0;
+  if (m < p.N_max) ns = (p.chunk_offsets[m + 1] - p.chunk_offsets[m] + p.seg - 1) / p.seg;
+  int n = -1, s = 0, nseg = 0, acc = 0;
+  for (int i = 0; i < p.N_max; ++i) {
+    const int ni = __builtin_amdgcn_readlane(ns, i);
+    if (sig < acc + ni) {
+      n = i;
+      s = sig - acc;
+      nseg = ni;
+      break;
+    }
+    acc += ni;
+  }
+  if (n < 0) return 0;
+  wk.n = n;
+  wk.j0 = p.chunk_offsets[n] + s * p.seg;
+  wk.j1 = min(wk.j0 + p.seg, p.chunk_offsets[n + 1]);
+  wk.t0 = p.cu_seqlens[n] + s * p.seg * kBT;
+  wk.eos = p.cu_seqlens[n + 1];
+  const size_t here = ((size_t)sig * H + wk.h) * mat, next = here + (size_t)H * mat;
+  const size_t sb = ((size_t)n * H + wk.h) * mat;
+  if (p.pass == 1) {
+    if (s == 0) {
+      if (slice >= p.S) return 0;
+      if (p.h0) wk.init = p.h0 + sb;
+      if (nseg > 1) wk.fin = p.hin + next;
+      else if (p.ht) wk.fin = p.ht + sb;
+      return 1;
+    }
+    if (s == nseg - 1) return 0;
+    if (slice < p.S) {
+      wk.fin = p.dlt + here;
+    } else {
+      wk.col0 = (slice - p.S) * W;
+      wk.vzero = true;
+      wk.init_id = true;
+      wk.pimg = p.pimg + 2 * here;
+    }
+    return 2;
+  }
+  if (s == 0 || slice >= p.S) return 0;
+  wk.init = p.hin + here;
+  if (s == nseg - 1 && p.ht) wk.fin = p.ht + sb;
+  return 1;
+}
+
+template <bool KDA, typename In, int DK, int NW>
+__global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParams p) {
+  using SH = ReduceShape<KDA, In, DK, NW>;
+  __shared__ __attribute__((aligned(16))) char smem[SH::NBUF * SH::STAGE];
+  Work wk;
+  const int role = decode_work<DK, SH::W>(p, wk);
+  if (role == 1) reduce_body<KDA, In, DK, NW, true>(p, wk, smem);
+  else if (role == 2) reduce_body<KDA, In, DK, NW, false>(p, wk, smem);
 }
 
 }  // namespace
 
 template <bool KDA, typename In, int DK, int NW>
 static hipError_t launch_reduce_t(const ReduceParams &p, hipStream_t st) {
-  const int units = p.N_max * p.H;
-  const int grid = ((units + 7) / 8) * 8 * p.S;
+  const int units = (p.seg ? p.NS_max : p.N_max) * p.H;
+  const int grid = ((units + 7) / 8) * 8 * (p.pass == 1 ? p.S + p.SP : p.S);
   hipLaunchKernelGGL((chunk_reduce_kernel<KDA, In, DK, NW>), dim3(grid), dim3(64 * (NW + 1)), 0, st, p);
   return hipGetLastError();
 }

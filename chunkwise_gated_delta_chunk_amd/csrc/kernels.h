@@ -26,6 +26,22 @@ struct ReduceParams {
   const void *img;
   int H, N_max, S;  // S = d_v slices per (sequence, head)
   float scale;
+  // sequence-parallel reduce (chunk_reduce.hip): seg = chunks per segment
+  // (0: one workgroup walks a whole sequence), pass 1 or 2, SP = d_k slices
+  // of the transitions, NS_max segment slots; per (segment slot, head):
+  // hin, dlt [d_k][d_v] fp32 and pimg 2 x [d_k][d_k] fp16
+  int seg, pass, SP, NS_max;
+  float *hin, *dlt;
+  _Float16 *pimg;
+};
+
+// Segment combine: H_{s+1} = P_s H_s + D_s along each sequence's segments.
+struct CombineParams {
+  const int32_t *chunk_offsets;
+  int H, N_max, seg;
+  float *hin;
+  const float *dlt;
+  const _Float16 *pimg;
 };
 
 hipError_t launch_chunk_meta(const int32_t *cu, int N_max, int T_max, int BT, int NT_max,
@@ -34,5 +50,6 @@ hipError_t launch_chunk_map(const MapParams &p, bool kda, bool bf16_in, int dk, 
 // W = d_v / S columns per workgroup: 32 per wave
 hipError_t launch_chunk_reduce(const ReduceParams &p, bool kda, bool bf16_in, int dk, int W,
                                hipStream_t st);
+hipError_t launch_chunk_combine(const CombineParams &p, int dk, hipStream_t st);
 
 }  // namespace la

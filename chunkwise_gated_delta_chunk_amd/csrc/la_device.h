@@ -197,7 +197,12 @@ __device__ __host__ constexpr ImageLayout image_layout(bool kda, int e, int dk) 
 }
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
-__device__ __forceinline__ lds_ptr_t to_lds(void *p) { return (lds_ptr_t)(p); }
+// A generic pointer into LDS holds the LDS byte offset in its low 32 bits
+// (the LDS aperture is 4 GiB aligned); taking it from there, rather than by an
+// address-space cast, needs no null check.  Only for pointers into LDS.
+__device__ __forceinline__ lds_ptr_t to_lds(void *p) {
+  return (lds_ptr_t)(uintptr_t)(uint32_t)(uintptr_t)p;
+}
 
 // Direct global-to-LDS copy of 16 bytes per lane: lane l's bytes at buffer
 // offset voff (+ soff, not range checked) land at lds + 16 l; lanes out of the
@@ -318,9 +323,7 @@ __device__ __forceinline__ void ds_read_tr16_at(s16x4 &r, uint32_t a) {
 // others read after the barrier must have completed (vmcnt) in the issuing
 // wave.  The memory clobber keeps the compiler's memory accesses in place.
 __device__ __forceinline__ void barrier_lds() { asm volatile("s_barrier" ::: "memory"); }
-__device__ __forceinline__ uint32_t lds_addr(const void *p) {
-  return (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) char *)p);
-}
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)p; }
 
 // compile-time loop: f(std::integral_constant<int, i>) for i = 0 .. N-1
 template <typename F, int... Is>

@@ -30,6 +30,9 @@ int check_shape(const la_chunk_fwd_args *a) {
   const int s = a->dv_split;
   if (s != 0 && s != 1 && s != 2 && s != 4) return LA_ERR_UNSUPPORTED;
   if (s != 0 && a->d_v / s < 32) return LA_ERR_UNSUPPORTED;
+  // seg_len: -1 (off), 0 (auto) or chunks per segment, bf16 and N_max <= 64
+  if (a->seg_len < -1) return LA_ERR_UNSUPPORTED;
+  if (a->seg_len > 0 && (a->qkv_dtype != LA_BF16 || a->N_max > 64)) return LA_ERR_UNSUPPORTED;
   // every (token, head) index and (slot, head) workspace index stays in size_t
   const int64_t nt = la_nt_max(a->T_max, a->N_max, a->BT);
   if (nt < 1 || nt > 0x7fffffff) return LA_ERR_SHAPE;
@@ -52,11 +55,42 @@ int split_for(const la_chunk_fwd_args *a) {
 
 size_t elem_bytes(const la_chunk_fwd_args *a) { return a->qkv_dtype == LA_BF16 ? 2 : 4; }
 
-// Workspace: one map-stage image per (chunk slot, head), image_layout bytes each
-size_t ws_bytes(const la_chunk_fwd_args *a, bool kda) {
+// Chunks per segment of the sequence-parallel reduce, 0 for one workgroup
+// per sequence.  Automatic when the (sequence, head) units cannot fill half
+// the CUs even at 64 columns per workgroup: about the length that spreads
+// the capacity's chunks of all units over the CUs once, at least 4, and only
+// where the longest possible sequence then has at least 3 segments.
+int seg_for(const la_chunk_fwd_args *a) {
+  if (a->seg_len < 0 || a->qkv_dtype != LA_BF16 || a->N_max > 64) return 0;
+  if (a->seg_len > 0) return a->seg_len;
+  const int64_t s2 = a->d_v / 64 > 0 ? a->d_v / 64 : 1;
+  if ((int64_t)a->N_max * a->H * s2 > kCUs / 2) return 0;
+  const int64_t nt = la_nt_max(a->T_max, a->N_max, a->BT);
+  int64_t L = (nt * a->H * s2 + kCUs - 1) / kCUs;
+  if (L < 4) L = 4;
+  const int64_t longest = (a->T_max + a->BT - 1) / a->BT;
+  if (longest < 3 * L) return 0;
+  return (int)L;
+}
+
+// segment slots: ceil(T_max / (BT L)) + N_max - 1
+int64_t ns_max(const la_chunk_fwd_args *a, int L) {
+  return ((int64_t)a->T_max + (int64_t)a->BT * L - 1) / ((int64_t)a->BT * L) + a->N_max - 1;
+}
+
+// Workspace: one map-stage image per (chunk slot, head), image_layout bytes
+// each; with segments, then hin, dlt ([d_k][d_v] fp32) and the transition
+// images (2 x [d_k][d_k] fp16) per (segment slot, head)
+size_t ws_img_bytes(const la_chunk_fwd_args *a, bool kda) {
   const size_t cells = (size_t)la_nt_max(a->T_max, a->N_max, a->BT) * a->H;
   return cells * (size_t)la::image_layout(kda, (int)elem_bytes(a), a->d_k).BYTES;
 }
+size_t ws_seg_bytes(const la_chunk_fwd_args *a) {
+  const int L = seg_for(a);
+  if (L == 0) return 0;
+  return 3 * (size_t)ns_max(a, L) * a->H * a->d_k * a->d_v * sizeof(float);
+}
+size_t ws_bytes(const la_chunk_fwd_args *a, bool kda) { return ws_img_bytes(a, kda) + ws_seg_bytes(a); }
 
 int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
   if (!a) return LA_ERR_NULL;
@@ -107,8 +141,36 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     rp.N_max = a->N_max;
     rp.S = split_for(a);
     rp.scale = a->scale;
-    if (la::launch_chunk_reduce(rp, kda, bf, a->d_k, a->d_v / rp.S, st) != hipSuccess)
-      return LA_ERR_HIP;
+    const int L = seg_for(a);
+    if (L == 0) {
+      if (la::launch_chunk_reduce(rp, kda, bf, a->d_k, a->d_v / rp.S, st) != hipSuccess)
+        return LA_ERR_HIP;
+    } else {
+      // segments: 64 columns per workgroup (the passes are throughput-bound)
+      rp.S = a->d_v / 64 > 0 ? a->d_v / 64 : 1;
+      rp.SP = a->d_k / (a->d_v / rp.S);
+      rp.seg = L;
+      rp.NS_max = (int)ns_max(a, L);
+      const size_t mat = (size_t)rp.NS_max * a->H * a->d_k * a->d_v;
+      rp.hin = reinterpret_cast<float *>(ws + ws_img_bytes(a, kda));
+      rp.dlt = rp.hin + mat;
+      rp.pimg = reinterpret_cast<_Float16 *>(rp.dlt + mat);
+      rp.pass = 1;
+      if (la::launch_chunk_reduce(rp, kda, bf, a->d_k, a->d_v / rp.S, st) != hipSuccess)
+        return LA_ERR_HIP;
+      la::CombineParams cp{};
+      cp.chunk_offsets = a->chunk_offsets;
+      cp.H = a->H;
+      cp.N_max = a->N_max;
+      cp.seg = L;
+      cp.hin = rp.hin;
+      cp.dlt = rp.dlt;
+      cp.pimg = rp.pimg;
+      if (la::launch_chunk_combine(cp, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
+      rp.pass = 2;
+      if (la::launch_chunk_reduce(rp, kda, bf, a->d_k, a->d_v / rp.S, st) != hipSuccess)
+        return LA_ERR_HIP;
+    }
   }
   return LA_OK;
 }
@@ -156,7 +218,12 @@ int la_chunk_fwd_stages(const la_chunk_fwd_args *a, int is_kda, int stages, void
 
 int32_t la_chunk_fwd_dv_split(const la_chunk_fwd_args *a) {
   if (!a || check_shape(a) != LA_OK) return 0;
-  return split_for(a);
+  return seg_for(a) ? (a->d_v / 64 > 0 ? a->d_v / 64 : 1) : split_for(a);
+}
+
+int32_t la_chunk_fwd_seg_len(const la_chunk_fwd_args *a) {
+  if (!a || check_shape(a) != LA_OK) return -1;
+  return seg_for(a);
 }
 
 const char *la_status_string(int status) {

@@ -106,6 +106,9 @@ typedef struct {
                                /* else 1, 2 or 4 with d_v / dv_split >= 32.      */
                                /* auto: d_v / 64 slices, twice that when         */
                                /* N_max * H * (d_v / 64) <= 256 (the CU count)   */
+    int32_t seg_len;           /* sequence-parallel reduce: chunks per segment;  */
+                               /* -1 = off, 0 = auto, > 0 needs bf16 inputs and  */
+                               /* N_max <= 64 (see la_chunk_fwd_seg_len)         */
     float scale;               /* o = scale * S q                                */
     const void *q, *k, *v;     /* [T_max][H][d_k] / [T_max][H][d_v], qkv_dtype   */
     const float *g;            /* log-decay: GDN [T_max][H]; KDA [T_max][H][d_k] */
@@ -169,8 +172,25 @@ int kda_chunk_fwd(const la_chunk_fwd_args *a, void *stream);
 int la_chunk_fwd_stages(const la_chunk_fwd_args *a, int is_kda, int stages,
                         void *stream);
 
-/* The dv_split the forward uses for these arguments (after "auto"). */
+/* The dv_split the forward uses for these arguments (after "auto"; 64-column
+ * slices whenever it runs segmented). */
 int32_t la_chunk_fwd_dv_split(const la_chunk_fwd_args *a);
+
+/*
+ * Chunks per segment the forward's reduce uses (after "auto"), 0 when one
+ * workgroup walks each whole sequence, -1 for an invalid shape.  Segmented,
+ * each sequence's chunks are cut into segments of seg_len chunks and the
+ * reduce runs in three launches: the first segments (with output) together
+ * with each later segment's transition P and zero-state result D (the state
+ * entering segment s+1 is P_s H_s + D_s: the recurrence is affine in the
+ * state), a serial combine of those along each sequence, then the later
+ * segments with output from their entering state.  Auto (seg_len = 0)
+ * segments only bf16 inputs with N_max <= 64 whose (sequence, head) units
+ * cannot fill half of the 256 CUs at 64 state columns per workgroup, with
+ * about ceil(NT_max * H * (d_v / 64) / 256) chunks per segment (at least 4),
+ * and only when a sequence of T_max tokens would have 3 segments or more.
+ */
+int32_t la_chunk_fwd_seg_len(const la_chunk_fwd_args *a);
 
 /* Static text for a la_status value. */
 const char *la_status_string(int status);

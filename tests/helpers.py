@@ -36,14 +36,14 @@ def to_dev(inp, device="cuda"):
 
 
 def run_gpu(inp, *, dv_split=0, scale=1.0, device="cuda", with_state=True, o=None, ht=None,
-            h0=None, stream=None):
+            h0=None, stream=None, seg_len=0):
     d = to_dev(inp, device)
     T = inp["q"].shape[0]
     ci, co, st = la.build_chunk_meta(d["cu_seqlens"], T, stream=stream)
     fwd = la.kda_chunk_fwd if inp["kda"] else la.gdn_chunk_fwd
     o, ht = fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], ci, co,
                 h0=d["h0"] if h0 is None else h0, o=o, ht=ht, output_final_state=with_state,
-                scale=scale, dv_split=dv_split, stream=stream)
+                scale=scale, dv_split=dv_split, seg_len=seg_len, stream=stream)
     torch.cuda.synchronize()
     return o, ht, (ci, co, st)
 

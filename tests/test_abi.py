@@ -128,7 +128,46 @@ def test_workspace_size_and_split():
     assert la.dv_split_for(8192, 8, 16, 128, 128, torch.bfloat16) == 4
     assert la.dv_split_for(8192, 8, 17, 128, 128, torch.bfloat16) == 2
     assert la.dv_split_for(16384, 64, 32, 128, 128, torch.bfloat16) == 2
-    assert la.dv_split_for(65536, 1, 10, 128, 128, torch.bfloat16) == 4
+    assert la.dv_split_for(65536, 1, 10, 128, 128, torch.bfloat16, seg_len=-1) == 4
+    # segmented: 64-column slices
+    assert la.dv_split_for(65536, 1, 10, 128, 128, torch.bfloat16) == 2
     assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32) == 2
     assert la.dv_split_for(4096, 512, 2, 64, 64, torch.float32) == 1
     assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32, dv_split=1) == 1
+
+
+def test_segment_length_choice():
+    """Sequence-parallel reduce: auto segments only bf16 buckets whose
+    (sequence, head) units cannot fill half the CUs at 64 columns, about
+    NT_max * H * (d_v / 64) / 256 chunks per segment (at least 4), when a
+    T_max-token sequence would have 3 or more segments."""
+    import torch
+    bf, f32 = torch.bfloat16, torch.float32
+    assert la.seg_len_for(65536, 1, 10, 128, 128, bf) == 80      # 1024 * 10 * 2 / 256
+    assert la.seg_len_for(4096, 1, 16, 128, 128, bf) == 8        # 64 * 16 * 2 / 256
+    assert la.seg_len_for(2048, 1, 10, 128, 128, bf) == 4        # 2.5 -> at least 4
+    assert la.seg_len_for(8192, 8, 16, 128, 128, bf) == 0        # 256 units: plain
+    assert la.seg_len_for(16384, 64, 32, 128, 128, bf) == 0
+    assert la.seg_len_for(512, 1, 2, 128, 128, bf) == 0          # 8 chunks < 3 segments
+    assert la.seg_len_for(65536, 1, 10, 64, 64, f32) == 0        # fp32: plain
+    assert la.seg_len_for(65536, 1, 10, 128, 128, bf, seg_len=-1) == 0
+    assert la.seg_len_for(4096, 3, 2, 128, 128, bf, seg_len=5) == 5
+    assert la.seg_len_for(4096, 3, 2, 64, 64, f32, seg_len=5) == -1      # unsupported
+    assert la.seg_len_for(4096, 65, 2, 128, 128, bf, seg_len=5) == -1    # N_max > 64
+    assert la.seg_len_for(4096, 3, 2, 128, 128, bf, seg_len=-2) == -1
+
+
+def test_workspace_with_segments():
+    """Segmented: the images, then hin, dlt and the transition images, each
+    [segment slots][H][d_k][d_v] x 4 bytes, segment slots =
+    ceil(T_max / (64 L)) + N_max - 1."""
+    import torch
+    T, N, H, d, L = 4096, 3, 2, 128, 5
+    plain = la.workspace_bytes(T, N, H, d, d, torch.bfloat16, seg_len=-1)
+    seg = la.workspace_bytes(T, N, H, d, d, torch.bfloat16, seg_len=L)
+    ns = -(-T // (64 * L)) + N - 1
+    assert seg - plain == 3 * ns * H * d * d * 4
+    # auto: 12 units at 64 columns, NT_max = 66 -> 4 chunks per segment
+    assert la.seg_len_for(T, N, H, d, d, torch.bfloat16) == 4
+    assert la.workspace_bytes(T, N, H, d, d, torch.bfloat16) == \
+        la.workspace_bytes(T, N, H, d, d, torch.bfloat16, seg_len=4)

@@ -212,6 +212,48 @@ def test_kda_strong_channel_decay(dtype):
     assert eo <= tol and eh <= tol
 
 
+# ------------------------------------------------- segmented (sequence-parallel) reduce ---
+SEG_CU = [0, 64, 64, 130, 400, 401, 1000, 1152]   # 1, 0, 2, 5, 1, 10, 3 chunks
+
+
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+@pytest.mark.parametrize("d", [64, 128])
+@pytest.mark.parametrize("seg", [1, 2, 3])
+def test_segmented_reduce(kda, d, seg):
+    """The reduce cut into segments of `seg` chunks (first pass, combine of
+    the transitions, second pass): sequences of 0, 1, 2, 3, 5 and 10 chunks,
+    i.e. with one to ten segments, a tail chunk and a one-token sequence;
+    initial states given; against the oracle and against the one-pass
+    reduce."""
+    inp = make_inputs(SEG_CU[-1], 3, d, d, kda=kda, dtype="bf16", seed=100 + seg + d,
+                      cu_seqlens=SEG_CU, h0_std=0.1)
+    assert la.seg_len_for(SEG_CU[-1], len(SEG_CU) - 1, 3, d, d, torch.bfloat16,
+                          seg_len=seg) == seg
+    o, ht, _ = run_gpu(inp, seg_len=seg)
+    o_ref, ht_ref = run_oracle(inp)
+    eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref)
+    o1, ht1, _ = run_gpu(inp, seg_len=-1)
+    e1 = rel_err(o.float().cpu().numpy()[:SEG_CU[-1]], o1.float().cpu().numpy()[:SEG_CU[-1]])
+    _say(f"segmented kda={kda} d={d} seg={seg}: o {eo:.2e} ht {eh:.2e} vs one-pass {e1:.2e}")
+    assert eo <= tol and eh <= tol
+
+
+def test_segmented_reduce_no_state_and_padding():
+    """Segmented without h0 and without ht; canaries in padding rows survive."""
+    cu = [0, 700, 700, 1300]
+    T_max = 1500
+    inp = make_inputs(T_max, 2, 128, 128, kda=False, dtype="bf16", seed=131, cu_seqlens=cu)
+    o = torch.full((T_max, 2, 128), 321.0, device="cuda")
+    o, ht, _ = run_gpu(inp, seg_len=2, o=o, with_state=False)
+    assert ht is None
+    o_np = o.cpu().numpy()
+    assert (o_np[1300:] == 321.0).all()
+    o_ref, _ = run_oracle(inp)
+    eo = rel_err(o_np[:1300], o_ref[:1300])
+    _say(f"segmented, no state: o {eo:.2e}")
+    assert eo <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
 def test_config4_short(kda):
     inp = config(4, kda=kda, T=2048)
