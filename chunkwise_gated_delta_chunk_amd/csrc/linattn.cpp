@@ -58,7 +58,7 @@ size_t elem_bytes(const la_chunk_fwd_args *a) { return a->qkv_dtype == LA_BF16 ?
 // Chunks per segment of the sequence-parallel reduce, 0 for one workgroup
 // per sequence.  Automatic when the (sequence, head) units cannot fill half
 // the CUs even at 64 columns per workgroup: about the length that spreads
-// the capacity's chunks of all units over the CUs once, at least 4, and only
+// the capacity's chunks of all units over the CUs once, at least 8, and only
 // where the longest possible sequence then has at least 3 segments.
 int seg_for(const la_chunk_fwd_args *a) {
   if (a->seg_len < 0 || a->qkv_dtype != LA_BF16 || a->N_max > 64) return 0;
@@ -67,10 +67,25 @@ int seg_for(const la_chunk_fwd_args *a) {
   if ((int64_t)a->N_max * a->H * s2 > kCUs / 2) return 0;
   const int64_t nt = la_nt_max(a->T_max, a->N_max, a->BT);
   int64_t L = (nt * a->H * s2 + kCUs - 1) / kCUs;
-  if (L < 4) L = 4;
+  if (L < 8) L = 8;
   const int64_t longest = (a->T_max + a->BT - 1) / a->BT;
   if (longest < 3 * L) return 0;
   return (int)L;
+}
+
+// d_v slices of the segmented passes unless dv_split is given: 32 columns
+// (two compute waves, a faster chunk) while the first pass then has at most
+// two workgroups per CU (d_v / 32 output or D slices and d_k / 32 P slices
+// per segment and head), else 64 (the passes are throughput-bound)
+int seg_split(const la_chunk_fwd_args *a) {
+  if (a->dv_split) return a->dv_split;
+  const int L = seg_for(a);
+  if (L > 0) {
+    const int64_t nt = la_nt_max(a->T_max, a->N_max, a->BT);
+    const int64_t narrow = (nt + L - 1) / L * a->H * (a->d_v / 32 + a->d_k / 32);
+    if (narrow <= 2 * kCUs) return a->d_v / 32;
+  }
+  return a->d_v / 64 > 0 ? a->d_v / 64 : 1;
 }
 
 // segment slots: ceil(T_max / (BT L)) + N_max - 1
@@ -146,8 +161,9 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
       if (la::launch_chunk_reduce(rp, kda, bf, a->d_k, a->d_v / rp.S, st) != hipSuccess)
         return LA_ERR_HIP;
     } else {
-      // segments: 64 columns per workgroup (the passes are throughput-bound)
-      rp.S = a->d_v / 64 > 0 ? a->d_v / 64 : 1;
+      // segments: 64 columns per workgroup unless asked otherwise (the passes
+      // are throughput-bound)
+      rp.S = seg_split(a);
       rp.SP = a->d_k / (a->d_v / rp.S);
       rp.seg = L;
       rp.NS_max = (int)ns_max(a, L);
@@ -218,7 +234,7 @@ int la_chunk_fwd_stages(const la_chunk_fwd_args *a, int is_kda, int stages, void
 
 int32_t la_chunk_fwd_dv_split(const la_chunk_fwd_args *a) {
   if (!a || check_shape(a) != LA_OK) return 0;
-  return seg_for(a) ? (a->d_v / 64 > 0 ? a->d_v / 64 : 1) : split_for(a);
+  return seg_for(a) ? seg_split(a) : split_for(a);
 }
 
 int32_t la_chunk_fwd_seg_len(const la_chunk_fwd_args *a) {

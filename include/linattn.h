@@ -172,8 +172,9 @@ int kda_chunk_fwd(const la_chunk_fwd_args *a, void *stream);
 int la_chunk_fwd_stages(const la_chunk_fwd_args *a, int is_kda, int stages,
                         void *stream);
 
-/* The dv_split the forward uses for these arguments (after "auto"; 64-column
- * slices whenever it runs segmented). */
+/* The dv_split the forward uses for these arguments (after "auto").  Run
+ * segmented, auto takes 32-column slices while the first pass has at most
+ * 512 workgroups with them (2 per CU), else 64-column slices. */
 int32_t la_chunk_fwd_dv_split(const la_chunk_fwd_args *a);
 
 /*
@@ -187,7 +188,7 @@ int32_t la_chunk_fwd_dv_split(const la_chunk_fwd_args *a);
  * segments with output from their entering state.  Auto (seg_len = 0)
  * segments only bf16 inputs with N_max <= 64 whose (sequence, head) units
  * cannot fill half of the 256 CUs at 64 state columns per workgroup, with
- * about ceil(NT_max * H * (d_v / 64) / 256) chunks per segment (at least 4),
+ * about ceil(NT_max * H * (d_v / 64) / 256) chunks per segment (at least 8),
  * and only when a sequence of T_max tokens would have 3 segments or more.
  */
 int32_t la_chunk_fwd_seg_len(const la_chunk_fwd_args *a);

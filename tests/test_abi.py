@@ -129,7 +129,7 @@ def test_workspace_size_and_split():
     assert la.dv_split_for(8192, 8, 17, 128, 128, torch.bfloat16) == 2
     assert la.dv_split_for(16384, 64, 32, 128, 128, torch.bfloat16) == 2
     assert la.dv_split_for(65536, 1, 10, 128, 128, torch.bfloat16, seg_len=-1) == 4
-    # segmented: 64-column slices
+    # segmented: 64-column slices (13 x 10 x 8 = 1040 workgroups at 32)
     assert la.dv_split_for(65536, 1, 10, 128, 128, torch.bfloat16) == 2
     assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32) == 2
     assert la.dv_split_for(4096, 512, 2, 64, 64, torch.float32) == 1
@@ -145,10 +145,14 @@ def test_segment_length_choice():
     bf, f32 = torch.bfloat16, torch.float32
     assert la.seg_len_for(65536, 1, 10, 128, 128, bf) == 80      # 1024 * 10 * 2 / 256
     assert la.seg_len_for(4096, 1, 16, 128, 128, bf) == 8        # 64 * 16 * 2 / 256
-    assert la.seg_len_for(2048, 1, 10, 128, 128, bf) == 4        # 2.5 -> at least 4
+    assert la.seg_len_for(2048, 1, 10, 128, 128, bf) == 8        # 2.5 -> at least 8
+    assert la.seg_len_for(1024, 1, 10, 128, 128, bf) == 0        # 16 chunks < 3 x 8
     assert la.seg_len_for(8192, 8, 16, 128, 128, bf) == 0        # 256 units: plain
     assert la.seg_len_for(16384, 64, 32, 128, 128, bf) == 0
     assert la.seg_len_for(512, 1, 2, 128, 128, bf) == 0          # 8 chunks < 3 segments
+    # segmented slices: 32 columns while the first pass has <= 512 workgroups
+    assert la.dv_split_for(2048, 1, 10, 128, 128, bf) == 4       # 4 x 10 x 8 = 320
+    assert la.dv_split_for(4096, 1, 16, 128, 128, bf) == 2       # 8 x 16 x 8 = 1024
     assert la.seg_len_for(65536, 1, 10, 64, 64, f32) == 0        # fp32: plain
     assert la.seg_len_for(65536, 1, 10, 128, 128, bf, seg_len=-1) == 0
     assert la.seg_len_for(4096, 3, 2, 128, 128, bf, seg_len=5) == 5
@@ -167,7 +171,7 @@ def test_workspace_with_segments():
     seg = la.workspace_bytes(T, N, H, d, d, torch.bfloat16, seg_len=L)
     ns = -(-T // (64 * L)) + N - 1
     assert seg - plain == 3 * ns * H * d * d * 4
-    # auto: 12 units at 64 columns, NT_max = 66 -> 4 chunks per segment
-    assert la.seg_len_for(T, N, H, d, d, torch.bfloat16) == 4
+    # auto: 12 units at 64 columns, NT_max = 66 -> 8 chunks per segment
+    assert la.seg_len_for(T, N, H, d, d, torch.bfloat16) == 8
     assert la.workspace_bytes(T, N, H, d, d, torch.bfloat16) == \
-        la.workspace_bytes(T, N, H, d, d, torch.bfloat16, seg_len=4)
+        la.workspace_bytes(T, N, H, d, d, torch.bfloat16, seg_len=8)
