@@ -125,21 +125,26 @@ typedef struct {
 
 /*
  * Workspace the forward needs for this shape (only T_max, N_max, H, d_k, d_v,
- * BT and qkv_dtype are read); 0 if the shape is invalid.  The workspace holds
- * the map stage's results for the reduce.  With e = 2 (bf16 inputs: fp16
- * values) or 4 (fp32 inputs) and cells = NT_max * H, in this order, each
- * region indexed [slot][head] and starting on a 256-byte boundary:
- *   Tn  cells x [BT][BT]  T = A^-1 diag(beta) with its diagonal removed
- *   M   cells x [BT][BT]  masked decayed Q K^T (lower triangle incl. diagonal)
- *   vec cells x [192 + d_k] fp32: exp(G_r), exp(G_C - G_r), beta_r (BT each),
- *                         then the state decay of each key row
- * and for KDA also
- *   Kd  cells x [BT][d_k] K * exp(G);   Qd cells x [BT][d_k] Q * exp(G)
- *   Kbt cells x [d_k][BT] (K * exp(G_C - G))^T
- * where G is the chunk-local cumulative gate and G_C its last row.  For e = 2
- * the column index of each row is stored permuted inside every 32-column
- * block (the MFMA operand order of the reduce).  Content between calls is
- * unspecified.
+ * BT, qkv_dtype, dv_split and seg_len are read); 0 if the shape is invalid.
+ * It holds the map stage's results for the reduce: one image per
+ * (chunk slot, head) cell, NT_max * H cells in slot-major order, each a
+ * multiple of 1 KiB.  With e = 2 (bf16 inputs: fp16 values) or 4 (fp32
+ * inputs), a cell holds in order
+ *   K, Q  [BT][d_k]  the chunk's keys and queries (KDA: K*exp(G), Q*exp(G))
+ *   KT    [d_k][BT]  KDA: (K*exp(G_C - G))^T; fp32 inputs: K^T; absent for
+ *                    GDN with bf16 inputs
+ *   Tn    [BT][BT]   T = A^-1 diag(beta) with its diagonal removed
+ *   M     [BT][BT]   masked decayed Q K^T (lower triangle incl. diagonal)
+ *   vec   [192 + d_k] fp32: exp(G_r), exp(G_C - G_r), beta_r (BT each), then
+ *                    the state decay of each key row; padded to 1 KiB
+ * where G is the chunk-local cumulative gate and G_C its last row.  Matrices
+ * are rows of 16-byte pieces whose piece index is XOR-swizzled per row; for
+ * e = 2 the column index inside every 32-column block is stored permuted
+ * (the MFMA operand order of the reduce).  When the reduce runs segmented
+ * (la_chunk_fwd_seg_len), the images are followed by hin and dlt
+ * ([d_k][d_v] fp32) and the transition images (2 x [d_k][d_k] fp16), each
+ * [NS_max][H], NS_max = ceil(T_max / (BT * seg_len)) + N_max - 1.  Content
+ * between calls is unspecified.
  */
 size_t la_chunk_fwd_workspace_bytes(const la_chunk_fwd_args *shape, int is_kda);
 
