@@ -24,6 +24,7 @@ import torch
 __all__ = [
     "LinAttnError", "lib", "nt_max", "build_chunk_meta", "workspace_bytes",
     "gdn_chunk_fwd", "kda_chunk_fwd", "chunk_fwd_stages", "dv_split_for", "seg_len_for",
+    "gdn_recurrent_fwd", "kda_recurrent_fwd",
     "STAGE_MAP", "STAGE_REDUCE", "META_BAD_START", "META_NOT_MONOTONE",
     "META_OVER_CAPACITY", "LIB_PATH",
 ]
@@ -56,6 +57,17 @@ class ChunkFwdArgs(ctypes.Structure):
     ]
 
 
+class RecurrentArgs(ctypes.Structure):
+    _fields_ = [
+        ("N", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+        ("qkv_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("h0", ctypes.c_void_p),
+        ("o", ctypes.c_void_p), ("ht", ctypes.c_void_p),
+    ]
+
+
 _lib = None
 
 
@@ -85,6 +97,10 @@ def lib():
         L.la_chunk_fwd_dv_split.argtypes = [P]
         L.la_chunk_fwd_seg_len.restype = ctypes.c_int32
         L.la_chunk_fwd_seg_len.argtypes = [P]
+        R = ctypes.POINTER(RecurrentArgs)
+        for f in (L.gdn_recurrent_fwd, L.kda_recurrent_fwd):
+            f.restype = ctypes.c_int
+            f.argtypes = [R, ctypes.c_void_p]
         L.la_status_string.restype = ctypes.c_char_p
         L.la_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -266,3 +282,54 @@ def chunk_fwd_stages(kda, stages, q, k, v, g, beta, cu_seqlens, chunk_indices, c
     """Run STAGE_MAP and/or STAGE_REDUCE of the forward (la_chunk_fwd_stages)."""
     return _call("la_chunk_fwd_stages", bool(kda), stages, q, k, v, g, beta, cu_seqlens,
                  chunk_indices, chunk_offsets, **kw)
+
+
+def _recurrent(name, kda, q, k, v, g, beta, h0=None, o=None, ht=None, output_final_state=True,
+               scale=1.0, stream=None):
+    if q.dtype not in (torch.bfloat16, torch.float32):
+        raise ValueError(f"q must be bfloat16 or float32, got {q.dtype}")
+    if q.dim() != 3:
+        raise ValueError("q must be [N, H, d_k]")
+    N, H, d_k = q.shape
+    d_v = v.shape[-1]
+    dev = q.device
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (N, H, d_k), dev)
+    _need(v, "v", q.dtype, (N, H, d_v), dev)
+    _need(g, "g", torch.float32, (N, H, d_k) if kda else (N, H), dev)
+    _need(beta, "beta", torch.float32, (N, H), dev)
+    st_shape = (N, H, d_k, d_v)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, st_shape, dev)
+    if o is None:
+        o = torch.empty((N, H, d_v), dtype=torch.float32, device=dev)
+    _need(o, "o", torch.float32, (N, H, d_v), dev)
+    if ht is None and output_final_state:
+        ht = torch.empty(st_shape, dtype=torch.float32, device=dev)
+    if ht is not None:
+        _need(ht, "ht", torch.float32, st_shape, dev)
+    a = RecurrentArgs()
+    a.N, a.H, a.d_k, a.d_v = N, H, d_k, d_v
+    a.qkv_dtype = LA_BF16 if q.dtype == torch.bfloat16 else LA_F32
+    a.scale = float(scale)
+    a.q, a.k, a.v, a.g, a.beta = (t.data_ptr() for t in (q, k, v, g, beta))
+    a.h0 = None if h0 is None else h0.data_ptr()
+    a.o = o.data_ptr()
+    a.ht = None if ht is None else ht.data_ptr()
+    L = lib()
+    f = L.kda_recurrent_fwd if kda else L.gdn_recurrent_fwd
+    rc = f(ctypes.byref(a), _stream(stream))
+    if rc != 0:
+        raise LinAttnError(rc, name)
+    return o, ht
+
+
+def gdn_recurrent_fwd(q, k, v, g, beta, **kw):
+    """One GDN decode step (q, k, v [N, H, d]; g, beta [N, H]); returns (o, ht).
+    ht=h0 updates the state in place."""
+    return _recurrent("gdn_recurrent_fwd", False, q, k, v, g, beta, **kw)
+
+
+def kda_recurrent_fwd(q, k, v, g, beta, **kw):
+    """One KDA decode step (g [N, H, d_k]); returns (o, ht)."""
+    return _recurrent("kda_recurrent_fwd", True, q, k, v, g, beta, **kw)

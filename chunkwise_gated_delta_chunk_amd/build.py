@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblinattn.so")
-SOURCES = ["meta.hip", "chunk_map.hip", "chunk_reduce.hip", "chunk_combine.hip", "linattn.cpp"]
+SOURCES = ["meta.hip", "chunk_map.hip", "chunk_reduce.hip", "chunk_combine.hip", "recurrent.hip",
+           "linattn.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

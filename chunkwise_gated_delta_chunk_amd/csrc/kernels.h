@@ -44,6 +44,15 @@ struct CombineParams {
   const _Float16 *pimg;
 };
 
+// One recurrent step per (sequence, head) unit (recurrent.hip).
+struct RecurrentParams {
+  const void *q, *k, *v;
+  const float *g, *beta, *h0;
+  float *o, *ht;
+  int units;  // N * H
+  float scale;
+};
+
 hipError_t launch_chunk_meta(const int32_t *cu, int N_max, int T_max, int BT, int NT_max,
                              int32_t *ci, int32_t *co, int32_t *status, hipStream_t stream);
 hipError_t launch_chunk_map(const MapParams &p, bool kda, bool bf16_in, int dk, hipStream_t st);
@@ -51,5 +60,7 @@ hipError_t launch_chunk_map(const MapParams &p, bool kda, bool bf16_in, int dk, 
 hipError_t launch_chunk_reduce(const ReduceParams &p, bool kda, bool bf16_in, int dk, int W,
                                hipStream_t st);
 hipError_t launch_chunk_combine(const CombineParams &p, int dk, hipStream_t st);
+hipError_t launch_recurrent(const RecurrentParams &p, bool kda, bool bf16_in, int dk,
+                            hipStream_t st);
 
 }  // namespace la

@@ -242,6 +242,42 @@ int32_t la_chunk_fwd_seg_len(const la_chunk_fwd_args *a) {
   return seg_for(a);
 }
 
+static int recurrent(const la_recurrent_args *a, bool kda, void *stream) {
+  if (!a) return LA_ERR_NULL;
+  if (a->N < 1 || a->H < 1) return LA_ERR_SHAPE;
+  if ((int64_t)a->N * a->H > 0x7fffffff) return LA_ERR_SHAPE;
+  if (a->qkv_dtype != LA_BF16 && a->qkv_dtype != LA_F32) return LA_ERR_DTYPE;
+  if (a->d_k != a->d_v || (a->d_k != 64 && a->d_k != 128)) return LA_ERR_UNSUPPORTED;
+  if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o) return LA_ERR_NULL;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->k) |
+                        reinterpret_cast<uintptr_t>(a->v) | reinterpret_cast<uintptr_t>(a->o) |
+                        reinterpret_cast<uintptr_t>(a->h0) | reinterpret_cast<uintptr_t>(a->ht);
+  if (mis % 16 != 0) return LA_ERR_SHAPE;
+  if (a->h0 && a->ht && a->h0 != a->ht) {
+    const size_t sb = (size_t)a->N * a->H * a->d_k * a->d_v * sizeof(float);
+    if (overlaps(a->h0, sb, a->ht, sb)) return LA_ERR_ALIAS;
+  }
+  la::RecurrentParams rp{};
+  rp.q = a->q;
+  rp.k = a->k;
+  rp.v = a->v;
+  rp.g = a->g;
+  rp.beta = a->beta;
+  rp.h0 = a->h0;
+  rp.o = a->o;
+  rp.ht = a->ht;
+  rp.units = a->N * a->H;
+  rp.scale = a->scale;
+  if (la::launch_recurrent(rp, kda, a->qkv_dtype == LA_BF16, a->d_k,
+                           static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LA_ERR_HIP;
+  return LA_OK;
+}
+
+int gdn_recurrent_fwd(const la_recurrent_args *a, void *stream) { return recurrent(a, false, stream); }
+
+int kda_recurrent_fwd(const la_recurrent_args *a, void *stream) { return recurrent(a, true, stream); }
+
 const char *la_status_string(int status) {
   switch (status) {
     case LA_OK: return "ok";

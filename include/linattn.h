@@ -198,6 +198,38 @@ int32_t la_chunk_fwd_dv_split(const la_chunk_fwd_args *a);
  */
 int32_t la_chunk_fwd_seg_len(const la_chunk_fwd_args *a);
 
+/* Arguments of one recurrent (decode) step: one token per sequence. */
+typedef struct {
+    int32_t N, H;              /* sequences (one token each) and heads (>= 1)    */
+    int32_t d_k, d_v;          /* d_k == d_v: 64 or 128                          */
+    int32_t qkv_dtype;         /* LA_BF16 or LA_F32: dtype of q, k, v            */
+    float scale;               /* o = scale * S q                                */
+    const void *q, *k;         /* [N][H][d_k], qkv_dtype                         */
+    const void *v;             /* [N][H][d_v], qkv_dtype                         */
+    const float *g;            /* log-decay: GDN [N][H]; KDA [N][H][d_k]         */
+    const float *beta;         /* [N][H]                                         */
+    const float *h0;           /* [N][H][d_k][d_v] or NULL (zero state)          */
+    float *o;                  /* [N][H][d_v] fp32                               */
+    float *ht;                 /* [N][H][d_k][d_v] or NULL; may equal h0         */
+} la_recurrent_args;
+
+/*
+ * One step of the recurrence per sequence n and head h (the token-level
+ * form the chunk forward computes in bulk): with alpha = exp(g),
+ *   H = diag(alpha) h0[n][h];  u = beta (v - H^T k);  H += k u^T;
+ *   ht[n][h] = H;  o[n][h] = scale H^T q
+ * (H = S^T, [d_k][d_v] fp32; alpha one value per (n, h) for GDN, one per key
+ * channel for KDA).  ht == h0 updates the state in place; a partial overlap
+ * is LA_ERR_ALIAS.  Arithmetic is fp32 throughout.  One launch, no
+ * workspace, capturable.
+ * Host errors: LA_ERR_NULL (q, k, v, g, beta or o NULL), LA_ERR_SHAPE (N or
+ * H < 1, N * H beyond 2^31 - 1, or q, k, v, h0, ht, o not 16-byte aligned),
+ * LA_ERR_DTYPE, LA_ERR_UNSUPPORTED (d_k != d_v or not 64 / 128),
+ * LA_ERR_ALIAS, LA_ERR_HIP.
+ */
+int gdn_recurrent_fwd(const la_recurrent_args *a, void *stream);
+int kda_recurrent_fwd(const la_recurrent_args *a, void *stream);
+
 /* Static text for a la_status value. */
 const char *la_status_string(int status);
 

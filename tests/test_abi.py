@@ -175,3 +175,39 @@ def test_workspace_with_segments():
     assert la.seg_len_for(T, N, H, d, d, torch.bfloat16) == 8
     assert la.workspace_bytes(T, N, H, d, d, torch.bfloat16) == \
         la.workspace_bytes(T, N, H, d, d, torch.bfloat16, seg_len=8)
+
+
+def _rargs(**kw):
+    a = la.RecurrentArgs()
+    a.N, a.H, a.d_k, a.d_v, a.qkv_dtype, a.scale = 4, 2, 128, 128, 0, 1.0
+    fake = 0x100000  # never dereferenced: every case fails before launch
+    for f in ("q", "k", "v", "g", "beta", "o"):
+        setattr(a, f, fake)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+RBAD = [
+    ("null q", dict(q=None), -1),
+    ("null beta", dict(beta=None), -1),
+    ("null o", dict(o=None), -1),
+    ("N 0", dict(N=0), -2),
+    ("H 0", dict(H=0), -2),
+    ("N*H too big", dict(N=1 << 20, H=1 << 12), -2),
+    ("dtype 5", dict(qkv_dtype=5), -3),
+    ("d 96", dict(d_k=96, d_v=96), -4),
+    ("d_k != d_v", dict(d_v=64), -4),
+    ("v misaligned", dict(v=0x100004), -2),
+    ("h0 misaligned", dict(h0=0x100008), -2),
+    ("ht partly over h0", dict(h0=0x200000, ht=0x200000 + 4096), -6),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", RBAD, ids=[b[0] for b in RBAD])
+def test_recurrent_rejects_on_host(name, kw, code):
+    a = _rargs(**kw)
+    L = la.lib()
+    assert L.gdn_recurrent_fwd(ctypes.byref(a), None) == code
+    assert L.kda_recurrent_fwd(ctypes.byref(a), None) == code
+    assert L.gdn_recurrent_fwd(None, None) == -1
