@@ -47,7 +47,8 @@ class ChunkFwdArgs(ctypes.Structure):
         ("T_max", ctypes.c_int32), ("N_max", ctypes.c_int32), ("H", ctypes.c_int32),
         ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("BT", ctypes.c_int32),
         ("qkv_dtype", ctypes.c_int32), ("dv_split", ctypes.c_int32),
-        ("seg_len", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("seg_len", ctypes.c_int32), ("H_qk", ctypes.c_int32), ("o_bf16", ctypes.c_int32),
+        ("scale", ctypes.c_float),
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
         ("cu_seqlens", ctypes.c_void_p), ("chunk_indices", ctypes.c_void_p),
@@ -61,7 +62,8 @@ class RecurrentArgs(ctypes.Structure):
     _fields_ = [
         ("N", ctypes.c_int32), ("H", ctypes.c_int32),
         ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
-        ("qkv_dtype", ctypes.c_int32), ("scale", ctypes.c_float),
+        ("qkv_dtype", ctypes.c_int32), ("H_qk", ctypes.c_int32), ("o_bf16", ctypes.c_int32),
+        ("scale", ctypes.c_float),
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("h0", ctypes.c_void_p),
         ("o", ctypes.c_void_p), ("ht", ctypes.c_void_p),
@@ -200,17 +202,35 @@ def seg_len_for(T_max, N_max, H, d_k, d_v, qkv_dtype, seg_len=0):
     return int(lib().la_chunk_fwd_seg_len(ctypes.byref(a)))
 
 
+def _heads(q, v, what):
+    """(value heads, q/k heads) of q [.., H_qk, d_k] and v [.., H, d_v]."""
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError(f"q and v must be [{what}, heads, d]")
+    H, H_qk = v.shape[1], q.shape[1]
+    if H_qk < 1 or H % H_qk:
+        raise ValueError(f"value heads ({H}) must be a multiple of q/k heads ({H_qk})")
+    return H, H_qk
+
+
+def _out(o, o_dtype, shape, dev):
+    if o is None:
+        o = torch.empty(shape, dtype=o_dtype or torch.float32, device=dev)
+    if o.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"o must be float32 or bfloat16, got {o.dtype}")
+    _need(o, "o", o.dtype, shape, dev)
+    return o
+
+
 def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0, o, ht,
-             output_final_state, workspace, scale, dv_split, seg_len):
+             output_final_state, workspace, scale, dv_split, seg_len, o_dtype=None):
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError(f"q must be bfloat16 or float32, got {q.dtype}")
-    if q.dim() != 3:
-        raise ValueError("q must be [T_max, H, d_k]")
-    T_max, H, d_k = q.shape
+    H, H_qk = _heads(q, v, "T_max")
+    T_max, _, d_k = q.shape
     d_v = v.shape[-1]
     dev = q.device
     _need(q, "q", q.dtype)
-    _need(k, "k", q.dtype, (T_max, H, d_k), dev)
+    _need(k, "k", q.dtype, (T_max, H_qk, d_k), dev)
     _need(v, "v", q.dtype, (T_max, H, d_v), dev)
     _need(g, "g", torch.float32, (T_max, H, d_k) if kda else (T_max, H), dev)
     _need(beta, "beta", torch.float32, (T_max, H), dev)
@@ -222,14 +242,14 @@ def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0
     st_shape = (N_max, H, d_k, d_v)
     if h0 is not None:
         _need(h0, "h0", torch.float32, st_shape, dev)
-    if o is None:
-        o = torch.empty((T_max, H, d_v), dtype=torch.float32, device=dev)
-    _need(o, "o", torch.float32, (T_max, H, d_v), dev)
+    o = _out(o, o_dtype, (T_max, H, d_v), dev)
     if ht is None and output_final_state:
         ht = torch.empty(st_shape, dtype=torch.float32, device=dev)
     if ht is not None:
         _need(ht, "ht", torch.float32, st_shape, dev)
     a = _shape_args(T_max, N_max, H, d_k, d_v, q.dtype, dv_split, seg_len=seg_len)
+    a.H_qk = H_qk
+    a.o_bf16 = int(o.dtype == torch.bfloat16)
     need = int(lib().la_chunk_fwd_workspace_bytes(ctypes.byref(a), int(kda)))
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
@@ -249,10 +269,10 @@ def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0
 
 def _call(name, kda, stages, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, *,
           h0=None, o=None, ht=None, output_final_state=True, workspace=None, scale=1.0,
-          dv_split=0, seg_len=0, stream=None):
+          dv_split=0, seg_len=0, o_dtype=None, stream=None):
     a, o, ht, workspace = _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices,
                                    chunk_offsets, h0, o, ht, output_final_state, workspace,
-                                   scale, dv_split, seg_len)
+                                   scale, dv_split, seg_len, o_dtype)
     L = lib()
     s = _stream(stream)
     if stages is None:
@@ -285,31 +305,30 @@ def chunk_fwd_stages(kda, stages, q, k, v, g, beta, cu_seqlens, chunk_indices, c
 
 
 def _recurrent(name, kda, q, k, v, g, beta, h0=None, o=None, ht=None, output_final_state=True,
-               scale=1.0, stream=None):
+               scale=1.0, o_dtype=None, stream=None):
     if q.dtype not in (torch.bfloat16, torch.float32):
         raise ValueError(f"q must be bfloat16 or float32, got {q.dtype}")
-    if q.dim() != 3:
-        raise ValueError("q must be [N, H, d_k]")
-    N, H, d_k = q.shape
+    H, H_qk = _heads(q, v, "N")
+    N, _, d_k = q.shape
     d_v = v.shape[-1]
     dev = q.device
     _need(q, "q", q.dtype)
-    _need(k, "k", q.dtype, (N, H, d_k), dev)
+    _need(k, "k", q.dtype, (N, H_qk, d_k), dev)
     _need(v, "v", q.dtype, (N, H, d_v), dev)
     _need(g, "g", torch.float32, (N, H, d_k) if kda else (N, H), dev)
     _need(beta, "beta", torch.float32, (N, H), dev)
     st_shape = (N, H, d_k, d_v)
     if h0 is not None:
         _need(h0, "h0", torch.float32, st_shape, dev)
-    if o is None:
-        o = torch.empty((N, H, d_v), dtype=torch.float32, device=dev)
-    _need(o, "o", torch.float32, (N, H, d_v), dev)
+    o = _out(o, o_dtype, (N, H, d_v), dev)
     if ht is None and output_final_state:
         ht = torch.empty(st_shape, dtype=torch.float32, device=dev)
     if ht is not None:
         _need(ht, "ht", torch.float32, st_shape, dev)
     a = RecurrentArgs()
     a.N, a.H, a.d_k, a.d_v = N, H, d_k, d_v
+    a.H_qk = H_qk
+    a.o_bf16 = int(o.dtype == torch.bfloat16)
     a.qkv_dtype = LA_BF16 if q.dtype == torch.bfloat16 else LA_F32
     a.scale = float(scale)
     a.q, a.k, a.v, a.g, a.beta = (t.data_ptr() for t in (q, k, v, g, beta))

@@ -90,8 +90,10 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   T *sMt = reinterpret_cast<T *>(sX);
   static_assert(kBT * LDM * sizeof(T) <= kBT * LDL * sizeof(float), "M inside X");
 
-  const int slot = blockIdx.x;
-  const int h = blockIdx.y;
+  // heads vary fastest: the workgroups of one slot run together and share
+  // the L2 lines of its token rows (q, k rows of adjacent heads, g, beta)
+  const int h = blockIdx.x % p.H;
+  const int slot = blockIdx.x / p.H;
   const int i_n = p.chunk_indices[2 * slot];
   if (i_n < 0) return;  // sentinel: nothing to do, nothing written
   const int i_t = p.chunk_indices[2 * slot + 1];
@@ -130,6 +132,7 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
     static_assert(kBT * UPR % kThreads == 0, "staging split");
     const In *q = static_cast<const In *>(p.q);
     const In *k = static_cast<const In *>(p.k);
+    const int hqk = h / (H / p.Hqk);  // grouped value heads share q and k
     u32x4 kraw[NU][NP], qraw[NU][NP];
 #pragma unroll
     for (int it = 0; it < NU; ++it) {
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
         kraw[it][j] = u32x4{0, 0, 0, 0};
         qraw[it][j] = u32x4{0, 0, 0, 0};
         if (r < C) {
-          const size_t off = ((size_t)(r0 + r) * H + h) * DK + piece * VEC;
+          const size_t off = ((size_t)(r0 + r) * p.Hqk + hqk) * DK + piece * VEC;
           kraw[it][j] = *reinterpret_cast<const u32x4 *>(k + off);
           qraw[it][j] = *reinterpret_cast<const u32x4 *>(q + off);
         }
@@ -538,7 +541,7 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
 
 template <bool KDA, typename In, int DK>
 static hipError_t launch_map_t(const MapParams &p, hipStream_t st) {
-  hipLaunchKernelGGL((chunk_map_kernel<KDA, In, DK>), dim3(p.NT_max, p.H), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((chunk_map_kernel<KDA, In, DK>), dim3(p.H * p.NT_max), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
 

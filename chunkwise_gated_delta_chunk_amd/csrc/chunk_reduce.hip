@@ -113,7 +113,8 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
   const int lr = lane & 15, lg = lane >> 4;
   const int cw = wk.col0 + 16 * w;                   // this wave's first state column
   const int rs_v = H * DV * (int)sizeof(In);         // token stride of v (bytes)
-  const int rs_o = H * DV * 4;                       // token stride of o (bytes)
+  const int osz = p.o_bf16 ? 2 : 4;                  // o element bytes
+  const int rs_o = H * DV * osz;                     // token stride of o (bytes)
 
   // ---------------------------------------------------------------- staging
   // One extra wave per workgroup does all the staging: piece q (1 KiB) of a
@@ -198,9 +199,23 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
 
   int off_o[4];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) off_o[e] = (lg * 4 + e) * rs_o + (cw + lr) * 4;
-  float *o_c = p.o + ((size_t)wk.t0 * H + h) * DV;
-  const size_t o_step = (size_t)kBT * H * DV;
+  for (int e = 0; e < 4; ++e) off_o[e] = (lg * 4 + e) * rs_o + (cw + lr) * osz;
+  char *o_c = static_cast<char *>(p.o) + ((size_t)wk.t0 * H + h) * DV * osz;
+  const size_t o_step = (size_t)kBT * H * DV * osz;
+  // 4 output rows of a row tile: fp32, or bf16 rounded to nearest even
+  auto store_o = [&](int R, int C, const f32x4 &oa) {
+    const auto ro = buffer_rsrc(o_c + (size_t)16 * R * rs_o, (C - 16 * R) * rs_o);
+    if (p.o_bf16) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(p.scale * oa[e]), ro,
+                                              off_o[e], 0, 0);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p.scale * oa[e]), ro, off_o[e], 0, 0);
+    }
+  };
 
   // ---------------------------------------------------------- one chunk
   // buffer BUF holds chunk jj; the copy of the next chunk, if any, goes to
@@ -410,12 +425,7 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
         });
         if constexpr (!HAS_KT) read_kt(std::integral_constant<int, NHT / 2>{});
 #pragma unroll
-        for (int R = 0; R < 4; ++R) {
-          const auto ro = buffer_rsrc(o_c + (size_t)16 * R * H * DV, (C - 16 * R) * rs_o);
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p.scale * oa[R][e]), ro, off_o[e], 0, 0);
-        }
+        for (int R = 0; R < 4; ++R) store_o(R, C, oa[R]);
       } else {
         if constexpr (!HAS_KT) read_kt(std::integral_constant<int, NHT / 2>{});
       }
@@ -463,10 +473,7 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
 #pragma unroll
         for (int s = 0; s < ksteps_lower<O>(R); ++s)
           oa = O::mfma(a_frag_img<O, PT>(tMM, 16 * R, s, lane), ufr[s], oa);
-        const auto ro = buffer_rsrc(o_c + (size_t)16 * R * H * DV, (C - 16 * R) * rs_o);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p.scale * oa[e]), ro, off_o[e], 0, 0);
+        store_o(R, C, oa);
       }
     }
 

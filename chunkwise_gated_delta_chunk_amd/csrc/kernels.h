@@ -15,6 +15,7 @@ struct MapParams {
   const float *g, *beta;
   const int32_t *cu_seqlens, *chunk_indices;
   int H, NT_max;
+  int Hqk;  // q, k heads: value head h reads q, k head h / (H / Hqk)
   void *img;
 };
 
@@ -22,10 +23,12 @@ struct ReduceParams {
   const void *v;
   const int32_t *cu_seqlens, *chunk_offsets;
   const float *h0;
-  float *o, *ht;
+  void *o;       // fp32, or bf16 with o_bf16
+  float *ht;
   const void *img;
   int H, N_max, S;  // S = d_v slices per (sequence, head)
   float scale;
+  int o_bf16;
   // sequence-parallel reduce (chunk_reduce.hip): seg = chunks per segment
   // (0: one workgroup walks a whole sequence), pass 1 or 2, SP = d_k slices
   // of the transitions, NS_max segment slots; per (segment slot, head):
@@ -48,9 +51,12 @@ struct CombineParams {
 struct RecurrentParams {
   const void *q, *k, *v;
   const float *g, *beta, *h0;
-  float *o, *ht;
-  int units;  // N * H
+  void *o;       // fp32, or bf16 with o_bf16
+  float *ht;
+  int units;     // N * H
+  int H, Hqk;    // value heads, q / k heads
   float scale;
+  int o_bf16;
 };
 
 hipError_t launch_chunk_meta(const int32_t *cu, int N_max, int T_max, int BT, int NT_max,

@@ -197,6 +197,13 @@ __device__ __host__ constexpr ImageLayout image_layout(bool kda, int e, int dk) 
 }
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
+// fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN)
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  const uint32_t b = __float_as_uint(x);
+  if ((b & 0x7fffffffu) > 0x7f800000u) return (b >> 16) | 0x40u;
+  return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
+}
+
 // A generic pointer into LDS holds the LDS byte offset in its low 32 bits
 // (the LDS aperture is 4 GiB aligned); taking it from there, rather than by an
 // address-space cast, needs no null check.  Only for pointers into LDS.

@@ -22,6 +22,8 @@ int check_shape(const la_chunk_fwd_args *a) {
   if (a->T_max < 1 || a->N_max < 1 || a->H < 1) return LA_ERR_SHAPE;
   if (a->T_max > 0x7fffffff - 2 * kBTSupported) return LA_ERR_SHAPE;
   if (a->qkv_dtype != LA_BF16 && a->qkv_dtype != LA_F32) return LA_ERR_DTYPE;
+  if (a->o_bf16 != 0 && a->o_bf16 != 1) return LA_ERR_DTYPE;
+  if (a->H_qk < 0 || (a->H_qk > 0 && a->H % a->H_qk != 0)) return LA_ERR_SHAPE;
   if (a->BT != kBTSupported) return LA_ERR_UNSUPPORTED;
   if (a->d_k != a->d_v) return LA_ERR_UNSUPPORTED;
   if (a->qkv_dtype == LA_BF16 && a->d_k != 64 && a->d_k != 128) return LA_ERR_UNSUPPORTED;
@@ -37,6 +39,7 @@ int check_shape(const la_chunk_fwd_args *a) {
   const int64_t nt = la_nt_max(a->T_max, a->N_max, a->BT);
   if (nt < 1 || nt > 0x7fffffff) return LA_ERR_SHAPE;
   if ((int64_t)a->N_max * a->H > 0x7fffffff / 8) return LA_ERR_SHAPE;
+  if (nt * a->H > 0x7fffffff) return LA_ERR_SHAPE;  // one map workgroup per cell
   // byte offsets inside one chunk of v / o (64 token rows) stay in int
   if ((int64_t)a->H * a->d_v * 4 * 64 > 0x7fffffff) return LA_ERR_SHAPE;
   return LA_OK;
@@ -124,7 +127,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
   }
   // 16-byte vector loads of q, k and v rows
   const uintptr_t mis = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->k) |
-                        reinterpret_cast<uintptr_t>(a->v);
+                        reinterpret_cast<uintptr_t>(a->v) | reinterpret_cast<uintptr_t>(a->o);
   if (mis % 16 != 0) return LA_ERR_SHAPE;
 
   const bool bf = a->qkv_dtype == LA_BF16;
@@ -139,6 +142,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     mp.cu_seqlens = a->cu_seqlens;
     mp.chunk_indices = a->chunk_indices;
     mp.H = a->H;
+    mp.Hqk = a->H_qk ? a->H_qk : a->H;
     mp.NT_max = (int)la_nt_max(a->T_max, a->N_max, a->BT);
     mp.img = ws;
     if (la::launch_chunk_map(mp, kda, bf, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
@@ -156,6 +160,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     rp.N_max = a->N_max;
     rp.S = split_for(a);
     rp.scale = a->scale;
+    rp.o_bf16 = a->o_bf16;
     const int L = seg_for(a);
     if (L == 0) {
       if (la::launch_chunk_reduce(rp, kda, bf, a->d_k, a->d_v / rp.S, st) != hipSuccess)
@@ -247,6 +252,8 @@ static int recurrent(const la_recurrent_args *a, bool kda, void *stream) {
   if (a->N < 1 || a->H < 1) return LA_ERR_SHAPE;
   if ((int64_t)a->N * a->H > 0x7fffffff) return LA_ERR_SHAPE;
   if (a->qkv_dtype != LA_BF16 && a->qkv_dtype != LA_F32) return LA_ERR_DTYPE;
+  if (a->o_bf16 != 0 && a->o_bf16 != 1) return LA_ERR_DTYPE;
+  if (a->H_qk < 0 || (a->H_qk > 0 && a->H % a->H_qk != 0)) return LA_ERR_SHAPE;
   if (a->d_k != a->d_v || (a->d_k != 64 && a->d_k != 128)) return LA_ERR_UNSUPPORTED;
   if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->o) return LA_ERR_NULL;
   const uintptr_t mis = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->k) |
@@ -267,7 +274,10 @@ static int recurrent(const la_recurrent_args *a, bool kda, void *stream) {
   rp.o = a->o;
   rp.ht = a->ht;
   rp.units = a->N * a->H;
+  rp.H = a->H;
+  rp.Hqk = a->H_qk ? a->H_qk : a->H;
   rp.scale = a->scale;
+  rp.o_bf16 = a->o_bf16;
   if (la::launch_recurrent(rp, kda, a->qkv_dtype == LA_BF16, a->d_k,
                            static_cast<hipStream_t>(stream)) != hipSuccess)
     return LA_ERR_HIP;

@@ -40,8 +40,11 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecurrentParams p) {
   const int t = threadIdx.x;
   const int cq = t % QD, rg = t / QD;
   const int c0 = 4 * cq, r0 = rg * RPG;
-  const In *q = static_cast<const In *>(p.q) + (size_t)unit * DK;
-  const In *k = static_cast<const In *>(p.k) + (size_t)unit * DK;
+  // grouped value heads share q and k: value head h reads q, k head h / (H / Hqk)
+  const int n = unit / p.H, hqk = (unit % p.H) / (p.H / p.Hqk);
+  const size_t uqk = (size_t)n * p.Hqk + hqk;
+  const In *q = static_cast<const In *>(p.q) + uqk * DK;
+  const In *k = static_cast<const In *>(p.k) + uqk * DK;
   const In *v = static_cast<const In *>(p.v) + (size_t)unit * DV;
   const size_t sb = (size_t)unit * DK * DV;
 
@@ -98,7 +101,14 @@ __global__ __launch_bounds__(256) void recurrent_kernel(RecurrentParams p) {
       for (int e = 0; e < 4; ++e) ot[e] += sred[g2][cq][e];
 #pragma unroll
     for (int e = 0; e < 4; ++e) ot[e] *= p.scale;
-    *reinterpret_cast<f32x4 *>(p.o + (size_t)unit * DV + c0) = ot;
+    if (p.o_bf16) {
+      uint2 b;
+      b.x = f32_to_bf16_rne(ot[0]) | (f32_to_bf16_rne(ot[1]) << 16);
+      b.y = f32_to_bf16_rne(ot[2]) | (f32_to_bf16_rne(ot[3]) << 16);
+      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(p.o) + (size_t)unit * DV + c0) = b;
+    } else {
+      *reinterpret_cast<f32x4 *>(static_cast<float *>(p.o) + (size_t)unit * DV + c0) = ot;
+    }
   }
 }
 

@@ -109,15 +109,19 @@ typedef struct {
     int32_t seg_len;           /* sequence-parallel reduce: chunks per segment;  */
                                /* -1 = off, 0 = auto, > 0 needs bf16 inputs and  */
                                /* N_max <= 64 (see la_chunk_fwd_seg_len)         */
+    int32_t H_qk;              /* q, k heads: 0 = H; else H % H_qk == 0 and      */
+                               /* value head h reads q, k head h / (H / H_qk)    */
+                               /* (grouped value heads share keys and queries)   */
+    int32_t o_bf16;            /* 0: o fp32; 1: o bf16, rounded to nearest even  */
     float scale;               /* o = scale * S q                                */
-    const void *q, *k, *v;     /* [T_max][H][d_k] / [T_max][H][d_v], qkv_dtype   */
+    const void *q, *k, *v;     /* [T_max][H_qk][d_k] / [T_max][H][d_v], qkv_dtype */
     const float *g;            /* log-decay: GDN [T_max][H]; KDA [T_max][H][d_k] */
     const float *beta;         /* [T_max][H]                                     */
     const int32_t *cu_seqlens; /* [N_max+1]                                      */
     const int32_t *chunk_indices; /* [NT_max][2], from build_chunk_meta          */
     const int32_t *chunk_offsets; /* [N_max+1], from build_chunk_meta            */
     const float *h0;           /* [N_max][H][d_k][d_v] or NULL (zero state)      */
-    float *o;                  /* [T_max][H][d_v] fp32 output                    */
+    void *o;                   /* [T_max][H][d_v] fp32 (bf16 with o_bf16)        */
     float *ht;                 /* [N_max][H][d_k][d_v] or NULL; may equal h0     */
     void *workspace;           /* >= la_chunk_fwd_workspace_bytes(...) bytes,    */
     size_t workspace_bytes;    /* 256-byte aligned                               */
@@ -203,13 +207,15 @@ typedef struct {
     int32_t N, H;              /* sequences (one token each) and heads (>= 1)    */
     int32_t d_k, d_v;          /* d_k == d_v: 64 or 128                          */
     int32_t qkv_dtype;         /* LA_BF16 or LA_F32: dtype of q, k, v            */
+    int32_t H_qk;              /* q, k heads: 0 = H; else H % H_qk == 0          */
+    int32_t o_bf16;            /* 0: o fp32; 1: o bf16 (nearest even)            */
     float scale;               /* o = scale * S q                                */
-    const void *q, *k;         /* [N][H][d_k], qkv_dtype                         */
+    const void *q, *k;         /* [N][H_qk][d_k], qkv_dtype                      */
     const void *v;             /* [N][H][d_v], qkv_dtype                         */
     const float *g;            /* log-decay: GDN [N][H]; KDA [N][H][d_k]         */
     const float *beta;         /* [N][H]                                         */
     const float *h0;           /* [N][H][d_k][d_v] or NULL (zero state)          */
-    float *o;                  /* [N][H][d_v] fp32                               */
+    void *o;                   /* [N][H][d_v] fp32 (bf16 with o_bf16)            */
     float *ht;                 /* [N][H][d_k][d_v] or NULL; may equal h0         */
 } la_recurrent_args;
 
@@ -223,9 +229,9 @@ typedef struct {
  * is LA_ERR_ALIAS.  Arithmetic is fp32 throughout.  One launch, no
  * workspace, capturable.
  * Host errors: LA_ERR_NULL (q, k, v, g, beta or o NULL), LA_ERR_SHAPE (N or
- * H < 1, N * H beyond 2^31 - 1, or q, k, v, h0, ht, o not 16-byte aligned),
- * LA_ERR_DTYPE, LA_ERR_UNSUPPORTED (d_k != d_v or not 64 / 128),
- * LA_ERR_ALIAS, LA_ERR_HIP.
+ * H < 1, N * H beyond 2^31 - 1, H_qk < 0 or not dividing H, or q, k, v, h0,
+ * ht, o not 16-byte aligned), LA_ERR_DTYPE (qkv_dtype, o_bf16 not 0 / 1),
+ * LA_ERR_UNSUPPORTED (d_k != d_v or not 64 / 128), LA_ERR_ALIAS, LA_ERR_HIP.
  */
 int gdn_recurrent_fwd(const la_recurrent_args *a, void *stream);
 int kda_recurrent_fwd(const la_recurrent_args *a, void *stream);

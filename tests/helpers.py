@@ -23,6 +23,38 @@ def rel_err(x, ref, mask=None):
     return float(np.abs(x - ref).max() / max(np.abs(ref).max(), 1e-30))
 
 
+def bf16_ulp(x):
+    """Spacing of bf16 values at |x| (normal range): 2^(floor(log2|x|) - 7)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    e = np.floor(np.log2(np.maximum(a, 2.0 ** -126)))
+    return np.exp2(e - 7)
+
+
+def rel_err_bf16_out(x, ref):
+    """rel_err of a bf16 output against the fp64 reference, allowing half a
+    bf16 ulp of the reference per element for the final rounding."""
+    x = np.asarray(x, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    over = np.maximum(np.abs(x - ref) - 0.5 * bf16_ulp(ref), 0.0)
+    return float(over.max() / max(np.abs(ref).max(), 1e-30))
+
+
+def gva(inp, H_qk):
+    """The inputs with H_qk q/k heads (every G-th head of the drawn ones,
+    G = H / H_qk) and, for the oracle, q/k expanded back to the value heads."""
+    H = inp["H"]
+    G = H // H_qk
+    small = dict(inp)
+    small["q"] = np.ascontiguousarray(inp["q"][:, ::G])
+    small["k"] = np.ascontiguousarray(inp["k"][:, ::G])
+    full = dict(inp)
+    full["q"] = np.repeat(small["q"], G, axis=1)
+    full["k"] = np.repeat(small["k"], G, axis=1)
+    return small, full
+
+
 def to_dev(inp, device="cuda"):
     tdt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
     d = {}
@@ -36,14 +68,14 @@ def to_dev(inp, device="cuda"):
 
 
 def run_gpu(inp, *, dv_split=0, scale=1.0, device="cuda", with_state=True, o=None, ht=None,
-            h0=None, stream=None, seg_len=0):
+            h0=None, stream=None, seg_len=0, o_dtype=None):
     d = to_dev(inp, device)
     T = inp["q"].shape[0]
     ci, co, st = la.build_chunk_meta(d["cu_seqlens"], T, stream=stream)
     fwd = la.kda_chunk_fwd if inp["kda"] else la.gdn_chunk_fwd
     o, ht = fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], ci, co,
                 h0=d["h0"] if h0 is None else h0, o=o, ht=ht, output_final_state=with_state,
-                scale=scale, dv_split=dv_split, seg_len=seg_len, stream=stream)
+                scale=scale, dv_split=dv_split, seg_len=seg_len, o_dtype=o_dtype, stream=stream)
     torch.cuda.synchronize()
     return o, ht, (ci, co, st)
 

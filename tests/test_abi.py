@@ -78,6 +78,10 @@ BAD = [
     ("workspace misaligned", dict(workspace=0x100010), -5),
     ("q misaligned", dict(q=0x100008), -2),
     ("ht partly over h0", dict(h0=0x200000, ht=0x200000 + 4096), -6),
+    ("o misaligned", dict(o=0x100008), -2),
+    ("H_qk not dividing H", dict(H=6, H_qk=4), -2),
+    ("H_qk negative", dict(H_qk=-1), -2),
+    ("o_bf16 2", dict(o_bf16=2), -3),
 ]
 
 
@@ -201,6 +205,8 @@ RBAD = [
     ("v misaligned", dict(v=0x100004), -2),
     ("h0 misaligned", dict(h0=0x100008), -2),
     ("ht partly over h0", dict(h0=0x200000, ht=0x200000 + 4096), -6),
+    ("H_qk not dividing H", dict(H=6, H_qk=4), -2),
+    ("o_bf16 2", dict(o_bf16=2), -3),
 ]
 
 

@@ -12,7 +12,7 @@ import torch
 
 import chunkwise_gated_delta_chunk_amd as la
 from synth import make_inputs
-from tests.helpers import TOL, rel_err, run_oracle
+from tests.helpers import TOL, gva, rel_err, rel_err_bf16_out, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -92,3 +92,23 @@ def test_recurrent_zero_state_and_no_final_state():
     eo = rel_err(o.cpu().numpy(), o_ref)
     _say(f"decode zero state: o {eo:.2e}")
     assert eo <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+def test_recurrent_grouped_value_heads_and_bf16_output(kda):
+    """8 value heads over 2 q/k heads; o in bf16 equals the rounded fp32 o."""
+    inp = _step_inputs(21, 8, 128, kda, "bf16", seed=230)
+    small, full = gva(inp, 2)
+    dv = _dev(small)
+    fwd = la.kda_recurrent_fwd if kda else la.gdn_recurrent_fwd
+    o, ht = fwd(dv["q"], dv["k"], dv["v"], dv["g"], dv["beta"], h0=dv["h0"])
+    o16, _ = fwd(dv["q"], dv["k"], dv["v"], dv["g"], dv["beta"], h0=dv["h0"],
+                 o_dtype=torch.bfloat16, output_final_state=False)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o.to(torch.bfloat16))
+    o_ref, ht_ref = run_oracle(full)
+    eo = rel_err(o.cpu().numpy(), o_ref)
+    eh = rel_err(ht.cpu().numpy(), ht_ref)
+    e16 = rel_err_bf16_out(o16.float().cpu().numpy(), o_ref)
+    _say(f"decode GVA + bf16 o kda={kda}: o {eo:.2e} ht {eh:.2e} bf16 o {e16:.2e}")
+    assert eo <= TOL["bf16"] and eh <= TOL["bf16"] and e16 <= TOL["bf16"]

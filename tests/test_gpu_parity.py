@@ -13,7 +13,8 @@ import torch
 import chunkwise_gated_delta_chunk_amd as la
 from oracle import chunkwise_ref, meta_ref
 from synth import config, make_inputs
-from tests.helpers import TOL, compare, decode_images, rel_err, run_gpu, run_oracle, to_dev
+from tests.helpers import (TOL, compare, decode_images, gva, rel_err, rel_err_bf16_out, run_gpu,
+                           run_oracle, to_dev)
 
 pytestmark = pytest.mark.gpu
 
@@ -251,6 +252,42 @@ def test_segmented_reduce_no_state_and_padding():
     o_ref, _ = run_oracle(inp)
     eo = rel_err(o_np[:1300], o_ref[:1300])
     _say(f"segmented, no state: o {eo:.2e}")
+    assert eo <= TOL["bf16"]
+
+
+# -------------------------------------------- grouped value heads, bf16 output ---
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+@pytest.mark.parametrize("H_qk", [1, 2])
+@pytest.mark.parametrize("seg", [-1, 2])
+def test_grouped_value_heads(kda, H_qk, seg):
+    """4 value heads over H_qk q/k heads (value head h reads q/k head
+    h / (4 / H_qk)); one-pass and segmented reduce."""
+    cu = [0, 100, 100, 420, 700]
+    inp = make_inputs(cu[-1], 4, 128, 128, kda=kda, dtype="bf16", seed=140 + H_qk,
+                      cu_seqlens=cu, h0_std=0.1)
+    small, full = gva(inp, H_qk)
+    o, ht, _ = run_gpu(small | {"H": 4}, seg_len=seg)
+    o_ref, ht_ref = run_oracle(full)
+    eo, eh, tol = compare(full, o, ht, o_ref, ht_ref)
+    _say(f"GVA kda={kda} H_qk={H_qk} seg={seg}: o {eo:.2e} ht {eh:.2e}")
+    assert eo <= tol and eh <= tol
+
+
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+@pytest.mark.parametrize("seg", [-1, 2])
+def test_bf16_output(kda, seg):
+    """o in bf16: bit-equal to the nearest-even rounding of the fp32 output of
+    the same call, and within the bar of the oracle plus half a bf16 ulp."""
+    cu = [0, 64, 300, 301, 700]
+    inp = make_inputs(cu[-1], 3, 128, 128, kda=kda, dtype="bf16", seed=150, cu_seqlens=cu,
+                      h0_std=0.1)
+    o32, _, _ = run_gpu(inp, seg_len=seg)
+    o16, ht16, _ = run_gpu(inp, seg_len=seg, o_dtype=torch.bfloat16)
+    assert o16.dtype == torch.bfloat16
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    o_ref, ht_ref = run_oracle(inp)
+    eo = rel_err_bf16_out(o16.float().cpu().numpy(), o_ref)
+    _say(f"bf16 o kda={kda} seg={seg}: o {eo:.2e}")
     assert eo <= TOL["bf16"]
 
 
