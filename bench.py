@@ -95,6 +95,19 @@ def alg_flops(inp):
     return chunks * inp["H"] * per
 
 
+KERNEL_SOURCE = {"reduce": "chunk_reduce.hip", "map": "chunk_map.hip", "recurrent": "recurrent.hip"}
+
+# decode workloads: sequences (one token each), heads, head dim
+DECODE_N, DECODE_H, DECODE_D = 64, 16, 128
+
+
+def decode_alg_bytes(kda):
+    """Algorithmic bytes of one decode step: the state read and written, q, k,
+    v, g, beta and o."""
+    N, H, d = DECODE_N, DECODE_H, DECODE_D
+    return N * H * (2 * d * d * 4 + 3 * d * 2 + (4 * d if kda else 4) + 4 + 4 * d)
+
+
 def load_traffic(kernel_kind, workload):
     """HBM traffic of the dominant kernel from the committed counter summary, if
     it was taken on the current kernel source; else None."""
@@ -102,7 +115,7 @@ def load_traffic(kernel_kind, workload):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = "chunk_reduce.hip" if kernel_kind == "reduce" else "chunk_map.hip"
+    src = KERNEL_SOURCE[kernel_kind]
     if rec.get("kernel_src_sha") != kernel_source_hash(src):
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -234,7 +247,7 @@ def bench_decode(args, torch, la, synth, dev):
     the state updated in place; HIP events around the launch, then a graph of
     one step replayed."""
     _, kda, desc = WORKLOADS[args.workload]
-    N, H, d = 64, 16, 128
+    N, H, d = DECODE_N, DECODE_H, DECODE_D
     inp = synth.make_inputs(N, H, d, d, kda=kda, dtype="bf16", seed=5,
                             cu_seqlens=np.arange(N + 1, dtype=np.int32), h0_std=0.1)
     bf = torch.bfloat16
@@ -288,8 +301,7 @@ def bench_decode(args, torch, la, synth, dev):
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = elapsed * 1e3 / args.steps
-    # algorithmic bytes: the state read and written, q k v, g, beta, o
-    ab = N * H * (2 * d * d * 4 + 3 * d * 2 + (4 * d if kda else 4) + 4 + 4 * d)
+    ab = decode_alg_bytes(kda)
     achieved = ab / (launch_ms * 1e-3) / 1e9
     out = {
         "metric": "GDN/KDA chunk-fwd tokens/s (H=16,d=128,8K varlen); % of HBM/MFMA roofline",
@@ -301,7 +313,8 @@ def bench_decode(args, torch, la, synth, dev):
         "config": {"workload": desc, "mode": "graph-replay of one recurrent step",
                    "sequences": N, "heads": H, "d": d},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": load_traffic("recurrent", args.workload),
                      "kernel": "recurrent_kernel", "alg_bytes_per_launch": ab,
                      "avg_launch_ms": round(launch_ms, 5)},
         "graph_equals_eager": graph_eq,
@@ -451,7 +464,9 @@ def main():
     dom_ms = kernels[dom]
     ab = alg_bytes(inp, dom)
     achieved = ab / (dom_ms * 1e-3) / 1e9
-    traffic = load_traffic(dom, args.workload)
+    # per-launch counters describe one kernel; the segmented reduce stage is
+    # three launches of two kernels
+    traffic = load_traffic(dom, args.workload) if not (dom == "reduce" and seg) else None
     op_bytes = alg_bytes(inp, "op")
     op_flops = alg_flops(inp)
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
