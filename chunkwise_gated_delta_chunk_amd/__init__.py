@@ -10,8 +10,8 @@ raised -- there is no other path.
 
 Layouts (token-major varlen packing, batch 1): q, k [T_max, H, d_k];
 v [T_max, H, d_v]; g [T_max, H] (GDN) or [T_max, H, d_k] (KDA); beta
-[T_max, H]; cu_seqlens int32 [N_max + 1]; h0 / ht [N_max, H, d_k, d_v] fp32;
-o [T_max, H, d_v] fp32.
+[T_max, H]; cu_seqlens int32 or int64 [N_max + 1]; h0 / ht [N_max, H, d_k, d_v]
+fp32; o [T_max, H, d_v] fp32 or bf16.  q, k, v are bfloat16, float16 or float32.
 """
 
 from __future__ import annotations
@@ -31,7 +31,9 @@ __all__ = [
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "liblinattn.so")
 
-LA_BF16, LA_F32 = 0, 1
+LA_BF16, LA_F32, LA_F16 = 0, 1, 2
+_DTYPES = {torch.bfloat16: LA_BF16, torch.float32: LA_F32, torch.float16: LA_F16}
+_IDX = (torch.int32, torch.int64)
 STAGE_MAP, STAGE_REDUCE = 1, 2
 META_BAD_START, META_NOT_MONOTONE, META_OVER_CAPACITY = 1, 2, 4
 
@@ -48,7 +50,7 @@ class ChunkFwdArgs(ctypes.Structure):
         ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("BT", ctypes.c_int32),
         ("qkv_dtype", ctypes.c_int32), ("dv_split", ctypes.c_int32),
         ("seg_len", ctypes.c_int32), ("H_qk", ctypes.c_int32), ("o_bf16", ctypes.c_int32),
-        ("scale", ctypes.c_float),
+        ("cu_seqlens_i64", ctypes.c_int32), ("scale", ctypes.c_float),
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p),
         ("cu_seqlens", ctypes.c_void_p), ("chunk_indices", ctypes.c_void_p),
@@ -83,10 +85,10 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.la_nt_max.restype = ctypes.c_int64
         L.la_nt_max.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32]
-        L.build_chunk_meta.restype = ctypes.c_int
-        L.build_chunk_meta.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32,
-                                       ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p,
-                                       ctypes.c_void_p, ctypes.c_void_p]
+        for f in (L.build_chunk_meta, L.build_chunk_meta_i64):
+            f.restype = ctypes.c_int
+            f.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                          ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
         P = ctypes.POINTER(ChunkFwdArgs)
         L.la_chunk_fwd_workspace_bytes.restype = ctypes.c_size_t
         L.la_chunk_fwd_workspace_bytes.argtypes = [P, ctypes.c_int]
@@ -150,12 +152,12 @@ def nt_max(T_max, N_max, BT=64):
 
 def build_chunk_meta(cu_seqlens, T_max, BT=64, *, chunk_indices=None, chunk_offsets=None,
                      status=None, stream=None):
-    """Device-side chunk metadata from cu_seqlens [N_max+1] int32.
+    """Device-side chunk metadata from cu_seqlens [N_max+1] int32 or int64.
 
     Returns (chunk_indices [NT_max, 2], chunk_offsets [N_max+1], status [1]),
     all int32 on cu_seqlens' device; pass preallocated tensors for capture.
     """
-    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    _need_idx(cu_seqlens)
     N_max = cu_seqlens.numel() - 1
     NT = nt_max(T_max, N_max, BT)
     dev = cu_seqlens.device
@@ -168,18 +170,30 @@ def build_chunk_meta(cu_seqlens, T_max, BT=64, *, chunk_indices=None, chunk_offs
     _need(chunk_indices, "chunk_indices", torch.int32, (NT, 2), dev)
     _need(chunk_offsets, "chunk_offsets", torch.int32, (N_max + 1,), dev)
     _need(status, "status", torch.int32, (1,), dev)
-    rc = lib().build_chunk_meta(_ptr(cu_seqlens), N_max, int(T_max), int(BT),
-                                _ptr(chunk_indices), _ptr(chunk_offsets), _ptr(status),
-                                _stream(stream))
+    f = lib().build_chunk_meta_i64 if cu_seqlens.dtype == torch.int64 else lib().build_chunk_meta
+    rc = f(_ptr(cu_seqlens), N_max, int(T_max), int(BT), _ptr(chunk_indices), _ptr(chunk_offsets),
+           _ptr(status), _stream(stream))
     if rc != 0:
         raise LinAttnError(rc, "build_chunk_meta")
     return chunk_indices, chunk_offsets, status
 
 
+def _need_idx(cu, dev=None):
+    if cu.dtype not in _IDX:
+        raise ValueError(f"cu_seqlens must be int32 or int64, got {cu.dtype}")
+    _need(cu, "cu_seqlens", cu.dtype, None, dev)
+
+
+def _qkv_dtype(t):
+    if t.dtype not in _DTYPES:
+        raise ValueError(f"q must be bfloat16, float16 or float32, got {t.dtype}")
+    return _DTYPES[t.dtype]
+
+
 def _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, dv_split=0, BT=64, seg_len=0):
     a = ChunkFwdArgs()
     a.T_max, a.N_max, a.H, a.d_k, a.d_v, a.BT = T_max, N_max, H, d_k, d_v, BT
-    a.qkv_dtype = LA_BF16 if qkv_dtype == torch.bfloat16 else LA_F32
+    a.qkv_dtype = _DTYPES.get(qkv_dtype, LA_F32)
     a.dv_split = dv_split
     a.seg_len = seg_len
     return a
@@ -223,8 +237,7 @@ def _out(o, o_dtype, shape, dev):
 
 def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0, o, ht,
              output_final_state, workspace, scale, dv_split, seg_len, o_dtype=None):
-    if q.dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError(f"q must be bfloat16 or float32, got {q.dtype}")
+    _qkv_dtype(q)
     H, H_qk = _heads(q, v, "T_max")
     T_max, _, d_k = q.shape
     d_v = v.shape[-1]
@@ -234,7 +247,7 @@ def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0
     _need(v, "v", q.dtype, (T_max, H, d_v), dev)
     _need(g, "g", torch.float32, (T_max, H, d_k) if kda else (T_max, H), dev)
     _need(beta, "beta", torch.float32, (T_max, H), dev)
-    _need(cu_seqlens, "cu_seqlens", torch.int32, None, dev)
+    _need_idx(cu_seqlens, dev)
     N_max = cu_seqlens.numel() - 1
     NT = nt_max(T_max, N_max)
     _need(chunk_indices, "chunk_indices", torch.int32, (NT, 2), dev)
@@ -250,6 +263,7 @@ def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0
     a = _shape_args(T_max, N_max, H, d_k, d_v, q.dtype, dv_split, seg_len=seg_len)
     a.H_qk = H_qk
     a.o_bf16 = int(o.dtype == torch.bfloat16)
+    a.cu_seqlens_i64 = int(cu_seqlens.dtype == torch.int64)
     need = int(lib().la_chunk_fwd_workspace_bytes(ctypes.byref(a), int(kda)))
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
@@ -306,8 +320,7 @@ def chunk_fwd_stages(kda, stages, q, k, v, g, beta, cu_seqlens, chunk_indices, c
 
 def _recurrent(name, kda, q, k, v, g, beta, h0=None, o=None, ht=None, output_final_state=True,
                scale=1.0, o_dtype=None, stream=None):
-    if q.dtype not in (torch.bfloat16, torch.float32):
-        raise ValueError(f"q must be bfloat16 or float32, got {q.dtype}")
+    _qkv_dtype(q)
     H, H_qk = _heads(q, v, "N")
     N, _, d_k = q.shape
     d_v = v.shape[-1]
@@ -329,7 +342,7 @@ def _recurrent(name, kda, q, k, v, g, beta, h0=None, o=None, ht=None, output_fin
     a.N, a.H, a.d_k, a.d_v = N, H, d_k, d_v
     a.H_qk = H_qk
     a.o_bf16 = int(o.dtype == torch.bfloat16)
-    a.qkv_dtype = LA_BF16 if q.dtype == torch.bfloat16 else LA_F32
+    a.qkv_dtype = _qkv_dtype(q)
     a.scale = float(scale)
     a.q, a.k, a.v, a.g, a.beta = (t.data_ptr() for t in (q, k, v, g, beta))
     a.h0 = None if h0 is None else h0.data_ptr()

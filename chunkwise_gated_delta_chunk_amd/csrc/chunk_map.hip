@@ -97,8 +97,8 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   const int i_n = p.chunk_indices[2 * slot];
   if (i_n < 0) return;  // sentinel: nothing to do, nothing written
   const int i_t = p.chunk_indices[2 * slot + 1];
-  const int bos = p.cu_seqlens[i_n];
-  const int eos = p.cu_seqlens[i_n + 1];
+  const int bos = cu_at(p.cu_seqlens, p.cu64, i_n);
+  const int eos = cu_at(p.cu_seqlens, p.cu64, i_n + 1);
   const int r0 = bos + i_t * kBT;
   const int C = min(kBT, eos - r0);
   const int H = p.H;
@@ -173,7 +173,15 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
       T kv[NP][VEC], qv[NP][VEC];
 #pragma unroll
       for (int j = 0; j < NP; ++j) {
-        if constexpr (VEC == 8) {  // bf16 -> fp16
+        if constexpr (VEC == 8 && std::is_same<In, f16>::value) {  // fp16: the bits as they are
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            kv[j][2 * e] = f16_from_bits(kraw[it][j][e]);
+            kv[j][2 * e + 1] = f16_from_bits(kraw[it][j][e] >> 16);
+            qv[j][2 * e] = f16_from_bits(qraw[it][j][e]);
+            qv[j][2 * e + 1] = f16_from_bits(qraw[it][j][e] >> 16);
+          }
+        } else if constexpr (VEC == 8) {  // bf16 -> fp16
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             kv[j][2 * e] = (T)__uint_as_float(kraw[it][j][e] << 16);
@@ -545,13 +553,18 @@ static hipError_t launch_map_t(const MapParams &p, hipStream_t st) {
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_map(const MapParams &p, bool kda, bool bf16_in, int dk, hipStream_t st) {
-  if (bf16_in) {
-    if (dk == 128) return kda ? launch_map_t<true, bf16, 128>(p, st) : launch_map_t<false, bf16, 128>(p, st);
-    return kda ? launch_map_t<true, bf16, 64>(p, st) : launch_map_t<false, bf16, 64>(p, st);
-  }
+template <typename In>
+static hipError_t launch_map_16(const MapParams &p, bool kda, int dk, hipStream_t st) {
+  if (dk == 128) return kda ? launch_map_t<true, In, 128>(p, st) : launch_map_t<false, In, 128>(p, st);
+  if (dk == 64) return kda ? launch_map_t<true, In, 64>(p, st) : launch_map_t<false, In, 64>(p, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_map(const MapParams &p, bool kda, int dt, int dk, hipStream_t st) {
+  if (dt == LA_BF16) return launch_map_16<bf16>(p, kda, dk, st);
+  if (dt == LA_F16) return launch_map_16<f16>(p, kda, dk, st);
   // fp32 inputs: d = 64 only (the fp32 d = 128 KDA tiles exceed the 160 KiB LDS)
-  if (dk != 64) return hipErrorInvalidValue;
+  if (dt != LA_F32 || dk != 64) return hipErrorInvalidValue;
   return kda ? launch_map_t<true, float, 64>(p, st) : launch_map_t<false, float, 64>(p, st);
 }
 

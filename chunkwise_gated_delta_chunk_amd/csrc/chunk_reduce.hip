@@ -347,7 +347,7 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
       for (int R = 0; R < 4; ++R)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          x[R][e] = __uint_as_float((uint32_t)(uint16_t)vr[R][e] << 16) - gam[R][e] * yk[R][e];
+          x[R][e] = in16_to_f32<In>((uint16_t)vr[R][e]) - gam[R][e] * yk[R][e];
       static_for<4>([&](auto rc) {
         constexpr int R = decltype(rc)::value;
         ds_read_b128_at<512 + 64 * R>(bet[R], aS[BUF]);
@@ -604,8 +604,8 @@ __device__ __forceinline__ int decode_work(const ReduceParams &p, Work &wk) {
     wk.j0 = p.chunk_offsets[n];
     wk.j1 = p.chunk_offsets[n + 1];
     if (wk.j0 == wk.j1) return 0;  // empty sequence (or invalid cu_seqlens): no writes
-    wk.t0 = p.cu_seqlens[n];
-    wk.eos = p.cu_seqlens[n + 1];
+    wk.t0 = cu_at(p.cu_seqlens, p.cu64, n);
+    wk.eos = cu_at(p.cu_seqlens, p.cu64, n + 1);
     const size_t sb = ((size_t)n * H + wk.h) * mat;
     if (p.h0) wk.init = p.h0 + sb;
     if (p.ht) wk.fin = p.ht + sb;
@@ -632,8 +632,8 @@ __device__ __forceinline__ int decode_work(const ReduceParams &p, Work &wk) {
   wk.n = n;
   wk.j0 = p.chunk_offsets[n] + s * p.seg;
   wk.j1 = min(wk.j0 + p.seg, p.chunk_offsets[n + 1]);
-  wk.t0 = p.cu_seqlens[n] + s * p.seg * kBT;
-  wk.eos = p.cu_seqlens[n + 1];
+  wk.t0 = cu_at(p.cu_seqlens, p.cu64, n) + s * p.seg * kBT;
+  wk.eos = cu_at(p.cu_seqlens, p.cu64, n + 1);
   const size_t here = ((size_t)sig * H + wk.h) * mat, next = here + (size_t)H * mat;
   const size_t sb = ((size_t)n * H + wk.h) * mat;
   if (p.pass == 1) {
@@ -693,14 +693,20 @@ static hipError_t launch_reduce_w(const ReduceParams &p, int W, hipStream_t st) 
   }
 }
 
-hipError_t launch_chunk_reduce(const ReduceParams &p, bool kda, bool bf16_in, int dk, int W,
+template <typename In>
+static hipError_t launch_reduce_16(const ReduceParams &p, bool kda, int dk, int W, hipStream_t st) {
+  if (dk == 128)
+    return kda ? launch_reduce_w<true, In, 128>(p, W, st) : launch_reduce_w<false, In, 128>(p, W, st);
+  if (dk == 64)
+    return kda ? launch_reduce_w<true, In, 64>(p, W, st) : launch_reduce_w<false, In, 64>(p, W, st);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_chunk_reduce(const ReduceParams &p, bool kda, int dt, int dk, int W,
                                hipStream_t st) {
-  if (bf16_in) {
-    if (dk == 128)
-      return kda ? launch_reduce_w<true, bf16, 128>(p, W, st) : launch_reduce_w<false, bf16, 128>(p, W, st);
-    return kda ? launch_reduce_w<true, bf16, 64>(p, W, st) : launch_reduce_w<false, bf16, 64>(p, W, st);
-  }
-  if (dk != 64) return hipErrorInvalidValue;
+  if (dt == LA_BF16) return launch_reduce_16<bf16>(p, kda, dk, W, st);
+  if (dt == LA_F16) return launch_reduce_16<f16>(p, kda, dk, W, st);
+  if (dt != LA_F32 || dk != 64) return hipErrorInvalidValue;
   return kda ? launch_reduce_w<true, float, 64>(p, W, st) : launch_reduce_w<false, float, 64>(p, W, st);
 }
 

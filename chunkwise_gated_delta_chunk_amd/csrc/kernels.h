@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include "la_device.h"
+#include "../../include/linattn.h"
 
 namespace la {
 
@@ -13,7 +14,9 @@ namespace la {
 struct MapParams {
   const void *q, *k;
   const float *g, *beta;
-  const int32_t *cu_seqlens, *chunk_indices;
+  const void *cu_seqlens;  // int32, or int64 with cu64
+  const int32_t *chunk_indices;
+  int cu64;
   int H, NT_max;
   int Hqk;  // q, k heads: value head h reads q, k head h / (H / Hqk)
   void *img;
@@ -21,7 +24,9 @@ struct MapParams {
 
 struct ReduceParams {
   const void *v;
-  const int32_t *cu_seqlens, *chunk_offsets;
+  const void *cu_seqlens;  // int32, or int64 with cu64
+  const int32_t *chunk_offsets;
+  int cu64;
   const float *h0;
   void *o;       // fp32, or bf16 with o_bf16
   float *ht;
@@ -59,14 +64,15 @@ struct RecurrentParams {
   int o_bf16;
 };
 
-hipError_t launch_chunk_meta(const int32_t *cu, int N_max, int T_max, int BT, int NT_max,
+// cu: int32 cu_seqlens, or int64 with cu64
+hipError_t launch_chunk_meta(const void *cu, int cu64, int N_max, int T_max, int BT, int NT_max,
                              int32_t *ci, int32_t *co, int32_t *status, hipStream_t stream);
-hipError_t launch_chunk_map(const MapParams &p, bool kda, bool bf16_in, int dk, hipStream_t st);
+// dt: la_dtype code of q, k, v (LA_BF16, LA_F32, LA_F16)
+hipError_t launch_chunk_map(const MapParams &p, bool kda, int dt, int dk, hipStream_t st);
 // W = d_v / S columns per workgroup: 32 per wave
-hipError_t launch_chunk_reduce(const ReduceParams &p, bool kda, bool bf16_in, int dk, int W,
+hipError_t launch_chunk_reduce(const ReduceParams &p, bool kda, int dt, int dk, int W,
                                hipStream_t st);
 hipError_t launch_chunk_combine(const CombineParams &p, int dk, hipStream_t st);
-hipError_t launch_recurrent(const RecurrentParams &p, bool kda, bool bf16_in, int dk,
-                            hipStream_t st);
+hipError_t launch_recurrent(const RecurrentParams &p, bool kda, int dt, int dk, hipStream_t st);
 
 }  // namespace la

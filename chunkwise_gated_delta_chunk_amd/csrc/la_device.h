@@ -12,6 +12,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
 #include <utility>
 
 namespace la {
@@ -25,13 +26,33 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // raw 16-byte piece
 
 struct bf16 { uint16_t bits; };
+struct f16 { uint16_t bits; };  // fp16 input element
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
+__device__ __forceinline__ _Float16 f16_from_bits(uint32_t b) {
+  return __builtin_bit_cast(_Float16, static_cast<uint16_t>(b));
+}
 
-// Operand traits: bf16 inputs run on fp16 MFMA (bf16 values are exact in fp16
-// inside its normal range), fp32 inputs on fp32 MFMA.
+// 16-bit input element (bf16 or fp16 bits) -> fp32
+template <typename In> __device__ __forceinline__ float in16_to_f32(uint32_t b);
+template <> __device__ __forceinline__ float in16_to_f32<bf16>(uint32_t b) {
+  return bf16_to_f32(static_cast<uint16_t>(b));
+}
+template <> __device__ __forceinline__ float in16_to_f32<f16>(uint32_t b) {
+  return static_cast<float>(f16_from_bits(b));
+}
+
+// cu_seqlens[i] of an int32 or int64 array (values checked to fit in int by
+// the metadata kernel before any forward kernel uses them)
+__device__ __forceinline__ int cu_at(const void *cu, int cu64, int i) {
+  return cu64 ? static_cast<int>(static_cast<const int64_t *>(cu)[i])
+              : static_cast<const int32_t *>(cu)[i];
+}
+
+// Operand traits: bf16 and fp16 inputs run on fp16 MFMA (bf16 values are
+// exact in fp16 inside its normal range), fp32 inputs on fp32 MFMA.
 template <typename In> struct Op;
 template <> struct Op<bf16> {
   using T = _Float16;
@@ -42,6 +63,9 @@ template <> struct Op<bf16> {
     return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
   }
   __device__ static __forceinline__ float load(const bf16 *p) { return bf16_to_f32(p->bits); }
+};
+template <> struct Op<f16> : Op<bf16> {
+  __device__ static __forceinline__ float load(const f16 *p) { return (float)f16_from_bits(p->bits); }
 };
 template <> struct Op<float> {
   using T = float;

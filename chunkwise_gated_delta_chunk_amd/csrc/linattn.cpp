@@ -12,6 +12,8 @@ namespace {
 constexpr int kBTSupported = 64;
 constexpr int kCUs = 256;  // compute units of one MI355X
 
+bool known_dtype(int dt) { return dt == LA_BF16 || dt == LA_F16 || dt == LA_F32; }
+
 bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
   const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
   return x < y + nb && y < x + na;
@@ -21,20 +23,21 @@ bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
 int check_shape(const la_chunk_fwd_args *a) {
   if (a->T_max < 1 || a->N_max < 1 || a->H < 1) return LA_ERR_SHAPE;
   if (a->T_max > 0x7fffffff - 2 * kBTSupported) return LA_ERR_SHAPE;
-  if (a->qkv_dtype != LA_BF16 && a->qkv_dtype != LA_F32) return LA_ERR_DTYPE;
+  if (!known_dtype(a->qkv_dtype)) return LA_ERR_DTYPE;
   if (a->o_bf16 != 0 && a->o_bf16 != 1) return LA_ERR_DTYPE;
+  if (a->cu_seqlens_i64 != 0 && a->cu_seqlens_i64 != 1) return LA_ERR_DTYPE;
   if (a->H_qk < 0 || (a->H_qk > 0 && a->H % a->H_qk != 0)) return LA_ERR_SHAPE;
   if (a->BT != kBTSupported) return LA_ERR_UNSUPPORTED;
   if (a->d_k != a->d_v) return LA_ERR_UNSUPPORTED;
-  if (a->qkv_dtype == LA_BF16 && a->d_k != 64 && a->d_k != 128) return LA_ERR_UNSUPPORTED;
+  if (a->qkv_dtype != LA_F32 && a->d_k != 64 && a->d_k != 128) return LA_ERR_UNSUPPORTED;
   if (a->qkv_dtype == LA_F32 && a->d_k != 64) return LA_ERR_UNSUPPORTED;
   // dv_split: 0 (auto) or a power of two leaving 32, 64 or 128 columns
   const int s = a->dv_split;
   if (s != 0 && s != 1 && s != 2 && s != 4) return LA_ERR_UNSUPPORTED;
   if (s != 0 && a->d_v / s < 32) return LA_ERR_UNSUPPORTED;
-  // seg_len: -1 (off), 0 (auto) or chunks per segment, bf16 and N_max <= 64
+  // seg_len: -1 (off), 0 (auto) or chunks per segment, 16-bit and N_max <= 64
   if (a->seg_len < -1) return LA_ERR_UNSUPPORTED;
-  if (a->seg_len > 0 && (a->qkv_dtype != LA_BF16 || a->N_max > 64)) return LA_ERR_UNSUPPORTED;
+  if (a->seg_len > 0 && (a->qkv_dtype == LA_F32 || a->N_max > 64)) return LA_ERR_UNSUPPORTED;
   // every (token, head) index and (slot, head) workspace index stays in size_t
   const int64_t nt = la_nt_max(a->T_max, a->N_max, a->BT);
   if (nt < 1 || nt > 0x7fffffff) return LA_ERR_SHAPE;
@@ -56,7 +59,7 @@ int split_for(const la_chunk_fwd_args *a) {
   return s;
 }
 
-size_t elem_bytes(const la_chunk_fwd_args *a) { return a->qkv_dtype == LA_BF16 ? 2 : 4; }
+size_t elem_bytes(const la_chunk_fwd_args *a) { return a->qkv_dtype == LA_F32 ? 4 : 2; }
 
 // Chunks per segment of the sequence-parallel reduce, 0 for one workgroup
 // per sequence.  Automatic when the (sequence, head) units cannot fill half
@@ -64,7 +67,7 @@ size_t elem_bytes(const la_chunk_fwd_args *a) { return a->qkv_dtype == LA_BF16 ?
 // the capacity's chunks of all units over the CUs once, at least 8, and only
 // where the longest possible sequence then has at least 3 segments.
 int seg_for(const la_chunk_fwd_args *a) {
-  if (a->seg_len < 0 || a->qkv_dtype != LA_BF16 || a->N_max > 64) return 0;
+  if (a->seg_len < 0 || a->qkv_dtype == LA_F32 || a->N_max > 64) return 0;
   if (a->seg_len > 0) return a->seg_len;
   const int64_t s2 = a->d_v / 64 > 0 ? a->d_v / 64 : 1;
   if ((int64_t)a->N_max * a->H * s2 > kCUs / 2) return 0;
@@ -130,7 +133,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
                         reinterpret_cast<uintptr_t>(a->v) | reinterpret_cast<uintptr_t>(a->o);
   if (mis % 16 != 0) return LA_ERR_SHAPE;
 
-  const bool bf = a->qkv_dtype == LA_BF16;
+  const int dt = a->qkv_dtype;
   char *ws = static_cast<char *>(a->workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (stages & LA_STAGE_MAP) {
@@ -140,17 +143,19 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     mp.g = a->g;
     mp.beta = a->beta;
     mp.cu_seqlens = a->cu_seqlens;
+    mp.cu64 = a->cu_seqlens_i64;
     mp.chunk_indices = a->chunk_indices;
     mp.H = a->H;
     mp.Hqk = a->H_qk ? a->H_qk : a->H;
     mp.NT_max = (int)la_nt_max(a->T_max, a->N_max, a->BT);
     mp.img = ws;
-    if (la::launch_chunk_map(mp, kda, bf, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
+    if (la::launch_chunk_map(mp, kda, dt, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
   }
   if (stages & LA_STAGE_REDUCE) {
     la::ReduceParams rp{};
     rp.v = a->v;
     rp.cu_seqlens = a->cu_seqlens;
+    rp.cu64 = a->cu_seqlens_i64;
     rp.chunk_offsets = a->chunk_offsets;
     rp.h0 = a->h0;
     rp.o = a->o;
@@ -163,7 +168,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     rp.o_bf16 = a->o_bf16;
     const int L = seg_for(a);
     if (L == 0) {
-      if (la::launch_chunk_reduce(rp, kda, bf, a->d_k, a->d_v / rp.S, st) != hipSuccess)
+      if (la::launch_chunk_reduce(rp, kda, dt, a->d_k, a->d_v / rp.S, st) != hipSuccess)
         return LA_ERR_HIP;
     } else {
       // segments: 64 columns per workgroup unless asked otherwise (the passes
@@ -177,7 +182,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
       rp.dlt = rp.hin + mat;
       rp.pimg = reinterpret_cast<_Float16 *>(rp.dlt + mat);
       rp.pass = 1;
-      if (la::launch_chunk_reduce(rp, kda, bf, a->d_k, a->d_v / rp.S, st) != hipSuccess)
+      if (la::launch_chunk_reduce(rp, kda, dt, a->d_k, a->d_v / rp.S, st) != hipSuccess)
         return LA_ERR_HIP;
       la::CombineParams cp{};
       cp.chunk_offsets = a->chunk_offsets;
@@ -189,7 +194,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
       cp.pimg = rp.pimg;
       if (la::launch_chunk_combine(cp, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
       rp.pass = 2;
-      if (la::launch_chunk_reduce(rp, kda, bf, a->d_k, a->d_v / rp.S, st) != hipSuccess)
+      if (la::launch_chunk_reduce(rp, kda, dt, a->d_k, a->d_v / rp.S, st) != hipSuccess)
         return LA_ERR_HIP;
     }
   }
@@ -205,19 +210,31 @@ int64_t la_nt_max(int64_t T_max, int64_t N_max, int32_t BT) {
   return (T_max + BT - 1) / BT + N_max - 1;
 }
 
-int build_chunk_meta(const int32_t *cu_seqlens, int32_t N_max, int32_t T_max, int32_t BT,
-                     int32_t *chunk_indices, int32_t *chunk_offsets, int32_t *status,
-                     void *stream) {
+static int chunk_meta(const void *cu_seqlens, int cu64, int32_t N_max, int32_t T_max, int32_t BT,
+                      int32_t *chunk_indices, int32_t *chunk_offsets, int32_t *status,
+                      void *stream) {
   if (!cu_seqlens || !chunk_indices || !chunk_offsets) return LA_ERR_NULL;
   if (N_max < 1 || N_max > LA_MAX_N || T_max < 1 || T_max > 0x7fffffff - 2 * kBTSupported)
     return LA_ERR_SHAPE;
-  if (BT != kBTSupported) return LA_ERR_UNSUPPORTED;
+  if (BT != 32 && BT != 64) return LA_ERR_UNSUPPORTED;
   const int64_t nt = la_nt_max(T_max, N_max, BT);
   if (nt > 0x7fffffff / 2) return LA_ERR_SHAPE;
-  if (la::launch_chunk_meta(cu_seqlens, N_max, T_max, BT, (int)nt, chunk_indices, chunk_offsets,
-                            status, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (la::launch_chunk_meta(cu_seqlens, cu64, N_max, T_max, BT, (int)nt, chunk_indices,
+                            chunk_offsets, status, static_cast<hipStream_t>(stream)) != hipSuccess)
     return LA_ERR_HIP;
   return LA_OK;
+}
+
+int build_chunk_meta(const int32_t *cu_seqlens, int32_t N_max, int32_t T_max, int32_t BT,
+                     int32_t *chunk_indices, int32_t *chunk_offsets, int32_t *status,
+                     void *stream) {
+  return chunk_meta(cu_seqlens, 0, N_max, T_max, BT, chunk_indices, chunk_offsets, status, stream);
+}
+
+int build_chunk_meta_i64(const int64_t *cu_seqlens, int32_t N_max, int32_t T_max, int32_t BT,
+                         int32_t *chunk_indices, int32_t *chunk_offsets, int32_t *status,
+                         void *stream) {
+  return chunk_meta(cu_seqlens, 1, N_max, T_max, BT, chunk_indices, chunk_offsets, status, stream);
 }
 
 size_t la_chunk_fwd_workspace_bytes(const la_chunk_fwd_args *a, int is_kda) {
@@ -251,7 +268,7 @@ static int recurrent(const la_recurrent_args *a, bool kda, void *stream) {
   if (!a) return LA_ERR_NULL;
   if (a->N < 1 || a->H < 1) return LA_ERR_SHAPE;
   if ((int64_t)a->N * a->H > 0x7fffffff) return LA_ERR_SHAPE;
-  if (a->qkv_dtype != LA_BF16 && a->qkv_dtype != LA_F32) return LA_ERR_DTYPE;
+  if (!known_dtype(a->qkv_dtype)) return LA_ERR_DTYPE;
   if (a->o_bf16 != 0 && a->o_bf16 != 1) return LA_ERR_DTYPE;
   if (a->H_qk < 0 || (a->H_qk > 0 && a->H % a->H_qk != 0)) return LA_ERR_SHAPE;
   if (a->d_k != a->d_v || (a->d_k != 64 && a->d_k != 128)) return LA_ERR_UNSUPPORTED;
@@ -278,8 +295,8 @@ static int recurrent(const la_recurrent_args *a, bool kda, void *stream) {
   rp.Hqk = a->H_qk ? a->H_qk : a->H;
   rp.scale = a->scale;
   rp.o_bf16 = a->o_bf16;
-  if (la::launch_recurrent(rp, kda, a->qkv_dtype == LA_BF16, a->d_k,
-                           static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (la::launch_recurrent(rp, kda, a->qkv_dtype, a->d_k, static_cast<hipStream_t>(stream)) !=
+      hipSuccess)
     return LA_ERR_HIP;
   return LA_OK;
 }

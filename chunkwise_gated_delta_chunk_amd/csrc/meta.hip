@@ -6,7 +6,9 @@
 // on the device into fixed-shape buffers, with no host round-trip, no
 // data-dependent grid and the sentinel {-1, 0} in unused slots.  One
 // workgroup: a validity check, a prefix sum of per-sequence chunk counts held
-// in LDS, then one binary search per slot.
+// in LDS, then one binary search per slot.  cu_seqlens may be int32 or int64;
+// it is checked in its own width, so an int64 layout that passes the checks
+// has every offset in [0, T_max] and the forward kernels read it as int.
 #include "la_device.h"
 #include "../../include/linattn.h"
 
@@ -14,8 +16,9 @@ namespace la {
 
 constexpr int kMetaThreads = 1024;
 
+template <typename Idx>
 __global__ __launch_bounds__(kMetaThreads) void chunk_meta_kernel(
-    const int32_t *__restrict__ cu, int N_max, int T_max, int BT, int NT_max,
+    const Idx *__restrict__ cu, int N_max, int T_max, int BT, int NT_max,
     int32_t *__restrict__ ci, int32_t *__restrict__ co, int32_t *__restrict__ status) {
   __shared__ int s_flags;
   __shared__ int s_part[kMetaThreads];
@@ -29,7 +32,7 @@ __global__ __launch_bounds__(kMetaThreads) void chunk_meta_kernel(
     if (cu[n + 1] < cu[n]) f |= LA_META_NOT_MONOTONE;
   if (tid == 0) {
     if (cu[0] != 0) f |= LA_META_BAD_START;
-    if (cu[N_max] > T_max) f |= LA_META_OVER_CAPACITY;
+    if (cu[N_max] > (Idx)T_max) f |= LA_META_OVER_CAPACITY;
   }
   if (f) atomicOr(&s_flags, f);
   __syncthreads();
@@ -40,7 +43,7 @@ __global__ __launch_bounds__(kMetaThreads) void chunk_meta_kernel(
   const int n1 = min(N_max, n0 + per);
   int local = 0;
   if (s_flags == 0)
-    for (int n = n0; n < n1; ++n) local += (cu[n + 1] - cu[n] + BT - 1) / BT;
+    for (int n = n0; n < n1; ++n) local += ((int)(cu[n + 1] - cu[n]) + BT - 1) / BT;
   s_part[tid] = local;
   __syncthreads();
   for (int off = 1; off < kMetaThreads; off <<= 1) {  // inclusive scan
@@ -69,7 +72,7 @@ __global__ __launch_bounds__(kMetaThreads) void chunk_meta_kernel(
   int run = s_part[tid] - local;
   for (int n = n0; n < n1; ++n) {
     s_off[n] = run;
-    run += (cu[n + 1] - cu[n] + BT - 1) / BT;
+    run += ((int)(cu[n + 1] - cu[n]) + BT - 1) / BT;
   }
   if (tid == 0) s_off[N_max] = s_part[kMetaThreads - 1];
   __syncthreads();
@@ -93,10 +96,14 @@ __global__ __launch_bounds__(kMetaThreads) void chunk_meta_kernel(
   if (status && tid == 0) *status = 0;
 }
 
-hipError_t launch_chunk_meta(const int32_t *cu, int N_max, int T_max, int BT, int NT_max,
+hipError_t launch_chunk_meta(const void *cu, int cu64, int N_max, int T_max, int BT, int NT_max,
                              int32_t *ci, int32_t *co, int32_t *status, hipStream_t stream) {
-  hipLaunchKernelGGL(chunk_meta_kernel, dim3(1), dim3(kMetaThreads), 0, stream, cu, N_max,
-                     T_max, BT, NT_max, ci, co, status);
+  if (cu64)
+    hipLaunchKernelGGL(chunk_meta_kernel<int64_t>, dim3(1), dim3(kMetaThreads), 0, stream,
+                       static_cast<const int64_t *>(cu), N_max, T_max, BT, NT_max, ci, co, status);
+  else
+    hipLaunchKernelGGL(chunk_meta_kernel<int32_t>, dim3(1), dim3(kMetaThreads), 0, stream,
+                       static_cast<const int32_t *>(cu), N_max, T_max, BT, NT_max, ci, co, status);
   return hipGetLastError();
 }
 

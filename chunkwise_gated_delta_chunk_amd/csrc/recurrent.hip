@@ -14,7 +14,7 @@
 // d_k / RG consecutive rows (RG row groups of d_v / 4 threads), so each wave
 // reads and writes whole 512-byte row spans with 16-byte accesses.  The two
 // column sums p and o are reduced across the row groups through LDS.  All
-// arithmetic is fp32; q, k, v may be bf16.
+// arithmetic is fp32; q, k, v may be bf16 or fp16.
 #include "la_device.h"
 #include "kernels.h"
 
@@ -123,9 +123,10 @@ hipError_t launch_rec_t(const RecurrentParams &p, int dk, hipStream_t st) {
 
 }  // namespace
 
-hipError_t launch_recurrent(const RecurrentParams &p, bool kda, bool bf16_in, int dk,
-                            hipStream_t st) {
-  if (bf16_in) return kda ? launch_rec_t<true, bf16>(p, dk, st) : launch_rec_t<false, bf16>(p, dk, st);
+hipError_t launch_recurrent(const RecurrentParams &p, bool kda, int dt, int dk, hipStream_t st) {
+  if (dt == LA_BF16) return kda ? launch_rec_t<true, bf16>(p, dk, st) : launch_rec_t<false, bf16>(p, dk, st);
+  if (dt == LA_F16) return kda ? launch_rec_t<true, f16>(p, dk, st) : launch_rec_t<false, f16>(p, dk, st);
+  if (dt != LA_F32) return hipErrorInvalidValue;
   return kda ? launch_rec_t<true, float>(p, dk, st) : launch_rec_t<false, float>(p, dk, st);
 }
 

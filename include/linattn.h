@@ -60,7 +60,7 @@ typedef enum {
     LA_ERR_HIP = -7          /* a HIP launch failed (hipGetLastError)           */
 } la_status;
 
-typedef enum { LA_BF16 = 0, LA_F32 = 1 } la_dtype;
+typedef enum { LA_BF16 = 0, LA_F32 = 1, LA_F16 = 2 } la_dtype;
 
 /* Device status bits written by build_chunk_meta (0 = valid cu_seqlens). */
 #define LA_META_BAD_START 1     /* cu_seqlens[0] != 0                           */
@@ -76,48 +76,54 @@ int64_t la_nt_max(int64_t T_max, int64_t N_max, int32_t BT);
 
 /*
  * Device-side metadata (FLA RFC, sections "Fixed-capacity execution" and
- * "Device-side metadata").  Reads cu_seqlens[N_max+1] (int32) on the device
- * and writes
+ * "Device-side metadata").  Reads cu_seqlens[N_max+1] (int32; int64 for
+ * build_chunk_meta_i64) on the device and writes
  *   chunk_offsets[n]    = sum_{m<n} ceil((cu[m+1]-cu[m]) / BT)   (int32, N_max+1)
  *   chunk_indices[j]    = {n, i_t} for j = chunk_offsets[n] + i_t,
  *                         {-1, 0}  for j >= chunk_offsets[N_max] (int32, NT_max x 2)
  *   *status             = OR of LA_META_* bits (int32; status may be NULL).
  * Slots are sequence-major then chunk-minor; zero-length sequences own none.
  * If cu_seqlens is invalid (status != 0) every slot is the sentinel and every
- * offset is 0, so the forward calls then write nothing.  One launch of one
- * workgroup; capturable.
+ * offset is 0, so the forward calls then write nothing.  The int64 variant
+ * checks the offsets as int64 (a valid layout has all of them in
+ * [0, T_max]).  BT may be 32 or 64 (the RFC's two chunk sizes; the chunk
+ * forward runs BT = 64).  One launch of one workgroup; capturable.
  * Host errors: LA_ERR_NULL (cu_seqlens, chunk_indices or chunk_offsets NULL),
  * LA_ERR_SHAPE (N_max < 1, N_max > LA_MAX_N, T_max < 1),
- * LA_ERR_UNSUPPORTED (BT not 64), LA_ERR_HIP.
+ * LA_ERR_UNSUPPORTED (BT not 32 or 64), LA_ERR_HIP.
  */
 int build_chunk_meta(const int32_t *cu_seqlens, int32_t N_max, int32_t T_max,
                      int32_t BT, int32_t *chunk_indices,
                      int32_t *chunk_offsets, int32_t *status, void *stream);
+int build_chunk_meta_i64(const int64_t *cu_seqlens, int32_t N_max, int32_t T_max,
+                         int32_t BT, int32_t *chunk_indices,
+                         int32_t *chunk_offsets, int32_t *status, void *stream);
 
 /* Arguments of the forward calls.  Sizes describe the bucket (capacity); the
  * actual layout comes from cu_seqlens on the device. */
 typedef struct {
     int32_t T_max, N_max, H;   /* bucket capacity and head count (>= 1)          */
-    int32_t d_k, d_v;          /* head dims: d_k == d_v; 64 or 128 (bf16),       */
+    int32_t d_k, d_v;          /* head dims: d_k == d_v; 64 or 128 (bf16, fp16), */
                                /* 64 (fp32 inputs)                               */
     int32_t BT;                /* chunk size: 64                                 */
-    int32_t qkv_dtype;         /* LA_BF16 or LA_F32: dtype of q, k, v            */
+    int32_t qkv_dtype;         /* LA_BF16, LA_F16 or LA_F32: dtype of q, k, v    */
     int32_t dv_split;          /* state column slices per (seq, head): 0 = auto, */
                                /* else 1, 2 or 4 with d_v / dv_split >= 32.      */
                                /* auto: d_v / 64 slices, twice that when         */
                                /* N_max * H * (d_v / 64) <= 256 (the CU count)   */
     int32_t seg_len;           /* sequence-parallel reduce: chunks per segment;  */
-                               /* -1 = off, 0 = auto, > 0 needs bf16 inputs and  */
-                               /* N_max <= 64 (see la_chunk_fwd_seg_len)         */
+                               /* -1 = off, 0 = auto, > 0 needs 16-bit inputs    */
+                               /* and N_max <= 64 (see la_chunk_fwd_seg_len)     */
     int32_t H_qk;              /* q, k heads: 0 = H; else H % H_qk == 0 and      */
                                /* value head h reads q, k head h / (H / H_qk)    */
                                /* (grouped value heads share keys and queries)   */
     int32_t o_bf16;            /* 0: o fp32; 1: o bf16, rounded to nearest even  */
+    int32_t cu_seqlens_i64;    /* 0: cu_seqlens int32; 1: int64                  */
     float scale;               /* o = scale * S q                                */
     const void *q, *k, *v;     /* [T_max][H_qk][d_k] / [T_max][H][d_v], qkv_dtype */
     const float *g;            /* log-decay: GDN [T_max][H]; KDA [T_max][H][d_k] */
     const float *beta;         /* [T_max][H]                                     */
-    const int32_t *cu_seqlens; /* [N_max+1]                                      */
+    const void *cu_seqlens;    /* [N_max+1], int32 or int64 (cu_seqlens_i64)     */
     const int32_t *chunk_indices; /* [NT_max][2], from build_chunk_meta          */
     const int32_t *chunk_offsets; /* [N_max+1], from build_chunk_meta            */
     const float *h0;           /* [N_max][H][d_k][d_v] or NULL (zero state)      */
@@ -132,11 +138,11 @@ typedef struct {
  * BT, qkv_dtype, dv_split and seg_len are read); 0 if the shape is invalid.
  * It holds the map stage's results for the reduce: one image per
  * (chunk slot, head) cell, NT_max * H cells in slot-major order, each a
- * multiple of 1 KiB.  With e = 2 (bf16 inputs: fp16 values) or 4 (fp32
+ * multiple of 1 KiB.  With e = 2 (bf16, fp16 inputs: fp16 values) or 4 (fp32
  * inputs), a cell holds in order
  *   K, Q  [BT][d_k]  the chunk's keys and queries (KDA: K*exp(G), Q*exp(G))
  *   KT    [d_k][BT]  KDA: (K*exp(G_C - G))^T; fp32 inputs: K^T; absent for
- *                    GDN with bf16 inputs
+ *                    GDN with 16-bit inputs
  *   Tn    [BT][BT]   T = A^-1 diag(beta) with its diagonal removed
  *   M     [BT][BT]   masked decayed Q K^T (lower triangle incl. diagonal)
  *   vec   [192 + d_k] fp32: exp(G_r), exp(G_C - G_r), beta_r (BT each), then
@@ -158,7 +164,7 @@ size_t la_chunk_fwd_workspace_bytes(const la_chunk_fwd_args *shape, int is_kda);
  * o rows >= cu[N_max], sentinel slots and zero-length sequences are never
  * written.  h0 == NULL means a zero initial state.  ht may be the same
  * pointer as h0 (in-place state update); a partial overlap is LA_ERR_ALIAS.
- * Matrix products run on MFMA: bf16 inputs in fp16 operands with fp32
+ * Matrix products run on MFMA: bf16 and fp16 inputs in fp16 operands with fp32
  * accumulation (inputs and intermediates must stay within fp16 range,
  * |x| < 65504; g <= 0 is assumed for KDA), fp32 inputs in fp32 operands.
  * The metadata must come from build_chunk_meta on the same cu_seqlens, T_max,
@@ -195,7 +201,7 @@ int32_t la_chunk_fwd_dv_split(const la_chunk_fwd_args *a);
  * entering segment s+1 is P_s H_s + D_s: the recurrence is affine in the
  * state), a serial combine of those along each sequence, then the later
  * segments with output from their entering state.  Auto (seg_len = 0)
- * segments only bf16 inputs with N_max <= 64 whose (sequence, head) units
+ * segments only 16-bit inputs with N_max <= 64 whose (sequence, head) units
  * cannot fill half of the 256 CUs at 64 state columns per workgroup, with
  * about ceil(NT_max * H * (d_v / 64) / 256) chunks per segment (at least 8),
  * and only when a sequence of T_max tokens would have 3 segments or more.
@@ -206,7 +212,7 @@ int32_t la_chunk_fwd_seg_len(const la_chunk_fwd_args *a);
 typedef struct {
     int32_t N, H;              /* sequences (one token each) and heads (>= 1)    */
     int32_t d_k, d_v;          /* d_k == d_v: 64 or 128                          */
-    int32_t qkv_dtype;         /* LA_BF16 or LA_F32: dtype of q, k, v            */
+    int32_t qkv_dtype;         /* LA_BF16, LA_F16 or LA_F32: dtype of q, k, v    */
     int32_t H_qk;              /* q, k heads: 0 = H; else H % H_qk == 0          */
     int32_t o_bf16;            /* 0: o fp32; 1: o bf16 (nearest even)            */
     float scale;               /* o = scale * S q                                */
@@ -230,7 +236,7 @@ typedef struct {
  * workspace, capturable.
  * Host errors: LA_ERR_NULL (q, k, v, g, beta or o NULL), LA_ERR_SHAPE (N or
  * H < 1, N * H beyond 2^31 - 1, H_qk < 0 or not dividing H, or q, k, v, h0,
- * ht, o not 16-byte aligned), LA_ERR_DTYPE (qkv_dtype, o_bf16 not 0 / 1),
+ * ht, o not 16-byte aligned), LA_ERR_DTYPE (qkv_dtype unknown, o_bf16 not 0 / 1),
  * LA_ERR_UNSUPPORTED (d_k != d_v or not 64 / 128), LA_ERR_ALIAS, LA_ERR_HIP.
  */
 int gdn_recurrent_fwd(const la_recurrent_args *a, void *stream);

@@ -48,6 +48,8 @@ def _l2norm(x):
 
 def _store(x, dtype):
     x = np.asarray(x, dtype=np.float32)
+    if dtype == "f16":
+        return x.astype(np.float16).astype(np.float32)   # nearest fp16
     return bf16_round(x) if dtype == "bf16" else x
 
 
@@ -58,7 +60,7 @@ def make_inputs(T, H, dk, dv, *, kda, dtype, seed, cu_seqlens=None, h0_std=None,
     q, k ~ N(0,1) then L2-normalised per (token, head); v ~ N(0,1);
     beta = sigmoid(N(0,1)); g = logsigmoid(N(0,1) + 3), per (token, head) for
     GDN and per (token, head, key channel) for KDA.  q/k/v are rounded to the
-    storage dtype ("bf16" or "f32"); g and beta stay float32 unless
+    storage dtype ("bf16", "f16" or "f32"); g and beta stay float32 unless
     ``round_gate`` asks for bf16-valued gates.
 
     ``cuts`` is an optional callable ``rng -> cu_seqlens`` drawn after beta, so a

@@ -8,8 +8,10 @@ import chunkwise_gated_delta_chunk_amd as la
 from oracle import recurrence
 
 # max relative error gates: bf16 inputs (fp16 MFMA operands, fp32 accumulation)
-# and fp32 inputs (fp32 MFMA)
-TOL = {"bf16": 2e-3, "f32": 1e-4}
+# and fp32 inputs (fp32 MFMA); fp16 inputs take the bf16 path's operands and
+# its gate
+TOL = {"bf16": 2e-3, "f16": 2e-3, "f32": 1e-4}
+TORCH_DT = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}
 
 
 def rel_err(x, ref, mask=None):
@@ -55,21 +57,21 @@ def gva(inp, H_qk):
     return small, full
 
 
-def to_dev(inp, device="cuda"):
-    tdt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+def to_dev(inp, device="cuda", cu_dtype=torch.int32):
+    tdt = TORCH_DT[inp["dtype"]]
     d = {}
     for key in ("q", "k", "v"):
         d[key] = torch.from_numpy(inp[key]).to(device=device, dtype=tdt).contiguous()
     for key in ("g", "beta"):
         d[key] = torch.from_numpy(inp[key]).to(device=device).contiguous()
-    d["cu_seqlens"] = torch.from_numpy(inp["cu_seqlens"].astype(np.int32)).to(device)
+    d["cu_seqlens"] = torch.from_numpy(inp["cu_seqlens"].astype(np.int64)).to(device, cu_dtype)
     d["h0"] = None if inp["h0"] is None else torch.from_numpy(inp["h0"]).to(device).contiguous()
     return d
 
 
 def run_gpu(inp, *, dv_split=0, scale=1.0, device="cuda", with_state=True, o=None, ht=None,
-            h0=None, stream=None, seg_len=0, o_dtype=None):
-    d = to_dev(inp, device)
+            h0=None, stream=None, seg_len=0, o_dtype=None, cu_dtype=torch.int32):
+    d = to_dev(inp, device, cu_dtype)
     T = inp["q"].shape[0]
     ci, co, st = la.build_chunk_meta(d["cu_seqlens"], T, stream=stream)
     fwd = la.kda_chunk_fwd if inp["kda"] else la.gdn_chunk_fwd

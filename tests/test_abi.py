@@ -24,7 +24,7 @@ def declared_functions():
 
 def test_exports_every_declared_function():
     names = declared_functions()
-    assert {"build_chunk_meta", "gdn_chunk_fwd", "kda_chunk_fwd", "la_nt_max",
+    assert {"build_chunk_meta", "build_chunk_meta_i64", "gdn_chunk_fwd", "kda_chunk_fwd", "la_nt_max",
             "la_chunk_fwd_workspace_bytes", "la_status_string"} <= set(names)
     L = ctypes.CDLL(la.LIB_PATH)
     for n in names:
@@ -82,6 +82,10 @@ BAD = [
     ("H_qk not dividing H", dict(H=6, H_qk=4), -2),
     ("H_qk negative", dict(H_qk=-1), -2),
     ("o_bf16 2", dict(o_bf16=2), -3),
+    ("cu_seqlens_i64 2", dict(cu_seqlens_i64=2), -3),
+    ("fp16 d 96", dict(qkv_dtype=2, d_k=96, d_v=96), -4),
+    ("fp16 BT 32", dict(qkv_dtype=2, BT=32), -4),
+    ("fp32 segmented", dict(qkv_dtype=1, seg_len=4), -4),
 ]
 
 
@@ -102,15 +106,17 @@ def test_forward_null_args_and_bad_stages():
     assert L.la_chunk_fwd_stages(ctypes.byref(a), 0, 4, None) == -4
 
 
-def test_meta_rejects_on_host():
-    L = la.lib()
+@pytest.mark.parametrize("fn", ["build_chunk_meta", "build_chunk_meta_i64"])
+def test_meta_rejects_on_host(fn):
+    f = getattr(la.lib(), fn)
     p = ctypes.c_void_p(0x100000)
-    assert L.build_chunk_meta(None, 2, 256, 64, p, p, None, None) == -1
-    assert L.build_chunk_meta(p, 2, 256, 64, None, p, None, None) == -1
-    assert L.build_chunk_meta(p, 0, 256, 64, p, p, None, None) == -2
-    assert L.build_chunk_meta(p, 8193, 256, 64, p, p, None, None) == -2
-    assert L.build_chunk_meta(p, 2, 0, 64, p, p, None, None) == -2
-    assert L.build_chunk_meta(p, 2, 256, 32, p, p, None, None) == -4
+    assert f(None, 2, 256, 64, p, p, None, None) == -1
+    assert f(p, 2, 256, 64, None, p, None, None) == -1
+    assert f(p, 0, 256, 64, p, p, None, None) == -2
+    assert f(p, 8193, 256, 64, p, p, None, None) == -2
+    assert f(p, 2, 0, 64, p, p, None, None) == -2
+    for bt in (16, 48, 128, 0):  # 32 and 64 are built
+        assert f(p, 2, 256, bt, p, p, None, None) == -4
 
 
 def test_workspace_size_and_split():
@@ -200,6 +206,7 @@ RBAD = [
     ("H 0", dict(H=0), -2),
     ("N*H too big", dict(N=1 << 20, H=1 << 12), -2),
     ("dtype 5", dict(qkv_dtype=5), -3),
+    ("fp16 d 96", dict(qkv_dtype=2, d_k=96, d_v=96), -4),
     ("d 96", dict(d_k=96, d_v=96), -4),
     ("d_k != d_v", dict(d_v=64), -4),
     ("v misaligned", dict(v=0x100004), -2),

@@ -12,7 +12,7 @@ import torch
 
 import chunkwise_gated_delta_chunk_amd as la
 from synth import make_inputs
-from tests.helpers import TOL, gva, rel_err, rel_err_bf16_out, run_oracle
+from tests.helpers import TOL, TORCH_DT, gva, rel_err, rel_err_bf16_out, run_oracle
 
 pytestmark = pytest.mark.gpu
 
@@ -29,7 +29,7 @@ def _step_inputs(N, H, d, kda, dtype, seed, h0_std=0.1):
 
 
 def _dev(inp):
-    tdt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    tdt = TORCH_DT[inp["dtype"]]
     d = {key: torch.from_numpy(inp[key]).cuda().to(tdt).contiguous() for key in ("q", "k", "v")}
     for key in ("g", "beta"):
         d[key] = torch.from_numpy(inp[key]).cuda().contiguous()
@@ -38,7 +38,8 @@ def _dev(inp):
 
 
 @pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
-@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f32", 128), ("f32", 64)])
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f16", 128), ("f32", 128),
+                                     ("f32", 64)])
 def test_recurrent_step_matches_oracle(kda, dtype, d):
     inp = _step_inputs(37, 5, d, kda, dtype, seed=200 + d)
     dv = _dev(inp)

@@ -24,11 +24,11 @@ def _say(*a):
 
 
 # ------------------------------------------------------------- metadata ---
-def _meta_case(cu, N_max, T_max):
-    cu_t = torch.tensor(cu, dtype=torch.int32, device="cuda")
-    ci, co, st = la.build_chunk_meta(cu_t, T_max)
+def _meta_case(cu, N_max, T_max, BT=64, idx=torch.int32):
+    cu_t = torch.tensor(cu, dtype=idx, device="cuda")
+    ci, co, st = la.build_chunk_meta(cu_t, T_max, BT)
     torch.cuda.synchronize()
-    ref_i, ref_o, ref_s = meta_ref.chunk_meta(cu, N_max, T_max, 64)
+    ref_i, ref_o, ref_s = meta_ref.chunk_meta(cu, N_max, T_max, BT)
     assert np.array_equal(ci.cpu().numpy(), ref_i)
     assert np.array_equal(co.cpu().numpy(), ref_o)
     assert int(st.item()) == ref_s
@@ -38,10 +38,9 @@ def test_meta_golden_cases():
     import json, os
     cases = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "meta_cases.json")))
     for c in cases["cases"]:
-        if c["BT"] != 64:
-            continue
-        _say("meta case", c["name"])
-        _meta_case(c["cu"], c["N_max"], c["T_max"])
+        for idx in (torch.int32, torch.int64):
+            _say("meta case", c["name"], c["BT"], idx)
+            _meta_case(c["cu"], c["N_max"], c["T_max"], c["BT"], idx)
 
 
 @pytest.mark.parametrize("seed", range(6))
