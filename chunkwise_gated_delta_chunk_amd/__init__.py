@@ -24,7 +24,7 @@ import torch
 __all__ = [
     "LinAttnError", "lib", "nt_max", "build_chunk_meta", "workspace_bytes",
     "gdn_chunk_fwd", "kda_chunk_fwd", "chunk_fwd_stages", "dv_split_for", "seg_len_for",
-    "gdn_recurrent_fwd", "kda_recurrent_fwd",
+    "gdn_recurrent_fwd", "kda_recurrent_fwd", "short_conv_fwd",
     "STAGE_MAP", "STAGE_REDUCE", "META_BAD_START", "META_NOT_MONOTONE",
     "META_OVER_CAPACITY", "LIB_PATH",
 ]
@@ -72,6 +72,20 @@ class RecurrentArgs(ctypes.Structure):
     ]
 
 
+class ShortConvArgs(ctypes.Structure):
+    _fields_ = [
+        ("T_max", ctypes.c_int32), ("N_max", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("W", ctypes.c_int32), ("BT", ctypes.c_int32), ("x_dtype", ctypes.c_int32),
+        ("activation", ctypes.c_int32), ("cu_seqlens_i64", ctypes.c_int32),
+        ("x", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("bias", ctypes.c_void_p),
+        ("residual", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+        ("chunk_indices", ctypes.c_void_p), ("h0", ctypes.c_void_p), ("y", ctypes.c_void_p),
+        ("ht", ctypes.c_void_p),
+    ]
+
+
+ACTIVATIONS = {None: 0, "silu": 1}
+
 _lib = None
 
 
@@ -105,6 +119,8 @@ def lib():
         for f in (L.gdn_recurrent_fwd, L.kda_recurrent_fwd):
             f.restype = ctypes.c_int
             f.argtypes = [R, ctypes.c_void_p]
+        L.la_short_conv_fwd.restype = ctypes.c_int
+        L.la_short_conv_fwd.argtypes = [ctypes.POINTER(ShortConvArgs), ctypes.c_void_p]
         L.la_status_string.restype = ctypes.c_char_p
         L.la_status_string.argtypes = [ctypes.c_int]
         _lib = L
@@ -365,3 +381,57 @@ def gdn_recurrent_fwd(q, k, v, g, beta, **kw):
 def kda_recurrent_fwd(q, k, v, g, beta, **kw):
     """One KDA decode step (g [N, H, d_k]); returns (o, ht)."""
     return _recurrent("kda_recurrent_fwd", True, q, k, v, g, beta, **kw)
+
+
+def short_conv_fwd(x, weight, cu_seqlens, chunk_indices, *, bias=None, residual=None, h0=None,
+                   y=None, ht=None, output_final_state=True, activation=None, BT=64,
+                   stream=None):
+    """Varlen causal short convolution (la_short_conv_fwd); returns (y, ht).
+
+    x [T_max, D] bf16 / fp16 / fp32; weight [D, W] fp32; bias [D] fp32;
+    residual [T_max, D] like x; h0 / ht [N_max, W-1, D] like x; activation
+    None or "silu"; chunk_indices from build_chunk_meta(cu_seqlens, T_max, BT).
+    """
+    xdt = _qkv_dtype(x)
+    if x.dim() != 2 or weight.dim() != 2:
+        raise ValueError("x must be [T_max, D] and weight [D, W]")
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be None or 'silu', got {activation!r}")
+    T_max, D = x.shape
+    W = weight.shape[1]
+    dev = x.device
+    _need(x, "x", x.dtype)
+    _need(weight, "weight", torch.float32, (D, W), dev)
+    if bias is not None:
+        _need(bias, "bias", torch.float32, (D,), dev)
+    if residual is not None:
+        _need(residual, "residual", x.dtype, (T_max, D), dev)
+    _need_idx(cu_seqlens, dev)
+    N_max = cu_seqlens.numel() - 1
+    _need(chunk_indices, "chunk_indices", torch.int32, (nt_max(T_max, N_max, BT), 2), dev)
+    st_shape = (N_max, max(W - 1, 0), D)
+    if h0 is not None:
+        _need(h0, "h0", x.dtype, st_shape, dev)
+    if y is None:
+        y = torch.empty((T_max, D), dtype=x.dtype, device=dev)
+    _need(y, "y", x.dtype, (T_max, D), dev)
+    if ht is None and output_final_state and W > 1:
+        ht = torch.empty(st_shape, dtype=x.dtype, device=dev)
+    if ht is not None:
+        _need(ht, "ht", x.dtype, st_shape, dev)
+    a = ShortConvArgs()
+    a.T_max, a.N_max, a.D, a.W, a.BT = T_max, N_max, D, W, int(BT)
+    a.x_dtype = xdt
+    a.activation = ACTIVATIONS[activation]
+    a.cu_seqlens_i64 = int(cu_seqlens.dtype == torch.int64)
+    a.x, a.weight, a.y = x.data_ptr(), weight.data_ptr(), y.data_ptr()
+    a.bias = None if bias is None else bias.data_ptr()
+    a.residual = None if residual is None else residual.data_ptr()
+    a.cu_seqlens = cu_seqlens.data_ptr()
+    a.chunk_indices = chunk_indices.data_ptr()
+    a.h0 = None if h0 is None else h0.data_ptr()
+    a.ht = None if ht is None else ht.data_ptr()
+    rc = lib().la_short_conv_fwd(ctypes.byref(a), _stream(stream))
+    if rc != 0:
+        raise LinAttnError(rc, "la_short_conv_fwd")
+    return y, ht

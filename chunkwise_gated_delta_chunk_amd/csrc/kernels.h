@@ -64,6 +64,17 @@ struct RecurrentParams {
   int o_bf16;
 };
 
+// Varlen causal short convolution (short_conv.hip): x, res, y and the states
+// in the input dtype; w [D][W], b [D] fp32; states [N_max][W-1][D].
+struct ConvParams {
+  const void *x, *res, *h0;
+  const float *w, *b;
+  const void *cu_seqlens;  // int32, or int64 with cu64
+  const int32_t *chunk_indices;
+  int cu64, D, BT;
+  void *y, *ht;
+};
+
 // cu: int32 cu_seqlens, or int64 with cu64
 hipError_t launch_chunk_meta(const void *cu, int cu64, int N_max, int T_max, int BT, int NT_max,
                              int32_t *ci, int32_t *co, int32_t *status, hipStream_t stream);
@@ -74,5 +85,8 @@ hipError_t launch_chunk_reduce(const ReduceParams &p, bool kda, int dt, int dk, 
                                hipStream_t st);
 hipError_t launch_chunk_combine(const CombineParams &p, int dk, hipStream_t st);
 hipError_t launch_recurrent(const RecurrentParams &p, bool kda, int dt, int dk, hipStream_t st);
+// NT chunk slots, W in 1..4
+hipError_t launch_short_conv(const ConvParams &p, int dt, int NT, int W, bool silu,
+                             hipStream_t st);
 
 }  // namespace la

@@ -305,6 +305,55 @@ int gdn_recurrent_fwd(const la_recurrent_args *a, void *stream) { return recurre
 
 int kda_recurrent_fwd(const la_recurrent_args *a, void *stream) { return recurrent(a, true, stream); }
 
+int la_short_conv_fwd(const la_short_conv_args *a, void *stream) {
+  if (!a) return LA_ERR_NULL;
+  if (!a->x || !a->weight || !a->cu_seqlens || !a->chunk_indices || !a->y) return LA_ERR_NULL;
+  if (!known_dtype(a->x_dtype)) return LA_ERR_DTYPE;
+  if (a->activation != LA_ACT_NONE && a->activation != LA_ACT_SILU) return LA_ERR_DTYPE;
+  if (a->cu_seqlens_i64 != 0 && a->cu_seqlens_i64 != 1) return LA_ERR_DTYPE;
+  if (a->W < 1 || a->W > 4) return LA_ERR_UNSUPPORTED;
+  if (a->BT != 32 && a->BT != 64) return LA_ERR_UNSUPPORTED;
+  if (a->T_max < 1 || a->N_max < 1 || a->D < 1) return LA_ERR_SHAPE;
+  if (a->T_max > 0x7fffffff - 2 * kBTSupported) return LA_ERR_SHAPE;
+  const int esz = a->x_dtype == LA_F32 ? 4 : 2;
+  if (a->D % (16 / esz) != 0) return LA_ERR_SHAPE;
+  const int64_t nt = la_nt_max(a->T_max, a->N_max, a->BT);
+  if (nt < 1 || nt > 0x7fffffff) return LA_ERR_SHAPE;
+  // element indices of x / y and of the states stay in size_t; the grid's y
+  // dimension (channel blocks of 64 x 16 bytes) stays within 65535
+  if ((int64_t)a->D * esz / 1024 >= 65535) return LA_ERR_SHAPE;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(a->x) | reinterpret_cast<uintptr_t>(a->y) |
+                        reinterpret_cast<uintptr_t>(a->residual) |
+                        reinterpret_cast<uintptr_t>(a->h0) | reinterpret_cast<uintptr_t>(a->ht) |
+                        reinterpret_cast<uintptr_t>(a->weight) |
+                        reinterpret_cast<uintptr_t>(a->bias);
+  if (mis % 16 != 0) return LA_ERR_SHAPE;
+  const size_t xb = (size_t)a->T_max * a->D * esz;
+  if (overlaps(a->x, xb, a->y, xb)) return LA_ERR_ALIAS;
+  if (a->residual && a->residual != a->y && overlaps(a->residual, xb, a->y, xb)) return LA_ERR_ALIAS;
+  if (a->W > 1 && a->h0 && a->ht && a->h0 != a->ht) {
+    const size_t sb = (size_t)a->N_max * (a->W - 1) * a->D * esz;
+    if (overlaps(a->h0, sb, a->ht, sb)) return LA_ERR_ALIAS;
+  }
+  la::ConvParams cp{};
+  cp.x = a->x;
+  cp.res = a->residual;
+  cp.h0 = a->W > 1 ? a->h0 : nullptr;
+  cp.w = a->weight;
+  cp.b = a->bias;
+  cp.cu_seqlens = a->cu_seqlens;
+  cp.chunk_indices = a->chunk_indices;
+  cp.cu64 = a->cu_seqlens_i64;
+  cp.D = a->D;
+  cp.BT = a->BT;
+  cp.y = a->y;
+  cp.ht = a->W > 1 ? a->ht : nullptr;
+  if (la::launch_short_conv(cp, a->x_dtype, (int)nt, a->W, a->activation == LA_ACT_SILU,
+                            static_cast<hipStream_t>(stream)) != hipSuccess)
+    return LA_ERR_HIP;
+  return LA_OK;
+}
+
 const char *la_status_string(int status) {
   switch (status) {
     case LA_OK: return "ok";

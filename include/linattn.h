@@ -242,6 +242,57 @@ typedef struct {
 int gdn_recurrent_fwd(const la_recurrent_args *a, void *stream);
 int kda_recurrent_fwd(const la_recurrent_args *a, void *stream);
 
+/* Activation of the short convolution. */
+#define LA_ACT_NONE 0
+#define LA_ACT_SILU 1
+
+/* Arguments of the varlen causal short convolution. */
+typedef struct {
+    int32_t T_max, N_max;      /* bucket capacity (>= 1)                         */
+    int32_t D;                 /* channels: a multiple of 8 (16-bit x) or 4      */
+    int32_t W;                 /* kernel width, 1 .. 4                           */
+    int32_t BT;                /* chunk size chunk_indices was built with: 32/64 */
+    int32_t x_dtype;           /* LA_BF16, LA_F16 or LA_F32: x, residual, y,     */
+                               /* h0 and ht                                      */
+    int32_t activation;        /* LA_ACT_NONE or LA_ACT_SILU                     */
+    int32_t cu_seqlens_i64;    /* 0: cu_seqlens int32; 1: int64                  */
+    const void *x;             /* [T_max][D]                                     */
+    const float *weight;       /* [D][W] fp32                                    */
+    const float *bias;         /* [D] fp32 or NULL                               */
+    const void *residual;      /* [T_max][D] or NULL; may be y itself            */
+    const void *cu_seqlens;    /* [N_max+1], int32 or int64                      */
+    const int32_t *chunk_indices; /* [NT_max][2], build_chunk_meta with this BT  */
+    const void *h0;            /* [N_max][W-1][D] or NULL (zero history)         */
+    void *y;                   /* [T_max][D]; must not overlap x                 */
+    void *ht;                  /* [N_max][W-1][D] or NULL; may equal h0          */
+} la_short_conv_args;
+
+/*
+ * Varlen causal short convolution forward, the layer step before the chunk
+ * attention, run on the same chunk metadata (FLA RFC, sections "Proposed API"
+ * and "Step 3: GDN and short-convolution graph support"; the reuse of that
+ * metadata: "Empowering Hybrid Attention Models on NPUs", section 7).  Per
+ * sequence n, channel c and token t of the sequence (inputs x_p, p < 0, are
+ * row W-1+p of h0[n], zero when h0 is NULL):
+ *   y_t[c] = act(bias[c] + sum_{i<W} weight[c][i] x_{t-W+1+i}[c]) + residual_t[c]
+ * with act the identity or SiLU (z sigmoid(z)), computed in fp32 and rounded
+ * to x_dtype (nearest even).  ht[n] = the W-1 inputs ending at the sequence's
+ * last token (reaching into h0[n] for sequences shorter than W-1), copied
+ * bit for bit; ht may equal h0.  Rows of y outside every sequence, sentinel
+ * slots and ht of zero-length sequences are not written.  chunk_indices must
+ * come from build_chunk_meta on the same cu_seqlens, T_max, N_max and BT.
+ * One launch, no workspace, capturable.  x, residual, y, h0, ht, weight and
+ * bias must be 16-byte aligned.
+ * Host errors: LA_ERR_NULL (x, weight, cu_seqlens, chunk_indices or y NULL),
+ * LA_ERR_SHAPE (T_max, N_max or D < 1, D not a multiple of the channels of a
+ * 16-byte piece, sizes beyond the index range, misaligned pointers),
+ * LA_ERR_DTYPE (x_dtype, activation or cu_seqlens_i64 unknown),
+ * LA_ERR_UNSUPPORTED (W not 1 .. 4, BT not 32 or 64), LA_ERR_ALIAS (y
+ * overlapping x or partly overlapping residual, ht partly overlapping h0),
+ * LA_ERR_HIP.
+ */
+int la_short_conv_fwd(const la_short_conv_args *a, void *stream);
+
 /* Static text for a la_status value. */
 const char *la_status_string(int status);
 

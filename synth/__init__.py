@@ -93,6 +93,28 @@ def make_inputs(T, H, dk, dv, *, kda, dtype, seed, cu_seqlens=None, h0_std=None,
                 T=T, H=H, dk=dk, dv=dv, kda=bool(kda), dtype=dtype)
 
 
+def make_conv_inputs(T, D, W, *, dtype, seed, cu_seqlens=None, bias=True, residual=False,
+                     h0=False):
+    """Inputs of the short convolution, drawn in a fixed order: x, weight,
+    bias, residual, h0.
+
+    x ~ N(0,1) [T, D] rounded to the storage dtype; weight ~ N(0, 0.5)
+    [D, W] float32; bias ~ N(0, 0.1) [D] float32; residual ~ N(0,1) [T, D] and
+    h0 ~ N(0,1) [N, W-1, D], both in the storage dtype (h0 holds past inputs).
+    ``cu_seqlens`` defaults to one sequence of length T.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    x = _store(rng.standard_normal((T, D)), dtype)
+    w = (rng.standard_normal((D, W)) * 0.5).astype(np.float32)
+    b = (rng.standard_normal(D) * 0.1).astype(np.float32) if bias else None
+    r = _store(rng.standard_normal((T, D)), dtype) if residual else None
+    cu = np.array([0, T] if cu_seqlens is None else cu_seqlens, dtype=np.int64)
+    N = len(cu) - 1
+    s0 = _store(rng.standard_normal((N, W - 1, D)), dtype) if h0 else None
+    return dict(x=x, weight=w, bias=b, residual=r, h0=s0, cu_seqlens=cu, T=T, D=D, W=W,
+                dtype=dtype)
+
+
 def _uniform_cuts(T, n):
     """n sequences covering [0, T): n-1 distinct cut points uniform on {1..T-1}."""
     def draw(rng):

@@ -224,3 +224,45 @@ def test_recurrent_rejects_on_host(name, kw, code):
     assert L.gdn_recurrent_fwd(ctypes.byref(a), None) == code
     assert L.kda_recurrent_fwd(ctypes.byref(a), None) == code
     assert L.gdn_recurrent_fwd(None, None) == -1
+
+
+def _cargs(**kw):
+    a = la.ShortConvArgs()
+    a.T_max, a.N_max, a.D, a.W, a.BT, a.x_dtype = 256, 2, 64, 4, 64, 0
+    fake = 0x100000  # never dereferenced: every case fails before launch
+    for f in ("x", "weight", "cu_seqlens", "chunk_indices"):
+        setattr(a, f, fake)
+    a.y = 0x8000000
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+CBAD = [
+    ("null x", dict(x=None), -1),
+    ("null weight", dict(weight=None), -1),
+    ("null y", dict(y=None), -1),
+    ("null chunk_indices", dict(chunk_indices=None), -1),
+    ("dtype 3", dict(x_dtype=3), -3),
+    ("activation 2", dict(activation=2), -3),
+    ("cu_seqlens_i64 2", dict(cu_seqlens_i64=2), -3),
+    ("W 0", dict(W=0), -4),
+    ("W 5", dict(W=5), -4),
+    ("BT 16", dict(BT=16), -4),
+    ("T_max 0", dict(T_max=0), -2),
+    ("D 0", dict(D=0), -2),
+    ("D 12 bf16", dict(D=12), -2),
+    ("D 6 fp32", dict(D=6, x_dtype=1), -2),
+    ("x misaligned", dict(x=0x100008), -2),
+    ("bias misaligned", dict(bias=0x100004), -2),
+    ("y over x", dict(y=0x100000 + 64), -6),
+    ("y partly over residual", dict(residual=0x9000000, y=0x9000000 + 32), -6),
+    ("ht partly over h0", dict(h0=0x200000, ht=0x200000 + 128), -6),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", CBAD, ids=[b[0] for b in CBAD])
+def test_short_conv_rejects_on_host(name, kw, code):
+    a = _cargs(**kw)
+    assert la.lib().la_short_conv_fwd(ctypes.byref(a), None) == code
+    assert la.lib().la_short_conv_fwd(None, None) == -1
