@@ -28,6 +28,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16/bf16 MFMA, published
+MFMA_F32_PEAK_TFLOPS = 157.3   # MI355X dense fp32 matrix, published
 
 WORKLOADS = {
     "c1": (1, None, "GDN varlen prefill: bf16 q/k/v, fp32 g/beta/state, H=16, d_k=d_v=128, "
@@ -45,6 +46,8 @@ WORKLOADS = {
                          "d_k=d_v=128, fp32 state N(0,0.1) updated in place, seed 5"),
     "deck": (None, True, "KDA decode step: 64 sequences x 1 token, bf16 q/k/v, H=16, "
                          "d_k=d_v=128, fp32 state N(0,0.1) updated in place, seed 5"),
+    "bwd": (1, None, "GDN chunk backward on the 8K varlen workload: bf16 q/k/v, fp32 g/beta, "
+                     "H=16, d_k=d_v=128, h0~N(0,0.1), dout~N(0,1) fp32, no dht, seed 1"),
     "conv": (None, None, "varlen causal short convolution: bf16 x [8192, 6144] (q, k, v "
                          "projections of H=16, d=128) in the 8 sequences of the 8K varlen "
                          "layout, W=4, bias, SiLU, bf16 states N(0,1) updated in place, "
@@ -369,6 +372,97 @@ def conv_cpu_baseline(inp, budget_s=12.0):
                       f"{len(times)} run(s) of the fp64 numpy token loop"}
 
 
+def bwd_alg_flops(cells, d):
+    """Algorithmic flops of the chunk backward per (chunk, head) cell, summed:
+    the per-chunk products of the state-gradient pass (3 x 64 d^2 + 2 x 64^2 d
+    MACs), of the dV / partial-product pass (5 x 64 d^2 + 5 x 64^2 d), of the
+    final pass (4 x 64^2 d + 2 x 64^3), of the prep (2 x 64^2 d + 64^3 / 3) and
+    of the forward state recompute (2 x 64 d^2 + 64^2 d + the map's 2 x 64^2 d
+    + 64^3 / 3); 2 flops per MAC."""
+    c = 64
+    macs = (3 * c * d * d + 2 * c * c * d) + (5 * c * d * d + 5 * c * c * d) + \
+        (4 * c * c * d + 2 * c ** 3) + (2 * c * c * d + c ** 3 / 3) + \
+        (2 * c * d * d + c * c * d + 2 * c * c * d + c ** 3 / 3)
+    return 2 * macs * cells
+
+
+def bench_bwd(args, torch, la, synth, dev):
+    """One GDN chunk backward per step (forward recompute + four backward
+    launches) on the 8K varlen inputs; HIP events around the calls, then a
+    graph of one call replayed."""
+    desc = WORKLOADS[args.workload][2]
+    inp = synth.config(1)
+    T, H, d = inp["q"].shape[0], inp["H"], inp["dk"]
+    bf = torch.bfloat16
+    q, k, v = (torch.from_numpy(inp[x]).to(dev, bf) for x in ("q", "k", "v"))
+    g = torch.from_numpy(inp["g"]).to(dev)
+    beta = torch.from_numpy(inp["beta"]).to(dev)
+    h0 = torch.from_numpy(inp["h0"]).to(dev)
+    rng = np.random.default_rng(1)
+    dout = torch.from_numpy(rng.standard_normal((T, H, d)).astype(np.float32)).to(dev)
+    cu = torch.from_numpy(inp["cu_seqlens"].astype(np.int32)).to(dev)
+    N = cu.numel() - 1
+    ci, co, _ = la.build_chunk_meta(cu, T)
+    ws = torch.empty((la.bwd_workspace_bytes(T, N, H, d, d, bf),), dtype=torch.uint8, device=dev)
+    outs = dict(dq=torch.empty((T, H, d), device=dev), dk=torch.empty((T, H, d), device=dev),
+                dv=torch.empty((T, H, d), device=dev), dg=torch.empty((T, H), device=dev),
+                dbeta=torch.empty((T, H), device=dev), dh0=torch.empty_like(h0))
+
+    def step():
+        la.gdn_chunk_bwd(q, k, v, g, beta, cu, ci, co, dout, h0=h0, workspace=ws, **outs)
+
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    call_ms = e0.elapsed_time(e1) / args.steps
+    eager = {key: t.clone() for key, t in outs.items()}
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    graph.replay()
+    torch.cuda.synchronize()
+    graph_eq = all(torch.equal(outs[key], eager[key]) for key in outs)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+    cells = int(np.ceil(np.diff(inp["cu_seqlens"]) / 64).sum()) * H
+    fl = bwd_alg_flops(cells, d)
+    achieved = fl / (call_ms * 1e-3) / 1e12
+    out = {
+        "metric": "GDN/KDA chunk-fwd tokens/s (H=16,d=128,8K varlen); % of HBM/MFMA roofline",
+        "value": round(T * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 inputs; fp32 backward arithmetic",
+        "data": "synthetic (seeded, resident in HBM)",
+        "config": {"workload": desc, "mode": "graph-replay of one backward call",
+                   "tokens": T, "heads": H, "d": d, "sequences": N},
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_F32_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "gdn_chunk_bwd (whole call: map, reduce, prep, dh, part, final)",
+                     "alg_flops_per_call": fl, "avg_call_ms": round(call_ms, 5)},
+        "graph_equals_eager": graph_eq,
+    }
+    print(json.dumps(out), flush=True)
+
+
 def bench_decode(args, torch, la, synth, dev):
     """One recurrent (decode) step per replay: a token for each of N sequences,
     the state updated in place; HIP events around the launch, then a graph of
@@ -497,6 +591,9 @@ def main():
         return
     if args.workload == "conv":
         bench_conv(args, torch, la, synth, dev)
+        return
+    if args.workload == "bwd":
+        bench_bwd(args, torch, la, synth, dev)
         return
 
     cfg, kda, desc = WORKLOADS[args.workload]

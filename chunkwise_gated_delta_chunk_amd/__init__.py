@@ -24,7 +24,8 @@ import torch
 __all__ = [
     "LinAttnError", "lib", "nt_max", "build_chunk_meta", "workspace_bytes",
     "gdn_chunk_fwd", "kda_chunk_fwd", "chunk_fwd_stages", "dv_split_for", "seg_len_for",
-    "gdn_recurrent_fwd", "kda_recurrent_fwd", "short_conv_fwd",
+    "gdn_recurrent_fwd", "kda_recurrent_fwd", "short_conv_fwd", "gdn_chunk_bwd",
+    "bwd_workspace_bytes",
     "STAGE_MAP", "STAGE_REDUCE", "META_BAD_START", "META_NOT_MONOTONE",
     "META_OVER_CAPACITY", "LIB_PATH",
 ]
@@ -84,6 +85,22 @@ class ShortConvArgs(ctypes.Structure):
     ]
 
 
+class ChunkBwdArgs(ctypes.Structure):
+    _fields_ = [
+        ("T_max", ctypes.c_int32), ("N_max", ctypes.c_int32), ("H", ctypes.c_int32),
+        ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("BT", ctypes.c_int32),
+        ("qkv_dtype", ctypes.c_int32), ("cu_seqlens_i64", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
+        ("chunk_indices", ctypes.c_void_p), ("chunk_offsets", ctypes.c_void_p),
+        ("h0", ctypes.c_void_p), ("dout", ctypes.c_void_p), ("dht", ctypes.c_void_p),
+        ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
+        ("dg", ctypes.c_void_p), ("dbeta", ctypes.c_void_p), ("dh0", ctypes.c_void_p),
+        ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+    ]
+
+
 ACTIVATIONS = {None: 0, "silu": 1}
 
 _lib = None
@@ -119,6 +136,11 @@ def lib():
         for f in (L.gdn_recurrent_fwd, L.kda_recurrent_fwd):
             f.restype = ctypes.c_int
             f.argtypes = [R, ctypes.c_void_p]
+        B = ctypes.POINTER(ChunkBwdArgs)
+        L.la_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.la_chunk_bwd_workspace_bytes.argtypes = [B]
+        L.gdn_chunk_bwd.restype = ctypes.c_int
+        L.gdn_chunk_bwd.argtypes = [B, ctypes.c_void_p]
         L.la_short_conv_fwd.restype = ctypes.c_int
         L.la_short_conv_fwd.argtypes = [ctypes.POINTER(ShortConvArgs), ctypes.c_void_p]
         L.la_status_string.restype = ctypes.c_char_p
@@ -435,3 +457,82 @@ def short_conv_fwd(x, weight, cu_seqlens, chunk_indices, *, bias=None, residual=
     if rc != 0:
         raise LinAttnError(rc, "la_short_conv_fwd")
     return y, ht
+
+
+def _bwd_shape(T_max, N_max, H, d_k, d_v, qkv_dtype, BT=64):
+    a = ChunkBwdArgs()
+    a.T_max, a.N_max, a.H, a.d_k, a.d_v, a.BT = T_max, N_max, H, d_k, d_v, BT
+    a.qkv_dtype = _DTYPES.get(qkv_dtype, LA_F32)
+    return a
+
+
+def bwd_workspace_bytes(T_max, N_max, H, d_k, d_v, qkv_dtype, BT=64):
+    return int(lib().la_chunk_bwd_workspace_bytes(ctypes.byref(
+        _bwd_shape(T_max, N_max, H, d_k, d_v, qkv_dtype, BT))))
+
+
+def gdn_chunk_bwd(q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, dout, *, h0=None,
+                  dht=None, scale=1.0, dq=None, dk=None, dv=None, dg=None, dbeta=None, dh0=None,
+                  workspace=None, stream=None):
+    """GDN chunk backward (gdn_chunk_bwd): gradients of sum(o * dout) + sum(ht * dht).
+
+    Returns (dq, dk, dv, dg, dbeta, dh0) as fp32 tensors; dh0 is None unless
+    h0 is given or dh0 is passed.  dout [T_max, H, d_v] fp32.
+    """
+    _qkv_dtype(q)
+    T_max, H, d_k = q.shape
+    d_v = v.shape[-1]
+    dev = q.device
+    _need(q, "q", q.dtype)
+    _need(k, "k", q.dtype, (T_max, H, d_k), dev)
+    _need(v, "v", q.dtype, (T_max, H, d_v), dev)
+    _need(g, "g", torch.float32, (T_max, H), dev)
+    _need(beta, "beta", torch.float32, (T_max, H), dev)
+    _need_idx(cu_seqlens, dev)
+    N_max = cu_seqlens.numel() - 1
+    NT = nt_max(T_max, N_max)
+    _need(chunk_indices, "chunk_indices", torch.int32, (NT, 2), dev)
+    _need(chunk_offsets, "chunk_offsets", torch.int32, (N_max + 1,), dev)
+    _need(dout, "dout", torch.float32, (T_max, H, d_v), dev)
+    st_shape = (N_max, H, d_k, d_v)
+    if h0 is not None:
+        _need(h0, "h0", torch.float32, st_shape, dev)
+    if dht is not None:
+        _need(dht, "dht", torch.float32, st_shape, dev)
+
+    def out(t, shape, name):
+        if t is None:
+            t = torch.empty(shape, dtype=torch.float32, device=dev)
+        _need(t, name, torch.float32, shape, dev)
+        return t
+    dq = out(dq, (T_max, H, d_k), "dq")
+    dk = out(dk, (T_max, H, d_k), "dk")
+    dv = out(dv, (T_max, H, d_v), "dv")
+    dg = out(dg, (T_max, H), "dg")
+    dbeta = out(dbeta, (T_max, H), "dbeta")
+    if dh0 is None and h0 is not None:
+        dh0 = torch.empty(st_shape, dtype=torch.float32, device=dev)
+    if dh0 is not None:
+        _need(dh0, "dh0", torch.float32, st_shape, dev)
+    a = _bwd_shape(T_max, N_max, H, d_k, d_v, q.dtype)
+    a.cu_seqlens_i64 = int(cu_seqlens.dtype == torch.int64)
+    a.scale = float(scale)
+    need = int(lib().la_chunk_bwd_workspace_bytes(ctypes.byref(a)))
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, None, dev)
+    a.q, a.k, a.v, a.g, a.beta = (t.data_ptr() for t in (q, k, v, g, beta))
+    a.cu_seqlens = cu_seqlens.data_ptr()
+    a.chunk_indices = chunk_indices.data_ptr()
+    a.chunk_offsets = chunk_offsets.data_ptr()
+    a.h0 = None if h0 is None else h0.data_ptr()
+    a.dout = dout.data_ptr()
+    a.dht = None if dht is None else dht.data_ptr()
+    a.dq, a.dk, a.dv, a.dg, a.dbeta = (t.data_ptr() for t in (dq, dk, dv, dg, dbeta))
+    a.dh0 = None if dh0 is None else dh0.data_ptr()
+    a.workspace = workspace.data_ptr()
+    a.workspace_bytes = workspace.numel()
+    rc = lib().gdn_chunk_bwd(ctypes.byref(a), _stream(stream))
+    if rc != 0:
+        raise LinAttnError(rc, "gdn_chunk_bwd")
+    return dq, dk, dv, dg, dbeta, dh0

@@ -1,0 +1,588 @@
+// GDN chunk backward: gradients of L = <o, do> + <ht, dht> for q, k, v, the
+// log-decay g, beta and the initial state (the backward half of the FLA
+// graph-capture RFC's scope, sections "Scope" and "Step 3"), chunk by chunk
+// in the chunkwise form of "Empowering Hybrid Attention Models on NPUs"
+// (section 2.1).  Per chunk of C rows, with G the chunk-local cumulative
+// gate, gam_r = exp(G_r), fac_r = exp(G_{C-1} - G_r), gam_C = exp(G_{C-1}),
+// E_rs = exp(G_r - G_s), S = strict_lower(K K^T * E), A = I + diag(beta) S,
+// T = A^-1 diag(beta) and M = lower_incl(Q K^T * E), the forward is
+//   X = V - gam*(K H),  U = T X,  O = scale (gam*(Q H) + M U),
+//   H' = gam_C H + K^T (fac*U)
+// and its adjoint, given dO (dOb = scale dO) and dH' (the gradient of the
+// state leaving the chunk):
+//   dU = M^T dOb + fac*(K dH'),   dX = T^T dU,   dV = dX
+//   dH = gam_C dH' + Q^T (gam*dOb) - K^T (gam*dX)          (state entering)
+//   dQ = gam*(dOb H^T) + (dM*E) K,      dM = dOb U^T
+//   dK = -gam*(dX H^T) + fac*(U dH'^T) + (dM*E)^T Q + F K + F^T K
+//   dT = dU X^T -> dA^-1 = dT diag(beta), dA = -A^-T dA^-1 A^-T,
+//   dbeta_s += sum_r dT_rs A^-1_rs,  dbeta_r += sum_s dA_rs S_rs,
+//   F = beta_r dA_rs E_rs (strict lower), and the gate terms below,
+// with dg the reverse cumulative sum of dG inside the chunk.
+//
+// Four launches after the forward recompute (map + reduce storing every
+// chunk's entering state H): prep (per chunk slot and head: A^-1, M, S and the
+// gate vectors, fp32), dh (per sequence, head and 32 state columns, chunks in
+// reverse: the dH recurrence, storing dH' of every chunk and dh0), part (per
+// slot and head: dV and the d_v-contracted products dOb H^T, dX H^T,
+// U dH'^T, dM, dT and <dH', H>) and final (per slot and head: the chunk-local
+// algebra to dq, dk, dg, dbeta).  Arithmetic is fp32 on 16x16x4 MFMA.
+#include "la_device.h"
+#include "kernels.h"
+
+namespace la {
+
+namespace {
+
+constexpr int kL = 68;  // row stride of the [64][64] LDS matrices (floats)
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// acc += A(0..15, 0..K) B(0..K, 0..15) with A(m, k) at a[m * ams + k * aks] and
+// B(k, n) at b[k * bks + n * bns]; the result tile in the MFMA layout (lane l:
+// rows 4 (l / 16) + i, column l % 16).
+__device__ __forceinline__ f32x4 mm(f32x4 acc, const float *a, int ams, int aks, const float *b,
+                                    int bks, int bns, int K) {
+  const int l = lane_id(), r = l & 15, g = l >> 4;
+  const float *pa = a + r * ams + g * aks;
+  const float *pb = b + g * bks + r * bns;
+#pragma unroll 4
+  for (int k = 0; k < K; k += 4) acc = mfma4(pa[k * aks], pb[k * bks], acc);
+  return acc;
+}
+
+template <typename In>
+__device__ __forceinline__ float ldin(const void *p, size_t i) {
+  return Op<In>::load(static_cast<const In *>(p) + i);
+}
+
+// the chunk of slot jj: first row, valid rows; false for a sentinel slot
+struct Chunk { int n, r0, C; };
+__device__ __forceinline__ bool chunk_of(const BwdParams &p, int slot, Chunk &c) {
+  const int n = p.chunk_indices[2 * slot];
+  if (n < 0) return false;
+  const int i_t = p.chunk_indices[2 * slot + 1];
+  const int bos = cu_at(p.cu_seqlens, p.cu64, n);
+  const int eos = cu_at(p.cu_seqlens, p.cu64, n + 1);
+  c.n = n;
+  c.r0 = bos + i_t * kBT;
+  c.C = min(kBT, eos - c.r0);
+  return true;
+}
+
+// The loaders move 16-byte pieces, all of a thread's loads issued before its
+// LDS stores, so a chunk's operands arrive in about one memory round trip.
+
+// rows r < C of a [T][H][D] input, head h, columns c0 .. c0 + W, into LDS
+// rows of stride ld (fp32, 16-byte aligned rows); rows >= C are zero
+template <typename In, int D, int W = D, int R = kBT>
+__device__ __forceinline__ void load_rows(float *dst, int ld, const void *src, int r0, int C, int H,
+                                          int h, int c0 = 0) {
+  constexpr int VEC = 16 / (int)sizeof(In);
+  constexpr int PR = W / VEC;                 // pieces per row
+  constexpr int NP = R * PR;                  // pieces
+  constexpr int IT = (NP + 255) / 256;
+  uint32_t raw[IT][4];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int pc = threadIdx.x + 256 * it, r = pc / PR, c = (pc % PR) * VEC;
+    const u32x4 v = (pc < NP && r < C)
+        ? *reinterpret_cast<const u32x4 *>(static_cast<const char *>(src) +
+                                           (((size_t)(r0 + r) * H + h) * D + c0 + c) * sizeof(In))
+        : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) raw[it][e] = v[e];
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int pc = threadIdx.x + 256 * it, r = pc / PR, c = (pc % PR) * VEC;
+    if (pc < NP) {
+      float f[VEC];
+      unpack16<In>(raw[it], f);
+#pragma unroll
+      for (int q = 0; q < VEC / 4; ++q)
+        *reinterpret_cast<f32x4 *>(dst + r * ld + c + 4 * q) =
+            f32x4{f[4 * q], f[4 * q + 1], f[4 * q + 2], f[4 * q + 3]};
+    }
+  }
+}
+
+// an [R][W] fp32 block at src (row stride sld floats) into LDS (stride ld)
+template <int R, int W>
+__device__ __forceinline__ void load_block(float *dst, int ld, const float *src, size_t sld) {
+  constexpr int PR = W / 4, NP = R * PR, IT = (NP + 255) / 256;
+  f32x4 v[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int pc = threadIdx.x + 256 * it;
+    v[it] = pc < NP ? *reinterpret_cast<const f32x4 *>(src + (pc / PR) * sld + (pc % PR) * 4)
+                    : zero4();
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int pc = threadIdx.x + 256 * it;
+    if (pc < NP) *reinterpret_cast<f32x4 *>(dst + (pc / PR) * ld + (pc % PR) * 4) = v[it];
+  }
+}
+
+__device__ __forceinline__ void load_mat64(float *dst, const float *src) {
+  load_block<64, 64>(dst, kL, src, 64);
+}
+
+// ------------------------------------------------------------------ prep
+template <typename In, int DK>
+__global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
+  constexpr int LK = DK + 4;
+  __shared__ __attribute__((aligned(16))) float sK[kBT * LK], sQ[kBT * LK], sS[64 * kL], sX[64 * kL];
+  __shared__ __attribute__((aligned(16))) float sG[64], sB[64];
+  const int H = p.H;
+  const int slot = blockIdx.x / H, h = blockIdx.x % H;
+  Chunk ch;
+  if (!chunk_of(p, slot, ch)) return;
+  const int C = ch.C;
+  load_rows<In, DK>(sK, LK, p.k, ch.r0, C, H, h);
+  load_rows<In, DK>(sQ, LK, p.q, ch.r0, C, H, h);
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const float gr = tid < C ? p.g[(size_t)(ch.r0 + tid) * H + h] : 0.f;
+    sG[tid] = wave_inclusive_scan(gr);  // rows >= C repeat G_{C-1}
+    sB[tid] = tid < C ? p.beta[(size_t)(ch.r0 + tid) * H + h] : 0.f;
+  }
+  __syncthreads();
+  float *img = p.prep + (size_t)blockIdx.x * kPrepFloats;
+  const int w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
+  // S = strict_lower(K K^T * E), M = lower_incl(Q K^T * E): wave w, rows 16w
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    f32x4 as = mm(zero4(), sK + 16 * w * LK, LK, 1, sK + 16 * s4 * LK, 1, LK, DK);
+    f32x4 am = mm(zero4(), sQ + 16 * w * LK, LK, 1, sK + 16 * s4 * LK, 1, LK, DK);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * lg + i, s = 16 * s4 + lr;
+      const float e = (r < C && s <= r) ? __expf(sG[r] - sG[s]) : 0.f;
+      const float Sv = s < r ? as[i] * e : 0.f;
+      const float Mv = am[i] * e;
+      sS[r * kL + s] = Sv;
+      img[kPrepS + r * 64 + s] = Sv;
+      img[kPrepM + r * 64 + s] = Mv;
+    }
+  }
+  __syncthreads();
+  // A^-1 (unit lower) by forward substitution, one column per lane of wave 0:
+  // X_rc = -sum_{s=c}^{r-1} beta_r S_rs X_sc
+  if (tid < 64) {
+    const int c = tid;
+    for (int r = 0; r < 64; ++r) sX[r * kL + c] = (r == c && r < C) ? 1.f : 0.f;
+    for (int r = c + 1; r < C; ++r) {
+      float acc = 0.f;
+      for (int s = c; s < r; ++s) acc += sS[r * kL + s] * sX[s * kL + c];
+      sX[r * kL + c] = -sB[r] * acc;
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < 64 * 64; idx += 256) img[kPrepA + idx] = sX[(idx >> 6) * kL + (idx & 63)];
+  if (tid < 64) {
+    const float Gc = sG[C - 1];
+    img[kPrepG + tid] = sG[tid];
+    img[kPrepGam + tid] = tid < C ? __expf(sG[tid]) : 0.f;
+    img[kPrepFac + tid] = tid < C ? __expf(Gc - sG[tid]) : 0.f;
+    img[kPrepBeta + tid] = sB[tid];
+  }
+}
+
+// -------------------------------------------------------------------- dh
+// per (sequence, head, 32 columns), chunks in reverse; the state gradient
+// slice [d_k][32] lives in LDS
+template <typename In, int DK>
+__global__ __launch_bounds__(256) void bwd_dh_kernel(BwdParams p) {
+  constexpr int LK = DK + 4, LC = 36, DV = DK;
+  constexpr int SV = DV / 32;
+  __shared__ __attribute__((aligned(16))) float sK[kBT * LK], sQ[kBT * LK], sA[64 * kL], sM[64 * kL];
+  __shared__ __attribute__((aligned(16))) float sO[64 * LC], sGO[64 * LC], sU[64 * LC], sY[64 * LC], sD[DK * LC];
+  __shared__ __attribute__((aligned(16))) float sGam[64], sFac[64], sBeta[64];
+  const int H = p.H;
+  const int sv = blockIdx.x % SV, unit = blockIdx.x / SV;
+  const int n = unit / H, h = unit % H;
+  if (n >= p.N_max) return;
+  const int j0 = p.chunk_offsets[n], j1 = p.chunk_offsets[n + 1];
+  if (j0 == j1) return;
+  const int bos = cu_at(p.cu_seqlens, p.cu64, n), eos = cu_at(p.cu_seqlens, p.cu64, n + 1);
+  const int c0 = sv * 32;
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
+  const size_t mat = (size_t)DK * DV;
+  const size_t sb = ((size_t)n * H + h) * mat;
+  if (p.dht) {
+    load_block<DK, 32>(sD, LC, p.dht + sb + c0, DV);
+  } else {
+    for (int idx = tid; idx < DK * 32; idx += 256) sD[(idx / 32) * LC + idx % 32] = 0.f;
+  }
+  for (int jj = j1 - 1; jj >= j0; --jj) {
+    __syncthreads();
+    const int r0 = bos + (jj - j0) * kBT, C = min(kBT, eos - r0);
+    load_rows<In, DK>(sK, LK, p.k, r0, C, H, h);
+    load_rows<In, DK>(sQ, LK, p.q, r0, C, H, h);
+    const float *img = p.prep + ((size_t)jj * H + h) * kPrepFloats;
+    load_mat64(sA, img + kPrepA);
+    load_mat64(sM, img + kPrepM);
+    if (tid < 64) {
+      sGam[tid] = img[kPrepGam + tid];
+      sFac[tid] = img[kPrepFac + tid];
+      sBeta[tid] = img[kPrepBeta + tid];
+    }
+    load_rows<float, DV, 32>(sO, LC, p.dout, r0, C, H, h, c0);
+    // the gradient leaving this chunk, for the part kernel
+    float *dst = p.dhs + ((size_t)jj * H + h) * mat + c0;
+#pragma unroll
+    for (int it = 0; it < DK * 8 / 256; ++it) {
+      const int pc = tid + 256 * it, i = pc / 8, c = (pc % 8) * 4;
+      *reinterpret_cast<f32x4 *>(dst + (size_t)i * DV + c) =
+          *reinterpret_cast<const f32x4 *>(sD + i * LC + c);
+    }
+    __syncthreads();
+    for (int idx = tid; idx < 64 * 32; idx += 256) {
+      const int r = idx / 32, c = idx % 32;
+      const float v = p.scale * sO[r * LC + c];
+      sO[r * LC + c] = v;
+      sGO[r * LC + c] = sGam[r] * v;
+    }
+    __syncthreads();
+    // dU = M^T dOb + fac * (K dH'), rows 16w
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x4 kd = mm(zero4(), sK + 16 * w * LK, LK, 1, sD + 16 * nt, LC, 1, DK);
+      f32x4 du = mm(zero4(), sM + 16 * w, 1, kL, sO + 16 * nt, LC, 1, 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * lg + i;
+        sU[r * LC + 16 * nt + lr] = du[i] + sFac[r] * kd[i];
+      }
+    }
+    __syncthreads();
+    // dX = beta * (A^-T dU); Y = gam * dX
+#pragma unroll
+    for (int nt = 0; nt < 2; ++nt) {
+      f32x4 dx = mm(zero4(), sA + 16 * w, 1, kL, sU + 16 * nt, LC, 1, 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * lg + i;
+        sY[r * LC + 16 * nt + lr] = sGam[r] * sBeta[r] * dx[i];
+      }
+    }
+    __syncthreads();
+    // dH = gam_C dH' + Q^T (gam dOb) - K^T Y
+    const float gamC = sGam[C - 1];
+    for (int t = w; t < DK / 16; t += 4) {
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt) {
+        f32x4 acc;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] = gamC * sD[(16 * t + 4 * lg + i) * LC + 16 * nt + lr];
+        acc = mm(acc, sQ + 16 * t, 1, LK, sGO + 16 * nt, LC, 1, 64);
+        f32x4 ky = mm(zero4(), sK + 16 * t, 1, LK, sY + 16 * nt, LC, 1, 64);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sD[(16 * t + 4 * lg + i) * LC + 16 * nt + lr] = acc[i] - ky[i];
+      }
+    }
+  }
+  __syncthreads();
+  if (p.dh0)
+    for (int idx = tid; idx < DK * 32; idx += 256) {
+      const int i = idx / 32, c = idx % 32;
+      p.dh0[sb + (size_t)i * DV + c0 + c] = sD[i * LC + c];
+    }
+}
+
+// ------------------------------------------------------------------ part
+// per (slot, head): dV and the d_v-contracted products, over 16-column blocks
+template <typename In, int DK>
+__global__ __launch_bounds__(256) void bwd_part_kernel(BwdParams p) {
+  constexpr int LK = DK + 4, LB = 20, DV = DK, NT = DK / 16;
+  __shared__ __attribute__((aligned(16))) float sK[kBT * LK], sA[64 * kL], sM[64 * kL];
+  __shared__ __attribute__((aligned(16))) float sH[DK * LB], sDH[DK * LB];
+  __shared__ __attribute__((aligned(16))) float sV[64 * LB], sO[64 * LB], sX[64 * LB], sBX[64 * LB], sU[64 * LB],
+      sDU[64 * LB], sDX[64 * LB];
+  __shared__ __attribute__((aligned(16))) float sGam[64], sFac[64], sBeta[64], sRed[256];
+  const int H = p.H;
+  const int slot = blockIdx.x / H, h = blockIdx.x % H;
+  Chunk ch;
+  if (!chunk_of(p, slot, ch)) return;
+  const int C = ch.C, r0 = ch.r0;
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
+  load_rows<In, DK>(sK, LK, p.k, r0, C, H, h);
+  const float *img = p.prep + (size_t)blockIdx.x * kPrepFloats;
+  load_mat64(sA, img + kPrepA);
+  load_mat64(sM, img + kPrepM);
+  if (tid < 64) {
+    sGam[tid] = img[kPrepGam + tid];
+    sFac[tid] = img[kPrepFac + tid];
+    sBeta[tid] = img[kPrepBeta + tid];
+  }
+  const size_t mat = (size_t)DK * DV;
+  const float *Hs = p.hs + (size_t)blockIdx.x * mat;
+  const float *Ds = p.dhs + (size_t)blockIdx.x * mat;
+  f32x4 P1[NT], P2[NT], P3[NT], dM[4], dT[4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) P1[t] = P2[t] = P3[t] = zero4();
+#pragma unroll
+  for (int t = 0; t < 4; ++t) dM[t] = dT[t] = zero4();
+  float shd = 0.f;
+  for (int cb = 0; cb < DV / 16; ++cb) {
+    __syncthreads();
+    load_block<DK, 16>(sH, LB, Hs + 16 * cb, DV);
+    load_block<DK, 16>(sDH, LB, Ds + 16 * cb, DV);
+    load_rows<In, DV, 16>(sV, LB, p.v, r0, C, H, h, 16 * cb);
+    load_rows<float, DV, 16>(sO, LB, p.dout, r0, C, H, h, 16 * cb);
+    __syncthreads();
+    for (int idx = tid; idx < DK * 16; idx += 256) {
+      const int i = idx / 16, c = idx % 16;
+      shd += sH[i * LB + c] * sDH[i * LB + c];
+    }
+    for (int idx = tid; idx < 64 * 16; idx += 256) sO[(idx / 16) * LB + idx % 16] *= p.scale;
+    __syncthreads();
+    {
+      const f32x4 kh = mm(zero4(), sK + 16 * w * LK, LK, 1, sH, LB, 1, DK);
+      const f32x4 kd = mm(zero4(), sK + 16 * w * LK, LK, 1, sDH, LB, 1, DK);
+      const f32x4 mo = mm(zero4(), sM + 16 * w, 1, kL, sO, LB, 1, 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * lg + i;
+        const float x = sV[r * LB + lr] - sGam[r] * kh[i];
+        sX[r * LB + lr] = x;
+        sBX[r * LB + lr] = sBeta[r] * x;
+        sDU[r * LB + lr] = mo[i] + sFac[r] * kd[i];
+      }
+    }
+    __syncthreads();
+    {
+      const f32x4 u = mm(zero4(), sA + 16 * w * kL, kL, 1, sBX, LB, 1, 64);
+      const f32x4 dx = mm(zero4(), sA + 16 * w, 1, kL, sDU, LB, 1, 64);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * lg + i;
+        sU[r * LB + lr] = u[i];
+        const float d = sBeta[r] * dx[i];
+        sDX[r * LB + lr] = d;
+        if (r < C) p.dv[((size_t)(r0 + r) * H + h) * DV + 16 * cb + lr] = d;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+      P1[t] = mm(P1[t], sO + 16 * w * LB, LB, 1, sH + 16 * t * LB, 1, LB, 16);
+      P2[t] = mm(P2[t], sDX + 16 * w * LB, LB, 1, sH + 16 * t * LB, 1, LB, 16);
+      P3[t] = mm(P3[t], sU + 16 * w * LB, LB, 1, sDH + 16 * t * LB, 1, LB, 16);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      dM[t] = mm(dM[t], sO + 16 * w * LB, LB, 1, sU + 16 * t * LB, 1, LB, 16);
+      dT[t] = mm(dT[t], sDU + 16 * w * LB, LB, 1, sX + 16 * t * LB, 1, LB, 16);
+    }
+  }
+  float *gw = p.part + (size_t)blockIdx.x * part_floats(DK);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * lg + i, c = 16 * t + lr;
+      gw[kPartP1 + r * DK + c] = P1[t][i];
+      gw[part_p2(DK) + r * DK + c] = P2[t][i];
+      gw[part_p3(DK) + r * DK + c] = P3[t][i];
+    }
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * lg + i, c = 16 * t + lr;
+      gw[part_dm(DK) + r * 64 + c] = dM[t][i];
+      gw[part_dt(DK) + r * 64 + c] = dT[t][i];
+    }
+  sRed[tid] = shd;
+  __syncthreads();
+  if (tid == 0) {
+    float s = 0.f;
+    for (int i = 0; i < 256; ++i) s += sRed[i];
+    gw[part_sh(DK)] = s;
+  }
+}
+
+// ----------------------------------------------------------------- final
+template <typename In, int DK>
+__global__ __launch_bounds__(256) void bwd_final_kernel(BwdParams p) {
+  constexpr int LK = DK + 4, NT = DK / 16;
+  // phase A: A^-1, M, S, dM, dT and a product scratch; phase B: K, Q over the
+  // first four of them, dM*E and F kept
+  constexpr int MAT = 64 * kL;
+  constexpr int KQ = 2 * kBT * LK;
+  static_assert(KQ <= 4 * MAT, "K and Q fit over the phase-A matrices");
+  __shared__ __attribute__((aligned(16))) float smem[6 * MAT];
+  __shared__ __attribute__((aligned(16))) float sG[64], sGam[64], sFac[64], sBeta[64];
+  __shared__ __attribute__((aligned(16))) float zr[64], zc[64], yr[64], yc[64], bt[64], ba[64], dG[64], t3s[64];
+  float *sA = smem, *sM = smem + MAT, *sS = smem + 2 * MAT, *sTmp = smem + 3 * MAT;
+  float *sDM = smem + 4 * MAT, *sDT = smem + 5 * MAT;
+  const int H = p.H;
+  const int slot = blockIdx.x / H, h = blockIdx.x % H;
+  Chunk ch;
+  if (!chunk_of(p, slot, ch)) return;
+  const int C = ch.C, r0 = ch.r0;
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
+  const float *img = p.prep + (size_t)blockIdx.x * kPrepFloats;
+  const float *gw = p.part + (size_t)blockIdx.x * part_floats(DK);
+  load_mat64(sA, img + kPrepA);
+  load_mat64(sM, img + kPrepM);
+  load_mat64(sS, img + kPrepS);
+  load_mat64(sDM, gw + part_dm(DK));
+  load_mat64(sDT, gw + part_dt(DK));
+  if (tid < 64) {
+    sG[tid] = img[kPrepG + tid];
+    sGam[tid] = img[kPrepGam + tid];
+    sFac[tid] = img[kPrepFac + tid];
+    sBeta[tid] = img[kPrepBeta + tid];
+  }
+  __syncthreads();
+  // Z = dM * M (gates), dT * A^-1 (beta), then dM <- dM * E, dT <- dA^-1
+  for (int idx = tid; idx < 4096; idx += 256) {
+    const int r = idx >> 6, s = idx & 63, o = r * kL + s;
+    const bool lo = s <= r && r < C;
+    const float dm = sDM[o], dt = sDT[o];
+    sTmp[o] = lo ? dt * sA[o] : 0.f;
+    sM[o] = lo ? dm * sM[o] : 0.f;
+    sDM[o] = lo ? dm * __expf(sG[r] - sG[s]) : 0.f;
+    sDT[o] = lo ? dt * sBeta[s] : 0.f;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float a = 0.f, b = 0.f, c = 0.f;
+    for (int s = 0; s < 64; ++s) a += sM[tid * kL + s];
+    for (int r = 0; r < 64; ++r) {
+      b += sM[r * kL + tid];
+      c += sTmp[r * kL + tid];
+    }
+    zr[tid] = a;
+    zc[tid] = b;
+    bt[tid] = c;
+  }
+  __syncthreads();
+  // tmp = dA^-1 A^-T
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    const f32x4 t = mm(zero4(), sDT + 16 * w * kL, kL, 1, sA + 16 * s4 * kL, 1, kL, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sTmp[(16 * w + 4 * lg + i) * kL + 16 * s4 + lr] = t[i];
+  }
+  __syncthreads();
+  // dA = -A^-T tmp; strict lower part: W = dA S (beta), Y = beta dA S (gates),
+  // F = beta dA E (keys)
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+    const f32x4 t = mm(zero4(), sA + 16 * w, 1, kL, sTmp + 16 * s4, kL, 1, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * lg + i, s = 16 * s4 + lr, o = r * kL + s;
+      const bool sl = s < r && r < C;
+      const float dA = -t[i];
+      const float Sv = sS[o];
+      sM[o] = sl ? dA * Sv : 0.f;
+      sS[o] = sl ? sBeta[r] * dA * Sv : 0.f;
+      sDT[o] = sl ? sBeta[r] * dA * __expf(sG[r] - sG[s]) : 0.f;
+    }
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float a = 0.f, b = 0.f, c = 0.f;
+    for (int s = 0; s < 64; ++s) {
+      a += sM[tid * kL + s];
+      b += sS[tid * kL + s];
+    }
+    for (int r = 0; r < 64; ++r) c += sS[r * kL + tid];
+    ba[tid] = a;
+    yr[tid] = b;
+    yc[tid] = c;
+  }
+  __syncthreads();
+  // phase B: K and Q over the first four matrices
+  float *sK = smem, *sQ = smem + kBT * LK;
+  load_rows<In, DK>(sK, LK, p.k, r0, C, H, h);
+  load_rows<In, DK>(sQ, LK, p.q, r0, C, H, h);
+  __syncthreads();
+  const float *P1 = gw + kPartP1, *P2 = gw + part_p2(DK), *P3 = gw + part_p3(DK);
+  // gates: per row, with the dot products of q / k with P1, P2, P3
+  if (tid < 64) {
+    const int r = tid;
+    float q1 = 0.f, k2 = 0.f, k3 = 0.f;
+    for (int i = 0; i < DK; ++i) {
+      q1 += sQ[r * LK + i] * P1[r * DK + i];
+      k2 += sK[r * LK + i] * P2[r * DK + i];
+      k3 += sK[r * LK + i] * P3[r * DK + i];
+    }
+    const float t3 = sFac[r] * k3;
+    dG[r] = r < C ? sGam[r] * (q1 - k2) - t3 + zr[r] - zc[r] + yr[r] - yc[r] : 0.f;
+    t3s[r] = r < C ? t3 : 0.f;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    float dGc = 0.f;
+    for (int r = 0; r < C; ++r) dGc += t3s[r];
+    dGc += sGam[C - 1] * gw[part_sh(DK)];
+    dG[C - 1] += dGc;
+    // dg_t = sum_{r >= t} dG_r
+    float acc = 0.f;
+    for (int r = C - 1; r >= 0; --r) {
+      acc += dG[r];
+      dG[r] = acc;
+    }
+  }
+  __syncthreads();
+  if (tid < C) {
+    const size_t o = (size_t)(r0 + tid) * H + h;
+    p.dg[o] = dG[tid];
+    p.dbeta[o] = bt[tid] + ba[tid];
+  }
+  // dQ = gam P1 + (dM E) K;  dK = -gam P2 + fac P3 + (dM E)^T Q + F K + F^T K
+  for (int t = 0; t < NT; ++t) {
+    f32x4 dq = mm(zero4(), sDM + 16 * w * kL, kL, 1, sK + 16 * t, LK, 1, 64);
+    f32x4 dk = mm(zero4(), sDM + 16 * w, 1, kL, sQ + 16 * t, LK, 1, 64);
+    dk = mm(dk, sDT + 16 * w * kL, kL, 1, sK + 16 * t, LK, 1, 64);
+    dk = mm(dk, sDT + 16 * w, 1, kL, sK + 16 * t, LK, 1, 64);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * lg + i, c = 16 * t + lr;
+      if (r < C) {
+        const size_t o = ((size_t)(r0 + r) * H + h) * DK + c;
+        p.dq[o] = sGam[r] * P1[r * DK + c] + dq[i];
+        p.dk[o] = -sGam[r] * P2[r * DK + c] + sFac[r] * P3[r * DK + c] + dk[i];
+      }
+    }
+  }
+}
+
+template <typename In, int DK>
+hipError_t launch_all(const BwdParams &p, hipStream_t st) {
+  const int cells = p.NT * p.H;
+  hipLaunchKernelGGL((bwd_prep_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL((bwd_dh_kernel<In, DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL((bwd_part_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  hipLaunchKernelGGL((bwd_final_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
+  return hipGetLastError();
+}
+
+template <typename In>
+hipError_t launch_dk(const BwdParams &p, int dk, hipStream_t st) {
+  if (dk == 128) return launch_all<In, 128>(p, st);
+  if (dk == 64) return launch_all<In, 64>(p, st);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_chunk_bwd(const BwdParams &p, int dt, int dk, hipStream_t st) {
+  if (dt == LA_BF16) return launch_dk<bf16>(p, dk, st);
+  if (dt == LA_F16) return launch_dk<f16>(p, dk, st);
+  if (dt == LA_F32) return dk == 64 ? launch_all<float, 64>(p, st) : hipErrorInvalidValue;
+  return hipErrorInvalidValue;
+}
+
+}  // namespace la

@@ -249,6 +249,13 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
     const int r0 = wk.t0 + (jj - j0) * kBT;
     const int C = min(kBT, eos - r0);
     chunk_barrier();
+    if (p.hsave) {  // the state entering chunk jj (backward recompute)
+      float *hs = p.hsave + ((size_t)jj * H + h) * DK * DV;
+#pragma unroll
+      for (int t = 0; t < NHT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hs[(size_t)(16 * t + lg * 4 + e) * DV + cw + lr] = hacc[t][e];
+    }
     const char *buf = smem + BUF * STAGE;
     const char *tV = buf;
     const char *tK = buf + IMG + I.K;
@@ -609,7 +616,7 @@ __device__ __forceinline__ int decode_work(const ReduceParams &p, Work &wk) {
     const size_t sb = ((size_t)n * H + wk.h) * mat;
     if (p.h0) wk.init = p.h0 + sb;
     if (p.ht) wk.fin = p.ht + sb;
-    return 1;
+    return p.o ? 1 : 2;  // without o: states only
   }
   if (unit >= p.NS_max * H) return 0;
   const int sig = unit / H;

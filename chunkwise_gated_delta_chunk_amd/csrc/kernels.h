@@ -41,6 +41,10 @@ struct ReduceParams {
   int seg, pass, SP, NS_max;
   float *hin, *dlt;
   _Float16 *pimg;
+  // one-pass reduce only: when set, the state at the start of every chunk is
+  // stored to hsave[slot][h] ([d_k][d_v] fp32, the backward's recompute);
+  // o may then be NULL (no output)
+  float *hsave;
 };
 
 // Segment combine: H_{s+1} = P_s H_s + D_s along each sequence's segments.
@@ -75,6 +79,33 @@ struct ConvParams {
   void *y, *ht;
 };
 
+// Chunk backward (chunk_bwd.hip).  prep: per (slot, head) cell, kPrepFloats
+// fp32: A^-1, M, S ([64][64] each), then G, exp(G), exp(G_C - G), beta (64
+// each).  part: per cell, part_floats(d) fp32: dOb H^T, dX H^T, U dH'^T
+// ([64][d] each), dM, dT ([64][64] each), <dH', H>.  hs / dhs: per cell the
+// state entering / the state gradient leaving the chunk, [d][d] fp32.
+constexpr int kPrepA = 0, kPrepM = 4096, kPrepS = 8192, kPrepG = 12288, kPrepGam = 12352,
+              kPrepFac = 12416, kPrepBeta = 12480, kPrepFloats = 12544;
+constexpr int kPartP1 = 0;
+__host__ __device__ constexpr int part_p2(int d) { return 64 * d; }
+__host__ __device__ constexpr int part_p3(int d) { return 128 * d; }
+__host__ __device__ constexpr int part_dm(int d) { return 192 * d; }
+__host__ __device__ constexpr int part_dt(int d) { return 192 * d + 4096; }
+__host__ __device__ constexpr int part_sh(int d) { return 192 * d + 8192; }
+__host__ __device__ constexpr int part_floats(int d) { return 192 * d + 8192 + 64; }
+
+struct BwdParams {
+  const void *q, *k, *v;
+  const float *g, *beta;
+  const void *cu_seqlens;  // int32, or int64 with cu64
+  const int32_t *chunk_indices, *chunk_offsets;
+  const float *dout, *dht;
+  float *dq, *dk, *dv, *dg, *dbeta, *dh0;
+  float *prep, *part, *hs, *dhs;
+  int cu64, H, N_max, NT;
+  float scale;
+};
+
 // cu: int32 cu_seqlens, or int64 with cu64
 hipError_t launch_chunk_meta(const void *cu, int cu64, int N_max, int T_max, int BT, int NT_max,
                              int32_t *ci, int32_t *co, int32_t *status, hipStream_t stream);
@@ -85,6 +116,7 @@ hipError_t launch_chunk_reduce(const ReduceParams &p, bool kda, int dt, int dk, 
                                hipStream_t st);
 hipError_t launch_chunk_combine(const CombineParams &p, int dk, hipStream_t st);
 hipError_t launch_recurrent(const RecurrentParams &p, bool kda, int dt, int dk, hipStream_t st);
+hipError_t launch_chunk_bwd(const BwdParams &p, int dt, int dk, hipStream_t st);
 // NT chunk slots, W in 1..4
 hipError_t launch_short_conv(const ConvParams &p, int dt, int NT, int W, bool silu,
                              hipStream_t st);

@@ -51,6 +51,21 @@ __device__ __forceinline__ int cu_at(const void *cu, int cu64, int i) {
               : static_cast<const int32_t *>(cu)[i];
 }
 
+// One 16-byte piece of input elements (8 bf16 / fp16 or 4 fp32) -> fp32.
+template <typename In>
+__device__ __forceinline__ void unpack16(const uint32_t (&r)[4], float *v) {
+  if constexpr (sizeof(In) == 4) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) v[e] = __uint_as_float(r[e]);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = in16_to_f32<In>(r[e] & 0xffffu);
+      v[2 * e + 1] = in16_to_f32<In>(r[e] >> 16);
+    }
+  }
+}
+
 // Operand traits: bf16 and fp16 inputs run on fp16 MFMA (bf16 values are
 // exact in fp16 inside its normal range), fp32 inputs on fp32 MFMA.
 template <typename In> struct Op;

@@ -354,6 +354,141 @@ int la_short_conv_fwd(const la_short_conv_args *a, void *stream) {
   return LA_OK;
 }
 
+static la_chunk_fwd_args fwd_view(const la_chunk_bwd_args *a) {
+  la_chunk_fwd_args f{};
+  f.T_max = a->T_max;
+  f.N_max = a->N_max;
+  f.H = a->H;
+  f.d_k = a->d_k;
+  f.d_v = a->d_v;
+  f.BT = a->BT;
+  f.qkv_dtype = a->qkv_dtype;
+  f.seg_len = -1;  // the recompute stores per-chunk states: one pass
+  f.cu_seqlens_i64 = a->cu_seqlens_i64;
+  f.scale = a->scale;
+  return f;
+}
+
+// backward workspace: [forward images][hs][dhs][prep][part], each 256-aligned
+struct BwdLayout { size_t img, hs, dhs, prep, part, total; };
+static BwdLayout bwd_layout(const la_chunk_bwd_args *a) {
+  const la_chunk_fwd_args f = fwd_view(a);
+  const size_t cells = (size_t)la_nt_max(a->T_max, a->N_max, a->BT) * a->H;
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  BwdLayout L{};
+  L.img = 0;
+  L.hs = up(ws_img_bytes(&f, false));
+  L.dhs = L.hs + up(cells * a->d_k * a->d_v * sizeof(float));
+  L.prep = L.dhs + up(cells * a->d_k * a->d_v * sizeof(float));
+  L.part = L.prep + up(cells * la::kPrepFloats * sizeof(float));
+  L.total = L.part + up(cells * la::part_floats(a->d_k) * sizeof(float));
+  return L;
+}
+
+static int check_bwd(const la_chunk_bwd_args *a) {
+  const la_chunk_fwd_args f = fwd_view(a);
+  const int sc = check_shape(&f);
+  if (sc != LA_OK) return sc;
+  return LA_OK;
+}
+
+size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *a) {
+  if (!a || check_bwd(a) != LA_OK) return 0;
+  return bwd_layout(a).total;
+}
+
+int gdn_chunk_bwd(const la_chunk_bwd_args *a, void *stream) {
+  if (!a) return LA_ERR_NULL;
+  const int sc = check_bwd(a);
+  if (sc != LA_OK) return sc;
+  if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->cu_seqlens || !a->chunk_indices ||
+      !a->chunk_offsets || !a->dout || !a->dq || !a->dk || !a->dv || !a->dg || !a->dbeta)
+    return LA_ERR_NULL;
+  if (!a->workspace) return LA_ERR_WORKSPACE;
+  const BwdLayout L = bwd_layout(a);
+  if (a->workspace_bytes < L.total) return LA_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(a->workspace) % 256 != 0) return LA_ERR_WORKSPACE;
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->k) |
+                        reinterpret_cast<uintptr_t>(a->v);
+  if (mis % 16 != 0) return LA_ERR_SHAPE;
+  char *ws = static_cast<char *>(a->workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // forward recompute: map images, then the reduce storing every chunk's
+  // entering state (no output, no final state)
+  la_chunk_fwd_args f = fwd_view(a);
+  f.q = a->q;
+  f.k = a->k;
+  f.v = a->v;
+  f.g = a->g;
+  f.beta = a->beta;
+  f.cu_seqlens = a->cu_seqlens;
+  f.chunk_indices = a->chunk_indices;
+  f.chunk_offsets = a->chunk_offsets;
+  f.h0 = a->h0;
+  f.workspace = ws;
+  f.workspace_bytes = L.hs;
+  const int NT = (int)la_nt_max(a->T_max, a->N_max, a->BT);
+  {
+    la::MapParams mp{};
+    mp.q = a->q;
+    mp.k = a->k;
+    mp.g = a->g;
+    mp.beta = a->beta;
+    mp.cu_seqlens = a->cu_seqlens;
+    mp.cu64 = a->cu_seqlens_i64;
+    mp.chunk_indices = a->chunk_indices;
+    mp.H = a->H;
+    mp.Hqk = a->H;
+    mp.NT_max = NT;
+    mp.img = ws;
+    if (la::launch_chunk_map(mp, false, a->qkv_dtype, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
+    la::ReduceParams rp{};
+    rp.v = a->v;
+    rp.cu_seqlens = a->cu_seqlens;
+    rp.cu64 = a->cu_seqlens_i64;
+    rp.chunk_offsets = a->chunk_offsets;
+    rp.h0 = a->h0;
+    rp.o = nullptr;
+    rp.ht = nullptr;
+    rp.img = ws;
+    rp.H = a->H;
+    rp.N_max = a->N_max;
+    rp.S = split_for(&f);
+    rp.scale = a->scale;
+    rp.hsave = reinterpret_cast<float *>(ws + L.hs);
+    if (la::launch_chunk_reduce(rp, false, a->qkv_dtype, a->d_k, a->d_v / rp.S, st) != hipSuccess)
+      return LA_ERR_HIP;
+  }
+  la::BwdParams bp{};
+  bp.q = a->q;
+  bp.k = a->k;
+  bp.v = a->v;
+  bp.g = a->g;
+  bp.beta = a->beta;
+  bp.cu_seqlens = a->cu_seqlens;
+  bp.cu64 = a->cu_seqlens_i64;
+  bp.chunk_indices = a->chunk_indices;
+  bp.chunk_offsets = a->chunk_offsets;
+  bp.dout = a->dout;
+  bp.dht = a->dht;
+  bp.dq = a->dq;
+  bp.dk = a->dk;
+  bp.dv = a->dv;
+  bp.dg = a->dg;
+  bp.dbeta = a->dbeta;
+  bp.dh0 = a->dh0;
+  bp.hs = reinterpret_cast<float *>(ws + L.hs);
+  bp.dhs = reinterpret_cast<float *>(ws + L.dhs);
+  bp.prep = reinterpret_cast<float *>(ws + L.prep);
+  bp.part = reinterpret_cast<float *>(ws + L.part);
+  bp.H = a->H;
+  bp.N_max = a->N_max;
+  bp.NT = NT;
+  bp.scale = a->scale;
+  if (la::launch_chunk_bwd(bp, a->qkv_dtype, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
+  return LA_OK;
+}
+
 const char *la_status_string(int status) {
   switch (status) {
     case LA_OK: return "ok";

@@ -242,6 +242,55 @@ typedef struct {
 int gdn_recurrent_fwd(const la_recurrent_args *a, void *stream);
 int kda_recurrent_fwd(const la_recurrent_args *a, void *stream);
 
+/* Arguments of the GDN chunk backward: the forward's inputs and metadata,
+ * the output gradient, and the gradient outputs. */
+typedef struct {
+    int32_t T_max, N_max, H;   /* as la_chunk_fwd_args                           */
+    int32_t d_k, d_v;          /* d_k == d_v: 64 or 128 (16-bit), 64 (fp32)      */
+    int32_t BT;                /* 64                                             */
+    int32_t qkv_dtype;         /* LA_BF16, LA_F16 or LA_F32                      */
+    int32_t cu_seqlens_i64;    /* 0: cu_seqlens int32; 1: int64                  */
+    float scale;               /* the forward's scale                            */
+    const void *q, *k, *v;     /* [T_max][H][d_k] / [T_max][H][d_v], qkv_dtype  */
+    const float *g;            /* log-decay [T_max][H]                           */
+    const float *beta;         /* [T_max][H]                                     */
+    const void *cu_seqlens;    /* [N_max+1]                                      */
+    const int32_t *chunk_indices, *chunk_offsets; /* from build_chunk_meta      */
+    const float *h0;           /* [N_max][H][d_k][d_v] or NULL (zero state)      */
+    const float *dout;         /* gradient of o: [T_max][H][d_v] fp32            */
+    const float *dht;          /* gradient of ht: [N_max][H][d_k][d_v] or NULL   */
+    float *dq, *dk;            /* [T_max][H][d_k] fp32                           */
+    float *dv;                 /* [T_max][H][d_v] fp32                           */
+    float *dg, *dbeta;         /* [T_max][H] fp32                                */
+    float *dh0;                /* [N_max][H][d_k][d_v] fp32 or NULL              */
+    void *workspace;           /* >= la_chunk_bwd_workspace_bytes(...) bytes,    */
+    size_t workspace_bytes;    /* 256-byte aligned                               */
+} la_chunk_bwd_args;
+
+/* Workspace of gdn_chunk_bwd for this shape (T_max, N_max, H, d_k, d_v, BT,
+ * qkv_dtype read); 0 if the shape is invalid.  It holds the forward
+ * recompute's map images, the state entering and the state gradient leaving
+ * every chunk ([d_k][d_v] fp32 per chunk slot and head), per-cell fp32
+ * matrices A^-1, M, S and per-cell partial products. */
+size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *shape);
+
+/*
+ * GDN chunk backward: the gradients of L = sum(o * dout) + sum(ht * dht) of
+ * gdn_chunk_fwd with the same inputs, for q, k, v, g, beta and h0 (FLA RFC,
+ * sections "Scope" and "Step 3": the backward of the chunk path).  It
+ * recomputes the forward's per-chunk states (map, then the reduce storing the
+ * state entering each chunk), then runs four launches: a chunk-parallel prep
+ * (A^-1, M, S, gates), a reverse pass over each sequence's chunks for the
+ * state gradient (writing dh0), a chunk-parallel pass for dv and the
+ * d_v-contracted products, and a chunk-parallel pass for dq, dk, dg, dbeta.
+ * Arithmetic after the recompute is fp32.  Rows outside every sequence,
+ * sentinel slots and dh0 of zero-length sequences are not written.  Grouped
+ * value heads are not supported here (q, k carry H heads).
+ * Host errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_UNSUPPORTED,
+ * LA_ERR_WORKSPACE, LA_ERR_HIP.
+ */
+int gdn_chunk_bwd(const la_chunk_bwd_args *a, void *stream);
+
 /* Activation of the short convolution. */
 #define LA_ACT_NONE 0
 #define LA_ACT_SILU 1

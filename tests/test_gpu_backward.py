@@ -1,0 +1,127 @@
+"""GPU parity of the GDN chunk backward against the fp64 oracle
+(oracle/backward.py: reverse-mode gradients of the token recurrence).
+
+Bar, per gradient (dq, dk, dv, dg, dbeta over the rows of real tokens; dh0
+over non-empty sequences): max |x - ref| / max |ref| <= 2e-3 for 16-bit
+inputs and 1e-4 for fp32 inputs.  Rows outside every sequence are never
+written.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import chunkwise_gated_delta_chunk_amd as la
+from oracle.backward import gated_delta_bwd
+from synth import make_inputs
+from tests.helpers import TOL, TORCH_DT, rel_err
+
+pytestmark = pytest.mark.gpu
+
+SMALL_CU = [0, 1, 64, 64, 200, 333, 460]   # one token, exact chunk, empty, tails
+
+
+def _say(*a):
+    print(*a, flush=True)
+
+
+def run_bwd(inp, do, dht, scale, *, with_h0=True, idx=torch.int32, fill=None):
+    tdt = TORCH_DT[inp["dtype"]]
+    d = {x: torch.from_numpy(inp[x]).cuda().to(tdt).contiguous() for x in ("q", "k", "v")}
+    g = torch.from_numpy(inp["g"]).cuda().contiguous()
+    b = torch.from_numpy(inp["beta"]).cuda().contiguous()
+    cu = torch.from_numpy(np.asarray(inp["cu_seqlens"], dtype=np.int64)).cuda().to(idx)
+    T = inp["q"].shape[0]
+    ci, co, _ = la.build_chunk_meta(cu, T)
+    h0 = torch.from_numpy(inp["h0"]).cuda() if (with_h0 and inp["h0"] is not None) else None
+    dout = torch.from_numpy(np.asarray(do, dtype=np.float32)).cuda()
+    dh = None if dht is None else torch.from_numpy(np.asarray(dht, dtype=np.float32)).cuda()
+    outs = {}
+    if fill is not None:
+        H, dk, dv = inp["H"], inp["dk"], inp["dv"]
+        outs = dict(dq=torch.full((T, H, dk), fill, device="cuda"),
+                    dk=torch.full((T, H, dk), fill, device="cuda"),
+                    dv=torch.full((T, H, dv), fill, device="cuda"),
+                    dg=torch.full((T, H), fill, device="cuda"),
+                    dbeta=torch.full((T, H), fill, device="cuda"))
+    res = la.gdn_chunk_bwd(d["q"], d["k"], d["v"], g, b, cu, ci, co, dout, h0=h0, dht=dh,
+                           scale=scale, **outs)
+    torch.cuda.synchronize()
+    return dict(zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), res))
+
+
+def compare(inp, got, ref):
+    cu = np.asarray(inp["cu_seqlens"])
+    rows = slice(0, int(cu[-1]))
+    ne = np.diff(cu) > 0
+    errs = {}
+    for key in ("dq", "dk", "dv", "dg", "dbeta"):
+        errs[key] = rel_err(got[key].cpu().numpy()[rows], ref[key][rows])
+    if got["dh0"] is not None:
+        errs["dh0"] = rel_err(got["dh0"].cpu().numpy()[ne], ref["dh0"][ne])
+    return errs
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f16", 128), ("f32", 64)])
+def test_backward_matches_oracle(dtype, d):
+    inp = make_inputs(SMALL_CU[-1], 3, d, d, kda=False, dtype=dtype, seed=700 + d,
+                      cu_seqlens=SMALL_CU, h0_std=0.1)
+    rng = np.random.default_rng(701)
+    do = rng.standard_normal(inp["v"].shape).astype(np.float32)
+    dht = rng.standard_normal(inp["h0"].shape).astype(np.float32)
+    ref = gated_delta_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], SMALL_CU,
+                          inp["h0"], do, dht, 0.75)
+    got = run_bwd(inp, do, dht, 0.75)
+    errs = compare(inp, got, ref)
+    _say(f"bwd {dtype} d={d}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    tol = TOL[dtype]
+    assert all(v <= tol for v in errs.values()), errs
+
+
+def test_backward_no_state_no_dht_and_padding_untouched():
+    T_max = 300
+    cu = [0, 70, 70, 250]
+    inp = make_inputs(T_max, 2, 64, 64, kda=False, dtype="bf16", seed=710, cu_seqlens=cu)
+    rng = np.random.default_rng(711)
+    do = rng.standard_normal(inp["v"].shape).astype(np.float32)
+    ref = gated_delta_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], cu, None, do, None)
+    got = run_bwd(inp, do, None, 1.0, fill=7.0)
+    errs = compare(inp, got, ref)
+    _say("bwd no state: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL["bf16"] for v in errs.values()), errs
+    for key in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert bool((got[key][250:] == 7.0).all()), key
+
+
+def test_backward_int64_offsets_and_determinism():
+    inp = make_inputs(SMALL_CU[-1], 2, 128, 128, kda=False, dtype="bf16", seed=720,
+                      cu_seqlens=SMALL_CU, h0_std=0.1)
+    rng = np.random.default_rng(721)
+    do = rng.standard_normal(inp["v"].shape).astype(np.float32)
+    dht = rng.standard_normal(inp["h0"].shape).astype(np.float32)
+    a = run_bwd(inp, do, dht, 1.0)
+    b = run_bwd(inp, do, dht, 1.0, idx=torch.int64)
+    ne = torch.from_numpy(np.diff(np.asarray(SMALL_CU)) > 0)
+    for key in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert torch.equal(a[key][:460], b[key][:460]), key
+    assert torch.equal(a["dh0"][ne], b["dh0"][ne])
+
+
+def test_backward_config1_sampled_heads():
+    """The 8K varlen workload's layout and inputs (H = 16, d = 128, bf16), the
+    oracle on one head (its autograd tape holds every token's state)."""
+    from synth import config
+    inp = config(1)
+    rng = np.random.default_rng(730)
+    do = rng.standard_normal(inp["v"].shape).astype(np.float32)
+    got = run_bwd(inp, do, None, 1.0)
+    heads = [11]
+    sub = {x: np.ascontiguousarray(inp[x][:, heads]) for x in ("q", "k", "v", "g", "beta")}
+    ref = gated_delta_bwd(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], inp["cu_seqlens"],
+                          inp["h0"][:, heads], do[:, heads], None, 1.0)
+    errs = {}
+    for key in ("dq", "dk", "dv", "dg", "dbeta"):
+        errs[key] = rel_err(got[key].cpu().numpy()[:, heads], ref[key])
+    errs["dh0"] = rel_err(got["dh0"].cpu().numpy()[:, heads], ref["dh0"])
+    _say("bwd config1 head 11: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL["bf16"] for v in errs.values()), errs
