@@ -39,22 +39,41 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// acc += A(0..15, 0..K) B(0..K, 0..15) with A(m, k) at a[m * ams + k * aks] and
-// B(k, n) at b[k * bks + n * bns]; the result tile in the MFMA layout (lane l:
-// rows 4 (l / 16) + i, column l % 16).
-__device__ __forceinline__ f32x4 mm(f32x4 acc, const float *a, int ams, int aks, const float *b,
-                                    int bks, int bns, int K) {
+// Products of 16x16 tiles on fp32 MFMA: A(m, k) at a[m * ams + k * aks],
+// B(k, n) at b[k * bks + n * bns]; results in the MFMA layout (lane l: rows
+// 4 (l / 16) + i, column l % 16).
+
+// N tiles sharing one A: acc[j] += A B_j with B_j at b + j * bt.  The N
+// accumulations are independent, so their MFMAs interleave, and each A value
+// is read once for all N.
+template <int N>
+__device__ __forceinline__ void mmN(f32x4 (&acc)[N], const float *a, int ams, int aks,
+                                    const float *b, int bks, int bns, int bt, int K) {
   const int l = lane_id(), r = l & 15, g = l >> 4;
   const float *pa = a + r * ams + g * aks;
   const float *pb = b + g * bks + r * bns;
-#pragma unroll 4
-  for (int k = 0; k < K; k += 4) acc = mfma4(pa[k * aks], pb[k * bks], acc);
-  return acc;
+#pragma unroll 2
+  for (int k = 0; k < K; k += 4) {
+    const float av = pa[k * aks];
+#pragma unroll
+    for (int j = 0; j < N; ++j) acc[j] = mfma4(av, pb[j * bt + k * bks], acc[j]);
+  }
 }
 
-template <typename In>
-__device__ __forceinline__ float ldin(const void *p, size_t i) {
-  return Op<In>::load(static_cast<const In *>(p) + i);
+// one tile with the k range split over two accumulators (two interleaved
+// chains), summed at the end
+__device__ __forceinline__ f32x4 mm2k(const float *a, int ams, int aks, const float *b, int bks,
+                                      int bns, int K) {
+  const int l = lane_id(), r = l & 15, g = l >> 4;
+  const float *pa = a + r * ams + g * aks;
+  const float *pb = b + g * bks + r * bns;
+  f32x4 c0 = zero4(), c1 = zero4();
+#pragma unroll 2
+  for (int k = 0; k < K; k += 8) {
+    c0 = mfma4(pa[k * aks], pb[k * bks], c0);
+    c1 = mfma4(pa[(k + 4) * aks], pb[(k + 4) * bks], c1);
+  }
+  return c0 + c1;
 }
 
 // the chunk of slot jj: first row, valid rows; false for a sentinel slot
@@ -153,10 +172,13 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   float *img = p.prep + (size_t)blockIdx.x * kPrepFloats;
   const int w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
   // S = strict_lower(K K^T * E), M = lower_incl(Q K^T * E): wave w, rows 16w
+  f32x4 aS[4] = {zero4(), zero4(), zero4(), zero4()};
+  f32x4 aM[4] = {zero4(), zero4(), zero4(), zero4()};
+  mmN<4>(aS, sK + 16 * w * LK, LK, 1, sK, 1, LK, 16 * LK, DK);
+  mmN<4>(aM, sQ + 16 * w * LK, LK, 1, sK, 1, LK, 16 * LK, DK);
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) {
-    f32x4 as = mm(zero4(), sK + 16 * w * LK, LK, 1, sK + 16 * s4 * LK, 1, LK, DK);
-    f32x4 am = mm(zero4(), sQ + 16 * w * LK, LK, 1, sK + 16 * s4 * LK, 1, LK, DK);
+    const f32x4 as = aS[s4], am = aM[s4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + 4 * lg + i, s = 16 * s4 + lr;
@@ -248,41 +270,47 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdParams p) {
     }
     __syncthreads();
     // dU = M^T dOb + fac * (K dH'), rows 16w
+    {
+      f32x4 kd[2] = {zero4(), zero4()}, du[2] = {zero4(), zero4()};
+      mmN<2>(kd, sK + 16 * w * LK, LK, 1, sD, LC, 1, 16, DK);
+      mmN<2>(du, sM + 16 * w, 1, kL, sO, LC, 1, 16, 64);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      f32x4 kd = mm(zero4(), sK + 16 * w * LK, LK, 1, sD + 16 * nt, LC, 1, DK);
-      f32x4 du = mm(zero4(), sM + 16 * w, 1, kL, sO + 16 * nt, LC, 1, 64);
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * lg + i;
-        sU[r * LC + 16 * nt + lr] = du[i] + sFac[r] * kd[i];
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * w + 4 * lg + i;
+          sU[r * LC + 16 * nt + lr] = du[nt][i] + sFac[r] * kd[nt][i];
+        }
     }
     __syncthreads();
     // dX = beta * (A^-T dU); Y = gam * dX
+    {
+      f32x4 dx[2] = {zero4(), zero4()};
+      mmN<2>(dx, sA + 16 * w, 1, kL, sU, LC, 1, 16, 64);
 #pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
-      f32x4 dx = mm(zero4(), sA + 16 * w, 1, kL, sU + 16 * nt, LC, 1, 64);
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * lg + i;
-        sY[r * LC + 16 * nt + lr] = sGam[r] * sBeta[r] * dx[i];
-      }
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * w + 4 * lg + i;
+          sY[r * LC + 16 * nt + lr] = sGam[r] * sBeta[r] * dx[nt][i];
+        }
     }
     __syncthreads();
     // dH = gam_C dH' + Q^T (gam dOb) - K^T Y
     const float gamC = sGam[C - 1];
     for (int t = w; t < DK / 16; t += 4) {
+      f32x4 acc[2], ky[2] = {zero4(), zero4()};
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        f32x4 acc;
+      for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = gamC * sD[(16 * t + 4 * lg + i) * LC + 16 * nt + lr];
-        acc = mm(acc, sQ + 16 * t, 1, LK, sGO + 16 * nt, LC, 1, 64);
-        f32x4 ky = mm(zero4(), sK + 16 * t, 1, LK, sY + 16 * nt, LC, 1, 64);
+        for (int i = 0; i < 4; ++i) acc[nt][i] = gamC * sD[(16 * t + 4 * lg + i) * LC + 16 * nt + lr];
+      mmN<2>(acc, sQ + 16 * t, 1, LK, sGO, LC, 1, 16, 64);
+      mmN<2>(ky, sK + 16 * t, 1, LK, sY, LC, 1, 16, 64);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sD[(16 * t + 4 * lg + i) * LC + 16 * nt + lr] = acc[i] - ky[i];
-      }
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          sD[(16 * t + 4 * lg + i) * LC + 16 * nt + lr] = acc[nt][i] - ky[nt][i];
     }
   }
   __syncthreads();
@@ -299,7 +327,8 @@ template <typename In, int DK>
 __global__ __launch_bounds__(256) void bwd_part_kernel(BwdParams p) {
   constexpr int LK = DK + 4, LB = 20, DV = DK, NT = DK / 16;
   __shared__ __attribute__((aligned(16))) float sK[kBT * LK], sA[64 * kL], sM[64 * kL];
-  __shared__ __attribute__((aligned(16))) float sH[DK * LB], sDH[DK * LB];
+  __shared__ __attribute__((aligned(16))) float sHD[2 * DK * LB];  // H block, then dH' block
+  float *sH = sHD, *sDH = sHD + DK * LB;
   __shared__ __attribute__((aligned(16))) float sV[64 * LB], sO[64 * LB], sX[64 * LB], sBX[64 * LB], sU[64 * LB],
       sDU[64 * LB], sDX[64 * LB];
   __shared__ __attribute__((aligned(16))) float sGam[64], sFac[64], sBeta[64], sRed[256];
@@ -341,9 +370,10 @@ __global__ __launch_bounds__(256) void bwd_part_kernel(BwdParams p) {
     for (int idx = tid; idx < 64 * 16; idx += 256) sO[(idx / 16) * LB + idx % 16] *= p.scale;
     __syncthreads();
     {
-      const f32x4 kh = mm(zero4(), sK + 16 * w * LK, LK, 1, sH, LB, 1, DK);
-      const f32x4 kd = mm(zero4(), sK + 16 * w * LK, LK, 1, sDH, LB, 1, DK);
-      const f32x4 mo = mm(zero4(), sM + 16 * w, 1, kL, sO, LB, 1, 64);
+      f32x4 khd[2] = {zero4(), zero4()};  // K H and K dH'
+      mmN<2>(khd, sK + 16 * w * LK, LK, 1, sHD, LB, 1, DK * LB, DK);
+      const f32x4 kh = khd[0], kd = khd[1];
+      const f32x4 mo = mm2k(sM + 16 * w, 1, kL, sO, LB, 1, 64);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
@@ -355,8 +385,8 @@ __global__ __launch_bounds__(256) void bwd_part_kernel(BwdParams p) {
     }
     __syncthreads();
     {
-      const f32x4 u = mm(zero4(), sA + 16 * w * kL, kL, 1, sBX, LB, 1, 64);
-      const f32x4 dx = mm(zero4(), sA + 16 * w, 1, kL, sDU, LB, 1, 64);
+      const f32x4 u = mm2k(sA + 16 * w * kL, kL, 1, sBX, LB, 1, 64);
+      const f32x4 dx = mm2k(sA + 16 * w, 1, kL, sDU, LB, 1, 64);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
@@ -367,17 +397,11 @@ __global__ __launch_bounds__(256) void bwd_part_kernel(BwdParams p) {
       }
     }
     __syncthreads();
-#pragma unroll
-    for (int t = 0; t < NT; ++t) {
-      P1[t] = mm(P1[t], sO + 16 * w * LB, LB, 1, sH + 16 * t * LB, 1, LB, 16);
-      P2[t] = mm(P2[t], sDX + 16 * w * LB, LB, 1, sH + 16 * t * LB, 1, LB, 16);
-      P3[t] = mm(P3[t], sU + 16 * w * LB, LB, 1, sDH + 16 * t * LB, 1, LB, 16);
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      dM[t] = mm(dM[t], sO + 16 * w * LB, LB, 1, sU + 16 * t * LB, 1, LB, 16);
-      dT[t] = mm(dT[t], sDU + 16 * w * LB, LB, 1, sX + 16 * t * LB, 1, LB, 16);
-    }
+    mmN<NT>(P1, sO + 16 * w * LB, LB, 1, sH, 1, LB, 16 * LB, 16);
+    mmN<NT>(P2, sDX + 16 * w * LB, LB, 1, sH, 1, LB, 16 * LB, 16);
+    mmN<NT>(P3, sU + 16 * w * LB, LB, 1, sDH, 1, LB, 16 * LB, 16);
+    mmN<4>(dM, sO + 16 * w * LB, LB, 1, sU, 1, LB, 16 * LB, 16);
+    mmN<4>(dT, sDU + 16 * w * LB, LB, 1, sX, 1, LB, 16 * LB, 16);
   }
   float *gw = p.part + (size_t)blockIdx.x * part_floats(DK);
 #pragma unroll
@@ -464,18 +488,22 @@ __global__ __launch_bounds__(256) void bwd_final_kernel(BwdParams p) {
   }
   __syncthreads();
   // tmp = dA^-1 A^-T
+  {
+    f32x4 t[4] = {zero4(), zero4(), zero4(), zero4()};
+    mmN<4>(t, sDT + 16 * w * kL, kL, 1, sA, 1, kL, 16 * kL, 64);
 #pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) {
-    const f32x4 t = mm(zero4(), sDT + 16 * w * kL, kL, 1, sA + 16 * s4 * kL, 1, kL, 64);
+    for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sTmp[(16 * w + 4 * lg + i) * kL + 16 * s4 + lr] = t[i];
+      for (int i = 0; i < 4; ++i) sTmp[(16 * w + 4 * lg + i) * kL + 16 * s4 + lr] = t[s4][i];
   }
   __syncthreads();
   // dA = -A^-T tmp; strict lower part: W = dA S (beta), Y = beta dA S (gates),
   // F = beta dA E (keys)
+  f32x4 tA[4] = {zero4(), zero4(), zero4(), zero4()};
+  mmN<4>(tA, sA + 16 * w, 1, kL, sTmp, kL, 1, 16, 64);
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) {
-    const f32x4 t = mm(zero4(), sA + 16 * w, 1, kL, sTmp + 16 * s4, kL, 1, 64);
+    const f32x4 t = tA[s4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + 4 * lg + i, s = 16 * s4 + lr, o = r * kL + s;
@@ -539,21 +567,24 @@ __global__ __launch_bounds__(256) void bwd_final_kernel(BwdParams p) {
     p.dbeta[o] = bt[tid] + ba[tid];
   }
   // dQ = gam P1 + (dM E) K;  dK = -gam P2 + fac P3 + (dM E)^T Q + F K + F^T K
-  for (int t = 0; t < NT; ++t) {
-    f32x4 dq = mm(zero4(), sDM + 16 * w * kL, kL, 1, sK + 16 * t, LK, 1, 64);
-    f32x4 dk = mm(zero4(), sDM + 16 * w, 1, kL, sQ + 16 * t, LK, 1, 64);
-    dk = mm(dk, sDT + 16 * w * kL, kL, 1, sK + 16 * t, LK, 1, 64);
-    dk = mm(dk, sDT + 16 * w, 1, kL, sK + 16 * t, LK, 1, 64);
+  f32x4 dq[NT], dk[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) dq[t] = dk[t] = zero4();
+  mmN<NT>(dq, sDM + 16 * w * kL, kL, 1, sK, LK, 1, 16, 64);
+  mmN<NT>(dk, sDM + 16 * w, 1, kL, sQ, LK, 1, 16, 64);
+  mmN<NT>(dk, sDT + 16 * w * kL, kL, 1, sK, LK, 1, 16, 64);
+  mmN<NT>(dk, sDT + 16 * w, 1, kL, sK, LK, 1, 16, 64);
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = 16 * w + 4 * lg + i, c = 16 * t + lr;
       if (r < C) {
         const size_t o = ((size_t)(r0 + r) * H + h) * DK + c;
-        p.dq[o] = sGam[r] * P1[r * DK + c] + dq[i];
-        p.dk[o] = -sGam[r] * P2[r * DK + c] + sFac[r] * P3[r * DK + c] + dk[i];
+        p.dq[o] = sGam[r] * P1[r * DK + c] + dq[t][i];
+        p.dk[o] = -sGam[r] * P2[r * DK + c] + sFac[r] * P3[r * DK + c] + dk[t][i];
       }
     }
-  }
 }
 
 template <typename In, int DK>
