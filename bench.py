@@ -48,6 +48,9 @@ WORKLOADS = {
                          "d_k=d_v=128, fp32 state N(0,0.1) updated in place, seed 5"),
     "bwd": (1, None, "GDN chunk backward on the 8K varlen workload: bf16 q/k/v, fp32 g/beta, "
                      "H=16, d_k=d_v=128, h0~N(0,0.1), dout~N(0,1) fp32, no dht, seed 1"),
+    "bwdk": (2, True, "KDA chunk backward on the 4K KDA workload: bf16 q/k/v, bf16-valued "
+                      "g/beta, one sequence T=4096, H=16, d_k=d_v=128, zero state, "
+                      "dout~N(0,1) fp32, no dht, seed 2"),
     "conv": (None, None, "varlen causal short convolution: bf16 x [8192, 6144] (q, k, v "
                          "projections of H=16, d=128) in the 8 sequences of the 8K varlen "
                          "layout, W=4, bias, SiLU, bf16 states N(0,1) updated in place, "
@@ -372,7 +375,7 @@ def conv_cpu_baseline(inp, budget_s=12.0):
                       f"{len(times)} run(s) of the fp64 numpy token loop"}
 
 
-def bwd_alg_flops(cells, d):
+def bwd_alg_flops(cells, d, kda=False):
     """Algorithmic flops of the chunk backward per (chunk, head) cell, summed:
     the per-chunk products of the state-gradient pass (3 x 64 d^2 + 2 x 64^2 d
     MACs), of the dV / partial-product pass (5 x 64 d^2 + 5 x 64^2 d), of the
@@ -383,6 +386,9 @@ def bwd_alg_flops(cells, d):
     macs = (3 * c * d * d + 2 * c * c * d) + (5 * c * d * d + 5 * c * c * d) + \
         (4 * c * c * d + 2 * c ** 3) + (2 * c * c * d + c ** 3 / 3) + \
         (2 * c * d * d + c * c * d + 2 * c * c * d + c ** 3 / 3)
+    # KDA: the per-channel E-weighted sums of the final pass (four sums of
+    # C^2 / 2 d terms) count as the 4 x 64^2 d products they replace; the
+    # decay is inside S and M, whose 2 x 64^2 d products the prep counts
     return 2 * macs * cells
 
 
@@ -390,26 +396,31 @@ def bench_bwd(args, torch, la, synth, dev):
     """One GDN chunk backward per step (forward recompute + four backward
     launches) on the 8K varlen inputs; HIP events around the calls, then a
     graph of one call replayed."""
-    desc = WORKLOADS[args.workload][2]
-    inp = synth.config(1)
+    cfg, kda, desc = WORKLOADS[args.workload]
+    kda = bool(kda)
+    inp = synth.config(cfg)
     T, H, d = inp["q"].shape[0], inp["H"], inp["dk"]
     bf = torch.bfloat16
     q, k, v = (torch.from_numpy(inp[x]).to(dev, bf) for x in ("q", "k", "v"))
     g = torch.from_numpy(inp["g"]).to(dev)
     beta = torch.from_numpy(inp["beta"]).to(dev)
-    h0 = torch.from_numpy(inp["h0"]).to(dev)
+    h0 = None if inp["h0"] is None else torch.from_numpy(inp["h0"]).to(dev)
     rng = np.random.default_rng(1)
     dout = torch.from_numpy(rng.standard_normal((T, H, d)).astype(np.float32)).to(dev)
     cu = torch.from_numpy(inp["cu_seqlens"].astype(np.int32)).to(dev)
     N = cu.numel() - 1
     ci, co, _ = la.build_chunk_meta(cu, T)
-    ws = torch.empty((la.bwd_workspace_bytes(T, N, H, d, d, bf),), dtype=torch.uint8, device=dev)
+    ws = torch.empty((la.bwd_workspace_bytes(T, N, H, d, d, bf, kda=kda),), dtype=torch.uint8,
+                     device=dev)
     outs = dict(dq=torch.empty((T, H, d), device=dev), dk=torch.empty((T, H, d), device=dev),
-                dv=torch.empty((T, H, d), device=dev), dg=torch.empty((T, H), device=dev),
-                dbeta=torch.empty((T, H), device=dev), dh0=torch.empty_like(h0))
+                dv=torch.empty((T, H, d), device=dev), dg=torch.empty(g.shape, device=dev),
+                dbeta=torch.empty((T, H), device=dev))
+    if h0 is not None:
+        outs["dh0"] = torch.empty_like(h0)
+    fn = la.kda_chunk_bwd if kda else la.gdn_chunk_bwd
 
     def step():
-        la.gdn_chunk_bwd(q, k, v, g, beta, cu, ci, co, dout, h0=h0, workspace=ws, **outs)
+        fn(q, k, v, g, beta, cu, ci, co, dout, h0=h0, workspace=ws, **outs)
 
     for _ in range(max(1, args.warmup)):
         step()
@@ -442,7 +453,7 @@ def bench_bwd(args, torch, la, synth, dev):
     elapsed = time.perf_counter() - t0
     ms = elapsed * 1e3 / args.steps
     cells = int(np.ceil(np.diff(inp["cu_seqlens"]) / 64).sum()) * H
-    fl = bwd_alg_flops(cells, d)
+    fl = bwd_alg_flops(cells, d, kda)
     achieved = fl / (call_ms * 1e-3) / 1e12
     out = {
         "metric": "GDN/KDA chunk-fwd tokens/s (H=16,d=128,8K varlen); % of HBM/MFMA roofline",
@@ -456,7 +467,8 @@ def bench_bwd(args, torch, la, synth, dev):
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
                      "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_F32_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "gdn_chunk_bwd (whole call: map, reduce, prep, dh, part, final)",
+                     "kernel": ("kda" if kda else "gdn") +
+                               "_chunk_bwd (whole call: map, reduce, prep, dh, part, final)",
                      "alg_flops_per_call": fl, "avg_call_ms": round(call_ms, 5)},
         "graph_equals_eager": graph_eq,
     }
@@ -592,7 +604,7 @@ def main():
     if args.workload == "conv":
         bench_conv(args, torch, la, synth, dev)
         return
-    if args.workload == "bwd":
+    if args.workload in ("bwd", "bwdk"):
         bench_bwd(args, torch, la, synth, dev)
         return
 

@@ -24,7 +24,7 @@ import torch
 __all__ = [
     "LinAttnError", "lib", "nt_max", "build_chunk_meta", "workspace_bytes",
     "gdn_chunk_fwd", "kda_chunk_fwd", "chunk_fwd_stages", "dv_split_for", "seg_len_for",
-    "gdn_recurrent_fwd", "kda_recurrent_fwd", "short_conv_fwd", "gdn_chunk_bwd",
+    "gdn_recurrent_fwd", "kda_recurrent_fwd", "short_conv_fwd", "gdn_chunk_bwd", "kda_chunk_bwd",
     "bwd_workspace_bytes",
     "STAGE_MAP", "STAGE_REDUCE", "META_BAD_START", "META_NOT_MONOTONE",
     "META_OVER_CAPACITY", "LIB_PATH",
@@ -138,9 +138,10 @@ def lib():
             f.argtypes = [R, ctypes.c_void_p]
         B = ctypes.POINTER(ChunkBwdArgs)
         L.la_chunk_bwd_workspace_bytes.restype = ctypes.c_size_t
-        L.la_chunk_bwd_workspace_bytes.argtypes = [B]
-        L.gdn_chunk_bwd.restype = ctypes.c_int
-        L.gdn_chunk_bwd.argtypes = [B, ctypes.c_void_p]
+        L.la_chunk_bwd_workspace_bytes.argtypes = [B, ctypes.c_int]
+        for f in (L.gdn_chunk_bwd, L.kda_chunk_bwd):
+            f.restype = ctypes.c_int
+            f.argtypes = [B, ctypes.c_void_p]
         L.la_short_conv_fwd.restype = ctypes.c_int
         L.la_short_conv_fwd.argtypes = [ctypes.POINTER(ShortConvArgs), ctypes.c_void_p]
         L.la_status_string.restype = ctypes.c_char_p
@@ -466,19 +467,29 @@ def _bwd_shape(T_max, N_max, H, d_k, d_v, qkv_dtype, BT=64):
     return a
 
 
-def bwd_workspace_bytes(T_max, N_max, H, d_k, d_v, qkv_dtype, BT=64):
+def bwd_workspace_bytes(T_max, N_max, H, d_k, d_v, qkv_dtype, BT=64, kda=False):
     return int(lib().la_chunk_bwd_workspace_bytes(ctypes.byref(
-        _bwd_shape(T_max, N_max, H, d_k, d_v, qkv_dtype, BT))))
+        _bwd_shape(T_max, N_max, H, d_k, d_v, qkv_dtype, BT)), int(kda)))
 
 
-def gdn_chunk_bwd(q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, dout, *, h0=None,
-                  dht=None, scale=1.0, dq=None, dk=None, dv=None, dg=None, dbeta=None, dh0=None,
-                  workspace=None, stream=None):
+def gdn_chunk_bwd(*args, **kw):
     """GDN chunk backward (gdn_chunk_bwd): gradients of sum(o * dout) + sum(ht * dht).
 
-    Returns (dq, dk, dv, dg, dbeta, dh0) as fp32 tensors; dh0 is None unless
-    h0 is given or dh0 is passed.  dout [T_max, H, d_v] fp32.
+    Arguments as gdn_chunk_fwd plus dout [T_max, H, d_v] fp32 (after
+    chunk_offsets) and dht; returns (dq, dk, dv, dg, dbeta, dh0) as fp32
+    tensors, dh0 None unless h0 is given or dh0 is passed.
     """
+    return _chunk_bwd(False, *args, **kw)
+
+
+def kda_chunk_bwd(*args, **kw):
+    """KDA chunk backward (kda_chunk_bwd); g and dg are [T_max, H, d_k]."""
+    return _chunk_bwd(True, *args, **kw)
+
+
+def _chunk_bwd(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, dout, *, h0=None,
+               dht=None, scale=1.0, dq=None, dk=None, dv=None, dg=None, dbeta=None, dh0=None,
+               workspace=None, stream=None):
     _qkv_dtype(q)
     T_max, H, d_k = q.shape
     d_v = v.shape[-1]
@@ -486,7 +497,8 @@ def gdn_chunk_bwd(q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, do
     _need(q, "q", q.dtype)
     _need(k, "k", q.dtype, (T_max, H, d_k), dev)
     _need(v, "v", q.dtype, (T_max, H, d_v), dev)
-    _need(g, "g", torch.float32, (T_max, H), dev)
+    g_shape = (T_max, H, d_k) if kda else (T_max, H)
+    _need(g, "g", torch.float32, g_shape, dev)
     _need(beta, "beta", torch.float32, (T_max, H), dev)
     _need_idx(cu_seqlens, dev)
     N_max = cu_seqlens.numel() - 1
@@ -508,7 +520,7 @@ def gdn_chunk_bwd(q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, do
     dq = out(dq, (T_max, H, d_k), "dq")
     dk = out(dk, (T_max, H, d_k), "dk")
     dv = out(dv, (T_max, H, d_v), "dv")
-    dg = out(dg, (T_max, H), "dg")
+    dg = out(dg, g_shape, "dg")
     dbeta = out(dbeta, (T_max, H), "dbeta")
     if dh0 is None and h0 is not None:
         dh0 = torch.empty(st_shape, dtype=torch.float32, device=dev)
@@ -517,7 +529,7 @@ def gdn_chunk_bwd(q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, do
     a = _bwd_shape(T_max, N_max, H, d_k, d_v, q.dtype)
     a.cu_seqlens_i64 = int(cu_seqlens.dtype == torch.int64)
     a.scale = float(scale)
-    need = int(lib().la_chunk_bwd_workspace_bytes(ctypes.byref(a)))
+    need = int(lib().la_chunk_bwd_workspace_bytes(ctypes.byref(a), int(kda)))
     if workspace is None:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
     _need(workspace, "workspace", torch.uint8, None, dev)
@@ -532,7 +544,8 @@ def gdn_chunk_bwd(q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, do
     a.dh0 = None if dh0 is None else dh0.data_ptr()
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel()
-    rc = lib().gdn_chunk_bwd(ctypes.byref(a), _stream(stream))
+    f = lib().kda_chunk_bwd if kda else lib().gdn_chunk_bwd
+    rc = f(ctypes.byref(a), _stream(stream))
     if rc != 0:
-        raise LinAttnError(rc, "gdn_chunk_bwd")
+        raise LinAttnError(rc, "kda_chunk_bwd" if kda else "gdn_chunk_bwd")
     return dq, dk, dv, dg, dbeta, dh0

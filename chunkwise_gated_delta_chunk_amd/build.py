@@ -10,7 +10,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblinattn.so")
 SOURCES = ["meta.hip", "chunk_map.hip", "chunk_reduce.hip", "chunk_combine.hip", "recurrent.hip",
-           "short_conv.hip", "chunk_bwd.hip", "linattn.cpp"]
+           "short_conv.hip", "chunk_bwd.hip", "chunk_bwd_kda.hip",
+           "linattn.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 FLAGS = [

@@ -1,0 +1,128 @@
+// Helpers shared by the chunk backward kernels (chunk_bwd.hip for GDN,
+// chunk_bwd_kda.hip for KDA); internal, device only.
+#pragma once
+
+#include "la_device.h"
+#include "kernels.h"
+
+namespace la {
+namespace bwd {
+
+constexpr int kL = 68;  // row stride of the [64][64] LDS matrices (floats)
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// Products of 16x16 tiles on fp32 MFMA: A(m, k) at a[m * ams + k * aks],
+// B(k, n) at b[k * bks + n * bns]; results in the MFMA layout (lane l: rows
+// 4 (l / 16) + i, column l % 16).
+
+// N tiles sharing one A: acc[j] += A B_j with B_j at b + j * bt.  The N
+// accumulations are independent, so their MFMAs interleave, and each A value
+// is read once for all N.
+template <int N>
+__device__ __forceinline__ void mmN(f32x4 (&acc)[N], const float *a, int ams, int aks,
+                                    const float *b, int bks, int bns, int bt, int K) {
+  const int l = lane_id(), r = l & 15, g = l >> 4;
+  const float *pa = a + r * ams + g * aks;
+  const float *pb = b + g * bks + r * bns;
+#pragma unroll 2
+  for (int k = 0; k < K; k += 4) {
+    const float av = pa[k * aks];
+#pragma unroll
+    for (int j = 0; j < N; ++j) acc[j] = mfma4(av, pb[j * bt + k * bks], acc[j]);
+  }
+}
+
+// one tile with the k range split over two accumulators (two interleaved
+// chains), summed at the end
+__device__ __forceinline__ f32x4 mm2k(const float *a, int ams, int aks, const float *b, int bks,
+                                      int bns, int K) {
+  const int l = lane_id(), r = l & 15, g = l >> 4;
+  const float *pa = a + r * ams + g * aks;
+  const float *pb = b + g * bks + r * bns;
+  f32x4 c0 = zero4(), c1 = zero4();
+#pragma unroll 2
+  for (int k = 0; k < K; k += 8) {
+    c0 = mfma4(pa[k * aks], pb[k * bks], c0);
+    c1 = mfma4(pa[(k + 4) * aks], pb[(k + 4) * bks], c1);
+  }
+  return c0 + c1;
+}
+
+// the chunk of slot jj: first row, valid rows; false for a sentinel slot
+struct Chunk { int n, r0, C; };
+__device__ __forceinline__ bool chunk_of(const BwdParams &p, int slot, Chunk &c) {
+  const int n = p.chunk_indices[2 * slot];
+  if (n < 0) return false;
+  const int i_t = p.chunk_indices[2 * slot + 1];
+  const int bos = cu_at(p.cu_seqlens, p.cu64, n);
+  const int eos = cu_at(p.cu_seqlens, p.cu64, n + 1);
+  c.n = n;
+  c.r0 = bos + i_t * kBT;
+  c.C = min(kBT, eos - c.r0);
+  return true;
+}
+
+// The loaders move 16-byte pieces, all of a thread's loads issued before its
+// LDS stores, so a chunk's operands arrive in about one memory round trip.
+
+// rows r < C of a [T][H][D] input, head h, columns c0 .. c0 + W, into LDS
+// rows of stride ld (fp32, 16-byte aligned rows); rows >= C are zero
+template <typename In, int D, int W = D, int R = kBT>
+__device__ __forceinline__ void load_rows(float *dst, int ld, const void *src, int r0, int C, int H,
+                                          int h, int c0 = 0) {
+  constexpr int VEC = 16 / (int)sizeof(In);
+  constexpr int PR = W / VEC;                 // pieces per row
+  constexpr int NP = R * PR;                  // pieces
+  constexpr int IT = (NP + 255) / 256;
+  uint32_t raw[IT][4];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int pc = threadIdx.x + 256 * it, r = pc / PR, c = (pc % PR) * VEC;
+    const u32x4 v = (pc < NP && r < C)
+        ? *reinterpret_cast<const u32x4 *>(static_cast<const char *>(src) +
+                                           (((size_t)(r0 + r) * H + h) * D + c0 + c) * sizeof(In))
+        : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) raw[it][e] = v[e];
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int pc = threadIdx.x + 256 * it, r = pc / PR, c = (pc % PR) * VEC;
+    if (pc < NP) {
+      float f[VEC];
+      unpack16<In>(raw[it], f);
+#pragma unroll
+      for (int q = 0; q < VEC / 4; ++q)
+        *reinterpret_cast<f32x4 *>(dst + r * ld + c + 4 * q) =
+            f32x4{f[4 * q], f[4 * q + 1], f[4 * q + 2], f[4 * q + 3]};
+    }
+  }
+}
+
+// an [R][W] fp32 block at src (row stride sld floats) into LDS (stride ld)
+template <int R, int W>
+__device__ __forceinline__ void load_block(float *dst, int ld, const float *src, size_t sld) {
+  constexpr int PR = W / 4, NP = R * PR, IT = (NP + 255) / 256;
+  f32x4 v[IT];
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int pc = threadIdx.x + 256 * it;
+    v[it] = pc < NP ? *reinterpret_cast<const f32x4 *>(src + (pc / PR) * sld + (pc % PR) * 4)
+                    : zero4();
+  }
+#pragma unroll
+  for (int it = 0; it < IT; ++it) {
+    const int pc = threadIdx.x + 256 * it;
+    if (pc < NP) *reinterpret_cast<f32x4 *>(dst + (pc / PR) * ld + (pc % PR) * 4) = v[it];
+  }
+}
+
+__device__ __forceinline__ void load_mat64(float *dst, const float *src) {
+  load_block<64, 64>(dst, kL, src, 64);
+}
+
+}  // namespace bwd
+}  // namespace la

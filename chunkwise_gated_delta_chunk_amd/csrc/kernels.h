@@ -92,7 +92,12 @@ __host__ __device__ constexpr int part_p3(int d) { return 128 * d; }
 __host__ __device__ constexpr int part_dm(int d) { return 192 * d; }
 __host__ __device__ constexpr int part_dt(int d) { return 192 * d + 4096; }
 __host__ __device__ constexpr int part_sh(int d) { return 192 * d + 8192; }
-__host__ __device__ constexpr int part_floats(int d) { return 192 * d + 8192 + 64; }
+// (KDA: the <dH', H> term is a vector over the d_k rows, at part_sh)
+__host__ __device__ constexpr int part_floats(int d) { return 192 * d + 8192 + 256; }
+// KDA prep cell: A^-1, M, S ([64][64] each), beta (64), then the per-channel
+// cumulative gate G ([64][d])
+constexpr int kKdaBeta = 12288, kKdaG = 12352;
+__host__ __device__ constexpr int kda_prep_floats(int d) { return kKdaG + 64 * d; }
 
 struct BwdParams {
   const void *q, *k, *v;
@@ -117,6 +122,7 @@ hipError_t launch_chunk_reduce(const ReduceParams &p, bool kda, int dt, int dk, 
 hipError_t launch_chunk_combine(const CombineParams &p, int dk, hipStream_t st);
 hipError_t launch_recurrent(const RecurrentParams &p, bool kda, int dt, int dk, hipStream_t st);
 hipError_t launch_chunk_bwd(const BwdParams &p, int dt, int dk, hipStream_t st);
+hipError_t launch_chunk_bwd_kda(const BwdParams &p, int dt, int dk, hipStream_t st);
 // NT chunk slots, W in 1..4
 hipError_t launch_short_conv(const ConvParams &p, int dt, int NT, int W, bool silu,
                              hipStream_t st);

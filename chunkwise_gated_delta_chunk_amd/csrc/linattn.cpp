@@ -371,16 +371,16 @@ static la_chunk_fwd_args fwd_view(const la_chunk_bwd_args *a) {
 
 // backward workspace: [forward images][hs][dhs][prep][part], each 256-aligned
 struct BwdLayout { size_t img, hs, dhs, prep, part, total; };
-static BwdLayout bwd_layout(const la_chunk_bwd_args *a) {
+static BwdLayout bwd_layout(const la_chunk_bwd_args *a, bool kda) {
   const la_chunk_fwd_args f = fwd_view(a);
   const size_t cells = (size_t)la_nt_max(a->T_max, a->N_max, a->BT) * a->H;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   BwdLayout L{};
   L.img = 0;
-  L.hs = up(ws_img_bytes(&f, false));
+  L.hs = up(ws_img_bytes(&f, kda));
   L.dhs = L.hs + up(cells * a->d_k * a->d_v * sizeof(float));
   L.prep = L.dhs + up(cells * a->d_k * a->d_v * sizeof(float));
-  L.part = L.prep + up(cells * la::kPrepFloats * sizeof(float));
+  L.part = L.prep + up(cells * (kda ? la::kda_prep_floats(a->d_k) : la::kPrepFloats) * sizeof(float));
   L.total = L.part + up(cells * la::part_floats(a->d_k) * sizeof(float));
   return L;
 }
@@ -392,12 +392,12 @@ static int check_bwd(const la_chunk_bwd_args *a) {
   return LA_OK;
 }
 
-size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *a) {
+size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *a, int is_kda) {
   if (!a || check_bwd(a) != LA_OK) return 0;
-  return bwd_layout(a).total;
+  return bwd_layout(a, is_kda != 0).total;
 }
 
-int gdn_chunk_bwd(const la_chunk_bwd_args *a, void *stream) {
+static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
   if (!a) return LA_ERR_NULL;
   const int sc = check_bwd(a);
   if (sc != LA_OK) return sc;
@@ -405,7 +405,7 @@ int gdn_chunk_bwd(const la_chunk_bwd_args *a, void *stream) {
       !a->chunk_offsets || !a->dout || !a->dq || !a->dk || !a->dv || !a->dg || !a->dbeta)
     return LA_ERR_NULL;
   if (!a->workspace) return LA_ERR_WORKSPACE;
-  const BwdLayout L = bwd_layout(a);
+  const BwdLayout L = bwd_layout(a, kda);
   if (a->workspace_bytes < L.total) return LA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(a->workspace) % 256 != 0) return LA_ERR_WORKSPACE;
   const uintptr_t mis = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->k) |
@@ -441,7 +441,7 @@ int gdn_chunk_bwd(const la_chunk_bwd_args *a, void *stream) {
     mp.Hqk = a->H;
     mp.NT_max = NT;
     mp.img = ws;
-    if (la::launch_chunk_map(mp, false, a->qkv_dtype, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
+    if (la::launch_chunk_map(mp, kda, a->qkv_dtype, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
     la::ReduceParams rp{};
     rp.v = a->v;
     rp.cu_seqlens = a->cu_seqlens;
@@ -456,7 +456,7 @@ int gdn_chunk_bwd(const la_chunk_bwd_args *a, void *stream) {
     rp.S = split_for(&f);
     rp.scale = a->scale;
     rp.hsave = reinterpret_cast<float *>(ws + L.hs);
-    if (la::launch_chunk_reduce(rp, false, a->qkv_dtype, a->d_k, a->d_v / rp.S, st) != hipSuccess)
+    if (la::launch_chunk_reduce(rp, kda, a->qkv_dtype, a->d_k, a->d_v / rp.S, st) != hipSuccess)
       return LA_ERR_HIP;
   }
   la::BwdParams bp{};
@@ -485,9 +485,15 @@ int gdn_chunk_bwd(const la_chunk_bwd_args *a, void *stream) {
   bp.N_max = a->N_max;
   bp.NT = NT;
   bp.scale = a->scale;
-  if (la::launch_chunk_bwd(bp, a->qkv_dtype, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
+  const hipError_t e = kda ? la::launch_chunk_bwd_kda(bp, a->qkv_dtype, a->d_k, st)
+                          : la::launch_chunk_bwd(bp, a->qkv_dtype, a->d_k, st);
+  if (e != hipSuccess) return LA_ERR_HIP;
   return LA_OK;
 }
+
+int gdn_chunk_bwd(const la_chunk_bwd_args *a, void *stream) { return chunk_bwd(a, false, stream); }
+
+int kda_chunk_bwd(const la_chunk_bwd_args *a, void *stream) { return chunk_bwd(a, true, stream); }
 
 const char *la_status_string(int status) {
   switch (status) {

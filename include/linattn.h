@@ -242,8 +242,8 @@ typedef struct {
 int gdn_recurrent_fwd(const la_recurrent_args *a, void *stream);
 int kda_recurrent_fwd(const la_recurrent_args *a, void *stream);
 
-/* Arguments of the GDN chunk backward: the forward's inputs and metadata,
- * the output gradient, and the gradient outputs. */
+/* Arguments of the GDN / KDA chunk backward: the forward's inputs and
+ * metadata, the output gradient, and the gradient outputs. */
 typedef struct {
     int32_t T_max, N_max, H;   /* as la_chunk_fwd_args                           */
     int32_t d_k, d_v;          /* d_k == d_v: 64 or 128 (16-bit), 64 (fp32)      */
@@ -252,7 +252,7 @@ typedef struct {
     int32_t cu_seqlens_i64;    /* 0: cu_seqlens int32; 1: int64                  */
     float scale;               /* the forward's scale                            */
     const void *q, *k, *v;     /* [T_max][H][d_k] / [T_max][H][d_v], qkv_dtype  */
-    const float *g;            /* log-decay [T_max][H]                           */
+    const float *g;            /* log-decay: GDN [T_max][H]; KDA [T_max][H][d_k] */
     const float *beta;         /* [T_max][H]                                     */
     const void *cu_seqlens;    /* [N_max+1]                                      */
     const int32_t *chunk_indices, *chunk_offsets; /* from build_chunk_meta      */
@@ -261,22 +261,25 @@ typedef struct {
     const float *dht;          /* gradient of ht: [N_max][H][d_k][d_v] or NULL   */
     float *dq, *dk;            /* [T_max][H][d_k] fp32                           */
     float *dv;                 /* [T_max][H][d_v] fp32                           */
-    float *dg, *dbeta;         /* [T_max][H] fp32                                */
+    float *dg;                 /* like g, fp32                                   */
+    float *dbeta;              /* [T_max][H] fp32                                */
     float *dh0;                /* [N_max][H][d_k][d_v] fp32 or NULL              */
     void *workspace;           /* >= la_chunk_bwd_workspace_bytes(...) bytes,    */
     size_t workspace_bytes;    /* 256-byte aligned                               */
 } la_chunk_bwd_args;
 
-/* Workspace of gdn_chunk_bwd for this shape (T_max, N_max, H, d_k, d_v, BT,
- * qkv_dtype read); 0 if the shape is invalid.  It holds the forward
- * recompute's map images, the state entering and the state gradient leaving
- * every chunk ([d_k][d_v] fp32 per chunk slot and head), per-cell fp32
- * matrices A^-1, M, S and per-cell partial products. */
-size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *shape);
+/* Workspace of gdn_chunk_bwd / kda_chunk_bwd for this shape (T_max, N_max,
+ * H, d_k, d_v, BT, qkv_dtype read); 0 if the shape is invalid.  It holds the
+ * forward recompute's map images, the state entering and the state gradient
+ * leaving every chunk ([d_k][d_v] fp32 per chunk slot and head), per-cell
+ * fp32 matrices A^-1, M, S (KDA: and the per-channel cumulative gate) and
+ * per-cell partial products. */
+size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *shape, int is_kda);
 
 /*
- * GDN chunk backward: the gradients of L = sum(o * dout) + sum(ht * dht) of
- * gdn_chunk_fwd with the same inputs, for q, k, v, g, beta and h0 (FLA RFC,
+ * GDN / KDA chunk backward: the gradients of L = sum(o * dout) + sum(ht * dht)
+ * of gdn_chunk_fwd / kda_chunk_fwd with the same inputs, for q, k, v, g, beta
+ * and h0 (FLA RFC,
  * sections "Scope" and "Step 3": the backward of the chunk path).  It
  * recomputes the forward's per-chunk states (map, then the reduce storing the
  * state entering each chunk), then runs four launches: a chunk-parallel prep
@@ -290,6 +293,7 @@ size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *shape);
  * LA_ERR_WORKSPACE, LA_ERR_HIP.
  */
 int gdn_chunk_bwd(const la_chunk_bwd_args *a, void *stream);
+int kda_chunk_bwd(const la_chunk_bwd_args *a, void *stream);
 
 /* Activation of the short convolution. */
 #define LA_ACT_NONE 0

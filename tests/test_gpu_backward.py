@@ -1,4 +1,4 @@
-"""GPU parity of the GDN chunk backward against the fp64 oracle
+"""GPU parity of the GDN and KDA chunk backward against the fp64 oracle
 (oracle/backward.py: reverse-mode gradients of the token recurrence).
 
 Bar, per gradient (dq, dk, dv, dg, dbeta over the rows of real tokens; dh0
@@ -42,10 +42,10 @@ def run_bwd(inp, do, dht, scale, *, with_h0=True, idx=torch.int32, fill=None):
         outs = dict(dq=torch.full((T, H, dk), fill, device="cuda"),
                     dk=torch.full((T, H, dk), fill, device="cuda"),
                     dv=torch.full((T, H, dv), fill, device="cuda"),
-                    dg=torch.full((T, H), fill, device="cuda"),
+                    dg=torch.full(inp["g"].shape, fill, device="cuda"),
                     dbeta=torch.full((T, H), fill, device="cuda"))
-    res = la.gdn_chunk_bwd(d["q"], d["k"], d["v"], g, b, cu, ci, co, dout, h0=h0, dht=dh,
-                           scale=scale, **outs)
+    f = la.kda_chunk_bwd if inp["kda"] else la.gdn_chunk_bwd
+    res = f(d["q"], d["k"], d["v"], g, b, cu, ci, co, dout, h0=h0, dht=dh, scale=scale, **outs)
     torch.cuda.synchronize()
     return dict(zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), res))
 
@@ -62,29 +62,32 @@ def compare(inp, got, ref):
     return errs
 
 
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
 @pytest.mark.parametrize("dtype,d", [("bf16", 128), ("bf16", 64), ("f16", 128), ("f32", 64)])
-def test_backward_matches_oracle(dtype, d):
-    inp = make_inputs(SMALL_CU[-1], 3, d, d, kda=False, dtype=dtype, seed=700 + d,
+def test_backward_matches_oracle(kda, dtype, d):
+    inp = make_inputs(SMALL_CU[-1], 3, d, d, kda=kda, dtype=dtype, seed=700 + d,
                       cu_seqlens=SMALL_CU, h0_std=0.1)
     rng = np.random.default_rng(701)
     do = rng.standard_normal(inp["v"].shape).astype(np.float32)
     dht = rng.standard_normal(inp["h0"].shape).astype(np.float32)
     ref = gated_delta_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], SMALL_CU,
-                          inp["h0"], do, dht, 0.75)
+                          inp["h0"], do, dht, 0.75, kda=kda)
     got = run_bwd(inp, do, dht, 0.75)
     errs = compare(inp, got, ref)
-    _say(f"bwd {dtype} d={d}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    _say(f"bwd {'kda' if kda else 'gdn'} {dtype} d={d}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     tol = TOL[dtype]
     assert all(v <= tol for v in errs.values()), errs
 
 
-def test_backward_no_state_no_dht_and_padding_untouched():
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+def test_backward_no_state_no_dht_and_padding_untouched(kda):
     T_max = 300
     cu = [0, 70, 70, 250]
-    inp = make_inputs(T_max, 2, 64, 64, kda=False, dtype="bf16", seed=710, cu_seqlens=cu)
+    inp = make_inputs(T_max, 2, 64, 64, kda=kda, dtype="bf16", seed=710, cu_seqlens=cu)
     rng = np.random.default_rng(711)
     do = rng.standard_normal(inp["v"].shape).astype(np.float32)
-    ref = gated_delta_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], cu, None, do, None)
+    ref = gated_delta_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], cu, None, do, None,
+                          kda=kda)
     got = run_bwd(inp, do, None, 1.0, fill=7.0)
     errs = compare(inp, got, ref)
     _say("bwd no state: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
@@ -124,4 +127,22 @@ def test_backward_config1_sampled_heads():
         errs[key] = rel_err(got[key].cpu().numpy()[:, heads], ref[key])
     errs["dh0"] = rel_err(got["dh0"].cpu().numpy()[:, heads], ref["dh0"])
     _say("bwd config1 head 11: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL["bf16"] for v in errs.values()), errs
+
+
+def test_backward_kda_config2_sampled_head():
+    """The KDA workload's inputs (one sequence T = 4096, H = 16, d = 128, bf16,
+    bf16-valued gates), the oracle on one head."""
+    from synth import config
+    inp = config(2)
+    rng = np.random.default_rng(740)
+    do = rng.standard_normal(inp["v"].shape).astype(np.float32)
+    got = run_bwd(inp, do, None, 1.0)
+    heads = [5]
+    sub = {x: np.ascontiguousarray(inp[x][:, heads]) for x in ("q", "k", "v", "g", "beta")}
+    ref = gated_delta_bwd(sub["q"], sub["k"], sub["v"], sub["g"], sub["beta"], inp["cu_seqlens"],
+                          None, do[:, heads], None, 1.0, kda=True)
+    errs = {key: rel_err(got[key].cpu().numpy()[:, heads], ref[key])
+            for key in ("dq", "dk", "dv", "dg", "dbeta")}
+    _say("bwd kda config2 head 5: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     assert all(v <= TOL["bf16"] for v in errs.values()), errs
