@@ -266,3 +266,55 @@ def test_short_conv_rejects_on_host(name, kw, code):
     a = _cargs(**kw)
     assert la.lib().la_short_conv_fwd(ctypes.byref(a), None) == code
     assert la.lib().la_short_conv_fwd(None, None) == -1
+
+
+def _bargs(**kw):
+    a = la.ChunkBwdArgs()
+    a.T_max, a.N_max, a.H, a.d_k, a.d_v, a.BT, a.qkv_dtype = 256, 2, 2, 64, 64, 64, 0
+    a.scale = 1.0
+    fake = 0x100000  # never dereferenced: every case fails before launch
+    for f in ("q", "k", "v", "g", "beta", "cu_seqlens", "chunk_indices", "chunk_offsets", "dout",
+              "dq", "dk", "dv", "dg", "dbeta", "workspace"):
+        setattr(a, f, fake)
+    a.workspace_bytes = 1 << 34
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+BBAD = [
+    ("null dout", dict(dout=None), -1),
+    ("null dq", dict(dq=None), -1),
+    ("null dbeta", dict(dbeta=None), -1),
+    ("dtype 4", dict(qkv_dtype=4), -3),
+    ("BT 32", dict(BT=32), -4),
+    ("d 96", dict(d_k=96, d_v=96), -4),
+    ("no workspace", dict(workspace=None), -5),
+    ("workspace small", dict(workspace_bytes=1000), -5),
+    ("q misaligned", dict(q=0x100008), -2),
+    ("H 0", dict(H=0), -2),
+]
+
+
+@pytest.mark.parametrize("name,kw,code", BBAD, ids=[b[0] for b in BBAD])
+def test_backward_rejects_on_host(name, kw, code):
+    a = _bargs(**kw)
+    L = la.lib()
+    assert L.gdn_chunk_bwd(ctypes.byref(a), None) == code
+    assert L.kda_chunk_bwd(ctypes.byref(a), None) == code
+    assert L.gdn_chunk_bwd(None, None) == -1
+
+
+def test_backward_workspace_size():
+    """[forward images][entering states][leaving gradients][prep][partials],
+    each region rounded up to 256 bytes."""
+    import torch
+    T, N, H, d = 1000, 3, 2, 128
+    cells = meta_ref.nt_max(T, N, 64) * H
+    up = lambda x: -(-x // 256) * 256
+    for kda in (False, True):
+        img = la.workspace_bytes(T, N, H, d, d, torch.bfloat16, kda=kda, seg_len=-1)
+        prep = (12544 if not kda else 12352 + 64 * d) * 4
+        part = (192 * d + 8192 + 256) * 4
+        want = up(img) + 2 * up(cells * d * d * 4) + up(cells * prep) + up(cells * part)
+        assert la.bwd_workspace_bytes(T, N, H, d, d, torch.bfloat16, kda=kda) == want
