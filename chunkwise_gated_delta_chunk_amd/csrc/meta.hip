@@ -6,7 +6,8 @@
 // on the device into fixed-shape buffers, with no host round-trip, no
 // data-dependent grid and the sentinel {-1, 0} in unused slots.  One
 // workgroup: a validity check, a prefix sum of per-sequence chunk counts held
-// in LDS, then one binary search per slot.  cu_seqlens may be int32 or int64;
+// in LDS, then one binary search per slot (up to 64 sequences: a single wave
+// does the check and the scan with lane shuffles).  cu_seqlens may be int32 or int64;
 // it is checked in its own width, so an int64 layout that passes the checks
 // has every offset in [0, T_max] and the forward kernels read it as int.
 #include "la_device.h"
@@ -96,8 +97,79 @@ __global__ __launch_bounds__(kMetaThreads) void chunk_meta_kernel(
   if (status && tid == 0) *status = 0;
 }
 
+// N_max <= 64: one wave checks the offsets and scans the chunk counts with
+// lane shuffles (lane n holding sequence n), one barrier, then the
+// workgroup's four waves fill the slots
+template <typename Idx>
+__global__ __launch_bounds__(256) void chunk_meta_small_kernel(
+    const Idx *__restrict__ cu, int N_max, int T_max, int BT, int NT_max,
+    int32_t *__restrict__ ci, int32_t *__restrict__ co, int32_t *__restrict__ status) {
+  __shared__ int s_off[65];
+  __shared__ int s_flags;
+  const int tid = threadIdx.x;
+  if (tid < 64) {
+    const int n = tid;
+    const bool live = n < N_max;
+    const Idx a = live ? cu[n] : Idx(0), b = live ? cu[n + 1] : Idx(0);
+    int f = 0;
+    if (__ballot(live && b < a)) f |= LA_META_NOT_MONOTONE;
+    if (cu[0] != 0) f |= LA_META_BAD_START;
+    if (cu[N_max] > (Idx)T_max) f |= LA_META_OVER_CAPACITY;
+    int cnt = (live && !f) ? ((int)(b - a) + BT - 1) / BT : 0;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int y = __shfl_up(cnt, off, 64);
+      if (n >= off) cnt += y;
+    }
+    const int total = __shfl(cnt, 63, 64);
+    if (!f && total > NT_max) f = LA_META_OVER_CAPACITY;
+    if (n == 0) {
+      s_off[0] = 0;
+      s_flags = f;
+    }
+    s_off[n + 1] = cnt;
+  }
+  __syncthreads();
+  const int flags = s_flags;
+  if (flags) {
+    for (int j = tid; j < NT_max; j += 256) {
+      ci[2 * j] = -1;
+      ci[2 * j + 1] = 0;
+    }
+    for (int n = tid; n <= N_max; n += 256) co[n] = 0;
+    if (status && tid == 0) *status = flags;
+    return;
+  }
+  for (int n = tid; n <= N_max; n += 256) co[n] = s_off[n];
+  const int total = s_off[N_max];
+  for (int j = tid; j < NT_max; j += 256) {
+    int i_n = -1, i_t = 0;
+    if (j < total) {
+      int lo = 0, hi = N_max - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (s_off[mid] <= j) lo = mid; else hi = mid - 1;
+      }
+      i_n = lo;
+      i_t = j - s_off[lo];
+    }
+    ci[2 * j] = i_n;
+    ci[2 * j + 1] = i_t;
+  }
+  if (status && tid == 0) *status = 0;
+}
+
 hipError_t launch_chunk_meta(const void *cu, int cu64, int N_max, int T_max, int BT, int NT_max,
                              int32_t *ci, int32_t *co, int32_t *status, hipStream_t stream) {
+  if (N_max <= 64) {
+    if (cu64)
+      hipLaunchKernelGGL(chunk_meta_small_kernel<int64_t>, dim3(1), dim3(256), 0, stream,
+                         static_cast<const int64_t *>(cu), N_max, T_max, BT, NT_max, ci, co, status);
+    else
+      hipLaunchKernelGGL(chunk_meta_small_kernel<int32_t>, dim3(1), dim3(256), 0, stream,
+                         static_cast<const int32_t *>(cu), N_max, T_max, BT, NT_max, ci, co, status);
+    return hipGetLastError();
+  }
   if (cu64)
     hipLaunchKernelGGL(chunk_meta_kernel<int64_t>, dim3(1), dim3(kMetaThreads), 0, stream,
                        static_cast<const int64_t *>(cu), N_max, T_max, BT, NT_max, ci, co, status);
