@@ -21,13 +21,15 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
 // N tiles sharing one A: acc[j] += A B_j with B_j at b + j * bt.  The N
 // accumulations are independent, so their MFMAs interleave, and each A value
 // is read once for all N.
-template <int N>
+// K is a compile-time length: the loop unrolls fully, so the LDS reads of
+// all k-steps can be issued ahead of the MFMAs that use them.
+template <int N, int K>
 __device__ __forceinline__ void mmN(f32x4 (&acc)[N], const float *a, int ams, int aks,
-                                    const float *b, int bks, int bns, int bt, int K) {
+                                    const float *b, int bks, int bns, int bt) {
   const int l = lane_id(), r = l & 15, g = l >> 4;
   const float *pa = a + r * ams + g * aks;
   const float *pb = b + g * bks + r * bns;
-#pragma unroll 2
+#pragma unroll
   for (int k = 0; k < K; k += 4) {
     const float av = pa[k * aks];
 #pragma unroll
@@ -37,13 +39,14 @@ __device__ __forceinline__ void mmN(f32x4 (&acc)[N], const float *a, int ams, in
 
 // one tile with the k range split over two accumulators (two interleaved
 // chains), summed at the end
+template <int K>
 __device__ __forceinline__ f32x4 mm2k(const float *a, int ams, int aks, const float *b, int bks,
-                                      int bns, int K) {
+                                      int bns) {
   const int l = lane_id(), r = l & 15, g = l >> 4;
   const float *pa = a + r * ams + g * aks;
   const float *pb = b + g * bks + r * bns;
   f32x4 c0 = zero4(), c1 = zero4();
-#pragma unroll 2
+#pragma unroll
   for (int k = 0; k < K; k += 8) {
     c0 = mfma4(pa[k * aks], pb[k * bks], c0);
     c1 = mfma4(pa[(k + 4) * aks], pb[(k + 4) * bks], c1);
@@ -122,6 +125,68 @@ __device__ __forceinline__ void load_block(float *dst, int ld, const float *src,
 
 __device__ __forceinline__ void load_mat64(float *dst, const float *src) {
   load_block<64, 64>(dst, kL, src, 64);
+}
+
+// X = (I + diag(beta) S)^-1 for the strict-lower S ([64][64], stride kL),
+// rows and columns >= C zero, into sX (stride kL); the whole workgroup
+// (4 waves) calls it between barriers.  The four 16x16 diagonal blocks by
+// forward substitution (wave 0, one lane per column), then the blocks below
+// the diagonal as X_ij = -X_ii sum_{k=j}^{i-1} L_ik X_kj on fp32 MFMA, one
+// block per wave and diagonal distance; the sum waits in the upper block
+// (j, i) of sX, which X never uses.
+__device__ __forceinline__ void unit_lower_inverse(const float *sS, const float *sB, float *sX,
+                                                   int C) {
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
+  for (int idx = tid; idx < 4096; idx += 256) sX[(idx >> 6) * kL + (idx & 63)] = 0.f;
+  __syncthreads();
+  if (w == 0) {
+    const int blk = l >> 4, c = l & 15;
+    float xd[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int rr = 16 * blk + r;
+      float acc = r == c ? 1.f : 0.f;
+#pragma unroll
+      for (int s = 0; s < r; ++s) acc -= sB[rr] * sS[rr * kL + 16 * blk + s] * xd[s];
+      xd[r] = acc;
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sX[(16 * blk + r) * kL + 16 * blk + c] = xd[r];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int dist = 1; dist < 4; ++dist) {
+    const int j = w, i = w + dist;
+    if (i < 4) {
+      f32x4 y = zero4();
+      for (int kb = j; kb < i; ++kb)
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+          const int row = 16 * i + lr;
+          const float a = sB[row] * sS[row * kL + 16 * kb + k0 + lg];
+          const float b = sX[(16 * kb + k0 + lg) * kL + 16 * j + lr];
+          y = mfma4(a, b, y);
+        }
+      float *Y = sX + (16 * j) * kL + 16 * i;  // upper block (j, i)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Y[(lg * 4 + e) * kL + lr] = y[e];
+      __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      f32x4 x = zero4();
+#pragma unroll
+      for (int k0 = 0; k0 < 16; k0 += 4)
+        x = mfma4(sX[(16 * i + lr) * kL + 16 * i + k0 + lg], Y[(k0 + lg) * kL + lr], x);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sX[(16 * i + lg * 4 + e) * kL + 16 * j + lr] = -x[e];
+    }
+    __syncthreads();
+  }
+  // clear the scratch blocks and the rows / columns past the chunk
+  for (int idx = tid; idx < 4096; idx += 256) {
+    const int r = idx >> 6, c = idx & 63;
+    if (c > r || r >= C || c >= C) sX[r * kL + c] = 0.f;
+  }
+  __syncthreads();
 }
 
 }  // namespace bwd

@@ -21,7 +21,7 @@
 //
 // Four launches after the forward recompute (map + reduce storing every
 // chunk's entering state H): prep (per chunk slot and head: A^-1, M, S and the
-// gate vectors, fp32), dh (per sequence, head and 32 state columns, chunks in
+// gate vectors, fp32; A^-1 by 16x16 blocks), dh (per sequence, head and 32 state columns, chunks in
 // reverse: the dH recurrence, storing dH' of every chunk and dh0), part (per
 // slot and head: dV and the d_v-contracted products dOb H^T, dX H^T,
 // U dH'^T, dM, dT and <dH', H>) and final (per slot and head: the chunk-local
@@ -59,8 +59,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   // S = strict_lower(K K^T * E), M = lower_incl(Q K^T * E): wave w, rows 16w
   f32x4 aS[4] = {zero4(), zero4(), zero4(), zero4()};
   f32x4 aM[4] = {zero4(), zero4(), zero4(), zero4()};
-  mmN<4>(aS, sK + 16 * w * LK, LK, 1, sK, 1, LK, 16 * LK, DK);
-  mmN<4>(aM, sQ + 16 * w * LK, LK, 1, sK, 1, LK, 16 * LK, DK);
+  mmN<4, DK>(aS, sK + 16 * w * LK, LK, 1, sK, 1, LK, 16 * LK);
+  mmN<4, DK>(aM, sQ + 16 * w * LK, LK, 1, sK, 1, LK, 16 * LK);
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) {
     const f32x4 as = aS[s4], am = aM[s4];
@@ -76,18 +76,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
     }
   }
   __syncthreads();
-  // A^-1 (unit lower) by forward substitution, one column per lane of wave 0:
-  // X_rc = -sum_{s=c}^{r-1} beta_r S_rs X_sc
-  if (tid < 64) {
-    const int c = tid;
-    for (int r = 0; r < 64; ++r) sX[r * kL + c] = (r == c && r < C) ? 1.f : 0.f;
-    for (int r = c + 1; r < C; ++r) {
-      float acc = 0.f;
-      for (int s = c; s < r; ++s) acc += sS[r * kL + s] * sX[s * kL + c];
-      sX[r * kL + c] = -sB[r] * acc;
-    }
-  }
-  __syncthreads();
+  // A^-1 = (I + diag(beta) S)^-1, by 16x16 blocks
+  unit_lower_inverse(sS, sB, sX, C);
   for (int idx = tid; idx < 64 * 64; idx += 256) img[kPrepA + idx] = sX[(idx >> 6) * kL + (idx & 63)];
   if (tid < 64) {
     const float Gc = sG[C - 1];
@@ -157,8 +147,8 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdParams p) {
     // dU = M^T dOb + fac * (K dH'), rows 16w
     {
       f32x4 kd[2] = {zero4(), zero4()}, du[2] = {zero4(), zero4()};
-      mmN<2>(kd, sK + 16 * w * LK, LK, 1, sD, LC, 1, 16, DK);
-      mmN<2>(du, sM + 16 * w, 1, kL, sO, LC, 1, 16, 64);
+      mmN<2, DK>(kd, sK + 16 * w * LK, LK, 1, sD, LC, 1, 16);
+      mmN<2, 64>(du, sM + 16 * w, 1, kL, sO, LC, 1, 16);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -171,7 +161,7 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdParams p) {
     // dX = beta * (A^-T dU); Y = gam * dX
     {
       f32x4 dx[2] = {zero4(), zero4()};
-      mmN<2>(dx, sA + 16 * w, 1, kL, sU, LC, 1, 16, 64);
+      mmN<2, 64>(dx, sA + 16 * w, 1, kL, sU, LC, 1, 16);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -189,8 +179,8 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdParams p) {
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) acc[nt][i] = gamC * sD[(16 * t + 4 * lg + i) * LC + 16 * nt + lr];
-      mmN<2>(acc, sQ + 16 * t, 1, LK, sGO, LC, 1, 16, 64);
-      mmN<2>(ky, sK + 16 * t, 1, LK, sY, LC, 1, 16, 64);
+      mmN<2, 64>(acc, sQ + 16 * t, 1, LK, sGO, LC, 1, 16);
+      mmN<2, 64>(ky, sK + 16 * t, 1, LK, sY, LC, 1, 16);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -256,9 +246,9 @@ __global__ __launch_bounds__(256) void bwd_part_kernel(BwdParams p) {
     __syncthreads();
     {
       f32x4 khd[2] = {zero4(), zero4()};  // K H and K dH'
-      mmN<2>(khd, sK + 16 * w * LK, LK, 1, sHD, LB, 1, DK * LB, DK);
+      mmN<2, DK>(khd, sK + 16 * w * LK, LK, 1, sHD, LB, 1, DK * LB);
       const f32x4 kh = khd[0], kd = khd[1];
-      const f32x4 mo = mm2k(sM + 16 * w, 1, kL, sO, LB, 1, 64);
+      const f32x4 mo = mm2k<64>(sM + 16 * w, 1, kL, sO, LB, 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
@@ -270,8 +260,8 @@ __global__ __launch_bounds__(256) void bwd_part_kernel(BwdParams p) {
     }
     __syncthreads();
     {
-      const f32x4 u = mm2k(sA + 16 * w * kL, kL, 1, sBX, LB, 1, 64);
-      const f32x4 dx = mm2k(sA + 16 * w, 1, kL, sDU, LB, 1, 64);
+      const f32x4 u = mm2k<64>(sA + 16 * w * kL, kL, 1, sBX, LB, 1);
+      const f32x4 dx = mm2k<64>(sA + 16 * w, 1, kL, sDU, LB, 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
@@ -282,11 +272,11 @@ __global__ __launch_bounds__(256) void bwd_part_kernel(BwdParams p) {
       }
     }
     __syncthreads();
-    mmN<NT>(P1, sO + 16 * w * LB, LB, 1, sH, 1, LB, 16 * LB, 16);
-    mmN<NT>(P2, sDX + 16 * w * LB, LB, 1, sH, 1, LB, 16 * LB, 16);
-    mmN<NT>(P3, sU + 16 * w * LB, LB, 1, sDH, 1, LB, 16 * LB, 16);
-    mmN<4>(dM, sO + 16 * w * LB, LB, 1, sU, 1, LB, 16 * LB, 16);
-    mmN<4>(dT, sDU + 16 * w * LB, LB, 1, sX, 1, LB, 16 * LB, 16);
+    mmN<NT, 16>(P1, sO + 16 * w * LB, LB, 1, sH, 1, LB, 16 * LB);
+    mmN<NT, 16>(P2, sDX + 16 * w * LB, LB, 1, sH, 1, LB, 16 * LB);
+    mmN<NT, 16>(P3, sU + 16 * w * LB, LB, 1, sDH, 1, LB, 16 * LB);
+    mmN<4, 16>(dM, sO + 16 * w * LB, LB, 1, sU, 1, LB, 16 * LB);
+    mmN<4, 16>(dT, sDU + 16 * w * LB, LB, 1, sX, 1, LB, 16 * LB);
   }
   float *gw = p.part + (size_t)blockIdx.x * part_floats(DK);
 #pragma unroll
@@ -375,7 +365,7 @@ __global__ __launch_bounds__(256) void bwd_final_kernel(BwdParams p) {
   // tmp = dA^-1 A^-T
   {
     f32x4 t[4] = {zero4(), zero4(), zero4(), zero4()};
-    mmN<4>(t, sDT + 16 * w * kL, kL, 1, sA, 1, kL, 16 * kL, 64);
+    mmN<4, 64>(t, sDT + 16 * w * kL, kL, 1, sA, 1, kL, 16 * kL);
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
@@ -385,7 +375,7 @@ __global__ __launch_bounds__(256) void bwd_final_kernel(BwdParams p) {
   // dA = -A^-T tmp; strict lower part: W = dA S (beta), Y = beta dA S (gates),
   // F = beta dA E (keys)
   f32x4 tA[4] = {zero4(), zero4(), zero4(), zero4()};
-  mmN<4>(tA, sA + 16 * w, 1, kL, sTmp, kL, 1, 16, 64);
+  mmN<4, 64>(tA, sA + 16 * w, 1, kL, sTmp, kL, 1, 16);
 #pragma unroll
   for (int s4 = 0; s4 < 4; ++s4) {
     const f32x4 t = tA[s4];
@@ -455,10 +445,10 @@ __global__ __launch_bounds__(256) void bwd_final_kernel(BwdParams p) {
   f32x4 dq[NT], dk[NT];
 #pragma unroll
   for (int t = 0; t < NT; ++t) dq[t] = dk[t] = zero4();
-  mmN<NT>(dq, sDM + 16 * w * kL, kL, 1, sK, LK, 1, 16, 64);
-  mmN<NT>(dk, sDM + 16 * w, 1, kL, sQ, LK, 1, 16, 64);
-  mmN<NT>(dk, sDT + 16 * w * kL, kL, 1, sK, LK, 1, 16, 64);
-  mmN<NT>(dk, sDT + 16 * w, 1, kL, sK, LK, 1, 16, 64);
+  mmN<NT, 64>(dq, sDM + 16 * w * kL, kL, 1, sK, LK, 1, 16);
+  mmN<NT, 64>(dk, sDM + 16 * w, 1, kL, sQ, LK, 1, 16);
+  mmN<NT, 64>(dk, sDT + 16 * w * kL, kL, 1, sK, LK, 1, 16);
+  mmN<NT, 64>(dk, sDT + 16 * w, 1, kL, sK, LK, 1, 16);
 #pragma unroll
   for (int t = 0; t < NT; ++t)
 #pragma unroll

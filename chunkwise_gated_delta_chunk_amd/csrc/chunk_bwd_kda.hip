@@ -116,16 +116,7 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(BwdParams p) {
     img[kPrepM + pr] = am;
   }
   __syncthreads();
-  if (tid < 64) {
-    const int c = tid;
-    for (int r = 0; r < 64; ++r) sX[r * kL + c] = (r == c && r < C) ? 1.f : 0.f;
-    for (int r = c + 1; r < C; ++r) {
-      float acc = 0.f;
-      for (int s = c; s < r; ++s) acc += sS[r * kL + s] * sX[s * kL + c];
-      sX[r * kL + c] = -sB[r] * acc;
-    }
-  }
-  __syncthreads();
+  unit_lower_inverse(sS, sB, sX, C);
   for (int idx = tid; idx < 4096; idx += 256) img[kPrepA + idx] = sX[(idx >> 6) * kL + (idx & 63)];
   if (tid < 64) img[kKdaBeta + tid] = sB[tid];
   for (int idx = tid; idx < 64 * DK; idx += 256) img[kKdaG + idx] = sG[(idx / DK) * LK + idx % DK];
@@ -179,8 +170,8 @@ __global__ __launch_bounds__(256) void kda_dh_kernel(BwdParams p) {
     __syncthreads();
     {  // dU = M^T dOb + Kh dH'
       f32x4 kd[2] = {zero4(), zero4()};
-      mmN<2>(kd, sK + 16 * w * LK, LK, 1, sD, LC, 1, 16, DK);
-      mmN<2>(kd, sM + 16 * w, 1, kL, sO, LC, 1, 16, 64);
+      mmN<2, DK>(kd, sK + 16 * w * LK, LK, 1, sD, LC, 1, 16);
+      mmN<2, 64>(kd, sM + 16 * w, 1, kL, sO, LC, 1, 16);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -189,7 +180,7 @@ __global__ __launch_bounds__(256) void kda_dh_kernel(BwdParams p) {
     __syncthreads();
     {  // dX = beta (A^-T dU); Kt replaces Kh meanwhile
       f32x4 dx[2] = {zero4(), zero4()};
-      mmN<2>(dx, sA + 16 * w, 1, kL, sU, LC, 1, 16, 64);
+      mmN<2, 64>(dx, sA + 16 * w, 1, kL, sU, LC, 1, 16);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -211,8 +202,8 @@ __global__ __launch_bounds__(256) void kda_dh_kernel(BwdParams p) {
           const int row = 16 * t + 4 * lg + i;
           acc[nt][i] = sGC[row] * sD[row * LC + 16 * nt + lr];
         }
-      mmN<2>(acc, sQ + 16 * t, 1, LK, sO, LC, 1, 16, 64);
-      mmN<2>(ky, sK + 16 * t, 1, LK, sY, LC, 1, 16, 64);
+      mmN<2, 64>(acc, sQ + 16 * t, 1, LK, sO, LC, 1, 16);
+      mmN<2, 64>(ky, sK + 16 * t, 1, LK, sY, LC, 1, 16);
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt)
 #pragma unroll
@@ -273,9 +264,9 @@ __global__ __launch_bounds__(256) void kda_part_kernel(BwdParams p) {
     __syncthreads();
     {
       f32x4 kh[1] = {zero4()}, kd[1] = {zero4()};
-      mmN<1>(kh, sKt + 16 * w * LK, LK, 1, sH, LB, 1, 0, DK);
-      mmN<1>(kd, sKh + 16 * w * LK, LK, 1, sDH, LB, 1, 0, DK);
-      const f32x4 mo = mm2k(sM + 16 * w, 1, kL, sO, LB, 1, 64);
+      mmN<1, DK>(kh, sKt + 16 * w * LK, LK, 1, sH, LB, 1, 0);
+      mmN<1, DK>(kd, sKh + 16 * w * LK, LK, 1, sDH, LB, 1, 0);
+      const f32x4 mo = mm2k<64>(sM + 16 * w, 1, kL, sO, LB, 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
@@ -287,8 +278,8 @@ __global__ __launch_bounds__(256) void kda_part_kernel(BwdParams p) {
     }
     __syncthreads();
     {
-      const f32x4 u = mm2k(sA + 16 * w * kL, kL, 1, sBX, LB, 1, 64);
-      const f32x4 dx = mm2k(sA + 16 * w, 1, kL, sDU, LB, 1, 64);
+      const f32x4 u = mm2k<64>(sA + 16 * w * kL, kL, 1, sBX, LB, 1);
+      const f32x4 dx = mm2k<64>(sA + 16 * w, 1, kL, sDU, LB, 1);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
@@ -299,11 +290,11 @@ __global__ __launch_bounds__(256) void kda_part_kernel(BwdParams p) {
       }
     }
     __syncthreads();
-    mmN<NT>(P1, sO + 16 * w * LB, LB, 1, sH, 1, LB, 16 * LB, 16);
-    mmN<NT>(P2, sDX + 16 * w * LB, LB, 1, sH, 1, LB, 16 * LB, 16);
-    mmN<NT>(P3, sU + 16 * w * LB, LB, 1, sDH, 1, LB, 16 * LB, 16);
-    mmN<4>(dM, sO + 16 * w * LB, LB, 1, sU, 1, LB, 16 * LB, 16);
-    mmN<4>(dT, sDU + 16 * w * LB, LB, 1, sX, 1, LB, 16 * LB, 16);
+    mmN<NT, 16>(P1, sO + 16 * w * LB, LB, 1, sH, 1, LB, 16 * LB);
+    mmN<NT, 16>(P2, sDX + 16 * w * LB, LB, 1, sH, 1, LB, 16 * LB);
+    mmN<NT, 16>(P3, sU + 16 * w * LB, LB, 1, sDH, 1, LB, 16 * LB);
+    mmN<4, 16>(dM, sO + 16 * w * LB, LB, 1, sU, 1, LB, 16 * LB);
+    mmN<4, 16>(dT, sDU + 16 * w * LB, LB, 1, sX, 1, LB, 16 * LB);
   }
   float *gw = p.part + (size_t)blockIdx.x * part_floats(DK);
 #pragma unroll
@@ -371,7 +362,7 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
   __syncthreads();
   {
     f32x4 t[4] = {zero4(), zero4(), zero4(), zero4()};
-    mmN<4>(t, sDAi + 16 * w * kL, kL, 1, sA, 1, kL, 16 * kL, 64);
+    mmN<4, 64>(t, sDAi + 16 * w * kL, kL, 1, sA, 1, kL, 16 * kL);
     __syncthreads();  // every wave is done reading sTmp's column sums above
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
@@ -381,7 +372,7 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
   __syncthreads();
   {
     f32x4 tA[4] = {zero4(), zero4(), zero4(), zero4()};
-    mmN<4>(tA, sA + 16 * w, 1, kL, sTmp, kL, 1, 16, 64);
+    mmN<4, 64>(tA, sA + 16 * w, 1, kL, sTmp, kL, 1, 16);
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
 #pragma unroll
