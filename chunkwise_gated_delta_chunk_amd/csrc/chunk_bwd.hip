@@ -409,19 +409,48 @@ __global__ __launch_bounds__(256) void bwd_final_kernel(BwdParams p) {
   load_rows<In, DK>(sQ, LK, p.q, r0, C, H, h);
   __syncthreads();
   const float *P1 = gw + kPartP1, *P2 = gw + part_p2(DK), *P3 = gw + part_p3(DK);
-  // gates: per row, with the dot products of q / k with P1, P2, P3
-  if (tid < 64) {
-    const int r = tid;
-    float q1 = 0.f, k2 = 0.f, k3 = 0.f;
-    for (int i = 0; i < DK; ++i) {
-      q1 += sQ[r * LK + i] * P1[r * DK + i];
-      k2 += sK[r * LK + i] * P2[r * DK + i];
-      k3 += sK[r * LK + i] * P3[r * DK + i];
+  // dQ = gam P1 + (dM E) K;  dK = -gam P2 + fac P3 + (dM E)^T Q + F K + F^T K,
+  // and the gate dot products <q_r, P1_r>, <k_r, P2_r>, <k_r, P3_r> from the
+  // same P reads: per lane over its columns, then over the 16 lanes of a row
+  f32x4 dq[NT], dk[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) dq[t] = dk[t] = zero4();
+  mmN<NT, 64>(dq, sDM + 16 * w * kL, kL, 1, sK, LK, 1, 16);
+  mmN<NT, 64>(dk, sDM + 16 * w, 1, kL, sQ, LK, 1, 16);
+  mmN<NT, 64>(dk, sDT + 16 * w * kL, kL, 1, sK, LK, 1, 16);
+  mmN<NT, 64>(dk, sDT + 16 * w, 1, kL, sK, LK, 1, 16);
+  float q1[4] = {0.f, 0.f, 0.f, 0.f}, k2[4] = {0.f, 0.f, 0.f, 0.f}, k3[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * lg + i, c = 16 * t + lr;
+      const float p1 = P1[r * DK + c], p2 = P2[r * DK + c], p3 = P3[r * DK + c];
+      q1[i] += sQ[r * LK + c] * p1;
+      k2[i] += sK[r * LK + c] * p2;
+      k3[i] += sK[r * LK + c] * p3;
+      if (r < C) {
+        const size_t o = ((size_t)(r0 + r) * H + h) * DK + c;
+        p.dq[o] = sGam[r] * p1 + dq[t][i];
+        p.dk[o] = -sGam[r] * p2 + sFac[r] * p3 + dk[t][i];
+      }
     }
-    const float t3 = sFac[r] * k3;
-    dG[r] = r < C ? sGam[r] * (q1 - k2) - t3 + zr[r] - zc[r] + yr[r] - yc[r] : 0.f;
-    t3s[r] = r < C ? t3 : 0.f;
-  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+      q1[i] += __shfl_xor(q1[i], m, 64);
+      k2[i] += __shfl_xor(k2[i], m, 64);
+      k3[i] += __shfl_xor(k3[i], m, 64);
+    }
+  if (lr == 0)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * lg + i;
+      const float t3 = sFac[r] * k3[i];
+      dG[r] = r < C ? sGam[r] * (q1[i] - k2[i]) - t3 + zr[r] - zc[r] + yr[r] - yc[r] : 0.f;
+      t3s[r] = r < C ? t3 : 0.f;
+    }
   __syncthreads();
   if (tid == 0) {
     float dGc = 0.f;
@@ -441,25 +470,6 @@ __global__ __launch_bounds__(256) void bwd_final_kernel(BwdParams p) {
     p.dg[o] = dG[tid];
     p.dbeta[o] = bt[tid] + ba[tid];
   }
-  // dQ = gam P1 + (dM E) K;  dK = -gam P2 + fac P3 + (dM E)^T Q + F K + F^T K
-  f32x4 dq[NT], dk[NT];
-#pragma unroll
-  for (int t = 0; t < NT; ++t) dq[t] = dk[t] = zero4();
-  mmN<NT, 64>(dq, sDM + 16 * w * kL, kL, 1, sK, LK, 1, 16);
-  mmN<NT, 64>(dk, sDM + 16 * w, 1, kL, sQ, LK, 1, 16);
-  mmN<NT, 64>(dk, sDT + 16 * w * kL, kL, 1, sK, LK, 1, 16);
-  mmN<NT, 64>(dk, sDT + 16 * w, 1, kL, sK, LK, 1, 16);
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + 4 * lg + i, c = 16 * t + lr;
-      if (r < C) {
-        const size_t o = ((size_t)(r0 + r) * H + h) * DK + c;
-        p.dq[o] = sGam[r] * P1[r * DK + c] + dq[t][i];
-        p.dk[o] = -sGam[r] * P2[r * DK + c] + sFac[r] * P3[r * DK + c] + dk[t][i];
-      }
-    }
 }
 
 template <typename In, int DK>

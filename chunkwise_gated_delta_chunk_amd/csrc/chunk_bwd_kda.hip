@@ -402,40 +402,45 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
   }
   const float *P1 = gw + kPartP1, *P2 = gw + part_p2(DK), *P3 = gw + part_p3(DK);
   const float *shv = gw + part_sh(DK);
-  // one channel per thread (DK of them), all rows: the E-weighted sums, the
-  // gradients, and the reverse cumulative sum of dG down the rows
+  // (row, channel) pairs over all threads, a wave's lanes on consecutive
+  // channels of one row: the E-weighted sums, dq, dk and each row's dG
+  for (int pr = tid; pr < 64 * DK; pr += 256) {
+    const int x = pr / DK, i = pr % DK;
+    if (x >= C) continue;
+    const float Gx = sG[x * LK + i], qx = sQ[x * LK + i], kx = sK[x * LK + i];
+    const float GCi = sG[(C - 1) * LK + i];
+    float f1 = 0.f, f2 = 0.f, f3 = 0.f, f4 = 0.f;
+    for (int s = 0; s <= x; ++s) {  // E_xs = exp(G_x - G_s), s <= x
+      const float e = __expf(Gx - sG[s * LK + i]) * sK[s * LK + i];
+      f1 += sDM[x * kL + s] * e;
+      f3 += sDS[x * kL + s] * e;
+    }
+    for (int r = x; r < C; ++r) {  // E_rx = exp(G_r - G_x), r >= x
+      const float e = __expf(sG[r * LK + i] - Gx);
+      f2 += sDM[r * kL + x] * sQ[r * LK + i] * e;
+      f4 += sDS[r * kL + x] * sK[r * LK + i] * e;
+    }
+    const float gam = __expf(Gx), kh = __expf(GCi - Gx);
+    const float p1 = P1[x * DK + i], p2 = P2[x * DK + i], p3 = P3[x * DK + i];
+    const size_t o = ((size_t)(r0 + x) * H + h) * DK + i;
+    p.dq[o] = gam * p1 + f1;
+    p.dk[o] = -gam * p2 + kh * p3 + f2 + f3 + f4;
+    p.dg[o] = gam * qx * p1 - gam * kx * p2 - kh * kx * p3 + qx * f1 - kx * f2 + kx * f3 - kx * f4;
+  }
+  __syncthreads();  // every row's dG is in dg
+  // per channel: the last-row terms (sum_r Kh P3 and exp(G_C) <dH', H>)
+  // belong to G_{C-1}, which every row's cumulative sum includes; then dg is
+  // the reverse cumulative sum down the rows
   for (int i = tid; i < DK; i += 256) {
     const float GCi = sG[(C - 1) * LK + i];
+    float extra = __expf(GCi) * shv[i];
+    for (int x = 0; x < C; ++x) extra += __expf(GCi - sG[x * LK + i]) * sK[x * LK + i] * P3[x * DK + i];
     float run = 0.f;
-    float dGlast = 0.f;
-    for (int x = 63; x >= 0; --x) {
-      if (x >= C) continue;
-      const float Gx = sG[x * LK + i], qx = sQ[x * LK + i], kx = sK[x * LK + i];
-      float f1 = 0.f, f2 = 0.f, f3 = 0.f, f4 = 0.f;
-      for (int s = 0; s <= x; ++s) {  // E_xs = exp(G_x - G_s), s <= x
-        const float e = __expf(Gx - sG[s * LK + i]) * sK[s * LK + i];
-        f1 += sDM[x * kL + s] * e;
-        f3 += sDS[x * kL + s] * e;
-      }
-      for (int r = x; r < C; ++r) {  // E_rx = exp(G_r - G_x), r >= x
-        const float e = __expf(sG[r * LK + i] - Gx);
-        f2 += sDM[r * kL + x] * sQ[r * LK + i] * e;
-        f4 += sDS[r * kL + x] * sK[r * LK + i] * e;
-      }
-      const float gam = __expf(Gx), kh = __expf(GCi - Gx);
-      const float p1 = P1[x * DK + i], p2 = P2[x * DK + i], p3 = P3[x * DK + i];
+    for (int x = C - 1; x >= 0; --x) {
       const size_t o = ((size_t)(r0 + x) * H + h) * DK + i;
-      p.dq[o] = gam * p1 + f1;
-      p.dk[o] = -gam * p2 + kh * p3 + f2 + f3 + f4;
-      float dG = gam * qx * p1 - gam * kx * p2 - kh * kx * p3 + qx * f1 - kx * f2 + kx * f3 - kx * f4;
-      dGlast += kh * kx * p3;
-      run += dG;
-      p.dg[o] = run;
+      run += p.dg[o];
+      p.dg[o] = run + extra;
     }
-    // last-row terms (sum_r Kh P3 and exp(G_C) <dH', H>) belong to G_{C-1},
-    // which every row's cumulative sum includes: add them to all C rows
-    const float extra = dGlast + __expf(GCi) * shv[i];
-    for (int x = 0; x < C; ++x) p.dg[((size_t)(r0 + x) * H + h) * DK + i] += extra;
   }
 }
 
