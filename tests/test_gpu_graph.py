@@ -167,3 +167,124 @@ def test_small_bucket_graph_layouts_with_state(kda):
             first = False
         o_g, ht_g = _check_replay(b, inp, heads=None, label=f"layout {i} kda={kda}")
         assert np.isfinite(o_g.cpu().numpy()[:total]).all()
+
+
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+def test_backward_graph_replays_over_layouts(kda):
+    """The chunk backward under the same contract: metadata and backward
+    captured once on static buffers, replayed over fresh layouts and inputs
+    copied in; every replay equals an eager call on the same buffers bit for
+    bit (rows of real tokens, dh0 of non-empty sequences)."""
+    T_max, N_max, H, d = 1024, 6, 2, 64
+    dev = torch.device("cuda")
+    bf = torch.bfloat16
+    q = torch.zeros((T_max, H, d), dtype=bf, device=dev)
+    k, v = torch.zeros_like(q), torch.zeros_like(q)
+    g = torch.zeros((T_max, H, d) if kda else (T_max, H), device=dev)
+    beta = torch.zeros((T_max, H), device=dev)
+    cu = torch.zeros((N_max + 1,), dtype=torch.int32, device=dev)
+    NT = la.nt_max(T_max, N_max)
+    ci = torch.empty((NT, 2), dtype=torch.int32, device=dev)
+    co = torch.empty((N_max + 1,), dtype=torch.int32, device=dev)
+    h0 = torch.zeros((N_max, H, d, d), device=dev)
+    dout = torch.zeros((T_max, H, d), device=dev)
+    outs = dict(dq=torch.zeros((T_max, H, d), device=dev), dk=torch.zeros((T_max, H, d), device=dev),
+                dv=torch.zeros((T_max, H, d), device=dev), dg=torch.zeros(g.shape, device=dev),
+                dbeta=torch.zeros((T_max, H), device=dev), dh0=torch.zeros_like(h0))
+    ws = torch.empty((la.bwd_workspace_bytes(T_max, N_max, H, d, d, bf, kda=kda),),
+                     dtype=torch.uint8, device=dev)
+    fn = la.kda_chunk_bwd if kda else la.gdn_chunk_bwd
+
+    def step():
+        la.build_chunk_meta(cu, T_max, chunk_indices=ci, chunk_offsets=co)
+        fn(q, k, v, g, beta, cu, ci, co, dout, h0=h0, workspace=ws, **outs)
+
+    def fill(seed):
+        rng = np.random.default_rng(seed)
+        lay = bucket_layout(rng, T_max, N_max)
+        inp = make_inputs(T_max, H, d, d, kda=kda, dtype="bf16", seed=seed, cu_seqlens=lay,
+                          h0_std=0.1)
+        q.copy_(torch.from_numpy(inp["q"]).to(bf))
+        k.copy_(torch.from_numpy(inp["k"]).to(bf))
+        v.copy_(torch.from_numpy(inp["v"]).to(bf))
+        g.copy_(torch.from_numpy(inp["g"]))
+        beta.copy_(torch.from_numpy(inp["beta"]))
+        cu.copy_(torch.from_numpy(lay.astype(np.int32)))
+        h0.copy_(torch.from_numpy(inp["h0"]))
+        dout.copy_(torch.from_numpy(rng.standard_normal((T_max, H, d)).astype(np.float32)))
+        return lay
+
+    fill(900)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for r in range(4):
+        lay = fill(901 + r)
+        step()
+        torch.cuda.synchronize()
+        eager = {key: t.clone() for key, t in outs.items()}
+        graph.replay()
+        torch.cuda.synchronize()
+        rows = int(lay[-1])
+        ne = torch.from_numpy(np.diff(lay) > 0)
+        for key in ("dq", "dk", "dv", "dg", "dbeta"):
+            assert torch.equal(outs[key][:rows], eager[key][:rows]), (r, key)
+        assert torch.equal(outs["dh0"][ne], eager["dh0"][ne]), r
+        _say(f"backward graph replay {r}: {int((np.diff(lay) > 0).sum())} sequences, {rows} tokens")
+
+
+def test_short_conv_graph_replays_over_layouts():
+    """The short convolution captured once with the metadata and replayed over
+    fresh layouts, states updated in place: each replay equals an eager call."""
+    T_max, N_max, D, W = 1024, 6, 512, 4
+    dev = torch.device("cuda")
+    bf = torch.bfloat16
+    x = torch.zeros((T_max, D), dtype=bf, device=dev)
+    w = torch.zeros((D, W), device=dev)
+    b = torch.zeros((D,), device=dev)
+    cu = torch.zeros((N_max + 1,), dtype=torch.int32, device=dev)
+    NT = la.nt_max(T_max, N_max)
+    ci = torch.empty((NT, 2), dtype=torch.int32, device=dev)
+    co = torch.empty((N_max + 1,), dtype=torch.int32, device=dev)
+    state = torch.zeros((N_max, W - 1, D), dtype=bf, device=dev)
+    y = torch.zeros((T_max, D), dtype=bf, device=dev)
+
+    def step():
+        la.build_chunk_meta(cu, T_max, chunk_indices=ci, chunk_offsets=co)
+        la.short_conv_fwd(x, w, cu, ci, bias=b, h0=state, ht=state, y=y, activation="silu")
+
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        step()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    from synth import make_conv_inputs
+    for r in range(4):
+        rng = np.random.default_rng(950 + r)
+        lay = bucket_layout(rng, T_max, N_max)
+        inp = make_conv_inputs(T_max, D, W, dtype="bf16", seed=950 + r, cu_seqlens=lay, h0=True)
+        x.copy_(torch.from_numpy(inp["x"]).to(bf))
+        w.copy_(torch.from_numpy(inp["weight"]))
+        b.copy_(torch.from_numpy(inp["bias"]))
+        cu.copy_(torch.from_numpy(lay.astype(np.int32)))
+        s0 = torch.from_numpy(inp["h0"]).to(dev, bf)
+        state.copy_(s0)
+        step()
+        torch.cuda.synchronize()
+        ey, es = y.clone(), state.clone()
+        state.copy_(s0)
+        graph.replay()
+        torch.cuda.synchronize()
+        rows = int(lay[-1])
+        ne = torch.from_numpy(np.diff(lay) > 0)
+        assert torch.equal(y[:rows], ey[:rows]) and torch.equal(state[ne], es[ne]), r
