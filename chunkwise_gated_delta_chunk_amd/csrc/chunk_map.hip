@@ -68,11 +68,11 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   constexpr int KSTEP = 4 * O::KPL;  // k per MFMA
   constexpr int KQ_BYTES = 2 * kBT * LDK * (int)sizeof(T);
   constexpr int LX_BYTES = 2 * kBT * LDL * (int)sizeof(float);
-  // GDN: K and Q are dead once the products are formed, and A / A^-1 take
-  // their bytes.  KDA keeps both (K and Q are read until M is complete).
-  constexpr int AREA = KDA ? KQ_BYTES : (KQ_BYTES > LX_BYTES ? KQ_BYTES : LX_BYTES);
+  // K and Q are dead once the products are formed, and A / A^-1 take their
+  // bytes (KDA: every wave holds its tiles of A and M in registers until all
+  // waves are done reading K and Q)
+  constexpr int AREA = KQ_BYTES > LX_BYTES ? KQ_BYTES : LX_BYTES;
   __shared__ __attribute__((aligned(16))) char sArea[AREA];
-  __shared__ __attribute__((aligned(16))) char sLXk[KDA ? LX_BYTES : 16];
   __shared__ float sY[4][16 * 17];    // per-wave 16x16 scratch
   __shared__ float sB[kBT];
   __shared__ float sg[kBT];
@@ -83,7 +83,7 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   constexpr int LDM = kBT + O::PAD;  // M, natural column order, before the write-out
   T *sK = reinterpret_cast<T *>(sArea);
   T *sQ = sK + kBT * LDK;
-  float *sL = KDA ? reinterpret_cast<float *>(sLXk) : reinterpret_cast<float *>(sArea);
+  float *sL = reinterpret_cast<float *>(sArea);
   float *sX = sL + kBT * LDL;
   // M waits for its write-out in the bytes of X, which the inverse fills
   // only after it
@@ -369,7 +369,11 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
     // both factors <= 1 when g <= 0.  Each lane forms its row's KPL channels
     // of both factors in registers (lane row r = b + lr for the A operands,
     // s = 16S + lr for the B operand) and feeds them to the MFMAs.
-    for (int t = w; t < 6; t += 4) {
+    f32x4 oca[2], ocm[2];  // this wave's off-diagonal tiles, written after the barrier
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      const int t = w + 4 * ti;
+      if (t >= 6) break;
       const int R = t < 1 ? 1 : t < 3 ? 2 : 3, S = t - R * (R - 1) / 2;
       const int b = 16 * R, r = b + lr, s = 16 * S + lr;
       f32x4 ca = zero4(), cm = zero4();
@@ -402,12 +406,8 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
         ca = O::mfma(af, hf, ca);
         cm = O::mfma(qf, hf, cm);
       }
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int rr = b + lg * 4 + e;
-        sL[rr * LDL + s] = sB[rr] * ca[e];
-      }
-      store_m(R, S, cm);
+      oca[ti] = ca;
+      ocm[ti] = cm;
     }
     // diagonal blocks: wave w takes block w (rows b .. b+15).  The decay of
     // pair (r, s) factors through row b per channel,
@@ -416,6 +416,9 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
     // A value of row r and the B value of column r).  The second factor grows
     // with the block's decay: a block where some |G_rc - G_bc| exceeds 60 is
     // summed elementwise instead, so no factor leaves the fp32 range.
+    f32x4 dca = zero4(), dcm = zero4();  // this wave's diagonal block
+    float ea[4], em[4];                   // or its elementwise sums
+    bool diag_mfma;
     {
       const int b = 16 * w, r = b + lr;
       f32x4 ca = zero4(), cm = zero4();
@@ -431,16 +434,14 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
         ca = F32::mfma(kr * e1, hs, ca);
         cm = F32::mfma(qr * e1, hs, cm);
       }
-      const int s = b + lr;
-      if (__ballot(span > 60.f) == 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int rr = b + lg * 4 + e;
-          sL[rr * LDL + s] = s < rr ? sB[rr] * ca[e] : 0.f;
-          sMt[rr * LDM + s] = s <= rr ? (T)cm[e] : (T)0.f;
-        }
+      diag_mfma = __ballot(span > 60.f) == 0;
+      if (diag_mfma) {
+        dca = ca;
+        dcm = cm;
       } else {
-        for (int idx = lane; idx < 256; idx += 64) {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int idx = lane + 64 * q4;
           const int rr = b + (idx >> 4), ss = b + (idx & 15);
           float a = 0.f, m = 0.f;
           if (ss <= rr) {
@@ -451,8 +452,41 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
               m += (float)sQ[rr * LDK + c] * ks * e;
             }
           }
-          sL[rr * LDL + ss] = ss < rr ? sB[rr] * a : 0.f;
-          sMt[rr * LDM + ss] = (T)m;
+          ea[q4] = a;
+          em[q4] = m;
+        }
+      }
+    }
+    __syncthreads();  // K and Q are dead: A and M take their bytes
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti) {
+      const int t = w + 4 * ti;
+      if (t >= 6) break;
+      const int R = t < 1 ? 1 : t < 3 ? 2 : 3, S = t - R * (R - 1) / 2;
+      const int b = 16 * R, s = 16 * S + lr;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int rr = b + lg * 4 + e;
+        sL[rr * LDL + s] = sB[rr] * oca[ti][e];
+      }
+      store_m(R, S, ocm[ti]);
+    }
+    {
+      const int b = 16 * w, s = b + lr;
+      if (diag_mfma) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int rr = b + lg * 4 + e;
+          sL[rr * LDL + s] = s < rr ? sB[rr] * dca[e] : 0.f;
+          sMt[rr * LDM + s] = s <= rr ? (T)dcm[e] : (T)0.f;
+        }
+      } else {
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int idx = lane + 64 * q4;
+          const int rr = b + (idx >> 4), ss = b + (idx & 15);
+          sL[rr * LDL + ss] = ss < rr ? sB[rr] * ea[q4] : 0.f;
+          sMt[rr * LDM + ss] = (T)em[q4];
         }
       }
     }
