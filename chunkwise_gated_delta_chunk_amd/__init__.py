@@ -239,6 +239,7 @@ def _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, dv_split=0, BT=64, seg_len
 
 
 def workspace_bytes(T_max, N_max, H, d_k, d_v, qkv_dtype, kda=False, BT=64, seg_len=0):
+    """Forward workspace bytes (BT = 32 adds the rebuilt 64-row chunk layout)."""
     a = _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, BT=BT, seg_len=seg_len)
     return int(lib().la_chunk_fwd_workspace_bytes(ctypes.byref(a), int(kda)))
 
@@ -275,7 +276,7 @@ def _out(o, o_dtype, shape, dev):
 
 
 def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0, o, ht,
-             output_final_state, workspace, scale, dv_split, seg_len, o_dtype=None):
+             output_final_state, workspace, scale, dv_split, seg_len, o_dtype=None, BT=64):
     _qkv_dtype(q)
     H, H_qk = _heads(q, v, "T_max")
     T_max, _, d_k = q.shape
@@ -288,7 +289,7 @@ def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0
     _need(beta, "beta", torch.float32, (T_max, H), dev)
     _need_idx(cu_seqlens, dev)
     N_max = cu_seqlens.numel() - 1
-    NT = nt_max(T_max, N_max)
+    NT = nt_max(T_max, N_max, BT)
     _need(chunk_indices, "chunk_indices", torch.int32, (NT, 2), dev)
     _need(chunk_offsets, "chunk_offsets", torch.int32, (N_max + 1,), dev)
     st_shape = (N_max, H, d_k, d_v)
@@ -299,7 +300,7 @@ def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0
         ht = torch.empty(st_shape, dtype=torch.float32, device=dev)
     if ht is not None:
         _need(ht, "ht", torch.float32, st_shape, dev)
-    a = _shape_args(T_max, N_max, H, d_k, d_v, q.dtype, dv_split, seg_len=seg_len)
+    a = _shape_args(T_max, N_max, H, d_k, d_v, q.dtype, dv_split, BT=BT, seg_len=seg_len)
     a.H_qk = H_qk
     a.o_bf16 = int(o.dtype == torch.bfloat16)
     a.cu_seqlens_i64 = int(cu_seqlens.dtype == torch.int64)
@@ -322,10 +323,10 @@ def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0
 
 def _call(name, kda, stages, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, *,
           h0=None, o=None, ht=None, output_final_state=True, workspace=None, scale=1.0,
-          dv_split=0, seg_len=0, o_dtype=None, stream=None):
+          dv_split=0, seg_len=0, o_dtype=None, BT=64, stream=None):
     a, o, ht, workspace = _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices,
                                    chunk_offsets, h0, o, ht, output_final_state, workspace,
-                                   scale, dv_split, seg_len, o_dtype)
+                                   scale, dv_split, seg_len, o_dtype, BT)
     L = lib()
     s = _stream(stream)
     if stages is None:
@@ -489,7 +490,7 @@ def kda_chunk_bwd(*args, **kw):
 
 def _chunk_bwd(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, dout, *, h0=None,
                dht=None, scale=1.0, dq=None, dk=None, dv=None, dg=None, dbeta=None, dh0=None,
-               workspace=None, stream=None):
+               workspace=None, BT=64, stream=None):
     _qkv_dtype(q)
     T_max, H, d_k = q.shape
     d_v = v.shape[-1]
@@ -502,7 +503,7 @@ def _chunk_bwd(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, 
     _need(beta, "beta", torch.float32, (T_max, H), dev)
     _need_idx(cu_seqlens, dev)
     N_max = cu_seqlens.numel() - 1
-    NT = nt_max(T_max, N_max)
+    NT = nt_max(T_max, N_max, BT)
     _need(chunk_indices, "chunk_indices", torch.int32, (NT, 2), dev)
     _need(chunk_offsets, "chunk_offsets", torch.int32, (N_max + 1,), dev)
     _need(dout, "dout", torch.float32, (T_max, H, d_v), dev)
@@ -526,7 +527,7 @@ def _chunk_bwd(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, 
         dh0 = torch.empty(st_shape, dtype=torch.float32, device=dev)
     if dh0 is not None:
         _need(dh0, "dh0", torch.float32, st_shape, dev)
-    a = _bwd_shape(T_max, N_max, H, d_k, d_v, q.dtype)
+    a = _bwd_shape(T_max, N_max, H, d_k, d_v, q.dtype, BT)
     a.cu_seqlens_i64 = int(cu_seqlens.dtype == torch.int64)
     a.scale = float(scale)
     need = int(lib().la_chunk_bwd_workspace_bytes(ctypes.byref(a), int(kda)))

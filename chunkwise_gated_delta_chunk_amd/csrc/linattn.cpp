@@ -10,6 +10,9 @@
 namespace {
 
 constexpr int kBTSupported = 64;
+// rows per chunk of the chunk kernels; a caller's BT = 32 layout is rebuilt on
+// the device at this size (see meta_bytes)
+constexpr int kBTk = 64;
 constexpr int kCUs = 256;  // compute units of one MI355X
 
 bool known_dtype(int dt) { return dt == LA_BF16 || dt == LA_F16 || dt == LA_F32; }
@@ -27,7 +30,7 @@ int check_shape(const la_chunk_fwd_args *a) {
   if (a->o_bf16 != 0 && a->o_bf16 != 1) return LA_ERR_DTYPE;
   if (a->cu_seqlens_i64 != 0 && a->cu_seqlens_i64 != 1) return LA_ERR_DTYPE;
   if (a->H_qk < 0 || (a->H_qk > 0 && a->H % a->H_qk != 0)) return LA_ERR_SHAPE;
-  if (a->BT != kBTSupported) return LA_ERR_UNSUPPORTED;
+  if (a->BT != 32 && a->BT != 64) return LA_ERR_UNSUPPORTED;
   if (a->d_k != a->d_v) return LA_ERR_UNSUPPORTED;
   if (a->qkv_dtype != LA_F32 && a->d_k != 64 && a->d_k != 128) return LA_ERR_UNSUPPORTED;
   if (a->qkv_dtype == LA_F32 && a->d_k != 64) return LA_ERR_UNSUPPORTED;
@@ -39,7 +42,7 @@ int check_shape(const la_chunk_fwd_args *a) {
   if (a->seg_len < -1) return LA_ERR_UNSUPPORTED;
   if (a->seg_len > 0 && (a->qkv_dtype == LA_F32 || a->N_max > 64)) return LA_ERR_UNSUPPORTED;
   // every (token, head) index and (slot, head) workspace index stays in size_t
-  const int64_t nt = la_nt_max(a->T_max, a->N_max, a->BT);
+  const int64_t nt = la_nt_max(a->T_max, a->N_max, kBTk);
   if (nt < 1 || nt > 0x7fffffff) return LA_ERR_SHAPE;
   if ((int64_t)a->N_max * a->H > 0x7fffffff / 8) return LA_ERR_SHAPE;
   if (nt * a->H > 0x7fffffff) return LA_ERR_SHAPE;  // one map workgroup per cell
@@ -71,10 +74,10 @@ int seg_for(const la_chunk_fwd_args *a) {
   if (a->seg_len > 0) return a->seg_len;
   const int64_t s2 = a->d_v / 64 > 0 ? a->d_v / 64 : 1;
   if ((int64_t)a->N_max * a->H * s2 > kCUs / 2) return 0;
-  const int64_t nt = la_nt_max(a->T_max, a->N_max, a->BT);
+  const int64_t nt = la_nt_max(a->T_max, a->N_max, kBTk);
   int64_t L = (nt * a->H * s2 + kCUs - 1) / kCUs;
   if (L < 8) L = 8;
-  const int64_t longest = (a->T_max + a->BT - 1) / a->BT;
+  const int64_t longest = (a->T_max + kBTk - 1) / kBTk;
   if (longest < 3 * L) return 0;
   return (int)L;
 }
@@ -87,7 +90,7 @@ int seg_split(const la_chunk_fwd_args *a) {
   if (a->dv_split) return a->dv_split;
   const int L = seg_for(a);
   if (L > 0) {
-    const int64_t nt = la_nt_max(a->T_max, a->N_max, a->BT);
+    const int64_t nt = la_nt_max(a->T_max, a->N_max, kBTk);
     const int64_t narrow = (nt + L - 1) / L * a->H * (a->d_v / 32 + a->d_k / 32);
     if (narrow <= 2 * kCUs) return a->d_v / 32;
   }
@@ -96,14 +99,14 @@ int seg_split(const la_chunk_fwd_args *a) {
 
 // segment slots: ceil(T_max / (BT L)) + N_max - 1
 int64_t ns_max(const la_chunk_fwd_args *a, int L) {
-  return ((int64_t)a->T_max + (int64_t)a->BT * L - 1) / ((int64_t)a->BT * L) + a->N_max - 1;
+  return ((int64_t)a->T_max + (int64_t)kBTk * L - 1) / ((int64_t)kBTk * L) + a->N_max - 1;
 }
 
 // Workspace: one map-stage image per (chunk slot, head), image_layout bytes
 // each; with segments, then hin, dlt ([d_k][d_v] fp32) and the transition
 // images (2 x [d_k][d_k] fp16) per (segment slot, head)
 size_t ws_img_bytes(const la_chunk_fwd_args *a, bool kda) {
-  const size_t cells = (size_t)la_nt_max(a->T_max, a->N_max, a->BT) * a->H;
+  const size_t cells = (size_t)la_nt_max(a->T_max, a->N_max, kBTk) * a->H;
   return cells * (size_t)la::image_layout(kda, (int)elem_bytes(a), a->d_k).BYTES;
 }
 size_t ws_seg_bytes(const la_chunk_fwd_args *a) {
@@ -111,7 +114,33 @@ size_t ws_seg_bytes(const la_chunk_fwd_args *a) {
   if (L == 0) return 0;
   return 3 * (size_t)ns_max(a, L) * a->H * a->d_k * a->d_v * sizeof(float);
 }
-size_t ws_bytes(const la_chunk_fwd_args *a, bool kda) { return ws_img_bytes(a, kda) + ws_seg_bytes(a); }
+// BT = 32: the 64-row chunk layout the kernels run on, rebuilt from
+// cu_seqlens into the workspace (chunk_indices, chunk_offsets, status)
+size_t meta_bytes(const la_chunk_fwd_args *a) {
+  if (a->BT == kBTk) return 0;
+  const size_t nt = (size_t)la_nt_max(a->T_max, a->N_max, kBTk);
+  return (2 * nt + a->N_max + 2) * sizeof(int32_t);
+}
+size_t ws_bytes(const la_chunk_fwd_args *a, bool kda) {
+  return ws_img_bytes(a, kda) + ws_seg_bytes(a) + meta_bytes(a);
+}
+
+// the chunk layout the kernels read: the caller's (BT = 64), or one built
+// now at the workspace's end (BT = 32)
+struct Meta { const int32_t *ci, *co; };
+hipError_t kernel_meta(const la_chunk_fwd_args *a, char *meta_base, hipStream_t st, Meta &m) {
+  m.ci = a->chunk_indices;
+  m.co = a->chunk_offsets;
+  if (a->BT == kBTk) return hipSuccess;
+  const int nt = (int)la_nt_max(a->T_max, a->N_max, kBTk);
+  int32_t *ci = reinterpret_cast<int32_t *>(meta_base);
+  int32_t *co = ci + 2 * (size_t)nt;
+  int32_t *stat = co + a->N_max + 1;
+  m.ci = ci;
+  m.co = co;
+  return la::launch_chunk_meta(a->cu_seqlens, a->cu_seqlens_i64, a->N_max, a->T_max, kBTk, nt, ci,
+                               co, stat, st);
+}
 
 int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
   if (!a) return LA_ERR_NULL;
@@ -136,6 +165,9 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
   const int dt = a->qkv_dtype;
   char *ws = static_cast<char *>(a->workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  Meta meta;
+  if (kernel_meta(a, ws + ws_img_bytes(a, kda) + ws_seg_bytes(a), st, meta) != hipSuccess)
+    return LA_ERR_HIP;
   if (stages & LA_STAGE_MAP) {
     la::MapParams mp{};
     mp.q = a->q;
@@ -144,10 +176,10 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     mp.beta = a->beta;
     mp.cu_seqlens = a->cu_seqlens;
     mp.cu64 = a->cu_seqlens_i64;
-    mp.chunk_indices = a->chunk_indices;
+    mp.chunk_indices = meta.ci;
     mp.H = a->H;
     mp.Hqk = a->H_qk ? a->H_qk : a->H;
-    mp.NT_max = (int)la_nt_max(a->T_max, a->N_max, a->BT);
+    mp.NT_max = (int)la_nt_max(a->T_max, a->N_max, kBTk);
     mp.img = ws;
     if (la::launch_chunk_map(mp, kda, dt, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
   }
@@ -156,7 +188,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     rp.v = a->v;
     rp.cu_seqlens = a->cu_seqlens;
     rp.cu64 = a->cu_seqlens_i64;
-    rp.chunk_offsets = a->chunk_offsets;
+    rp.chunk_offsets = meta.co;
     rp.h0 = a->h0;
     rp.o = a->o;
     rp.ht = a->ht;
@@ -185,7 +217,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
       if (la::launch_chunk_reduce(rp, kda, dt, a->d_k, a->d_v / rp.S, st) != hipSuccess)
         return LA_ERR_HIP;
       la::CombineParams cp{};
-      cp.chunk_offsets = a->chunk_offsets;
+      cp.chunk_offsets = meta.co;
       cp.H = a->H;
       cp.N_max = a->N_max;
       cp.seg = L;
@@ -370,10 +402,10 @@ static la_chunk_fwd_args fwd_view(const la_chunk_bwd_args *a) {
 }
 
 // backward workspace: [forward images][hs][dhs][prep][part], each 256-aligned
-struct BwdLayout { size_t img, hs, dhs, prep, part, total; };
+struct BwdLayout { size_t img, hs, dhs, prep, part, meta, total; };
 static BwdLayout bwd_layout(const la_chunk_bwd_args *a, bool kda) {
   const la_chunk_fwd_args f = fwd_view(a);
-  const size_t cells = (size_t)la_nt_max(a->T_max, a->N_max, a->BT) * a->H;
+  const size_t cells = (size_t)la_nt_max(a->T_max, a->N_max, kBTk) * a->H;
   auto up = [](size_t x) { return (x + 255) / 256 * 256; };
   BwdLayout L{};
   L.img = 0;
@@ -381,7 +413,8 @@ static BwdLayout bwd_layout(const la_chunk_bwd_args *a, bool kda) {
   L.dhs = L.hs + up(cells * a->d_k * a->d_v * sizeof(float));
   L.prep = L.dhs + up(cells * a->d_k * a->d_v * sizeof(float));
   L.part = L.prep + up(cells * (kda ? la::kda_prep_floats(a->d_k) : la::kPrepFloats) * sizeof(float));
-  L.total = L.part + up(cells * la::part_floats(a->d_k) * sizeof(float));
+  L.meta = L.part + up(cells * la::part_floats(a->d_k) * sizeof(float));
+  L.total = L.meta + up(meta_bytes(&f));
   return L;
 }
 
@@ -416,6 +449,11 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
   // forward recompute: map images, then the reduce storing every chunk's
   // entering state (no output, no final state)
   la_chunk_fwd_args f = fwd_view(a);
+  f.cu_seqlens = a->cu_seqlens;
+  f.chunk_indices = a->chunk_indices;
+  f.chunk_offsets = a->chunk_offsets;
+  Meta meta;
+  if (kernel_meta(&f, ws + L.meta, st, meta) != hipSuccess) return LA_ERR_HIP;
   f.q = a->q;
   f.k = a->k;
   f.v = a->v;
@@ -427,7 +465,7 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
   f.h0 = a->h0;
   f.workspace = ws;
   f.workspace_bytes = L.hs;
-  const int NT = (int)la_nt_max(a->T_max, a->N_max, a->BT);
+  const int NT = (int)la_nt_max(a->T_max, a->N_max, kBTk);
   {
     la::MapParams mp{};
     mp.q = a->q;
@@ -436,7 +474,7 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
     mp.beta = a->beta;
     mp.cu_seqlens = a->cu_seqlens;
     mp.cu64 = a->cu_seqlens_i64;
-    mp.chunk_indices = a->chunk_indices;
+    mp.chunk_indices = meta.ci;
     mp.H = a->H;
     mp.Hqk = a->H;
     mp.NT_max = NT;
@@ -446,7 +484,7 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
     rp.v = a->v;
     rp.cu_seqlens = a->cu_seqlens;
     rp.cu64 = a->cu_seqlens_i64;
-    rp.chunk_offsets = a->chunk_offsets;
+    rp.chunk_offsets = meta.co;
     rp.h0 = a->h0;
     rp.o = nullptr;
     rp.ht = nullptr;
@@ -467,8 +505,8 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
   bp.beta = a->beta;
   bp.cu_seqlens = a->cu_seqlens;
   bp.cu64 = a->cu_seqlens_i64;
-  bp.chunk_indices = a->chunk_indices;
-  bp.chunk_offsets = a->chunk_offsets;
+  bp.chunk_indices = meta.ci;
+  bp.chunk_offsets = meta.co;
   bp.dout = a->dout;
   bp.dht = a->dht;
   bp.dq = a->dq;

@@ -87,7 +87,7 @@ int64_t la_nt_max(int64_t T_max, int64_t N_max, int32_t BT);
  * offset is 0, so the forward calls then write nothing.  The int64 variant
  * checks the offsets as int64 (a valid layout has all of them in
  * [0, T_max]).  BT may be 32 or 64 (the RFC's two chunk sizes; the chunk
- * forward runs BT = 64).  One launch of one workgroup; capturable.
+ * kernels run 64-row chunks).  One launch of one workgroup; capturable.
  * Host errors: LA_ERR_NULL (cu_seqlens, chunk_indices or chunk_offsets NULL),
  * LA_ERR_SHAPE (N_max < 1, N_max > LA_MAX_N, T_max < 1),
  * LA_ERR_UNSUPPORTED (BT not 32 or 64), LA_ERR_HIP.
@@ -105,7 +105,11 @@ typedef struct {
     int32_t T_max, N_max, H;   /* bucket capacity and head count (>= 1)          */
     int32_t d_k, d_v;          /* head dims: d_k == d_v; 64 or 128 (bf16, fp16), */
                                /* 64 (fp32 inputs)                               */
-    int32_t BT;                /* chunk size: 64                                 */
+    int32_t BT;                /* chunk size of the caller's metadata: 32 or 64  */
+                               /* (the kernels run 64-row chunks; for 32 the    */
+                               /* call builds that layout from cu_seqlens in    */
+                               /* its workspace and does not read chunk_indices */
+                               /* or chunk_offsets)                             */
     int32_t qkv_dtype;         /* LA_BF16, LA_F16 or LA_F32: dtype of q, k, v    */
     int32_t dv_split;          /* state column slices per (seq, head): 0 = auto, */
                                /* else 1, 2 or 4 with d_v / dv_split >= 32.      */
@@ -247,7 +251,7 @@ int kda_recurrent_fwd(const la_recurrent_args *a, void *stream);
 typedef struct {
     int32_t T_max, N_max, H;   /* as la_chunk_fwd_args                           */
     int32_t d_k, d_v;          /* d_k == d_v: 64 or 128 (16-bit), 64 (fp32)      */
-    int32_t BT;                /* 64                                             */
+    int32_t BT;                /* 32 or 64, as la_chunk_fwd_args                 */
     int32_t qkv_dtype;         /* LA_BF16, LA_F16 or LA_F32                      */
     int32_t cu_seqlens_i64;    /* 0: cu_seqlens int32; 1: int64                  */
     float scale;               /* the forward's scale                            */

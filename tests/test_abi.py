@@ -66,7 +66,7 @@ BAD = [
     ("N_max 0", dict(N_max=0), -2),
     ("H 0", dict(H=0), -2),
     ("dtype 7", dict(qkv_dtype=7), -3),
-    ("BT 32", dict(BT=32), -4),
+    ("BT 16", dict(BT=16), -4),
     ("d 96", dict(d_k=96, d_v=96), -4),
     ("d_k != d_v", dict(d_v=128), -4),
     ("fp32 d 128", dict(qkv_dtype=1, d_k=128, d_v=128), -4),
@@ -84,7 +84,7 @@ BAD = [
     ("o_bf16 2", dict(o_bf16=2), -3),
     ("cu_seqlens_i64 2", dict(cu_seqlens_i64=2), -3),
     ("fp16 d 96", dict(qkv_dtype=2, d_k=96, d_v=96), -4),
-    ("fp16 BT 32", dict(qkv_dtype=2, BT=32), -4),
+    ("fp16 BT 48", dict(qkv_dtype=2, BT=48), -4),
     ("fp32 segmented", dict(qkv_dtype=1, seg_len=4), -4),
 ]
 
@@ -287,7 +287,7 @@ BBAD = [
     ("null dq", dict(dq=None), -1),
     ("null dbeta", dict(dbeta=None), -1),
     ("dtype 4", dict(qkv_dtype=4), -3),
-    ("BT 32", dict(BT=32), -4),
+    ("BT 16", dict(BT=16), -4),
     ("d 96", dict(d_k=96, d_v=96), -4),
     ("no workspace", dict(workspace=None), -5),
     ("workspace small", dict(workspace_bytes=1000), -5),
@@ -318,3 +318,13 @@ def test_backward_workspace_size():
         part = (192 * d + 8192 + 256) * 4
         want = up(img) + 2 * up(cells * d * d * 4) + up(cells * prep) + up(cells * part)
         assert la.bwd_workspace_bytes(T, N, H, d, d, torch.bfloat16, kda=kda) == want
+
+
+def test_workspace_with_bt32_layout():
+    """BT = 32: the forward's workspace also holds the rebuilt 64-row layout
+    (chunk_indices [NT_max(64)][2], chunk_offsets [N_max+1], a status word)."""
+    import torch
+    T, N, H, d = 4096, 3, 2, 128
+    base = la.workspace_bytes(T, N, H, d, d, torch.bfloat16, seg_len=-1)
+    b32 = la.workspace_bytes(T, N, H, d, d, torch.bfloat16, BT=32, seg_len=-1)
+    assert b32 - base == (2 * meta_ref.nt_max(T, N, 64) + N + 2) * 4

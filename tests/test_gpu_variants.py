@@ -1,6 +1,7 @@
 """GPU parity of the test-matrix variants the graph-capture RFC lists for
-every operator (section "Testing"): fp16 inputs, int64 cu_seqlens and the
-BT = 32 chunk layout of the metadata.
+every operator (section "Testing"): fp16 inputs, int64 cu_seqlens and
+BT = 32 layouts (the metadata itself, and the forward and backward given
+BT = 32 metadata).
 
 Bar: as for the bf16 path (max relative error <= 2e-3 against the fp64
 oracle; fp16 inputs use the same fp16 MFMA operands); metadata bit-exact
@@ -143,3 +144,53 @@ def test_forward_int64_invalid_writes_nothing():
     torch.cuda.synchronize()
     assert int(st.item()) != 0
     assert bool((o == 7.0).all()) and bool((ht == 5.0).all())
+
+
+# ------------------------------------------------------------- BT = 32 ---
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+@pytest.mark.parametrize("seg", [-1, 2])
+def test_forward_with_bt32_layout(kda, seg):
+    """A caller's BT = 32 metadata: the call rebuilds the 64-row layout its
+    kernels run on from cu_seqlens, so the result equals the BT = 64 call bit
+    for bit, and the oracle within the gate."""
+    inp = make_inputs(SMALL_CU[-1], 2, 128, 128, kda=kda, dtype="bf16", seed=350,
+                      cu_seqlens=SMALL_CU, h0_std=0.1)
+    d = to_dev(inp)
+    T = SMALL_CU[-1]
+    fwd = la.kda_chunk_fwd if kda else la.gdn_chunk_fwd
+    res = {}
+    for BT in (64, 32):
+        ci, co, st = la.build_chunk_meta(d["cu_seqlens"], T, BT)
+        o, ht = fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], ci, co,
+                    h0=d["h0"], seg_len=seg, BT=BT)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        res[BT] = (o, ht)
+    ne = torch.from_numpy(np.diff(np.asarray(SMALL_CU)) > 0)
+    assert torch.equal(res[32][0][:T], res[64][0][:T])
+    assert torch.equal(res[32][1][ne], res[64][1][ne])
+    o_ref, ht_ref = run_oracle(inp)
+    eo, eh, tol = compare(inp, res[32][0], res[32][1], o_ref, ht_ref)
+    _say(f"BT=32 layout kda={kda} seg={seg}: o {eo:.2e} ht {eh:.2e}")
+    assert eo <= tol and eh <= tol
+
+
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+def test_backward_with_bt32_layout(kda):
+    inp = make_inputs(SMALL_CU[-1], 2, 64, 64, kda=kda, dtype="bf16", seed=360,
+                      cu_seqlens=SMALL_CU, h0_std=0.1)
+    d = to_dev(inp)
+    T = SMALL_CU[-1]
+    rng = np.random.default_rng(361)
+    dout = torch.from_numpy(rng.standard_normal(inp["v"].shape).astype(np.float32)).cuda()
+    bwd = la.kda_chunk_bwd if kda else la.gdn_chunk_bwd
+    res = {}
+    for BT in (64, 32):
+        ci, co, _ = la.build_chunk_meta(d["cu_seqlens"], T, BT)
+        res[BT] = bwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], ci, co, dout,
+                      h0=d["h0"], BT=BT)
+        torch.cuda.synchronize()
+    ne = torch.from_numpy(np.diff(np.asarray(SMALL_CU)) > 0)
+    for i in range(5):
+        assert torch.equal(res[32][i][:T], res[64][i][:T]), i
+    assert torch.equal(res[32][5][ne], res[64][5][ne])
