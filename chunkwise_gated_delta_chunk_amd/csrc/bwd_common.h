@@ -127,6 +127,25 @@ __device__ __forceinline__ void load_mat64(float *dst, const float *src) {
   load_block<64, 64>(dst, kL, src, 64);
 }
 
+// The sequence of rank `rank` by decreasing chunk count (ties by index), so
+// that the reverse passes start the longest sequences first when their
+// workgroups outnumber the CUs; -1 past the non-empty ones.  Up to 64
+// sequences each wave ranks them itself (lane m holding sequence m); beyond
+// that the natural order is kept.
+__device__ __forceinline__ int seq_by_rank(const int32_t *co, int N_max, int rank) {
+  if (N_max > 64) return rank;
+  const int m = lane_id();
+  int len = -1;
+  if (m < N_max) len = co[m + 1] - co[m];
+  if (rank >= __popcll(__ballot(len > 0))) return -1;
+  int r = 0;
+  for (int i = 0; i < N_max; ++i) {
+    const int li = __builtin_amdgcn_readlane(len, i);
+    r += (li > len) | ((li == len) & (i < m));
+  }
+  return __builtin_ctzll(__ballot(r == rank));
+}
+
 // X = (I + diag(beta) S)^-1 for the strict-lower S ([64][64], stride kL),
 // rows and columns >= C zero, into sX (stride kL); the whole workgroup
 // (4 waves) calls it between barriers.  The four 16x16 diagonal blocks by

@@ -100,8 +100,9 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) float sGam[64], sFac[64], sBeta[64];
   const int H = p.H;
   const int sv = blockIdx.x % SV, unit = blockIdx.x / SV;
-  const int n = unit / H, h = unit % H;
-  if (n >= p.N_max) return;
+  if (unit >= p.N_max * H) return;
+  const int n = seq_by_rank(p.chunk_offsets, p.N_max, unit / H), h = unit % H;
+  if (n < 0) return;
   const int j0 = p.chunk_offsets[n], j1 = p.chunk_offsets[n + 1];
   if (j0 == j1) return;
   const int bos = cu_at(p.cu_seqlens, p.cu64, n), eos = cu_at(p.cu_seqlens, p.cu64, n + 1);
