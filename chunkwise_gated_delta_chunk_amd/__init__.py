@@ -90,7 +90,7 @@ class ChunkBwdArgs(ctypes.Structure):
         ("T_max", ctypes.c_int32), ("N_max", ctypes.c_int32), ("H", ctypes.c_int32),
         ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32), ("BT", ctypes.c_int32),
         ("qkv_dtype", ctypes.c_int32), ("cu_seqlens_i64", ctypes.c_int32),
-        ("scale", ctypes.c_float),
+        ("H_qk", ctypes.c_int32), ("scale", ctypes.c_float),
         ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
         ("g", ctypes.c_void_p), ("beta", ctypes.c_void_p), ("cu_seqlens", ctypes.c_void_p),
         ("chunk_indices", ctypes.c_void_p), ("chunk_offsets", ctypes.c_void_p),
@@ -468,9 +468,10 @@ def _bwd_shape(T_max, N_max, H, d_k, d_v, qkv_dtype, BT=64):
     return a
 
 
-def bwd_workspace_bytes(T_max, N_max, H, d_k, d_v, qkv_dtype, BT=64, kda=False):
-    return int(lib().la_chunk_bwd_workspace_bytes(ctypes.byref(
-        _bwd_shape(T_max, N_max, H, d_k, d_v, qkv_dtype, BT)), int(kda)))
+def bwd_workspace_bytes(T_max, N_max, H, d_k, d_v, qkv_dtype, BT=64, kda=False, H_qk=0):
+    a = _bwd_shape(T_max, N_max, H, d_k, d_v, qkv_dtype, BT)
+    a.H_qk = H_qk
+    return int(lib().la_chunk_bwd_workspace_bytes(ctypes.byref(a), int(kda)))
 
 
 def gdn_chunk_bwd(*args, **kw):
@@ -492,11 +493,12 @@ def _chunk_bwd(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, 
                dht=None, scale=1.0, dq=None, dk=None, dv=None, dg=None, dbeta=None, dh0=None,
                workspace=None, BT=64, stream=None):
     _qkv_dtype(q)
-    T_max, H, d_k = q.shape
+    H, H_qk = _heads(q, v, "T_max")
+    T_max, _, d_k = q.shape
     d_v = v.shape[-1]
     dev = q.device
     _need(q, "q", q.dtype)
-    _need(k, "k", q.dtype, (T_max, H, d_k), dev)
+    _need(k, "k", q.dtype, (T_max, H_qk, d_k), dev)
     _need(v, "v", q.dtype, (T_max, H, d_v), dev)
     g_shape = (T_max, H, d_k) if kda else (T_max, H)
     _need(g, "g", torch.float32, g_shape, dev)
@@ -518,8 +520,8 @@ def _chunk_bwd(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, 
             t = torch.empty(shape, dtype=torch.float32, device=dev)
         _need(t, name, torch.float32, shape, dev)
         return t
-    dq = out(dq, (T_max, H, d_k), "dq")
-    dk = out(dk, (T_max, H, d_k), "dk")
+    dq = out(dq, (T_max, H_qk, d_k), "dq")
+    dk = out(dk, (T_max, H_qk, d_k), "dk")
     dv = out(dv, (T_max, H, d_v), "dv")
     dg = out(dg, g_shape, "dg")
     dbeta = out(dbeta, (T_max, H), "dbeta")
@@ -528,6 +530,7 @@ def _chunk_bwd(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, 
     if dh0 is not None:
         _need(dh0, "dh0", torch.float32, st_shape, dev)
     a = _bwd_shape(T_max, N_max, H, d_k, d_v, q.dtype, BT)
+    a.H_qk = H_qk
     a.cu_seqlens_i64 = int(cu_seqlens.dtype == torch.int64)
     a.scale = float(scale)
     need = int(lib().la_chunk_bwd_workspace_bytes(ctypes.byref(a), int(kda)))

@@ -45,8 +45,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   Chunk ch;
   if (!chunk_of(p, slot, ch)) return;
   const int C = ch.C;
-  load_rows<In, DK>(sK, LK, p.k, ch.r0, C, H, h);
-  load_rows<In, DK>(sQ, LK, p.q, ch.r0, C, H, h);
+  load_rows<In, DK>(sK, LK, p.k, ch.r0, C, p.Hqk, h / (H / p.Hqk));
+  load_rows<In, DK>(sQ, LK, p.q, ch.r0, C, p.Hqk, h / (H / p.Hqk));
   const int tid = threadIdx.x;
   if (tid < 64) {
     const float gr = tid < C ? p.g[(size_t)(ch.r0 + tid) * H + h] : 0.f;
@@ -118,8 +118,8 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdParams p) {
   for (int jj = j1 - 1; jj >= j0; --jj) {
     __syncthreads();
     const int r0 = bos + (jj - j0) * kBT, C = min(kBT, eos - r0);
-    load_rows<In, DK>(sK, LK, p.k, r0, C, H, h);
-    load_rows<In, DK>(sQ, LK, p.q, r0, C, H, h);
+    load_rows<In, DK>(sK, LK, p.k, r0, C, p.Hqk, h / (H / p.Hqk));
+    load_rows<In, DK>(sQ, LK, p.q, r0, C, p.Hqk, h / (H / p.Hqk));
     const float *img = p.prep + ((size_t)jj * H + h) * kPrepFloats;
     load_mat64(sA, img + kPrepA);
     load_mat64(sM, img + kPrepM);
@@ -214,7 +214,7 @@ __global__ __launch_bounds__(256) void bwd_part_kernel(BwdParams p) {
   if (!chunk_of(p, slot, ch)) return;
   const int C = ch.C, r0 = ch.r0;
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
-  load_rows<In, DK>(sK, LK, p.k, r0, C, H, h);
+  load_rows<In, DK>(sK, LK, p.k, r0, C, p.Hqk, h / (H / p.Hqk));
   const float *img = p.prep + (size_t)blockIdx.x * kPrepFloats;
   load_mat64(sA, img + kPrepA);
   load_mat64(sM, img + kPrepM);
@@ -406,8 +406,8 @@ __global__ __launch_bounds__(256) void bwd_final_kernel(BwdParams p) {
   __syncthreads();
   // phase B: K and Q over the first four matrices
   float *sK = smem, *sQ = smem + kBT * LK;
-  load_rows<In, DK>(sK, LK, p.k, r0, C, H, h);
-  load_rows<In, DK>(sQ, LK, p.q, r0, C, H, h);
+  load_rows<In, DK>(sK, LK, p.k, r0, C, p.Hqk, h / (H / p.Hqk));
+  load_rows<In, DK>(sQ, LK, p.q, r0, C, p.Hqk, h / (H / p.Hqk));
   __syncthreads();
   const float *P1 = gw + kPartP1, *P2 = gw + part_p2(DK), *P3 = gw + part_p3(DK);
   // dQ = gam P1 + (dM E) K;  dK = -gam P2 + fac P3 + (dM E)^T Q + F K + F^T K,
@@ -493,7 +493,36 @@ hipError_t launch_dk(const BwdParams &p, int dk, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+// out [T][Hqk][d] = sum over the G = H / Hqk value heads of each group of
+// full [T][H][d], four floats per thread, rows of real tokens only (none when
+// the metadata marks cu_seqlens invalid)
+__global__ __launch_bounds__(256) void group_sum_kernel(const float *full, float *out, int T_max,
+                                                        int H, int Hqk, int d, const void *cu,
+                                                        int cu64, int N_max, const int32_t *co) {
+  const int total = co[N_max] > 0 ? cu_at(cu, cu64, N_max) : 0;
+  const size_t q4 = (size_t)d / 4, n4 = (size_t)T_max * Hqk * q4;
+  const size_t idx = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n4) return;
+  const int t = (int)(idx / ((size_t)Hqk * q4));
+  if (t >= total) return;
+  const int hq = (int)(idx / q4 % Hqk), c = (int)(idx % q4) * 4;
+  const int G = H / Hqk;
+  f32x4 acc = zero4();
+  for (int j = 0; j < G; ++j)
+    acc += *reinterpret_cast<const f32x4 *>(full + ((size_t)t * H + hq * G + j) * d + c);
+  *reinterpret_cast<f32x4 *>(out + ((size_t)t * Hqk + hq) * d + c) = acc;
+}
+
 }  // namespace
+
+hipError_t launch_group_sum(const float *full, float *out, int T_max, int H, int Hqk, int d,
+                            const void *cu, int cu64, int N_max, const int32_t *co,
+                            hipStream_t st) {
+  const size_t n4 = (size_t)T_max * Hqk * (d / 4);
+  hipLaunchKernelGGL(group_sum_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, full,
+                     out, T_max, H, Hqk, d, cu, cu64, N_max, co);
+  return hipGetLastError();
+}
 
 hipError_t launch_chunk_bwd(const BwdParams &p, int dt, int dk, hipStream_t st) {
   if (dt == LA_BF16) return launch_dk<bf16>(p, dk, st);

@@ -84,8 +84,8 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(BwdParams p) {
   Chunk ch;
   if (!chunk_of(p, slot, ch)) return;
   const int C = ch.C, tid = threadIdx.x;
-  load_rows<In, DK>(sK, LK, p.k, ch.r0, C, H, h);
-  load_rows<In, DK>(sQ, LK, p.q, ch.r0, C, H, h);
+  load_rows<In, DK>(sK, LK, p.k, ch.r0, C, p.Hqk, h / (H / p.Hqk));
+  load_rows<In, DK>(sQ, LK, p.q, ch.r0, C, p.Hqk, h / (H / p.Hqk));
   // raw gates [C][DK], then the per-channel cumulative sum down the rows
   load_rows<float, DK>(sG, LK, p.g, ch.r0, C, H, h);
   if (tid < 64) sB[tid] = tid < C ? p.beta[(size_t)(ch.r0 + tid) * H + h] : 0.f;
@@ -152,8 +152,8 @@ __global__ __launch_bounds__(256) void kda_dh_kernel(BwdParams p) {
     const int r0 = bos + (jj - j0) * kBT, C = min(kBT, eos - r0);
     const float *img = p.prep + ((size_t)jj * H + h) * kda_prep_floats(DK);
     const float *G = img + kKdaG;
-    load_decayed<In, DK, 1>(sK, LK, p.k, G, r0, C, H, h);  // Kh
-    load_decayed<In, DK, 0>(sQ, LK, p.q, G, r0, C, H, h);  // Qt
+    load_decayed<In, DK, 1>(sK, LK, p.k, G, r0, C, p.Hqk, h / (H / p.Hqk));  // Kh
+    load_decayed<In, DK, 0>(sQ, LK, p.q, G, r0, C, p.Hqk, h / (H / p.Hqk));  // Qt
     load_mat64(sA, img + kPrepA);
     load_mat64(sM, img + kPrepM);
     load_rows<float, DV, 32>(sO, LC, p.dout, r0, C, H, h, c0);
@@ -191,7 +191,7 @@ __global__ __launch_bounds__(256) void kda_dh_kernel(BwdParams p) {
         }
     }
     __syncthreads();
-    load_decayed<In, DK, 0>(sK, LK, p.k, G, r0, C, H, h);  // Kt
+    load_decayed<In, DK, 0>(sK, LK, p.k, G, r0, C, p.Hqk, h / (H / p.Hqk));  // Kt
     __syncthreads();
     // dH = exp(G_C) dH' + Qt^T dOb - Kt^T dX
     for (int t = w; t < DK / 16; t += 4) {
@@ -238,8 +238,8 @@ __global__ __launch_bounds__(256) void kda_part_kernel(BwdParams p) {
   const int C = ch.C, r0 = ch.r0;
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
   const float *img = p.prep + (size_t)blockIdx.x * kda_prep_floats(DK);
-  load_decayed<In, DK, 0>(sKt, LK, p.k, img + kKdaG, r0, C, H, h);
-  load_decayed<In, DK, 1>(sKh, LK, p.k, img + kKdaG, r0, C, H, h);
+  load_decayed<In, DK, 0>(sKt, LK, p.k, img + kKdaG, r0, C, p.Hqk, h / (H / p.Hqk));
+  load_decayed<In, DK, 1>(sKh, LK, p.k, img + kKdaG, r0, C, p.Hqk, h / (H / p.Hqk));
   load_mat64(sA, img + kPrepA);
   load_mat64(sM, img + kPrepM);
   if (tid < 64) sBeta[tid] = img[kKdaBeta + tid];
@@ -393,8 +393,8 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
   }
   __syncthreads();
   // phase B: K, Q, G over the phase-A matrices
-  load_rows<In, DK>(sK, LK, p.k, r0, C, H, h);
-  load_rows<In, DK>(sQ, LK, p.q, r0, C, H, h);
+  load_rows<In, DK>(sK, LK, p.k, r0, C, p.Hqk, h / (H / p.Hqk));
+  load_rows<In, DK>(sQ, LK, p.q, r0, C, p.Hqk, h / (H / p.Hqk));
   load_block<64, DK>(sG, LK, img + kKdaG, DK);
   __syncthreads();
   if (tid < C) {

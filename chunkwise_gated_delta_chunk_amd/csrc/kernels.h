@@ -108,6 +108,7 @@ struct BwdParams {
   float *dq, *dk, *dv, *dg, *dbeta, *dh0;
   float *prep, *part, *hs, *dhs;
   int cu64, H, N_max, NT;
+  int Hqk;  // q, k heads: value head h reads (and its dq, dk belong to) head h / (H / Hqk)
   float scale;
 };
 
@@ -123,6 +124,11 @@ hipError_t launch_chunk_combine(const CombineParams &p, int dk, hipStream_t st);
 hipError_t launch_recurrent(const RecurrentParams &p, bool kda, int dt, int dk, hipStream_t st);
 hipError_t launch_chunk_bwd(const BwdParams &p, int dt, int dk, hipStream_t st);
 hipError_t launch_chunk_bwd_kda(const BwdParams &p, int dt, int dk, hipStream_t st);
+// grouped value heads: out[t][hq] = sum of full[t][h] over the value heads h
+// of group hq, rows of real tokens only
+hipError_t launch_group_sum(const float *full, float *out, int T_max, int H, int Hqk, int d,
+                            const void *cu, int cu64, int N_max, const int32_t *co,
+                            hipStream_t st);
 // NT chunk slots, W in 1..4
 hipError_t launch_short_conv(const ConvParams &p, int dt, int NT, int W, bool silu,
                              hipStream_t st);

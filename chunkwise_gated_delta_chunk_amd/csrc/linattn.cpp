@@ -397,12 +397,13 @@ static la_chunk_fwd_args fwd_view(const la_chunk_bwd_args *a) {
   f.qkv_dtype = a->qkv_dtype;
   f.seg_len = -1;  // the recompute stores per-chunk states: one pass
   f.cu_seqlens_i64 = a->cu_seqlens_i64;
+  f.H_qk = a->H_qk;
   f.scale = a->scale;
   return f;
 }
 
 // backward workspace: [forward images][hs][dhs][prep][part], each 256-aligned
-struct BwdLayout { size_t img, hs, dhs, prep, part, meta, total; };
+struct BwdLayout { size_t img, hs, dhs, prep, part, meta, gva, total; };
 static BwdLayout bwd_layout(const la_chunk_bwd_args *a, bool kda) {
   const la_chunk_fwd_args f = fwd_view(a);
   const size_t cells = (size_t)la_nt_max(a->T_max, a->N_max, kBTk) * a->H;
@@ -414,7 +415,9 @@ static BwdLayout bwd_layout(const la_chunk_bwd_args *a, bool kda) {
   L.prep = L.dhs + up(cells * a->d_k * a->d_v * sizeof(float));
   L.part = L.prep + up(cells * (kda ? la::kda_prep_floats(a->d_k) : la::kPrepFloats) * sizeof(float));
   L.meta = L.part + up(cells * la::part_floats(a->d_k) * sizeof(float));
-  L.total = L.meta + up(meta_bytes(&f));
+  L.gva = L.meta + up(meta_bytes(&f));
+  const bool grouped = a->H_qk > 0 && a->H_qk != a->H;
+  L.total = L.gva + (grouped ? 2 * up((size_t)a->T_max * a->H * a->d_k * sizeof(float)) : 0);
   return L;
 }
 
@@ -476,7 +479,7 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
     mp.cu64 = a->cu_seqlens_i64;
     mp.chunk_indices = meta.ci;
     mp.H = a->H;
-    mp.Hqk = a->H;
+    mp.Hqk = a->H_qk ? a->H_qk : a->H;
     mp.NT_max = NT;
     mp.img = ws;
     if (la::launch_chunk_map(mp, kda, a->qkv_dtype, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
@@ -509,8 +512,15 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
   bp.chunk_offsets = meta.co;
   bp.dout = a->dout;
   bp.dht = a->dht;
-  bp.dq = a->dq;
-  bp.dk = a->dk;
+  const int Hqk = a->H_qk ? a->H_qk : a->H;
+  const bool grouped = Hqk != a->H;
+  const size_t full = (size_t)a->T_max * a->H * a->d_k * sizeof(float);
+  auto up = [](size_t x) { return (x + 255) / 256 * 256; };
+  float *dq_full = reinterpret_cast<float *>(ws + L.gva);
+  float *dk_full = reinterpret_cast<float *>(ws + L.gva + up(full));
+  bp.dq = grouped ? dq_full : a->dq;
+  bp.dk = grouped ? dk_full : a->dk;
+  bp.Hqk = Hqk;
   bp.dv = a->dv;
   bp.dg = a->dg;
   bp.dbeta = a->dbeta;
@@ -526,6 +536,13 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
   const hipError_t e = kda ? la::launch_chunk_bwd_kda(bp, a->qkv_dtype, a->d_k, st)
                           : la::launch_chunk_bwd(bp, a->qkv_dtype, a->d_k, st);
   if (e != hipSuccess) return LA_ERR_HIP;
+  if (grouped) {
+    if (la::launch_group_sum(dq_full, a->dq, a->T_max, a->H, Hqk, a->d_k, a->cu_seqlens,
+                             a->cu_seqlens_i64, a->N_max, meta.co, st) != hipSuccess ||
+        la::launch_group_sum(dk_full, a->dk, a->T_max, a->H, Hqk, a->d_k, a->cu_seqlens,
+                             a->cu_seqlens_i64, a->N_max, meta.co, st) != hipSuccess)
+      return LA_ERR_HIP;
+  }
   return LA_OK;
 }
 

@@ -254,8 +254,9 @@ typedef struct {
     int32_t BT;                /* 32 or 64, as la_chunk_fwd_args                 */
     int32_t qkv_dtype;         /* LA_BF16, LA_F16 or LA_F32                      */
     int32_t cu_seqlens_i64;    /* 0: cu_seqlens int32; 1: int64                  */
+    int32_t H_qk;              /* q, k heads as la_chunk_fwd_args (0 = H)        */
     float scale;               /* the forward's scale                            */
-    const void *q, *k, *v;     /* [T_max][H][d_k] / [T_max][H][d_v], qkv_dtype  */
+    const void *q, *k, *v;     /* [T_max][H_qk][d_k] / [T_max][H][d_v], qkv_dtype */
     const float *g;            /* log-decay: GDN [T_max][H]; KDA [T_max][H][d_k] */
     const float *beta;         /* [T_max][H]                                     */
     const void *cu_seqlens;    /* [N_max+1]                                      */
@@ -263,7 +264,8 @@ typedef struct {
     const float *h0;           /* [N_max][H][d_k][d_v] or NULL (zero state)      */
     const float *dout;         /* gradient of o: [T_max][H][d_v] fp32            */
     const float *dht;          /* gradient of ht: [N_max][H][d_k][d_v] or NULL   */
-    float *dq, *dk;            /* [T_max][H][d_k] fp32                           */
+    float *dq, *dk;            /* [T_max][H_qk][d_k] fp32 (summed over a group's */
+                               /* value heads)                                   */
     float *dv;                 /* [T_max][H][d_v] fp32                           */
     float *dg;                 /* like g, fp32                                   */
     float *dbeta;              /* [T_max][H] fp32                                */
@@ -276,8 +278,9 @@ typedef struct {
  * H, d_k, d_v, BT, qkv_dtype read); 0 if the shape is invalid.  It holds the
  * forward recompute's map images, the state entering and the state gradient
  * leaving every chunk ([d_k][d_v] fp32 per chunk slot and head), per-cell
- * fp32 matrices A^-1, M, S (KDA: and the per-channel cumulative gate) and
- * per-cell partial products. */
+ * fp32 matrices A^-1, M, S (KDA: and the per-channel cumulative gate),
+ * per-cell partial products, with BT = 32 the 64-row chunk layout, and with
+ * grouped value heads the per-value-head dq, dk ([T_max][H][d_k] fp32 each). */
 size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *shape, int is_kda);
 
 /*
@@ -291,8 +294,9 @@ size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *shape, int is_kda);
  * state gradient (writing dh0), a chunk-parallel pass for dv and the
  * d_v-contracted products, and a chunk-parallel pass for dq, dk, dg, dbeta.
  * Arithmetic after the recompute is fp32.  Rows outside every sequence,
- * sentinel slots and dh0 of zero-length sequences are not written.  Grouped
- * value heads are not supported here (q, k carry H heads).
+ * sentinel slots and dh0 of zero-length sequences are not written.  With
+ * grouped value heads each value head's dq, dk go to the workspace and one
+ * more launch sums every group into dq, dk.
  * Host errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_UNSUPPORTED,
  * LA_ERR_WORKSPACE, LA_ERR_HIP.
  */

@@ -146,3 +146,28 @@ def test_backward_kda_config2_sampled_head():
             for key in ("dq", "dk", "dv", "dg", "dbeta")}
     _say("bwd kda config2 head 5: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     assert all(v <= TOL["bf16"] for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+@pytest.mark.parametrize("H_qk", [1, 2])
+def test_backward_grouped_value_heads(kda, H_qk):
+    """q, k with H_qk heads shared by H = 4 value heads: dq, dk of a q/k head
+    are the sums of the oracle's gradients over its group (the oracle runs on
+    q, k repeated per value head)."""
+    from tests.helpers import gva
+    inp = make_inputs(SMALL_CU[-1], 4, 64, 64, kda=kda, dtype="bf16", seed=760 + H_qk,
+                      cu_seqlens=SMALL_CU, h0_std=0.1)
+    small, full = gva(inp, H_qk)
+    rng = np.random.default_rng(761)
+    do = rng.standard_normal(inp["v"].shape).astype(np.float32)
+    dht = rng.standard_normal(inp["h0"].shape).astype(np.float32)
+    ref = gated_delta_bwd(full["q"], full["k"], full["v"], full["g"], full["beta"], SMALL_CU,
+                          full["h0"], do, dht, 1.0, kda=kda)
+    G = 4 // H_qk
+    T = SMALL_CU[-1]
+    for key in ("dq", "dk"):
+        ref[key] = ref[key].reshape(T, H_qk, G, 64).sum(axis=2)
+    got = run_bwd(small, do, dht, 1.0)
+    errs = compare(small, got, ref)
+    _say(f"bwd gva kda={kda} H_qk={H_qk}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL["bf16"] for v in errs.values()), errs
