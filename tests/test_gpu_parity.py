@@ -392,3 +392,38 @@ def test_scale_is_linear():
     o1, ht1, _ = run_gpu(inp, scale=1.0)
     o2, ht2, _ = run_gpu(inp, scale=0.125)
     assert torch.equal(o1 * 0.125, o2) and torch.equal(ht1, ht2)
+
+
+# ------------------------------------------------------- degenerate cases ---
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+def test_zero_beta_and_unit_decay_keep_the_state(kda):
+    """beta = 0 and g = 0 (alpha = 1): the recurrence never writes, so ht is h0
+    bit for bit and o_t = scale * h0^T q_t (to the fp16 operand rounding)."""
+    inp = make_inputs(SMALL_CU[-1], 2, 128, 128, kda=kda, dtype="bf16", seed=800,
+                      cu_seqlens=SMALL_CU, h0_std=0.1)
+    inp["beta"] = np.zeros_like(inp["beta"])
+    inp["g"] = np.zeros_like(inp["g"])
+    o, ht, _ = run_gpu(inp, scale=0.5)
+    ne = np.diff(np.asarray(SMALL_CU)) > 0
+    assert np.array_equal(ht.cpu().numpy()[ne], inp["h0"][ne])
+    o_ref, ht_ref = run_oracle(inp, scale=0.5)
+    eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref)
+    _say(f"beta=0, g=0 kda={kda}: o {eo:.2e} ht {eh:.2e}")
+    assert eo <= tol and eh == 0.0
+
+
+def test_many_sequences_bucket():
+    """N_max = 100 (> 64: the reduce takes sequences in their natural order),
+    lengths 0 .. 130 tokens, compared with the oracle."""
+    rng = np.random.default_rng(810)
+    lens = rng.integers(0, 131, size=100)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    T_max = int(cu[-1]) + 37                     # padding rows after the last sequence
+    inp = make_inputs(T_max, 2, 64, 64, kda=False, dtype="bf16", seed=811,
+                      cu_seqlens=cu.tolist(), h0_std=0.1)
+    o, ht, (ci, co, st) = run_gpu(inp)
+    assert int(st.item()) == 0
+    o_ref, ht_ref = run_oracle(inp)
+    eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref)
+    _say(f"N_max=100 bucket: o {eo:.2e} ht {eh:.2e}")
+    assert eo <= tol and eh <= tol
