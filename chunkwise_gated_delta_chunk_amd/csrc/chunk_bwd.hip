@@ -73,12 +73,23 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
       sS[r * kL + s] = Sv;
       img[kPrepS + r * 64 + s] = Sv;
       img[kPrepM + r * 64 + s] = Mv;
+      __bf16 *mt = reinterpret_cast<__bf16 *>(img + kPrepH) + s * 64 + r;  // M^T
+      const __bf16 mh = (__bf16)Mv;
+      mt[0] = mh;
+      mt[4096] = (__bf16)(Mv - (float)mh);
     }
   }
   __syncthreads();
   // A^-1 = (I + diag(beta) S)^-1, by 16x16 blocks
   unit_lower_inverse(sS, sB, sX, C);
-  for (int idx = tid; idx < 64 * 64; idx += 256) img[kPrepA + idx] = sX[(idx >> 6) * kL + (idx & 63)];
+  for (int idx = tid; idx < 64 * 64; idx += 256) {
+    const int r = idx >> 6, c = idx & 63;
+    img[kPrepA + idx] = sX[r * kL + c];
+    const float at = sX[c * kL + r];  // (A^-1)^T
+    const __bf16 ah = (__bf16)at;
+    reinterpret_cast<__bf16 *>(img + kPrepH)[8192 + idx] = ah;
+    reinterpret_cast<__bf16 *>(img + kPrepH)[12288 + idx] = (__bf16)(at - (float)ah);
+  }
   if (tid < 64) {
     const float Gc = sG[C - 1];
     img[kPrepG + tid] = sG[tid];
@@ -190,6 +201,279 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdParams p) {
     }
   }
   __syncthreads();
+  if (p.dh0)
+    for (int idx = tid; idx < DK * 32; idx += 256) {
+      const int i = idx / 32, c = idx % 32;
+      p.dh0[sb + (size_t)i * DV + c0 + c] = sD[i * LC + c];
+    }
+}
+
+// ----------------------------------------------------------- dh, bf16 MFMA
+// The reverse pass for bf16 inputs on v_mfma_f32_16x16x32_bf16.  K and Q are
+// exact in bf16; every other operand is split x = hi + lo (hi = bf16(x), lo =
+// bf16(x - hi), about 17 significant bits together, with fp32's exponent
+// range, so the scale of dO does not matter).  A product with K or Q takes
+// the other side's two halves (2 MFMAs); a product of two split operands
+// takes hi*hi + hi*lo + lo*hi (3).
+//
+// Every LDS array is row-major.  An operand whose contraction index runs
+// down the rows (K^T, Q^T, dH', dOb, dU, Y) is read with ds_read_b64_tr_b16,
+// so nothing is scattered transposed into LDS.  The next chunk's inputs are
+// fetched into registers while the current chunk computes; barriers are
+// plain s_barrier after this wave's LDS operations, so those loads stay in
+// flight across them.
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma_bf(bf16x8_t a, bf16x8_t b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// fragment lane (g, j) <- X[row][k0 + 8g .. k0 + 8g + 7] (row picked by the caller)
+__device__ __forceinline__ bf16x8_t frag_row(const __bf16 *X, int ld, int row, int k0) {
+  return *reinterpret_cast<const bf16x8_t *>(X + row * ld + k0 + 8 * (lane_id() >> 4));
+}
+
+// fragment lane (g, j) <- X[k0 + 8g + e][n0 + j], e = 0..7: column n0 + j of
+// the row-major X read down eight rows.  Each 16-lane group reads rows
+// k0 + 8g .. +3 (then +4 .. +7) as sixteen 4-element pieces; the transposing
+// read hands lane j element e of the piece read by lane 4e + j/4, entry j%4,
+// so lane t addresses row k0 + 8g + t/4 at columns n0 + 4(t%4).
+__device__ __forceinline__ bf16x8_t frag_col(const __bf16 *X, int ld, int k0, int n0) {
+  const int l = lane_id(), g = l >> 4, t = l & 15;
+  const __bf16 *a = X + (k0 + 8 * g + (t >> 2)) * ld + n0 + 4 * (t & 3);
+  const s16x4 lo = ds_read_tr16(reinterpret_cast<const char *>(a));
+  const s16x4 hi = ds_read_tr16(reinterpret_cast<const char *>(a + 4 * ld));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ void splitb(float x, __bf16 &hi, __bf16 &lo) {
+  hi = (__bf16)x;
+  lo = (__bf16)(x - (float)hi);
+}
+
+// acc += A B over one 32-wide k-step, A and B both split
+__device__ __forceinline__ f32x4 mfma3(bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl, f32x4 c) {
+  c = mfma_bf(ah, bh, c);
+  c = mfma_bf(ah, bl, c);
+  return mfma_bf(al, bh, c);
+}
+
+// barrier after this wave's own LDS operations have completed; outstanding
+// global loads and stores are not waited for
+__device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int DK>
+__global__ __launch_bounds__(256) void bwd_dh_bf16_kernel(BwdParams p) {
+  constexpr int DV = DK, SV = DV / 32, LDK = DK + 16, LT = 72, LO = 48, LC = 36, NKS = DK / 32;
+  constexpr int KP = 64 * DK / 8 / 256;  // 16-byte K (and Q) pieces per thread
+  __shared__ __attribute__((aligned(16))) __bf16 sK[64 * LDK], sQ[64 * LDK];
+  __shared__ __attribute__((aligned(16))) __bf16 sMTh[64 * LT], sMTl[64 * LT], sATh[64 * LT],
+      sATl[64 * LT];
+  // dOb halves; Y's halves take their place once dU is formed
+  __shared__ __attribute__((aligned(16))) __bf16 sOh[64 * LO], sOl[64 * LO];
+  __shared__ __attribute__((aligned(16))) __bf16 sGOh[64 * LO], sGOl[64 * LO], sUh[64 * LO],
+      sUl[64 * LO];
+  __shared__ __attribute__((aligned(16))) __bf16 sDh[DK * LO], sDl[DK * LO];
+  __shared__ __attribute__((aligned(16))) float sD[DK * LC];
+  __shared__ __attribute__((aligned(16))) float sGam[64], sFac[64], sBeta[64];
+  __bf16 *const sYh = sOh, *const sYl = sOl;
+  const int H = p.H;
+  const int sv = blockIdx.x % SV, unit = blockIdx.x / SV;
+  if (unit >= p.N_max * H) return;
+  const int n = seq_by_rank(p.chunk_offsets, p.N_max, unit / H), h = unit % H;
+  if (n < 0) return;
+  const int j0 = p.chunk_offsets[n], j1 = p.chunk_offsets[n + 1];
+  if (j0 == j1) return;
+  const int bos = cu_at(p.cu_seqlens, p.cu64, n), eos = cu_at(p.cu_seqlens, p.cu64, n + 1);
+  const int c0 = sv * 32;
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
+  const int Hqk = p.Hqk, hq = h / (H / Hqk);
+  const size_t mat = (size_t)DK * DV;
+  const size_t sb = ((size_t)n * H + h) * mat;
+
+  // one chunk's inputs in registers
+  u32x4 rk[KP], rq[KP], rimg[8];
+  f32x4 rdo[2];
+  float rgo[2], rvec = 0.f;
+  auto fetch = [&](int jj) {
+    const int r0 = bos + (jj - j0) * kBT, C = min(kBT, eos - r0);
+    const float *img = p.prep + ((size_t)jj * H + h) * kPrepFloats;
+#pragma unroll
+    for (int it = 0; it < KP; ++it) {
+      const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+      const size_t off = ((size_t)(r0 + r) * Hqk + hq) * DK + c;
+      rk[it] = rq[it] = u32x4{0u, 0u, 0u, 0u};
+      if (r < C) {
+        rk[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.k) + off);
+        rq[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.q) + off);
+      }
+    }
+    const u32x4 *imh = reinterpret_cast<const u32x4 *>(img + kPrepH);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) rimg[it] = imh[tid + 256 * it];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int pc = tid + 256 * it, r = pc / 8, c = (pc % 8) * 4;
+      rdo[it] = r < C ? *reinterpret_cast<const f32x4 *>(p.dout + ((size_t)(r0 + r) * H + h) * DV + c0 + c)
+                      : zero4();
+      rgo[it] = img[kPrepGam + r];
+    }
+    if (tid < 192) rvec = img[kPrepGam + tid];  // gam, fac, beta: consecutive in the image
+  };
+  static_assert(kPrepFac == kPrepGam + 64 && kPrepBeta == kPrepFac + 64, "gate vectors");
+
+  // the state gradient: fp32 [DK][32] and its halves
+  for (int idx = tid; idx < DK * 32; idx += 256) {
+    const int i = idx / 32, c = idx % 32;
+    const float v = p.dht ? p.dht[sb + (size_t)i * DV + c0 + c] : 0.f;
+    sD[i * LC + c] = v;
+    splitb(v, sDh[i * LO + c], sDl[i * LO + c]);
+  }
+  fetch(j1 - 1);
+  for (int jj = j1 - 1; jj >= j0; --jj) {
+    sync_lds();
+    const int r0 = bos + (jj - j0) * kBT, C = min(kBT, eos - r0);
+#pragma unroll
+    for (int it = 0; it < KP; ++it) {
+      const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+      *reinterpret_cast<u32x4 *>(sK + r * LDK + c) = rk[it];
+      *reinterpret_cast<u32x4 *>(sQ + r * LDK + c) = rq[it];
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int pc = tid + 256 * it, a = pc >> 9, r = (pc & 511) / 8, c = (pc % 8) * 8;
+      __bf16 *dst = a == 0 ? sMTh : a == 1 ? sMTl : a == 2 ? sATh : sATl;
+      *reinterpret_cast<u32x4 *>(dst + r * LT + c) = rimg[it];
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int pc = tid + 256 * it, r = pc / 8, c = (pc % 8) * 4;
+      bf16x4_t oh, ol, gh, gl;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float v = p.scale * rdo[it][e];
+        const float gv = rgo[it] * v;
+        oh[e] = (__bf16)v;
+        ol[e] = (__bf16)(v - (float)oh[e]);
+        gh[e] = (__bf16)gv;
+        gl[e] = (__bf16)(gv - (float)gh[e]);
+      }
+      *reinterpret_cast<bf16x4_t *>(sOh + r * LO + c) = oh;
+      *reinterpret_cast<bf16x4_t *>(sOl + r * LO + c) = ol;
+      *reinterpret_cast<bf16x4_t *>(sGOh + r * LO + c) = gh;
+      *reinterpret_cast<bf16x4_t *>(sGOl + r * LO + c) = gl;
+    }
+    if (tid < 64) sGam[tid] = rvec;
+    else if (tid < 128) sFac[tid - 64] = rvec;
+    else if (tid < 192) sBeta[tid - 128] = rvec;
+    // the gradient leaving this chunk, for the part kernel
+    float *dst = p.dhs + ((size_t)jj * H + h) * mat + c0;
+#pragma unroll
+    for (int it = 0; it < DK * 8 / 256; ++it) {
+      const int pc = tid + 256 * it, i = pc / 8, c = (pc % 8) * 4;
+      *reinterpret_cast<f32x4 *>(dst + (size_t)i * DV + c) =
+          *reinterpret_cast<const f32x4 *>(sD + i * LC + c);
+    }
+    if (jj > j0) fetch(jj - 1);
+    sync_lds();
+    // dU = M^T dOb + fac * (K dH'): wave w, rows 16w, both column tiles
+    {
+      f32x4 kd[2] = {zero4(), zero4()}, du[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const bf16x8_t a = frag_row(sK, LDK, 16 * w + lr, 32 * s);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          kd[nt] = mfma_bf(a, frag_col(sDh, LO, 32 * s, 16 * nt), kd[nt]);
+          kd[nt] = mfma_bf(a, frag_col(sDl, LO, 32 * s, 16 * nt), kd[nt]);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8_t ah = frag_row(sMTh, LT, 16 * w + lr, 32 * s);
+        const bf16x8_t al = frag_row(sMTl, LT, 16 * w + lr, 32 * s);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          du[nt] = mfma3(ah, al, frag_col(sOh, LO, 32 * s, 16 * nt), frag_col(sOl, LO, 32 * s, 16 * nt),
+                         du[nt]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * w + 4 * lg + i, c = 16 * nt + lr;
+          splitb(du[nt][i] + sFac[r] * kd[nt][i], sUh[r * LO + c], sUl[r * LO + c]);
+        }
+    }
+    sync_lds();
+    // dX = beta * (A^-T dU); Y = gam * dX (over dOb, read by now)
+    {
+      f32x4 dx[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8_t ah = frag_row(sATh, LT, 16 * w + lr, 32 * s);
+        const bf16x8_t al = frag_row(sATl, LT, 16 * w + lr, 32 * s);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          dx[nt] = mfma3(ah, al, frag_col(sUh, LO, 32 * s, 16 * nt), frag_col(sUl, LO, 32 * s, 16 * nt),
+                         dx[nt]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * w + 4 * lg + i, c = 16 * nt + lr;
+          splitb(sGam[r] * sBeta[r] * dx[nt][i], sYh[r * LO + c], sYl[r * LO + c]);
+        }
+    }
+    sync_lds();
+    // dH = gam_C dH' + Q^T (gam dOb) - K^T Y
+    {
+      const float gamC = sGam[C - 1];
+      bf16x8_t bgh[2][2], bgl[2][2], byh[2][2], byl[2][2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          bgh[s][nt] = frag_col(sGOh, LO, 32 * s, 16 * nt);
+          bgl[s][nt] = frag_col(sGOl, LO, 32 * s, 16 * nt);
+          byh[s][nt] = frag_col(sYh, LO, 32 * s, 16 * nt);
+          byl[s][nt] = frag_col(sYl, LO, 32 * s, 16 * nt);
+        }
+#pragma unroll
+      for (int tt = 0; tt < DK / 64; ++tt) {
+        const int t = w + 4 * tt;
+        f32x4 acc[2], ky[2] = {zero4(), zero4()};
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[nt][i] = gamC * sD[(16 * t + 4 * lg + i) * LC + 16 * nt + lr];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8_t aq = frag_col(sQ, LDK, 32 * s, 16 * t);
+          const bf16x8_t ak = frag_col(sK, LDK, 32 * s, 16 * t);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            acc[nt] = mfma_bf(aq, bgh[s][nt], acc[nt]);
+            acc[nt] = mfma_bf(aq, bgl[s][nt], acc[nt]);
+            ky[nt] = mfma_bf(ak, byh[s][nt], ky[nt]);
+            ky[nt] = mfma_bf(ak, byl[s][nt], ky[nt]);
+          }
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * t + 4 * lg + i, c = 16 * nt + lr;
+            const float v = acc[nt][i] - ky[nt][i];
+            sD[row * LC + c] = v;
+            splitb(v, sDh[row * LO + c], sDl[row * LO + c]);
+          }
+      }
+    }
+  }
+  sync_lds();
   if (p.dh0)
     for (int idx = tid; idx < DK * 32; idx += 256) {
       const int i = idx / 32, c = idx % 32;
@@ -478,7 +762,10 @@ hipError_t launch_all(const BwdParams &p, hipStream_t st) {
   const int cells = p.NT * p.H;
   hipLaunchKernelGGL((bwd_prep_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  hipLaunchKernelGGL((bwd_dh_kernel<In, DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
+  if constexpr (std::is_same_v<In, bf16>)
+    hipLaunchKernelGGL((bwd_dh_bf16_kernel<DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_dh_kernel<In, DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL((bwd_part_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
