@@ -73,10 +73,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
       sS[r * kL + s] = Sv;
       img[kPrepS + r * 64 + s] = Sv;
       img[kPrepM + r * 64 + s] = Mv;
-      __bf16 *mt = reinterpret_cast<__bf16 *>(img + kPrepH) + s * 64 + r;  // M^T
-      const __bf16 mh = (__bf16)Mv;
-      mt[0] = mh;
-      mt[4096] = (__bf16)(Mv - (float)mh);
+      if constexpr (std::is_same_v<In, bf16>) {
+        __bf16 *mb = reinterpret_cast<__bf16 *>(img + kPrepH) + r * 64 + s;
+        const __bf16 mh = (__bf16)Mv;
+        mb[0] = mh;
+        mb[4096] = (__bf16)(Mv - (float)mh);
+      }
     }
   }
   __syncthreads();
@@ -85,10 +87,12 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   for (int idx = tid; idx < 64 * 64; idx += 256) {
     const int r = idx >> 6, c = idx & 63;
     img[kPrepA + idx] = sX[r * kL + c];
-    const float at = sX[c * kL + r];  // (A^-1)^T
-    const __bf16 ah = (__bf16)at;
-    reinterpret_cast<__bf16 *>(img + kPrepH)[8192 + idx] = ah;
-    reinterpret_cast<__bf16 *>(img + kPrepH)[12288 + idx] = (__bf16)(at - (float)ah);
+    if constexpr (std::is_same_v<In, bf16>) {
+      const float at = sX[r * kL + c] * sB[c];  // A^-1 diag(beta)
+      const __bf16 ah = (__bf16)at;
+      reinterpret_cast<__bf16 *>(img + kPrepH)[8192 + idx] = ah;
+      reinterpret_cast<__bf16 *>(img + kPrepH)[12288 + idx] = (__bf16)(at - (float)ah);
+    }
   }
   if (tid < 64) {
     const float Gc = sG[C - 1];
@@ -268,15 +272,16 @@ __global__ __launch_bounds__(256) void bwd_dh_bf16_kernel(BwdParams p) {
   constexpr int DV = DK, SV = DV / 32, LDK = DK + 16, LT = 72, LO = 48, LC = 36, NKS = DK / 32;
   constexpr int KP = 64 * DK / 8 / 256;  // 16-byte K (and Q) pieces per thread
   __shared__ __attribute__((aligned(16))) __bf16 sK[64 * LDK], sQ[64 * LDK];
-  __shared__ __attribute__((aligned(16))) __bf16 sMTh[64 * LT], sMTl[64 * LT], sATh[64 * LT],
-      sATl[64 * LT];
+  // M and A~ = A^-1 diag(beta), both halves; M^T and A~^T are read transposed
+  __shared__ __attribute__((aligned(16))) __bf16 sMh[64 * LT], sMl[64 * LT], sAh[64 * LT],
+      sAl[64 * LT];
   // dOb halves; Y's halves take their place once dU is formed
   __shared__ __attribute__((aligned(16))) __bf16 sOh[64 * LO], sOl[64 * LO];
   __shared__ __attribute__((aligned(16))) __bf16 sGOh[64 * LO], sGOl[64 * LO], sUh[64 * LO],
       sUl[64 * LO];
   __shared__ __attribute__((aligned(16))) __bf16 sDh[DK * LO], sDl[DK * LO];
   __shared__ __attribute__((aligned(16))) float sD[DK * LC];
-  __shared__ __attribute__((aligned(16))) float sGam[64], sFac[64], sBeta[64];
+  __shared__ __attribute__((aligned(16))) float sGam[64], sFac[64];
   __bf16 *const sYh = sOh, *const sYl = sOl;
   const int H = p.H;
   const int sv = blockIdx.x % SV, unit = blockIdx.x / SV;
@@ -319,9 +324,9 @@ __global__ __launch_bounds__(256) void bwd_dh_bf16_kernel(BwdParams p) {
                       : zero4();
       rgo[it] = img[kPrepGam + r];
     }
-    if (tid < 192) rvec = img[kPrepGam + tid];  // gam, fac, beta: consecutive in the image
+    if (tid < 128) rvec = img[kPrepGam + tid];  // gam, fac: consecutive in the image
   };
-  static_assert(kPrepFac == kPrepGam + 64 && kPrepBeta == kPrepFac + 64, "gate vectors");
+  static_assert(kPrepFac == kPrepGam + 64, "gate vectors");
 
   // the state gradient: fp32 [DK][32] and its halves
   for (int idx = tid; idx < DK * 32; idx += 256) {
@@ -343,7 +348,7 @@ __global__ __launch_bounds__(256) void bwd_dh_bf16_kernel(BwdParams p) {
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
       const int pc = tid + 256 * it, a = pc >> 9, r = (pc & 511) / 8, c = (pc % 8) * 8;
-      __bf16 *dst = a == 0 ? sMTh : a == 1 ? sMTl : a == 2 ? sATh : sATl;
+      __bf16 *dst = a == 0 ? sMh : a == 1 ? sMl : a == 2 ? sAh : sAl;
       *reinterpret_cast<u32x4 *>(dst + r * LT + c) = rimg[it];
     }
 #pragma unroll
@@ -366,7 +371,6 @@ __global__ __launch_bounds__(256) void bwd_dh_bf16_kernel(BwdParams p) {
     }
     if (tid < 64) sGam[tid] = rvec;
     else if (tid < 128) sFac[tid - 64] = rvec;
-    else if (tid < 192) sBeta[tid - 128] = rvec;
     // the gradient leaving this chunk, for the part kernel
     float *dst = p.dhs + ((size_t)jj * H + h) * mat + c0;
 #pragma unroll
@@ -391,8 +395,8 @@ __global__ __launch_bounds__(256) void bwd_dh_bf16_kernel(BwdParams p) {
       }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8_t ah = frag_row(sMTh, LT, 16 * w + lr, 32 * s);
-        const bf16x8_t al = frag_row(sMTl, LT, 16 * w + lr, 32 * s);
+        const bf16x8_t ah = frag_col(sMh, LT, 32 * s, 16 * w);
+        const bf16x8_t al = frag_col(sMl, LT, 32 * s, 16 * w);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
           du[nt] = mfma3(ah, al, frag_col(sOh, LO, 32 * s, 16 * nt), frag_col(sOl, LO, 32 * s, 16 * nt),
@@ -407,13 +411,13 @@ __global__ __launch_bounds__(256) void bwd_dh_bf16_kernel(BwdParams p) {
         }
     }
     sync_lds();
-    // dX = beta * (A^-T dU); Y = gam * dX (over dOb, read by now)
+    // dX = beta * (A^-T dU) = A~^T dU; Y = gam * dX (over dOb, read by now)
     {
       f32x4 dx[2] = {zero4(), zero4()};
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8_t ah = frag_row(sATh, LT, 16 * w + lr, 32 * s);
-        const bf16x8_t al = frag_row(sATl, LT, 16 * w + lr, 32 * s);
+        const bf16x8_t ah = frag_col(sAh, LT, 32 * s, 16 * w);
+        const bf16x8_t al = frag_col(sAl, LT, 32 * s, 16 * w);
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
           dx[nt] = mfma3(ah, al, frag_col(sUh, LO, 32 * s, 16 * nt), frag_col(sUl, LO, 32 * s, 16 * nt),
@@ -424,7 +428,7 @@ __global__ __launch_bounds__(256) void bwd_dh_bf16_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 16 * w + 4 * lg + i, c = 16 * nt + lr;
-          splitb(sGam[r] * sBeta[r] * dx[nt][i], sYh[r * LO + c], sYl[r * LO + c]);
+          splitb(sGam[r] * dx[nt][i], sYh[r * LO + c], sYl[r * LO + c]);
         }
     }
     sync_lds();
@@ -586,6 +590,228 @@ __global__ __launch_bounds__(256) void bwd_part_kernel(BwdParams p) {
   if (tid == 0) {
     float s = 0.f;
     for (int i = 0; i < 256; ++i) s += sRed[i];
+    gw[part_sh(DK)] = s;
+  }
+}
+
+// ------------------------------------------------------------ part, bf16
+// The same products for bf16 inputs on bf16 MFMA with split operands, 512
+// threads over 32-column blocks of d_v.  Per block: KH, K dH' and M^T dOb
+// give X = V - gam*KH and dU = M^T dOb + fac*(K dH'); then U = A~ X and
+// dX = A~^T dU with A~ = A^-1 diag(beta) (dX is dV); then the products
+// contracted over the block's columns accumulate in registers.  The next
+// block's H, dH', dO and V are fetched into registers during the current one.
+template <int DK>
+__global__ __launch_bounds__(512) void bwd_part_bf16_kernel(BwdParams p) {
+  constexpr int DV = DK, LDK = DK + 16, LT = 72, NB = 32, LB = NB + 8, NBLK = DV / NB, NKS = DK / 32;
+  constexpr int KP = 64 * DK / 8 / 512;  // 16-byte K pieces per thread
+  constexpr int HP = DK * NB / 4 / 512;  // float4 pieces of an H (or dH') block per thread
+  constexpr int PT = DK / 32;            // column tiles of P1..P3 per wave
+  __shared__ __attribute__((aligned(16))) __bf16 sK[64 * LDK];
+  __shared__ __attribute__((aligned(16))) __bf16 sMh[64 * LT], sMl[64 * LT], sAh[64 * LT], sAl[64 * LT];
+  __shared__ __attribute__((aligned(16))) __bf16 sHh[DK * LB], sHl[DK * LB], sDh[DK * LB], sDl[DK * LB];
+  __shared__ __attribute__((aligned(16))) __bf16 sOh[64 * LB], sOl[64 * LB], sXh[64 * LB], sXl[64 * LB];
+  __shared__ __attribute__((aligned(16))) __bf16 sGh[64 * LB], sGl[64 * LB], sUh[64 * LB], sUl[64 * LB];
+  __shared__ __attribute__((aligned(16))) __bf16 sEh[64 * LB], sEl[64 * LB], sV[64 * LB];  // dX, V
+  __shared__ __attribute__((aligned(16))) float sGam[64], sFac[64], sRed[8];
+  const int H = p.H;
+  const int slot = blockIdx.x / H, h = blockIdx.x % H;
+  Chunk ch;
+  if (!chunk_of(p, slot, ch)) return;
+  const int C = ch.C, r0 = ch.r0;
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
+  const int rt = w & 3, half = w >> 2;  // row tile; column half
+  const int Hqk = p.Hqk, hq = h / (H / Hqk);
+  const float *img = p.prep + (size_t)blockIdx.x * kPrepFloats;
+  const size_t mat = (size_t)DK * DV;
+  const float *Hs = p.hs + (size_t)blockIdx.x * mat;
+  const float *Ds = p.dhs + (size_t)blockIdx.x * mat;
+
+  // the cell's K, M and A~ halves, gam and fac: straight into LDS
+  {
+    u32x4 rk[KP], rimg[4];
+    float rvec = 0.f;
+#pragma unroll
+    for (int it = 0; it < KP; ++it) {
+      const int pc = tid + 512 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+      rk[it] = u32x4{0u, 0u, 0u, 0u};
+      if (r < C)
+        rk[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.k) +
+                                                   ((size_t)(r0 + r) * Hqk + hq) * DK + c);
+    }
+    const u32x4 *imh = reinterpret_cast<const u32x4 *>(img + kPrepH);
+#pragma unroll
+    for (int it = 0; it < 4; ++it) rimg[it] = imh[tid + 512 * it];
+    if (tid < 128) rvec = img[kPrepGam + tid];
+    static_assert(kPrepFac == kPrepGam + 64, "gate vectors");
+#pragma unroll
+    for (int it = 0; it < KP; ++it) {
+      const int pc = tid + 512 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+      *reinterpret_cast<u32x4 *>(sK + r * LDK + c) = rk[it];
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int pc = tid + 512 * it, a = pc >> 9, r = (pc & 511) / 8, c = (pc % 8) * 8;
+      __bf16 *dst = a == 0 ? sMh : a == 1 ? sMl : a == 2 ? sAh : sAl;
+      *reinterpret_cast<u32x4 *>(dst + r * LT + c) = rimg[it];
+    }
+    if (tid < 64) sGam[tid] = rvec;
+    else if (tid < 128) sFac[tid - 64] = rvec;
+  }
+
+  // one column block's inputs in registers
+  f32x4 rh[HP], rd[HP], ro = zero4();
+  u32x4 rv = u32x4{0u, 0u, 0u, 0u};
+  auto fetch = [&](int cb) {
+    const int cc = NB * cb;
+#pragma unroll
+    for (int it = 0; it < HP; ++it) {
+      const int pc = tid + 512 * it, i = pc / (NB / 4), c = (pc % (NB / 4)) * 4;
+      rh[it] = *reinterpret_cast<const f32x4 *>(Hs + (size_t)i * DV + cc + c);
+      rd[it] = *reinterpret_cast<const f32x4 *>(Ds + (size_t)i * DV + cc + c);
+    }
+    {
+      const int r = tid / (NB / 4), c = (tid % (NB / 4)) * 4;  // 64 rows x 8 pieces
+      ro = r < C ? *reinterpret_cast<const f32x4 *>(p.dout + ((size_t)(r0 + r) * H + h) * DV + cc + c)
+                 : zero4();
+    }
+    if (tid < 64 * NB / 8) {
+      const int r = tid / (NB / 8), c = (tid % (NB / 8)) * 8;
+      rv = r < C ? *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.v) +
+                                                     ((size_t)(r0 + r) * H + h) * DV + cc + c)
+                 : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto put4 = [](__bf16 *hi, __bf16 *lo, f32x4 v) {
+    bf16x4_t a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = (__bf16)v[e];
+      b[e] = (__bf16)(v[e] - (float)a[e]);
+    }
+    *reinterpret_cast<bf16x4_t *>(hi) = a;
+    *reinterpret_cast<bf16x4_t *>(lo) = b;
+  };
+
+  f32x4 P1[PT], P2[PT], P3[PT], dM[2], dT[2];
+#pragma unroll
+  for (int t = 0; t < PT; ++t) P1[t] = P2[t] = P3[t] = zero4();
+  dM[0] = dM[1] = dT[0] = dT[1] = zero4();
+  float shd = 0.f;
+  fetch(0);
+  for (int cb = 0; cb < NBLK; ++cb) {
+    sync_lds();
+#pragma unroll
+    for (int it = 0; it < HP; ++it) {
+      const int pc = tid + 512 * it, i = pc / (NB / 4), c = (pc % (NB / 4)) * 4;
+      put4(sHh + i * LB + c, sHl + i * LB + c, rh[it]);
+      put4(sDh + i * LB + c, sDl + i * LB + c, rd[it]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) shd += rh[it][e] * rd[it][e];
+    }
+    {
+      const int r = tid / (NB / 4), c = (tid % (NB / 4)) * 4;
+      put4(sOh + r * LB + c, sOl + r * LB + c, ro * p.scale);
+    }
+    if (tid < 64 * NB / 8) {
+      const int r = tid / (NB / 8), c = (tid % (NB / 8)) * 8;
+      *reinterpret_cast<u32x4 *>(sV + r * LB + c) = rv;
+    }
+    if (cb + 1 < NBLK) fetch(cb + 1);
+    sync_lds();
+    // X = V - gam*(K H), dU = M^T dOb + fac*(K dH'): rows 16rt, columns 16half
+    {
+      f32x4 kh = zero4(), kd = zero4(), mo = zero4();
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const bf16x8_t a = frag_row(sK, LDK, 16 * rt + lr, 32 * s);
+        kh = mfma_bf(a, frag_col(sHh, LB, 32 * s, 16 * half), kh);
+        kh = mfma_bf(a, frag_col(sHl, LB, 32 * s, 16 * half), kh);
+        kd = mfma_bf(a, frag_col(sDh, LB, 32 * s, 16 * half), kd);
+        kd = mfma_bf(a, frag_col(sDl, LB, 32 * s, 16 * half), kd);
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        mo = mfma3(frag_col(sMh, LT, 32 * s, 16 * rt), frag_col(sMl, LT, 32 * s, 16 * rt),
+                   frag_col(sOh, LB, 32 * s, 16 * half), frag_col(sOl, LB, 32 * s, 16 * half), mo);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i, c = 16 * half + lr;
+        const float x = (float)sV[r * LB + c] - sGam[r] * kh[i];
+        splitb(x, sXh[r * LB + c], sXl[r * LB + c]);
+        splitb(mo[i] + sFac[r] * kd[i], sGh[r * LB + c], sGl[r * LB + c]);
+      }
+    }
+    sync_lds();
+    // U = A~ X, dX = A~^T dU (= dV)
+    {
+      f32x4 u = zero4(), dx = zero4();
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        u = mfma3(frag_row(sAh, LT, 16 * rt + lr, 32 * s), frag_row(sAl, LT, 16 * rt + lr, 32 * s),
+                  frag_col(sXh, LB, 32 * s, 16 * half), frag_col(sXl, LB, 32 * s, 16 * half), u);
+        dx = mfma3(frag_col(sAh, LT, 32 * s, 16 * rt), frag_col(sAl, LT, 32 * s, 16 * rt),
+                   frag_col(sGh, LB, 32 * s, 16 * half), frag_col(sGl, LB, 32 * s, 16 * half), dx);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i, c = 16 * half + lr;
+        splitb(u[i], sUh[r * LB + c], sUl[r * LB + c]);
+        splitb(dx[i], sEh[r * LB + c], sEl[r * LB + c]);
+        if (r < C) p.dv[((size_t)(r0 + r) * H + h) * DV + NB * cb + c] = dx[i];
+      }
+    }
+    sync_lds();
+    // contracted over this block's columns: P1 += dOb H^T, P2 += dX H^T,
+    // P3 += U dH'^T (column tiles PT half ..), dM += dOb U^T,
+    // dT += dU X^T (column tiles 2half, 2half+1)
+    {
+      const int ar = 16 * rt + lr;
+      const bf16x8_t oh = frag_row(sOh, LB, ar, 0), ol = frag_row(sOl, LB, ar, 0);
+      const bf16x8_t eh = frag_row(sEh, LB, ar, 0), el = frag_row(sEl, LB, ar, 0);
+      const bf16x8_t uh = frag_row(sUh, LB, ar, 0), ul = frag_row(sUl, LB, ar, 0);
+      const bf16x8_t gh = frag_row(sGh, LB, ar, 0), gl = frag_row(sGl, LB, ar, 0);
+#pragma unroll
+      for (int t = 0; t < PT; ++t) {
+        const int br = 16 * (PT * half + t) + lr;
+        const bf16x8_t hh = frag_row(sHh, LB, br, 0), hl = frag_row(sHl, LB, br, 0);
+        P1[t] = mfma3(oh, ol, hh, hl, P1[t]);
+        P2[t] = mfma3(eh, el, hh, hl, P2[t]);
+        P3[t] = mfma3(uh, ul, frag_row(sDh, LB, br, 0), frag_row(sDl, LB, br, 0), P3[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        const int br = 16 * (2 * half + t) + lr;
+        dM[t] = mfma3(oh, ol, frag_row(sUh, LB, br, 0), frag_row(sUl, LB, br, 0), dM[t]);
+        dT[t] = mfma3(gh, gl, frag_row(sXh, LB, br, 0), frag_row(sXl, LB, br, 0), dT[t]);
+      }
+    }
+  }
+  float *gw = p.part + (size_t)blockIdx.x * part_floats(DK);
+#pragma unroll
+  for (int t = 0; t < PT; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rt + 4 * lg + i, c = 16 * (PT * half + t) + lr;
+      gw[kPartP1 + r * DK + c] = P1[t][i];
+      gw[part_p2(DK) + r * DK + c] = P2[t][i];
+      gw[part_p3(DK) + r * DK + c] = P3[t][i];
+    }
+#pragma unroll
+  for (int t = 0; t < 2; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * rt + 4 * lg + i, c = 16 * (2 * half + t) + lr;
+      gw[part_dm(DK) + r * 64 + c] = dM[t][i];
+      gw[part_dt(DK) + r * 64 + c] = dT[t][i];
+    }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) shd += __shfl_xor(shd, o);
+  if (l == 0) sRed[w] = shd;
+  sync_lds();
+  if (tid == 0) {
+    float s = 0.f;
+    for (int i = 0; i < 8; ++i) s += sRed[i];
     gw[part_sh(DK)] = s;
   }
 }
@@ -767,7 +993,10 @@ hipError_t launch_all(const BwdParams &p, hipStream_t st) {
   else
     hipLaunchKernelGGL((bwd_dh_kernel<In, DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  hipLaunchKernelGGL((bwd_part_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
+  if constexpr (std::is_same_v<In, bf16>)
+    hipLaunchKernelGGL((bwd_part_bf16_kernel<DK>), dim3(cells), dim3(512), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_part_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL((bwd_final_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
   return hipGetLastError();

@@ -86,9 +86,9 @@ struct ConvParams {
 // state entering / the state gradient leaving the chunk, [d][d] fp32.
 constexpr int kPrepA = 0, kPrepM = 4096, kPrepS = 8192, kPrepG = 12288, kPrepGam = 12352,
               kPrepFac = 12416, kPrepBeta = 12480;
-// then bf16 high and low halves of M^T and A^-T for the reverse pass of
-// bf16 inputs: [64][64] each, in the order M^T hi, M^T lo, A^-T hi, A^-T lo,
-// from float offset kPrepH
+// then, for bf16 inputs, bf16 high and low halves of M and of
+// A^-1 diag(beta), row-major [64][64] each, in the order M hi, M lo,
+// A^-1 diag(beta) hi, lo, from float offset kPrepH
 constexpr int kPrepH = 12544, kPrepFloats = kPrepH + 4 * 4096 / 2;
 constexpr int kPartP1 = 0;
 __host__ __device__ constexpr int part_p2(int d) { return 64 * d; }
