@@ -983,6 +983,276 @@ __global__ __launch_bounds__(256) void bwd_final_kernel(BwdParams p) {
   }
 }
 
+// ----------------------------------------------------------- final, bf16
+// The same chunk-local algebra for bf16 inputs.  Elementwise terms come
+// straight from registers (every global read is issued at the start), row
+// sums are wave reductions and column sums go through a [4][64] table; the
+// products run on bf16 MFMA with split operands.  F and F^T are folded into
+// one matrix F + F^T, and K, Q take the place of A^-1 and tmp once those are
+// read, so the block holds 72 KiB of LDS and two blocks share a CU.
+__device__ __forceinline__ float sum16(float x) {  // over the 16 lanes of a row group
+#pragma unroll
+  for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int m = 1; m < 64; m <<= 1) x += __shfl_xor(x, m, 64);
+  return x;
+}
+
+template <int DK>
+__global__ __launch_bounds__(256, 2) void bwd_final_bf16_kernel(BwdParams p) {
+  constexpr int NT = DK / 16, LT = 72, LDK = DK + 16, PAIR = 2 * 64 * LT;
+  constexpr int KP = 64 * DK / 8 / 256;  // 16-byte K (and Q) pieces per thread
+  static_assert(64 * LDK <= PAIR, "K and Q fit over A^-1 and tmp");
+  // [A^-1 hi, lo][tmp hi, lo][dT diag(beta) hi, lo -> F + F^T hi, lo][dM*E hi, lo]
+  __shared__ __attribute__((aligned(16))) __bf16 smem[4 * PAIR];
+  __shared__ __attribute__((aligned(16))) float sG[64], sGam[64], sFac[64], sBeta[64];
+  __shared__ __attribute__((aligned(16))) float cs[3][4][64];  // column partials: bt, zc, yc
+  __shared__ __attribute__((aligned(16))) float vr[3][64];     // row sums: zr, ba, yr
+  __shared__ __attribute__((aligned(16))) float dG[64], t3s[64];
+  __bf16 *const sAh = smem, *const sAl = smem + 64 * LT;
+  __bf16 *const sTh = smem + PAIR, *const sTl = smem + PAIR + 64 * LT;
+  __bf16 *const sDh = smem + 2 * PAIR, *const sDl = smem + 2 * PAIR + 64 * LT;  // dT', then F + F^T
+  __bf16 *const sEh = smem + 3 * PAIR, *const sEl = smem + 3 * PAIR + 64 * LT;  // dM * E
+  __bf16 *const sK = smem, *const sQ = smem + PAIR;
+  const int H = p.H;
+  const int slot = blockIdx.x / H, h = blockIdx.x % H;
+  Chunk ch;
+  if (!chunk_of(p, slot, ch)) return;
+  const int C = ch.C, r0 = ch.r0;
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
+  const int Hqk = p.Hqk, hq = h / (H / Hqk);
+  const float *img = p.prep + (size_t)blockIdx.x * kPrepFloats;
+  const float *gw = p.part + (size_t)blockIdx.x * part_floats(DK);
+
+  // every global read of the algebra, issued together
+  u32x4 rk[KP], rq[KP];
+#pragma unroll
+  for (int it = 0; it < KP; ++it) {
+    const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+    rk[it] = rq[it] = u32x4{0u, 0u, 0u, 0u};
+    if (r < C) {
+      const size_t off = ((size_t)(r0 + r) * Hqk + hq) * DK + c;
+      rk[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.k) + off);
+      rq[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.q) + off);
+    }
+  }
+  // elementwise entries: row w + 4e, column l
+  float ea[16], em[16], edm[16], edt[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int o = (w + 4 * e) * 64 + l;
+    ea[e] = img[kPrepA + o];
+    em[e] = img[kPrepM + o];
+    edm[e] = gw[part_dm(DK) + o];
+    edt[e] = gw[part_dt(DK) + o];
+  }
+  // S at this lane's tile positions of the dA product
+  float eS[4][4];
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) eS[s4][i] = img[kPrepS + (16 * w + 4 * lg + i) * 64 + 16 * s4 + lr];
+  if (tid < 64) {
+    sG[tid] = img[kPrepG + tid];
+    sGam[tid] = img[kPrepGam + tid];
+    sFac[tid] = img[kPrepFac + tid];
+    sBeta[tid] = img[kPrepBeta + tid];
+  }
+  sync_lds();
+
+  // Z = dM * M (gates), dT * A^-1 (beta); A^-1, dT' = dT diag(beta) and
+  // dM * E, split, over the lower triangle of real rows
+  {
+    float bt = 0.f, zc = 0.f;
+    const float gs = sG[l], bs = sBeta[l];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int r = w + 4 * e, o = r * LT + l;
+      const bool lo = l <= r && r < C;
+      const float z = lo ? edm[e] * em[e] : 0.f;
+      bt += lo ? edt[e] * ea[e] : 0.f;
+      zc += z;
+      const float zr = wave_sum(z);
+      if (l == 0) vr[0][r] = zr;
+      splitb(ea[e], sAh[o], sAl[o]);
+      splitb(lo ? edt[e] * bs : 0.f, sDh[o], sDl[o]);
+      splitb(lo ? edm[e] * __expf(sG[r] - gs) : 0.f, sEh[o], sEl[o]);
+    }
+    cs[0][w][l] = bt;
+    cs[1][w][l] = zc;
+  }
+  sync_lds();
+  // tmp = dT' A^-T: rows 16w
+  {
+    f32x4 t[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8_t ah = frag_row(sDh, LT, 16 * w + lr, 32 * s), al = frag_row(sDl, LT, 16 * w + lr, 32 * s);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        t[s4] = mfma3(ah, al, frag_row(sAh, LT, 16 * s4 + lr, 32 * s), frag_row(sAl, LT, 16 * s4 + lr, 32 * s),
+                      t[s4]);
+    }
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = (16 * w + 4 * lg + i) * LT + 16 * s4 + lr;
+        splitb(t[s4][i], sTh[o], sTl[o]);
+      }
+  }
+  sync_lds();
+  // dA = -A^-T tmp; strict lower part: W = dA S (beta), Y = beta dA S
+  // (gates), F = beta dA E (keys), stored as F + F^T over dT'
+  {
+    f32x4 t[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8_t ah = frag_col(sAh, LT, 32 * s, 16 * w), al = frag_col(sAl, LT, 32 * s, 16 * w);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4)
+        t[s4] = mfma3(ah, al, frag_col(sTh, LT, 32 * s, 16 * s4), frag_col(sTl, LT, 32 * s, 16 * s4), t[s4]);
+    }
+    float wr[4] = {0.f, 0.f, 0.f, 0.f}, yr[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int s = 16 * s4 + lr;
+      float yc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * lg + i;
+        const bool sl = s < r && r < C;
+        const float dA = -t[s4][i];
+        const float Wv = sl ? dA * eS[s4][i] : 0.f;
+        const float Yv = sBeta[r] * Wv;
+        const float Fv = sl ? sBeta[r] * dA * __expf(sG[r] - sG[s]) : 0.f;
+        wr[i] += Wv;
+        yr[i] += Yv;
+        yc += Yv;
+        if (s < r) {
+          splitb(Fv, sDh[r * LT + s], sDl[r * LT + s]);
+          splitb(Fv, sDh[s * LT + r], sDl[s * LT + r]);
+        } else if (s == r) {
+          sDh[r * LT + r] = sDl[r * LT + r] = (__bf16)0.f;
+        }
+      }
+      yc += __shfl_xor(yc, 16, 64);
+      yc += __shfl_xor(yc, 32, 64);
+      if (lg == 0) cs[2][w][s] = yc;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      wr[i] = sum16(wr[i]);
+      yr[i] = sum16(yr[i]);
+      if (lr == 0) {
+        vr[1][16 * w + 4 * lg + i] = wr[i];
+        vr[2][16 * w + 4 * lg + i] = yr[i];
+      }
+    }
+  }
+  sync_lds();
+  // K and Q over A^-1 and tmp
+#pragma unroll
+  for (int it = 0; it < KP; ++it) {
+    const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+    *reinterpret_cast<u32x4 *>(sK + r * LDK + c) = rk[it];
+    *reinterpret_cast<u32x4 *>(sQ + r * LDK + c) = rq[it];
+  }
+  sync_lds();
+  // dQ = gam P1 + (dM E) K;  dK = -gam P2 + fac P3 + (dM E)^T Q + (F + F^T) K,
+  // and the gate dots <q_r, P1_r>, <k_r, P2_r>, <k_r, P3_r>, per column tile
+  const float *P1 = gw + kPartP1, *P2 = gw + part_p2(DK), *P3 = gw + part_p3(DK);
+  float q1[4] = {0.f, 0.f, 0.f, 0.f}, k2[4] = {0.f, 0.f, 0.f, 0.f}, k3[4] = {0.f, 0.f, 0.f, 0.f};
+  float np1[4], np2[4], np3[4];
+  auto fetchP = [&](int t) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int o = (16 * w + 4 * lg + i) * DK + 16 * t + lr;
+      np1[i] = P1[o];
+      np2[i] = P2[o];
+      np3[i] = P3[o];
+    }
+  };
+  fetchP(0);
+  bf16x8_t aE[2][2], aET[2][2], aF[2][2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    aE[s][0] = frag_row(sEh, LT, 16 * w + lr, 32 * s);
+    aE[s][1] = frag_row(sEl, LT, 16 * w + lr, 32 * s);
+    aET[s][0] = frag_col(sEh, LT, 32 * s, 16 * w);
+    aET[s][1] = frag_col(sEl, LT, 32 * s, 16 * w);
+    aF[s][0] = frag_row(sDh, LT, 16 * w + lr, 32 * s);
+    aF[s][1] = frag_row(sDl, LT, 16 * w + lr, 32 * s);
+  }
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    float p1[4], p2[4], p3[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      p1[i] = np1[i];
+      p2[i] = np2[i];
+      p3[i] = np3[i];
+    }
+    if (t + 1 < NT) fetchP(t + 1);
+    f32x4 dq = zero4(), dk = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8_t bk = frag_col(sK, LDK, 32 * s, 16 * t), bq = frag_col(sQ, LDK, 32 * s, 16 * t);
+      dq = mfma_bf(aE[s][0], bk, dq);
+      dq = mfma_bf(aE[s][1], bk, dq);
+      dk = mfma_bf(aET[s][0], bq, dk);
+      dk = mfma_bf(aET[s][1], bq, dk);
+      dk = mfma_bf(aF[s][0], bk, dk);
+      dk = mfma_bf(aF[s][1], bk, dk);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * lg + i, c = 16 * t + lr;
+      q1[i] += (float)sQ[r * LDK + c] * p1[i];
+      k2[i] += (float)sK[r * LDK + c] * p2[i];
+      k3[i] += (float)sK[r * LDK + c] * p3[i];
+      if (r < C) {
+        const size_t o = ((size_t)(r0 + r) * H + h) * DK + c;
+        p.dq[o] = sGam[r] * p1[i] + dq[i];
+        p.dk[o] = -sGam[r] * p2[i] + sFac[r] * p3[i] + dk[i];
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    q1[i] = sum16(q1[i]);
+    k2[i] = sum16(k2[i]);
+    k3[i] = sum16(k3[i]);
+  }
+  if (lr == 0)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * lg + i;
+      const float zc = cs[1][0][r] + cs[1][1][r] + cs[1][2][r] + cs[1][3][r];
+      const float yc = cs[2][0][r] + cs[2][1][r] + cs[2][2][r] + cs[2][3][r];
+      const float t3 = sFac[r] * k3[i];
+      dG[r] = r < C ? sGam[r] * (q1[i] - k2[i]) - t3 + vr[0][r] - zc + vr[2][r] - yc : 0.f;
+      t3s[r] = r < C ? t3 : 0.f;
+    }
+  sync_lds();
+  if (w == 0) {
+    // dG_{C-1} also takes sum_r fac_r <k_r, P3_r> + gam_{C-1} <dH', H>;
+    // dg_t = sum_{r >= t} dG_r
+    const float extra = wave_sum(t3s[l]) + sGam[C - 1] * gw[part_sh(DK)];
+    const float x = dG[l] + (l == C - 1 ? extra : 0.f);
+    const float incl = wave_inclusive_scan(x);
+    const float suffix = __shfl(incl, 63, 64) - incl + x;
+    if (l < C) {
+      const size_t o = (size_t)(r0 + l) * H + h;
+      p.dg[o] = suffix;
+      p.dbeta[o] = cs[0][0][l] + cs[0][1][l] + cs[0][2][l] + cs[0][3][l] + vr[1][l];
+    }
+  }
+}
+
 template <typename In, int DK>
 hipError_t launch_all(const BwdParams &p, hipStream_t st) {
   const int cells = p.NT * p.H;
@@ -998,7 +1268,10 @@ hipError_t launch_all(const BwdParams &p, hipStream_t st) {
   else
     hipLaunchKernelGGL((bwd_part_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  hipLaunchKernelGGL((bwd_final_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
+  if constexpr (std::is_same_v<In, bf16>)
+    hipLaunchKernelGGL((bwd_final_bf16_kernel<DK>), dim3(cells), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_final_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
   return hipGetLastError();
 }
 
