@@ -19,13 +19,15 @@
 //   F = beta_r dA_rs E_rs (strict lower), and the gate terms below,
 // with dg the reverse cumulative sum of dG inside the chunk.
 //
-// Four launches after the forward recompute (map + reduce storing every
-// chunk's entering state H): prep (per chunk slot and head: A^-1, M, S and the
-// gate vectors, fp32; A^-1 by 16x16 blocks), dh (per sequence, head and 32 state columns, chunks in
-// reverse: the dH recurrence, storing dH' of every chunk and dh0), part (per
-// slot and head: dV and the d_v-contracted products dOb H^T, dX H^T,
-// U dH'^T, dM, dT and <dH', H>) and final (per slot and head: the chunk-local
-// algebra to dq, dk, dg, dbeta).  Arithmetic is fp32 on 16x16x4 MFMA.
+// Launches after the forward recompute (map + reduce storing every chunk's
+// entering state H): prep (per chunk slot and head: A^-1, M, S and the gate
+// vectors, fp32; A^-1 by 16x16 blocks), dh (per sequence, head and 32 state
+// columns, chunks in reverse: the dH recurrence, storing dH' of every chunk
+// and dh0), then per slot and head the d_v-contracted products (dV, dOb H^T,
+// dX H^T, U dH'^T, dM, dT, <dH', H>) and the chunk-local algebra to dq, dk,
+// dg, dbeta.  fp16 and fp32 inputs run part and final as two kernels in fp32
+// on 16x16x4 MFMA; bf16 inputs run dh and one fused part + final kernel on
+// bf16 MFMA with operands split into bf16 high and low halves.
 #include "bwd_common.h"
 
 namespace la {
@@ -594,228 +596,6 @@ __global__ __launch_bounds__(256) void bwd_part_kernel(BwdParams p) {
   }
 }
 
-// ------------------------------------------------------------ part, bf16
-// The same products for bf16 inputs on bf16 MFMA with split operands, 512
-// threads over 32-column blocks of d_v.  Per block: KH, K dH' and M^T dOb
-// give X = V - gam*KH and dU = M^T dOb + fac*(K dH'); then U = A~ X and
-// dX = A~^T dU with A~ = A^-1 diag(beta) (dX is dV); then the products
-// contracted over the block's columns accumulate in registers.  The next
-// block's H, dH', dO and V are fetched into registers during the current one.
-template <int DK>
-__global__ __launch_bounds__(512) void bwd_part_bf16_kernel(BwdParams p) {
-  constexpr int DV = DK, LDK = DK + 16, LT = 72, NB = 32, LB = NB + 8, NBLK = DV / NB, NKS = DK / 32;
-  constexpr int KP = 64 * DK / 8 / 512;  // 16-byte K pieces per thread
-  constexpr int HP = DK * NB / 4 / 512;  // float4 pieces of an H (or dH') block per thread
-  constexpr int PT = DK / 32;            // column tiles of P1..P3 per wave
-  __shared__ __attribute__((aligned(16))) __bf16 sK[64 * LDK];
-  __shared__ __attribute__((aligned(16))) __bf16 sMh[64 * LT], sMl[64 * LT], sAh[64 * LT], sAl[64 * LT];
-  __shared__ __attribute__((aligned(16))) __bf16 sHh[DK * LB], sHl[DK * LB], sDh[DK * LB], sDl[DK * LB];
-  __shared__ __attribute__((aligned(16))) __bf16 sOh[64 * LB], sOl[64 * LB], sXh[64 * LB], sXl[64 * LB];
-  __shared__ __attribute__((aligned(16))) __bf16 sGh[64 * LB], sGl[64 * LB], sUh[64 * LB], sUl[64 * LB];
-  __shared__ __attribute__((aligned(16))) __bf16 sEh[64 * LB], sEl[64 * LB], sV[64 * LB];  // dX, V
-  __shared__ __attribute__((aligned(16))) float sGam[64], sFac[64], sRed[8];
-  const int H = p.H;
-  const int slot = blockIdx.x / H, h = blockIdx.x % H;
-  Chunk ch;
-  if (!chunk_of(p, slot, ch)) return;
-  const int C = ch.C, r0 = ch.r0;
-  const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
-  const int rt = w & 3, half = w >> 2;  // row tile; column half
-  const int Hqk = p.Hqk, hq = h / (H / Hqk);
-  const float *img = p.prep + (size_t)blockIdx.x * kPrepFloats;
-  const size_t mat = (size_t)DK * DV;
-  const float *Hs = p.hs + (size_t)blockIdx.x * mat;
-  const float *Ds = p.dhs + (size_t)blockIdx.x * mat;
-
-  // the cell's K, M and A~ halves, gam and fac: straight into LDS
-  {
-    u32x4 rk[KP], rimg[4];
-    float rvec = 0.f;
-#pragma unroll
-    for (int it = 0; it < KP; ++it) {
-      const int pc = tid + 512 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
-      rk[it] = u32x4{0u, 0u, 0u, 0u};
-      if (r < C)
-        rk[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.k) +
-                                                   ((size_t)(r0 + r) * Hqk + hq) * DK + c);
-    }
-    const u32x4 *imh = reinterpret_cast<const u32x4 *>(img + kPrepH);
-#pragma unroll
-    for (int it = 0; it < 4; ++it) rimg[it] = imh[tid + 512 * it];
-    if (tid < 128) rvec = img[kPrepGam + tid];
-    static_assert(kPrepFac == kPrepGam + 64, "gate vectors");
-#pragma unroll
-    for (int it = 0; it < KP; ++it) {
-      const int pc = tid + 512 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
-      *reinterpret_cast<u32x4 *>(sK + r * LDK + c) = rk[it];
-    }
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int pc = tid + 512 * it, a = pc >> 9, r = (pc & 511) / 8, c = (pc % 8) * 8;
-      __bf16 *dst = a == 0 ? sMh : a == 1 ? sMl : a == 2 ? sAh : sAl;
-      *reinterpret_cast<u32x4 *>(dst + r * LT + c) = rimg[it];
-    }
-    if (tid < 64) sGam[tid] = rvec;
-    else if (tid < 128) sFac[tid - 64] = rvec;
-  }
-
-  // one column block's inputs in registers
-  f32x4 rh[HP], rd[HP], ro = zero4();
-  u32x4 rv = u32x4{0u, 0u, 0u, 0u};
-  auto fetch = [&](int cb) {
-    const int cc = NB * cb;
-#pragma unroll
-    for (int it = 0; it < HP; ++it) {
-      const int pc = tid + 512 * it, i = pc / (NB / 4), c = (pc % (NB / 4)) * 4;
-      rh[it] = *reinterpret_cast<const f32x4 *>(Hs + (size_t)i * DV + cc + c);
-      rd[it] = *reinterpret_cast<const f32x4 *>(Ds + (size_t)i * DV + cc + c);
-    }
-    {
-      const int r = tid / (NB / 4), c = (tid % (NB / 4)) * 4;  // 64 rows x 8 pieces
-      ro = r < C ? *reinterpret_cast<const f32x4 *>(p.dout + ((size_t)(r0 + r) * H + h) * DV + cc + c)
-                 : zero4();
-    }
-    if (tid < 64 * NB / 8) {
-      const int r = tid / (NB / 8), c = (tid % (NB / 8)) * 8;
-      rv = r < C ? *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.v) +
-                                                     ((size_t)(r0 + r) * H + h) * DV + cc + c)
-                 : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto put4 = [](__bf16 *hi, __bf16 *lo, f32x4 v) {
-    bf16x4_t a, b;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[e] = (__bf16)v[e];
-      b[e] = (__bf16)(v[e] - (float)a[e]);
-    }
-    *reinterpret_cast<bf16x4_t *>(hi) = a;
-    *reinterpret_cast<bf16x4_t *>(lo) = b;
-  };
-
-  f32x4 P1[PT], P2[PT], P3[PT], dM[2], dT[2];
-#pragma unroll
-  for (int t = 0; t < PT; ++t) P1[t] = P2[t] = P3[t] = zero4();
-  dM[0] = dM[1] = dT[0] = dT[1] = zero4();
-  float shd = 0.f;
-  fetch(0);
-  for (int cb = 0; cb < NBLK; ++cb) {
-    sync_lds();
-#pragma unroll
-    for (int it = 0; it < HP; ++it) {
-      const int pc = tid + 512 * it, i = pc / (NB / 4), c = (pc % (NB / 4)) * 4;
-      put4(sHh + i * LB + c, sHl + i * LB + c, rh[it]);
-      put4(sDh + i * LB + c, sDl + i * LB + c, rd[it]);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) shd += rh[it][e] * rd[it][e];
-    }
-    {
-      const int r = tid / (NB / 4), c = (tid % (NB / 4)) * 4;
-      put4(sOh + r * LB + c, sOl + r * LB + c, ro * p.scale);
-    }
-    if (tid < 64 * NB / 8) {
-      const int r = tid / (NB / 8), c = (tid % (NB / 8)) * 8;
-      *reinterpret_cast<u32x4 *>(sV + r * LB + c) = rv;
-    }
-    if (cb + 1 < NBLK) fetch(cb + 1);
-    sync_lds();
-    // X = V - gam*(K H), dU = M^T dOb + fac*(K dH'): rows 16rt, columns 16half
-    {
-      f32x4 kh = zero4(), kd = zero4(), mo = zero4();
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const bf16x8_t a = frag_row(sK, LDK, 16 * rt + lr, 32 * s);
-        kh = mfma_bf(a, frag_col(sHh, LB, 32 * s, 16 * half), kh);
-        kh = mfma_bf(a, frag_col(sHl, LB, 32 * s, 16 * half), kh);
-        kd = mfma_bf(a, frag_col(sDh, LB, 32 * s, 16 * half), kd);
-        kd = mfma_bf(a, frag_col(sDl, LB, 32 * s, 16 * half), kd);
-      }
-#pragma unroll
-      for (int s = 0; s < 2; ++s)
-        mo = mfma3(frag_col(sMh, LT, 32 * s, 16 * rt), frag_col(sMl, LT, 32 * s, 16 * rt),
-                   frag_col(sOh, LB, 32 * s, 16 * half), frag_col(sOl, LB, 32 * s, 16 * half), mo);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i, c = 16 * half + lr;
-        const float x = (float)sV[r * LB + c] - sGam[r] * kh[i];
-        splitb(x, sXh[r * LB + c], sXl[r * LB + c]);
-        splitb(mo[i] + sFac[r] * kd[i], sGh[r * LB + c], sGl[r * LB + c]);
-      }
-    }
-    sync_lds();
-    // U = A~ X, dX = A~^T dU (= dV)
-    {
-      f32x4 u = zero4(), dx = zero4();
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        u = mfma3(frag_row(sAh, LT, 16 * rt + lr, 32 * s), frag_row(sAl, LT, 16 * rt + lr, 32 * s),
-                  frag_col(sXh, LB, 32 * s, 16 * half), frag_col(sXl, LB, 32 * s, 16 * half), u);
-        dx = mfma3(frag_col(sAh, LT, 32 * s, 16 * rt), frag_col(sAl, LT, 32 * s, 16 * rt),
-                   frag_col(sGh, LB, 32 * s, 16 * half), frag_col(sGl, LB, 32 * s, 16 * half), dx);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i, c = 16 * half + lr;
-        splitb(u[i], sUh[r * LB + c], sUl[r * LB + c]);
-        splitb(dx[i], sEh[r * LB + c], sEl[r * LB + c]);
-        if (r < C) p.dv[((size_t)(r0 + r) * H + h) * DV + NB * cb + c] = dx[i];
-      }
-    }
-    sync_lds();
-    // contracted over this block's columns: P1 += dOb H^T, P2 += dX H^T,
-    // P3 += U dH'^T (column tiles PT half ..), dM += dOb U^T,
-    // dT += dU X^T (column tiles 2half, 2half+1)
-    {
-      const int ar = 16 * rt + lr;
-      const bf16x8_t oh = frag_row(sOh, LB, ar, 0), ol = frag_row(sOl, LB, ar, 0);
-      const bf16x8_t eh = frag_row(sEh, LB, ar, 0), el = frag_row(sEl, LB, ar, 0);
-      const bf16x8_t uh = frag_row(sUh, LB, ar, 0), ul = frag_row(sUl, LB, ar, 0);
-      const bf16x8_t gh = frag_row(sGh, LB, ar, 0), gl = frag_row(sGl, LB, ar, 0);
-#pragma unroll
-      for (int t = 0; t < PT; ++t) {
-        const int br = 16 * (PT * half + t) + lr;
-        const bf16x8_t hh = frag_row(sHh, LB, br, 0), hl = frag_row(sHl, LB, br, 0);
-        P1[t] = mfma3(oh, ol, hh, hl, P1[t]);
-        P2[t] = mfma3(eh, el, hh, hl, P2[t]);
-        P3[t] = mfma3(uh, ul, frag_row(sDh, LB, br, 0), frag_row(sDl, LB, br, 0), P3[t]);
-      }
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        const int br = 16 * (2 * half + t) + lr;
-        dM[t] = mfma3(oh, ol, frag_row(sUh, LB, br, 0), frag_row(sUl, LB, br, 0), dM[t]);
-        dT[t] = mfma3(gh, gl, frag_row(sXh, LB, br, 0), frag_row(sXl, LB, br, 0), dT[t]);
-      }
-    }
-  }
-  float *gw = p.part + (size_t)blockIdx.x * part_floats(DK);
-#pragma unroll
-  for (int t = 0; t < PT; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rt + 4 * lg + i, c = 16 * (PT * half + t) + lr;
-      gw[kPartP1 + r * DK + c] = P1[t][i];
-      gw[part_p2(DK) + r * DK + c] = P2[t][i];
-      gw[part_p3(DK) + r * DK + c] = P3[t][i];
-    }
-#pragma unroll
-  for (int t = 0; t < 2; ++t)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * rt + 4 * lg + i, c = 16 * (2 * half + t) + lr;
-      gw[part_dm(DK) + r * 64 + c] = dM[t][i];
-      gw[part_dt(DK) + r * 64 + c] = dT[t][i];
-    }
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) shd += __shfl_xor(shd, o);
-  if (l == 0) sRed[w] = shd;
-  sync_lds();
-  if (tid == 0) {
-    float s = 0.f;
-    for (int i = 0; i < 8; ++i) s += sRed[i];
-    gw[part_sh(DK)] = s;
-  }
-}
-
 // ----------------------------------------------------------------- final
 template <typename In, int DK>
 __global__ __launch_bounds__(256) void bwd_final_kernel(BwdParams p) {
@@ -983,13 +763,7 @@ __global__ __launch_bounds__(256) void bwd_final_kernel(BwdParams p) {
   }
 }
 
-// ----------------------------------------------------------- final, bf16
-// The same chunk-local algebra for bf16 inputs.  Elementwise terms come
-// straight from registers (every global read is issued at the start), row
-// sums are wave reductions and column sums go through a [4][64] table; the
-// products run on bf16 MFMA with split operands.  F and F^T are folded into
-// one matrix F + F^T, and K, Q take the place of A^-1 and tmp once those are
-// read, so the block holds 72 KiB of LDS and two blocks share a CU.
+// ------------------------------------------------------ reductions
 __device__ __forceinline__ float sum16(float x) {  // over the 16 lanes of a row group
 #pragma unroll
   for (int m = 1; m < 16; m <<= 1) x += __shfl_xor(x, m, 64);
@@ -1001,22 +775,44 @@ __device__ __forceinline__ float wave_sum(float x) {
   return x;
 }
 
+// ------------------------------------------------------- part + final, bf16
+// One kernel per (slot, head) for bf16 inputs: the partial products of the
+// part stage stay in registers and the chunk-local algebra of the final
+// stage follows in the same block, so nothing of either goes through HBM.
+// Phase 1 is the 32-column loop (X, dU, U, dX = dV, and P1 = dOb H^T,
+// P2 = dX H^T, P3 = U dH'^T, dM = dOb U^T, dT = dU X^T accumulated); phase 2
+// reuses the loop's LDS for A^-1, tmp = dT' A^-T, F + F^T and dM*E.  Wave w
+// owns row tile w throughout, so the P tiles it accumulates are the dq/dk
+// tiles it writes.  One wave per SIMD leaves each wave 512 registers for the
+// accumulators and the prefetched block, so nothing spills to memory (a
+// spill reload would wait for every load in flight).
 template <int DK>
-__global__ __launch_bounds__(256, 2) void bwd_final_bf16_kernel(BwdParams p) {
-  constexpr int NT = DK / 16, LT = 72, LDK = DK + 16, PAIR = 2 * 64 * LT;
-  constexpr int KP = 64 * DK / 8 / 256;  // 16-byte K (and Q) pieces per thread
-  static_assert(64 * LDK <= PAIR, "K and Q fit over A^-1 and tmp");
-  // [A^-1 hi, lo][tmp hi, lo][dT diag(beta) hi, lo -> F + F^T hi, lo][dM*E hi, lo]
-  __shared__ __attribute__((aligned(16))) __bf16 smem[4 * PAIR];
-  __shared__ __attribute__((aligned(16))) float sG[64], sGam[64], sFac[64], sBeta[64];
-  __shared__ __attribute__((aligned(16))) float cs[3][4][64];  // column partials: bt, zc, yc
-  __shared__ __attribute__((aligned(16))) float vr[3][64];     // row sums: zr, ba, yr
-  __shared__ __attribute__((aligned(16))) float dG[64], t3s[64];
-  __bf16 *const sAh = smem, *const sAl = smem + 64 * LT;
-  __bf16 *const sTh = smem + PAIR, *const sTl = smem + PAIR + 64 * LT;
-  __bf16 *const sDh = smem + 2 * PAIR, *const sDl = smem + 2 * PAIR + 64 * LT;  // dT', then F + F^T
-  __bf16 *const sEh = smem + 3 * PAIR, *const sEl = smem + 3 * PAIR + 64 * LT;  // dM * E
-  __bf16 *const sK = smem, *const sQ = smem + PAIR;
+__global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
+  constexpr int DV = DK, LDK = DK + 16, LT = 72, NB = 32, LB = NB + 8, NBLK = DV / NB, NKS = DK / 32;
+  constexpr int KP = 64 * DK / 8 / 256;  // 16-byte K (or Q) pieces per thread
+  constexpr int HP = DK * NB / 4 / 256;  // float4 pieces of an H (or dH') block per thread
+  constexpr int PT = DK / 16;            // column tiles of P1..P3, dq and dk
+  constexpr int MT = 64 * LT;            // one [64][LT] array
+  // pool: [K][phase 1: M, A~ halves | H, dH' halves | 64-row block arrays]
+  //       [K][phase 2: A^-1 (then Q), tmp, dT' (then F + F^T), dM*E, halves]
+  constexpr int P1SZ = 4 * MT + 4 * DK * LB + 11 * 64 * LB, P2SZ = 8 * MT;
+  static_assert(P2SZ <= P1SZ && 64 * LDK <= 2 * MT, "phase-2 arrays fit");
+  __shared__ __attribute__((aligned(16))) __bf16 pool[64 * LDK + P1SZ];
+  __shared__ __attribute__((aligned(16))) float sGam[64], sFac[64], sG[64], sBeta[64];
+  __shared__ __attribute__((aligned(16))) float rowt[6][64], colt[3][4][64], sh4[4];
+  __bf16 *const sK = pool, *const ph = pool + 64 * LDK;
+  __bf16 *const sMh = ph, *const sMl = ph + MT, *const sAh = ph + 2 * MT, *const sAl = ph + 3 * MT;
+  __bf16 *const sHh = ph + 4 * MT, *const sHl = sHh + DK * LB, *const sDh = sHl + DK * LB,
+                *const sDl = sDh + DK * LB;
+  __bf16 *const b64 = sDl + DK * LB;  // the 64-row block arrays
+  __bf16 *const sOh = b64, *const sOl = b64 + 64 * LB, *const sXh = b64 + 2 * 64 * LB,
+                *const sXl = b64 + 3 * 64 * LB, *const sGh = b64 + 4 * 64 * LB, *const sGl = b64 + 5 * 64 * LB,
+                *const sUh = b64 + 6 * 64 * LB, *const sUl = b64 + 7 * 64 * LB, *const sEh = b64 + 8 * 64 * LB,
+                *const sEl = b64 + 9 * 64 * LB, *const sV = b64 + 10 * 64 * LB;
+  __bf16 *const qA1h = ph, *const qA1l = ph + MT, *const qTh = ph + 2 * MT, *const qTl = ph + 3 * MT;
+  __bf16 *const qFh = ph + 4 * MT, *const qFl = ph + 5 * MT, *const qEh = ph + 6 * MT, *const qEl = ph + 7 * MT;
+  __bf16 *const sQ = ph;  // over A^-1 once it is read
+
   const int H = p.H;
   const int slot = blockIdx.x / H, h = blockIdx.x % H;
   Chunk ch;
@@ -1025,230 +821,401 @@ __global__ __launch_bounds__(256, 2) void bwd_final_bf16_kernel(BwdParams p) {
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
   const int Hqk = p.Hqk, hq = h / (H / Hqk);
   const float *img = p.prep + (size_t)blockIdx.x * kPrepFloats;
-  const float *gw = p.part + (size_t)blockIdx.x * part_floats(DK);
+  const size_t mat = (size_t)DK * DV;
+  const float *Hs = p.hs + (size_t)blockIdx.x * mat;
+  const float *Ds = p.dhs + (size_t)blockIdx.x * mat;
+  static_assert(kPrepFac == kPrepGam + 64, "gate vectors");
 
-  // every global read of the algebra, issued together
-  u32x4 rk[KP], rq[KP];
+  // ---- the cell's K, M and A~ halves, gam and fac
+  {
+    u32x4 rk[KP], rimg[8];
+    float rvec = 0.f;
+#pragma unroll
+    for (int it = 0; it < KP; ++it) {
+      const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+      rk[it] = u32x4{0u, 0u, 0u, 0u};
+      if (r < C)
+        rk[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.k) +
+                                                   ((size_t)(r0 + r) * Hqk + hq) * DK + c);
+    }
+    const u32x4 *imh = reinterpret_cast<const u32x4 *>(img + kPrepH);
+#pragma unroll
+    for (int it = 0; it < 8; ++it) rimg[it] = imh[tid + 256 * it];
+    if (tid < 128) rvec = img[kPrepGam + tid];
+#pragma unroll
+    for (int it = 0; it < KP; ++it) {
+      const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+      *reinterpret_cast<u32x4 *>(sK + r * LDK + c) = rk[it];
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int pc = tid + 256 * it, a = pc >> 9, r = (pc & 511) / 8, c = (pc % 8) * 8;
+      *reinterpret_cast<u32x4 *>(ph + a * MT + r * LT + c) = rimg[it];
+    }
+    if (tid < 64) sGam[tid] = rvec;
+    else if (tid < 128) sFac[tid - 64] = rvec;
+  }
+
+  // ---- phase 1
+  f32x4 rh[HP], rd[HP], ro[2];
+  u32x4 rv;
+  auto fetch = [&](int cb) {
+    const int cc = NB * cb;
+#pragma unroll
+    for (int it = 0; it < HP; ++it) {
+      const int pc = tid + 256 * it, i = pc / (NB / 4), c = (pc % (NB / 4)) * 4;
+      rh[it] = *reinterpret_cast<const f32x4 *>(Hs + (size_t)i * DV + cc + c);
+      rd[it] = *reinterpret_cast<const f32x4 *>(Ds + (size_t)i * DV + cc + c);
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int pc = tid + 256 * it, r = pc / (NB / 4), c = (pc % (NB / 4)) * 4;
+      ro[it] = r < C ? *reinterpret_cast<const f32x4 *>(p.dout + ((size_t)(r0 + r) * H + h) * DV + cc + c)
+                     : zero4();
+    }
+    {
+      const int r = tid / (NB / 8), c = (tid % (NB / 8)) * 8;
+      rv = r < C ? *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.v) +
+                                                     ((size_t)(r0 + r) * H + h) * DV + cc + c)
+                 : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto put4 = [](__bf16 *hi, __bf16 *lo, f32x4 v) {
+    bf16x4_t a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = (__bf16)v[e];
+      b[e] = (__bf16)(v[e] - (float)a[e]);
+    }
+    *reinterpret_cast<bf16x4_t *>(hi) = a;
+    *reinterpret_cast<bf16x4_t *>(lo) = b;
+  };
+
+  f32x4 P1[PT], P2[PT], P3[PT], dM[4], dT[4];
+#pragma unroll
+  for (int t = 0; t < PT; ++t) P1[t] = P2[t] = P3[t] = zero4();
+#pragma unroll
+  for (int t = 0; t < 4; ++t) dM[t] = dT[t] = zero4();
+  float shd = 0.f;
+  fetch(0);
+  for (int cb = 0; cb < NBLK; ++cb) {
+    sync_lds();
+#pragma unroll
+    for (int it = 0; it < HP; ++it) {
+      const int pc = tid + 256 * it, i = pc / (NB / 4), c = (pc % (NB / 4)) * 4;
+      put4(sHh + i * LB + c, sHl + i * LB + c, rh[it]);
+      put4(sDh + i * LB + c, sDl + i * LB + c, rd[it]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) shd += rh[it][e] * rd[it][e];
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int pc = tid + 256 * it, r = pc / (NB / 4), c = (pc % (NB / 4)) * 4;
+      put4(sOh + r * LB + c, sOl + r * LB + c, ro[it] * p.scale);
+    }
+    {
+      const int r = tid / (NB / 8), c = (tid % (NB / 8)) * 8;
+      *reinterpret_cast<u32x4 *>(sV + r * LB + c) = rv;
+    }
+    if (cb + 1 < NBLK) fetch(cb + 1);
+    sync_lds();
+    // X = V - gam*(K H), dU = M^T dOb + fac*(K dH'): rows 16w, both column tiles
+    {
+      f32x4 kh[2] = {zero4(), zero4()}, kd[2] = {zero4(), zero4()}, mo[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const bf16x8_t a = frag_row(sK, LDK, 16 * w + lr, 32 * s);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          kh[hf] = mfma_bf(a, frag_col(sHh, LB, 32 * s, 16 * hf), kh[hf]);
+          kh[hf] = mfma_bf(a, frag_col(sHl, LB, 32 * s, 16 * hf), kh[hf]);
+          kd[hf] = mfma_bf(a, frag_col(sDh, LB, 32 * s, 16 * hf), kd[hf]);
+          kd[hf] = mfma_bf(a, frag_col(sDl, LB, 32 * s, 16 * hf), kd[hf]);
+        }
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8_t ah = frag_col(sMh, LT, 32 * s, 16 * w), al = frag_col(sMl, LT, 32 * s, 16 * w);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf)
+          mo[hf] = mfma3(ah, al, frag_col(sOh, LB, 32 * s, 16 * hf), frag_col(sOl, LB, 32 * s, 16 * hf), mo[hf]);
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * w + 4 * lg + i, c = 16 * hf + lr;
+          const float x = (float)sV[r * LB + c] - sGam[r] * kh[hf][i];
+          splitb(x, sXh[r * LB + c], sXl[r * LB + c]);
+          splitb(mo[hf][i] + sFac[r] * kd[hf][i], sGh[r * LB + c], sGl[r * LB + c]);
+        }
+    }
+    sync_lds();
+    // U = A~ X, dX = A~^T dU (= dV)
+    {
+      f32x4 u[2] = {zero4(), zero4()}, dx[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8_t ah = frag_row(sAh, LT, 16 * w + lr, 32 * s), al = frag_row(sAl, LT, 16 * w + lr, 32 * s);
+        const bf16x8_t th = frag_col(sAh, LT, 32 * s, 16 * w), tl = frag_col(sAl, LT, 32 * s, 16 * w);
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          u[hf] = mfma3(ah, al, frag_col(sXh, LB, 32 * s, 16 * hf), frag_col(sXl, LB, 32 * s, 16 * hf), u[hf]);
+          dx[hf] = mfma3(th, tl, frag_col(sGh, LB, 32 * s, 16 * hf), frag_col(sGl, LB, 32 * s, 16 * hf), dx[hf]);
+        }
+      }
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * w + 4 * lg + i, c = 16 * hf + lr;
+          splitb(u[hf][i], sUh[r * LB + c], sUl[r * LB + c]);
+          splitb(dx[hf][i], sEh[r * LB + c], sEl[r * LB + c]);
+          if (r < C) p.dv[((size_t)(r0 + r) * H + h) * DV + NB * cb + c] = dx[hf][i];
+        }
+    }
+    sync_lds();
+    // contracted over this block's columns
+    {
+      const int ar = 16 * w + lr;
+      const bf16x8_t oh = frag_row(sOh, LB, ar, 0), ol = frag_row(sOl, LB, ar, 0);
+      const bf16x8_t eh = frag_row(sEh, LB, ar, 0), el = frag_row(sEl, LB, ar, 0);
+      const bf16x8_t uh = frag_row(sUh, LB, ar, 0), ul = frag_row(sUl, LB, ar, 0);
+      const bf16x8_t gh = frag_row(sGh, LB, ar, 0), gl = frag_row(sGl, LB, ar, 0);
+#pragma unroll
+      for (int t = 0; t < PT; ++t) {
+        const int br = 16 * t + lr;
+        const bf16x8_t hh = frag_row(sHh, LB, br, 0), hl = frag_row(sHl, LB, br, 0);
+        P1[t] = mfma3(oh, ol, hh, hl, P1[t]);
+        P2[t] = mfma3(eh, el, hh, hl, P2[t]);
+        P3[t] = mfma3(uh, ul, frag_row(sDh, LB, br, 0), frag_row(sDl, LB, br, 0), P3[t]);
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int br = 16 * t + lr;
+        dM[t] = mfma3(oh, ol, frag_row(sUh, LB, br, 0), frag_row(sUl, LB, br, 0), dM[t]);
+        dT[t] = mfma3(gh, gl, frag_row(sXh, LB, br, 0), frag_row(sXl, LB, br, 0), dT[t]);
+      }
+    }
+  }
+
+  // ---- phase 2
+  float fa[16], fam[4][4], fmm[4][4], fS[4][4], fvec = 0.f;
+  u32x4 rq[KP];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) fa[e] = img[kPrepA + tid + 256 * e];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int o = (16 * w + 4 * lg + i) * 64 + 16 * t + lr;
+      fam[t][i] = img[kPrepA + o];
+      fmm[t][i] = img[kPrepM + o];
+      fS[t][i] = img[kPrepS + o];
+    }
 #pragma unroll
   for (int it = 0; it < KP; ++it) {
     const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
-    rk[it] = rq[it] = u32x4{0u, 0u, 0u, 0u};
-    if (r < C) {
-      const size_t off = ((size_t)(r0 + r) * Hqk + hq) * DK + c;
-      rk[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.k) + off);
-      rq[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.q) + off);
-    }
+    rq[it] = u32x4{0u, 0u, 0u, 0u};
+    if (r < C)
+      rq[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.q) +
+                                                 ((size_t)(r0 + r) * Hqk + hq) * DK + c);
   }
-  // elementwise entries: row w + 4e, column l
-  float ea[16], em[16], edm[16], edt[16];
+  if (tid < 64) fvec = img[kPrepG + tid];
+  else if (tid < 128) fvec = img[kPrepBeta + tid - 64];
+  shd = wave_sum(shd);
+  if (l == 0) sh4[w] = shd;
+  sync_lds();  // every phase-1 LDS read is done
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int o = (w + 4 * e) * 64 + l;
-    ea[e] = img[kPrepA + o];
-    em[e] = img[kPrepM + o];
-    edm[e] = gw[part_dm(DK) + o];
-    edt[e] = gw[part_dt(DK) + o];
+    const int r = (tid + 256 * e) >> 6;  // row; the column is the lane
+    splitb(fa[e], qA1h[r * LT + l], qA1l[r * LT + l]);
   }
-  // S at this lane's tile positions of the dA product
-  float eS[4][4];
-#pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) eS[s4][i] = img[kPrepS + (16 * w + 4 * lg + i) * 64 + 16 * s4 + lr];
-  if (tid < 64) {
-    sG[tid] = img[kPrepG + tid];
-    sGam[tid] = img[kPrepGam + tid];
-    sFac[tid] = img[kPrepFac + tid];
-    sBeta[tid] = img[kPrepBeta + tid];
-  }
+  if (tid < 64) sG[tid] = fvec;
+  else if (tid < 128) sBeta[tid - 64] = fvec;
   sync_lds();
-
-  // Z = dM * M (gates), dT * A^-1 (beta); A^-1, dT' = dT diag(beta) and
-  // dM * E, split, over the lower triangle of real rows
+  // Z = dM * M (gates), dT * A^-1 (beta); dT' = dT diag(beta), dM * E, split,
+  // over the lower triangle of real rows
   {
-    float bt = 0.f, zc = 0.f;
-    const float gs = sG[l], bs = sBeta[l];
+    float zr[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int r = w + 4 * e, o = r * LT + l;
-      const bool lo = l <= r && r < C;
-      const float z = lo ? edm[e] * em[e] : 0.f;
-      bt += lo ? edt[e] * ea[e] : 0.f;
-      zc += z;
-      const float zr = wave_sum(z);
-      if (l == 0) vr[0][r] = zr;
-      splitb(ea[e], sAh[o], sAl[o]);
-      splitb(lo ? edt[e] * bs : 0.f, sDh[o], sDl[o]);
-      splitb(lo ? edm[e] * __expf(sG[r] - gs) : 0.f, sEh[o], sEl[o]);
-    }
-    cs[0][w][l] = bt;
-    cs[1][w][l] = zc;
-  }
-  sync_lds();
-  // tmp = dT' A^-T: rows 16w
-  {
-    f32x4 t[4] = {zero4(), zero4(), zero4(), zero4()};
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      const bf16x8_t ah = frag_row(sDh, LT, 16 * w + lr, 32 * s), al = frag_row(sDl, LT, 16 * w + lr, 32 * s);
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        t[s4] = mfma3(ah, al, frag_row(sAh, LT, 16 * s4 + lr, 32 * s), frag_row(sAl, LT, 16 * s4 + lr, 32 * s),
-                      t[s4]);
-    }
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4)
+    for (int t = 0; t < 4; ++t) {
+      const int s = 16 * t + lr;
+      float zc = 0.f, bt = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int o = (16 * w + 4 * lg + i) * LT + 16 * s4 + lr;
-        splitb(t[s4][i], sTh[o], sTl[o]);
+        const int r = 16 * w + 4 * lg + i, o = r * LT + s;
+        const bool lo = s <= r && r < C;
+        const float z = lo ? dM[t][i] * fmm[t][i] : 0.f;
+        zr[i] += z;
+        zc += z;
+        bt += lo ? dT[t][i] * fam[t][i] : 0.f;
+        splitb(lo ? dT[t][i] * sBeta[s] : 0.f, qFh[o], qFl[o]);
+        splitb(lo ? dM[t][i] * __expf(sG[r] - sG[s]) : 0.f, qEh[o], qEl[o]);
+      }
+      zc += __shfl_xor(zc, 16, 64);
+      zc += __shfl_xor(zc, 32, 64);
+      bt += __shfl_xor(bt, 16, 64);
+      bt += __shfl_xor(bt, 32, 64);
+      if (lg == 0) {
+        colt[0][w][s] = bt;
+        colt[1][w][s] = zc;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float v = sum16(zr[i]);
+      if (lr == 0) rowt[0][16 * w + 4 * lg + i] = v;
+    }
+  }
+  sync_lds();
+  // tmp = dT' A^-T
+  {
+    f32x4 t2[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const bf16x8_t ah = frag_row(qFh, LT, 16 * w + lr, 32 * s), al = frag_row(qFl, LT, 16 * w + lr, 32 * s);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        t2[t] = mfma3(ah, al, frag_row(qA1h, LT, 16 * t + lr, 32 * s), frag_row(qA1l, LT, 16 * t + lr, 32 * s),
+                      t2[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = (16 * w + 4 * lg + i) * LT + 16 * t + lr;
+        splitb(t2[t][i], qTh[o], qTl[o]);
       }
   }
   sync_lds();
   // dA = -A^-T tmp; strict lower part: W = dA S (beta), Y = beta dA S
   // (gates), F = beta dA E (keys), stored as F + F^T over dT'
   {
-    f32x4 t[4] = {zero4(), zero4(), zero4(), zero4()};
+    f32x4 t3[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const bf16x8_t ah = frag_col(sAh, LT, 32 * s, 16 * w), al = frag_col(sAl, LT, 32 * s, 16 * w);
+      const bf16x8_t ah = frag_col(qA1h, LT, 32 * s, 16 * w), al = frag_col(qA1l, LT, 32 * s, 16 * w);
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        t[s4] = mfma3(ah, al, frag_col(sTh, LT, 32 * s, 16 * s4), frag_col(sTl, LT, 32 * s, 16 * s4), t[s4]);
+      for (int t = 0; t < 4; ++t)
+        t3[t] = mfma3(ah, al, frag_col(qTh, LT, 32 * s, 16 * t), frag_col(qTl, LT, 32 * s, 16 * t), t3[t]);
     }
     float wr[4] = {0.f, 0.f, 0.f, 0.f}, yr[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int s = 16 * s4 + lr;
+    for (int t = 0; t < 4; ++t) {
+      const int s = 16 * t + lr;
       float yc = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = 16 * w + 4 * lg + i;
         const bool sl = s < r && r < C;
-        const float dA = -t[s4][i];
-        const float Wv = sl ? dA * eS[s4][i] : 0.f;
+        const float dA = -t3[t][i];
+        const float Wv = sl ? dA * fS[t][i] : 0.f;
         const float Yv = sBeta[r] * Wv;
         const float Fv = sl ? sBeta[r] * dA * __expf(sG[r] - sG[s]) : 0.f;
         wr[i] += Wv;
         yr[i] += Yv;
         yc += Yv;
         if (s < r) {
-          splitb(Fv, sDh[r * LT + s], sDl[r * LT + s]);
-          splitb(Fv, sDh[s * LT + r], sDl[s * LT + r]);
+          splitb(Fv, qFh[r * LT + s], qFl[r * LT + s]);
+          splitb(Fv, qFh[s * LT + r], qFl[s * LT + r]);
         } else if (s == r) {
-          sDh[r * LT + r] = sDl[r * LT + r] = (__bf16)0.f;
+          qFh[r * LT + r] = qFl[r * LT + r] = (__bf16)0.f;
         }
       }
       yc += __shfl_xor(yc, 16, 64);
       yc += __shfl_xor(yc, 32, 64);
-      if (lg == 0) cs[2][w][s] = yc;
+      if (lg == 0) colt[2][w][s] = yc;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      wr[i] = sum16(wr[i]);
-      yr[i] = sum16(yr[i]);
+      const float a = sum16(wr[i]), b = sum16(yr[i]);
       if (lr == 0) {
-        vr[1][16 * w + 4 * lg + i] = wr[i];
-        vr[2][16 * w + 4 * lg + i] = yr[i];
+        rowt[1][16 * w + 4 * lg + i] = a;
+        rowt[2][16 * w + 4 * lg + i] = b;
       }
     }
   }
   sync_lds();
-  // K and Q over A^-1 and tmp
+  // Q over A^-1
 #pragma unroll
   for (int it = 0; it < KP; ++it) {
     const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
-    *reinterpret_cast<u32x4 *>(sK + r * LDK + c) = rk[it];
     *reinterpret_cast<u32x4 *>(sQ + r * LDK + c) = rq[it];
   }
   sync_lds();
   // dQ = gam P1 + (dM E) K;  dK = -gam P2 + fac P3 + (dM E)^T Q + (F + F^T) K,
-  // and the gate dots <q_r, P1_r>, <k_r, P2_r>, <k_r, P3_r>, per column tile
-  const float *P1 = gw + kPartP1, *P2 = gw + part_p2(DK), *P3 = gw + part_p3(DK);
-  float q1[4] = {0.f, 0.f, 0.f, 0.f}, k2[4] = {0.f, 0.f, 0.f, 0.f}, k3[4] = {0.f, 0.f, 0.f, 0.f};
-  float np1[4], np2[4], np3[4];
-  auto fetchP = [&](int t) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int o = (16 * w + 4 * lg + i) * DK + 16 * t + lr;
-      np1[i] = P1[o];
-      np2[i] = P2[o];
-      np3[i] = P3[o];
-    }
-  };
-  fetchP(0);
-  bf16x8_t aE[2][2], aET[2][2], aF[2][2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) {
-    aE[s][0] = frag_row(sEh, LT, 16 * w + lr, 32 * s);
-    aE[s][1] = frag_row(sEl, LT, 16 * w + lr, 32 * s);
-    aET[s][0] = frag_col(sEh, LT, 32 * s, 16 * w);
-    aET[s][1] = frag_col(sEl, LT, 32 * s, 16 * w);
-    aF[s][0] = frag_row(sDh, LT, 16 * w + lr, 32 * s);
-    aF[s][1] = frag_row(sDl, LT, 16 * w + lr, 32 * s);
-  }
-#pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    float p1[4], p2[4], p3[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      p1[i] = np1[i];
-      p2[i] = np2[i];
-      p3[i] = np3[i];
-    }
-    if (t + 1 < NT) fetchP(t + 1);
-    f32x4 dq = zero4(), dk = zero4();
+  // and the gate dots <q_r, P1_r>, <k_r, P2_r>, <k_r, P3_r>
+  {
+    bf16x8_t aE[2][2], aET[2][2], aF[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const bf16x8_t bk = frag_col(sK, LDK, 32 * s, 16 * t), bq = frag_col(sQ, LDK, 32 * s, 16 * t);
-      dq = mfma_bf(aE[s][0], bk, dq);
-      dq = mfma_bf(aE[s][1], bk, dq);
-      dk = mfma_bf(aET[s][0], bq, dk);
-      dk = mfma_bf(aET[s][1], bq, dk);
-      dk = mfma_bf(aF[s][0], bk, dk);
-      dk = mfma_bf(aF[s][1], bk, dk);
+      aE[s][0] = frag_row(qEh, LT, 16 * w + lr, 32 * s);
+      aE[s][1] = frag_row(qEl, LT, 16 * w + lr, 32 * s);
+      aET[s][0] = frag_col(qEh, LT, 32 * s, 16 * w);
+      aET[s][1] = frag_col(qEl, LT, 32 * s, 16 * w);
+      aF[s][0] = frag_row(qFh, LT, 16 * w + lr, 32 * s);
+      aF[s][1] = frag_row(qFl, LT, 16 * w + lr, 32 * s);
+    }
+    float q1[4] = {0.f, 0.f, 0.f, 0.f}, k2[4] = {0.f, 0.f, 0.f, 0.f}, k3[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < PT; ++t) {
+      f32x4 dq = zero4(), dk = zero4();
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8_t bk = frag_col(sK, LDK, 32 * s, 16 * t), bq = frag_col(sQ, LDK, 32 * s, 16 * t);
+        dq = mfma_bf(aE[s][0], bk, dq);
+        dq = mfma_bf(aE[s][1], bk, dq);
+        dk = mfma_bf(aET[s][0], bq, dk);
+        dk = mfma_bf(aET[s][1], bq, dk);
+        dk = mfma_bf(aF[s][0], bk, dk);
+        dk = mfma_bf(aF[s][1], bk, dk);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * w + 4 * lg + i, c = 16 * t + lr;
+        q1[i] += (float)sQ[r * LDK + c] * P1[t][i];
+        k2[i] += (float)sK[r * LDK + c] * P2[t][i];
+        k3[i] += (float)sK[r * LDK + c] * P3[t][i];
+        if (r < C) {
+          const size_t o = ((size_t)(r0 + r) * H + h) * DK + c;
+          p.dq[o] = sGam[r] * P1[t][i] + dq[i];
+          p.dk[o] = -sGam[r] * P2[t][i] + sFac[r] * P3[t][i] + dk[i];
+        }
+      }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + 4 * lg + i, c = 16 * t + lr;
-      q1[i] += (float)sQ[r * LDK + c] * p1[i];
-      k2[i] += (float)sK[r * LDK + c] * p2[i];
-      k3[i] += (float)sK[r * LDK + c] * p3[i];
-      if (r < C) {
-        const size_t o = ((size_t)(r0 + r) * H + h) * DK + c;
-        p.dq[o] = sGam[r] * p1[i] + dq[i];
-        p.dk[o] = -sGam[r] * p2[i] + sFac[r] * p3[i] + dk[i];
+      const float a = sum16(q1[i]), b = sum16(k2[i]), c = sum16(k3[i]);
+      if (lr == 0) {
+        const int r = 16 * w + 4 * lg + i;
+        rowt[3][r] = a;
+        rowt[4][r] = b;
+        rowt[5][r] = c;
       }
     }
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    q1[i] = sum16(q1[i]);
-    k2[i] = sum16(k2[i]);
-    k3[i] = sum16(k3[i]);
-  }
-  if (lr == 0)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + 4 * lg + i;
-      const float zc = cs[1][0][r] + cs[1][1][r] + cs[1][2][r] + cs[1][3][r];
-      const float yc = cs[2][0][r] + cs[2][1][r] + cs[2][2][r] + cs[2][3][r];
-      const float t3 = sFac[r] * k3[i];
-      dG[r] = r < C ? sGam[r] * (q1[i] - k2[i]) - t3 + vr[0][r] - zc + vr[2][r] - yc : 0.f;
-      t3s[r] = r < C ? t3 : 0.f;
-    }
   sync_lds();
   if (w == 0) {
-    // dG_{C-1} also takes sum_r fac_r <k_r, P3_r> + gam_{C-1} <dH', H>;
-    // dg_t = sum_{r >= t} dG_r
-    const float extra = wave_sum(t3s[l]) + sGam[C - 1] * gw[part_sh(DK)];
-    const float x = dG[l] + (l == C - 1 ? extra : 0.f);
+    // dG_r = gam_r (<q_r,P1_r> - <k_r,P2_r>) - fac_r <k_r,P3_r> + row and
+    // column sums of Z and Y; dG_{C-1} also takes sum_r fac_r <k_r, P3_r> and
+    // gam_{C-1} <dH', H>; dg_t = sum_{r >= t} dG_r; dbeta = the two beta sums
+    const int r = l;
+    float cl[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) cl[k] = colt[k][0][r] + colt[k][1][r] + colt[k][2][r] + colt[k][3][r];
+    const float t3 = r < C ? sFac[r] * rowt[5][r] : 0.f;
+    const float dGr =
+        r < C ? sGam[r] * (rowt[3][r] - rowt[4][r]) - t3 + rowt[0][r] - cl[1] + rowt[2][r] - cl[2] : 0.f;
+    const float shs = sh4[0] + sh4[1] + sh4[2] + sh4[3];
+    const float extra = wave_sum(t3) + sGam[C - 1] * shs;
+    const float x = dGr + (r == C - 1 ? extra : 0.f);
     const float incl = wave_inclusive_scan(x);
     const float suffix = __shfl(incl, 63, 64) - incl + x;
-    if (l < C) {
-      const size_t o = (size_t)(r0 + l) * H + h;
+    if (r < C) {
+      const size_t o = (size_t)(r0 + r) * H + h;
       p.dg[o] = suffix;
-      p.dbeta[o] = cs[0][0][l] + cs[0][1][l] + cs[0][2][l] + cs[0][3][l] + vr[1][l];
+      p.dbeta[o] = cl[0] + rowt[1][r];
     }
   }
 }
@@ -1263,15 +1230,13 @@ hipError_t launch_all(const BwdParams &p, hipStream_t st) {
   else
     hipLaunchKernelGGL((bwd_dh_kernel<In, DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  if constexpr (std::is_same_v<In, bf16>)
-    hipLaunchKernelGGL((bwd_part_bf16_kernel<DK>), dim3(cells), dim3(512), 0, st, p);
-  else
+  if constexpr (std::is_same_v<In, bf16>) {
+    hipLaunchKernelGGL((bwd_cell_bf16_kernel<DK>), dim3(cells), dim3(256), 0, st, p);
+  } else {
     hipLaunchKernelGGL((bwd_part_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  if constexpr (std::is_same_v<In, bf16>)
-    hipLaunchKernelGGL((bwd_final_bf16_kernel<DK>), dim3(cells), dim3(256), 0, st, p);
-  else
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     hipLaunchKernelGGL((bwd_final_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
+  }
   return hipGetLastError();
 }
 
