@@ -36,6 +36,49 @@ namespace {
 
 using namespace bwd;
 
+// bf16 MFMA helpers for the kernels of bf16 inputs
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ f32x4 mfma_bf(bf16x8_t a, bf16x8_t b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// fragment lane (g, j) <- X[row][k0 + 8g .. k0 + 8g + 7] (row picked by the caller)
+__device__ __forceinline__ bf16x8_t frag_row(const __bf16 *X, int ld, int row, int k0) {
+  return *reinterpret_cast<const bf16x8_t *>(X + row * ld + k0 + 8 * (lane_id() >> 4));
+}
+
+// fragment lane (g, j) <- X[k0 + 8g + e][n0 + j], e = 0..7: column n0 + j of
+// the row-major X read down eight rows.  Each 16-lane group reads rows
+// k0 + 8g .. +3 (then +4 .. +7) as sixteen 4-element pieces; the transposing
+// read hands lane j element e of the piece read by lane 4e + j/4, entry j%4,
+// so lane t addresses row k0 + 8g + t/4 at columns n0 + 4(t%4).
+__device__ __forceinline__ bf16x8_t frag_col(const __bf16 *X, int ld, int k0, int n0) {
+  const int l = lane_id(), g = l >> 4, t = l & 15;
+  const __bf16 *a = X + (k0 + 8 * g + (t >> 2)) * ld + n0 + 4 * (t & 3);
+  const s16x4 lo = ds_read_tr16(reinterpret_cast<const char *>(a));
+  const s16x4 hi = ds_read_tr16(reinterpret_cast<const char *>(a + 4 * ld));
+  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+__device__ __forceinline__ void splitb(float x, __bf16 &hi, __bf16 &lo) {
+  hi = (__bf16)x;
+  lo = (__bf16)(x - (float)hi);
+}
+
+// acc += A B over one 32-wide k-step, A and B both split
+__device__ __forceinline__ f32x4 mfma3(bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl, f32x4 c) {
+  c = mfma_bf(ah, bh, c);
+  c = mfma_bf(ah, bl, c);
+  return mfma_bf(al, bh, c);
+}
+
+// barrier after this wave's own LDS operations have completed; outstanding
+// global loads and stores are not waited for
+__device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+
 // ------------------------------------------------------------------ prep
 template <typename In, int DK>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
@@ -75,12 +118,81 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
       sS[r * kL + s] = Sv;
       img[kPrepS + r * 64 + s] = Sv;
       img[kPrepM + r * 64 + s] = Mv;
-      if constexpr (std::is_same_v<In, bf16>) {
-        __bf16 *mb = reinterpret_cast<__bf16 *>(img + kPrepH) + r * 64 + s;
-        const __bf16 mh = (__bf16)Mv;
-        mb[0] = mh;
-        mb[4096] = (__bf16)(Mv - (float)mh);
-      }
+    }
+  }
+  __syncthreads();
+  // A^-1 = (I + diag(beta) S)^-1, by 16x16 blocks
+  unit_lower_inverse(sS, sB, sX, C);
+  for (int idx = tid; idx < 64 * 64; idx += 256) img[kPrepA + idx] = sX[(idx >> 6) * kL + (idx & 63)];
+  if (tid < 64) {
+    const float Gc = sG[C - 1];
+    img[kPrepG + tid] = sG[tid];
+    img[kPrepGam + tid] = tid < C ? __expf(sG[tid]) : 0.f;
+    img[kPrepFac + tid] = tid < C ? __expf(Gc - sG[tid]) : 0.f;
+    img[kPrepBeta + tid] = sB[tid];
+  }
+}
+
+// The same for bf16 inputs: K and Q stay bf16 in LDS (exact) and S, M run
+// on bf16 MFMA with fp32 accumulation, one product per k-step.
+template <int DK>
+__global__ __launch_bounds__(256, 2) void bwd_prep_bf16_kernel(BwdParams p) {
+  constexpr int LDK = DK + 16, KP = 64 * DK / 8 / 256;
+  __shared__ __attribute__((aligned(16))) __bf16 sK[64 * LDK], sQ[64 * LDK];
+  __shared__ __attribute__((aligned(16))) float sS[64 * kL], sX[64 * kL];
+  __shared__ __attribute__((aligned(16))) float sG[64], sB[64];
+  const int H = p.H;
+  const int slot = blockIdx.x / H, h = blockIdx.x % H;
+  Chunk ch;
+  if (!chunk_of(p, slot, ch)) return;
+  const int C = ch.C;
+  const int tid = threadIdx.x, hq = h / (H / p.Hqk);
+#pragma unroll
+  for (int it = 0; it < KP; ++it) {
+    const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+    u32x4 kv = u32x4{0u, 0u, 0u, 0u}, qv = kv;
+    if (r < C) {
+      const size_t off = ((size_t)(ch.r0 + r) * p.Hqk + hq) * DK + c;
+      kv = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.k) + off);
+      qv = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.q) + off);
+    }
+    *reinterpret_cast<u32x4 *>(sK + r * LDK + c) = kv;
+    *reinterpret_cast<u32x4 *>(sQ + r * LDK + c) = qv;
+  }
+  if (tid < 64) {
+    const float gr = tid < C ? p.g[(size_t)(ch.r0 + tid) * H + h] : 0.f;
+    sG[tid] = wave_inclusive_scan(gr);  // rows >= C repeat G_{C-1}
+    sB[tid] = tid < C ? p.beta[(size_t)(ch.r0 + tid) * H + h] : 0.f;
+  }
+  __syncthreads();
+  float *img = p.prep + (size_t)blockIdx.x * kPrepFloats;
+  __bf16 *imh = reinterpret_cast<__bf16 *>(img + kPrepH);
+  const int w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
+  // S = strict_lower(K K^T * E), M = lower_incl(Q K^T * E): wave w, rows 16w
+  f32x4 aS[4] = {zero4(), zero4(), zero4(), zero4()};
+  f32x4 aM[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+  for (int s = 0; s < DK / 32; ++s) {
+    const bf16x8_t ak = frag_row(sK, LDK, 16 * w + lr, 32 * s), aq = frag_row(sQ, LDK, 16 * w + lr, 32 * s);
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const bf16x8_t b = frag_row(sK, LDK, 16 * s4 + lr, 32 * s);
+      aS[s4] = mfma_bf(ak, b, aS[s4]);
+      aM[s4] = mfma_bf(aq, b, aM[s4]);
+    }
+  }
+#pragma unroll
+  for (int s4 = 0; s4 < 4; ++s4) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * lg + i, s = 16 * s4 + lr;
+      const float e = (r < C && s <= r) ? __expf(sG[r] - sG[s]) : 0.f;
+      const float Sv = s < r ? aS[s4][i] * e : 0.f;
+      const float Mv = aM[s4][i] * e;
+      sS[r * kL + s] = Sv;
+      img[kPrepS + r * 64 + s] = Sv;
+      img[kPrepM + r * 64 + s] = Mv;
+      splitb(Mv, imh[r * 64 + s], imh[4096 + r * 64 + s]);
     }
   }
   __syncthreads();
@@ -88,13 +200,9 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
   unit_lower_inverse(sS, sB, sX, C);
   for (int idx = tid; idx < 64 * 64; idx += 256) {
     const int r = idx >> 6, c = idx & 63;
-    img[kPrepA + idx] = sX[r * kL + c];
-    if constexpr (std::is_same_v<In, bf16>) {
-      const float at = sX[r * kL + c] * sB[c];  // A^-1 diag(beta)
-      const __bf16 ah = (__bf16)at;
-      reinterpret_cast<__bf16 *>(img + kPrepH)[8192 + idx] = ah;
-      reinterpret_cast<__bf16 *>(img + kPrepH)[12288 + idx] = (__bf16)(at - (float)ah);
-    }
+    const float a = sX[r * kL + c];
+    img[kPrepA + idx] = a;
+    splitb(a * sB[c], imh[8192 + idx], imh[12288 + idx]);  // A^-1 diag(beta)
   }
   if (tid < 64) {
     const float Gc = sG[C - 1];
@@ -228,47 +336,6 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdParams p) {
 // fetched into registers while the current chunk computes; barriers are
 // plain s_barrier after this wave's LDS operations, so those loads stay in
 // flight across them.
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma_bf(bf16x8_t a, bf16x8_t b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// fragment lane (g, j) <- X[row][k0 + 8g .. k0 + 8g + 7] (row picked by the caller)
-__device__ __forceinline__ bf16x8_t frag_row(const __bf16 *X, int ld, int row, int k0) {
-  return *reinterpret_cast<const bf16x8_t *>(X + row * ld + k0 + 8 * (lane_id() >> 4));
-}
-
-// fragment lane (g, j) <- X[k0 + 8g + e][n0 + j], e = 0..7: column n0 + j of
-// the row-major X read down eight rows.  Each 16-lane group reads rows
-// k0 + 8g .. +3 (then +4 .. +7) as sixteen 4-element pieces; the transposing
-// read hands lane j element e of the piece read by lane 4e + j/4, entry j%4,
-// so lane t addresses row k0 + 8g + t/4 at columns n0 + 4(t%4).
-__device__ __forceinline__ bf16x8_t frag_col(const __bf16 *X, int ld, int k0, int n0) {
-  const int l = lane_id(), g = l >> 4, t = l & 15;
-  const __bf16 *a = X + (k0 + 8 * g + (t >> 2)) * ld + n0 + 4 * (t & 3);
-  const s16x4 lo = ds_read_tr16(reinterpret_cast<const char *>(a));
-  const s16x4 hi = ds_read_tr16(reinterpret_cast<const char *>(a + 4 * ld));
-  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-__device__ __forceinline__ void splitb(float x, __bf16 &hi, __bf16 &lo) {
-  hi = (__bf16)x;
-  lo = (__bf16)(x - (float)hi);
-}
-
-// acc += A B over one 32-wide k-step, A and B both split
-__device__ __forceinline__ f32x4 mfma3(bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl, f32x4 c) {
-  c = mfma_bf(ah, bh, c);
-  c = mfma_bf(ah, bl, c);
-  return mfma_bf(al, bh, c);
-}
-
-// barrier after this wave's own LDS operations have completed; outstanding
-// global loads and stores are not waited for
-__device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
 template <int DK>
 __global__ __launch_bounds__(256) void bwd_dh_bf16_kernel(BwdParams p) {
   constexpr int DV = DK, SV = DV / 32, LDK = DK + 16, LT = 72, LO = 48, LC = 36, NKS = DK / 32;
@@ -1223,7 +1290,10 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
 template <typename In, int DK>
 hipError_t launch_all(const BwdParams &p, hipStream_t st) {
   const int cells = p.NT * p.H;
-  hipLaunchKernelGGL((bwd_prep_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
+  if constexpr (std::is_same_v<In, bf16>)
+    hipLaunchKernelGGL((bwd_prep_bf16_kernel<DK>), dim3(cells), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((bwd_prep_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   if constexpr (std::is_same_v<In, bf16>)
     hipLaunchKernelGGL((bwd_dh_bf16_kernel<DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
