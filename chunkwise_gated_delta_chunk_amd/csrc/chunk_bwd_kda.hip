@@ -411,11 +411,14 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
     const float Gx = sG[x * LK + i], qx = sQ[x * LK + i], kx = sK[x * LK + i];
     const float GCi = sG[(C - 1) * LK + i];
     float f1 = 0.f, f2 = 0.f, f3 = 0.f, f4 = 0.f;
+    // unrolled so that several iterations' LDS reads and exps are in flight
+#pragma unroll 8
     for (int s = 0; s <= x; ++s) {  // E_xs = exp(G_x - G_s), s <= x
       const float e = __expf(Gx - sG[s * LK + i]) * sK[s * LK + i];
       f1 += sDM[x * kL + s] * e;
       f3 += sDS[x * kL + s] * e;
     }
+#pragma unroll 8
     for (int r = x; r < C; ++r) {  // E_rx = exp(G_r - G_x), r >= x
       const float e = __expf(sG[r * LK + i] - Gx);
       f2 += sDM[r * kL + x] * sQ[r * LK + i] * e;
@@ -432,15 +435,25 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
   // per channel: the last-row terms (sum_r Kh P3 and exp(G_C) <dH', H>)
   // belong to G_{C-1}, which every row's cumulative sum includes; then dg is
   // the reverse cumulative sum down the rows
+  // (every row of the channel is read before any is written, so the 64
+  // reads are in flight together rather than one round trip per row)
   for (int i = tid; i < DK; i += 256) {
     const float GCi = sG[(C - 1) * LK + i];
     float extra = __expf(GCi) * shv[i];
-    for (int x = 0; x < C; ++x) extra += __expf(GCi - sG[x * LK + i]) * sK[x * LK + i] * P3[x * DK + i];
-    float run = 0.f;
-    for (int x = C - 1; x >= 0; --x) {
-      const size_t o = ((size_t)(r0 + x) * H + h) * DK + i;
-      run += p.dg[o];
-      p.dg[o] = run + extra;
+    float dgx[kBT];
+#pragma unroll
+    for (int x = 0; x < kBT; ++x) {
+      dgx[x] = 0.f;
+      if (x < C) {
+        extra += __expf(GCi - sG[x * LK + i]) * sK[x * LK + i] * P3[x * DK + i];
+        dgx[x] = p.dg[((size_t)(r0 + x) * H + h) * DK + i];
+      }
+    }
+    float run = extra;
+#pragma unroll
+    for (int x = kBT - 1; x >= 0; --x) {
+      run += dgx[x];
+      if (x < C) p.dg[((size_t)(r0 + x) * H + h) * DK + i] = run;
     }
   }
 }
