@@ -393,9 +393,12 @@ def bwd_alg_flops(cells, d, kda=False):
 
 
 def bench_bwd(args, torch, la, synth, dev):
-    """One GDN chunk backward per step (forward recompute + four backward
-    launches) on the 8K varlen inputs; HIP events around the calls, then a
-    graph of one call replayed."""
+    """One chunk backward per step (forward recompute + the backward
+    launches: prep, dh and the fused per-chunk kernel for GDN; prep, dh, part
+    and final for KDA) on the workload's inputs; HIP events around the calls,
+    then a graph of one call replayed.  GDN's bf16 path runs on bf16 MFMA
+    (operands split into bf16 high and low halves) and is priced against the
+    bf16 peak; KDA's runs on fp32 MFMA and is priced against the fp32 peak."""
     cfg, kda, desc = WORKLOADS[args.workload]
     kda = bool(kda)
     inp = synth.config(cfg)
@@ -455,20 +458,22 @@ def bench_bwd(args, torch, la, synth, dev):
     cells = int(np.ceil(np.diff(inp["cu_seqlens"]) / 64).sum()) * H
     fl = bwd_alg_flops(cells, d, kda)
     achieved = fl / (call_ms * 1e-3) / 1e12
+    peak = MFMA_F32_PEAK_TFLOPS if kda else MFMA_F16_PEAK_TFLOPS
     out = {
         "metric": "GDN/KDA chunk-fwd tokens/s (H=16,d=128,8K varlen); % of HBM/MFMA roofline",
         "value": round(T * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 inputs; fp32 backward arithmetic",
+        "dtype": ("bf16 inputs; fp32 MFMA and VALU" if kda else
+                  "bf16 inputs; bf16 MFMA on split operands, fp32 accumulation"),
         "data": "synthetic (seeded, resident in HBM)",
         "config": {"workload": desc, "mode": "graph-replay of one backward call",
                    "tokens": T, "heads": H, "d": d, "sequences": N},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2),
-                     "peak": MFMA_F32_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_F32_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": ("kda" if kda else "gdn") +
-                               "_chunk_bwd (whole call: map, reduce, prep, dh, part, final)",
+                     "peak": peak, "unit": "TFLOP/s",
+                     "frac": round(achieved / peak, 4), "traffic": None,
+                     "kernel": "kda_chunk_bwd (whole call: map, reduce, prep, dh, part, final)" if kda
+                               else "gdn_chunk_bwd (whole call: map, reduce, prep, dh, fused part+final)",
                      "alg_flops_per_call": fl, "avg_call_ms": round(call_ms, 5)},
         "graph_equals_eager": graph_eq,
     }
