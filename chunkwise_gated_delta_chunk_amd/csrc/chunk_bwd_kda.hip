@@ -99,21 +99,56 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(BwdParams p) {
   }
   __syncthreads();
   float *img = p.prep + (size_t)blockIdx.x * kda_prep_floats(DK);
-  // S and M: one (r, s) pair at a time, the decay inside the channel sum
-  for (int pr = tid; pr < 4096; pr += 256) {
+  // S and M by 16-row blocks, the decay inside the channel sum.  Within a
+  // diagonal block, pair by pair (e^{G_r - G_s} <= 1 for s <= r).  A block
+  // pair R > S' factorises through the last row b of S':
+  // e^{G_r - G_s} = e^{G_r - G_b} e^{G_b - G_s}, both factors <= 1, so the
+  // tile is a plain product of decayed rows on fp32 MFMA.
+  auto put = [&](int r, int s, float as, float am) {
+    const float Sv = s < r ? as : 0.f;
+    sS[r * kL + s] = Sv;
+    img[kPrepS + r * 64 + s] = Sv;
+    img[kPrepM + r * 64 + s] = am;
+  };
+  for (int pr = tid; pr < 4096; pr += 256) {  // zero everything above the diagonal blocks
     const int r = pr >> 6, s = pr & 63;
+    if ((s >> 4) > (r >> 4)) put(r, s, 0.f, 0.f);
+  }
+  for (int pr = tid; pr < 4 * 256; pr += 256) {
+    const int blk = pr >> 8, r = 16 * blk + ((pr >> 4) & 15), s = 16 * blk + (pr & 15);
     float as = 0.f, am = 0.f;
     if (r < C && s <= r) {
+#pragma unroll 8
       for (int i = 0; i < DK; ++i) {
         const float e = __expf(sG[r * LK + i] - sG[s * LK + i]) * sK[s * LK + i];
         as += sK[r * LK + i] * e;
         am += sQ[r * LK + i] * e;
       }
     }
-    const float Sv = s < r ? as : 0.f;
-    sS[r * kL + s] = Sv;
-    img[kPrepS + pr] = Sv;
-    img[kPrepM + pr] = am;
+    put(r, s, as, am);
+  }
+  {
+    const int w = tid >> 6, l = lane_id(), j = l & 15, g = l >> 4;
+    for (int t = w; t < 6; t += 4) {  // (R, S'): (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+      const int R = t < 1 ? 1 : t < 3 ? 2 : 3, Sb = t - R * (R - 1) / 2, b = 16 * Sb + 15;
+      const int ra = 16 * R + j, sa = 16 * Sb + j;  // this lane's A row and B column
+      f32x4 aS = zero4(), aM = zero4();
+#pragma unroll 4
+      for (int i0 = 0; i0 < DK; i0 += 4) {
+        const int i = i0 + g;
+        const float gb = sG[b * LK + i];
+        const float er = __expf(sG[ra * LK + i] - gb), es = __expf(gb - sG[sa * LK + i]);
+        const float bk = sK[sa * LK + i] * es;
+        aS = mfma4(sK[ra * LK + i] * er, bk, aS);
+        aM = mfma4(sQ[ra * LK + i] * er, bk, aM);
+      }
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int r = 16 * R + 4 * g + ii, s = 16 * Sb + j;
+        const bool ok = r < C;
+        put(r, s, ok ? aS[ii] : 0.f, ok ? aM[ii] : 0.f);
+      }
+    }
   }
   __syncthreads();
   unit_lower_inverse(sS, sB, sX, C);
