@@ -375,6 +375,14 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
   const float *img = p.prep + (size_t)blockIdx.x * kda_prep_floats(DK);
   const float *gw = p.part + (size_t)blockIdx.x * part_floats(DK);
+  const float *P1 = gw + kPartP1, *P2 = gw + part_p2(DK), *P3 = gw + part_p3(DK);
+  // this thread's P1..P3 entries for the first two steps of the (row,
+  // channel) pass, fetched now so that their latency passes under phase A;
+  // the pass then fetches two steps ahead
+  constexpr int NPR = 64 * DK / 256;
+  float pa[3], pb[3];
+  pa[0] = P1[tid], pa[1] = P2[tid], pa[2] = P3[tid];
+  pb[0] = P1[tid + 256], pb[1] = P2[tid + 256], pb[2] = P3[tid + 256];
   load_mat64(sA, img + kPrepA);
   load_mat64(sS, img + kPrepS);
   load_mat64(sDM, gw + part_dm(DK));
@@ -436,37 +444,109 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
     const size_t o = (size_t)(r0 + tid) * H + h;
     p.dbeta[o] = bt[tid] + ba[tid];
   }
-  const float *P1 = gw + kPartP1, *P2 = gw + part_p2(DK), *P3 = gw + part_p3(DK);
   const float *shv = gw + part_sh(DK);
   // (row, channel) pairs over all threads, a wave's lanes on consecutive
   // channels of one row: the E-weighted sums, dq, dk and each row's dG
-  for (int pr = tid; pr < 64 * DK; pr += 256) {
-    const int x = pr / DK, i = pr % DK;
+#pragma unroll 1
+  for (int k = 0; k < NPR; ++k) {
+    const int pr = tid + 256 * k, x = pr / DK, i = pr % DK;
+    const float p1 = pa[0], p2 = pa[1], p3 = pa[2];
+    pa[0] = pb[0], pa[1] = pb[1], pa[2] = pb[2];
+    if (k + 2 < NPR) {
+      const int q = pr + 512;
+      pb[0] = P1[q], pb[1] = P2[q], pb[2] = P3[q];
+    }
     if (x >= C) continue;
     const float Gx = sG[x * LK + i], qx = sQ[x * LK + i], kx = sK[x * LK + i];
     const float GCi = sG[(C - 1) * LK + i];
     float f1 = 0.f, f2 = 0.f, f3 = 0.f, f4 = 0.f;
-    // unrolled so that several iterations' LDS reads and exps are in flight
-#pragma unroll 8
-    for (int s = 0; s <= x; ++s) {  // E_xs = exp(G_x - G_s), s <= x
+    // the terms inside x's 16-row block (the other blocks follow on MFMA)
+    const int xb = x & ~15, xe = min(C, xb + 16);
+#pragma unroll 4
+    for (int s = xb; s <= x; ++s) {  // E_xs = exp(G_x - G_s), s <= x
       const float e = __expf(Gx - sG[s * LK + i]) * sK[s * LK + i];
       f1 += sDM[x * kL + s] * e;
       f3 += sDS[x * kL + s] * e;
     }
-#pragma unroll 8
-    for (int r = x; r < C; ++r) {  // E_rx = exp(G_r - G_x), r >= x
+#pragma unroll 4
+    for (int r = x; r < xe; ++r) {  // E_rx = exp(G_r - G_x), r >= x
       const float e = __expf(sG[r * LK + i] - Gx);
       f2 += sDM[r * kL + x] * sQ[r * LK + i] * e;
       f4 += sDS[r * kL + x] * sK[r * LK + i] * e;
     }
     const float gam = __expf(Gx), kh = __expf(GCi - Gx);
-    const float p1 = P1[x * DK + i], p2 = P2[x * DK + i], p3 = P3[x * DK + i];
     const size_t o = ((size_t)(r0 + x) * H + h) * DK + i;
     p.dq[o] = gam * p1 + f1;
     p.dk[o] = -gam * p2 + kh * p3 + f2 + f3 + f4;
     p.dg[o] = gam * qx * p1 - gam * kx * p2 - kh * kx * p3 + qx * f1 - kx * f2 + kx * f3 - kx * f4;
   }
-  __syncthreads();  // every row's dG is in dg
+  __syncthreads();  // every row's dq, dk and dG is in memory
+  // The E-weighted sums across 16-row blocks, added to dq, dk and dG.  Wave w
+  // owns row block X = w.  For a block S < X the decay factorises through
+  // the last row b of S: F1/F3 += exp(G_x - G_b) (dM|dS)[X,S] Kb_S with
+  // Kb_S = K_S exp(G_b - G_S); for blocks R > X through the last row b' of
+  // X: F2 + F4 += exp(G_b' - G_x) (dM[R,X]^T Qb_R + dS[R,X]^T Kb_R) with
+  // Qb_R, Kb_R = (Q_R, K_R) exp(G_R - G_b').  Every factor is at most one.
+  {
+    const int X = w, j = l & 15, g = l >> 4;
+    f32x4 F1[DK / 16], F3[DK / 16], F24[DK / 16];
+#pragma unroll
+    for (int t = 0; t < DK / 16; ++t) F1[t] = F3[t] = F24[t] = zero4();
+    for (int Sb = 0; Sb < X; ++Sb) {
+      const int b = 16 * Sb + 15;
+#pragma unroll
+      for (int t = 0; t < DK / 16; ++t) {
+        const int i = 16 * t + j;
+        f32x4 z1 = zero4(), z3 = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+          const int s = 16 * Sb + k0 + g;  // B row (k) of this lane
+          const float bv = sK[s * LK + i] * __expf(sG[b * LK + i] - sG[s * LK + i]);
+          const int am = 16 * X + j, ak = 16 * Sb + k0 + g;  // A (m, k) of this lane
+          z1 = mfma4(sDM[am * kL + ak], bv, z1);
+          z3 = mfma4(sDS[am * kL + ak], bv, z3);
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float sc = __expf(sG[(16 * X + 4 * g + ii) * LK + i] - sG[b * LK + i]);
+          F1[t][ii] += sc * z1[ii];
+          F3[t][ii] += sc * z3[ii];
+        }
+      }
+    }
+    const int bx = 16 * X + 15;
+    for (int Rb = X + 1; Rb < 4; ++Rb) {
+#pragma unroll
+      for (int t = 0; t < DK / 16; ++t) {
+        const int i = 16 * t + j;
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+          const int r = 16 * Rb + k0 + g;
+          const float e = __expf(sG[r * LK + i] - sG[bx * LK + i]);
+          const int am = 16 * X + j;
+          F24[t] = mfma4(sDM[r * kL + am], sQ[r * LK + i] * e, F24[t]);
+          F24[t] = mfma4(sDS[r * kL + am], sK[r * LK + i] * e, F24[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < DK / 16; ++t) {
+      const int i = 16 * t + j;
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int x = 16 * X + 4 * g + ii;
+        if (x >= C) continue;
+        const float f24 = X < 3 ? __expf(sG[bx * LK + i] - sG[x * LK + i]) * F24[t][ii] : 0.f;
+        const float f1 = F1[t][ii], f3 = F3[t][ii];
+        const float qx = sQ[x * LK + i], kx = sK[x * LK + i];
+        const size_t o = ((size_t)(r0 + x) * H + h) * DK + i;
+        p.dq[o] += f1;
+        p.dk[o] += f3 + f24;
+        p.dg[o] += qx * f1 + kx * (f3 - f24);
+      }
+    }
+  }
+  __syncthreads();  // every row's dG is complete
   // per channel: the last-row terms (sum_r Kh P3 and exp(G_C) <dH', H>)
   // belong to G_{C-1}, which every row's cumulative sum includes; then dg is
   // the reverse cumulative sum down the rows
