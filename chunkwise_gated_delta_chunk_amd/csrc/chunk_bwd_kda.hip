@@ -529,6 +529,23 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
         }
       }
     }
+    // every value is read before any is written: the three outputs may
+    // alias as far as the compiler knows, so interleaved read-modify-writes
+    // would each wait for the previous one
+    f32x4 oq[DK / 16], ok[DK / 16], og[DK / 16];
+#pragma unroll
+    for (int t = 0; t < DK / 16; ++t)
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int x = 16 * X + 4 * g + ii;
+        oq[t][ii] = ok[t][ii] = og[t][ii] = 0.f;
+        if (x < C) {
+          const size_t o = ((size_t)(r0 + x) * H + h) * DK + 16 * t + j;
+          oq[t][ii] = p.dq[o];
+          ok[t][ii] = p.dk[o];
+          og[t][ii] = p.dg[o];
+        }
+      }
 #pragma unroll
     for (int t = 0; t < DK / 16; ++t) {
       const int i = 16 * t + j;
@@ -540,9 +557,9 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
         const float f1 = F1[t][ii], f3 = F3[t][ii];
         const float qx = sQ[x * LK + i], kx = sK[x * LK + i];
         const size_t o = ((size_t)(r0 + x) * H + h) * DK + i;
-        p.dq[o] += f1;
-        p.dk[o] += f3 + f24;
-        p.dg[o] += qx * f1 + kx * (f3 - f24);
+        p.dq[o] = oq[t][ii] + f1;
+        p.dk[o] = ok[t][ii] + f3 + f24;
+        p.dg[o] = og[t][ii] + qx * f1 + kx * (f3 - f24);
       }
     }
   }
