@@ -10,6 +10,10 @@ namespace bwd {
 
 constexpr int kL = 68;  // row stride of the [64][64] LDS matrices (floats)
 
+// barrier after this wave's own LDS operations have completed; outstanding
+// global loads and stores are not waited for
+__device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }

@@ -74,9 +74,6 @@ __device__ __forceinline__ f32x4 mfma3(bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf
   return mfma_bf(al, bh, c);
 }
 
-// barrier after this wave's own LDS operations have completed; outstanding
-// global loads and stores are not waited for
-__device__ __forceinline__ void sync_lds() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
 
 
 // ------------------------------------------------------------------ prep

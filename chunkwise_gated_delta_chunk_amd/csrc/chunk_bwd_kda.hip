@@ -158,9 +158,17 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(BwdParams p) {
 }
 
 // -------------------------------------------------------------------- dh
+// The next chunk's raw K and Q rows, gates, A^-1 and M images and dO slice
+// are fetched into registers while the current chunk computes; the decays
+// are applied as the rows go to LDS, and Kt waits in registers until the dH
+// step needs it (in place of Kh), so no global read sits inside a chunk.
+// Barriers are plain s_barrier after the wave's own LDS operations, so the
+// fetch stays in flight across them.
 template <typename In, int DK>
 __global__ __launch_bounds__(256) void kda_dh_kernel(BwdParams p) {
   constexpr int LK = DK + 4, LC = 36, DV = DK, SV = DV / 32;
+  constexpr int VEC = 16 / (int)sizeof(In), PR = DK / VEC, IT = 64 * PR / 256;
+  static_assert(256 % PR == 0 && (64 * PR) % 256 == 0, "piece layout");
   __shared__ __attribute__((aligned(16))) float sK[kBT * LK], sQ[kBT * LK], sA[64 * kL],
       sM[64 * kL];
   __shared__ __attribute__((aligned(16))) float sO[64 * LC], sU[64 * LC], sY[64 * LC], sD[DK * LC];
@@ -175,25 +183,99 @@ __global__ __launch_bounds__(256) void kda_dh_kernel(BwdParams p) {
   const int bos = cu_at(p.cu_seqlens, p.cu64, n), eos = cu_at(p.cu_seqlens, p.cu64, n + 1);
   const int c0 = sv * 32;
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
+  const int Hqk = p.Hqk, hq = h / (H / Hqk);
   const size_t mat = (size_t)DK * DV;
   const size_t sb = ((size_t)n * H + h) * mat;
+  const int pcol = (tid % PR) * VEC;  // this thread's column in every K/Q piece
+
+  // one chunk's inputs in registers
+  u32x4 rk[IT], rq[IT];
+  f32x4 rg[IT][VEC / 4], rgc[VEC / 4], ra[4], rm[4], ro[2];
+  float rbeta = 0.f, rgcv = 0.f;
+  auto fetch = [&](int jj) {
+    const int r0 = bos + (jj - j0) * kBT, C = min(kBT, eos - r0);
+    const float *img = p.prep + ((size_t)jj * H + h) * kda_prep_floats(DK);
+    const float *G = img + kKdaG;
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int r = (tid + 256 * it) / PR;
+      rk[it] = rq[it] = u32x4{0u, 0u, 0u, 0u};
+      if (r < C) {
+        const size_t off = (((size_t)(r0 + r) * Hqk + hq) * DK + pcol) * sizeof(In);
+        rk[it] = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.k) + off);
+        rq[it] = *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.q) + off);
+      }
+#pragma unroll
+      for (int q = 0; q < VEC / 4; ++q) rg[it][q] = *reinterpret_cast<const f32x4 *>(G + r * DK + pcol + 4 * q);
+    }
+#pragma unroll
+    for (int q = 0; q < VEC / 4; ++q) rgc[q] = *reinterpret_cast<const f32x4 *>(G + (C - 1) * DK + pcol + 4 * q);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q;
+      ra[q] = *reinterpret_cast<const f32x4 *>(img + kPrepA + 4 * idx);
+      rm[q] = *reinterpret_cast<const f32x4 *>(img + kPrepM + 4 * idx);
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int pc = tid + 256 * q, r = pc / 8, c = (pc % 8) * 4;
+      ro[q] = r < C ? *reinterpret_cast<const f32x4 *>(p.dout + ((size_t)(r0 + r) * H + h) * DV + c0 + c)
+                    : zero4();
+    }
+    if (tid < 64) rbeta = img[kKdaBeta + tid];
+    if (tid < DK) rgcv = G[(C - 1) * DK + tid];
+  };
+
   if (p.dht) {
     load_block<DK, 32>(sD, LC, p.dht + sb + c0, DV);
   } else {
     for (int idx = tid; idx < DK * 32; idx += 256) sD[(idx / 32) * LC + idx % 32] = 0.f;
   }
+  fetch(j1 - 1);
+  float kt[IT][VEC];
   for (int jj = j1 - 1; jj >= j0; --jj) {
-    __syncthreads();
+    sync_lds();
     const int r0 = bos + (jj - j0) * kBT, C = min(kBT, eos - r0);
-    const float *img = p.prep + ((size_t)jj * H + h) * kda_prep_floats(DK);
-    const float *G = img + kKdaG;
-    load_decayed<In, DK, 1>(sK, LK, p.k, G, r0, C, p.Hqk, h / (H / p.Hqk));  // Kh
-    load_decayed<In, DK, 0>(sQ, LK, p.q, G, r0, C, p.Hqk, h / (H / p.Hqk));  // Qt
-    load_mat64(sA, img + kPrepA);
-    load_mat64(sM, img + kPrepM);
-    load_rows<float, DV, 32>(sO, LC, p.dout, r0, C, H, h, c0);
-    if (tid < 64) sBeta[tid] = img[kKdaBeta + tid];
-    if (tid < DK) sGC[tid] = __expf(G[(C - 1) * DK + tid]);
+    // Kh = K exp(G_C - G) and Qt = Q exp(G) to LDS; Kt = K exp(G) kept
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int r = (tid + 256 * it) / PR;
+      uint32_t kw[4], qw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kw[e] = rk[it][e];
+        qw[e] = rq[it][e];
+      }
+      float kf[VEC], qf[VEC];
+      unpack16<In>(kw, kf);
+      unpack16<In>(qw, qf);
+#pragma unroll
+      for (int q = 0; q < VEC / 4; ++q) {
+        f32x4 kh, qt;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float gv = rg[it][q][e], eg = __expf(gv);
+          kh[e] = kf[4 * q + e] * __expf(rgc[q][e] - gv);
+          qt[e] = qf[4 * q + e] * eg;
+          kt[it][4 * q + e] = kf[4 * q + e] * eg;
+        }
+        *reinterpret_cast<f32x4 *>(sK + r * LK + pcol + 4 * q) = kh;
+        *reinterpret_cast<f32x4 *>(sQ + r * LK + pcol + 4 * q) = qt;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int idx = tid + 256 * q, r = idx / 16, c = (idx % 16) * 4;
+      *reinterpret_cast<f32x4 *>(sA + r * kL + c) = ra[q];
+      *reinterpret_cast<f32x4 *>(sM + r * kL + c) = rm[q];
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int pc = tid + 256 * q, r = pc / 8, c = (pc % 8) * 4;
+      *reinterpret_cast<f32x4 *>(sO + r * LC + c) = ro[q] * p.scale;
+    }
+    if (tid < 64) sBeta[tid] = rbeta;
+    if (tid < DK) sGC[tid] = __expf(rgcv);
     float *dst = p.dhs + ((size_t)jj * H + h) * mat + c0;
 #pragma unroll
     for (int it = 0; it < DK * 8 / 256; ++it) {
@@ -201,9 +283,8 @@ __global__ __launch_bounds__(256) void kda_dh_kernel(BwdParams p) {
       *reinterpret_cast<f32x4 *>(dst + (size_t)i * DV + c) =
           *reinterpret_cast<const f32x4 *>(sD + i * LC + c);
     }
-    __syncthreads();
-    for (int idx = tid; idx < 64 * 32; idx += 256) sO[(idx / 32) * LC + idx % 32] *= p.scale;
-    __syncthreads();
+    if (jj > j0) fetch(jj - 1);
+    sync_lds();
     {  // dU = M^T dOb + Kh dH'
       f32x4 kd[2] = {zero4(), zero4()};
       mmN<2, DK>(kd, sK + 16 * w * LK, LK, 1, sD, LC, 1, 16);
@@ -213,8 +294,8 @@ __global__ __launch_bounds__(256) void kda_dh_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) sU[(16 * w + 4 * lg + i) * LC + 16 * nt + lr] = kd[nt][i];
     }
-    __syncthreads();
-    {  // dX = beta (A^-T dU); Kt replaces Kh meanwhile
+    sync_lds();
+    {  // dX = beta (A^-T dU)
       f32x4 dx[2] = {zero4(), zero4()};
       mmN<2, 64>(dx, sA + 16 * w, 1, kL, sU, LC, 1, 16);
 #pragma unroll
@@ -225,9 +306,17 @@ __global__ __launch_bounds__(256) void kda_dh_kernel(BwdParams p) {
           sY[r * LC + 16 * nt + lr] = sBeta[r] * dx[nt][i];
         }
     }
-    __syncthreads();
-    load_decayed<In, DK, 0>(sK, LK, p.k, G, r0, C, p.Hqk, h / (H / p.Hqk));  // Kt
-    __syncthreads();
+    sync_lds();
+    // Kt over Kh
+#pragma unroll
+    for (int it = 0; it < IT; ++it) {
+      const int r = (tid + 256 * it) / PR;
+#pragma unroll
+      for (int q = 0; q < VEC / 4; ++q)
+        *reinterpret_cast<f32x4 *>(sK + r * LK + pcol + 4 * q) =
+            f32x4{kt[it][4 * q], kt[it][4 * q + 1], kt[it][4 * q + 2], kt[it][4 * q + 3]};
+    }
+    sync_lds();
     // dH = exp(G_C) dH' + Qt^T dOb - Kt^T dX
     for (int t = w; t < DK / 16; t += 4) {
       f32x4 acc[2], ky[2] = {zero4(), zero4()};
@@ -247,7 +336,7 @@ __global__ __launch_bounds__(256) void kda_dh_kernel(BwdParams p) {
           sD[(16 * t + 4 * lg + i) * LC + 16 * nt + lr] = acc[nt][i] - ky[nt][i];
     }
   }
-  __syncthreads();
+  sync_lds();
   if (p.dh0)
     for (int idx = tid; idx < DK * 32; idx += 256) {
       const int i = idx / 32, c = idx % 32;
