@@ -376,17 +376,58 @@ __global__ __launch_bounds__(256) void kda_part_kernel(BwdParams p) {
 #pragma unroll
   for (int t = 0; t < 4; ++t) dM[t] = dT[t] = zero4();
   float shv = 0.f;  // <dH'_i, H_i> of row i = tid (tid < DK)
+  // the next 16-column block's H, dH', dO and V are fetched into registers
+  // while the current one computes; the loop's barriers wait only for LDS
+  constexpr int HPc = DK * 4 / 256, VECV = 16 / (int)sizeof(In), VPR = 16 / VECV, VNP = 64 * VPR;
+  f32x4 rh[HPc], rd[HPc], rdo;
+  u32x4 rvv = u32x4{0u, 0u, 0u, 0u};
+  auto fetch = [&](int cb) {
+#pragma unroll
+    for (int it = 0; it < HPc; ++it) {
+      const int pc = tid + 256 * it, i = pc / 4, c = (pc % 4) * 4;
+      rh[it] = *reinterpret_cast<const f32x4 *>(Hs + (size_t)i * DV + 16 * cb + c);
+      rd[it] = *reinterpret_cast<const f32x4 *>(Ds + (size_t)i * DV + 16 * cb + c);
+    }
+    {
+      const int r = tid / 4, c = (tid % 4) * 4;
+      rdo = r < C ? *reinterpret_cast<const f32x4 *>(p.dout + ((size_t)(r0 + r) * H + h) * DV + 16 * cb + c)
+                  : zero4();
+    }
+    if (tid < VNP) {
+      const int r = tid / VPR, c = (tid % VPR) * VECV;
+      rvv = r < C ? *reinterpret_cast<const u32x4 *>(static_cast<const char *>(p.v) +
+                                                      (((size_t)(r0 + r) * H + h) * DV + 16 * cb + c) * sizeof(In))
+                  : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  fetch(0);
   for (int cb = 0; cb < DV / 16; ++cb) {
-    __syncthreads();
-    load_block<DK, 16>(sH, LB, Hs + 16 * cb, DV);
-    load_block<DK, 16>(sDH, LB, Ds + 16 * cb, DV);
-    load_rows<In, DV, 16>(sV, LB, p.v, r0, C, H, h, 16 * cb);
-    load_rows<float, DV, 16>(sO, LB, p.dout, r0, C, H, h, 16 * cb);
-    __syncthreads();
+    sync_lds();
+#pragma unroll
+    for (int it = 0; it < HPc; ++it) {
+      const int pc = tid + 256 * it, i = pc / 4, c = (pc % 4) * 4;
+      *reinterpret_cast<f32x4 *>(sH + i * LB + c) = rh[it];
+      *reinterpret_cast<f32x4 *>(sDH + i * LB + c) = rd[it];
+    }
+    {
+      const int r = tid / 4, c = (tid % 4) * 4;
+      *reinterpret_cast<f32x4 *>(sO + r * LB + c) = rdo * p.scale;
+    }
+    if (tid < VNP) {
+      const int r = tid / VPR, c = (tid % VPR) * VECV;
+      uint32_t vw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) vw[e] = rvv[e];
+      float f[VECV];
+      unpack16<In>(vw, f);
+#pragma unroll
+      for (int q = 0; q < VECV / 4; ++q)
+        *reinterpret_cast<f32x4 *>(sV + r * LB + c + 4 * q) = f32x4{f[4 * q], f[4 * q + 1], f[4 * q + 2], f[4 * q + 3]};
+    }
+    if (cb + 1 < DV / 16) fetch(cb + 1);
+    sync_lds();
     if (tid < DK)
       for (int c = 0; c < 16; ++c) shv += sH[tid * LB + c] * sDH[tid * LB + c];
-    for (int idx = tid; idx < 64 * 16; idx += 256) sO[(idx / 16) * LB + idx % 16] *= p.scale;
-    __syncthreads();
     {
       f32x4 kh[1] = {zero4()}, kd[1] = {zero4()};
       mmN<1, DK>(kh, sKt + 16 * w * LK, LK, 1, sH, LB, 1, 0);
@@ -401,7 +442,7 @@ __global__ __launch_bounds__(256) void kda_part_kernel(BwdParams p) {
         sDU[r * LB + lr] = mo[i] + kd[0][i];
       }
     }
-    __syncthreads();
+    sync_lds();
     {
       const f32x4 u = mm2k<64>(sA + 16 * w * kL, kL, 1, sBX, LB, 1);
       const f32x4 dx = mm2k<64>(sA + 16 * w, 1, kL, sDU, LB, 1);
@@ -414,7 +455,7 @@ __global__ __launch_bounds__(256) void kda_part_kernel(BwdParams p) {
         if (r < C) p.dv[((size_t)(r0 + r) * H + h) * DV + 16 * cb + lr] = d;
       }
     }
-    __syncthreads();
+    sync_lds();
     mmN<NT, 16>(P1, sO + 16 * w * LB, LB, 1, sH, 1, LB, 16 * LB);
     mmN<NT, 16>(P2, sDX + 16 * w * LB, LB, 1, sH, 1, LB, 16 * LB);
     mmN<NT, 16>(P3, sU + 16 * w * LB, LB, 1, sDH, 1, LB, 16 * LB);
