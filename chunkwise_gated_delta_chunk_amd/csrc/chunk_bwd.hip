@@ -36,46 +36,6 @@ namespace {
 
 using namespace bwd;
 
-// bf16 MFMA helpers for the kernels of bf16 inputs
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ f32x4 mfma_bf(bf16x8_t a, bf16x8_t b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-// fragment lane (g, j) <- X[row][k0 + 8g .. k0 + 8g + 7] (row picked by the caller)
-__device__ __forceinline__ bf16x8_t frag_row(const __bf16 *X, int ld, int row, int k0) {
-  return *reinterpret_cast<const bf16x8_t *>(X + row * ld + k0 + 8 * (lane_id() >> 4));
-}
-
-// fragment lane (g, j) <- X[k0 + 8g + e][n0 + j], e = 0..7: column n0 + j of
-// the row-major X read down eight rows.  Each 16-lane group reads rows
-// k0 + 8g .. +3 (then +4 .. +7) as sixteen 4-element pieces; the transposing
-// read hands lane j element e of the piece read by lane 4e + j/4, entry j%4,
-// so lane t addresses row k0 + 8g + t/4 at columns n0 + 4(t%4).
-__device__ __forceinline__ bf16x8_t frag_col(const __bf16 *X, int ld, int k0, int n0) {
-  const int l = lane_id(), g = l >> 4, t = l & 15;
-  const __bf16 *a = X + (k0 + 8 * g + (t >> 2)) * ld + n0 + 4 * (t & 3);
-  const s16x4 lo = ds_read_tr16(reinterpret_cast<const char *>(a));
-  const s16x4 hi = ds_read_tr16(reinterpret_cast<const char *>(a + 4 * ld));
-  return __builtin_bit_cast(bf16x8_t, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-}
-
-__device__ __forceinline__ void splitb(float x, __bf16 &hi, __bf16 &lo) {
-  hi = (__bf16)x;
-  lo = (__bf16)(x - (float)hi);
-}
-
-// acc += A B over one 32-wide k-step, A and B both split
-__device__ __forceinline__ f32x4 mfma3(bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl, f32x4 c) {
-  c = mfma_bf(ah, bh, c);
-  c = mfma_bf(ah, bl, c);
-  return mfma_bf(al, bh, c);
-}
-
-
-
 // ------------------------------------------------------------------ prep
 template <typename In, int DK>
 __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {

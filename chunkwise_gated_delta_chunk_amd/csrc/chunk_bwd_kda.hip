@@ -104,11 +104,17 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(BwdParams p) {
   // pair R > S' factorises through the last row b of S':
   // e^{G_r - G_s} = e^{G_r - G_b} e^{G_b - G_s}, both factors <= 1, so the
   // tile is a plain product of decayed rows on fp32 MFMA.
+  __bf16 *imh = reinterpret_cast<__bf16 *>(img + kda_halves(DK));
   auto put = [&](int r, int s, float as, float am) {
     const float Sv = s < r ? as : 0.f;
     sS[r * kL + s] = Sv;
     img[kPrepS + r * 64 + s] = Sv;
     img[kPrepM + r * 64 + s] = am;
+    if constexpr (std::is_same_v<In, bf16>) {
+      const __bf16 mh = (__bf16)am;
+      imh[r * 64 + s] = mh;
+      imh[4096 + r * 64 + s] = (__bf16)(am - (float)mh);
+    }
   };
   for (int pr = tid; pr < 4096; pr += 256) {  // zero everything above the diagonal blocks
     const int r = pr >> 6, s = pr & 63;
@@ -152,7 +158,16 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(BwdParams p) {
   }
   __syncthreads();
   unit_lower_inverse(sS, sB, sX, C);
-  for (int idx = tid; idx < 4096; idx += 256) img[kPrepA + idx] = sX[(idx >> 6) * kL + (idx & 63)];
+  for (int idx = tid; idx < 4096; idx += 256) {
+    const float a = sX[(idx >> 6) * kL + (idx & 63)];
+    img[kPrepA + idx] = a;
+    if constexpr (std::is_same_v<In, bf16>) {
+      const float at = a * sB[idx & 63];  // A^-1 diag(beta)
+      const __bf16 ah = (__bf16)at;
+      imh[8192 + idx] = ah;
+      imh[12288 + idx] = (__bf16)(at - (float)ah);
+    }
+  }
   if (tid < 64) img[kKdaBeta + tid] = sB[tid];
   for (int idx = tid; idx < 64 * DK; idx += 256) img[kKdaG + idx] = sG[(idx / DK) * LK + idx % DK];
 }
@@ -334,6 +349,253 @@ __global__ __launch_bounds__(256) void kda_dh_kernel(BwdParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           sD[(16 * t + 4 * lg + i) * LC + 16 * nt + lr] = acc[nt][i] - ky[nt][i];
+    }
+  }
+  sync_lds();
+  if (p.dh0)
+    for (int idx = tid; idx < DK * 32; idx += 256) {
+      const int i = idx / 32, c = idx % 32;
+      p.dh0[sb + (size_t)i * DV + c0 + c] = sD[i * LC + c];
+    }
+}
+
+// ---------------------------------------------------------- dh, bf16 MFMA
+// The reverse pass for bf16 inputs on bf16 MFMA with split operands, as for
+// GDN.  The decayed rows Kh = K exp(G_C - G), Kt = K exp(G), Qt = Q exp(G)
+// are not exact in bf16, so they are split too (three MFMAs per product).
+// Kh and the M, A~ halves occupy LDS for dU and dX; Kt and Qt wait in
+// registers and take their places for the dH step.  The next chunk's raw
+// rows, gates, image halves and dO slice are fetched into registers while
+// the current chunk computes.
+template <int DK>
+__global__ __launch_bounds__(256) void kda_dh_bf16_kernel(BwdParams p) {
+  constexpr int DV = DK, SV = DV / 32, LDK = DK + 16, LT = 72, LO = 48, LC = 36, NKS = DK / 32;
+  constexpr int KP = 64 * DK / 8 / 256;  // 8-element K (and Q) pieces per thread
+  constexpr int R1 = 2 * 64 * LDK, R2 = 4 * 64 * LT;
+  static_assert(2 * 64 * LDK <= R2, "Qt halves fit over the M and A~ halves");
+  __shared__ __attribute__((aligned(16))) __bf16 r1[R1], r2[R2];
+  __shared__ __attribute__((aligned(16))) __bf16 sOh[64 * LO], sOl[64 * LO], sUh[64 * LO], sUl[64 * LO],
+      sXh[64 * LO], sXl[64 * LO];
+  __shared__ __attribute__((aligned(16))) __bf16 sDh[DK * LO], sDl[DK * LO];
+  __shared__ __attribute__((aligned(16))) float sD[DK * LC], sGC[DK];
+  __bf16 *const sKh = r1, *const sKl = r1 + 64 * LDK;          // Kh, then Kt
+  __bf16 *const sMh = r2, *const sMl = r2 + 64 * LT, *const sAh = r2 + 2 * 64 * LT,
+                *const sAl = r2 + 3 * 64 * LT;
+  __bf16 *const sQh = r2, *const sQl = r2 + 64 * LDK;          // Qt, after dX
+  const int H = p.H;
+  const int sv = blockIdx.x % SV, unit = blockIdx.x / SV;
+  if (unit >= p.N_max * H) return;
+  const int n = seq_by_rank(p.chunk_offsets, p.N_max, unit / H), h = unit % H;
+  if (n < 0) return;
+  const int j0 = p.chunk_offsets[n], j1 = p.chunk_offsets[n + 1];
+  if (j0 == j1) return;
+  const int bos = cu_at(p.cu_seqlens, p.cu64, n), eos = cu_at(p.cu_seqlens, p.cu64, n + 1);
+  const int c0 = sv * 32;
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
+  const int Hqk = p.Hqk, hq = h / (H / Hqk);
+  const size_t mat = (size_t)DK * DV;
+  const size_t sb = ((size_t)n * H + h) * mat;
+  const int pcol = (tid % (DK / 8)) * 8;  // this thread's column in every K/Q piece
+
+  u32x4 rk[KP], rq[KP], rimg[8];
+  f32x4 rg[KP][2], rgc[2], ro[2];
+  float rgcv = 0.f;
+  auto fetch = [&](int jj) {
+    const int r0 = bos + (jj - j0) * kBT, C = min(kBT, eos - r0);
+    const float *img = p.prep + ((size_t)jj * H + h) * kda_prep_floats(DK);
+    const float *G = img + kKdaG;
+#pragma unroll
+    for (int it = 0; it < KP; ++it) {
+      const int r = (tid + 256 * it) / (DK / 8);
+      rk[it] = rq[it] = u32x4{0u, 0u, 0u, 0u};
+      if (r < C) {
+        const size_t off = ((size_t)(r0 + r) * Hqk + hq) * DK + pcol;
+        rk[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.k) + off);
+        rq[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.q) + off);
+      }
+      rg[it][0] = *reinterpret_cast<const f32x4 *>(G + r * DK + pcol);
+      rg[it][1] = *reinterpret_cast<const f32x4 *>(G + r * DK + pcol + 4);
+    }
+    rgc[0] = *reinterpret_cast<const f32x4 *>(G + (C - 1) * DK + pcol);
+    rgc[1] = *reinterpret_cast<const f32x4 *>(G + (C - 1) * DK + pcol + 4);
+    const u32x4 *imh = reinterpret_cast<const u32x4 *>(img + kda_halves(DK));
+#pragma unroll
+    for (int it = 0; it < 8; ++it) rimg[it] = imh[tid + 256 * it];
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int pc = tid + 256 * q, r = pc / 8, c = (pc % 8) * 4;
+      ro[q] = r < C ? *reinterpret_cast<const f32x4 *>(p.dout + ((size_t)(r0 + r) * H + h) * DV + c0 + c)
+                    : zero4();
+    }
+    if (tid < DK) rgcv = G[(C - 1) * DK + tid];
+  };
+  auto put4 = [](__bf16 *hi, __bf16 *lo, f32x4 v) {
+    bf16x4_t a, b;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      a[e] = (__bf16)v[e];
+      b[e] = (__bf16)(v[e] - (float)a[e]);
+    }
+    *reinterpret_cast<bf16x4_t *>(hi) = a;
+    *reinterpret_cast<bf16x4_t *>(lo) = b;
+  };
+
+  for (int idx = tid; idx < DK * 32; idx += 256) {
+    const int i = idx / 32, c = idx % 32;
+    const float v = p.dht ? p.dht[sb + (size_t)i * DV + c0 + c] : 0.f;
+    sD[i * LC + c] = v;
+    splitb(v, sDh[i * LO + c], sDl[i * LO + c]);
+  }
+  fetch(j1 - 1);
+  bf16x8_t kth[KP], ktl[KP], qth[KP], qtl[KP];  // Kt and Qt halves until the dH step
+  for (int jj = j1 - 1; jj >= j0; --jj) {
+    sync_lds();
+    const int r0 = bos + (jj - j0) * kBT, C = min(kBT, eos - r0);
+#pragma unroll
+    for (int it = 0; it < KP; ++it) {
+      const int r = (tid + 256 * it) / (DK / 8);
+      uint32_t kw[4], qw[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kw[e] = rk[it][e];
+        qw[e] = rq[it][e];
+      }
+      float kf[8], qf[8];
+      unpack16<bf16>(kw, kf);
+      unpack16<bf16>(qw, qf);
+      bf16x8_t khh, khl;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float gv = rg[it][e >> 2][e & 3], eg = __expf(gv);
+        const float kh = kf[e] * __expf(rgc[e >> 2][e & 3] - gv), kt = kf[e] * eg, qt = qf[e] * eg;
+        khh[e] = (__bf16)kh;
+        khl[e] = (__bf16)(kh - (float)khh[e]);
+        kth[it][e] = (__bf16)kt;
+        ktl[it][e] = (__bf16)(kt - (float)kth[it][e]);
+        qth[it][e] = (__bf16)qt;
+        qtl[it][e] = (__bf16)(qt - (float)qth[it][e]);
+      }
+      *reinterpret_cast<bf16x8_t *>(sKh + r * LDK + pcol) = khh;
+      *reinterpret_cast<bf16x8_t *>(sKl + r * LDK + pcol) = khl;
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int pc = tid + 256 * it, a = pc >> 9, r = (pc & 511) / 8, c = (pc % 8) * 8;
+      *reinterpret_cast<u32x4 *>(r2 + a * 64 * LT + r * LT + c) = rimg[it];
+    }
+#pragma unroll
+    for (int q = 0; q < 2; ++q) {
+      const int pc = tid + 256 * q, r = pc / 8, c = (pc % 8) * 4;
+      put4(sOh + r * LO + c, sOl + r * LO + c, ro[q] * p.scale);
+    }
+    if (tid < DK) sGC[tid] = __expf(rgcv);
+    float *dst = p.dhs + ((size_t)jj * H + h) * mat + c0;
+#pragma unroll
+    for (int it = 0; it < DK * 8 / 256; ++it) {
+      const int pc = tid + 256 * it, i = pc / 8, c = (pc % 8) * 4;
+      *reinterpret_cast<f32x4 *>(dst + (size_t)i * DV + c) =
+          *reinterpret_cast<const f32x4 *>(sD + i * LC + c);
+    }
+    if (jj > j0) fetch(jj - 1);
+    sync_lds();
+    // dU = M^T dOb + Kh dH'
+    {
+      f32x4 du[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        const bf16x8_t ah = frag_row(sKh, LDK, 16 * w + lr, 32 * s), al = frag_row(sKl, LDK, 16 * w + lr, 32 * s);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          du[nt] = mfma3(ah, al, frag_col(sDh, LO, 32 * s, 16 * nt), frag_col(sDl, LO, 32 * s, 16 * nt), du[nt]);
+      }
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8_t ah = frag_col(sMh, LT, 32 * s, 16 * w), al = frag_col(sMl, LT, 32 * s, 16 * w);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          du[nt] = mfma3(ah, al, frag_col(sOh, LO, 32 * s, 16 * nt), frag_col(sOl, LO, 32 * s, 16 * nt), du[nt]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * w + 4 * lg + i, c = 16 * nt + lr;
+          splitb(du[nt][i], sUh[r * LO + c], sUl[r * LO + c]);
+        }
+    }
+    sync_lds();
+    // dX = A~^T dU
+    {
+      f32x4 dx[2] = {zero4(), zero4()};
+#pragma unroll
+      for (int s = 0; s < 2; ++s) {
+        const bf16x8_t ah = frag_col(sAh, LT, 32 * s, 16 * w), al = frag_col(sAl, LT, 32 * s, 16 * w);
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+          dx[nt] = mfma3(ah, al, frag_col(sUh, LO, 32 * s, 16 * nt), frag_col(sUl, LO, 32 * s, 16 * nt), dx[nt]);
+      }
+#pragma unroll
+      for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = 16 * w + 4 * lg + i, c = 16 * nt + lr;
+          splitb(dx[nt][i], sXh[r * LO + c], sXl[r * LO + c]);
+        }
+    }
+    sync_lds();
+    // Kt over Kh, Qt over the M and A~ halves
+#pragma unroll
+    for (int it = 0; it < KP; ++it) {
+      const int r = (tid + 256 * it) / (DK / 8);
+      *reinterpret_cast<bf16x8_t *>(sKh + r * LDK + pcol) = kth[it];
+      *reinterpret_cast<bf16x8_t *>(sKl + r * LDK + pcol) = ktl[it];
+      *reinterpret_cast<bf16x8_t *>(sQh + r * LDK + pcol) = qth[it];
+      *reinterpret_cast<bf16x8_t *>(sQl + r * LDK + pcol) = qtl[it];
+    }
+    sync_lds();
+    // dH = exp(G_C) dH' + Qt^T dOb - Kt^T dX
+    {
+      bf16x8_t boh[2][2], bol[2][2], bxh[2][2], bxl[2][2];
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt) {
+          boh[s][nt] = frag_col(sOh, LO, 32 * s, 16 * nt);
+          bol[s][nt] = frag_col(sOl, LO, 32 * s, 16 * nt);
+          bxh[s][nt] = frag_col(sXh, LO, 32 * s, 16 * nt);
+          bxl[s][nt] = frag_col(sXl, LO, 32 * s, 16 * nt);
+        }
+#pragma unroll
+      for (int tt = 0; tt < DK / 64; ++tt) {
+        const int t = w + 4 * tt;
+        f32x4 acc[2], ky[2] = {zero4(), zero4()};
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * t + 4 * lg + i;
+            acc[nt][i] = sGC[row] * sD[row * LC + 16 * nt + lr];
+          }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+          const bf16x8_t qh = frag_col(sQh, LDK, 32 * s, 16 * t), ql = frag_col(sQl, LDK, 32 * s, 16 * t);
+          const bf16x8_t kh = frag_col(sKh, LDK, 32 * s, 16 * t), kl = frag_col(sKl, LDK, 32 * s, 16 * t);
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            acc[nt] = mfma3(qh, ql, boh[s][nt], bol[s][nt], acc[nt]);
+            ky[nt] = mfma3(kh, kl, bxh[s][nt], bxl[s][nt], ky[nt]);
+          }
+        }
+#pragma unroll
+        for (int nt = 0; nt < 2; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int row = 16 * t + 4 * lg + i, c = 16 * nt + lr;
+            const float v = acc[nt][i] - ky[nt][i];
+            sD[row * LC + c] = v;
+            splitb(v, sDh[row * LO + c], sDl[row * LO + c]);
+          }
+      }
     }
   }
   sync_lds();
@@ -725,7 +987,10 @@ hipError_t launch_all(const BwdParams &p, hipStream_t st) {
   const int cells = p.NT * p.H;
   hipLaunchKernelGGL((kda_prep_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  hipLaunchKernelGGL((kda_dh_kernel<In, DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
+  if constexpr (std::is_same_v<In, bf16>)
+    hipLaunchKernelGGL((kda_dh_bf16_kernel<DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
+  else
+    hipLaunchKernelGGL((kda_dh_kernel<In, DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL((kda_part_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;

@@ -98,10 +98,12 @@ __host__ __device__ constexpr int part_dt(int d) { return 192 * d + 4096; }
 __host__ __device__ constexpr int part_sh(int d) { return 192 * d + 8192; }
 // (KDA: the <dH', H> term is a vector over the d_k rows, at part_sh)
 __host__ __device__ constexpr int part_floats(int d) { return 192 * d + 8192 + 256; }
-// KDA prep cell: A^-1, M, S ([64][64] each), beta (64), then the per-channel
-// cumulative gate G ([64][d])
+// KDA prep cell: A^-1, M, S ([64][64] each), beta (64), the per-channel
+// cumulative gate G ([64][d]), then for bf16 inputs bf16 high and low halves
+// of M and of A^-1 diag(beta), row-major [64][64] each (M hi, M lo, hi, lo)
 constexpr int kKdaBeta = 12288, kKdaG = 12352;
-__host__ __device__ constexpr int kda_prep_floats(int d) { return kKdaG + 64 * d; }
+__host__ __device__ constexpr int kda_halves(int d) { return kKdaG + 64 * d; }
+__host__ __device__ constexpr int kda_prep_floats(int d) { return kda_halves(d) + 4 * 4096 / 2; }
 
 struct BwdParams {
   const void *q, *k, *v;

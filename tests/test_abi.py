@@ -314,7 +314,7 @@ def test_backward_workspace_size():
     up = lambda x: -(-x // 256) * 256
     for kda in (False, True):
         img = la.workspace_bytes(T, N, H, d, d, torch.bfloat16, kda=kda, seg_len=-1)
-        prep = (12544 + 8192 if not kda else 12352 + 64 * d) * 4   # GDN: + bf16 halves of M^T, A^-T
+        prep = (12544 + 8192 if not kda else 12352 + 64 * d + 8192) * 4   # + bf16 halves of M, A~
         part = (192 * d + 8192 + 256) * 4
         want = up(img) + 2 * up(cells * d * d * 4) + up(cells * prep) + up(cells * part)
         assert la.bwd_workspace_bytes(T, N, H, d, d, torch.bfloat16, kda=kda) == want
