@@ -294,9 +294,9 @@ __global__ __launch_bounds__(256) void bwd_dh_kernel(BwdParams p) {
 // plain s_barrier after this wave's LDS operations, so those loads stay in
 // flight across them.
 template <int DK>
-__global__ __launch_bounds__(256) void bwd_dh_bf16_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void bwd_dh_bf16_kernel(BwdParams p) {
   constexpr int DV = DK, SV = DV / 32, LDK = DK + 16, LT = 72, LO = 48, LC = 36, NKS = DK / 32;
-  constexpr int KP = 64 * DK / 8 / 256;  // 16-byte K (and Q) pieces per thread
+  constexpr int KP = 64 * DK / 8 / 512;  // 16-byte K (and Q) pieces per thread
   __shared__ __attribute__((aligned(16))) __bf16 sK[64 * LDK], sQ[64 * LDK];
   // M and A~ = A^-1 diag(beta), both halves; M^T and A~^T are read transposed
   __shared__ __attribute__((aligned(16))) __bf16 sMh[64 * LT], sMl[64 * LT], sAh[64 * LT],
@@ -319,20 +319,23 @@ __global__ __launch_bounds__(256) void bwd_dh_bf16_kernel(BwdParams p) {
   const int bos = cu_at(p.cu_seqlens, p.cu64, n), eos = cu_at(p.cu_seqlens, p.cu64, n + 1);
   const int c0 = sv * 32;
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
+  // the dU and dX tiles: rows 16rt, columns 16ct; the dH tiles: column
+  // tile ht, row tiles (w >> 1) + 4k
+  const int rt = w & 3, ct = w >> 2, ht = w & 1;
   const int Hqk = p.Hqk, hq = h / (H / Hqk);
   const size_t mat = (size_t)DK * DV;
   const size_t sb = ((size_t)n * H + h) * mat;
 
   // one chunk's inputs in registers
-  u32x4 rk[KP], rq[KP], rimg[8];
-  f32x4 rdo[2];
-  float rgo[2], rvec = 0.f;
+  u32x4 rk[KP], rq[KP], rimg[4];
+  f32x4 rdo;
+  float rgo, rvec = 0.f;
   auto fetch = [&](int jj) {
     const int r0 = bos + (jj - j0) * kBT, C = min(kBT, eos - r0);
     const float *img = p.prep + ((size_t)jj * H + h) * kPrepFloats;
 #pragma unroll
     for (int it = 0; it < KP; ++it) {
-      const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+      const int pc = tid + 512 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
       const size_t off = ((size_t)(r0 + r) * Hqk + hq) * DK + c;
       rk[it] = rq[it] = u32x4{0u, 0u, 0u, 0u};
       if (r < C) {
@@ -342,20 +345,19 @@ __global__ __launch_bounds__(256) void bwd_dh_bf16_kernel(BwdParams p) {
     }
     const u32x4 *imh = reinterpret_cast<const u32x4 *>(img + kPrepH);
 #pragma unroll
-    for (int it = 0; it < 8; ++it) rimg[it] = imh[tid + 256 * it];
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int pc = tid + 256 * it, r = pc / 8, c = (pc % 8) * 4;
-      rdo[it] = r < C ? *reinterpret_cast<const f32x4 *>(p.dout + ((size_t)(r0 + r) * H + h) * DV + c0 + c)
-                      : zero4();
-      rgo[it] = img[kPrepGam + r];
+    for (int it = 0; it < 4; ++it) rimg[it] = imh[tid + 512 * it];
+    {
+      const int r = tid / 8, c = (tid % 8) * 4;
+      rdo = r < C ? *reinterpret_cast<const f32x4 *>(p.dout + ((size_t)(r0 + r) * H + h) * DV + c0 + c)
+                  : zero4();
+      rgo = img[kPrepGam + r];
     }
     if (tid < 128) rvec = img[kPrepGam + tid];  // gam, fac: consecutive in the image
   };
   static_assert(kPrepFac == kPrepGam + 64, "gate vectors");
 
   // the state gradient: fp32 [DK][32] and its halves
-  for (int idx = tid; idx < DK * 32; idx += 256) {
+  for (int idx = tid; idx < DK * 32; idx += 512) {
     const int i = idx / 32, c = idx % 32;
     const float v = p.dht ? p.dht[sb + (size_t)i * DV + c0 + c] : 0.f;
     sD[i * LC + c] = v;
@@ -367,24 +369,23 @@ __global__ __launch_bounds__(256) void bwd_dh_bf16_kernel(BwdParams p) {
     const int r0 = bos + (jj - j0) * kBT, C = min(kBT, eos - r0);
 #pragma unroll
     for (int it = 0; it < KP; ++it) {
-      const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+      const int pc = tid + 512 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
       *reinterpret_cast<u32x4 *>(sK + r * LDK + c) = rk[it];
       *reinterpret_cast<u32x4 *>(sQ + r * LDK + c) = rq[it];
     }
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int pc = tid + 256 * it, a = pc >> 9, r = (pc & 511) / 8, c = (pc % 8) * 8;
+    for (int it = 0; it < 4; ++it) {
+      const int pc = tid + 512 * it, a = pc >> 9, r = (pc & 511) / 8, c = (pc % 8) * 8;
       __bf16 *dst = a == 0 ? sMh : a == 1 ? sMl : a == 2 ? sAh : sAl;
       *reinterpret_cast<u32x4 *>(dst + r * LT + c) = rimg[it];
     }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int pc = tid + 256 * it, r = pc / 8, c = (pc % 8) * 4;
+    {
+      const int r = tid / 8, c = (tid % 8) * 4;
       bf16x4_t oh, ol, gh, gl;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float v = p.scale * rdo[it][e];
-        const float gv = rgo[it] * v;
+        const float v = p.scale * rdo[e];
+        const float gv = rgo * v;
         oh[e] = (__bf16)v;
         ol[e] = (__bf16)(v - (float)oh[e]);
         gh[e] = (__bf16)gv;
@@ -397,115 +398,89 @@ __global__ __launch_bounds__(256) void bwd_dh_bf16_kernel(BwdParams p) {
     }
     if (tid < 64) sGam[tid] = rvec;
     else if (tid < 128) sFac[tid - 64] = rvec;
-    // the gradient leaving this chunk, for the part kernel
+    // the gradient leaving this chunk, for the next kernel
     float *dst = p.dhs + ((size_t)jj * H + h) * mat + c0;
 #pragma unroll
-    for (int it = 0; it < DK * 8 / 256; ++it) {
-      const int pc = tid + 256 * it, i = pc / 8, c = (pc % 8) * 4;
+    for (int it = 0; it < DK * 8 / 512; ++it) {
+      const int pc = tid + 512 * it, i = pc / 8, c = (pc % 8) * 4;
       *reinterpret_cast<f32x4 *>(dst + (size_t)i * DV + c) =
           *reinterpret_cast<const f32x4 *>(sD + i * LC + c);
     }
     if (jj > j0) fetch(jj - 1);
     sync_lds();
-    // dU = M^T dOb + fac * (K dH'): wave w, rows 16w, both column tiles
+    // dU = M^T dOb + fac * (K dH'): one tile per wave
     {
-      f32x4 kd[2] = {zero4(), zero4()}, du[2] = {zero4(), zero4()};
+      f32x4 kd = zero4(), du = zero4();
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        const bf16x8_t a = frag_row(sK, LDK, 16 * w + lr, 32 * s);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          kd[nt] = mfma_bf(a, frag_col(sDh, LO, 32 * s, 16 * nt), kd[nt]);
-          kd[nt] = mfma_bf(a, frag_col(sDl, LO, 32 * s, 16 * nt), kd[nt]);
-        }
+        const bf16x8_t a = frag_row(sK, LDK, 16 * rt + lr, 32 * s);
+        kd = mfma_bf(a, frag_col(sDh, LO, 32 * s, 16 * ct), kd);
+        kd = mfma_bf(a, frag_col(sDl, LO, 32 * s, 16 * ct), kd);
       }
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8_t ah = frag_col(sMh, LT, 32 * s, 16 * w);
-        const bf16x8_t al = frag_col(sMl, LT, 32 * s, 16 * w);
+      for (int s = 0; s < 2; ++s)
+        du = mfma3(frag_col(sMh, LT, 32 * s, 16 * rt), frag_col(sMl, LT, 32 * s, 16 * rt),
+                   frag_col(sOh, LO, 32 * s, 16 * ct), frag_col(sOl, LO, 32 * s, 16 * ct), du);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          du[nt] = mfma3(ah, al, frag_col(sOh, LO, 32 * s, 16 * nt), frag_col(sOl, LO, 32 * s, 16 * nt),
-                         du[nt]);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i, c = 16 * ct + lr;
+        splitb(du[i] + sFac[r] * kd[i], sUh[r * LO + c], sUl[r * LO + c]);
       }
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + 4 * lg + i, c = 16 * nt + lr;
-          splitb(du[nt][i] + sFac[r] * kd[nt][i], sUh[r * LO + c], sUl[r * LO + c]);
-        }
     }
     sync_lds();
     // dX = beta * (A^-T dU) = A~^T dU; Y = gam * dX (over dOb, read by now)
     {
-      f32x4 dx[2] = {zero4(), zero4()};
+      f32x4 dx = zero4();
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8_t ah = frag_col(sAh, LT, 32 * s, 16 * w);
-        const bf16x8_t al = frag_col(sAl, LT, 32 * s, 16 * w);
+      for (int s = 0; s < 2; ++s)
+        dx = mfma3(frag_col(sAh, LT, 32 * s, 16 * rt), frag_col(sAl, LT, 32 * s, 16 * rt),
+                   frag_col(sUh, LO, 32 * s, 16 * ct), frag_col(sUl, LO, 32 * s, 16 * ct), dx);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          dx[nt] = mfma3(ah, al, frag_col(sUh, LO, 32 * s, 16 * nt), frag_col(sUl, LO, 32 * s, 16 * nt),
-                         dx[nt]);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i, c = 16 * ct + lr;
+        splitb(sGam[r] * dx[i], sYh[r * LO + c], sYl[r * LO + c]);
       }
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + 4 * lg + i, c = 16 * nt + lr;
-          splitb(sGam[r] * dx[nt][i], sYh[r * LO + c], sYl[r * LO + c]);
-        }
     }
     sync_lds();
     // dH = gam_C dH' + Q^T (gam dOb) - K^T Y
     {
       const float gamC = sGam[C - 1];
-      bf16x8_t bgh[2][2], bgl[2][2], byh[2][2], byl[2][2];
+      bf16x8_t bgh[2], bgl[2], byh[2], byl[2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          bgh[s][nt] = frag_col(sGOh, LO, 32 * s, 16 * nt);
-          bgl[s][nt] = frag_col(sGOl, LO, 32 * s, 16 * nt);
-          byh[s][nt] = frag_col(sYh, LO, 32 * s, 16 * nt);
-          byl[s][nt] = frag_col(sYl, LO, 32 * s, 16 * nt);
-        }
+      for (int s = 0; s < 2; ++s) {
+        bgh[s] = frag_col(sGOh, LO, 32 * s, 16 * ht);
+        bgl[s] = frag_col(sGOl, LO, 32 * s, 16 * ht);
+        byh[s] = frag_col(sYh, LO, 32 * s, 16 * ht);
+        byl[s] = frag_col(sYl, LO, 32 * s, 16 * ht);
+      }
 #pragma unroll
       for (int tt = 0; tt < DK / 64; ++tt) {
-        const int t = w + 4 * tt;
-        f32x4 acc[2], ky[2] = {zero4(), zero4()};
+        const int t = (w >> 1) + 4 * tt;
+        f32x4 acc, ky = zero4();
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[nt][i] = gamC * sD[(16 * t + 4 * lg + i) * LC + 16 * nt + lr];
+        for (int i = 0; i < 4; ++i) acc[i] = gamC * sD[(16 * t + 4 * lg + i) * LC + 16 * ht + lr];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           const bf16x8_t aq = frag_col(sQ, LDK, 32 * s, 16 * t);
           const bf16x8_t ak = frag_col(sK, LDK, 32 * s, 16 * t);
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            acc[nt] = mfma_bf(aq, bgh[s][nt], acc[nt]);
-            acc[nt] = mfma_bf(aq, bgl[s][nt], acc[nt]);
-            ky[nt] = mfma_bf(ak, byh[s][nt], ky[nt]);
-            ky[nt] = mfma_bf(ak, byl[s][nt], ky[nt]);
-          }
+          acc = mfma_bf(aq, bgh[s], acc);
+          acc = mfma_bf(aq, bgl[s], acc);
+          ky = mfma_bf(ak, byh[s], ky);
+          ky = mfma_bf(ak, byl[s], ky);
         }
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 16 * t + 4 * lg + i, c = 16 * nt + lr;
-            const float v = acc[nt][i] - ky[nt][i];
-            sD[row * LC + c] = v;
-            splitb(v, sDh[row * LO + c], sDl[row * LO + c]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * t + 4 * lg + i, c = 16 * ht + lr;
+          const float v = acc[i] - ky[i];
+          sD[row * LC + c] = v;
+          splitb(v, sDh[row * LO + c], sDl[row * LO + c]);
+        }
       }
     }
   }
   sync_lds();
   if (p.dh0)
-    for (int idx = tid; idx < DK * 32; idx += 256) {
+    for (int idx = tid; idx < DK * 32; idx += 512) {
       const int i = idx / 32, c = idx % 32;
       p.dh0[sb + (size_t)i * DV + c0 + c] = sD[i * LC + c];
     }
@@ -1253,7 +1228,7 @@ hipError_t launch_all(const BwdParams &p, hipStream_t st) {
     hipLaunchKernelGGL((bwd_prep_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   if constexpr (std::is_same_v<In, bf16>)
-    hipLaunchKernelGGL((bwd_dh_bf16_kernel<DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((bwd_dh_bf16_kernel<DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(512), 0, st, p);
   else
     hipLaunchKernelGGL((bwd_dh_kernel<In, DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
