@@ -368,9 +368,9 @@ __global__ __launch_bounds__(256) void kda_dh_kernel(BwdParams p) {
 // rows, gates, image halves and dO slice are fetched into registers while
 // the current chunk computes.
 template <int DK>
-__global__ __launch_bounds__(256) void kda_dh_bf16_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void kda_dh_bf16_kernel(BwdParams p) {
   constexpr int DV = DK, SV = DV / 32, LDK = DK + 16, LT = 72, LO = 48, LC = 36, NKS = DK / 32;
-  constexpr int KP = 64 * DK / 8 / 256;  // 8-element K (and Q) pieces per thread
+  constexpr int KP = 64 * DK / 8 / 512;  // 8-element K (and Q) pieces per thread
   constexpr int R1 = 2 * 64 * LDK, R2 = 4 * 64 * LT;
   static_assert(2 * 64 * LDK <= R2, "Qt halves fit over the M and A~ halves");
   __shared__ __attribute__((aligned(16))) __bf16 r1[R1], r2[R2];
@@ -392,13 +392,16 @@ __global__ __launch_bounds__(256) void kda_dh_bf16_kernel(BwdParams p) {
   const int bos = cu_at(p.cu_seqlens, p.cu64, n), eos = cu_at(p.cu_seqlens, p.cu64, n + 1);
   const int c0 = sv * 32;
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
+  // the dU and dX tiles: rows 16rt, columns 16ct; the dH tiles: column
+  // tile ht, row tiles (w >> 1) + 4k
+  const int rt = w & 3, ct = w >> 2, ht = w & 1;
   const int Hqk = p.Hqk, hq = h / (H / Hqk);
   const size_t mat = (size_t)DK * DV;
   const size_t sb = ((size_t)n * H + h) * mat;
   const int pcol = (tid % (DK / 8)) * 8;  // this thread's column in every K/Q piece
 
-  u32x4 rk[KP], rq[KP], rimg[8];
-  f32x4 rg[KP][2], rgc[2], ro[2];
+  u32x4 rk[KP], rq[KP], rimg[4];
+  f32x4 rg[KP][2], rgc[2], ro;
   float rgcv = 0.f;
   auto fetch = [&](int jj) {
     const int r0 = bos + (jj - j0) * kBT, C = min(kBT, eos - r0);
@@ -406,7 +409,7 @@ __global__ __launch_bounds__(256) void kda_dh_bf16_kernel(BwdParams p) {
     const float *G = img + kKdaG;
 #pragma unroll
     for (int it = 0; it < KP; ++it) {
-      const int r = (tid + 256 * it) / (DK / 8);
+      const int r = (tid + 512 * it) / (DK / 8);
       rk[it] = rq[it] = u32x4{0u, 0u, 0u, 0u};
       if (r < C) {
         const size_t off = ((size_t)(r0 + r) * Hqk + hq) * DK + pcol;
@@ -420,12 +423,11 @@ __global__ __launch_bounds__(256) void kda_dh_bf16_kernel(BwdParams p) {
     rgc[1] = *reinterpret_cast<const f32x4 *>(G + (C - 1) * DK + pcol + 4);
     const u32x4 *imh = reinterpret_cast<const u32x4 *>(img + kda_halves(DK));
 #pragma unroll
-    for (int it = 0; it < 8; ++it) rimg[it] = imh[tid + 256 * it];
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int pc = tid + 256 * q, r = pc / 8, c = (pc % 8) * 4;
-      ro[q] = r < C ? *reinterpret_cast<const f32x4 *>(p.dout + ((size_t)(r0 + r) * H + h) * DV + c0 + c)
-                    : zero4();
+    for (int it = 0; it < 4; ++it) rimg[it] = imh[tid + 512 * it];
+    {
+      const int r = tid / 8, c = (tid % 8) * 4;
+      ro = r < C ? *reinterpret_cast<const f32x4 *>(p.dout + ((size_t)(r0 + r) * H + h) * DV + c0 + c)
+                 : zero4();
     }
     if (tid < DK) rgcv = G[(C - 1) * DK + tid];
   };
@@ -440,7 +442,7 @@ __global__ __launch_bounds__(256) void kda_dh_bf16_kernel(BwdParams p) {
     *reinterpret_cast<bf16x4_t *>(lo) = b;
   };
 
-  for (int idx = tid; idx < DK * 32; idx += 256) {
+  for (int idx = tid; idx < DK * 32; idx += 512) {
     const int i = idx / 32, c = idx % 32;
     const float v = p.dht ? p.dht[sb + (size_t)i * DV + c0 + c] : 0.f;
     sD[i * LC + c] = v;
@@ -453,7 +455,7 @@ __global__ __launch_bounds__(256) void kda_dh_bf16_kernel(BwdParams p) {
     const int r0 = bos + (jj - j0) * kBT, C = min(kBT, eos - r0);
 #pragma unroll
     for (int it = 0; it < KP; ++it) {
-      const int r = (tid + 256 * it) / (DK / 8);
+      const int r = (tid + 512 * it) / (DK / 8);
       uint32_t kw[4], qw[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -479,74 +481,60 @@ __global__ __launch_bounds__(256) void kda_dh_bf16_kernel(BwdParams p) {
       *reinterpret_cast<bf16x8_t *>(sKl + r * LDK + pcol) = khl;
     }
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int pc = tid + 256 * it, a = pc >> 9, r = (pc & 511) / 8, c = (pc % 8) * 8;
+    for (int it = 0; it < 4; ++it) {
+      const int pc = tid + 512 * it, a = pc >> 9, r = (pc & 511) / 8, c = (pc % 8) * 8;
       *reinterpret_cast<u32x4 *>(r2 + a * 64 * LT + r * LT + c) = rimg[it];
     }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int pc = tid + 256 * q, r = pc / 8, c = (pc % 8) * 4;
-      put4(sOh + r * LO + c, sOl + r * LO + c, ro[q] * p.scale);
+    {
+      const int r = tid / 8, c = (tid % 8) * 4;
+      put4(sOh + r * LO + c, sOl + r * LO + c, ro * p.scale);
     }
     if (tid < DK) sGC[tid] = __expf(rgcv);
     float *dst = p.dhs + ((size_t)jj * H + h) * mat + c0;
 #pragma unroll
-    for (int it = 0; it < DK * 8 / 256; ++it) {
-      const int pc = tid + 256 * it, i = pc / 8, c = (pc % 8) * 4;
+    for (int it = 0; it < DK * 8 / 512; ++it) {
+      const int pc = tid + 512 * it, i = pc / 8, c = (pc % 8) * 4;
       *reinterpret_cast<f32x4 *>(dst + (size_t)i * DV + c) =
           *reinterpret_cast<const f32x4 *>(sD + i * LC + c);
     }
     if (jj > j0) fetch(jj - 1);
     sync_lds();
-    // dU = M^T dOb + Kh dH'
+    // dU = M^T dOb + Kh dH': one tile per wave
     {
-      f32x4 du[2] = {zero4(), zero4()};
+      f32x4 du = zero4();
 #pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        const bf16x8_t ah = frag_row(sKh, LDK, 16 * w + lr, 32 * s), al = frag_row(sKl, LDK, 16 * w + lr, 32 * s);
+      for (int s = 0; s < NKS; ++s)
+        du = mfma3(frag_row(sKh, LDK, 16 * rt + lr, 32 * s), frag_row(sKl, LDK, 16 * rt + lr, 32 * s),
+                   frag_col(sDh, LO, 32 * s, 16 * ct), frag_col(sDl, LO, 32 * s, 16 * ct), du);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          du[nt] = mfma3(ah, al, frag_col(sDh, LO, 32 * s, 16 * nt), frag_col(sDl, LO, 32 * s, 16 * nt), du[nt]);
+      for (int s = 0; s < 2; ++s)
+        du = mfma3(frag_col(sMh, LT, 32 * s, 16 * rt), frag_col(sMl, LT, 32 * s, 16 * rt),
+                   frag_col(sOh, LO, 32 * s, 16 * ct), frag_col(sOl, LO, 32 * s, 16 * ct), du);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i, c = 16 * ct + lr;
+        splitb(du[i], sUh[r * LO + c], sUl[r * LO + c]);
       }
-#pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8_t ah = frag_col(sMh, LT, 32 * s, 16 * w), al = frag_col(sMl, LT, 32 * s, 16 * w);
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          du[nt] = mfma3(ah, al, frag_col(sOh, LO, 32 * s, 16 * nt), frag_col(sOl, LO, 32 * s, 16 * nt), du[nt]);
-      }
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + 4 * lg + i, c = 16 * nt + lr;
-          splitb(du[nt][i], sUh[r * LO + c], sUl[r * LO + c]);
-        }
     }
     sync_lds();
     // dX = A~^T dU
     {
-      f32x4 dx[2] = {zero4(), zero4()};
+      f32x4 dx = zero4();
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8_t ah = frag_col(sAh, LT, 32 * s, 16 * w), al = frag_col(sAl, LT, 32 * s, 16 * w);
+      for (int s = 0; s < 2; ++s)
+        dx = mfma3(frag_col(sAh, LT, 32 * s, 16 * rt), frag_col(sAl, LT, 32 * s, 16 * rt),
+                   frag_col(sUh, LO, 32 * s, 16 * ct), frag_col(sUl, LO, 32 * s, 16 * ct), dx);
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-          dx[nt] = mfma3(ah, al, frag_col(sUh, LO, 32 * s, 16 * nt), frag_col(sUl, LO, 32 * s, 16 * nt), dx[nt]);
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * rt + 4 * lg + i, c = 16 * ct + lr;
+        splitb(dx[i], sXh[r * LO + c], sXl[r * LO + c]);
       }
-#pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + 4 * lg + i, c = 16 * nt + lr;
-          splitb(dx[nt][i], sXh[r * LO + c], sXl[r * LO + c]);
-        }
     }
     sync_lds();
     // Kt over Kh, Qt over the M and A~ halves
 #pragma unroll
     for (int it = 0; it < KP; ++it) {
-      const int r = (tid + 256 * it) / (DK / 8);
+      const int r = (tid + 512 * it) / (DK / 8);
       *reinterpret_cast<bf16x8_t *>(sKh + r * LDK + pcol) = kth[it];
       *reinterpret_cast<bf16x8_t *>(sKl + r * LDK + pcol) = ktl[it];
       *reinterpret_cast<bf16x8_t *>(sQh + r * LDK + pcol) = qth[it];
@@ -555,52 +543,41 @@ __global__ __launch_bounds__(256) void kda_dh_bf16_kernel(BwdParams p) {
     sync_lds();
     // dH = exp(G_C) dH' + Qt^T dOb - Kt^T dX
     {
-      bf16x8_t boh[2][2], bol[2][2], bxh[2][2], bxl[2][2];
+      bf16x8_t boh[2], bol[2], bxh[2], bxl[2];
 #pragma unroll
-      for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          boh[s][nt] = frag_col(sOh, LO, 32 * s, 16 * nt);
-          bol[s][nt] = frag_col(sOl, LO, 32 * s, 16 * nt);
-          bxh[s][nt] = frag_col(sXh, LO, 32 * s, 16 * nt);
-          bxl[s][nt] = frag_col(sXl, LO, 32 * s, 16 * nt);
-        }
+      for (int s = 0; s < 2; ++s) {
+        boh[s] = frag_col(sOh, LO, 32 * s, 16 * ht);
+        bol[s] = frag_col(sOl, LO, 32 * s, 16 * ht);
+        bxh[s] = frag_col(sXh, LO, 32 * s, 16 * ht);
+        bxl[s] = frag_col(sXl, LO, 32 * s, 16 * ht);
+      }
 #pragma unroll
       for (int tt = 0; tt < DK / 64; ++tt) {
-        const int t = w + 4 * tt;
-        f32x4 acc[2], ky[2] = {zero4(), zero4()};
+        const int t = (w >> 1) + 4 * tt;
+        f32x4 acc, ky = zero4();
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 16 * t + 4 * lg + i;
-            acc[nt][i] = sGC[row] * sD[row * LC + 16 * nt + lr];
-          }
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          const bf16x8_t qh = frag_col(sQh, LDK, 32 * s, 16 * t), ql = frag_col(sQl, LDK, 32 * s, 16 * t);
-          const bf16x8_t kh = frag_col(sKh, LDK, 32 * s, 16 * t), kl = frag_col(sKl, LDK, 32 * s, 16 * t);
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            acc[nt] = mfma3(qh, ql, boh[s][nt], bol[s][nt], acc[nt]);
-            ky[nt] = mfma3(kh, kl, bxh[s][nt], bxl[s][nt], ky[nt]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * t + 4 * lg + i;
+          acc[i] = sGC[row] * sD[row * LC + 16 * ht + lr];
         }
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt)
+        for (int s = 0; s < 2; ++s) {
+          acc = mfma3(frag_col(sQh, LDK, 32 * s, 16 * t), frag_col(sQl, LDK, 32 * s, 16 * t), boh[s], bol[s], acc);
+          ky = mfma3(frag_col(sKh, LDK, 32 * s, 16 * t), frag_col(sKl, LDK, 32 * s, 16 * t), bxh[s], bxl[s], ky);
+        }
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int row = 16 * t + 4 * lg + i, c = 16 * nt + lr;
-            const float v = acc[nt][i] - ky[nt][i];
-            sD[row * LC + c] = v;
-            splitb(v, sDh[row * LO + c], sDl[row * LO + c]);
-          }
+        for (int i = 0; i < 4; ++i) {
+          const int row = 16 * t + 4 * lg + i, c = 16 * ht + lr;
+          const float v = acc[i] - ky[i];
+          sD[row * LC + c] = v;
+          splitb(v, sDh[row * LO + c], sDl[row * LO + c]);
+        }
       }
     }
   }
   sync_lds();
   if (p.dh0)
-    for (int idx = tid; idx < DK * 32; idx += 256) {
+    for (int idx = tid; idx < DK * 32; idx += 512) {
       const int i = idx / 32, c = idx % 32;
       p.dh0[sb + (size_t)i * DV + c0 + c] = sD[i * LC + c];
     }
@@ -988,7 +965,7 @@ hipError_t launch_all(const BwdParams &p, hipStream_t st) {
   hipLaunchKernelGGL((kda_prep_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   if constexpr (std::is_same_v<In, bf16>)
-    hipLaunchKernelGGL((kda_dh_bf16_kernel<DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((kda_dh_bf16_kernel<DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(512), 0, st, p);
   else
     hipLaunchKernelGGL((kda_dh_kernel<In, DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
