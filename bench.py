@@ -398,7 +398,8 @@ def bench_bwd(args, torch, la, synth, dev):
     and final for KDA) on the workload's inputs; HIP events around the calls,
     then a graph of one call replayed.  GDN's bf16 path runs on bf16 MFMA
     (operands split into bf16 high and low halves) and is priced against the
-    bf16 peak; KDA's runs on fp32 MFMA and is priced against the fp32 peak."""
+    bf16 peak; KDA's prep, part and final run on fp32 MFMA (its dh on split
+    bf16) and the call is priced against the fp32 peak."""
     cfg, kda, desc = WORKLOADS[args.workload]
     kda = bool(kda)
     inp = synth.config(cfg)
@@ -464,7 +465,8 @@ def bench_bwd(args, torch, la, synth, dev):
         "value": round(T * args.steps / elapsed, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": ("bf16 inputs; fp32 MFMA and VALU" if kda else
+        "dtype": ("bf16 inputs; dh on bf16 MFMA with split operands, prep/part/final on fp32 "
+                  "MFMA and VALU" if kda else
                   "bf16 inputs; bf16 MFMA on split operands, fp32 accumulation"),
         "data": "synthetic (seeded, resident in HBM)",
         "config": {"workload": desc, "mode": "graph-replay of one backward call",
