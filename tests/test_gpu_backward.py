@@ -171,3 +171,44 @@ def test_backward_grouped_value_heads(kda, H_qk):
     errs = compare(small, got, ref)
     _say(f"bwd gva kda={kda} H_qk={H_qk}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     assert all(v <= TOL["bf16"] for v in errs.values()), errs
+
+
+@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
+@pytest.mark.parametrize("dscale", [1e-6, 1e5])
+def test_backward_gradient_scale(kda, dscale):
+    """The bf16 path splits every non-key operand into bf16 high and low
+    halves, which keep fp32's exponent range: a loss scaled by 1e-6 (a mean
+    over many tokens) or 1e5 (loss scaling) must keep the same relative
+    accuracy.  The oracle's gradients are linear in (dout, dht)."""
+    inp = make_inputs(SMALL_CU[-1], 2, 128, 128, kda=kda, dtype="bf16", seed=770,
+                      cu_seqlens=SMALL_CU, h0_std=0.1)
+    rng = np.random.default_rng(771)
+    do = rng.standard_normal(inp["v"].shape) * dscale
+    dht = rng.standard_normal(inp["h0"].shape) * dscale
+    ref = gated_delta_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], SMALL_CU,
+                          inp["h0"], do, dht, 1.0, kda=kda)
+    got = run_bwd(inp, do.astype(np.float32), dht.astype(np.float32), 1.0)
+    errs = compare(inp, got, ref)
+    _say(f"bwd scale {dscale:g} kda={kda}: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL["bf16"] for v in errs.values()), errs
+
+
+def test_backward_kda_strong_decay():
+    """KDA gates of -2 .. -6 per token and channel: the cumulative gate falls
+    by up to ~380 over a chunk, so exp(-G) overflows fp32.  The block
+    factorisation keeps every exponential factor at most one; the gradients
+    must stay finite and match the oracle."""
+    inp = make_inputs(SMALL_CU[-1], 2, 64, 64, kda=True, dtype="bf16", seed=780,
+                      cu_seqlens=SMALL_CU, h0_std=0.1)
+    rng = np.random.default_rng(781)
+    inp["g"] = (-rng.uniform(2.0, 6.0, size=inp["g"].shape)).astype(np.float32)
+    do = rng.standard_normal(inp["v"].shape).astype(np.float32)
+    dht = rng.standard_normal(inp["h0"].shape).astype(np.float32)
+    ref = gated_delta_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], SMALL_CU,
+                          inp["h0"], do, dht, 1.0, kda=True)
+    got = run_bwd(inp, do, dht, 1.0)
+    for key in ("dq", "dk", "dv", "dg", "dbeta"):
+        assert bool(torch.isfinite(got[key][:SMALL_CU[-1]]).all()), key
+    errs = compare(inp, got, ref)
+    _say("bwd kda strong decay: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL["bf16"] for v in errs.values()), errs
