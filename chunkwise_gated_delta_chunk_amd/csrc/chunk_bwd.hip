@@ -1220,18 +1220,23 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
 }
 
 template <typename In, int DK>
-hipError_t launch_all(const BwdParams &p, hipStream_t st) {
+hipError_t launch_all(const BwdParams &p, int stage, hipStream_t st) {
   const int cells = p.NT * p.H;
-  if constexpr (std::is_same_v<In, bf16>)
-    hipLaunchKernelGGL((bwd_prep_bf16_kernel<DK>), dim3(cells), dim3(256), 0, st, p);
-  else
-    hipLaunchKernelGGL((bwd_prep_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  if constexpr (std::is_same_v<In, bf16>)
-    hipLaunchKernelGGL((bwd_dh_bf16_kernel<DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(512), 0, st, p);
-  else
-    hipLaunchKernelGGL((bwd_dh_kernel<In, DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  if (stage == 1) {  // prep: needs no forward recompute
+    if constexpr (std::is_same_v<In, bf16>)
+      hipLaunchKernelGGL((bwd_prep_bf16_kernel<DK>), dim3(cells), dim3(256), 0, st, p);
+    else
+      hipLaunchKernelGGL((bwd_prep_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
+    return hipGetLastError();
+  }
+  if (stage == 2) {  // the reverse pass: needs prep only
+    if constexpr (std::is_same_v<In, bf16>)
+      hipLaunchKernelGGL((bwd_dh_bf16_kernel<DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(512), 0, st, p);
+    else
+      hipLaunchKernelGGL((bwd_dh_kernel<In, DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
+    return hipGetLastError();
+  }
+  // the per-chunk stage: needs the recomputed states and the reverse pass
   if constexpr (std::is_same_v<In, bf16>) {
     hipLaunchKernelGGL((bwd_cell_bf16_kernel<DK>), dim3(cells), dim3(256), 0, st, p);
   } else {
@@ -1243,9 +1248,9 @@ hipError_t launch_all(const BwdParams &p, hipStream_t st) {
 }
 
 template <typename In>
-hipError_t launch_dk(const BwdParams &p, int dk, hipStream_t st) {
-  if (dk == 128) return launch_all<In, 128>(p, st);
-  if (dk == 64) return launch_all<In, 64>(p, st);
+hipError_t launch_dk(const BwdParams &p, int dk, int stage, hipStream_t st) {
+  if (dk == 128) return launch_all<In, 128>(p, stage, st);
+  if (dk == 64) return launch_all<In, 64>(p, stage, st);
   return hipErrorInvalidValue;
 }
 
@@ -1280,10 +1285,10 @@ hipError_t launch_group_sum(const float *full, float *out, int T_max, int H, int
   return hipGetLastError();
 }
 
-hipError_t launch_chunk_bwd(const BwdParams &p, int dt, int dk, hipStream_t st) {
-  if (dt == LA_BF16) return launch_dk<bf16>(p, dk, st);
-  if (dt == LA_F16) return launch_dk<f16>(p, dk, st);
-  if (dt == LA_F32) return dk == 64 ? launch_all<float, 64>(p, st) : hipErrorInvalidValue;
+hipError_t launch_chunk_bwd(const BwdParams &p, int dt, int dk, int stage, hipStream_t st) {
+  if (dt == LA_BF16) return launch_dk<bf16>(p, dk, stage, st);
+  if (dt == LA_F16) return launch_dk<f16>(p, dk, stage, st);
+  if (dt == LA_F32) return dk == 64 ? launch_all<float, 64>(p, stage, st) : hipErrorInvalidValue;
   return hipErrorInvalidValue;
 }
 

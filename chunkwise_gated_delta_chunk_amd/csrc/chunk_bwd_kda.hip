@@ -960,15 +960,19 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
 }
 
 template <typename In, int DK>
-hipError_t launch_all(const BwdParams &p, hipStream_t st) {
+hipError_t launch_all(const BwdParams &p, int stage, hipStream_t st) {
   const int cells = p.NT * p.H;
-  hipLaunchKernelGGL((kda_prep_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-  if constexpr (std::is_same_v<In, bf16>)
-    hipLaunchKernelGGL((kda_dh_bf16_kernel<DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(512), 0, st, p);
-  else
-    hipLaunchKernelGGL((kda_dh_kernel<In, DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
-  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  if (stage == 1) {  // prep: needs no forward recompute
+    hipLaunchKernelGGL((kda_prep_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
+    return hipGetLastError();
+  }
+  if (stage == 2) {  // the reverse pass: needs prep only
+    if constexpr (std::is_same_v<In, bf16>)
+      hipLaunchKernelGGL((kda_dh_bf16_kernel<DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(512), 0, st, p);
+    else
+      hipLaunchKernelGGL((kda_dh_kernel<In, DK>), dim3(p.N_max * p.H * (DK / 32)), dim3(256), 0, st, p);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((kda_part_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   hipLaunchKernelGGL((kda_final_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
@@ -976,18 +980,18 @@ hipError_t launch_all(const BwdParams &p, hipStream_t st) {
 }
 
 template <typename In>
-hipError_t launch_dk(const BwdParams &p, int dk, hipStream_t st) {
-  if (dk == 128) return launch_all<In, 128>(p, st);
-  if (dk == 64) return launch_all<In, 64>(p, st);
+hipError_t launch_dk(const BwdParams &p, int dk, int stage, hipStream_t st) {
+  if (dk == 128) return launch_all<In, 128>(p, stage, st);
+  if (dk == 64) return launch_all<In, 64>(p, stage, st);
   return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-hipError_t launch_chunk_bwd_kda(const BwdParams &p, int dt, int dk, hipStream_t st) {
-  if (dt == LA_BF16) return launch_dk<bf16>(p, dk, st);
-  if (dt == LA_F16) return launch_dk<f16>(p, dk, st);
-  if (dt == LA_F32) return dk == 64 ? launch_all<float, 64>(p, st) : hipErrorInvalidValue;
+hipError_t launch_chunk_bwd_kda(const BwdParams &p, int dt, int dk, int stage, hipStream_t st) {
+  if (dt == LA_BF16) return launch_dk<bf16>(p, dk, stage, st);
+  if (dt == LA_F16) return launch_dk<f16>(p, dk, stage, st);
+  if (dt == LA_F32) return dk == 64 ? launch_all<float, 64>(p, stage, st) : hipErrorInvalidValue;
   return hipErrorInvalidValue;
 }
 

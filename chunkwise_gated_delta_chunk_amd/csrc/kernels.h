@@ -128,8 +128,11 @@ hipError_t launch_chunk_reduce(const ReduceParams &p, bool kda, int dt, int dk, 
                                hipStream_t st);
 hipError_t launch_chunk_combine(const CombineParams &p, int dk, hipStream_t st);
 hipError_t launch_recurrent(const RecurrentParams &p, bool kda, int dt, int dk, hipStream_t st);
-hipError_t launch_chunk_bwd(const BwdParams &p, int dt, int dk, hipStream_t st);
-hipError_t launch_chunk_bwd_kda(const BwdParams &p, int dt, int dk, hipStream_t st);
+// stage 1: prep; stage 2: the reverse pass (both need only q, k, g, beta,
+// dout and dht); stage 3: the per-chunk kernels, after stage 2 and the
+// forward recompute
+hipError_t launch_chunk_bwd(const BwdParams &p, int dt, int dk, int stage, hipStream_t st);
+hipError_t launch_chunk_bwd_kda(const BwdParams &p, int dt, int dk, int stage, hipStream_t st);
 // grouped value heads: out[t][hq] = sum of full[t][h] over the value heads h
 // of group hq, rows of real tokens only
 hipError_t launch_group_sum(const float *full, float *out, int T_max, int H, int Hqk, int d,

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace {
@@ -433,6 +435,39 @@ size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *a, int is_kda) {
   return bwd_layout(a, is_kda != 0).total;
 }
 
+// The backward's reverse pass needs only the inputs and the prep, so it runs
+// on a side stream of the device while the caller's stream recomputes the
+// forward; the caller's stream waits for both before the per-chunk stage.
+// One side stream and two events per device, created on first use (default
+// priority); the mutex keeps concurrent calls' record/wait pairs apart.  If
+// they cannot be created, everything runs in order on the caller's stream.
+namespace {
+struct Side {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+  bool tried = false;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mu;
+Side g_side[kMaxDevices];
+
+Side *side_stream() {  // caller holds g_side_mu
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  Side &sd = g_side[dev];
+  if (!sd.tried) {
+    sd.tried = true;
+    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess ||
+        hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) {
+      sd.s = nullptr;
+      (void)hipGetLastError();
+    }
+  }
+  return sd.s ? &sd : nullptr;
+}
+}  // namespace
+
 static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
   if (!a) return LA_ERR_NULL;
   const int sc = check_bwd(a);
@@ -457,49 +492,7 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
   f.chunk_offsets = a->chunk_offsets;
   Meta meta;
   if (kernel_meta(&f, ws + L.meta, st, meta) != hipSuccess) return LA_ERR_HIP;
-  f.q = a->q;
-  f.k = a->k;
-  f.v = a->v;
-  f.g = a->g;
-  f.beta = a->beta;
-  f.cu_seqlens = a->cu_seqlens;
-  f.chunk_indices = a->chunk_indices;
-  f.chunk_offsets = a->chunk_offsets;
-  f.h0 = a->h0;
-  f.workspace = ws;
-  f.workspace_bytes = L.hs;
   const int NT = (int)la_nt_max(a->T_max, a->N_max, kBTk);
-  {
-    la::MapParams mp{};
-    mp.q = a->q;
-    mp.k = a->k;
-    mp.g = a->g;
-    mp.beta = a->beta;
-    mp.cu_seqlens = a->cu_seqlens;
-    mp.cu64 = a->cu_seqlens_i64;
-    mp.chunk_indices = meta.ci;
-    mp.H = a->H;
-    mp.Hqk = a->H_qk ? a->H_qk : a->H;
-    mp.NT_max = NT;
-    mp.img = ws;
-    if (la::launch_chunk_map(mp, kda, a->qkv_dtype, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
-    la::ReduceParams rp{};
-    rp.v = a->v;
-    rp.cu_seqlens = a->cu_seqlens;
-    rp.cu64 = a->cu_seqlens_i64;
-    rp.chunk_offsets = meta.co;
-    rp.h0 = a->h0;
-    rp.o = nullptr;
-    rp.ht = nullptr;
-    rp.img = ws;
-    rp.H = a->H;
-    rp.N_max = a->N_max;
-    rp.S = split_for(&f);
-    rp.scale = a->scale;
-    rp.hsave = reinterpret_cast<float *>(ws + L.hs);
-    if (la::launch_chunk_reduce(rp, kda, a->qkv_dtype, a->d_k, a->d_v / rp.S, st) != hipSuccess)
-      return LA_ERR_HIP;
-  }
   la::BwdParams bp{};
   bp.q = a->q;
   bp.k = a->k;
@@ -533,9 +526,69 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
   bp.N_max = a->N_max;
   bp.NT = NT;
   bp.scale = a->scale;
-  const hipError_t e = kda ? la::launch_chunk_bwd_kda(bp, a->qkv_dtype, a->d_k, st)
-                          : la::launch_chunk_bwd(bp, a->qkv_dtype, a->d_k, st);
-  if (e != hipSuccess) return LA_ERR_HIP;
+  const auto stage = [&](int k, hipStream_t sk) {
+    return kda ? la::launch_chunk_bwd_kda(bp, a->qkv_dtype, a->d_k, k, sk)
+               : la::launch_chunk_bwd(bp, a->qkv_dtype, a->d_k, k, sk);
+  };
+  // prep first (the reverse pass needs it), then the reverse pass on the
+  // side stream while this stream recomputes the forward
+  if (stage(1, st) != hipSuccess) return LA_ERR_HIP;
+  {
+    std::lock_guard<std::mutex> lk(g_side_mu);
+    Side *sd = side_stream();
+    hipStream_t s1 = st;
+    if (sd) {
+      if (hipEventRecord(sd->fork, st) != hipSuccess || hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
+        return LA_ERR_HIP;
+      s1 = sd->s;
+    }
+    if (stage(2, s1) != hipSuccess) return LA_ERR_HIP;
+    f.q = a->q;
+    f.k = a->k;
+    f.v = a->v;
+    f.g = a->g;
+    f.beta = a->beta;
+    f.cu_seqlens = a->cu_seqlens;
+    f.chunk_indices = a->chunk_indices;
+    f.chunk_offsets = a->chunk_offsets;
+    f.h0 = a->h0;
+    f.workspace = ws;
+    f.workspace_bytes = L.hs;
+    {
+      la::MapParams mp{};
+      mp.q = a->q;
+      mp.k = a->k;
+      mp.g = a->g;
+      mp.beta = a->beta;
+      mp.cu_seqlens = a->cu_seqlens;
+      mp.cu64 = a->cu_seqlens_i64;
+      mp.chunk_indices = meta.ci;
+      mp.H = a->H;
+      mp.Hqk = a->H_qk ? a->H_qk : a->H;
+      mp.NT_max = NT;
+      mp.img = ws;
+      if (la::launch_chunk_map(mp, kda, a->qkv_dtype, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
+      la::ReduceParams rp{};
+      rp.v = a->v;
+      rp.cu_seqlens = a->cu_seqlens;
+      rp.cu64 = a->cu_seqlens_i64;
+      rp.chunk_offsets = meta.co;
+      rp.h0 = a->h0;
+      rp.o = nullptr;
+      rp.ht = nullptr;
+      rp.img = ws;
+      rp.H = a->H;
+      rp.N_max = a->N_max;
+      rp.S = split_for(&f);
+      rp.scale = a->scale;
+      rp.hsave = reinterpret_cast<float *>(ws + L.hs);
+      if (la::launch_chunk_reduce(rp, kda, a->qkv_dtype, a->d_k, a->d_v / rp.S, st) != hipSuccess)
+        return LA_ERR_HIP;
+    }
+    if (sd && (hipEventRecord(sd->join, s1) != hipSuccess || hipStreamWaitEvent(st, sd->join, 0) != hipSuccess))
+      return LA_ERR_HIP;
+  }
+  if (stage(3, st) != hipSuccess) return LA_ERR_HIP;
   if (grouped) {
     if (la::launch_group_sum(dq_full, a->dq, a->T_max, a->H, Hqk, a->d_k, a->cu_seqlens,
                              a->cu_seqlens_i64, a->N_max, meta.co, st) != hipSuccess ||

@@ -288,15 +288,23 @@ size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *shape, int is_kda);
  * of gdn_chunk_fwd / kda_chunk_fwd with the same inputs, for q, k, v, g, beta
  * and h0 (FLA RFC,
  * sections "Scope" and "Step 3": the backward of the chunk path).  It
- * recomputes the forward's per-chunk states (map, then the reduce storing the
- * state entering each chunk), then runs four launches: a chunk-parallel prep
- * (A^-1, M, S, gates), a reverse pass over each sequence's chunks for the
- * state gradient (writing dh0), a chunk-parallel pass for dv and the
- * d_v-contracted products, and a chunk-parallel pass for dq, dk, dg, dbeta.
- * Arithmetic after the recompute is fp32.  Rows outside every sequence,
- * sentinel slots and dh0 of zero-length sequences are not written.  With
- * grouped value heads each value head's dq, dk go to the workspace and one
- * more launch sums every group into dq, dk.
+ * runs a chunk-parallel prep (A^-1, M, S, gates), then a reverse pass over
+ * each sequence's chunks for the state gradient (writing dh0) while the
+ * forward's per-chunk states are recomputed (map, then the reduce storing the
+ * state entering each chunk), then chunk-parallel passes for dv and the
+ * d_v-contracted products and for dq, dk, dg, dbeta (one fused kernel for
+ * bf16 inputs).  bf16 inputs run on bf16 MFMA with operands split into bf16
+ * high and low halves (about 17 significant bits, fp32 exponent range); fp16
+ * and fp32 inputs on fp32 MFMA; accumulation is fp32.  Rows outside every
+ * sequence, sentinel slots and dh0 of zero-length sequences are not written.
+ * With grouped value heads each value head's dq, dk go to the workspace and
+ * one more launch sums every group into dq, dk.
+ * Streams: everything is ordered after the work already queued on `stream`,
+ * and work queued on `stream` afterwards sees every output.  The reverse pass
+ * runs on a library-owned stream of the current device (created on first
+ * use, default priority), forked from and joined back to `stream` through
+ * events; capturing `stream` into a HIP graph captures both.  The call
+ * allocates no device memory.
  * Host errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_UNSUPPORTED,
  * LA_ERR_WORKSPACE, LA_ERR_HIP.
  */
