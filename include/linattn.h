@@ -303,8 +303,9 @@ size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *shape, int is_kda);
  * and work queued on `stream` afterwards sees every output.  The reverse pass
  * runs on a library-owned stream of the current device (created on first
  * use, default priority), forked from and joined back to `stream` through
- * events; capturing `stream` into a HIP graph captures both.  The call
- * allocates no device memory.
+ * events; capturing `stream` into a HIP graph captures both.  Apart from
+ * creating that stream and its two events on the first call on a device, the
+ * call allocates nothing (all scratch is the caller's workspace).
  * Host errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_UNSUPPORTED,
  * LA_ERR_WORKSPACE, LA_ERR_HIP.
  */
