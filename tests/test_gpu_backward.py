@@ -212,3 +212,58 @@ def test_backward_kda_strong_decay():
     errs = compare(inp, got, ref)
     _say("bwd kda strong decay: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
     assert all(v <= TOL["bf16"] for v in errs.values()), errs
+
+
+def test_backward_concurrent_streams_match_sequential():
+    """Two host threads issue backward calls on two streams at once (the
+    library forks each call's reverse pass onto its own side stream and joins
+    it back with events): every output must equal the same call run alone."""
+    import threading
+    cases = []
+    for seed in (790, 791):
+        inp = make_inputs(SMALL_CU[-1], 2, 64, 64, kda=False, dtype="bf16", seed=seed,
+                          cu_seqlens=SMALL_CU, h0_std=0.1)
+        rng = np.random.default_rng(seed + 1)
+        do = rng.standard_normal(inp["v"].shape).astype(np.float32)
+        dht = rng.standard_normal(inp["h0"].shape).astype(np.float32)
+        cases.append((inp, do, dht))
+    alone = [run_bwd(inp, do, dht, 1.0) for inp, do, dht in cases]
+
+    def prepared(inp, do, dht):
+        d = {x: torch.from_numpy(inp[x]).cuda().to(torch.bfloat16).contiguous() for x in ("q", "k", "v")}
+        cu = torch.tensor(SMALL_CU, dtype=torch.int32, device="cuda")
+        ci, co, _ = la.build_chunk_meta(cu, inp["q"].shape[0])
+        return dict(q=d["q"], k=d["k"], v=d["v"], g=torch.from_numpy(inp["g"]).cuda(),
+                    beta=torch.from_numpy(inp["beta"]).cuda(), cu=cu, ci=ci, co=co,
+                    h0=torch.from_numpy(inp["h0"]).cuda(), do=torch.from_numpy(do).cuda(),
+                    dht=torch.from_numpy(dht).cuda())
+
+    args = [prepared(*c) for c in cases]
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    results = [[None] * 4, [None] * 4]
+    start = threading.Barrier(2)
+
+    def worker(i):
+        a = args[i]
+        start.wait()
+        with torch.cuda.stream(streams[i]):
+            for rep in range(4):
+                results[i][rep] = la.gdn_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"],
+                                                   a["ci"], a["co"], a["do"], h0=a["h0"], dht=a["dht"],
+                                                   scale=1.0)
+        streams[i].synchronize()
+
+    threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    ne = torch.from_numpy(np.diff(np.asarray(SMALL_CU)) > 0)
+    for i in range(2):
+        for rep in range(4):
+            got = dict(zip(("dq", "dk", "dv", "dg", "dbeta", "dh0"), results[i][rep]))
+            for key in ("dq", "dk", "dv", "dg", "dbeta"):
+                assert torch.equal(got[key][:SMALL_CU[-1]], alone[i][key][:SMALL_CU[-1]]), (i, rep, key)
+            assert torch.equal(got["dh0"][ne], alone[i]["dh0"][ne]), (i, rep)
