@@ -18,8 +18,13 @@
 //   dG = gam q P1 - gam k P2 - Kh P3 + q F1 - k F2 + k F3 - k F4,
 //        plus, on the last row, sum_r Kh P3 and exp(G_C) <dH', H> per channel
 // and dg the reverse cumulative sum of dG over the chunk's rows, per channel.
-// The E-weighted sums run as direct loops (exp(G_r - G_s) <= 1 for s <= r);
-// the rest on fp32 MFMA, as for GDN.
+// S, M (prep) and the E-weighted sums (final) go by 16-row blocks: inside a
+// diagonal block as direct loops (exp(G_r - G_s) <= 1 for s <= r); across
+// blocks R > S' the decay factorises through the last row b of S',
+// exp(G_r - G_s) = exp(G_r - G_b) exp(G_b - G_s), both factors at most one
+// for a decay (g <= 0), and those tiles run on fp32 MFMA.  The reverse pass
+// runs for bf16 inputs on bf16 MFMA with split operands (as for GDN), for
+// fp16 and fp32 inputs on fp32 MFMA; prep, part and final on fp32 MFMA.
 #include "bwd_common.h"
 
 namespace la {
