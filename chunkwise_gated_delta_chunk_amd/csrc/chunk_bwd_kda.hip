@@ -737,7 +737,7 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
   constexpr int KQG = 3 * kBT * LK;
   constexpr int AREA = KQG > 4 * MAT ? KQG : 4 * MAT;
   __shared__ __attribute__((aligned(16))) float smem[AREA + 2 * MAT];
-  __shared__ __attribute__((aligned(16))) float sBeta[64], bt[64], ba[64];
+  __shared__ __attribute__((aligned(16))) float sBeta[64], bt[64], ba[64], sEx[256], sTot[256];
   float *sK = smem, *sQ = smem + kBT * LK, *sG = smem + 2 * kBT * LK;
   float *sDM = smem + AREA, *sDS = smem + AREA + MAT;
   float *sA = smem, *sS = smem + MAT, *sTmp = smem + 2 * MAT, *sDAi = smem + 3 * MAT;
@@ -905,7 +905,8 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
     }
     // every value is read before any is written: the three outputs may
     // alias as far as the compiler knows, so interleaved read-modify-writes
-    // would each wait for the previous one
+    // would each wait for the previous one.  The complete dG goes to LDS
+    // (over dM and dS, read by now) for the scan below.
     f32x4 oq[DK / 16], ok[DK / 16], og[DK / 16];
 #pragma unroll
     for (int t = 0; t < DK / 16; ++t)
@@ -920,6 +921,8 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
           og[t][ii] = p.dg[o];
         }
       }
+    __syncthreads();  // every wave is done reading dM and dS
+    float *dGs = sDM;  // [64][DK], over dM and dS
 #pragma unroll
     for (int t = 0; t < DK / 16; ++t) {
       const int i = 16 * t + j;
@@ -933,33 +936,47 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
         const size_t o = ((size_t)(r0 + x) * H + h) * DK + i;
         p.dq[o] = oq[t][ii] + f1;
         p.dk[o] = ok[t][ii] + f3 + f24;
-        p.dg[o] = og[t][ii] + qx * f1 + kx * (f3 - f24);
+        dGs[x * DK + i] = og[t][ii] + qx * f1 + kx * (f3 - f24);
       }
     }
   }
+  static_assert(64 * DK <= 2 * MAT, "dG fits over dM and dS");
   __syncthreads();  // every row's dG is complete
   // per channel: the last-row terms (sum_r Kh P3 and exp(G_C) <dH', H>)
   // belong to G_{C-1}, which every row's cumulative sum includes; then dg is
-  // the reverse cumulative sum down the rows
-  // (every row of the channel is read before any is written, so the 64
-  // reads are in flight together rather than one round trip per row)
-  for (int i = tid; i < DK; i += 256) {
+  // the reverse cumulative sum down the rows.  NQ threads per channel take
+  // RP rows each; their partial sums meet in a small table.
+  {
+    constexpr int NQ = 256 / DK, RP = 64 / NQ;
+    const float *dGs = sDM;
+    const int i = tid % DK, part = tid / DK, x0 = part * RP;
     const float GCi = sG[(C - 1) * LK + i];
-    float extra = __expf(GCi) * shv[i];
-    float dgx[kBT];
+    float ex = part == 0 ? __expf(GCi) * shv[i] : 0.f;
+    float loc[RP], tot = 0.f;
 #pragma unroll
-    for (int x = 0; x < kBT; ++x) {
-      dgx[x] = 0.f;
+    for (int e = RP - 1; e >= 0; --e) {
+      const int x = x0 + e;
+      float v = 0.f;
       if (x < C) {
-        extra += __expf(GCi - sG[x * LK + i]) * sK[x * LK + i] * P3[x * DK + i];
-        dgx[x] = p.dg[((size_t)(r0 + x) * H + h) * DK + i];
+        v = dGs[x * DK + i];
+        ex += __expf(GCi - sG[x * LK + i]) * sK[x * LK + i] * P3[x * DK + i];
       }
+      tot += v;
+      loc[e] = tot;  // sum of this part's rows x .. x0 + RP - 1
     }
-    float run = extra;
+    sEx[tid] = ex;
+    sTot[tid] = tot;
+    __syncthreads();
+    float exT = 0.f, above = 0.f;
 #pragma unroll
-    for (int x = kBT - 1; x >= 0; --x) {
-      run += dgx[x];
-      if (x < C) p.dg[((size_t)(r0 + x) * H + h) * DK + i] = run;
+    for (int q = 0; q < NQ; ++q) {
+      exT += sEx[q * DK + i];
+      if (q > part) above += sTot[q * DK + i];
+    }
+#pragma unroll
+    for (int e = 0; e < RP; ++e) {
+      const int x = x0 + e;
+      if (x < C) p.dg[((size_t)(r0 + x) * H + h) * DK + i] = loc[e] + above + exT;
     }
   }
 }
