@@ -147,9 +147,7 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_bf16_kernel(BwdParams p) {
       const float Sv = s < r ? aS[s4][i] * e : 0.f;
       const float Mv = aM[s4][i] * e;
       sS[r * kL + s] = Sv;
-      img[kPrepS + r * 64 + s] = Sv;
-      img[kPrepM + r * 64 + s] = Mv;
-      splitb(Mv, imh[r * 64 + s], imh[4096 + r * 64 + s]);
+      splitb(Mv, imh[r * 64 + s], imh[4096 + r * 64 + s]);  // (no fp32 S, M: see the fused kernel)
     }
   }
   __syncthreads();
@@ -999,19 +997,23 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
   }
 
   // ---- phase 2
-  float fa[16], fam[4][4], fmm[4][4], fS[4][4], fvec = 0.f;
+  // M at this lane's tile positions from its halves, still in LDS (the prep
+  // writes no fp32 M or S for bf16 inputs; S is recomputed below)
+  float fa[16], fam[4][4], fmm[4][4], fvec = 0.f;
   u32x4 rq[KP];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int o = (16 * w + 4 * lg + i) * LT + 16 * t + lr;
+      fmm[t][i] = (float)sMh[o] + (float)sMl[o];
+    }
 #pragma unroll
   for (int e = 0; e < 16; ++e) fa[e] = img[kPrepA + tid + 256 * e];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int o = (16 * w + 4 * lg + i) * 64 + 16 * t + lr;
-      fam[t][i] = img[kPrepA + o];
-      fmm[t][i] = img[kPrepM + o];
-      fS[t][i] = img[kPrepS + o];
-    }
+    for (int i = 0; i < 4; ++i) fam[t][i] = img[kPrepA + (16 * w + 4 * lg + i) * 64 + 16 * t + lr];
 #pragma unroll
   for (int it = 0; it < KP; ++it) {
     const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
@@ -1089,8 +1091,16 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
   }
   sync_lds();
   // dA = -A^-T tmp; strict lower part: W = dA S (beta), Y = beta dA S
-  // (gates), F = beta dA E (keys), stored as F + F^T over dT'
+  // (gates), F = beta dA E (keys), stored as F + F^T over dT'.  S = K K^T * E
+  // is recomputed here: K is exact in bf16 and still in LDS.
   {
+    f32x4 kk[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      const bf16x8_t a = frag_row(sK, LDK, 16 * w + lr, 32 * s);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) kk[t] = mfma_bf(a, frag_row(sK, LDK, 16 * t + lr, 32 * s), kk[t]);
+    }
     f32x4 t3[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
@@ -1109,7 +1119,7 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
         const int r = 16 * w + 4 * lg + i;
         const bool sl = s < r && r < C;
         const float dA = -t3[t][i];
-        const float Wv = sl ? dA * fS[t][i] : 0.f;
+        const float Wv = sl ? dA * kk[t][i] * __expf(sG[r] - sG[s]) : 0.f;
         const float Yv = sBeta[r] * Wv;
         const float Fv = sl ? sBeta[r] * dA * __expf(sG[r] - sG[s]) : 0.f;
         wr[i] += Wv;
