@@ -278,7 +278,8 @@ typedef struct {
  * H, d_k, d_v, BT, qkv_dtype read); 0 if the shape is invalid.  It holds the
  * forward recompute's map images, the state entering and the state gradient
  * leaving every chunk ([d_k][d_v] fp32 per chunk slot and head), per-cell
- * fp32 matrices A^-1, M, S (KDA: and the per-channel cumulative gate),
+ * prep images (fp32 A^-1, M, S and gate vectors, KDA also the per-channel
+ * cumulative gate, and bf16 high/low halves of M and A^-1 diag(beta)),
  * per-cell partial products, with BT = 32 the 64-row chunk layout, and with
  * grouped value heads the per-value-head dq, dk ([T_max][H][d_k] fp32 each). */
 size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *shape, int is_kda);
