@@ -255,7 +255,6 @@ __global__ __launch_bounds__(256) void kda_dh_kernel(BwdParams p) {
   float kt[IT][VEC];
   for (int jj = j1 - 1; jj >= j0; --jj) {
     sync_lds();
-    const int r0 = bos + (jj - j0) * kBT, C = min(kBT, eos - r0);
     // Kh = K exp(G_C - G) and Qt = Q exp(G) to LDS; Kt = K exp(G) kept
 #pragma unroll
     for (int it = 0; it < IT; ++it) {
@@ -457,7 +456,6 @@ __global__ __launch_bounds__(512) void kda_dh_bf16_kernel(BwdParams p) {
   bf16x8_t kth[KP], ktl[KP], qth[KP], qtl[KP];  // Kt and Qt halves until the dH step
   for (int jj = j1 - 1; jj >= j0; --jj) {
     sync_lds();
-    const int r0 = bos + (jj - j0) * kBT, C = min(kBT, eos - r0);
 #pragma unroll
     for (int it = 0; it < KP; ++it) {
       const int r = (tid + 512 * it) / (DK / 8);
