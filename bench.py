@@ -700,10 +700,19 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms = elapsed * 1e3 / args.steps
+    # per-replay event pairs on the replay stream, for the p50 / p95 of one step
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
+    for i in range(args.steps):
+        evs[2 * i].record()
+        graph.replay()
+        evs[2 * i + 1].record()
+    torch.cuda.synchronize()
+    rep = np.array([evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(args.steps)])
     graph_eq = bool(torch.equal(o, eager_o) and torch.equal(ht, eager_ht))
 
     tokens = int(inp["cu_seqlens"][-1])
     value = tokens * args.steps / elapsed
+    nt_actual = int(np.ceil(np.diff(np.asarray(inp["cu_seqlens"])) / 64).sum())
 
     kernels = {"meta": t_meta, "map": t_map, "reduce": t_red}
     dom = "reduce" if t_red >= t_map else "map"
@@ -741,6 +750,12 @@ def main():
             "mfma_frac": round(op_flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
         "kernels_ms": {k2: round(v2, 5) for k2, v2 in kernels.items()},
         "eager_ms_per_step": round(eager_ms, 5), "capture_ms": round(capture_ms, 3),
+        "replay_p50_ms": round(float(np.median(rep)), 5),
+        "replay_p95_ms": round(float(np.percentile(rep, 95)), 5),
+        "kernels_per_step": 3 if seg == 0 else 5,
+        "chunk_utilisation": round(nt_actual / NT, 4),
+        "token_utilisation": round(tokens / T, 4),
+        "workspace_bytes": int(ws.numel()),
         "graph_equals_eager": graph_eq,
     }
     if not args.no_cpu_baseline:
