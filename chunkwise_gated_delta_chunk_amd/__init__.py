@@ -4,7 +4,10 @@ prefill forward (GDN and KDA) and its device-side chunk metadata.
 Argument marshalling only: tensors are checked for dtype, device, shape and
 contiguity, their device pointers and the current HIP stream are handed to
 the C ABI (include/linattn.h), and outputs the caller did not provide are
-allocated with torch.  Every step of the computation runs in the library's
+allocated with torch.  The library never writes rows outside every sequence
+nor the final state (or dh0) of a zero-length sequence; outputs the binding
+allocates start at the values those take: zero rows, ht = h0 (or 0), dh0 =
+dht (or 0).  Every step of the computation runs in the library's
 gfx950 kernels; if the library is missing or a call fails, an exception is
 raised -- there is no other path.
 
@@ -25,7 +28,7 @@ __all__ = [
     "LinAttnError", "lib", "nt_max", "build_chunk_meta", "workspace_bytes",
     "gdn_chunk_fwd", "kda_chunk_fwd", "chunk_fwd_stages", "dv_split_for", "seg_len_for",
     "gdn_recurrent_fwd", "kda_recurrent_fwd", "short_conv_fwd", "gdn_chunk_bwd", "kda_chunk_bwd",
-    "bwd_workspace_bytes",
+    "bwd_workspace_bytes", "fork_join_events",
     "STAGE_MAP", "STAGE_REDUCE", "META_BAD_START", "META_NOT_MONOTONE",
     "META_OVER_CAPACITY", "LIB_PATH",
 ]
@@ -98,6 +101,8 @@ class ChunkBwdArgs(ctypes.Structure):
         ("dq", ctypes.c_void_p), ("dk", ctypes.c_void_p), ("dv", ctypes.c_void_p),
         ("dg", ctypes.c_void_p), ("dbeta", ctypes.c_void_p), ("dh0", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("aux_stream", ctypes.c_void_p), ("fork_event", ctypes.c_void_p),
+        ("join_event", ctypes.c_void_p),
     ]
 
 
@@ -268,7 +273,9 @@ def _heads(q, v, what):
 
 def _out(o, o_dtype, shape, dev):
     if o is None:
-        o = torch.empty(shape, dtype=o_dtype or torch.float32, device=dev)
+        # rows outside every sequence are never written by the library: an
+        # output the binding allocates starts at zero there
+        o = torch.zeros(shape, dtype=o_dtype or torch.float32, device=dev)
     if o.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError(f"o must be float32 or bfloat16, got {o.dtype}")
     _need(o, "o", o.dtype, shape, dev)
@@ -276,7 +283,8 @@ def _out(o, o_dtype, shape, dev):
 
 
 def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0, o, ht,
-             output_final_state, workspace, scale, dv_split, seg_len, o_dtype=None, BT=64):
+             output_final_state, workspace, scale, dv_split, seg_len, o_dtype=None, BT=64,
+             static=False):
     _qkv_dtype(q)
     H, H_qk = _heads(q, v, "T_max")
     T_max, _, d_k = q.shape
@@ -297,7 +305,10 @@ def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0
         _need(h0, "h0", torch.float32, st_shape, dev)
     o = _out(o, o_dtype, (T_max, H, d_v), dev)
     if ht is None and output_final_state:
-        ht = torch.empty(st_shape, dtype=torch.float32, device=dev)
+        # the library leaves ht of a zero-length sequence unwritten; a final
+        # state the binding allocates holds that sequence's state, h0 (or 0)
+        ht = h0.clone() if h0 is not None else torch.zeros(st_shape, dtype=torch.float32,
+                                                           device=dev)
     if ht is not None:
         _need(ht, "ht", torch.float32, st_shape, dev)
     a = _shape_args(T_max, N_max, H, d_k, d_v, q.dtype, dv_split, BT=BT, seg_len=seg_len)
@@ -305,9 +316,10 @@ def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0
     a.o_bf16 = int(o.dtype == torch.bfloat16)
     a.cu_seqlens_i64 = int(cu_seqlens.dtype == torch.int64)
     need = int(lib().la_chunk_fwd_workspace_bytes(ctypes.byref(a), int(kda)))
-    if workspace is None:
+    if workspace is None and not static:
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
-    _need(workspace, "workspace", torch.uint8, None, dev)
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, None, dev)
     a.scale = float(scale)
     a.q, a.k, a.v, a.g, a.beta = (t.data_ptr() for t in (q, k, v, g, beta))
     a.cu_seqlens = cu_seqlens.data_ptr()
@@ -316,8 +328,9 @@ def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0
     a.h0 = None if h0 is None else h0.data_ptr()
     a.o = o.data_ptr()
     a.ht = None if ht is None else ht.data_ptr()
-    a.workspace = workspace.data_ptr()
-    a.workspace_bytes = workspace.numel()
+    if workspace is not None:
+        a.workspace = workspace.data_ptr()
+        a.workspace_bytes = workspace.numel()
     return a, o, ht, workspace
 
 
@@ -437,10 +450,12 @@ def short_conv_fwd(x, weight, cu_seqlens, chunk_indices, *, bias=None, residual=
     if h0 is not None:
         _need(h0, "h0", x.dtype, st_shape, dev)
     if y is None:
-        y = torch.empty((T_max, D), dtype=x.dtype, device=dev)
+        # rows outside every sequence are not written: zero there
+        y = torch.zeros((T_max, D), dtype=x.dtype, device=dev)
     _need(y, "y", x.dtype, (T_max, D), dev)
     if ht is None and output_final_state and W > 1:
-        ht = torch.empty(st_shape, dtype=x.dtype, device=dev)
+        # a zero-length sequence's history passes through unchanged
+        ht = h0.clone() if h0 is not None else torch.zeros(st_shape, dtype=x.dtype, device=dev)
     if ht is not None:
         _need(ht, "ht", x.dtype, st_shape, dev)
     a = ShortConvArgs()
@@ -479,7 +494,10 @@ def gdn_chunk_bwd(*args, **kw):
 
     Arguments as gdn_chunk_fwd plus dout [T_max, H, d_v] fp32 (after
     chunk_offsets) and dht; returns (dq, dk, dv, dg, dbeta, dh0) as fp32
-    tensors, dh0 None unless h0 is given or dh0 is passed.
+    tensors, dh0 None unless h0 is given or dh0 is passed.  aux_stream (a
+    torch.cuda.Stream) with events = fork_join_events() runs the reverse pass
+    on that stream beside the forward recompute; the caller keeps the stream
+    and events to itself until the call's work is done.
     """
     return _chunk_bwd(False, *args, **kw)
 
@@ -489,9 +507,32 @@ def kda_chunk_bwd(*args, **kw):
     return _chunk_bwd(True, *args, **kw)
 
 
+def fork_join_events():
+    """Two fresh events (fork, join) for the backward's optional second stream,
+    created on the current device (a record on the current stream makes
+    their handles exist)."""
+    evs = (torch.cuda.Event(), torch.cuda.Event())
+    for e in evs:
+        e.record()
+    return evs
+
+
+def _handle(x, what):
+    if x is None:
+        return None
+    if isinstance(x, torch.cuda.Stream):
+        return x.cuda_stream
+    if isinstance(x, torch.cuda.Event):
+        h = x.cuda_event
+        if not h:
+            raise ValueError(f"{what} has no handle yet (record it once first)")
+        return h
+    return int(x)
+
+
 def _chunk_bwd(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, dout, *, h0=None,
                dht=None, scale=1.0, dq=None, dk=None, dv=None, dg=None, dbeta=None, dh0=None,
-               workspace=None, BT=64, stream=None):
+               workspace=None, BT=64, stream=None, aux_stream=None, events=None):
     _qkv_dtype(q)
     H, H_qk = _heads(q, v, "T_max")
     T_max, _, d_k = q.shape
@@ -517,7 +558,8 @@ def _chunk_bwd(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, 
 
     def out(t, shape, name):
         if t is None:
-            t = torch.empty(shape, dtype=torch.float32, device=dev)
+            # rows outside every sequence are not written: zero gradients
+            t = torch.zeros(shape, dtype=torch.float32, device=dev)
         _need(t, name, torch.float32, shape, dev)
         return t
     dq = out(dq, (T_max, H_qk, d_k), "dq")
@@ -526,7 +568,10 @@ def _chunk_bwd(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, 
     dg = out(dg, g_shape, "dg")
     dbeta = out(dbeta, (T_max, H), "dbeta")
     if dh0 is None and h0 is not None:
-        dh0 = torch.empty(st_shape, dtype=torch.float32, device=dev)
+        # dh0 of a zero-length sequence is not written; its gradient is dht
+        # (the state passes through unchanged), or 0 without dht
+        dh0 = dht.clone() if dht is not None else torch.zeros(st_shape, dtype=torch.float32,
+                                                              device=dev)
     if dh0 is not None:
         _need(dh0, "dh0", torch.float32, st_shape, dev)
     a = _bwd_shape(T_max, N_max, H, d_k, d_v, q.dtype, BT)
@@ -548,6 +593,12 @@ def _chunk_bwd(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, 
     a.dh0 = None if dh0 is None else dh0.data_ptr()
     a.workspace = workspace.data_ptr()
     a.workspace_bytes = workspace.numel()
+    if (aux_stream is None) != (events is None):
+        raise ValueError("aux_stream and events (fork, join) go together")
+    if aux_stream is not None:
+        a.aux_stream = _handle(aux_stream, "aux_stream")
+        a.fork_event = _handle(events[0], "fork event")
+        a.join_event = _handle(events[1], "join event")
     f = lib().kda_chunk_bwd if kda else lib().gdn_chunk_bwd
     rc = f(ctypes.byref(a), _stream(stream))
     if rc != 0:

@@ -5,8 +5,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <mutex>
-
 #include "kernels.h"
 
 namespace {
@@ -288,6 +286,7 @@ int la_chunk_fwd_stages(const la_chunk_fwd_args *a, int is_kda, int stages, void
   return forward(a, is_kda != 0, stages, stream);
 }
 
+
 int32_t la_chunk_fwd_dv_split(const la_chunk_fwd_args *a) {
   if (!a || check_shape(a) != LA_OK) return 0;
   return seg_for(a) ? seg_split(a) : split_for(a);
@@ -435,39 +434,12 @@ size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *a, int is_kda) {
   return bwd_layout(a, is_kda != 0).total;
 }
 
-// The backward's reverse pass needs only the inputs and the prep, so it runs
-// on a side stream of the device while the caller's stream recomputes the
-// forward; the caller's stream waits for both before the per-chunk stage.
-// One side stream and two events per device, created on first use (default
-// priority); the mutex keeps concurrent calls' record/wait pairs apart.  If
-// they cannot be created, everything runs in order on the caller's stream.
-namespace {
-struct Side {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, join = nullptr;
-  bool tried = false;
-};
-constexpr int kMaxDevices = 64;
-std::mutex g_side_mu;
-Side g_side[kMaxDevices];
-
-Side *side_stream() {  // caller holds g_side_mu
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  Side &sd = g_side[dev];
-  if (!sd.tried) {
-    sd.tried = true;
-    if (hipStreamCreateWithFlags(&sd.s, hipStreamNonBlocking) != hipSuccess ||
-        hipEventCreateWithFlags(&sd.fork, hipEventDisableTiming) != hipSuccess ||
-        hipEventCreateWithFlags(&sd.join, hipEventDisableTiming) != hipSuccess) {
-      sd.s = nullptr;
-      (void)hipGetLastError();
-    }
-  }
-  return sd.s ? &sd : nullptr;
-}
-}  // namespace
-
+// The backward's reverse pass needs only the inputs and the prep.  When the
+// caller hands over a second stream and two events (la_chunk_bwd_args
+// aux_stream, fork_event, join_event), the reverse pass is forked onto that
+// stream while `stream` recomputes the forward, and joined back before the
+// per-chunk stage; otherwise everything runs in order on `stream`.  The
+// library creates no stream or event and keeps no state between calls.
 static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
   if (!a) return LA_ERR_NULL;
   const int sc = check_bwd(a);
@@ -475,6 +447,9 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
   if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->cu_seqlens || !a->chunk_indices ||
       !a->chunk_offsets || !a->dout || !a->dq || !a->dk || !a->dv || !a->dg || !a->dbeta)
     return LA_ERR_NULL;
+  const int aux = (a->aux_stream != nullptr) + (a->fork_event != nullptr) +
+                  (a->join_event != nullptr);
+  if (aux != 0 && aux != 3) return LA_ERR_NULL;
   if (!a->workspace) return LA_ERR_WORKSPACE;
   const BwdLayout L = bwd_layout(a, kda);
   if (a->workspace_bytes < L.total) return LA_ERR_WORKSPACE;
@@ -531,63 +506,55 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
                : la::launch_chunk_bwd(bp, a->qkv_dtype, a->d_k, k, sk);
   };
   // prep first (the reverse pass needs it), then the reverse pass on the
-  // side stream while this stream recomputes the forward
+  // caller's second stream (if given) while this stream recomputes the
+  // forward
   if (stage(1, st) != hipSuccess) return LA_ERR_HIP;
-  {
-    std::lock_guard<std::mutex> lk(g_side_mu);
-    Side *sd = side_stream();
-    hipStream_t s1 = st;
-    if (sd) {
-      if (hipEventRecord(sd->fork, st) != hipSuccess || hipStreamWaitEvent(sd->s, sd->fork, 0) != hipSuccess)
-        return LA_ERR_HIP;
-      s1 = sd->s;
-    }
-    if (stage(2, s1) != hipSuccess) return LA_ERR_HIP;
-    f.q = a->q;
-    f.k = a->k;
-    f.v = a->v;
-    f.g = a->g;
-    f.beta = a->beta;
-    f.cu_seqlens = a->cu_seqlens;
-    f.chunk_indices = a->chunk_indices;
-    f.chunk_offsets = a->chunk_offsets;
-    f.h0 = a->h0;
-    f.workspace = ws;
-    f.workspace_bytes = L.hs;
-    {
-      la::MapParams mp{};
-      mp.q = a->q;
-      mp.k = a->k;
-      mp.g = a->g;
-      mp.beta = a->beta;
-      mp.cu_seqlens = a->cu_seqlens;
-      mp.cu64 = a->cu_seqlens_i64;
-      mp.chunk_indices = meta.ci;
-      mp.H = a->H;
-      mp.Hqk = a->H_qk ? a->H_qk : a->H;
-      mp.NT_max = NT;
-      mp.img = ws;
-      if (la::launch_chunk_map(mp, kda, a->qkv_dtype, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
-      la::ReduceParams rp{};
-      rp.v = a->v;
-      rp.cu_seqlens = a->cu_seqlens;
-      rp.cu64 = a->cu_seqlens_i64;
-      rp.chunk_offsets = meta.co;
-      rp.h0 = a->h0;
-      rp.o = nullptr;
-      rp.ht = nullptr;
-      rp.img = ws;
-      rp.H = a->H;
-      rp.N_max = a->N_max;
-      rp.S = split_for(&f);
-      rp.scale = a->scale;
-      rp.hsave = reinterpret_cast<float *>(ws + L.hs);
-      if (la::launch_chunk_reduce(rp, kda, a->qkv_dtype, a->d_k, a->d_v / rp.S, st) != hipSuccess)
-        return LA_ERR_HIP;
-    }
-    if (sd && (hipEventRecord(sd->join, s1) != hipSuccess || hipStreamWaitEvent(st, sd->join, 0) != hipSuccess))
+  hipStream_t s1 = st;
+  hipEvent_t fork = static_cast<hipEvent_t>(a->fork_event);
+  hipEvent_t join = static_cast<hipEvent_t>(a->join_event);
+  if (aux) {
+    s1 = static_cast<hipStream_t>(a->aux_stream);
+    if (hipEventRecord(fork, st) != hipSuccess || hipStreamWaitEvent(s1, fork, 0) != hipSuccess)
       return LA_ERR_HIP;
   }
+  bool ok = stage(2, s1) == hipSuccess;
+  if (ok) {
+    la::MapParams mp{};
+    mp.q = a->q;
+    mp.k = a->k;
+    mp.g = a->g;
+    mp.beta = a->beta;
+    mp.cu_seqlens = a->cu_seqlens;
+    mp.cu64 = a->cu_seqlens_i64;
+    mp.chunk_indices = meta.ci;
+    mp.H = a->H;
+    mp.Hqk = a->H_qk ? a->H_qk : a->H;
+    mp.NT_max = NT;
+    mp.img = ws;
+    ok = la::launch_chunk_map(mp, kda, a->qkv_dtype, a->d_k, st) == hipSuccess;
+  }
+  if (ok) {
+    la::ReduceParams rp{};
+    rp.v = a->v;
+    rp.cu_seqlens = a->cu_seqlens;
+    rp.cu64 = a->cu_seqlens_i64;
+    rp.chunk_offsets = meta.co;
+    rp.h0 = a->h0;
+    rp.o = nullptr;
+    rp.ht = nullptr;
+    rp.img = ws;
+    rp.H = a->H;
+    rp.N_max = a->N_max;
+    rp.S = split_for(&f);
+    rp.scale = a->scale;
+    rp.hsave = reinterpret_cast<float *>(ws + L.hs);
+    ok = la::launch_chunk_reduce(rp, kda, a->qkv_dtype, a->d_k, a->d_v / rp.S, st) == hipSuccess;
+  }
+  // the join is recorded even after a failed launch, so a capture of
+  // `stream` never holds an unjoined fork
+  if (aux && (hipEventRecord(join, s1) != hipSuccess || hipStreamWaitEvent(st, join, 0) != hipSuccess))
+    ok = false;
+  if (!ok) return LA_ERR_HIP;
   if (stage(3, st) != hipSuccess) return LA_ERR_HIP;
   if (grouped) {
     if (la::launch_group_sum(dq_full, a->dq, a->T_max, a->H, Hqk, a->d_k, a->cu_seqlens,

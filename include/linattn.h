@@ -272,6 +272,11 @@ typedef struct {
     float *dh0;                /* [N_max][H][d_k][d_v] fp32 or NULL              */
     void *workspace;           /* >= la_chunk_bwd_workspace_bytes(...) bytes,    */
     size_t workspace_bytes;    /* 256-byte aligned                               */
+    void *aux_stream;          /* optional second stream (hipStream_t) of the   */
+                               /* caller for the reverse pass, with two of the  */
+                               /* caller's events (hipEvent_t) to fork it from  */
+    void *fork_event;          /* `stream` and join it back; all three NULL     */
+    void *join_event;          /* (everything on `stream`) or all three set     */
 } la_chunk_bwd_args;
 
 /* Workspace of gdn_chunk_bwd / kda_chunk_bwd for this shape (T_max, N_max,
@@ -301,13 +306,21 @@ size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *shape, int is_kda);
  * With grouped value heads each value head's dq, dk go to the workspace and
  * one more launch sums every group into dq, dk.
  * Streams: everything is ordered after the work already queued on `stream`,
- * and work queued on `stream` afterwards sees every output.  The reverse pass
- * runs on a library-owned stream of the current device (created on first
- * use, default priority), forked from and joined back to `stream` through
- * events; capturing `stream` into a HIP graph captures both.  Apart from
- * creating that stream and its two events on the first call on a device, the
- * call allocates nothing (all scratch is the caller's workspace).
- * Host errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_UNSUPPORTED,
+ * and work queued on `stream` afterwards sees every output.  With
+ * aux_stream, fork_event and join_event all NULL every launch goes to
+ * `stream`, in order.  With all three set (the caller's own stream and
+ * events, on the current device), the reverse pass runs on aux_stream,
+ * forked after the prep (fork_event recorded on `stream`, waited for by
+ * aux_stream) and joined back before the per-chunk stage (join_event
+ * recorded on aux_stream, waited for by `stream`) while `stream` recomputes
+ * the forward; capturing `stream` into a HIP graph captures both branches.
+ * The join is recorded even when a launch fails.  The caller must not use
+ * aux_stream or the two events for anything else until the call's work on
+ * `stream` has completed (two concurrent calls need their own triples).  As
+ * every call, it creates no stream or event and allocates nothing (all
+ * scratch is the caller's workspace).
+ * Host errors: LA_ERR_NULL (also: only some of aux_stream, fork_event,
+ * join_event set), LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_UNSUPPORTED,
  * LA_ERR_WORKSPACE, LA_ERR_HIP.
  */
 int gdn_chunk_bwd(const la_chunk_bwd_args *a, void *stream);

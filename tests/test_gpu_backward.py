@@ -215,9 +215,9 @@ def test_backward_kda_strong_decay():
 
 
 def test_backward_concurrent_streams_match_sequential():
-    """Two host threads issue backward calls on two streams at once (the
-    library forks each call's reverse pass onto its own side stream and joins
-    it back with events): every output must equal the same call run alone."""
+    """Two host threads issue backward calls on two streams at once, each
+    forking its reverse pass onto its own second stream with its own events:
+    every output must equal the same call run alone on one stream."""
     import threading
     cases = []
     for seed in (790, 791):
@@ -241,6 +241,9 @@ def test_backward_concurrent_streams_match_sequential():
     args = [prepared(*c) for c in cases]
     torch.cuda.synchronize()
     streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    aux = [torch.cuda.Stream(), torch.cuda.Stream()]
+    events = [la.fork_join_events(), la.fork_join_events()]
+    torch.cuda.synchronize()
     results = [[None] * 4, [None] * 4]
     start = threading.Barrier(2)
 
@@ -251,7 +254,7 @@ def test_backward_concurrent_streams_match_sequential():
             for rep in range(4):
                 results[i][rep] = la.gdn_chunk_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["cu"],
                                                    a["ci"], a["co"], a["do"], h0=a["h0"], dht=a["dht"],
-                                                   scale=1.0)
+                                                   scale=1.0, aux_stream=aux[i], events=events[i])
         streams[i].synchronize()
 
     threads = [threading.Thread(target=worker, args=(i,)) for i in range(2)]
@@ -267,3 +270,24 @@ def test_backward_concurrent_streams_match_sequential():
             for key in ("dq", "dk", "dv", "dg", "dbeta"):
                 assert torch.equal(got[key][:SMALL_CU[-1]], alone[i][key][:SMALL_CU[-1]]), (i, rep, key)
             assert torch.equal(got["dh0"][ne], alone[i]["dh0"][ne]), (i, rep)
+
+
+def test_backward_default_allocations_fill_padding():
+    """Outputs the binding allocates: rows outside every sequence are zero,
+    dh0 of a zero-length sequence is its dht (the state passes through
+    unchanged), and every value is finite."""
+    inp = make_inputs(SMALL_CU[-1] + 37, 2, 64, 64, kda=False, dtype="bf16", seed=795,
+                      cu_seqlens=SMALL_CU, h0_std=0.1)
+    rng = np.random.default_rng(796)
+    do = rng.standard_normal(inp["v"].shape).astype(np.float32)
+    dht = rng.standard_normal(inp["h0"].shape).astype(np.float32)
+    got = run_bwd(inp, do, dht, 1.0)
+    rows = SMALL_CU[-1]
+    for key in ("dq", "dk", "dv", "dg", "dbeta"):
+        t = got[key]
+        assert bool(torch.isfinite(t).all()), key
+        assert bool((t[rows:] == 0).all()), key
+    empty = np.flatnonzero(np.diff(np.asarray(SMALL_CU)) == 0)
+    assert len(empty) > 0
+    for n in empty:
+        assert torch.equal(got["dh0"][n].cpu(), torch.from_numpy(dht[n])), n

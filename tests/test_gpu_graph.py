@@ -169,12 +169,14 @@ def test_small_bucket_graph_layouts_with_state(kda):
         assert np.isfinite(o_g.cpu().numpy()[:total]).all()
 
 
+@pytest.mark.parametrize("fork", [False, True], ids=["one_stream", "aux_stream"])
 @pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
-def test_backward_graph_replays_over_layouts(kda):
+def test_backward_graph_replays_over_layouts(kda, fork):
     """The chunk backward under the same contract: metadata and backward
     captured once on static buffers, replayed over fresh layouts and inputs
     copied in; every replay equals an eager call on the same buffers bit for
-    bit (rows of real tokens, dh0 of non-empty sequences)."""
+    bit (rows of real tokens, dh0 of non-empty sequences).  With the caller's
+    second stream and events, the capture holds the forked reverse pass."""
     T_max, N_max, H, d = 1024, 6, 2, 64
     dev = torch.device("cuda")
     bf = torch.bfloat16
@@ -194,10 +196,11 @@ def test_backward_graph_replays_over_layouts(kda):
     ws = torch.empty((la.bwd_workspace_bytes(T_max, N_max, H, d, d, bf, kda=kda),),
                      dtype=torch.uint8, device=dev)
     fn = la.kda_chunk_bwd if kda else la.gdn_chunk_bwd
+    side = dict(aux_stream=torch.cuda.Stream(), events=la.fork_join_events()) if fork else {}
 
     def step():
         la.build_chunk_meta(cu, T_max, chunk_indices=ci, chunk_offsets=co)
-        fn(q, k, v, g, beta, cu, ci, co, dout, h0=h0, workspace=ws, **outs)
+        fn(q, k, v, g, beta, cu, ci, co, dout, h0=h0, workspace=ws, **outs, **side)
 
     def fill(seed):
         rng = np.random.default_rng(seed)
@@ -236,7 +239,8 @@ def test_backward_graph_replays_over_layouts(kda):
         for key in ("dq", "dk", "dv", "dg", "dbeta"):
             assert torch.equal(outs[key][:rows], eager[key][:rows]), (r, key)
         assert torch.equal(outs["dh0"][ne], eager["dh0"][ne]), r
-        _say(f"backward graph replay {r}: {int((np.diff(lay) > 0).sum())} sequences, {rows} tokens")
+        _say(f"backward graph replay {r} (fork {fork}): {int((np.diff(lay) > 0).sum())} "
+             f"sequences, {rows} tokens")
 
 
 def test_short_conv_graph_replays_over_layouts():
