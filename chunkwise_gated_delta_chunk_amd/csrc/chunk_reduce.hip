@@ -197,6 +197,16 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
       for (int e = 0; e < 4; ++e) hacc[t][e] = wk.init_id && 16 * t + lg * 4 + e == cw + lr ? 1.f : 0.f;
   }
 
+  // ---- operand scale (16-bit inputs).  The fp16 MFMA operands that carry
+  // state-side values (H, X, U) are formed from those values times a power
+  // of two cs, one per wave: the recurrence is linear in (V, H), so the wave
+  // runs on cs V and cs H exactly and divides o and the states it stores by
+  // cs.  cs maps the largest |value| of the wave's columns of the initial
+  // state and of the first chunk's V into [4, 8) (1 if both are zero), which
+  // keeps those operands inside fp16's normal range whatever the input scale.
+  float cs = 1.f, ics = 1.f;
+  float osc = p.scale;  // o = p.scale * (cs-scaled result) / cs
+
   int off_o[4];
 #pragma unroll
   for (int e = 0; e < 4; ++e) off_o[e] = (lg * 4 + e) * rs_o + (cw + lr) * osz;
@@ -208,12 +218,12 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
     if (p.o_bf16) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(p.scale * oa[e]), ro,
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_rne(osc * oa[e]), ro,
                                               off_o[e], 0, 0);
     } else {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(p.scale * oa[e]), ro, off_o[e], 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(osc * oa[e]), ro, off_o[e], 0, 0);
     }
   };
 
@@ -254,7 +264,7 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
 #pragma unroll
       for (int t = 0; t < NHT; ++t)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) hs[(size_t)(16 * t + lg * 4 + e) * DV + cw + lr] = hacc[t][e];
+        for (int e = 0; e < 4; ++e) hs[(size_t)(16 * t + lg * 4 + e) * DV + cw + lr] = hacc[t][e] * ics;
     }
     const char *buf = smem + BUF * STAGE;
     const char *tV = buf;
@@ -354,7 +364,7 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
       for (int R = 0; R < 4; ++R)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          x[R][e] = in16_to_f32<In>((uint16_t)vr[R][e]) - gam[R][e] * yk[R][e];
+          x[R][e] = fmaf(in16_to_f32<In>((uint16_t)vr[R][e]), cs, -gam[R][e] * yk[R][e]);
       static_for<4>([&](auto rc) {
         constexpr int R = decltype(rc)::value;
         ds_read_b128_at<512 + 64 * R>(bet[R], aS[BUF]);
@@ -517,8 +527,44 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
   // ---------------------------------------------------------- chunk loop
   if (copier) {
     copy_chunk(0, img_c, v_c, min(kBT, eos - wk.t0));
+    if constexpr (F16) {  // the compute waves read the first chunk's V for cs
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      chunk_barrier();
+    }
     for (int jj = j0; jj < j1; ++jj) copy_step(jj);
     return;
+  }
+  if constexpr (F16) {
+    chunk_barrier();  // the first chunk's stage has landed in buffer 0
+    s16x4 v0[4];
+    static_for<4>([&](auto rc) {
+      constexpr int R = decltype(rc)::value;
+      ds_read_tr16_at<R * 256 * PV>(v0[R], aV[0]);
+    });
+    wait_lds_tied<0>(v0[0], v0[1], v0[2], v0[3]);
+    float m = 0.f;
+#pragma unroll
+    for (int R = 0; R < 4; ++R)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(in16_to_f32<In>((uint16_t)v0[R][e])));
+#pragma unroll
+    for (int t = 0; t < NHT; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) m = fmaxf(m, fabsf(hacc[t][e]));
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if (m > 0.f && m <= 3.0e38f) {
+      int ex;
+      (void)frexpf(m, &ex);  // m in [2^(ex-1), 2^ex)
+      const int k = min(max(3 - ex, -100), 100);
+      cs = ldexpf(1.f, k);
+      ics = ldexpf(1.f, -k);
+      osc = p.scale * ics;
+#pragma unroll
+      for (int t = 0; t < NHT; ++t)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) hacc[t][e] *= cs;
+    }
   }
   // two chunks per trip, one per buffer; leaving through the breaks keeps a
   // single path into the loop header, so the state accumulators keep their
@@ -537,7 +583,7 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
 #pragma unroll
     for (int t = 0; t < NHT; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) wk.fin[(size_t)(16 * t + lg * 4 + e) * DV + cw + lr] = hacc[t][e];
+      for (int e = 0; e < 4; ++e) wk.fin[(size_t)(16 * t + lg * 4 + e) * DV + cw + lr] = hacc[t][e] * ics;
   }
   if (wk.pimg) {
     constexpr int PP = DK * 2 / 16;  // 16-byte pieces per fp16 row
@@ -548,9 +594,10 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
       for (int e = 0; e < 4; ++e) {
         const int r = 16 * t + lg * 4 + e;
         const int off = (tile_off<PP>(r, kc >> 3) >> 1) + (kc & 7);
-        const _Float16 hi = (_Float16)hacc[t][e];
+        const float hv = hacc[t][e] * ics;
+        const _Float16 hi = (_Float16)hv;
         wk.pimg[off] = hi;
-        wk.pimg[DK * DK + off] = (_Float16)(hacc[t][e] - (float)hi);
+        wk.pimg[DK * DK + off] = (_Float16)(hv - (float)hi);
       }
   }
 }
