@@ -22,20 +22,27 @@ from __future__ import annotations
 import numpy as np
 
 __all__ = [
-    "bf16_round", "make_inputs", "config", "bucket_layout", "CONFIG_NAMES",
+    "bf16_round", "make_inputs", "config", "bucket_layout", "bucket_replay_layout",
+    "CONFIG_NAMES",
 ]
 
 
 def bf16_round(x):
-    """Round float32 values to the nearest bf16 value (ties to even); float32 out."""
+    """Round float32 values to the nearest bf16 value (ties to even); float32 out.
+
+    On the bit pattern u: add 0x7FFF plus the lowest kept bit, clear the low 16
+    bits.  For every non-NaN u the sum stays below 2^32, so uint32 arithmetic
+    is exact; NaNs are restored afterwards (the sum can carry out of a NaN's
+    payload)."""
     x = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
-    u = x.view(np.uint32).astype(np.uint64)
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16) << 16
-    out = r.astype(np.uint32).view(np.float32)
-    # keep NaN as NaN (the rounding above can carry into the exponent of a NaN payload)
+    u = x.view(np.uint32)
+    r = (u >> np.uint32(16)) & np.uint32(1)
+    r += u
+    r += np.uint32(0x7FFF)
+    r &= np.uint32(0xFFFF0000)
+    out = r.view(np.float32)
     nan = np.isnan(x)
     if nan.any():
-        out = out.copy()
         out[nan] = np.float32("nan")
     return out
 
@@ -54,7 +61,7 @@ def _store(x, dtype):
 
 
 def make_inputs(T, H, dk, dv, *, kda, dtype, seed, cu_seqlens=None, h0_std=None,
-                round_gate=False, n_seqs=None, cuts=None):
+                round_gate=False, n_seqs=None, cuts=None, rng=None):
     """Draw one batch of inputs in a fixed order: q, k, v, g, beta, (cuts), h0.
 
     q, k ~ N(0,1) then L2-normalised per (token, head); v ~ N(0,1);
@@ -66,9 +73,11 @@ def make_inputs(T, H, dk, dv, *, kda, dtype, seed, cu_seqlens=None, h0_std=None,
     ``cuts`` is an optional callable ``rng -> cu_seqlens`` drawn after beta, so a
     layout can come from the same stream; otherwise ``cu_seqlens`` (or one
     sequence of length T) is used.  h0 ~ N(0, h0_std) of shape [N, H, dk, dv]
-    when ``h0_std`` is given, else None.
+    when ``h0_std`` is given, else None.  ``rng`` continues a given generator
+    instead of seeding a new one.
     """
-    rng = np.random.Generator(np.random.PCG64(seed))
+    if rng is None:
+        rng = np.random.Generator(np.random.PCG64(seed))
     q = _store(_l2norm(rng.standard_normal((T, H, dk))), dtype)
     k = _store(_l2norm(rng.standard_normal((T, H, dk))), dtype)
     v = _store(rng.standard_normal((T, H, dv)), dtype)
@@ -143,6 +152,17 @@ def bucket_layout(rng, T_max, N_max, n=None):
     return cu.astype(np.int32)
 
 
+BUCKET_T_MAX, BUCKET_N_MAX = 16384, 64
+
+
+def bucket_replay_layout(replay):
+    """The layout of bucket replay ``replay`` (workload 3) alone: the first
+    draw of that replay's stream, so it needs none of the inputs drawn after
+    it."""
+    rng = np.random.Generator(np.random.PCG64(3000 + replay))
+    return bucket_layout(rng, BUCKET_T_MAX, BUCKET_N_MAX)
+
+
 CONFIG_NAMES = {
     0: "gdn fp32 T=256 N=1 H=2 d=64",
     1: "gdn bf16 varlen T=8192 N=8 H=16 d=128 (h0~N(0,0.1))",
@@ -161,8 +181,9 @@ def config(idx, *, replay=0, kda=None, T=None):
     2: KDA bf16 (q/k/v and bf16-valued g/beta), one sequence T=4096, H=16,
        d=128, zero state, seed 2.
     3: fixed-capacity bucket T_max=16384, N_max=64, GDN bf16, H=32, d=128,
-       no initial state; replay r draws a fresh layout and inputs with seed
-       3000+r (padding rows hold ordinary non-zero data).
+       no initial state; replay r draws a fresh layout (bucket_replay_layout)
+       and then its inputs from one stream seeded 3000+r (padding rows hold
+       ordinary non-zero data).
     4: GDN (kda=False) or KDA (kda=True) bf16, one sequence, H=10, d=128,
        T=65536 (default) or T=2048, zero state, seed 4.
     """
@@ -175,9 +196,10 @@ def config(idx, *, replay=0, kda=None, T=None):
         return make_inputs(4096, 16, 128, 128, kda=True, dtype="bf16", seed=2,
                            round_gate=True)
     if idx == 3:
-        return make_inputs(16384, 32, 128, 128, kda=False, dtype="bf16",
-                           seed=3000 + replay,
-                           cuts=lambda rng: bucket_layout(rng, 16384, 64))
+        rng = np.random.Generator(np.random.PCG64(3000 + replay))
+        cu = bucket_layout(rng, BUCKET_T_MAX, BUCKET_N_MAX)
+        return make_inputs(BUCKET_T_MAX, 32, 128, 128, kda=False, dtype="bf16",
+                           seed=3000 + replay, cu_seqlens=cu, rng=rng)
     if idx == 4:
         T = 65536 if T is None else T
         return make_inputs(T, 10, 128, 128, kda=bool(kda), dtype="bf16", seed=4)

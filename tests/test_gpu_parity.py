@@ -301,15 +301,19 @@ def test_config4_short(kda):
 
 
 @pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
-def test_config4_long_sampled_heads(kda):
-    """T=65536, one sequence: oracle on two of the ten heads."""
+def test_config4_long_all_heads(kda):
+    """T=65536, one sequence, the segmented reduce: every one of the ten heads
+    against the oracle (H = 10 is not a multiple of the 8 XCDs the workgroup
+    numbering deals heads over)."""
     inp = config(4, kda=kda)
     o, ht, _ = run_gpu(inp)
-    heads = [0, 7]
-    o_ref, ht_ref = run_oracle(inp, heads=heads)
-    eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref, heads=heads)
-    _say(f"config4 T=65536 kda={kda} heads {heads}: o {eo:.2e} ht {eh:.2e}")
-    assert eo <= tol and eh <= tol
+    o_ref, ht_ref = run_oracle(inp)
+    cu = inp["cu_seqlens"]
+    for h in range(inp["H"]):
+        eo = rel_err(o.cpu().numpy()[: int(cu[-1]), h], o_ref[: int(cu[-1]), h])
+        eh = rel_err(ht.cpu().numpy()[:, h], ht_ref[:, h])
+        _say(f"config4 T=65536 kda={kda} head {h}: o {eo:.2e} ht {eh:.2e}")
+        assert eo <= TOL["bf16"] and eh <= TOL["bf16"], h
 
 
 @pytest.mark.parametrize("replay", [0, 1])
@@ -322,6 +326,36 @@ def test_config3_layouts_sampled_heads(replay):
     o_ref, ht_ref = run_oracle(inp, heads=heads)
     eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref, heads=heads)
     _say(f"config3 o {eo:.2e} ht {eh:.2e}")
+    assert eo <= tol and eh <= tol
+
+
+@pytest.mark.parametrize("replay", list(range(20)))
+def test_config3_every_layout(replay):
+    """Every one of the bucket's 20 replay layouts (T_max = 16384, N_max = 64,
+    H = 32) in the launch configuration the bench replays, two heads per
+    layout against the oracle, rotating so the 20 layouts cover all 32 heads.
+    The two heads hold seeded inputs of the workload's distributions; every
+    other head holds the same data shifted by a head-dependent number of
+    tokens, so a result that read another head's rows would not match."""
+    import synth
+    T, H, d = synth.BUCKET_T_MAX, 32, 128
+    cu = synth.bucket_replay_layout(replay)
+    heads = [replay % H, (replay + 16) % H]
+    two = make_inputs(T, 2, d, d, kda=False, dtype="bf16", seed=33000 + replay, cu_seqlens=cu)
+    inp = dict(two, H=H)
+    for key in ("q", "k", "v", "g", "beta"):
+        full = np.empty((T, H) + two[key].shape[2:], dtype=np.float32)
+        for h in range(H):
+            src = 0 if h == heads[0] else 1 if h == heads[1] else h % 2
+            shift = 0 if h in heads else 997 * h
+            full[:, h] = np.roll(two[key][:, src], shift, axis=0)
+        inp[key] = full
+    n = int((np.diff(cu) > 0).sum())
+    _say(f"config3 layout {replay}: {n} sequences, {int(cu[-1])} tokens, heads {heads}")
+    o, ht, _ = run_gpu(inp)
+    o_ref, ht_ref = run_oracle(inp, heads=heads)
+    eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref, heads=heads)
+    _say(f"config3 layout {replay}: o {eo:.2e} ht {eh:.2e}")
     assert eo <= tol and eh <= tol
 
 
