@@ -72,12 +72,13 @@ def alg_bytes(inp, kind):
     """Algorithmic HBM bytes of one launch.
 
     "op": the whole forward, T*H*[(2 d_k + d_v) s_qkv + s_g + 4 + 4 d_v] plus
-    4 d_k d_v per (non-empty sequence, head) for each of h0 / ht.
-    The kernels split these bytes by who has to touch the operation's own
-    inputs and outputs: the map reads q, k (GDN: only to form its chunk
-    matrices), g and beta; the reduce reads q, k (GDN), v and h0 and writes o
-    and ht.  Intermediates handed from map to reduce through the workspace
-    are implementation overhead and are not counted."""
+    4 d_k d_v per (non-empty sequence, head) for each of h0 / ht.  This is the
+    figure the headline roofline divides by the step time.
+    Per kernel (diagnostics), the part of those bytes a kernel has to touch
+    itself: the map reads q, k, g and beta; the reduce reads v (and h0) and
+    writes o (and ht) -- it takes the chunk matrices and the staged keys and
+    queries from the map's workspace images, which are implementation
+    overhead and not counted."""
     T = int(inp["cu_seqlens"][-1])
     H, dk, dv = inp["H"], inp["dk"], inp["dv"]
     s_qkv = 2 if inp["dtype"] == "bf16" else 4
@@ -90,8 +91,7 @@ def alg_bytes(inp, kind):
     if kind == "map":
         return T * H * (2 * dk * s_qkv + s_g + 4)
     if kind == "reduce":
-        qk = 0 if inp["kda"] else 2 * dk * s_qkv
-        return T * H * (qk + dv * s_qkv + 4 * dv) + state
+        return T * H * (dv * s_qkv + 4 * dv) + state
     raise ValueError(kind)
 
 
@@ -564,6 +564,356 @@ def bench_decode(args, torch, la, synth, dev):
     print(json.dumps(out), flush=True)
 
 
+def env_record(torch):
+    """Versions and device of this run (the RFC's CI plan records them)."""
+    props = torch.cuda.get_device_properties(0)
+    rocm = None
+    if os.path.exists("/opt/rocm/.info/version"):
+        rocm = open("/opt/rocm/.info/version").read().strip()
+    return {"torch": torch.__version__, "hip": getattr(torch.version, "hip", None),
+            "rocm": rocm, "gfx_arch": getattr(props, "gcnArchName", None),
+            "device": props.name, "compute_units": props.multi_processor_count}
+
+
+class FwdBucket:
+    """Static device buffers of one fixed-capacity bucket (T_max, N_max) of a
+    forward workload, and the step on them: build_chunk_meta, then the chunk
+    forward (the FLA graph-capture RFC, "Static buffer contract")."""
+
+    def __init__(self, torch, la, inp, T_max, N_max, dev, dv_split=0, seg_len=0):
+        self.torch, self.la = torch, la
+        H, dk, dv = inp["H"], inp["dk"], inp["dv"]
+        tdt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+        self.kda = bool(inp["kda"])
+        z = lambda shape, dt=torch.float32: torch.zeros(shape, dtype=dt, device=dev)  # noqa: E731
+        self.q, self.k, self.v = (z((T_max, H, dk), tdt) for _ in range(3))
+        self.g = z((T_max, H, dk) if self.kda else (T_max, H))
+        self.beta = z((T_max, H))
+        self.cu = z((N_max + 1,), torch.int32)
+        self.has_h0 = inp["h0"] is not None
+        self.h0 = z((N_max, H, dk, dv)) if self.has_h0 else None
+        NT = la.nt_max(T_max, N_max)
+        self.ci = z((NT, 2), torch.int32)
+        self.co = z((N_max + 1,), torch.int32)
+        self.st = z((1,), torch.int32)
+        self.o = z((T_max, H, dv))
+        self.ht = z((N_max, H, dk, dv))
+        self.ws = torch.empty((la.workspace_bytes(T_max, N_max, H, dk, dv, tdt, self.kda,
+                                                  seg_len=seg_len),), dtype=torch.uint8, device=dev)
+        self.kw = dict(h0=self.h0, o=self.o, ht=self.ht, workspace=self.ws, dv_split=dv_split,
+                       seg_len=seg_len)
+        self.T_max, self.N_max, self.NT = T_max, N_max, NT
+        self.split = la.dv_split_for(T_max, N_max, H, dk, dv, tdt, dv_split, seg_len=seg_len)
+        self.seg = la.seg_len_for(T_max, N_max, H, dk, dv, tdt, seg_len=seg_len)
+        self.fwd = la.kda_chunk_fwd if self.kda else la.gdn_chunk_fwd
+        self.graph = None
+
+    def load(self, src, cu_host):
+        """Write one layout into the static buffers: device inputs ``src`` (the
+        rows of real tokens) and cu_seqlens from pinned host memory."""
+        T = int(cu_host[-1])
+        for name in ("q", "k", "v", "g", "beta"):
+            getattr(self, name)[:T].copy_(src[name][:T], non_blocking=True)
+        if self.has_h0:
+            n = src["h0"].shape[0]
+            self.h0[:n].copy_(src["h0"], non_blocking=True)
+        self.cu.copy_(cu_host, non_blocking=True)
+
+    def step(self):
+        la = self.la
+        la.build_chunk_meta(self.cu, self.T_max, chunk_indices=self.ci, chunk_offsets=self.co,
+                            status=self.st)
+        self.fwd(self.q, self.k, self.v, self.g, self.beta, self.cu, self.ci, self.co, **self.kw)
+
+    def capture(self):
+        torch = self.torch
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            self.step()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        self.graph = torch.cuda.CUDAGraph()
+        tc = time.perf_counter()
+        with torch.cuda.graph(self.graph):
+            self.step()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - tc) * 1e3
+
+
+def padded_cu(cu, N_max):
+    out = np.full(N_max + 1, cu[-1], dtype=np.int32)
+    out[:len(cu)] = cu
+    return out
+
+
+def event_times(torch, fn, steps, warmup):
+    """p50, p95 and mean (ms) of ``steps`` calls of fn, each bracketed by HIP
+    events on the current stream."""
+    for _ in range(warmup):
+        fn()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        ev[2 * i].record()
+        fn()
+        ev[2 * i + 1].record()
+    torch.cuda.synchronize()
+    t = np.array([ev[2 * i].elapsed_time(ev[2 * i + 1]) for i in range(steps)])
+    return float(np.median(t)), float(np.percentile(t, 95)), float(t.mean())
+
+
+def wall_ms(torch, fn, steps, warmup):
+    """Wall-clock ms per call of ``steps`` back-to-back calls (host dispatch
+    included), synchronised at both ends."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / steps
+
+
+def device_inputs(torch, inp, dev):
+    tdt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
+    d = {x: torch.from_numpy(inp[x]).to(dev, tdt) for x in ("q", "k", "v")}
+    d["g"] = torch.from_numpy(inp["g"]).to(dev)
+    d["beta"] = torch.from_numpy(inp["beta"]).to(dev)
+    d["h0"] = None if inp["h0"] is None else torch.from_numpy(inp["h0"]).to(dev)
+    return d
+
+
+def timing_protocol(args, torch, la, inp, src, dev, exact_replay_p50):
+    """The RFC's four modes on this workload ("Performance evaluation"):
+    eager-live (the exact sizes, host dispatch included), eager-fixed and
+    graph-replay in a fixed-capacity bucket (N_max = 64 sequence slots), and
+    graph-update-replay (the layout's rows copied into the bucket's static
+    buffers and cu_seqlens from pinned host memory, then the replay).  Also
+    the padding cost of the bucket, the update overhead, and the break-even
+    length: eager-live against graph-update-replay for one sequence of
+    growing length in the same bucket."""
+    cu = np.asarray(inp["cu_seqlens"], dtype=np.int32)
+    T, N = int(cu[-1]), len(cu) - 1
+    N_max = max(64, N)
+    b = FwdBucket(torch, la, inp, T, N_max, dev)
+    cu_pin = torch.from_numpy(padded_cu(cu, N_max)).pin_memory()
+    b.load(src, cu_pin)
+    torch.cuda.synchronize()
+    steps, warm = max(10, args.steps // 4), 3
+    eager_fixed = wall_ms(torch, b.step, steps, warm)
+    capture_ms = b.capture()
+    rp50, rp95, _ = event_times(torch, b.graph.replay, steps, warm)
+
+    def update_replay():
+        b.load(src, cu_pin)
+        b.graph.replay()
+
+    up50, up95, _ = event_times(torch, update_replay, steps, warm)
+    upd50, _, _ = event_times(torch, lambda: b.load(src, cu_pin), steps, warm)
+
+    # break-even: one sequence of length L, eager-live (exact sizes) against
+    # graph-update-replay in this bucket
+    rows = []
+    for L in (64, 256, 1024, 4096, T):
+        if L > T:
+            continue
+        cu_l = np.array([0, L], dtype=np.int32)
+        sub = {x: (None if src[x] is None else src[x][:L] if x != "h0" else src[x][:1])
+               for x in src}
+        ex = FwdBucket(torch, la, dict(inp, h0=inp["h0"]), L, 1, dev)
+        ex.load(sub, torch.from_numpy(cu_l).pin_memory())
+        live = wall_ms(torch, ex.step, steps, warm)
+        cu_b = torch.from_numpy(padded_cu(cu_l, N_max)).pin_memory()
+
+        def upd():
+            b.load(sub, cu_b)
+            b.graph.replay()
+
+        gu50, _, _ = event_times(torch, upd, steps, warm)
+        rows.append({"tokens": L, "eager_live_ms": round(live, 5),
+                     "graph_update_replay_ms": round(gu50, 5)})
+        del ex
+    faster = [r["tokens"] for r in rows if r["graph_update_replay_ms"] < r["eager_live_ms"]]
+    return {
+        "bucket": {"T_max": T, "N_max": N_max, "nt_max": b.NT},
+        "eager_fixed_ms": round(eager_fixed, 5),
+        "graph_replay_bucket_p50_ms": round(rp50, 5), "graph_replay_bucket_p95_ms": round(rp95, 5),
+        "graph_update_replay_p50_ms": round(up50, 5),
+        "graph_update_replay_p95_ms": round(up95, 5),
+        "update_ms": round(upd50, 5),
+        "padding_cost_ms": round(rp50 - exact_replay_p50, 5),
+        "bucket_capture_ms": round(capture_ms, 3),
+        "break_even": {"rows": rows,
+                       "graph_faster_up_to_tokens": max(faster) if faster else 0},
+    }
+
+
+def bucket_leg(args, torch, la, dev):
+    """The fixed-capacity bucket (T_max = 16384, N_max = 64, GDN, H = 32,
+    d = 128, no initial state) over its 20 replay layouts: one capture, each
+    layout's cu_seqlens copied into the static buffer and replayed; per-layout
+    op fraction (the layout's algorithmic bytes over its replay p50 at
+    8 TB/s).  The layouts are the workload's own (synth.bucket_replay_layout);
+    the token data are drawn on the device from a seeded generator with the
+    workload's distributions (the timing does not depend on their values)."""
+    import synth
+    T_max, N_max, H, d = synth.BUCKET_T_MAX, synth.BUCKET_N_MAX, 32, 128
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(3000)
+    bf = torch.bfloat16
+
+    def unit(shape):
+        x = torch.randn(shape, generator=gen, device=dev, dtype=torch.float64)
+        return (x / x.norm(dim=-1, keepdim=True).clamp_min(1e-6)).to(bf)
+
+    src = {"q": unit((T_max, H, d)), "k": unit((T_max, H, d)),
+           "v": torch.randn((T_max, H, d), generator=gen, device=dev).to(bf),
+           "g": torch.nn.functional.logsigmoid(
+               torch.randn((T_max, H), generator=gen, device=dev) + 3.0),
+           "beta": torch.sigmoid(torch.randn((T_max, H), generator=gen, device=dev)),
+           "h0": None}
+    spec = dict(H=H, dk=d, dv=d, dtype="bf16", kda=False, h0=None)
+    b = FwdBucket(torch, la, spec, T_max, N_max, dev)
+    for x in ("q", "k", "v", "g", "beta"):
+        getattr(b, x).copy_(src[x])
+    b.cu.copy_(torch.from_numpy(synth.bucket_replay_layout(0)))
+    b.capture()
+    fr = []
+    for r in range(args.layouts):
+        cu = synth.bucket_replay_layout(r)
+        b.cu.copy_(torch.from_numpy(cu))
+        p50, _, _ = event_times(torch, b.graph.replay, 5, 2)
+        ab = alg_bytes(dict(spec, cu_seqlens=cu), "op")
+        fr.append(ab / (p50 * 1e-3) / 1e9 / HBM_PEAK_GBS)
+    fr.sort()
+    return {"workload": WORKLOADS["c3"][2], "layouts": len(fr),
+            "op_hbm_frac_median": round(fr[len(fr) // 2], 4), "op_hbm_frac_min": round(fr[0], 4),
+            "op_hbm_frac_max": round(fr[-1], 4)}
+
+
+def bench_forward(args, torch, la, synth, dev):
+    cfg, kda, desc = WORKLOADS[args.workload]
+    T_arg = 2048 if args.workload.endswith("_short") else None
+    inp = synth.config(cfg, kda=kda, T=T_arg) if cfg == 4 else synth.config(cfg)
+    T = inp["q"].shape[0]
+    H, dk, dv = inp["H"], inp["dk"], inp["dv"]
+    cu_np = np.asarray(inp["cu_seqlens"], dtype=np.int32)
+    N = len(cu_np) - 1
+    src = device_inputs(torch, inp, dev)
+    b = FwdBucket(torch, la, inp, T, N, dev, args.dv_split, args.seg_len)
+    b.load(src, torch.from_numpy(cu_np).pin_memory())
+    torch.cuda.synchronize()
+    is_kda = bool(inp["kda"])
+    split, seg = b.split, b.seg
+    fwd_kw = b.kw
+    args_t = (b.q, b.k, b.v, b.g, b.beta, b.cu, b.ci, b.co)
+
+    # ---- eager warmup + per-kernel HIP-event timing on the launch stream
+    for _ in range(max(1, args.warmup)):
+        b.step()
+    torch.cuda.synchronize()
+    assert int(b.st.item()) == 0
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        e = evs[i]
+        e[0].record()
+        la.build_chunk_meta(b.cu, T, chunk_indices=b.ci, chunk_offsets=b.co, status=b.st)
+        e[1].record()
+        la.chunk_fwd_stages(is_kda, la.STAGE_MAP, *args_t, **fwd_kw)
+        e[2].record()
+        la.chunk_fwd_stages(is_kda, la.STAGE_REDUCE, *args_t, **fwd_kw)
+        e[3].record()
+    torch.cuda.synchronize()
+    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])  # ms
+    t_meta, t_map, t_red = (float(x) for x in per.mean(axis=0))
+    eager_o = b.o.clone()
+    eager_ht = b.ht.clone()
+
+    # eager-live: whole steps at the exact sizes, host dispatch included
+    eager_ms = wall_ms(torch, b.step, args.steps, 0)
+
+    # ---- graph capture of one step, replay timing
+    capture_ms = b.capture()
+    for _ in range(args.warmup):
+        b.graph.replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        b.graph.replay()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+    # per-replay event pairs on the replay stream: p50 / p95 of one step and
+    # the event-timed mean the headline roofline uses
+    p50, p95, ev_mean = event_times(torch, b.graph.replay, args.steps, 0)
+    graph_eq = bool(torch.equal(b.o, eager_o) and torch.equal(b.ht, eager_ht))
+
+    tokens = int(cu_np[-1])
+    value = tokens * args.steps / elapsed
+    nt_actual = int(np.ceil(np.diff(cu_np) / 64).sum())
+
+    op_bytes = alg_bytes(inp, "op")
+    op_flops = alg_flops(inp)
+    kernels = {"meta": t_meta, "map": t_map, "reduce": t_red}
+    diag = {}
+    for kind, t in kernels.items():
+        ab = alg_bytes(inp, kind) if kind != "meta" else 4 * (N + 1) * 2 + 8 * b.NT
+        diag[kind] = {"ms": round(t, 5), "alg_bytes": ab,
+                      "hbm_frac": round(ab / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # HBM traffic of one step: the sum of every kernel's counter-measured
+    # bytes, when all were taken on the current sources (else null)
+    tr = [load_traffic(kind, args.workload) for kind in ("map", "reduce")]
+    traffic = None if (any(x is None for x in tr) or seg) else float(sum(tr))
+    achieved = op_bytes / (ev_mean * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+            "kernel": ("whole step (graph replay): chunk_meta + chunk_map + chunk_reduce"
+                       + ("" if seg == 0 else
+                          f" x2 + chunk_combine (segments of {seg} chunks)")
+                       + f", d_v split {split}"),
+            "alg_bytes_per_launch": op_bytes, "avg_launch_ms": round(ev_mean, 5)}
+
+    out = {
+        "metric": "GDN/KDA chunk-fwd tokens/s (H=16,d=128,8K varlen); % of HBM/MFMA roofline",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16 inputs; fp16 MFMA operands, fp32 accumulation and state"
+        if inp["dtype"] == "bf16" else "fp32",
+        "data": "synthetic (seeded, resident in HBM)",
+        "config": {"workload": desc, "mode": "graph-replay of meta+map+reduce",
+                   "tokens": tokens, "heads": H, "d": dk, "sequences": N, "nt_max": b.NT,
+                   "dv_split": split, "seg_len": seg},
+        "roofline": roof,
+        "op_roofline": {
+            "alg_bytes": op_bytes, "alg_flops": op_flops,
+            "hbm_frac": round(op_bytes / (ev_mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "mfma_frac": round(op_flops / (ev_mean * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
+        "kernels": diag,
+        "eager_live_ms": round(eager_ms, 5), "capture_ms": round(capture_ms, 3),
+        "replay_p50_ms": round(p50, 5), "replay_p95_ms": round(p95, 5),
+        "kernels_per_step": 3 if seg == 0 else 5,
+        "host_launches_per_step": {"eager": 3 if seg == 0 else 5, "graph": 1},
+        "chunk_utilisation": round(nt_actual / b.NT, 4),
+        "token_utilisation": round(tokens / T, 4),
+        "workspace_bytes": int(b.ws.numel()),
+        "graph_equals_eager": graph_eq,
+        "env": env_record(torch),
+    }
+    if not args.no_protocol:
+        out["protocol"] = timing_protocol(args, torch, la, inp, src, dev, p50)
+        mem = torch.cuda.max_memory_allocated(dev)
+        out["protocol"]["peak_allocated_bytes"] = int(mem)
+    if args.workload == "c1" and not args.no_bucket:
+        out["bucket_c3"] = bucket_leg(args, torch, la, dev)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(inp)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -574,6 +924,10 @@ def main():
     ap.add_argument("--seg-len", type=int, default=0,
                     help="chunks per segment of the reduce (0 auto, -1 one pass per sequence)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-protocol", action="store_true",
+                    help="skip the eager-fixed / graph-update-replay / break-even timings")
+    ap.add_argument("--no-bucket", action="store_true",
+                    help="skip the bucket (20-layout) leg of the default workload")
     ap.add_argument("--layouts", type=int, default=20, help="bucket layouts (c3 only)")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="only run a plain device copy of this many MiB (counter calibration)")
@@ -615,152 +969,7 @@ def main():
         bench_bwd(args, torch, la, synth, dev)
         return
 
-    cfg, kda, desc = WORKLOADS[args.workload]
-    T_arg = 2048 if args.workload.endswith("_short") else None
-    inp = synth.config(cfg, kda=kda, T=T_arg) if cfg == 4 else synth.config(cfg)
-    T = inp["q"].shape[0]
-    H, dk, dv = inp["H"], inp["dk"], inp["dv"]
-    tdt = torch.bfloat16 if inp["dtype"] == "bf16" else torch.float32
-    q = torch.from_numpy(inp["q"]).to(dev, tdt)
-    k = torch.from_numpy(inp["k"]).to(dev, tdt)
-    v = torch.from_numpy(inp["v"]).to(dev, tdt)
-    g = torch.from_numpy(inp["g"]).to(dev)
-    beta = torch.from_numpy(inp["beta"]).to(dev)
-    cu = torch.from_numpy(inp["cu_seqlens"].astype(np.int32)).to(dev)
-    N = cu.numel() - 1
-    h0 = None if inp["h0"] is None else torch.from_numpy(inp["h0"]).to(dev)
-    NT = la.nt_max(T, N)
-    ci = torch.empty((NT, 2), dtype=torch.int32, device=dev)
-    co = torch.empty((N + 1,), dtype=torch.int32, device=dev)
-    st = torch.empty((1,), dtype=torch.int32, device=dev)
-    o = torch.empty((T, H, dv), dtype=torch.float32, device=dev)
-    ht = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
-    ws = torch.empty((la.workspace_bytes(T, N, H, dk, dv, tdt, bool(inp["kda"]),
-                                         seg_len=args.seg_len),),
-                     dtype=torch.uint8, device=dev)
-    fwd_kw = dict(h0=h0, o=o, ht=ht, workspace=ws, dv_split=args.dv_split, seg_len=args.seg_len)
-    split = la.dv_split_for(T, N, H, dk, dv, tdt, args.dv_split, seg_len=args.seg_len)
-    seg = la.seg_len_for(T, N, H, dk, dv, tdt, seg_len=args.seg_len)
-    is_kda = bool(inp["kda"])
-    fwd = la.kda_chunk_fwd if is_kda else la.gdn_chunk_fwd
-
-    def step():
-        la.build_chunk_meta(cu, T, chunk_indices=ci, chunk_offsets=co, status=st)
-        fwd(q, k, v, g, beta, cu, ci, co, **fwd_kw)
-
-    # ---- eager warmup + per-kernel HIP-event timing on the launch stream
-    for _ in range(max(1, args.warmup)):
-        step()
-    torch.cuda.synchronize()
-    assert int(st.item()) == 0
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    for i in range(args.steps):
-        e = evs[i]
-        e[0].record()
-        la.build_chunk_meta(cu, T, chunk_indices=ci, chunk_offsets=co, status=st)
-        e[1].record()
-        la.chunk_fwd_stages(is_kda, la.STAGE_MAP, q, k, v, g, beta, cu, ci, co, **fwd_kw)
-        e[2].record()
-        la.chunk_fwd_stages(is_kda, la.STAGE_REDUCE, q, k, v, g, beta, cu, ci, co, **fwd_kw)
-        e[3].record()
-    torch.cuda.synchronize()
-    per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])  # ms
-    t_meta, t_map, t_red = (float(x) for x in per.mean(axis=0))
-    eager_o = o.clone()
-    eager_ht = ht.clone()
-
-    # eager whole-step timing (no events between kernels)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    # ---- graph capture of one step, replay timing
-    s = torch.cuda.Stream()
-    s.wait_stream(torch.cuda.current_stream())
-    with torch.cuda.stream(s):
-        step()
-    torch.cuda.current_stream().wait_stream(s)
-    torch.cuda.synchronize()
-    graph = torch.cuda.CUDAGraph()
-    tc = time.perf_counter()
-    with torch.cuda.graph(graph):
-        step()
-    torch.cuda.synchronize()
-    capture_ms = (time.perf_counter() - tc) * 1e3
-    for _ in range(args.warmup):
-        graph.replay()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        graph.replay()
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms = elapsed * 1e3 / args.steps
-    # per-replay event pairs on the replay stream, for the p50 / p95 of one step
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps)]
-    for i in range(args.steps):
-        evs[2 * i].record()
-        graph.replay()
-        evs[2 * i + 1].record()
-    torch.cuda.synchronize()
-    rep = np.array([evs[2 * i].elapsed_time(evs[2 * i + 1]) for i in range(args.steps)])
-    graph_eq = bool(torch.equal(o, eager_o) and torch.equal(ht, eager_ht))
-
-    tokens = int(inp["cu_seqlens"][-1])
-    value = tokens * args.steps / elapsed
-    nt_actual = int(np.ceil(np.diff(np.asarray(inp["cu_seqlens"])) / 64).sum())
-
-    kernels = {"meta": t_meta, "map": t_map, "reduce": t_red}
-    dom = "reduce" if t_red >= t_map else "map"
-    dom_ms = kernels[dom]
-    ab = alg_bytes(inp, dom)
-    achieved = ab / (dom_ms * 1e-3) / 1e9
-    # per-launch counters describe one kernel; the segmented reduce stage is
-    # three launches of two kernels
-    traffic = load_traffic(dom, args.workload) if not (dom == "reduce" and seg) else None
-    op_bytes = alg_bytes(inp, "op")
-    op_flops = alg_flops(inp)
-    roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": (f"chunk_reduce_kernel (d_v split {split})" if seg == 0 else
-                       f"reduce stage: chunk_reduce_kernel x2 + chunk_combine_kernel "
-                       f"(segments of {seg} chunks, d_v split {split})")
-            if dom == "reduce" else "chunk_map_kernel",
-            "alg_bytes_per_launch": ab, "avg_launch_ms": round(dom_ms, 5)}
-
-    out = {
-        "metric": "GDN/KDA chunk-fwd tokens/s (H=16,d=128,8K varlen); % of HBM/MFMA roofline",
-        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None,
-        "dtype": "bf16 inputs; fp16 MFMA operands, fp32 accumulation and state"
-        if inp["dtype"] == "bf16" else "fp32",
-        "data": "synthetic (seeded, resident in HBM)",
-        "config": {"workload": desc, "mode": "graph-replay of meta+map+reduce",
-                   "tokens": tokens, "heads": H, "d": dk, "sequences": N, "nt_max": NT,
-                   "dv_split": split, "seg_len": seg},
-        "roofline": roof,
-        "op_roofline": {
-            "alg_bytes": op_bytes, "alg_flops": op_flops,
-            "hbm_frac": round(op_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "mfma_frac": round(op_flops / (ms * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
-        "kernels_ms": {k2: round(v2, 5) for k2, v2 in kernels.items()},
-        "eager_ms_per_step": round(eager_ms, 5), "capture_ms": round(capture_ms, 3),
-        "replay_p50_ms": round(float(np.median(rep)), 5),
-        "replay_p95_ms": round(float(np.percentile(rep, 95)), 5),
-        "kernels_per_step": 3 if seg == 0 else 5,
-        "chunk_utilisation": round(nt_actual / NT, 4),
-        "token_utilisation": round(tokens / T, 4),
-        "workspace_bytes": int(ws.numel()),
-        "graph_equals_eager": graph_eq,
-    }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp)
-    print(json.dumps(out), flush=True)
+    bench_forward(args, torch, la, synth, dev)
 
 
 if __name__ == "__main__":
