@@ -26,7 +26,8 @@ import torch
 
 __all__ = [
     "LinAttnError", "lib", "nt_max", "build_chunk_meta", "workspace_bytes",
-    "gdn_chunk_fwd", "kda_chunk_fwd", "chunk_fwd_stages", "dv_split_for", "seg_len_for",
+    "gdn_chunk_fwd", "kda_chunk_fwd", "chunk_fwd_stages", "chunk_fwd_static", "dv_split_for",
+    "seg_len_for",
     "gdn_recurrent_fwd", "kda_recurrent_fwd", "short_conv_fwd", "gdn_chunk_bwd", "kda_chunk_bwd",
     "bwd_workspace_bytes", "fork_join_events",
     "STAGE_MAP", "STAGE_REDUCE", "META_BAD_START", "META_NOT_MONOTONE",
@@ -133,6 +134,8 @@ def lib():
             f.argtypes = [P, ctypes.c_void_p]
         L.la_chunk_fwd_stages.restype = ctypes.c_int
         L.la_chunk_fwd_stages.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+        L.la_chunk_fwd_static.restype = ctypes.c_int
+        L.la_chunk_fwd_static.argtypes = [P, ctypes.c_int, ctypes.c_void_p]
         L.la_chunk_fwd_dv_split.restype = ctypes.c_int32
         L.la_chunk_fwd_dv_split.argtypes = [P]
         L.la_chunk_fwd_seg_len.restype = ctypes.c_int32
@@ -369,6 +372,22 @@ def chunk_fwd_stages(kda, stages, q, k, v, g, beta, cu_seqlens, chunk_indices, c
     """Run STAGE_MAP and/or STAGE_REDUCE of the forward (la_chunk_fwd_stages)."""
     return _call("la_chunk_fwd_stages", bool(kda), stages, q, k, v, g, beta, cu_seqlens,
                  chunk_indices, chunk_offsets, **kw)
+
+
+def chunk_fwd_static(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, *,
+                     h0=None, o=None, ht=None, output_final_state=True, scale=1.0, dv_split=0,
+                     seg_len=0, o_dtype=None, BT=64, stream=None):
+    """The forward with the library's static device scratch as its workspace
+    (la_chunk_fwd_static): for callers that cannot allocate device memory
+    during the call.  Pass o (and ht) to allocate nothing here either.
+    Calls that overlap on one GPU share that scratch and race."""
+    a, o, ht, _ = _prepare(bool(kda), q, k, v, g, beta, cu_seqlens, chunk_indices,
+                           chunk_offsets, h0, o, ht, output_final_state, None, scale, dv_split,
+                           seg_len, o_dtype, BT, static=True)
+    rc = lib().la_chunk_fwd_static(ctypes.byref(a), int(bool(kda)), _stream(stream))
+    if rc != 0:
+        raise LinAttnError(rc, "la_chunk_fwd_static")
+    return o, ht
 
 
 def _recurrent(name, kda, q, k, v, g, beta, h0=None, o=None, ht=None, output_final_state=True,

@@ -5,6 +5,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <mutex>
+
 #include "kernels.h"
 
 namespace {
@@ -286,6 +288,54 @@ int la_chunk_fwd_stages(const la_chunk_fwd_args *a, int is_kda, int stages, void
   return forward(a, is_kda != 0, stages, stream);
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward: the workspace is this static device array, one
+// copy per GPU the library runs on (held until the process ends).  In host
+// code `scratch` names a host-side stand-in, never the device memory: its
+// device address is looked up once per device (hipGetSymbolAddress, with
+// that device current) and only that address is handed to kernels.
+namespace {
+static __device__ __align__(256) char scratch[LA_STATIC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+// the current device's scratch address, nullptr if it cannot be found
+void *scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+extern "C" {
+
+int la_chunk_fwd_static(const la_chunk_fwd_args *a, int is_kda, void *stream) {
+  if (!a) return LA_ERR_NULL;
+  const int sc = check_shape(a);
+  if (sc != LA_OK) return sc;
+  // the largest workspace the array holds: larger shapes are rejected before
+  // anything is looked up or enqueued
+  if (ws_bytes(a, is_kda != 0) > LA_STATIC_SCRATCH_BYTES) return LA_ERR_WORKSPACE;
+  void *ws = scratch_ptr();
+  if (!ws) return LA_ERR_HIP;
+  la_chunk_fwd_args b = *a;
+  b.workspace = ws;
+  b.workspace_bytes = LA_STATIC_SCRATCH_BYTES;
+  return forward(&b, is_kda != 0, LA_STAGE_MAP | LA_STAGE_REDUCE, stream);
+}
 
 int32_t la_chunk_fwd_dv_split(const la_chunk_fwd_args *a) {
   if (!a || check_shape(a) != LA_OK) return 0;

@@ -191,6 +191,27 @@ int kda_chunk_fwd(const la_chunk_fwd_args *a, void *stream);
 int la_chunk_fwd_stages(const la_chunk_fwd_args *a, int is_kda, int stages,
                         void *stream);
 
+/*
+ * For callers that cannot allocate -- code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc: gdn_chunk_fwd (is_kda = 0)
+ * or kda_chunk_fwd (is_kda = 1) with the library's own static device array of
+ * LA_STATIC_SCRATCH_BYTES bytes as the workspace; a->workspace and
+ * a->workspace_bytes are ignored, every other argument and result is as for
+ * those calls (same kernels, bit-identical outputs).  A shape whose workspace
+ * (la_chunk_fwd_workspace_bytes) exceeds LA_STATIC_SCRATCH_BYTES returns
+ * LA_ERR_WORKSPACE before anything is enqueued.  The array exists once per
+ * GPU the library runs on and is held until the process ends; the call
+ * allocates nothing (its first call on a device looks up that device's copy,
+ * with the device current).  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU -- on two streams, from two threads, or as
+ * graphs replayed concurrently -- race and give wrong results; calls ordered
+ * on one stream do not.  Nothing in the array needs to start at zero.
+ * Host errors: as gdn_chunk_fwd, and LA_ERR_HIP if the array's device
+ * address cannot be found.
+ */
+#define LA_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
+int la_chunk_fwd_static(const la_chunk_fwd_args *a, int is_kda, void *stream);
+
 /* The dv_split the forward uses for these arguments (after "auto").  Run
  * segmented, auto takes 32-column slices while the first pass has at most
  * 512 workgroups with them (2 per CU), else 64-column slices. */
