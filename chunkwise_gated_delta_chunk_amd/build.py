@@ -9,7 +9,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "liblinattn.so")
-SOURCES = ["meta.hip", "chunk_map.hip", "chunk_reduce.hip", "chunk_combine.hip", "recurrent.hip",
+SOURCES = ["meta.hip", "chunk_map.hip", "chunk_reduce.hip", "chunk_reduce16.hip", "chunk_combine.hip",
+           "recurrent.hip",
            "short_conv.hip", "chunk_bwd.hip", "chunk_bwd_kda.hip",
            "linattn.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -16,7 +16,9 @@
 // Written to the workspace for the reduce, per (slot, head), as one image
 // (image_layout in la_device.h: swizzled 16-byte pieces, ready to be copied
 // into LDS verbatim):
-//   K, Q  in the operand element type, key index in chained order
+//   K, Q  in the operand element type, key index in chained order (KDA and
+//         fp32 inputs only: with 16-bit inputs the GDN reduce stages them
+//         itself from the raw rows, and the stored image starts at Tn)
 //   Tn  = T with its diagonal (beta) removed -- the reduce applies beta in fp32
 //   M
 //   vec = [exp(G_r) | exp(G_C - G_r) | beta_r | per-key-row state decay]
@@ -109,7 +111,10 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   constexpr int PK = DK * E / 16, PT = kBT * E / 16;  // 16-byte pieces per row
   constexpr int CH = 16 / E;                          // elements per piece
   const size_t unit = (size_t)slot * H + h;
-  char *img = static_cast<char *>(p.img) + unit * I.BYTES;
+  // the stored part of the image starts at I.TN for 16-bit GDN (the reduce
+  // stages K and Q from the raw rows): region offsets are relative to img
+  constexpr int SKIP = image_skip(KDA, E, DK);
+  char *img = static_cast<char *>(p.img) + unit * (size_t)image_hbm_bytes(KDA, E, DK) - SKIP;
   float *vec = reinterpret_cast<float *>(img + I.VEC);
   // 16 bytes of v[0..CH) -> piece `piece` of row `row` of an image tile
   auto put = [&](int region, int P, int row, int piece, const T *v) {
@@ -200,7 +205,7 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
         *reinterpret_cast<u32x4 *>(sK + r * LDK + piece * VEC) = *reinterpret_cast<const u32x4 *>(kv[j]);
         *reinterpret_cast<u32x4 *>(sQ + r * LDK + piece * VEC) = *reinterpret_cast<const u32x4 *>(qv[j]);
       }
-      if constexpr (!KDA) {  // the reduce's K and Q operands, chained order
+      if constexpr (!KDA && SKIP == 0) {  // the reduce's K and Q operands, chained order
         if constexpr (VEC == 8) {
           const int cp = 4 * (pi >> 1) + 2 * (pi & 1);
           T lo[8], hi[8];

@@ -24,6 +24,9 @@ struct MapParams {
 
 struct ReduceParams {
   const void *v;
+  // 16-bit GDN: the raw q, k rows ([T][Hqk][d_k]), staged by the reduce itself
+  const void *q_raw, *k_raw;
+  int Hqk;
   const void *cu_seqlens;  // int32, or int64 with cu64
   const int32_t *chunk_offsets;
   int cu64;
@@ -126,6 +129,9 @@ hipError_t launch_chunk_map(const MapParams &p, bool kda, int dt, int dk, hipStr
 // W = d_v / S columns per workgroup: 32 per wave
 hipError_t launch_chunk_reduce(const ReduceParams &p, bool kda, int dt, int dk, int W,
                                hipStream_t st);
+// 16-bit inputs (bf16, fp16): W = 32 (or 64 for GDN) columns per workgroup
+hipError_t launch_chunk_reduce16(const ReduceParams &p, bool kda, int dt, int dk, int W,
+                                 hipStream_t st);
 hipError_t launch_chunk_combine(const CombineParams &p, int dk, hipStream_t st);
 hipError_t launch_recurrent(const RecurrentParams &p, bool kda, int dt, int dk, hipStream_t st);
 // stage 1: prep; stage 2: the reverse pass (both need only q, k, g, beta,

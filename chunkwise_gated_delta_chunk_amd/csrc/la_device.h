@@ -235,6 +235,18 @@ __device__ __host__ constexpr ImageLayout image_layout(bool kda, int e, int dk) 
   return L;
 }
 
+// What of a cell's image the map stores in the workspace.  For GDN with
+// 16-bit inputs the reduce stages K and Q itself from the raw q, k rows, so
+// the stored image is the part from TN on (TN, MM, VEC); otherwise it is the
+// whole image.  image_skip is the byte offset of the stored part inside the
+// image layout, image_hbm_bytes its size per cell.
+__device__ __host__ constexpr int image_skip(bool kda, int e, int dk) {
+  return (!kda && e == 2) ? image_layout(kda, e, dk).TN : 0;
+}
+__device__ __host__ constexpr int image_hbm_bytes(bool kda, int e, int dk) {
+  return image_layout(kda, e, dk).BYTES - image_skip(kda, e, dk);
+}
+
 typedef __attribute__((address_space(3))) void *lds_ptr_t;
 // fp32 -> bf16 bits, round to nearest even (NaN stays a quiet NaN)
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {

@@ -55,13 +55,28 @@ int check_shape(const la_chunk_fwd_args *a) {
 
 int split_for(const la_chunk_fwd_args *a) {
   if (a->dv_split) return a->dv_split;
-  // 64 state columns per workgroup (four compute waves); when that leaves at
-  // most one workgroup per CU, 32 columns (two compute waves), which run a
-  // chunk faster: the sequences' serial chains then bound the time, not the
-  // total work
+  // 16-bit inputs: 32 state columns per workgroup (one chain wave, one
+  // output wave, two copy waves)
+  if (a->qkv_dtype != LA_F32) return a->d_v / 32;
+  // fp32 inputs: 64 state columns per workgroup (four compute waves); when
+  // that leaves at most one workgroup per CU, 32 columns (two compute waves)
   const int s = a->d_v / 64 > 0 ? a->d_v / 64 : 1;
   if ((int64_t)a->N_max * a->H * s <= kCUs && a->d_v / (2 * s) >= 32) return 2 * s;
   return s;
+}
+
+// columns per workgroup the reduce kernels are built for
+bool split_supported(const la_chunk_fwd_args *a, int S) {
+  const int W = a->d_v / S;
+  if (a->qkv_dtype == LA_F32) return W == 32 || W == 64;
+  return W == 32;
+}
+
+hipError_t launch_reduce(const la::ReduceParams &rp, const la_chunk_fwd_args *a, bool kda,
+                         hipStream_t st) {
+  const int W = a->d_v / rp.S;
+  if (a->qkv_dtype == LA_F32) return la::launch_chunk_reduce(rp, kda, a->qkv_dtype, a->d_k, W, st);
+  return la::launch_chunk_reduce16(rp, kda, a->qkv_dtype, a->d_k, W, st);
 }
 
 size_t elem_bytes(const la_chunk_fwd_args *a) { return a->qkv_dtype == LA_F32 ? 4 : 2; }
@@ -84,21 +99,6 @@ int seg_for(const la_chunk_fwd_args *a) {
   return (int)L;
 }
 
-// d_v slices of the segmented passes unless dv_split is given: 32 columns
-// (two compute waves, a faster chunk) while the first pass then has at most
-// two workgroups per CU (d_v / 32 output or D slices and d_k / 32 P slices
-// per segment and head), else 64 (the passes are throughput-bound)
-int seg_split(const la_chunk_fwd_args *a) {
-  if (a->dv_split) return a->dv_split;
-  const int L = seg_for(a);
-  if (L > 0) {
-    const int64_t nt = la_nt_max(a->T_max, a->N_max, kBTk);
-    const int64_t narrow = (nt + L - 1) / L * a->H * (a->d_v / 32 + a->d_k / 32);
-    if (narrow <= 2 * kCUs) return a->d_v / 32;
-  }
-  return a->d_v / 64 > 0 ? a->d_v / 64 : 1;
-}
-
 // segment slots: ceil(T_max / (BT L)) + N_max - 1
 int64_t ns_max(const la_chunk_fwd_args *a, int L) {
   return ((int64_t)a->T_max + (int64_t)kBTk * L - 1) / ((int64_t)kBTk * L) + a->N_max - 1;
@@ -109,7 +109,7 @@ int64_t ns_max(const la_chunk_fwd_args *a, int L) {
 // images (2 x [d_k][d_k] fp16) per (segment slot, head)
 size_t ws_img_bytes(const la_chunk_fwd_args *a, bool kda) {
   const size_t cells = (size_t)la_nt_max(a->T_max, a->N_max, kBTk) * a->H;
-  return cells * (size_t)la::image_layout(kda, (int)elem_bytes(a), a->d_k).BYTES;
+  return cells * (size_t)la::image_hbm_bytes(kda, (int)elem_bytes(a), a->d_k);
 }
 size_t ws_seg_bytes(const la_chunk_fwd_args *a) {
   const int L = seg_for(a);
@@ -165,6 +165,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
   if (mis % 16 != 0) return LA_ERR_SHAPE;
 
   const int dt = a->qkv_dtype;
+  if (!split_supported(a, split_for(a))) return LA_ERR_UNSUPPORTED;
   char *ws = static_cast<char *>(a->workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   Meta meta;
@@ -188,6 +189,9 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
   if (stages & LA_STAGE_REDUCE) {
     la::ReduceParams rp{};
     rp.v = a->v;
+    rp.q_raw = a->q;
+    rp.k_raw = a->k;
+    rp.Hqk = a->H_qk ? a->H_qk : a->H;
     rp.cu_seqlens = a->cu_seqlens;
     rp.cu64 = a->cu_seqlens_i64;
     rp.chunk_offsets = meta.co;
@@ -202,12 +206,8 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     rp.o_bf16 = a->o_bf16;
     const int L = seg_for(a);
     if (L == 0) {
-      if (la::launch_chunk_reduce(rp, kda, dt, a->d_k, a->d_v / rp.S, st) != hipSuccess)
-        return LA_ERR_HIP;
+      if (launch_reduce(rp, a, kda, st) != hipSuccess) return LA_ERR_HIP;
     } else {
-      // segments: 64 columns per workgroup unless asked otherwise (the passes
-      // are throughput-bound)
-      rp.S = seg_split(a);
       rp.SP = a->d_k / (a->d_v / rp.S);
       rp.seg = L;
       rp.NS_max = (int)ns_max(a, L);
@@ -216,8 +216,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
       rp.dlt = rp.hin + mat;
       rp.pimg = reinterpret_cast<_Float16 *>(rp.dlt + mat);
       rp.pass = 1;
-      if (la::launch_chunk_reduce(rp, kda, dt, a->d_k, a->d_v / rp.S, st) != hipSuccess)
-        return LA_ERR_HIP;
+      if (launch_reduce(rp, a, kda, st) != hipSuccess) return LA_ERR_HIP;
       la::CombineParams cp{};
       cp.chunk_offsets = meta.co;
       cp.H = a->H;
@@ -228,8 +227,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
       cp.pimg = rp.pimg;
       if (la::launch_chunk_combine(cp, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
       rp.pass = 2;
-      if (la::launch_chunk_reduce(rp, kda, dt, a->d_k, a->d_v / rp.S, st) != hipSuccess)
-        return LA_ERR_HIP;
+      if (launch_reduce(rp, a, kda, st) != hipSuccess) return LA_ERR_HIP;
     }
   }
   return LA_OK;
@@ -339,7 +337,7 @@ int la_chunk_fwd_static(const la_chunk_fwd_args *a, int is_kda, void *stream) {
 
 int32_t la_chunk_fwd_dv_split(const la_chunk_fwd_args *a) {
   if (!a || check_shape(a) != LA_OK) return 0;
-  return seg_for(a) ? seg_split(a) : split_for(a);
+  return split_for(a);
 }
 
 int32_t la_chunk_fwd_seg_len(const la_chunk_fwd_args *a) {
@@ -595,10 +593,14 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
     rp.img = ws;
     rp.H = a->H;
     rp.N_max = a->N_max;
+    rp.q_raw = a->q;
+    rp.k_raw = a->k;
+    rp.Hqk = a->H_qk ? a->H_qk : a->H;
     rp.S = split_for(&f);
+    if (a->qkv_dtype != LA_F32) rp.S = a->d_v / 32;
     rp.scale = a->scale;
     rp.hsave = reinterpret_cast<float *>(ws + L.hs);
-    ok = la::launch_chunk_reduce(rp, kda, a->qkv_dtype, a->d_k, a->d_v / rp.S, st) == hipSuccess;
+    ok = launch_reduce(rp, &f, kda, st) == hipSuccess;
   }
   // the join is recorded even after a failed launch, so a capture of
   // `stream` never holds an unjoined fork

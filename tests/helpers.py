@@ -135,6 +135,10 @@ def image_layout(kda, esz, d):
     L["VEC"] = L["MM"] + 64 * 64 * esz
     L["BYTES"] = L["VEC"] + -(-(192 + d) * 4 // 1024) * 1024
     L["has_kt"] = has_kt
+    # what the workspace stores per cell: 16-bit GDN from TN on (its reduce
+    # stages K and Q from the raw rows), otherwise the whole image
+    L["SKIP"] = L["TN"] if (not kda and esz == 2) else 0
+    L["HBM"] = L["BYTES"] - L["SKIP"]
     return L
 
 
@@ -156,15 +160,19 @@ def untile(cell, off, rows, cols, esz):
 def decode_images(ws, NT, H, d, kda, esz):
     """Every cell of a workspace (torch uint8 tensor) as dict of logical arrays."""
     L = image_layout(kda, esz, d)
-    raw = ws[:NT * H * L["BYTES"]].cpu().numpy().reshape(NT, H, L["BYTES"])
+    raw = ws[:NT * H * L["HBM"]].cpu().numpy().reshape(NT, H, L["HBM"])
+    sk = L["SKIP"]
     out = {}
     for slot in range(NT):
         for h in range(H):
             cell = np.ascontiguousarray(raw[slot, h])
-            rec = {"K": untile(cell, L["K"], 64, d, esz), "Q": untile(cell, L["Q"], 64, d, esz),
-                   "TN": untile(cell, L["TN"], 64, 64, esz),
-                   "MM": untile(cell, L["MM"], 64, 64, esz),
-                   "VEC": cell[L["VEC"]:L["VEC"] + (192 + d) * 4].view(np.float32).astype(np.float64)}
+            rec = {"TN": untile(cell, L["TN"] - sk, 64, 64, esz),
+                   "MM": untile(cell, L["MM"] - sk, 64, 64, esz),
+                   "VEC": cell[L["VEC"] - sk:L["VEC"] - sk + (192 + d) * 4].view(np.float32)
+                   .astype(np.float64)}
+            if sk == 0:
+                rec["K"] = untile(cell, L["K"], 64, d, esz)
+                rec["Q"] = untile(cell, L["Q"], 64, d, esz)
             if L["has_kt"]:
                 rec["KT"] = untile(cell, L["KT"], d, 64, esz)
             out[(slot, h)] = rec

@@ -73,6 +73,7 @@ BAD = [
     ("dv_split 3", dict(dv_split=3), -4),
     ("dv_split 8", dict(dv_split=8), -4),
     ("dv_split too fine", dict(dv_split=4), -4),
+    ("16-bit 64 columns", dict(qkv_dtype=0, d_k=128, d_v=128, dv_split=2), -4),
     ("no workspace", dict(workspace=None), -5),
     ("workspace small", dict(workspace_bytes=100), -5),
     ("workspace misaligned", dict(workspace=0x100010), -5),
@@ -125,22 +126,24 @@ def test_workspace_size_and_split():
                                   (256, 1, 2, 64, torch.float32, 4),
                                   (16384, 64, 32, 128, torch.bfloat16, 2)]:
         cells = meta_ref.nt_max(T, N, 64) * H
-        # one image per cell: K, Q, [K^T: KDA or fp32], Tn, M, vec padded to 1 KiB
+        # one image per cell: K, Q, [K^T: KDA or fp32], Tn, M, vec padded to
+        # 1 KiB; 16-bit GDN stores no K and Q (its reduce stages them itself)
         vec = -(-(192 + d) * 4 // 1024) * 1024
         kt = 64 * d * esz
-        gdn = 2 * 64 * d * esz + (kt if esz == 4 else 0) + 2 * 64 * 64 * esz + vec
+        gdn = (2 * 64 * d * esz if esz == 4 else 0) + (kt if esz == 4 else 0) + \
+            2 * 64 * 64 * esz + vec
         assert la.workspace_bytes(T, N, H, d, d, dt) == cells * gdn
         kda = 2 * 64 * d * esz + kt + 2 * 64 * 64 * esz + vec
         assert la.workspace_bytes(T, N, H, d, d, dt, kda=True) == cells * kda
     assert la.workspace_bytes(0, 1, 1, 64, 64, torch.bfloat16) == 0
-    # 64 columns per workgroup, 32 when that leaves at most one workgroup per
-    # CU (256 of them)
+    # 16-bit inputs: 32 columns per workgroup
     assert la.dv_split_for(8192, 8, 16, 128, 128, torch.bfloat16) == 4
-    assert la.dv_split_for(8192, 8, 17, 128, 128, torch.bfloat16) == 2
-    assert la.dv_split_for(16384, 64, 32, 128, 128, torch.bfloat16) == 2
+    assert la.dv_split_for(8192, 8, 17, 128, 128, torch.bfloat16) == 4
+    assert la.dv_split_for(16384, 64, 32, 128, 128, torch.bfloat16) == 4
     assert la.dv_split_for(65536, 1, 10, 128, 128, torch.bfloat16, seg_len=-1) == 4
-    # segmented: 64-column slices (13 x 10 x 8 = 1040 workgroups at 32)
-    assert la.dv_split_for(65536, 1, 10, 128, 128, torch.bfloat16) == 2
+    assert la.dv_split_for(65536, 1, 10, 128, 128, torch.bfloat16) == 4
+    assert la.dv_split_for(4096, 1, 2, 64, 64, torch.bfloat16) == 2
+    # fp32 inputs: 64 columns, 32 when that leaves at most one workgroup per CU
     assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32) == 2
     assert la.dv_split_for(4096, 512, 2, 64, 64, torch.float32) == 1
     assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32, dv_split=1) == 1
@@ -160,9 +163,9 @@ def test_segment_length_choice():
     assert la.seg_len_for(8192, 8, 16, 128, 128, bf) == 0        # 256 units: plain
     assert la.seg_len_for(16384, 64, 32, 128, 128, bf) == 0
     assert la.seg_len_for(512, 1, 2, 128, 128, bf) == 0          # 8 chunks < 3 segments
-    # segmented slices: 32 columns while the first pass has <= 512 workgroups
-    assert la.dv_split_for(2048, 1, 10, 128, 128, bf) == 4       # 4 x 10 x 8 = 320
-    assert la.dv_split_for(4096, 1, 16, 128, 128, bf) == 2       # 8 x 16 x 8 = 1024
+    # segmented slices of 16-bit inputs: 32 columns
+    assert la.dv_split_for(2048, 1, 10, 128, 128, bf) == 4
+    assert la.dv_split_for(4096, 1, 16, 128, 128, bf) == 4
     assert la.seg_len_for(65536, 1, 10, 64, 64, f32) == 0        # fp32: plain
     assert la.seg_len_for(65536, 1, 10, 128, 128, bf, seg_len=-1) == 0
     assert la.seg_len_for(4096, 3, 2, 128, 128, bf, seg_len=5) == 5
