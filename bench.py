@@ -57,12 +57,11 @@ WORKLOADS = {
                          "BT=64 chunk metadata built once, seed 7"),
 }
 
-KERNEL_SOURCES = ["la_device.h", "kernels.h", "chunk_map.hip", "chunk_reduce.hip", "meta.hip"]
-
-
-def kernel_source_hash(name):
+def kernel_source_hash(files):
+    """Hash of the shared device headers plus ``files`` (a name or a list)."""
     h = hashlib.sha256()
-    for f in ["la_device.h", "kernels.h", name]:
+    files = [files] if isinstance(files, str) else list(files)
+    for f in ["la_device.h", "kernels.h"] + files:
         with open(os.path.join(ROOT, "chunkwise_gated_delta_chunk_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -76,8 +75,9 @@ def alg_bytes(inp, kind):
     figure the headline roofline divides by the step time.
     Per kernel (diagnostics), the part of those bytes a kernel has to touch
     itself: the map reads q, k, g and beta; the reduce reads v (and h0) and
-    writes o (and ht) -- it takes the chunk matrices and the staged keys and
-    queries from the map's workspace images, which are implementation
+    writes o (and ht), and with 16-bit GDN inputs it reads the q and k rows
+    too -- it takes the chunk matrices (and otherwise the staged keys and
+    queries) from the map's workspace images, which are implementation
     overhead and not counted."""
     T = int(inp["cu_seqlens"][-1])
     H, dk, dv = inp["H"], inp["dk"], inp["dv"]
@@ -91,7 +91,8 @@ def alg_bytes(inp, kind):
     if kind == "map":
         return T * H * (2 * dk * s_qkv + s_g + 4)
     if kind == "reduce":
-        return T * H * (dv * s_qkv + 4 * dv) + state
+        qk = 2 * dk * s_qkv if (s_qkv == 2 and not inp["kda"]) else 0
+        return T * H * (qk + dv * s_qkv + 4 * dv) + state
     raise ValueError(kind)
 
 
@@ -105,8 +106,13 @@ def alg_flops(inp):
     return chunks * inp["H"] * per
 
 
-KERNEL_SOURCE = {"reduce": "chunk_reduce.hip", "map": "chunk_map.hip", "recurrent": "recurrent.hip",
-                 "conv": "short_conv.hip"}
+def kernel_sources(kind, inp=None):
+    """The source files (besides the shared headers) of a kernel kind; the
+    reduce of 16-bit inputs has its own file."""
+    if kind == "reduce":
+        sixteen = inp is None or inp["dtype"] != "f32"
+        return ["reduce_work.h", "chunk_reduce16.hip" if sixteen else "chunk_reduce.hip"]
+    return [{"map": "chunk_map.hip", "recurrent": "recurrent.hip", "conv": "short_conv.hip"}[kind]]
 
 # decode workloads: sequences (one token each), heads, head dim
 DECODE_N, DECODE_H, DECODE_D = 64, 16, 128
@@ -119,15 +125,14 @@ def decode_alg_bytes(kda):
     return N * H * (2 * d * d * 4 + 3 * d * 2 + (4 * d if kda else 4) + 4 + 4 * d)
 
 
-def load_traffic(kernel_kind, workload):
+def load_traffic(kernel_kind, workload, inp=None):
     """HBM traffic of the dominant kernel from the committed counter summary, if
     it was taken on the current kernel source; else None."""
     path = os.path.join(ROOT, "profiles", f"traffic_{kernel_kind}_{workload}.json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = KERNEL_SOURCE[kernel_kind]
-    if rec.get("kernel_src_sha") != kernel_source_hash(src):
+    if rec.get("kernel_src_sha") != kernel_source_hash(kernel_sources(kernel_kind, inp)):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -177,7 +182,8 @@ def bench_bucket(args, torch, la, synth, dev):
     st = torch.empty((1,), dtype=torch.int32, device=dev)
     o = torch.empty((T_max, H, d), device=dev)
     ht = torch.empty((N_max, H, d, d), device=dev)
-    ws = torch.empty((la.workspace_bytes(T_max, N_max, H, d, d, bf, False, seg_len=args.seg_len),),
+    ws = torch.empty((la.workspace_bytes(T_max, N_max, H, d, d, bf, False, seg_len=args.seg_len,
+                                         dv_split=args.dv_split),),
                      dtype=torch.uint8, device=dev)
     kw = dict(o=o, ht=ht, workspace=ws, dv_split=args.dv_split, seg_len=args.seg_len)
 
@@ -599,7 +605,8 @@ class FwdBucket:
         self.o = z((T_max, H, dv))
         self.ht = z((N_max, H, dk, dv))
         self.ws = torch.empty((la.workspace_bytes(T_max, N_max, H, dk, dv, tdt, self.kda,
-                                                  seg_len=seg_len),), dtype=torch.uint8, device=dev)
+                                                  seg_len=seg_len, dv_split=dv_split),),
+                              dtype=torch.uint8, device=dev)
         self.kw = dict(h0=self.h0, o=self.o, ht=self.ht, workspace=self.ws, dv_split=dv_split,
                        seg_len=seg_len)
         self.T_max, self.N_max, self.NT = T_max, N_max, NT
@@ -865,7 +872,7 @@ def bench_forward(args, torch, la, synth, dev):
                       "hbm_frac": round(ab / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     # HBM traffic of one step: the sum of every kernel's counter-measured
     # bytes, when all were taken on the current sources (else null)
-    tr = [load_traffic(kind, args.workload) for kind in ("map", "reduce")]
+    tr = [load_traffic(kind, args.workload, inp) for kind in ("map", "reduce")]
     traffic = None if (any(x is None for x in tr) or seg) else float(sum(tr))
     achieved = op_bytes / (ev_mean * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",

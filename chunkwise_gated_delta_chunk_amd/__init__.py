@@ -246,9 +246,11 @@ def _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, dv_split=0, BT=64, seg_len
     return a
 
 
-def workspace_bytes(T_max, N_max, H, d_k, d_v, qkv_dtype, kda=False, BT=64, seg_len=0):
-    """Forward workspace bytes (BT = 32 adds the rebuilt 64-row chunk layout)."""
-    a = _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, BT=BT, seg_len=seg_len)
+def workspace_bytes(T_max, N_max, H, d_k, d_v, qkv_dtype, kda=False, BT=64, seg_len=0,
+                    dv_split=0):
+    """Forward workspace bytes (BT = 32 adds the rebuilt 64-row chunk layout;
+    the images depend on the d_v split)."""
+    a = _shape_args(T_max, N_max, H, d_k, d_v, qkv_dtype, dv_split, BT=BT, seg_len=seg_len)
     return int(lib().la_chunk_fwd_workspace_bytes(ctypes.byref(a), int(kda)))
 
 

@@ -16,9 +16,10 @@
 // Written to the workspace for the reduce, per (slot, head), as one image
 // (image_layout in la_device.h: swizzled 16-byte pieces, ready to be copied
 // into LDS verbatim):
-//   K, Q  in the operand element type, key index in chained order (KDA and
-//         fp32 inputs only: with 16-bit inputs the GDN reduce stages them
-//         itself from the raw rows, and the stored image starts at Tn)
+//   K, Q  in the operand element type, key index in chained order (not for
+//         GDN with RAW set, 16-bit inputs reduced in 32-column slices: that
+//         reduce stages them itself from the raw rows, and the stored image
+//         starts at Tn)
 //   Tn  = T with its diagonal (beta) removed -- the reduce applies beta in fp32
 //   M
 //   vec = [exp(G_r) | exp(G_C - G_r) | beta_r | per-key-row state decay]
@@ -61,7 +62,7 @@ __device__ __forceinline__ int tile_s(int p) { return (0xE4910 >> (2 * p)) & 3; 
 
 using F32 = Op<float>;
 
-template <bool KDA, typename In, int DK>
+template <bool KDA, typename In, int DK, bool RAW>
 __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   using O = Op<In>;
   using T = typename O::T;
@@ -113,8 +114,8 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   const size_t unit = (size_t)slot * H + h;
   // the stored part of the image starts at I.TN for 16-bit GDN (the reduce
   // stages K and Q from the raw rows): region offsets are relative to img
-  constexpr int SKIP = image_skip(KDA, E, DK);
-  char *img = static_cast<char *>(p.img) + unit * (size_t)image_hbm_bytes(KDA, E, DK) - SKIP;
+  constexpr int SKIP = image_skip(KDA, E, DK, RAW);
+  char *img = static_cast<char *>(p.img) + unit * (size_t)image_hbm_bytes(KDA, E, DK, RAW) - SKIP;
   float *vec = reinterpret_cast<float *>(img + I.VEC);
   // 16 bytes of v[0..CH) -> piece `piece` of row `row` of an image tile
   auto put = [&](int region, int P, int row, int piece, const T *v) {
@@ -586,16 +587,23 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
 
 }  // namespace
 
-template <bool KDA, typename In, int DK>
+template <bool KDA, typename In, int DK, bool RAW>
 static hipError_t launch_map_t(const MapParams &p, hipStream_t st) {
-  hipLaunchKernelGGL((chunk_map_kernel<KDA, In, DK>), dim3(p.H * p.NT_max), dim3(kThreads), 0, st, p);
+  hipLaunchKernelGGL((chunk_map_kernel<KDA, In, DK, RAW>), dim3(p.H * p.NT_max), dim3(kThreads), 0, st,
+                     p);
   return hipGetLastError();
+}
+
+template <typename In, int DK>
+static hipError_t launch_map_d(const MapParams &p, bool kda, hipStream_t st) {
+  if (kda) return launch_map_t<true, In, DK, false>(p, st);
+  return p.raw_kq ? launch_map_t<false, In, DK, true>(p, st) : launch_map_t<false, In, DK, false>(p, st);
 }
 
 template <typename In>
 static hipError_t launch_map_16(const MapParams &p, bool kda, int dk, hipStream_t st) {
-  if (dk == 128) return kda ? launch_map_t<true, In, 128>(p, st) : launch_map_t<false, In, 128>(p, st);
-  if (dk == 64) return kda ? launch_map_t<true, In, 64>(p, st) : launch_map_t<false, In, 64>(p, st);
+  if (dk == 128) return launch_map_d<In, 128>(p, kda, st);
+  if (dk == 64) return launch_map_d<In, 64>(p, kda, st);
   return hipErrorInvalidValue;
 }
 
@@ -604,7 +612,7 @@ hipError_t launch_chunk_map(const MapParams &p, bool kda, int dt, int dk, hipStr
   if (dt == LA_F16) return launch_map_16<f16>(p, kda, dk, st);
   // fp32 inputs: d = 64 only (the fp32 d = 128 KDA tiles exceed the 160 KiB LDS)
   if (dt != LA_F32 || dk != 64) return hipErrorInvalidValue;
-  return kda ? launch_map_t<true, float, 64>(p, st) : launch_map_t<false, float, 64>(p, st);
+  return kda ? launch_map_t<true, float, 64, false>(p, st) : launch_map_t<false, float, 64, false>(p, st);
 }
 
 }  // namespace la

@@ -53,8 +53,8 @@ using O16 = Op<bf16>;  // fp16 MFMA operand traits (bf16 and fp16 inputs alike)
 template <bool KDA, int DK, int NCW, int CT>
 struct R16 {
   static constexpr ImageLayout I = image_layout(KDA, 2, DK);  // stage layout from K on
-  static constexpr int SKIP = image_skip(KDA, 2, DK);         // staged from raw q, k rows
-  static constexpr int HBM = image_hbm_bytes(KDA, 2, DK);     // DMA'd from the workspace
+  static constexpr int SKIP = image_skip(KDA, 2, DK, !KDA);   // GDN: staged from raw q, k rows
+  static constexpr int HBM = image_hbm_bytes(KDA, 2, DK, !KDA);  // DMA'd from the workspace
   static constexpr int W = 16 * CT * NCW;                     // state columns
   static constexpr int PV = W * 2 / 16;                       // 16-byte V pieces per row
   static constexpr int V_BYTES = kBT * W * 2;

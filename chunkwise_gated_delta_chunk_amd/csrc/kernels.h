@@ -19,6 +19,7 @@ struct MapParams {
   int cu64;
   int H, NT_max;
   int Hqk;  // q, k heads: value head h reads q, k head h / (H / Hqk)
+  int raw_kq;  // GDN, 16-bit: the reduce stages K and Q itself (no K, Q stored)
   void *img;
 };
 
@@ -126,10 +127,11 @@ hipError_t launch_chunk_meta(const void *cu, int cu64, int N_max, int T_max, int
                              int32_t *ci, int32_t *co, int32_t *status, hipStream_t stream);
 // dt: la_dtype code of q, k, v (LA_BF16, LA_F32, LA_F16)
 hipError_t launch_chunk_map(const MapParams &p, bool kda, int dt, int dk, hipStream_t st);
-// W = d_v / S columns per workgroup: 32 per wave
+// W = d_v / S columns per workgroup (16 per compute wave); full images
 hipError_t launch_chunk_reduce(const ReduceParams &p, bool kda, int dt, int dk, int W,
                                hipStream_t st);
-// 16-bit inputs (bf16, fp16): W = 32 (or 64 for GDN) columns per workgroup
+// 16-bit inputs (bf16, fp16), W = 32 columns per workgroup; GDN stages K and
+// Q from the raw rows (the map's images start at TN)
 hipError_t launch_chunk_reduce16(const ReduceParams &p, bool kda, int dt, int dk, int W,
                                  hipStream_t st);
 hipError_t launch_chunk_combine(const CombineParams &p, int dk, hipStream_t st);

@@ -235,16 +235,16 @@ __device__ __host__ constexpr ImageLayout image_layout(bool kda, int e, int dk) 
   return L;
 }
 
-// What of a cell's image the map stores in the workspace.  For GDN with
-// 16-bit inputs the reduce stages K and Q itself from the raw q, k rows, so
-// the stored image is the part from TN on (TN, MM, VEC); otherwise it is the
-// whole image.  image_skip is the byte offset of the stored part inside the
-// image layout, image_hbm_bytes its size per cell.
-__device__ __host__ constexpr int image_skip(bool kda, int e, int dk) {
-  return (!kda && e == 2) ? image_layout(kda, e, dk).TN : 0;
+// What of a cell's image the map stores in the workspace.  When the reduce
+// stages K and Q itself from the raw q, k rows (raw: GDN with 16-bit inputs
+// and 32-column slices) the stored image is the part from TN on (TN, MM,
+// VEC); otherwise it is the whole image.  image_skip is the byte offset of
+// the stored part inside the image layout, image_hbm_bytes its size per cell.
+__device__ __host__ constexpr int image_skip(bool kda, int e, int dk, bool raw) {
+  return raw ? image_layout(kda, e, dk).TN : 0;
 }
-__device__ __host__ constexpr int image_hbm_bytes(bool kda, int e, int dk) {
-  return image_layout(kda, e, dk).BYTES - image_skip(kda, e, dk);
+__device__ __host__ constexpr int image_hbm_bytes(bool kda, int e, int dk, bool raw) {
+  return image_layout(kda, e, dk).BYTES - image_skip(kda, e, dk, raw);
 }
 
 typedef __attribute__((address_space(3))) void *lds_ptr_t;

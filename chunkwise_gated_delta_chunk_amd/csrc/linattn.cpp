@@ -55,28 +55,25 @@ int check_shape(const la_chunk_fwd_args *a) {
 
 int split_for(const la_chunk_fwd_args *a) {
   if (a->dv_split) return a->dv_split;
-  // 16-bit inputs: 32 state columns per workgroup (one chain wave, one
-  // output wave, two copy waves)
-  if (a->qkv_dtype != LA_F32) return a->d_v / 32;
-  // fp32 inputs: 64 state columns per workgroup (four compute waves); when
-  // that leaves at most one workgroup per CU, 32 columns (two compute waves)
+  // 64 state columns per workgroup; when that leaves at most one workgroup
+  // per CU, 32 columns, which run a chunk faster: the sequences' serial
+  // chains then bound the time, not the total work
   const int s = a->d_v / 64 > 0 ? a->d_v / 64 : 1;
   if ((int64_t)a->N_max * a->H * s <= kCUs && a->d_v / (2 * s) >= 32) return 2 * s;
   return s;
 }
 
-// columns per workgroup the reduce kernels are built for
-bool split_supported(const la_chunk_fwd_args *a, int S) {
-  const int W = a->d_v / S;
-  if (a->qkv_dtype == LA_F32) return W == 32 || W == 64;
-  return W == 32;
+// 16-bit inputs in 32-column slices run the dedicated 16-bit reduce, which
+// for GDN stages K and Q from the raw q, k rows (the map then stores no K, Q)
+bool reduce16(const la_chunk_fwd_args *a, int S) {
+  return a->qkv_dtype != LA_F32 && a->d_v / S == 32;
 }
 
 hipError_t launch_reduce(const la::ReduceParams &rp, const la_chunk_fwd_args *a, bool kda,
                          hipStream_t st) {
   const int W = a->d_v / rp.S;
-  if (a->qkv_dtype == LA_F32) return la::launch_chunk_reduce(rp, kda, a->qkv_dtype, a->d_k, W, st);
-  return la::launch_chunk_reduce16(rp, kda, a->qkv_dtype, a->d_k, W, st);
+  if (reduce16(a, rp.S)) return la::launch_chunk_reduce16(rp, kda, a->qkv_dtype, a->d_k, W, st);
+  return la::launch_chunk_reduce(rp, kda, a->qkv_dtype, a->d_k, W, st);
 }
 
 size_t elem_bytes(const la_chunk_fwd_args *a) { return a->qkv_dtype == LA_F32 ? 4 : 2; }
@@ -99,6 +96,27 @@ int seg_for(const la_chunk_fwd_args *a) {
   return (int)L;
 }
 
+// d_v slices of the segmented passes unless dv_split is given: 32 columns
+// (a faster chunk) while the first pass then has at most two workgroups per
+// CU (d_v / 32 output or D slices and d_k / 32 P slices per segment and
+// head), else 64 (the passes are throughput-bound)
+int seg_split(const la_chunk_fwd_args *a) {
+  if (a->dv_split) return a->dv_split;
+  const int L = seg_for(a);
+  if (L > 0) {
+    const int64_t nt = la_nt_max(a->T_max, a->N_max, kBTk);
+    const int64_t narrow = (nt + L - 1) / L * a->H * (a->d_v / 32 + a->d_k / 32);
+    if (narrow <= 2 * kCUs) return a->d_v / 32;
+  }
+  return a->d_v / 64 > 0 ? a->d_v / 64 : 1;
+}
+
+// the d_v slices of the forward's reduce
+int fwd_split(const la_chunk_fwd_args *a) { return seg_for(a) ? seg_split(a) : split_for(a); }
+
+// whether the map stores no K, Q (the reduce stages them from the raw rows)
+bool raw_kq(const la_chunk_fwd_args *a, bool kda) { return !kda && reduce16(a, fwd_split(a)); }
+
 // segment slots: ceil(T_max / (BT L)) + N_max - 1
 int64_t ns_max(const la_chunk_fwd_args *a, int L) {
   return ((int64_t)a->T_max + (int64_t)kBTk * L - 1) / ((int64_t)kBTk * L) + a->N_max - 1;
@@ -109,7 +127,7 @@ int64_t ns_max(const la_chunk_fwd_args *a, int L) {
 // images (2 x [d_k][d_k] fp16) per (segment slot, head)
 size_t ws_img_bytes(const la_chunk_fwd_args *a, bool kda) {
   const size_t cells = (size_t)la_nt_max(a->T_max, a->N_max, kBTk) * a->H;
-  return cells * (size_t)la::image_hbm_bytes(kda, (int)elem_bytes(a), a->d_k);
+  return cells * (size_t)la::image_hbm_bytes(kda, (int)elem_bytes(a), a->d_k, raw_kq(a, kda));
 }
 size_t ws_seg_bytes(const la_chunk_fwd_args *a) {
   const int L = seg_for(a);
@@ -165,7 +183,6 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
   if (mis % 16 != 0) return LA_ERR_SHAPE;
 
   const int dt = a->qkv_dtype;
-  if (!split_supported(a, split_for(a))) return LA_ERR_UNSUPPORTED;
   char *ws = static_cast<char *>(a->workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   Meta meta;
@@ -183,6 +200,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     mp.H = a->H;
     mp.Hqk = a->H_qk ? a->H_qk : a->H;
     mp.NT_max = (int)la_nt_max(a->T_max, a->N_max, kBTk);
+    mp.raw_kq = raw_kq(a, kda);
     mp.img = ws;
     if (la::launch_chunk_map(mp, kda, dt, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
   }
@@ -201,7 +219,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     rp.img = ws;
     rp.H = a->H;
     rp.N_max = a->N_max;
-    rp.S = split_for(a);
+    rp.S = fwd_split(a);
     rp.scale = a->scale;
     rp.o_bf16 = a->o_bf16;
     const int L = seg_for(a);
@@ -337,7 +355,7 @@ int la_chunk_fwd_static(const la_chunk_fwd_args *a, int is_kda, void *stream) {
 
 int32_t la_chunk_fwd_dv_split(const la_chunk_fwd_args *a) {
   if (!a || check_shape(a) != LA_OK) return 0;
-  return split_for(a);
+  return fwd_split(a);
 }
 
 int32_t la_chunk_fwd_seg_len(const la_chunk_fwd_args *a) {
@@ -445,6 +463,9 @@ static la_chunk_fwd_args fwd_view(const la_chunk_bwd_args *a) {
   f.BT = a->BT;
   f.qkv_dtype = a->qkv_dtype;
   f.seg_len = -1;  // the recompute stores per-chunk states: one pass
+  // 16-bit inputs: 32-column slices (the dedicated 16-bit reduce, which stores
+  // the per-chunk states)
+  f.dv_split = a->qkv_dtype != LA_F32 ? a->d_v / 32 : 0;
   f.cu_seqlens_i64 = a->cu_seqlens_i64;
   f.H_qk = a->H_qk;
   f.scale = a->scale;
@@ -578,6 +599,7 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
     mp.H = a->H;
     mp.Hqk = a->H_qk ? a->H_qk : a->H;
     mp.NT_max = NT;
+    mp.raw_kq = raw_kq(&f, kda);
     mp.img = ws;
     ok = la::launch_chunk_map(mp, kda, a->qkv_dtype, a->d_k, st) == hipSuccess;
   }
@@ -597,7 +619,6 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
     rp.k_raw = a->k;
     rp.Hqk = a->H_qk ? a->H_qk : a->H;
     rp.S = split_for(&f);
-    if (a->qkv_dtype != LA_F32) rp.S = a->d_v / 32;
     rp.scale = a->scale;
     rp.hsave = reinterpret_cast<float *>(ws + L.hs);
     ok = launch_reduce(rp, &f, kda, st) == hipSuccess;

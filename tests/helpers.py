@@ -126,7 +126,7 @@ def swz(row, P):
     return 0
 
 
-def image_layout(kda, esz, d):
+def image_layout(kda, esz, d, raw=False):
     has_kt = kda or esz == 4
     L = {"K": 0, "Q": 64 * d * esz}
     L["KT"] = L["Q"] + 64 * d * esz
@@ -135,9 +135,10 @@ def image_layout(kda, esz, d):
     L["VEC"] = L["MM"] + 64 * 64 * esz
     L["BYTES"] = L["VEC"] + -(-(192 + d) * 4 // 1024) * 1024
     L["has_kt"] = has_kt
-    # what the workspace stores per cell: 16-bit GDN from TN on (its reduce
-    # stages K and Q from the raw rows), otherwise the whole image
-    L["SKIP"] = L["TN"] if (not kda and esz == 2) else 0
+    # what the workspace stores per cell: with raw (GDN, 16-bit inputs,
+    # 32-column slices) from TN on, since that reduce stages K and Q from the
+    # raw rows; otherwise the whole image
+    L["SKIP"] = L["TN"] if raw else 0
     L["HBM"] = L["BYTES"] - L["SKIP"]
     return L
 
@@ -157,9 +158,9 @@ def untile(cell, off, rows, cols, esz):
     return flat[byte // esz].astype(np.float64)
 
 
-def decode_images(ws, NT, H, d, kda, esz):
+def decode_images(ws, NT, H, d, kda, esz, raw=False):
     """Every cell of a workspace (torch uint8 tensor) as dict of logical arrays."""
-    L = image_layout(kda, esz, d)
+    L = image_layout(kda, esz, d, raw)
     raw = ws[:NT * H * L["HBM"]].cpu().numpy().reshape(NT, H, L["HBM"])
     sk = L["SKIP"]
     out = {}

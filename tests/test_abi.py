@@ -73,7 +73,6 @@ BAD = [
     ("dv_split 3", dict(dv_split=3), -4),
     ("dv_split 8", dict(dv_split=8), -4),
     ("dv_split too fine", dict(dv_split=4), -4),
-    ("16-bit 64 columns", dict(qkv_dtype=0, d_k=128, d_v=128, dv_split=2), -4),
     ("no workspace", dict(workspace=None), -5),
     ("workspace small", dict(workspace_bytes=100), -5),
     ("workspace misaligned", dict(workspace=0x100010), -5),
@@ -122,28 +121,33 @@ def test_meta_rejects_on_host(fn):
 
 def test_workspace_size_and_split():
     import torch
-    for (T, N, H, d, dt, esz) in [(8192, 8, 16, 128, torch.bfloat16, 2),
-                                  (256, 1, 2, 64, torch.float32, 4),
-                                  (16384, 64, 32, 128, torch.bfloat16, 2)]:
+    for (T, N, H, d, dt, esz, raw) in [(8192, 8, 16, 128, torch.bfloat16, 2, True),
+                                       (256, 1, 2, 64, torch.float32, 4, False),
+                                       (16384, 64, 32, 128, torch.bfloat16, 2, False)]:
         cells = meta_ref.nt_max(T, N, 64) * H
         # one image per cell: K, Q, [K^T: KDA or fp32], Tn, M, vec padded to
-        # 1 KiB; 16-bit GDN stores no K and Q (its reduce stages them itself)
+        # 1 KiB; GDN with 16-bit inputs in 32-column slices (raw) stores no K
+        # and Q (its reduce stages them itself)
         vec = -(-(192 + d) * 4 // 1024) * 1024
         kt = 64 * d * esz
-        gdn = (2 * 64 * d * esz if esz == 4 else 0) + (kt if esz == 4 else 0) + \
+        gdn = (0 if raw else 2 * 64 * d * esz) + (kt if esz == 4 else 0) + \
             2 * 64 * 64 * esz + vec
         assert la.workspace_bytes(T, N, H, d, d, dt) == cells * gdn
         kda = 2 * 64 * d * esz + kt + 2 * 64 * 64 * esz + vec
         assert la.workspace_bytes(T, N, H, d, d, dt, kda=True) == cells * kda
+    # a 64-column split of the first shape stores K and Q again
+    full = (2 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 2048) * meta_ref.nt_max(8192, 8, 64) * 16
+    assert la.workspace_bytes(8192, 8, 16, 128, 128, torch.bfloat16, dv_split=2) == full
     assert la.workspace_bytes(0, 1, 1, 64, 64, torch.bfloat16) == 0
-    # 16-bit inputs: 32 columns per workgroup
+    # 64 columns per workgroup, 32 when that leaves at most one workgroup per
+    # CU (256 of them)
     assert la.dv_split_for(8192, 8, 16, 128, 128, torch.bfloat16) == 4
-    assert la.dv_split_for(8192, 8, 17, 128, 128, torch.bfloat16) == 4
-    assert la.dv_split_for(16384, 64, 32, 128, 128, torch.bfloat16) == 4
+    assert la.dv_split_for(8192, 8, 17, 128, 128, torch.bfloat16) == 2
+    assert la.dv_split_for(16384, 64, 32, 128, 128, torch.bfloat16) == 2
     assert la.dv_split_for(65536, 1, 10, 128, 128, torch.bfloat16, seg_len=-1) == 4
-    assert la.dv_split_for(65536, 1, 10, 128, 128, torch.bfloat16) == 4
+    # segmented: 64-column slices (13 x 10 x 8 = 1040 workgroups at 32)
+    assert la.dv_split_for(65536, 1, 10, 128, 128, torch.bfloat16) == 2
     assert la.dv_split_for(4096, 1, 2, 64, 64, torch.bfloat16) == 2
-    # fp32 inputs: 64 columns, 32 when that leaves at most one workgroup per CU
     assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32) == 2
     assert la.dv_split_for(4096, 512, 2, 64, 64, torch.float32) == 1
     assert la.dv_split_for(256, 1, 2, 64, 64, torch.float32, dv_split=1) == 1
@@ -163,9 +167,9 @@ def test_segment_length_choice():
     assert la.seg_len_for(8192, 8, 16, 128, 128, bf) == 0        # 256 units: plain
     assert la.seg_len_for(16384, 64, 32, 128, 128, bf) == 0
     assert la.seg_len_for(512, 1, 2, 128, 128, bf) == 0          # 8 chunks < 3 segments
-    # segmented slices of 16-bit inputs: 32 columns
-    assert la.dv_split_for(2048, 1, 10, 128, 128, bf) == 4
-    assert la.dv_split_for(4096, 1, 16, 128, 128, bf) == 4
+    # segmented slices: 32 columns while the first pass has <= 512 workgroups
+    assert la.dv_split_for(2048, 1, 10, 128, 128, bf) == 4       # 4 x 10 x 8 = 320
+    assert la.dv_split_for(4096, 1, 16, 128, 128, bf) == 2       # 8 x 16 x 8 = 1024
     assert la.seg_len_for(65536, 1, 10, 64, 64, f32) == 0        # fp32: plain
     assert la.seg_len_for(65536, 1, 10, 128, 128, bf, seg_len=-1) == 0
     assert la.seg_len_for(4096, 3, 2, 128, 128, bf, seg_len=5) == 5
@@ -318,7 +322,9 @@ def test_backward_workspace_size():
     cells = meta_ref.nt_max(T, N, 64) * H
     up = lambda x: -(-x // 256) * 256
     for kda in (False, True):
-        img = la.workspace_bytes(T, N, H, d, d, torch.bfloat16, kda=kda, seg_len=-1)
+        # the recompute reduces 16-bit inputs in 32-column slices
+        img = la.workspace_bytes(T, N, H, d, d, torch.bfloat16, kda=kda, seg_len=-1,
+                                 dv_split=d // 32)
         prep = (12544 + 8192 if not kda else 12352 + 64 * d + 8192) * 4   # + bf16 halves of M, A~
         part = (192 * d + 8192 + 256) * 4
         want = up(img) + 2 * up(cells * d * d * 4) + up(cells * prep) + up(cells * part)

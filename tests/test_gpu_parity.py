@@ -78,12 +78,10 @@ SMALL_CU = [0, 1, 64, 64, 200, 333, 460]   # one-token, exact chunk, empty, tail
 
 @pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("split", [0, 2, 4])
+@pytest.mark.parametrize("split", [0, 1, 2, 4])
 def test_small_bf16(kda, d, split):
-    # 16-bit inputs run 32 state columns per workgroup: dv_split d / 32 (or
-    # auto); other splits are rejected on the host
-    if split and d // split != 32:
-        pytest.skip("16-bit reduce slices are 32 columns")
+    if split and d // split < 32:
+        pytest.skip("slice narrower than 32 columns")
     inp = make_inputs(SMALL_CU[-1], 3, d, d, kda=kda, dtype="bf16", seed=20 + d + split,
                       cu_seqlens=SMALL_CU, h0_std=0.1)
     o, ht, _ = run_gpu(inp, dv_split=split)
@@ -112,24 +110,27 @@ def kpos(k):
     return (k & ~31) + 8 * ((k & 15) >> 2) + (k & 3) + 4 * ((k & 31) >> 4)
 
 
-@pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
-def test_map_stage_matrices(kda):
+@pytest.mark.parametrize("kda,split", [(False, 0), (False, 2), (True, 0)],
+                         ids=["gdn-raw", "gdn-full", "kda"])
+def test_map_stage_matrices(kda, split):
     """Map-stage images against the chunkwise reference: T without its
-    diagonal, M, the row vectors and the decayed operands (KDA).  GDN with
-    16-bit inputs stores no K and Q: its reduce stages them from the raw
-    rows."""
+    diagonal, M, the row vectors, K and Q (GDN: exact fp16 copies) and the
+    decayed operands (KDA).  GDN with 16-bit inputs in 32-column slices (auto
+    split here) stores no K and Q: its reduce stages them from the raw rows."""
     cu = [0, 64, 100, 230]
     d = 128
     inp = make_inputs(230, 2, d, d, kda=kda, dtype="bf16", seed=41, cu_seqlens=cu)
     dv = to_dev(inp)
     ci, co, _ = la.build_chunk_meta(dv["cu_seqlens"], 230)
-    nbytes = la.workspace_bytes(230, 3, 2, d, d, torch.bfloat16, kda)
+    nbytes = la.workspace_bytes(230, 3, 2, d, d, torch.bfloat16, kda, dv_split=split)
     ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
     la.chunk_fwd_stages(kda, la.STAGE_MAP, dv["q"], dv["k"], dv["v"], dv["g"], dv["beta"],
-                        dv["cu_seqlens"], ci, co, workspace=ws)
+                        dv["cu_seqlens"], ci, co, workspace=ws, dv_split=split)
     torch.cuda.synchronize()
     NT = la.nt_max(230, 3)
-    img = decode_images(ws, NT, 2, d, kda, 2)
+    raw = not kda and la.dv_split_for(230, 3, 2, d, d, torch.bfloat16, split) == d // 32
+    assert raw == (not kda and split == 0)
+    img = decode_images(ws, NT, 2, d, kda, 2, raw)
     _, _, inter = chunkwise_ref.chunk_forward(inp["q"], inp["k"], inp["v"], inp["g"],
                                               inp["beta"], cu, None, kda=kda, keep=True)
     slot = 0
@@ -152,7 +153,16 @@ def test_map_stage_matrices(kda):
                 assert rel_err(vec[128:128 + C], inp["beta"][rows, h]) == 0.0
                 K, Q = inp["k"][rows, h], inp["q"][rows, h]
                 if not kda:
-                    assert "K" not in im and "Q" not in im
+                    if raw:
+                        assert "K" not in im and "Q" not in im
+                    else:
+                        # bf16 values are exact in fp16 inside its normal range;
+                        # below it they round to the subnormal grid (step 2^-24)
+                        for got, ref in ((im["K"][:C], K), (im["Q"][:C], Q)):
+                            normal = np.abs(ref) >= 2.0 ** -14
+                            assert np.array_equal(got[normal], ref[normal])
+                            assert np.abs(got - ref).max() <= 2.0 ** -25
+                        assert not im["K"][C:].any() and not im["Q"][C:].any()
                     assert rel_err(vec[:C], np.exp(G)) < 1e-5
                     assert rel_err(vec[64:64 + C], np.exp(G[-1] - G)) < 1e-5
                     assert rel_err(vec[192:192 + d], np.full(d, np.exp(G[-1]))) < 1e-5

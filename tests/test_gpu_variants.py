@@ -33,7 +33,7 @@ def test_fp16_inputs(kda, d):
     inp = make_inputs(SMALL_CU[-1], 3, d, d, kda=kda, dtype="f16", seed=300 + d,
                       cu_seqlens=SMALL_CU, h0_std=0.1)
     o_ref, ht_ref = run_oracle(inp)
-    for split in (0, d // 32):
+    for split in (0, 1, d // 32):
         o, ht, _ = run_gpu(inp, dv_split=split)
         eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref)
         _say(f"fp16 kda={kda} d={d} split={split}: o {eo:.2e} ht {eh:.2e}")
