@@ -112,11 +112,9 @@ typedef struct {
                                /* or chunk_offsets)                             */
     int32_t qkv_dtype;         /* LA_BF16, LA_F16 or LA_F32: dtype of q, k, v    */
     int32_t dv_split;          /* state column slices per (seq, head): 0 = auto, */
-                               /* else 1, 2 or 4 leaving d_v / dv_split columns: */
-                               /* 32 for bf16 / fp16 inputs, 32 or 64 for fp32   */
-                               /* (other values: LA_ERR_UNSUPPORTED).  auto:     */
-                               /* 16-bit d_v / 32; fp32 d_v / 64 slices, twice   */
-                               /* that when N_max * H * (d_v / 64) <= 256 (CUs)  */
+                               /* else 1, 2 or 4 with d_v / dv_split >= 32.      */
+                               /* auto: d_v / 64 slices, twice that when         */
+                               /* N_max * H * (d_v / 64) <= 256 (the CU count)   */
     int32_t seg_len;           /* sequence-parallel reduce: chunks per segment;  */
                                /* -1 = off, 0 = auto, > 0 needs 16-bit inputs    */
                                /* and N_max <= 64 (see la_chunk_fwd_seg_len)     */
@@ -147,8 +145,8 @@ typedef struct {
  * multiple of 1 KiB.  With e = 2 (bf16, fp16 inputs: fp16 values) or 4 (fp32
  * inputs), a cell holds in order
  *   K, Q  [BT][d_k]  the chunk's keys and queries (KDA: K*exp(G), Q*exp(G));
- *                    absent for GDN with 16-bit inputs, whose reduce reads
- *                    the rows of k and q itself
+ *                    absent for GDN with 16-bit inputs in 32-column slices,
+ *                    whose reduce reads the rows of k and q itself
  *   KT    [d_k][BT]  KDA: (K*exp(G_C - G))^T; fp32 inputs: K^T; absent for
  *                    GDN with 16-bit inputs
  *   Tn    [BT][BT]   T = A^-1 diag(beta) with its diagonal removed
@@ -220,8 +218,9 @@ int la_chunk_fwd_stages(const la_chunk_fwd_args *a, int is_kda, int stages,
 #define LA_STATIC_SCRATCH_BYTES ((size_t)128 << 20)
 int la_chunk_fwd_static(const la_chunk_fwd_args *a, int is_kda, void *stream);
 
-/* The dv_split the forward uses for these arguments (after "auto"); the
- * segmented passes use the same slices. */
+/* The dv_split the forward uses for these arguments (after "auto").  Run
+ * segmented, auto takes 32-column slices while the first pass has at most
+ * 512 workgroups with them (2 per CU), else 64-column slices. */
 int32_t la_chunk_fwd_dv_split(const la_chunk_fwd_args *a);
 
 /*
