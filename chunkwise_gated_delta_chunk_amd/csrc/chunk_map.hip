@@ -76,9 +76,9 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   // waves are done reading K and Q)
   constexpr int AREA = KQ_BYTES > LX_BYTES ? KQ_BYTES : LX_BYTES;
   __shared__ __attribute__((aligned(16))) char sArea[AREA];
-  __shared__ float sY[4][16 * 17];    // per-wave 16x16 scratch
-  __shared__ float sB[kBT];
-  __shared__ float sg[kBT];
+  __shared__ __attribute__((aligned(16))) float sY[4][16 * 17];  // per-wave 16x16 scratch
+  __shared__ __attribute__((aligned(16))) float sB[kBT];
+  __shared__ __attribute__((aligned(16))) float sg[kBT];
   // KDA: per-channel cumulative gate (rows padded so that 16 rows at one
   // channel hit distinct banks)
   constexpr int GS = DK + 4;
@@ -256,6 +256,263 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
       for (int e = 0; e < CH; ++e) v[e] = sK[kidx<O>(pc * CH + e) * LDK + c];
       put(I.KT, PT, c, pc, v);
     }
+  }
+
+  if constexpr (!KDA && O::KPL == 8) {
+    // ---- 16-bit GDN.  Every tile (R, S) of K K^T and Q K^T is formed with
+    // A = K row tile S and B = K / Q row tile R, so lane l holds row
+    // r = 16 R + l%16 at columns s = 16 S + 4 (l/16) .. +3 and the tile
+    // leaves as rows (8-byte pieces straight to the image).  Wave 0 takes the
+    // diagonal tiles of both products, the diagonal blocks X_ii of
+    // X = (I + L)^-1 and then block column 0 of X; wave 1 the off-diagonal
+    // tiles of K K^T (L's rows 16..63 as fp16 hi / lo operands) and then
+    // block columns 1 and 2; wave 2 the off-diagonal tiles of Q K^T (M);
+    // wave 3 the row vectors and the zero tiles.
+    float *Gw = &sY[w][0];  // this wave's copy of G, for lookups by row / column
+    const float G = wave_inclusive_scan(sg[lane]);  // lane r holds G_r
+    Gw[lane] = G;
+    const float bv = sB[lane];
+    constexpr int NKS = DK / KSTEP;
+    auto oR = [](int i) { return i < 1 ? 1 : i < 3 ? 2 : 3; };  // off-diagonal tile i:
+    auto oS = [](int i) { return i < 1 ? 0 : i < 3 ? i - 1 : i - 3; };  // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+    f32x4 a[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = zero4();
+    if (w == 0) {
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        typename O::Frag kf[4], qf[4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+          kf[R] = frag_lds<O>(sK, LDK, 16 * R, KSTEP * s, lane);
+          qf[R] = frag_lds<O>(sQ, LDK, 16 * R, KSTEP * s, lane);
+        }
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+          a[R] = O::mfma(kf[R], kf[R], a[R]);
+          a[4 + R] = O::mfma(kf[R], qf[R], a[4 + R]);
+        }
+      }
+    } else if (w < 3) {
+      const T *bsrc = w == 1 ? sK : sQ;
+#pragma unroll
+      for (int s = 0; s < NKS; ++s) {
+        typename O::Frag af[3], bf[3];
+#pragma unroll
+        for (int R = 0; R < 3; ++R) {
+          af[R] = frag_lds<O>(sK, LDK, 16 * R, KSTEP * s, lane);
+          bf[R] = frag_lds<O>(bsrc, LDK, 16 * (R + 1), KSTEP * s, lane);
+        }
+#pragma unroll
+        for (int i = 0; i < 6; ++i) a[i] = O::mfma(af[oS(i)], bf[oR(i) - 1], a[i]);
+      }
+    }
+    __syncthreads();  // K and Q are dead: the inverse's scratch takes their bytes
+    // scratch: L's diagonal blocks transposed (fp32), L's rows 16..63 as fp16
+    // hi and lo (chained columns, swizzled), X_ii row-major and transposed
+    constexpr int LT = 0, LH = 4096, LL = LH + 48 * 128, XR = LL + 48 * 128, XT = XR + 4096;
+    static_assert(XT + 4096 <= AREA, "inverse scratch inside the K / Q area");
+    char *sc = sArea;
+    // byte offset of 8-byte half `half` of piece pc of row r of a [64][64]
+    // fp16 tile (8 pieces per row, swizzled as the image tiles)
+    auto t8 = [](int r, int pc, int half) { return tile_off<8>(r, pc) + 8 * half; };
+    auto put4 = [&](char *dst, const f32x4 &v) {
+      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+      *reinterpret_cast<h4 *>(dst) = h4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+    };
+    auto lo16 = [](float v) { return (_Float16)(v - (float)(_Float16)v); };
+    if (w == 0) {
+      // L_rs = beta_r (K K^T)_rs exp(G_r - G_s), s < r, stored transposed
+      // for the column-order solve; M_rs = (Q K^T)_rs exp(G_r - G_s), s <= r
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        const int r = 16 * R + lr;
+        const float grr = Gw[r], brr = sB[r];
+        const f32x4 gs = *reinterpret_cast<const f32x4 *>(Gw + 16 * R + 4 * lg);
+        f32x4 mv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int sl = 4 * lg + e;  // column inside the tile
+          const float ge = __expf(grr - gs[e]);
+          *reinterpret_cast<float *>(sc + LT + R * 1024 + sl * 64 + lr * 4) =
+              sl < lr ? a[R][e] * brr * ge : 0.f;
+          mv[e] = sl <= lr ? a[4 + R][e] * ge : 0.f;
+        }
+        put4(img + I.MM + t8(r, 4 * (R >> 1) + lg, R & 1), mv);
+      }
+      // X_ii = (I + L_ii)^-1, column c = l%16 of block l/16, in column order:
+      // once x_s is final, x_r -= L_rs x_s for every r > s (the updates of
+      // one step are independent)
+      {
+        const int blk = lane >> 4, c = lane & 15;
+        const char *Lb = sc + LT + blk * 1024;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = r == c ? 1.f : 0.f;
+#pragma unroll
+        for (int s = 0; s < 15; ++s) {
+          const float xs = x[s];
+#pragma unroll
+          for (int q4 = (s + 1) >> 2; q4 < 4; ++q4) {
+            const f32x4 lv = *reinterpret_cast<const f32x4 *>(Lb + s * 64 + 16 * q4);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (4 * q4 + e > s) x[4 * q4 + e] = fmaf(-lv[e], xs, x[4 * q4 + e]);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) *reinterpret_cast<float *>(sc + XR + blk * 1024 + r * 64 + c * 4) = x[r];
+#pragma unroll
+        for (int q4 = 0; q4 < 4; ++q4)
+          *reinterpret_cast<f32x4 *>(sc + XT + blk * 1024 + c * 64 + 16 * q4) =
+              f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
+      }
+      // Tn's diagonal tiles: X_RR diag(beta), strict lower
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        const f32x4 xr = *reinterpret_cast<const f32x4 *>(sc + XR + R * 1024 + lr * 64 + lg * 16);
+        const f32x4 bs = *reinterpret_cast<const f32x4 *>(sB + 16 * R + 4 * lg);
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = 4 * lg + e < lr ? xr[e] * bs[e] : 0.f;
+        put4(img + I.TN + t8(16 * R + lr, 4 * (R >> 1) + lg, R & 1), v);
+      }
+    } else if (w == 1) {
+      // L's rows 16..63 as fp16 hi / lo A operands of the block levels; the
+      // diagonal tiles 1 and 3, which the levels read against zero rows, zero
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        const int R = oR(i), S = oS(i), r = 16 * R + lr;
+        const float grr = Gw[r], brr = sB[r];
+        const f32x4 gs = *reinterpret_cast<const f32x4 *>(Gw + 16 * S + 4 * lg);
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        h4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = a[i][e] * brr * __expf(grr - gs[e]);
+          hi[e] = (_Float16)v;
+          lo[e] = lo16(v);
+        }
+        const int o = t8(r - 16, 4 * (S >> 1) + lg, S & 1);
+        *reinterpret_cast<h4 *>(sc + LH + o) = hi;
+        *reinterpret_cast<h4 *>(sc + LL + o) = lo;
+      }
+#pragma unroll
+      for (int R = 1; R < 4; R += 2) {
+        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+        const int o = t8(16 * R - 16 + lr, 4 * (R >> 1) + lg, R & 1);
+        *reinterpret_cast<h4 *>(sc + LH + o) = h4{0, 0, 0, 0};
+        *reinterpret_cast<h4 *>(sc + LL + o) = h4{0, 0, 0, 0};
+      }
+    } else if (w == 2) {
+      // M's off-diagonal tiles
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        const int R = oR(i), S = oS(i), r = 16 * R + lr;
+        const float grr = Gw[r];
+        const f32x4 gs = *reinterpret_cast<const f32x4 *>(Gw + 16 * S + 4 * lg);
+        f32x4 mv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mv[e] = a[i][e] * __expf(grr - gs[e]);
+        put4(img + I.MM + t8(r, 4 * (S >> 1) + lg, S & 1), mv);
+      }
+    } else {
+      // the upper tiles of M and Tn (zero) and the row vectors
+      const f32x4 z = zero4();
+#pragma unroll
+      for (int R = 0; R < 3; ++R)
+#pragma unroll
+        for (int S = R + 1; S < 4; ++S) {
+          put4(img + I.MM + t8(16 * R + lr, 4 * (S >> 1) + lg, S & 1), z);
+          put4(img + I.TN + t8(16 * R + lr, 4 * (S >> 1) + lg, S & 1), z);
+        }
+      const float GC = Gw[kBT - 1];
+      vec[lane] = __expf(G);
+      vec[64 + lane] = __expf(GC - G);
+      vec[128 + lane] = bv;
+      const float gC = __expf(GC);
+      for (int d = lane; d < DK; d += 64) vec[192 + d] = gC;
+    }
+    __syncthreads();  // L's hi / lo rows and the diagonal blocks of X are in LDS
+    if (w < 2) {
+      // the off-diagonal blocks of X by levels,
+      //   X_ij = -X_ii sum_{k=j}^{i-1} L_ik X_kj,
+      // as fp16 MFMAs on hi / lo splits (about fp32 accuracy): wave 0 takes
+      // block column 0, wave 1 block columns 1 and 2.  The B operands X_kj
+      // stay in the accumulators (chained k order, b_frag's layout); the
+      // tiles Tn_ij = X_ij diag(beta_j) are transposed for their row-wise
+      // store by one MFMA with an identity operand.
+      const f32x4 z = zero4();
+      auto bsplit = [&](const f32x4 &t0, const f32x4 &t1, half8 &bh, half8 &bl) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bh[e] = (_Float16)t0[e];
+          bl[e] = lo16(t0[e]);
+          bh[4 + e] = (_Float16)t1[e];
+          bl[4 + e] = lo16(t1[e]);
+        }
+      };
+      auto mfma3 = [&](const half8 &ah, const half8 &al, const half8 &bh, const half8 &bl, f32x4 c) {
+        c = O::mfma(ah, bh, c);
+        c = O::mfma(ah, bl, c);
+        return O::mfma(al, bh, c);
+      };
+      auto close = [&](int i, const f32x4 &y) {  // -X_ii Y
+        const f32x4 xv = *reinterpret_cast<const f32x4 *>(sc + XR + i * 1024 + lr * 64 + lg * 16);
+        half8 ah, al, bh, bl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ah[e] = (_Float16)xv[e];
+          al[e] = lo16(xv[e]);
+          ah[4 + e] = (_Float16)0.f;
+          al[4 + e] = (_Float16)0.f;
+        }
+        bsplit(y, z, bh, bl);
+        const f32x4 r = mfma3(ah, al, bh, bl, z);
+        return f32x4{-r[0], -r[1], -r[2], -r[3]};
+      };
+      auto lev = [&](int i, int s, const f32x4 &t0, const f32x4 &t1, const f32x4 &y) {  // y + L_i,[2s,2s+1] [t0; t1]
+        const int o = tile_off<8>(16 * i - 16 + lr, 4 * s + lg);
+        const half8 ah = *reinterpret_cast<const half8 *>(sc + LH + o);
+        const half8 al = *reinterpret_cast<const half8 *>(sc + LL + o);
+        half8 bh, bl;
+        bsplit(t0, t1, bh, bl);
+        return mfma3(ah, al, bh, bl, y);
+      };
+      auto xcol = [&](int j) {  // X_jj as an accumulator tile
+        return *reinterpret_cast<const f32x4 *>(sc + XT + j * 1024 + lr * 64 + lg * 16);
+      };
+      auto put_tn = [&](int i, int j, const f32x4 &x) {
+        const float bj = sB[16 * j + lr];
+        half8 ident, av;  // B = [I; 0]: lane l supplies rows 4 (l/16) .. +3 of column l%16
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ident[e] = (_Float16)(4 * lg + e == lr ? 1.f : 0.f);
+          ident[4 + e] = (_Float16)0.f;
+          av[e] = (_Float16)(x[e] * bj);
+          av[4 + e] = (_Float16)0.f;
+        }
+        put4(img + I.TN + t8(16 * i + lr, 4 * (j >> 1) + lg, j & 1), O::mfma(av, ident, z));
+      };
+      if (w == 0) {
+        const f32x4 x00 = xcol(0);
+        const f32x4 x10 = close(1, lev(1, 0, x00, z, z));
+        const f32x4 x20 = close(2, lev(2, 0, x00, x10, z));
+        const f32x4 x30 = close(3, lev(3, 1, x20, z, lev(3, 0, x00, x10, z)));
+        put_tn(1, 0, x10);
+        put_tn(2, 0, x20);
+        put_tn(3, 0, x30);
+      } else {
+        const f32x4 x11 = xcol(1), x22 = xcol(2);
+        const f32x4 x21 = close(2, lev(2, 0, z, x11, z));
+        const f32x4 x31 = close(3, lev(3, 1, x21, z, lev(3, 0, z, x11, z)));
+        const f32x4 x32 = close(3, lev(3, 1, x22, z, z));
+        put_tn(2, 1, x21);
+        put_tn(3, 1, x31);
+        put_tn(3, 2, x32);
+      }
+    }
+    return;
   }
 
   // M tile (R, S) from an accumulator -> sMt (natural order; the write-out
