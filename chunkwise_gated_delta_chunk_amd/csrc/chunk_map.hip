@@ -258,263 +258,6 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
     }
   }
 
-  if constexpr (!KDA && O::KPL == 8) {
-    // ---- 16-bit GDN.  Every tile (R, S) of K K^T and Q K^T is formed with
-    // A = K row tile S and B = K / Q row tile R, so lane l holds row
-    // r = 16 R + l%16 at columns s = 16 S + 4 (l/16) .. +3 and the tile
-    // leaves as rows (8-byte pieces straight to the image).  Wave 0 takes the
-    // diagonal tiles of both products, the diagonal blocks X_ii of
-    // X = (I + L)^-1 and then block column 0 of X; wave 1 the off-diagonal
-    // tiles of K K^T (L's rows 16..63 as fp16 hi / lo operands) and then
-    // block columns 1 and 2; wave 2 the off-diagonal tiles of Q K^T (M);
-    // wave 3 the row vectors and the zero tiles.
-    float *Gw = &sY[w][0];  // this wave's copy of G, for lookups by row / column
-    const float G = wave_inclusive_scan(sg[lane]);  // lane r holds G_r
-    Gw[lane] = G;
-    const float bv = sB[lane];
-    constexpr int NKS = DK / KSTEP;
-    auto oR = [](int i) { return i < 1 ? 1 : i < 3 ? 2 : 3; };  // off-diagonal tile i:
-    auto oS = [](int i) { return i < 1 ? 0 : i < 3 ? i - 1 : i - 3; };  // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
-    f32x4 a[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = zero4();
-    if (w == 0) {
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        typename O::Frag kf[4], qf[4];
-#pragma unroll
-        for (int R = 0; R < 4; ++R) {
-          kf[R] = frag_lds<O>(sK, LDK, 16 * R, KSTEP * s, lane);
-          qf[R] = frag_lds<O>(sQ, LDK, 16 * R, KSTEP * s, lane);
-        }
-#pragma unroll
-        for (int R = 0; R < 4; ++R) {
-          a[R] = O::mfma(kf[R], kf[R], a[R]);
-          a[4 + R] = O::mfma(kf[R], qf[R], a[4 + R]);
-        }
-      }
-    } else if (w < 3) {
-      const T *bsrc = w == 1 ? sK : sQ;
-#pragma unroll
-      for (int s = 0; s < NKS; ++s) {
-        typename O::Frag af[3], bf[3];
-#pragma unroll
-        for (int R = 0; R < 3; ++R) {
-          af[R] = frag_lds<O>(sK, LDK, 16 * R, KSTEP * s, lane);
-          bf[R] = frag_lds<O>(bsrc, LDK, 16 * (R + 1), KSTEP * s, lane);
-        }
-#pragma unroll
-        for (int i = 0; i < 6; ++i) a[i] = O::mfma(af[oS(i)], bf[oR(i) - 1], a[i]);
-      }
-    }
-    __syncthreads();  // K and Q are dead: the inverse's scratch takes their bytes
-    // scratch: L's diagonal blocks transposed (fp32), L's rows 16..63 as fp16
-    // hi and lo (chained columns, swizzled), X_ii row-major and transposed
-    constexpr int LT = 0, LH = 4096, LL = LH + 48 * 128, XR = LL + 48 * 128, XT = XR + 4096;
-    static_assert(XT + 4096 <= AREA, "inverse scratch inside the K / Q area");
-    char *sc = sArea;
-    // byte offset of 8-byte half `half` of piece pc of row r of a [64][64]
-    // fp16 tile (8 pieces per row, swizzled as the image tiles)
-    auto t8 = [](int r, int pc, int half) { return tile_off<8>(r, pc) + 8 * half; };
-    auto put4 = [&](char *dst, const f32x4 &v) {
-      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-      *reinterpret_cast<h4 *>(dst) = h4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
-    };
-    auto lo16 = [](float v) { return (_Float16)(v - (float)(_Float16)v); };
-    if (w == 0) {
-      // L_rs = beta_r (K K^T)_rs exp(G_r - G_s), s < r, stored transposed
-      // for the column-order solve; M_rs = (Q K^T)_rs exp(G_r - G_s), s <= r
-#pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        const int r = 16 * R + lr;
-        const float grr = Gw[r], brr = sB[r];
-        const f32x4 gs = *reinterpret_cast<const f32x4 *>(Gw + 16 * R + 4 * lg);
-        f32x4 mv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int sl = 4 * lg + e;  // column inside the tile
-          const float ge = __expf(grr - gs[e]);
-          *reinterpret_cast<float *>(sc + LT + R * 1024 + sl * 64 + lr * 4) =
-              sl < lr ? a[R][e] * brr * ge : 0.f;
-          mv[e] = sl <= lr ? a[4 + R][e] * ge : 0.f;
-        }
-        put4(img + I.MM + t8(r, 4 * (R >> 1) + lg, R & 1), mv);
-      }
-      // X_ii = (I + L_ii)^-1, column c = l%16 of block l/16, in column order:
-      // once x_s is final, x_r -= L_rs x_s for every r > s (the updates of
-      // one step are independent)
-      {
-        const int blk = lane >> 4, c = lane & 15;
-        const char *Lb = sc + LT + blk * 1024;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = r == c ? 1.f : 0.f;
-#pragma unroll
-        for (int s = 0; s < 15; ++s) {
-          const float xs = x[s];
-#pragma unroll
-          for (int q4 = (s + 1) >> 2; q4 < 4; ++q4) {
-            const f32x4 lv = *reinterpret_cast<const f32x4 *>(Lb + s * 64 + 16 * q4);
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (4 * q4 + e > s) x[4 * q4 + e] = fmaf(-lv[e], xs, x[4 * q4 + e]);
-          }
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) *reinterpret_cast<float *>(sc + XR + blk * 1024 + r * 64 + c * 4) = x[r];
-#pragma unroll
-        for (int q4 = 0; q4 < 4; ++q4)
-          *reinterpret_cast<f32x4 *>(sc + XT + blk * 1024 + c * 64 + 16 * q4) =
-              f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
-      }
-      // Tn's diagonal tiles: X_RR diag(beta), strict lower
-#pragma unroll
-      for (int R = 0; R < 4; ++R) {
-        const f32x4 xr = *reinterpret_cast<const f32x4 *>(sc + XR + R * 1024 + lr * 64 + lg * 16);
-        const f32x4 bs = *reinterpret_cast<const f32x4 *>(sB + 16 * R + 4 * lg);
-        f32x4 v;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) v[e] = 4 * lg + e < lr ? xr[e] * bs[e] : 0.f;
-        put4(img + I.TN + t8(16 * R + lr, 4 * (R >> 1) + lg, R & 1), v);
-      }
-    } else if (w == 1) {
-      // L's rows 16..63 as fp16 hi / lo A operands of the block levels; the
-      // diagonal tiles 1 and 3, which the levels read against zero rows, zero
-#pragma unroll
-      for (int i = 0; i < 6; ++i) {
-        const int R = oR(i), S = oS(i), r = 16 * R + lr;
-        const float grr = Gw[r], brr = sB[r];
-        const f32x4 gs = *reinterpret_cast<const f32x4 *>(Gw + 16 * S + 4 * lg);
-        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-        h4 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float v = a[i][e] * brr * __expf(grr - gs[e]);
-          hi[e] = (_Float16)v;
-          lo[e] = lo16(v);
-        }
-        const int o = t8(r - 16, 4 * (S >> 1) + lg, S & 1);
-        *reinterpret_cast<h4 *>(sc + LH + o) = hi;
-        *reinterpret_cast<h4 *>(sc + LL + o) = lo;
-      }
-#pragma unroll
-      for (int R = 1; R < 4; R += 2) {
-        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-        const int o = t8(16 * R - 16 + lr, 4 * (R >> 1) + lg, R & 1);
-        *reinterpret_cast<h4 *>(sc + LH + o) = h4{0, 0, 0, 0};
-        *reinterpret_cast<h4 *>(sc + LL + o) = h4{0, 0, 0, 0};
-      }
-    } else if (w == 2) {
-      // M's off-diagonal tiles
-#pragma unroll
-      for (int i = 0; i < 6; ++i) {
-        const int R = oR(i), S = oS(i), r = 16 * R + lr;
-        const float grr = Gw[r];
-        const f32x4 gs = *reinterpret_cast<const f32x4 *>(Gw + 16 * S + 4 * lg);
-        f32x4 mv;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) mv[e] = a[i][e] * __expf(grr - gs[e]);
-        put4(img + I.MM + t8(r, 4 * (S >> 1) + lg, S & 1), mv);
-      }
-    } else {
-      // the upper tiles of M and Tn (zero) and the row vectors
-      const f32x4 z = zero4();
-#pragma unroll
-      for (int R = 0; R < 3; ++R)
-#pragma unroll
-        for (int S = R + 1; S < 4; ++S) {
-          put4(img + I.MM + t8(16 * R + lr, 4 * (S >> 1) + lg, S & 1), z);
-          put4(img + I.TN + t8(16 * R + lr, 4 * (S >> 1) + lg, S & 1), z);
-        }
-      const float GC = Gw[kBT - 1];
-      vec[lane] = __expf(G);
-      vec[64 + lane] = __expf(GC - G);
-      vec[128 + lane] = bv;
-      const float gC = __expf(GC);
-      for (int d = lane; d < DK; d += 64) vec[192 + d] = gC;
-    }
-    __syncthreads();  // L's hi / lo rows and the diagonal blocks of X are in LDS
-    if (w < 2) {
-      // the off-diagonal blocks of X by levels,
-      //   X_ij = -X_ii sum_{k=j}^{i-1} L_ik X_kj,
-      // as fp16 MFMAs on hi / lo splits (about fp32 accuracy): wave 0 takes
-      // block column 0, wave 1 block columns 1 and 2.  The B operands X_kj
-      // stay in the accumulators (chained k order, b_frag's layout); the
-      // tiles Tn_ij = X_ij diag(beta_j) are transposed for their row-wise
-      // store by one MFMA with an identity operand.
-      const f32x4 z = zero4();
-      auto bsplit = [&](const f32x4 &t0, const f32x4 &t1, half8 &bh, half8 &bl) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          bh[e] = (_Float16)t0[e];
-          bl[e] = lo16(t0[e]);
-          bh[4 + e] = (_Float16)t1[e];
-          bl[4 + e] = lo16(t1[e]);
-        }
-      };
-      auto mfma3 = [&](const half8 &ah, const half8 &al, const half8 &bh, const half8 &bl, f32x4 c) {
-        c = O::mfma(ah, bh, c);
-        c = O::mfma(ah, bl, c);
-        return O::mfma(al, bh, c);
-      };
-      auto close = [&](int i, const f32x4 &y) {  // -X_ii Y
-        const f32x4 xv = *reinterpret_cast<const f32x4 *>(sc + XR + i * 1024 + lr * 64 + lg * 16);
-        half8 ah, al, bh, bl;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ah[e] = (_Float16)xv[e];
-          al[e] = lo16(xv[e]);
-          ah[4 + e] = (_Float16)0.f;
-          al[4 + e] = (_Float16)0.f;
-        }
-        bsplit(y, z, bh, bl);
-        const f32x4 r = mfma3(ah, al, bh, bl, z);
-        return f32x4{-r[0], -r[1], -r[2], -r[3]};
-      };
-      auto lev = [&](int i, int s, const f32x4 &t0, const f32x4 &t1, const f32x4 &y) {  // y + L_i,[2s,2s+1] [t0; t1]
-        const int o = tile_off<8>(16 * i - 16 + lr, 4 * s + lg);
-        const half8 ah = *reinterpret_cast<const half8 *>(sc + LH + o);
-        const half8 al = *reinterpret_cast<const half8 *>(sc + LL + o);
-        half8 bh, bl;
-        bsplit(t0, t1, bh, bl);
-        return mfma3(ah, al, bh, bl, y);
-      };
-      auto xcol = [&](int j) {  // X_jj as an accumulator tile
-        return *reinterpret_cast<const f32x4 *>(sc + XT + j * 1024 + lr * 64 + lg * 16);
-      };
-      auto put_tn = [&](int i, int j, const f32x4 &x) {
-        const float bj = sB[16 * j + lr];
-        half8 ident, av;  // B = [I; 0]: lane l supplies rows 4 (l/16) .. +3 of column l%16
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          ident[e] = (_Float16)(4 * lg + e == lr ? 1.f : 0.f);
-          ident[4 + e] = (_Float16)0.f;
-          av[e] = (_Float16)(x[e] * bj);
-          av[4 + e] = (_Float16)0.f;
-        }
-        put4(img + I.TN + t8(16 * i + lr, 4 * (j >> 1) + lg, j & 1), O::mfma(av, ident, z));
-      };
-      if (w == 0) {
-        const f32x4 x00 = xcol(0);
-        const f32x4 x10 = close(1, lev(1, 0, x00, z, z));
-        const f32x4 x20 = close(2, lev(2, 0, x00, x10, z));
-        const f32x4 x30 = close(3, lev(3, 1, x20, z, lev(3, 0, x00, x10, z)));
-        put_tn(1, 0, x10);
-        put_tn(2, 0, x20);
-        put_tn(3, 0, x30);
-      } else {
-        const f32x4 x11 = xcol(1), x22 = xcol(2);
-        const f32x4 x21 = close(2, lev(2, 0, z, x11, z));
-        const f32x4 x31 = close(3, lev(3, 1, x21, z, lev(3, 0, z, x11, z)));
-        const f32x4 x32 = close(3, lev(3, 1, x22, z, z));
-        put_tn(2, 1, x21);
-        put_tn(3, 1, x31);
-        put_tn(3, 2, x32);
-      }
-    }
-    return;
-  }
-
   // M tile (R, S) from an accumulator -> sMt (natural order; the write-out
   // below zeroes the upper triangle)
   auto store_m = [&](int R, int S, const f32x4 &c) {
@@ -842,6 +585,441 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// 16-bit GDN (bf16 / fp16 inputs on fp16 MFMA): a persistent kernel, one
+// workgroup per resident slot, walking cells (chunk slot, head) with a stride
+// of the grid.  The raw q / k rows of a workgroup's next cell are loaded into
+// registers while it computes the current one, so the HBM reads of one cell
+// overlap the products, the inverse and the stores of the previous.
+//
+// Every tile (R, S) of K K^T and Q K^T is one accumulator formed with
+// A = K row tile S and B = K / Q row tile R: lane l holds row 16 R + l%16 at
+// columns 16 S + 4 (l/16) .. +3, so M and Tn leave as 8-byte row pieces in
+// the image's chained column order.  Products over the natural key order
+// (both operands read alike).  Wave roles, per cell:
+//   products:  w0 the diagonal tiles of K K^T, w1 its six lower tiles,
+//              w2 the diagonal tiles of Q K^T and tile (1, 0), w3 the rest;
+//   masks:     w0 L's diagonal blocks (fp32, column-major) and their inverse
+//              X_ii by forward substitution, one lane per column; w1 L's rows
+//              16..63 as fp16 hi / lo operands and the zero tiles; w2, w3 M
+//              and the row vectors;
+//   levels:    X_ij = -X_ii sum_{k=j}^{i-1} L_ik X_kj on fp16 hi / lo MFMAs
+//              (about fp32 accuracy): w0 block column 0, w1 block columns 1
+//              and 2; w2 Tn's diagonal tiles.
+template <typename In, int DK, bool RAW>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))) void chunk_map16_kernel(MapParams p) {
+  using O = Op<In>;
+  using T = typename O::T;
+  static_assert(O::KPL == 8, "16-bit inputs");
+  constexpr int LDK = DK + O::PAD;  // K / Q row stride (elements)
+  constexpr int KSTEP = 32;
+  constexpr int NKS = DK / KSTEP;
+  constexpr int KQ_BYTES = 2 * kBT * LDK * 2;
+  // inverse scratch over the K / Q bytes: L's diagonal blocks column-major
+  // (fp32), L's rows 16..63 fp16 hi and lo (chained columns, swizzled), X_ii
+  // row-major and column-major (fp32).  The 16x16 fp32 blocks sit BS bytes
+  // apart (1 KiB + 64): the four blocks' accesses of one instruction fall on
+  // different LDS banks.
+  constexpr int BS = 1024 + 64;
+  constexpr int LT = 0, LH = 4 * BS, LL = LH + 48 * 128, XR = LL + 48 * 128, XT = XR + 4 * BS;
+  constexpr int AREA = KQ_BYTES > XT + 4 * BS ? KQ_BYTES : XT + 4 * BS;
+  __shared__ __attribute__((aligned(16))) char sArea[AREA];
+  __shared__ __attribute__((aligned(16))) float sGw[4][kBT];  // G, one copy per wave
+  __shared__ __attribute__((aligned(16))) float sB[kBT];
+  __shared__ __attribute__((aligned(16))) float sg[kBT];
+  T *sK = reinterpret_cast<T *>(sArea);
+  T *sQ = sK + kBT * LDK;
+  char *sc = sArea;
+  typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+
+  const int H = p.H;
+  const int w = wave_id();
+  constexpr ImageLayout I = image_layout(false, 2, DK);
+  constexpr int PK = DK * 2 / 16;
+  constexpr int SKIP = image_skip(false, 2, DK, RAW);
+  constexpr int HBM = image_hbm_bytes(false, 2, DK, RAW);
+  const int ncell = p.NT_max * H;
+  float *Gw = sGw[w];
+
+  // staging unit of a thread: row r, 32-element block b, half g2: input
+  // pieces 4b + g2 and 4b + 2 + g2 (8 elements each), which hold exactly the
+  // chained pieces 4b + 2 g2 (their low halves) and 4b + 2 g2 + 1 (their high
+  // halves)
+  constexpr int UPR = DK / 16;
+  constexpr int NU = kBT * UPR / kThreads;
+  static_assert(kBT * UPR % kThreads == 0, "staging split");
+  const In *qsrc = static_cast<const In *>(p.q);
+  const In *ksrc = static_cast<const In *>(p.k);
+  const int G = H / p.Hqk;  // grouped value heads share q and k
+  u32x4 kraw[NU][2], qraw[NU][2];
+  float bval, gval;
+  // the cell's chunk: first row, valid rows (0: sentinel)
+  auto cell_rows = [&](int cell, int &r0, int &C) {
+    const int slot = cell / H;
+    const int i_n = p.chunk_indices[2 * slot];
+    C = 0;
+    r0 = 0;
+    if (i_n < 0) return;
+    const int i_t = p.chunk_indices[2 * slot + 1];
+    const int bos = cu_at(p.cu_seqlens, p.cu64, i_n);
+    const int eos = cu_at(p.cu_seqlens, p.cu64, i_n + 1);
+    r0 = bos + i_t * kBT;
+    C = min(kBT, eos - r0);
+  };
+  auto load = [&](int tid, int cell, int r0, int C) {
+    const int h = cell % H, hqk = h / G;
+#pragma unroll
+    for (int it = 0; it < NU; ++it) {
+      const int u = tid + it * kThreads;
+      const int r = u / UPR, pi = u % UPR;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int piece = 4 * (pi >> 1) + (pi & 1) + 2 * j;
+        kraw[it][j] = u32x4{0, 0, 0, 0};
+        qraw[it][j] = u32x4{0, 0, 0, 0};
+        if (r < C) {
+          const size_t off = ((size_t)(r0 + r) * p.Hqk + hqk) * DK + piece * 8;
+          kraw[it][j] = *reinterpret_cast<const u32x4 *>(ksrc + off);
+          qraw[it][j] = *reinterpret_cast<const u32x4 *>(qsrc + off);
+        }
+      }
+    }
+    bval = 0.f;
+    gval = 0.f;
+    if (tid < C) {
+      bval = p.beta[(size_t)(r0 + tid) * H + h];
+      gval = p.g[(size_t)(r0 + tid) * H + h];
+    }
+  };
+  auto cvt = [](uint32_t x) -> T {  // one 16-bit input value in the low half
+    if constexpr (std::is_same<In, f16>::value) return f16_from_bits(x);
+    else return (T)__uint_as_float(x << 16);
+  };
+
+  int cell = blockIdx.x;
+  if (cell >= ncell) return;
+  int r0, C;
+  cell_rows(cell, r0, C);
+  if (C <= 0) return;  // sentinel: this and every later cell (slots fill in order)
+  load((int)threadIdx.x, cell, r0, C);
+
+  auto oR = [](int i) { return i < 1 ? 1 : i < 3 ? 2 : 3; };          // lower tile i:
+  auto oS = [](int i) { return i < 1 ? 0 : i < 3 ? i - 1 : i - 3; };  // (1,0) (2,0) (2,1) (3,0) (3,1) (3,2)
+  auto t8 = [](int r, int pc, int half) { return tile_off<8>(r, pc) + 8 * half; };
+  auto put4 = [](char *dst, const f32x4 &v) {
+    *reinterpret_cast<h4 *>(dst) = h4{(_Float16)v[0], (_Float16)v[1], (_Float16)v[2], (_Float16)v[3]};
+  };
+  auto lo16 = [](float v) { return (_Float16)(v - (float)(_Float16)v); };
+
+  for (;;) {
+    // lane-derived offsets are formed anew in every pass, not kept live
+    // across the loop
+    int lane = lane_id();
+    asm volatile("" : "+v"(lane));
+    const int lr = lane & 15, lg = lane >> 4, tid = 64 * w + lane;
+    const int h = cell % H;
+    char *img = static_cast<char *>(p.img) + (size_t)cell * HBM - SKIP;
+    float *vec = reinterpret_cast<float *>(img + I.VEC);
+
+    // ---- stage K, Q (fp16, natural order; rows >= C zero), beta, g
+#pragma unroll
+    for (int it = 0; it < NU; ++it) {
+      const int u = tid + it * kThreads;
+      const int r = u / UPR, pi = u % UPR;
+      T kv[2][8], qv[2][8];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          kv[j][2 * e] = cvt(kraw[it][j][e]);
+          kv[j][2 * e + 1] = cvt(kraw[it][j][e] >> 16);
+          qv[j][2 * e] = cvt(qraw[it][j][e]);
+          qv[j][2 * e + 1] = cvt(qraw[it][j][e] >> 16);
+        }
+        const int piece = 4 * (pi >> 1) + (pi & 1) + 2 * j;
+        *reinterpret_cast<u32x4 *>(sK + r * LDK + piece * 8) = *reinterpret_cast<const u32x4 *>(kv[j]);
+        *reinterpret_cast<u32x4 *>(sQ + r * LDK + piece * 8) = *reinterpret_cast<const u32x4 *>(qv[j]);
+      }
+      if constexpr (!RAW) {  // the reduce's K and Q operands, chained order
+        const int cp = 4 * (pi >> 1) + 2 * (pi & 1);
+        T lo[8], hi[8];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = kv[0][e];
+          lo[4 + e] = kv[1][e];
+          hi[e] = kv[0][4 + e];
+          hi[4 + e] = kv[1][4 + e];
+        }
+        *reinterpret_cast<u32x4 *>(img + I.K + tile_off<PK>(r, cp)) = *reinterpret_cast<const u32x4 *>(lo);
+        *reinterpret_cast<u32x4 *>(img + I.K + tile_off<PK>(r, cp + 1)) = *reinterpret_cast<const u32x4 *>(hi);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          lo[e] = qv[0][e];
+          lo[4 + e] = qv[1][e];
+          hi[e] = qv[0][4 + e];
+          hi[4 + e] = qv[1][4 + e];
+        }
+        *reinterpret_cast<u32x4 *>(img + I.Q + tile_off<PK>(r, cp)) = *reinterpret_cast<const u32x4 *>(lo);
+        *reinterpret_cast<u32x4 *>(img + I.Q + tile_off<PK>(r, cp + 1)) = *reinterpret_cast<const u32x4 *>(hi);
+      }
+    }
+    if (tid < kBT) {
+      sB[tid] = bval;
+      sg[tid] = gval;
+    }
+    // the next cell's rows (issued once the current ones are consumed)
+    const int next = cell + gridDim.x;
+    int nr0 = 0, nC = 0;
+    if (next < ncell) cell_rows(next, nr0, nC);
+    __syncthreads();  // S1: K, Q, beta, g in LDS
+
+    const float Gl = wave_inclusive_scan(sg[lane]);  // lane r holds G_r
+    Gw[lane] = Gl;
+    f32x4 a[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) a[i] = zero4();
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      if (w < 2) {
+        typename O::Frag kf[4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R) kf[R] = frag_lds<O>(sK, LDK, 16 * R, KSTEP * s, lane);
+        if (w == 0) {
+#pragma unroll
+          for (int R = 0; R < 4; ++R) a[R] = O::mfma(kf[R], kf[R], a[R]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 6; ++i) a[i] = O::mfma(kf[oS(i)], kf[oR(i)], a[i]);
+        }
+      } else if (w == 2) {
+        typename O::Frag kf[4], qf[4];
+#pragma unroll
+        for (int R = 0; R < 4; ++R) {
+          kf[R] = frag_lds<O>(sK, LDK, 16 * R, KSTEP * s, lane);
+          qf[R] = frag_lds<O>(sQ, LDK, 16 * R, KSTEP * s, lane);
+        }
+#pragma unroll
+        for (int R = 0; R < 4; ++R) a[R] = O::mfma(kf[R], qf[R], a[R]);
+        a[4] = O::mfma(kf[0], qf[1], a[4]);
+      } else {
+        typename O::Frag kf[3], qf[2];
+#pragma unroll
+        for (int R = 0; R < 3; ++R) kf[R] = frag_lds<O>(sK, LDK, 16 * R, KSTEP * s, lane);
+#pragma unroll
+        for (int R = 0; R < 2; ++R) qf[R] = frag_lds<O>(sQ, LDK, 16 * (R + 2), KSTEP * s, lane);
+#pragma unroll
+        for (int i = 1; i < 6; ++i) a[i - 1] = O::mfma(kf[oS(i)], qf[oR(i) - 2], a[i - 1]);
+      }
+    }
+    __syncthreads();  // S2: K and Q are dead, the inverse's scratch takes their bytes
+    if (nC > 0) load(tid, next, nr0, nC);
+
+    if (w == 0) {
+      // L's diagonal blocks, column-major: the product is symmetric, so lane
+      // (row lr, columns 4 lg + e) also holds row 4 lg + e at column lr:
+      //   L_rs = beta_r (K K^T)_rs exp(G_r - G_s), s < r
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        const float gs = Gw[16 * R + lr];
+        const f32x4 gr = *reinterpret_cast<const f32x4 *>(Gw + 16 * R + 4 * lg);
+        const f32x4 br = *reinterpret_cast<const f32x4 *>(sB + 16 * R + 4 * lg);
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = 4 * lg + e > lr ? br[e] * a[R][e] * __expf(gr[e] - gs) : 0.f;
+        *reinterpret_cast<f32x4 *>(sc + LT + R * BS + lr * 64 + lg * 16) = v;
+      }
+      // X_ii = (I + L_ii)^-1, column c = l%16 of block l/16, in column order:
+      // once x_s is final, x_r -= L_rs x_s for every r > s.  Column s of L
+      // is read three steps ahead of its use.
+      const int blk = lane >> 4, c = lane & 15;
+      const char *Lb = sc + LT + blk * BS;
+      float x[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r) x[r] = r == c ? 1.f : 0.f;
+      f32x4 lc[15][4];
+      auto ldcol = [&](int s) {
+#pragma unroll
+        for (int q4 = (s + 1) >> 2; q4 < 4; ++q4) lc[s][q4] = *reinterpret_cast<const f32x4 *>(Lb + s * 64 + 16 * q4);
+      };
+      ldcol(0);
+      ldcol(1);
+      ldcol(2);
+#pragma unroll
+      for (int s = 0; s < 15; ++s) {
+        if (s + 3 < 15) ldcol(s + 3);
+        const float xs = x[s];
+#pragma unroll
+        for (int q4 = (s + 1) >> 2; q4 < 4; ++q4)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (4 * q4 + e > s) x[4 * q4 + e] = fmaf(-lc[s][q4][e], xs, x[4 * q4 + e]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) *reinterpret_cast<float *>(sc + XR + blk * BS + r * 64 + c * 4) = x[r];
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4 *>(sc + XT + blk * BS + c * 64 + 16 * q4) =
+            f32x4{x[4 * q4], x[4 * q4 + 1], x[4 * q4 + 2], x[4 * q4 + 3]};
+    } else if (w == 1) {
+      // L's rows 16..63 as fp16 hi / lo A operands of the levels; the
+      // diagonal tiles 1 and 3, read there against zero operands, zero
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        const int R = oR(i), S = oS(i), r = 16 * R + lr;
+        const float grr = Gw[r], brr = sB[r];
+        const f32x4 gs = *reinterpret_cast<const f32x4 *>(Gw + 16 * S + 4 * lg);
+        h4 hi, lo;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = a[i][e] * brr * __expf(grr - gs[e]);
+          hi[e] = (_Float16)v;
+          lo[e] = lo16(v);
+        }
+        const int o = t8(r - 16, 4 * (S >> 1) + lg, S & 1);
+        *reinterpret_cast<h4 *>(sc + LH + o) = hi;
+        *reinterpret_cast<h4 *>(sc + LL + o) = lo;
+      }
+#pragma unroll
+      for (int R = 1; R < 4; R += 2) {
+        const int o = t8(16 * R - 16 + lr, 4 * (R >> 1) + lg, R & 1);
+        *reinterpret_cast<h4 *>(sc + LH + o) = h4{0, 0, 0, 0};
+        *reinterpret_cast<h4 *>(sc + LL + o) = h4{0, 0, 0, 0};
+      }
+      // the tiles above the diagonal that the reduce reads (the upper halves
+      // of the 32-column k-steps of block rows 0 and 2): zero.  Tiles (0,2),
+      // (0,3), (1,2) and (1,3) are read by no one and not written.
+#pragma unroll
+      for (int R = 0; R < 4; R += 2) {
+        const int o = t8(16 * R + lr, 4 * (R >> 1) + lg, 1);
+        put4(img + I.MM + o, zero4());
+        put4(img + I.TN + o, zero4());
+      }
+    } else if (w == 2) {
+      // M_rs = (Q K^T)_rs exp(G_r - G_s), s <= r: the diagonal tiles, (1, 0)
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const int R = i < 4 ? i : 1, S = i < 4 ? i : 0, r = 16 * R + lr;
+        const float grr = Gw[r];
+        const f32x4 gs = *reinterpret_cast<const f32x4 *>(Gw + 16 * S + 4 * lg);
+        f32x4 mv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float m = a[i][e] * __expf(grr - gs[e]);
+          mv[e] = i == 4 || 4 * lg + e <= lr ? m : 0.f;
+        }
+        put4(img + I.MM + t8(r, 4 * (S >> 1) + lg, S & 1), mv);
+      }
+    } else {
+      // M's tiles (2,0) (2,1) (3,0) (3,1) (3,2); the row vectors
+#pragma unroll
+      for (int i = 1; i < 6; ++i) {
+        const int R = oR(i), S = oS(i), r = 16 * R + lr;
+        const float grr = Gw[r];
+        const f32x4 gs = *reinterpret_cast<const f32x4 *>(Gw + 16 * S + 4 * lg);
+        f32x4 mv;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mv[e] = a[i - 1][e] * __expf(grr - gs[e]);
+        put4(img + I.MM + t8(r, 4 * (S >> 1) + lg, S & 1), mv);
+      }
+      const float GC = Gw[kBT - 1];
+      vec[lane] = __expf(Gl);
+      vec[64 + lane] = __expf(GC - Gl);
+      vec[128 + lane] = sB[lane];
+      const float gC = __expf(GC);
+      for (int d = lane; d < DK; d += 64) vec[192 + d] = gC;
+    }
+    __syncthreads();  // S3: L's hi / lo rows and the diagonal blocks of X are in LDS
+    if (w < 2) {
+      // The B operands X_kj stay in accumulators (chained k order, b_frag's
+      // layout); Tn_ij = X_ij diag(beta_j) is transposed for its row-wise
+      // store by one MFMA against an identity operand.
+      const f32x4 z = zero4();
+      auto bsplit = [&](const f32x4 &t0, const f32x4 &t1, half8 &bh, half8 &bl) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          bh[e] = (_Float16)t0[e];
+          bl[e] = lo16(t0[e]);
+          bh[4 + e] = (_Float16)t1[e];
+          bl[4 + e] = lo16(t1[e]);
+        }
+      };
+      auto mfma3 = [&](const half8 &ah, const half8 &al, const half8 &bh, const half8 &bl, f32x4 c) {
+        c = O::mfma(ah, bh, c);
+        c = O::mfma(ah, bl, c);
+        return O::mfma(al, bh, c);
+      };
+      auto close = [&](int i, const f32x4 &y) {  // -X_ii Y
+        const f32x4 xv = *reinterpret_cast<const f32x4 *>(sc + XR + i * BS + lr * 64 + lg * 16);
+        half8 ah, al, bh, bl;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ah[e] = (_Float16)xv[e];
+          al[e] = lo16(xv[e]);
+          ah[4 + e] = (_Float16)0.f;
+          al[4 + e] = (_Float16)0.f;
+        }
+        bsplit(y, z, bh, bl);
+        const f32x4 r = mfma3(ah, al, bh, bl, z);
+        return f32x4{-r[0], -r[1], -r[2], -r[3]};
+      };
+      auto lev = [&](int i, int s, const f32x4 &t0, const f32x4 &t1, const f32x4 &y) {  // y + L_i,[2s,2s+1] [t0; t1]
+        const int o = tile_off<8>(16 * i - 16 + lr, 4 * s + lg);
+        const half8 ah = *reinterpret_cast<const half8 *>(sc + LH + o);
+        const half8 al = *reinterpret_cast<const half8 *>(sc + LL + o);
+        half8 bh, bl;
+        bsplit(t0, t1, bh, bl);
+        return mfma3(ah, al, bh, bl, y);
+      };
+      auto xcol = [&](int j) {  // X_jj as an accumulator tile
+        return *reinterpret_cast<const f32x4 *>(sc + XT + j * BS + lr * 64 + lg * 16);
+      };
+      auto put_tn = [&](int i, int j, const f32x4 &x) {
+        const float bj = sB[16 * j + lr];
+        half8 ident, av;  // B = [I; 0]: lane l supplies rows 4 (l/16) .. +3 of column l%16
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          ident[e] = (_Float16)(4 * lg + e == lr ? 1.f : 0.f);
+          ident[4 + e] = (_Float16)0.f;
+          av[e] = (_Float16)(x[e] * bj);
+          av[4 + e] = (_Float16)0.f;
+        }
+        put4(img + I.TN + t8(16 * i + lr, 4 * (j >> 1) + lg, j & 1), O::mfma(av, ident, z));
+      };
+      if (w == 0) {
+        const f32x4 x00 = xcol(0);
+        const f32x4 x10 = close(1, lev(1, 0, x00, z, z));
+        const f32x4 x20 = close(2, lev(2, 0, x00, x10, z));
+        const f32x4 x30 = close(3, lev(3, 1, x20, z, lev(3, 0, x00, x10, z)));
+        put_tn(1, 0, x10);
+        put_tn(2, 0, x20);
+        put_tn(3, 0, x30);
+      } else {
+        const f32x4 x11 = xcol(1), x22 = xcol(2);
+        const f32x4 x21 = close(2, lev(2, 0, z, x11, z));
+        const f32x4 x31 = close(3, lev(3, 1, x21, z, lev(3, 0, z, x11, z)));
+        const f32x4 x32 = close(3, lev(3, 1, x22, z, z));
+        put_tn(2, 1, x21);
+        put_tn(3, 1, x31);
+        put_tn(3, 2, x32);
+      }
+    } else if (w == 2) {
+      // Tn's diagonal tiles: X_RR diag(beta), strict lower
+#pragma unroll
+      for (int R = 0; R < 4; ++R) {
+        const f32x4 xr = *reinterpret_cast<const f32x4 *>(sc + XR + R * BS + lr * 64 + lg * 16);
+        const f32x4 bs = *reinterpret_cast<const f32x4 *>(sB + 16 * R + 4 * lg);
+        f32x4 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) v[e] = 4 * lg + e < lr ? xr[e] * bs[e] : 0.f;
+        put4(img + I.TN + t8(16 * R + lr, 4 * (R >> 1) + lg, R & 1), v);
+      }
+    }
+    if (nC <= 0) break;  // no next cell, or a sentinel (slots fill in order)
+    cell = next;
+    __syncthreads();  // S4: the scratch is free for the next cell's K and Q
+  }
+}
+
 }  // namespace
 
 template <bool KDA, typename In, int DK, bool RAW>
@@ -851,10 +1029,34 @@ static hipError_t launch_map_t(const MapParams &p, hipStream_t st) {
   return hipGetLastError();
 }
 
+// the 16-bit GDN kernel's grid: as many workgroups as the device holds at
+// once (CUs x resident workgroups per CU, found once per device), capped by
+// the cells
+template <typename In, int DK, bool RAW>
+static hipError_t launch_map16(const MapParams &p, hipStream_t st) {
+  static int slots[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  int res = dev < 64 ? slots[dev] : 0;
+  if (res == 0) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, chunk_map16_kernel<In, DK, RAW>, kThreads, 0) !=
+            hipSuccess)
+      return hipErrorInvalidValue;
+    res = cus * per > 0 ? cus * per : 1;
+    if (dev < 64) slots[dev] = res;
+  }
+  const int cells = p.H * p.NT_max;
+  const int grid = cells < res ? cells : res;
+  hipLaunchKernelGGL((chunk_map16_kernel<In, DK, RAW>), dim3(grid), dim3(kThreads), 0, st, p);
+  return hipGetLastError();
+}
+
 template <typename In, int DK>
 static hipError_t launch_map_d(const MapParams &p, bool kda, hipStream_t st) {
   if (kda) return launch_map_t<true, In, DK, false>(p, st);
-  return p.raw_kq ? launch_map_t<false, In, DK, true>(p, st) : launch_map_t<false, In, DK, false>(p, st);
+  return p.raw_kq ? launch_map16<In, DK, true>(p, st) : launch_map16<In, DK, false>(p, st);
 }
 
 template <typename In>

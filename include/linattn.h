@@ -151,6 +151,10 @@ typedef struct {
  *                    GDN with 16-bit inputs
  *   Tn    [BT][BT]   T = A^-1 diag(beta) with its diagonal removed
  *   M     [BT][BT]   masked decayed Q K^T (lower triangle incl. diagonal)
+ *                    (of the 16x16 tiles above the diagonal of Tn and M only
+ *                    (0,1) and (2,3) are written, as zeros; with GDN and
+ *                    16-bit inputs the others are left as they were, since
+ *                    the reduce never reads them)
  *   vec   [192 + d_k] fp32: exp(G_r), exp(G_C - G_r), beta_r (BT each), then
  *                    the state decay of each key row; padded to 1 KiB
  * where G is the chunk-local cumulative gate and G_C its last row.  Matrices

@@ -18,6 +18,13 @@ from tests.helpers import (TOL, compare, decode_images, gva, rel_err, rel_err_bf
 
 pytestmark = pytest.mark.gpu
 
+# 16x16 tiles (R, S) of a chunk's Tn and M that the reduce reads
+READ_TILES = np.zeros((64, 64), dtype=bool)
+for _R in range(4):
+    for _S in range(4):
+        if _S <= _R or (_R, _S) in ((0, 1), (2, 3)):
+            READ_TILES[16 * _R:16 * _R + 16, 16 * _S:16 * _S + 16] = True
+
 
 def _say(*a):
     print(*a, flush=True)
@@ -91,6 +98,27 @@ def test_small_bf16(kda, d, split):
     assert eo <= tol and eh <= tol
 
 
+@pytest.mark.parametrize("dtype,split", [("bf16", 0), ("bf16", 2), ("f16", 0), ("f16", 1)],
+                         ids=["bf16-32col", "bf16-64col", "f16-32col", "f16-128col"])
+def test_nan_filled_workspace(dtype, split):
+    """The reduce reads only workspace bytes the map wrote: a workspace whose
+    every byte starts as 0xFF (NaN in fp16 and fp32) gives the same parity."""
+    inp = make_inputs(SMALL_CU[-1], 3, 128, 128, kda=False, dtype=dtype, seed=44 + split,
+                      cu_seqlens=SMALL_CU, h0_std=0.1)
+    d = to_dev(inp)
+    T = inp["q"].shape[0]
+    ci, co, _ = la.build_chunk_meta(d["cu_seqlens"], T)
+    n = la.workspace_bytes(T, len(SMALL_CU) - 1, 3, 128, 128, d["q"].dtype, False, dv_split=split)
+    ws = torch.full((n,), 0xFF, dtype=torch.uint8, device="cuda")
+    o, ht = la.gdn_chunk_fwd(d["q"], d["k"], d["v"], d["g"], d["beta"], d["cu_seqlens"], ci, co,
+                             h0=d["h0"], output_final_state=True, workspace=ws, dv_split=split)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = run_oracle(inp)
+    eo, eh, tol = compare(inp, o, ht, o_ref, ht_ref)
+    _say(f"NaN-filled workspace {dtype} split={split}: o {eo:.2e} ht {eh:.2e}")
+    assert eo <= tol and eh <= tol
+
+
 @pytest.mark.parametrize("kda", [False, True], ids=["gdn", "kda"])
 def test_small_fp32(kda):
     inp = make_inputs(SMALL_CU[-1], 2, 64, 64, kda=kda, dtype="f32", seed=31,
@@ -123,7 +151,8 @@ def test_map_stage_matrices(kda, split):
     dv = to_dev(inp)
     ci, co, _ = la.build_chunk_meta(dv["cu_seqlens"], 230)
     nbytes = la.workspace_bytes(230, 3, 2, d, d, torch.bfloat16, kda, dv_split=split)
-    ws = torch.zeros(nbytes, dtype=torch.uint8, device="cuda")
+    # bytes the map does not write read back as NaN (0xFFFF in fp16 and fp32)
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
     la.chunk_fwd_stages(kda, la.STAGE_MAP, dv["q"], dv["k"], dv["v"], dv["g"], dv["beta"],
                         dv["cu_seqlens"], ci, co, workspace=ws, dv_split=split)
     torch.cuda.synchronize()
@@ -141,7 +170,14 @@ def test_map_stage_matrices(kda, split):
             for h in range(2):
                 it = inter[(slot, h)]
                 im = img[(slot, h)]
-                tn, mm, vec = im["TN"], im["MM"], im["VEC"]
+                # the tiles the reduce reads: the lower block triangle and the
+                # upper halves of the 32-column k-steps of block rows 0 and 2
+                # ((0,1) and (2,3), zero); no other tile is promised
+                assert np.isfinite(im["TN"][READ_TILES]).all()
+                assert np.isfinite(im["MM"][READ_TILES]).all()
+                tn = np.where(READ_TILES, im["TN"], 0.0)
+                mm = np.where(READ_TILES, im["MM"], 0.0)
+                vec = im["VEC"]
                 Tref = it["T"] - np.diag(np.diag(it["T"]))
                 assert rel_err(tn[:C, :C], Tref) < 2e-3, (slot, h)
                 assert rel_err(mm[:C, :C], it["M"]) < 2e-3, (slot, h)
