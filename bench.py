@@ -107,11 +107,11 @@ def alg_flops(inp):
 
 
 def kernel_sources(kind, inp=None):
-    """The source files (besides the shared headers) of a kernel kind; the
-    reduce of 16-bit inputs has its own file."""
+    """The source files (besides the shared headers) of a kernel kind; 16-bit
+    inputs run the 32-column reduce of its own file or the general one."""
     if kind == "reduce":
         sixteen = inp is None or inp["dtype"] != "f32"
-        return ["reduce_work.h", "chunk_reduce16.hip" if sixteen else "chunk_reduce.hip"]
+        return ["reduce_work.h"] + (["chunk_reduce16.hip"] if sixteen else []) + ["chunk_reduce.hip"]
     return [{"map": "chunk_map.hip", "recurrent": "recurrent.hip", "conv": "short_conv.hip"}[kind]]
 
 # decode workloads: sequences (one token each), heads, head dim

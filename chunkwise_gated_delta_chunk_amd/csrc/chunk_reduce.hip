@@ -56,11 +56,16 @@ namespace la {
 namespace {
 
 // Geometry shared by the kernel (LDS size) and its body.
-template <bool KDA, typename In, int DK, int NW>
+template <bool KDA, typename In, int DK, int NW, bool RAW>
 struct ReduceShape {
   using O = Op<In>;
   static constexpr int E = (int)sizeof(typename O::T);
   static constexpr ImageLayout I = image_layout(KDA, E, DK);
+  // RAW (GDN, 16-bit): the image in the workspace starts at Tn; K and Q are
+  // staged from the raw rows of k and q by the copy waves (a second one for Q)
+  static constexpr int SKIP = image_skip(KDA, E, DK, RAW);
+  static constexpr int HBM = image_hbm_bytes(KDA, E, DK, RAW);
+  static constexpr int THREADS = 64 * (NW + 1 + (RAW ? 1 : 0));
   static constexpr int W = 16 * NW;                       // state columns per workgroup
   static constexpr int V_BYTES = kBT * W * (int)sizeof(In);
   // stage buffer: the V tile first (its reads and those of K and Q stay
@@ -70,10 +75,10 @@ struct ReduceShape {
   static constexpr int NBUF = 2 * STAGE <= 160 * 1024 ? 2 : 1;
 };
 
-template <bool KDA, typename In, int DK, int NW, bool OUT>
+template <bool KDA, typename In, int DK, int NW, bool OUT, bool RAW>
 __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &wk, char *smem) {
   using O = Op<In>;
-  using SH = ReduceShape<KDA, In, DK, NW>;
+  using SH = ReduceShape<KDA, In, DK, NW, RAW>;
   constexpr int E = SH::E;
   constexpr ImageLayout I = SH::I;
   constexpr bool HAS_KT = KDA || O::KPL == 1;
@@ -89,15 +94,16 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
   constexpr int IMG = SH::IMG;
   constexpr int STAGE = SH::STAGE;
   constexpr int NBUF = SH::NBUF;
-  constexpr int NVL = V_BYTES / 1024, NIMG = I.BYTES / 1024;
+  constexpr int NVL = V_BYTES / 1024, NIMG = SH::HBM / 1024;
   static_assert(I.BYTES % 1024 == 0 && V_BYTES % 1024 == 0, "1 KiB staging pieces");
+  static_assert(!RAW || (F16 && !KDA && NBUF == 2), "raw K / Q staging: 16-bit GDN, two buffers");
   static_assert(!F16 || IMG + I.Q + 3 * 256 * PK + 16 <= 65536, "immediate offsets");
 
   const int H = p.H;
   const int n = wk.n, h = wk.h, j0 = wk.j0, j1 = wk.j1, eos = wk.eos;
   (void)n;
   const int lane = lane_id(), w = wave_id();
-  const bool copier = w == NW;  // the extra wave only stages operands
+  const bool copier = w >= NW;  // the extra wave(s) only stage operands
   const int lr = lane & 15, lg = lane >> 4;
   const int cw = wk.col0 + 16 * w;                   // this wave's first state column
   const int rs_v = H * DV * (int)sizeof(In);         // token stride of v (bytes)
@@ -118,26 +124,37 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
     const int row = e / PV, phys = e % PV;
     voff[q] = row * rs_v + ((phys ^ swz<PV>(row)) << 4);
   }
-  const char *img_c = static_cast<const char *>(p.img) + ((size_t)j0 * H + h) * I.BYTES;
-  const size_t img_step = (size_t)H * I.BYTES;
+  const char *img_c = static_cast<const char *>(p.img) + ((size_t)j0 * H + h) * SH::HBM;
+  const size_t img_step = (size_t)H * SH::HBM;
   const In *v_c = static_cast<const In *>(p.v) + ((size_t)wk.t0 * H + h) * DV + (wk.vzero ? 0 : wk.col0);
   const size_t v_step = (size_t)kBT * H * DV;
   // copy of the chunk whose image starts at img and whose C V rows start at vrow
   // (no output: the Q and M pieces of the image are not needed; a zero V
   // has an empty range, so its loads write zeros)
   auto copy_chunk = [&](int buf, const char *img, const In *vrow, int C) {
-    const auto ri = buffer_rsrc(img, I.BYTES);
+    const auto ri = buffer_rsrc(img, C > 0 ? SH::HBM : 0);
     const auto rv = buffer_rsrc(vrow, wk.vzero ? 0 : C * rs_v);
     char *dst = smem + buf * STAGE;
 #pragma unroll
     for (int q = 0; q < NVL; ++q) copy16_to_lds(rv, dst + q * 1024, voff[q], 0);
 #pragma unroll
     for (int q = 0; q < NIMG; ++q) {
-      const bool unused = !OUT && ((q * 1024 >= I.Q && q * 1024 < I.Q + kBT * DK * E) ||
-                                   (q * 1024 >= I.MM && q * 1024 < I.MM + kBT * kBT * E));
-      if (!unused) copy16_to_lds(ri, dst + (NVL + q) * 1024, lane * 16, q * 1024);
+      const int at = SH::SKIP + q * 1024;  // stage offset of the piece
+      const bool unused = !OUT && ((at >= I.Q && at < I.Q + kBT * DK * E) ||
+                                   (at >= I.MM && at < I.MM + kBT * kBT * E));
+      if (!unused) copy16_to_lds(ri, dst + IMG + at, lane * 16, q * 1024);
     }
   };
+  // the direct loads copy_chunk issues (compile-time count)
+  constexpr int NDMA = [] {
+    int n = NVL;
+    for (int q = 0; q < NIMG; ++q) {
+      const int at = SH::SKIP + q * 1024;
+      n += !(!OUT && ((at >= SH::I.Q && at < SH::I.Q + kBT * DK * SH::E) ||
+                      (at >= SH::I.MM && at < SH::I.MM + kBT * kBT * SH::E)));
+    }
+    return n;
+  }();
 
   // ---------------------------------------------------------- LDS patterns
   // per-lane byte addresses, one set per buffer; immediates add the rest
@@ -513,6 +530,113 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
   };
 
   // ---------------------------------------------------------- chunk loop
+  if constexpr (RAW) {
+    if (copier) {
+      // Two copy waves.  Wave NW stages V and the image (from Tn on) by
+      // direct loads and K from the raw rows of k; wave NW + 1 stages Q from
+      // the raw rows of q (when there is output).  Raw rows are loaded two
+      // chunks ahead into registers and converted to fp16 in the chained k
+      // order one chunk ahead, into the buffer the compute waves will read
+      // next.  Unit i of a lane: row r, 32-element block b, half g2: input
+      // pieces 4b + g2 and 4b + 2 + g2 hold the chained pieces 4b + 2 g2
+      // (their low halves) and 4b + 2 g2 + 1 (their high halves).  Loads past
+      // the sequence run over empty ranges (zeros, no memory traffic), so the
+      // counts the vmcnt waits rely on stay fixed.
+      const int cpw = w - NW;
+      const bool active = cpw == 0 || OUT;
+      constexpr int NU = DK / 16, UPR = DK / 16;  // units per lane, per row
+      const In *src = static_cast<const In *>(cpw == 0 ? p.k_raw : p.q_raw);
+      const int Hqk = p.Hqk, hqk = h / (H / Hqk);
+      const int rs_q = Hqk * DK * (int)sizeof(In);  // token stride of q, k (bytes)
+      const In *src_c = src + ((size_t)wk.t0 * Hqk + hqk) * DK;
+      const size_t src_step = (size_t)kBT * Hqk * DK;
+      int roff0[NU], roff1[NU];
+      uint32_t loff[NU];
+#pragma unroll
+      for (int i = 0; i < NU; ++i) {
+        const int u = lane + 64 * i;
+        const int r = u / UPR, b = (u % UPR) >> 1, g2 = u & 1;
+        roff0[i] = r * rs_q + (4 * b + g2) * 16;
+        roff1[i] = r * rs_q + (4 * b + 2 + g2) * 16;
+        loff[i] = (uint32_t)(IMG + (cpw == 0 ? I.K : I.Q) + tile_off<PK>(r, 4 * b + 2 * g2));
+      }
+      u32x4 raw[2][NU][2];
+      auto chunk_rows = [&](int jj) { return jj < j1 ? min(kBT, eos - (wk.t0 + (jj - j0) * kBT)) : 0; };
+      auto load_raw = [&](auto rc, int jj) {
+        constexpr int RB = decltype(rc)::value;
+        const int C = active ? chunk_rows(jj) : 0;
+        const auto rr = buffer_rsrc(src_c + (size_t)(jj - j0) * src_step, C * rs_q);
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+          raw[RB][i][0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, roff0[i], 0, 0));
+          raw[RB][i][1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rr, roff1[i], 0, 0));
+        }
+      };
+      auto put_raw = [&](auto rc, int buf) {
+        constexpr int RB = decltype(rc)::value;
+        if (!active) return;
+        const uint32_t b0 = base + buf * STAGE;
+#pragma unroll
+        for (int i = 0; i < NU; ++i) {
+          const u32x4 &a = raw[RB][i][0], &c = raw[RB][i][1];
+          const u32x4 lo = {to_f16x2<In>(a[0]), to_f16x2<In>(a[1]), to_f16x2<In>(c[0]), to_f16x2<In>(c[1])};
+          const u32x4 hi = {to_f16x2<In>(a[2]), to_f16x2<In>(a[3]), to_f16x2<In>(c[2]), to_f16x2<In>(c[3])};
+          ds_write_b128(b0 + loff[i], lo);
+          ds_write_b128(b0 + (loff[i] ^ 16u), hi);
+        }
+      };
+      // direct loads of chunk jj into buffer buf (wave NW only)
+      auto dma = [&](int buf, int jj) {
+        if (cpw != 0) return;
+        copy_chunk(buf, img_c + (size_t)(jj - j0) * img_step, v_c + (size_t)(jj - j0) * v_step,
+                   chunk_rows(jj));
+      };
+      constexpr int NR = 2 * NU;  // raw loads per chunk
+      auto run = [&](auto cpc) {
+        constexpr int CP = decltype(cpc)::value;
+        constexpr int ND = CP == 0 ? NDMA : 0;
+        // prologue, in the steady state's issue order: the first chunk's raw
+        // rows, its direct loads, the second chunk's raw rows; then the
+        // first chunk's K / Q into buffer 0
+        load_raw(std::integral_constant<int, 0>{}, j0);
+        issue_fence();
+        dma(0, j0);
+        issue_fence();
+        load_raw(std::integral_constant<int, 1>{}, j0 + 1);
+        issue_fence();
+        wait_vm<ND + NR>();  // raw rows of j0
+        put_raw(std::integral_constant<int, 0>{}, 0);
+        wait_vm<NR>();       // direct loads of j0
+        wait_lgkm<0>();
+        chunk_barrier();     // the first chunk's stage has landed in buffer 0
+        // chunk jj: buffer and register set B hold it; the next chunk goes
+        // to the other buffer once every compute wave is done with it
+        auto step = [&](auto bc, int jj) {
+          constexpr int B = decltype(bc)::value;
+          chunk_barrier();  // opens chunk jj: chunk jj - 1's buffer is free
+          issue_fence();
+          dma(1 - B, jj + 1);
+          issue_fence();
+          load_raw(std::integral_constant<int, B>{}, jj + 2);
+          issue_fence();
+          wait_vm<ND + NR>();  // raw rows of jj + 1
+          put_raw(std::integral_constant<int, 1 - B>{}, 1 - B);
+          wait_vm<NR>();       // direct loads of jj + 1
+          wait_lgkm<0>();
+        };
+        for (int jj = j0;;) {
+          step(std::integral_constant<int, 0>{}, jj);
+          if (++jj == j1) break;
+          step(std::integral_constant<int, 1>{}, jj);
+          if (++jj == j1) break;
+        }
+        wait_vm<0>();
+      };
+      if (cpw == 0) run(std::integral_constant<int, 0>{});
+      else run(std::integral_constant<int, 1>{});
+      return;
+    }
+  }
   if (copier) {
     copy_chunk(0, img_c, v_c, min(kBT, eos - wk.t0));
     if constexpr (F16) {  // the compute waves read the first chunk's V for cs
@@ -590,28 +714,37 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
   }
 }
 
-template <bool KDA, typename In, int DK, int NW>
-__global__ __launch_bounds__(64 * (NW + 1)) void chunk_reduce_kernel(ReduceParams p) {
-  using SH = ReduceShape<KDA, In, DK, NW>;
+template <bool KDA, typename In, int DK, int NW, bool RAW>
+__global__ __launch_bounds__(64 * (NW + 1 + (RAW ? 1 : 0))) void chunk_reduce_kernel(ReduceParams p) {
+  using SH = ReduceShape<KDA, In, DK, NW, RAW>;
   __shared__ __attribute__((aligned(16))) char smem[SH::NBUF * SH::STAGE];
   Work wk;
   const int role = decode_work<DK, SH::W>(p, wk);
-  if (role == 1) reduce_body<KDA, In, DK, NW, true>(p, wk, smem);
-  else if (role == 2) reduce_body<KDA, In, DK, NW, false>(p, wk, smem);
+  if (role == 1) reduce_body<KDA, In, DK, NW, true, RAW>(p, wk, smem);
+  else if (role == 2) reduce_body<KDA, In, DK, NW, false, RAW>(p, wk, smem);
 }
 
 }  // namespace
 
-template <bool KDA, typename In, int DK, int NW>
+template <bool KDA, typename In, int DK, int NW, bool RAW = false>
 static hipError_t launch_reduce_t(const ReduceParams &p, hipStream_t st) {
+  using SH = ReduceShape<KDA, In, DK, NW, RAW>;
   const int units = (p.seg ? p.NS_max : p.N_max) * p.H;
   const int grid = ((units + 7) / 8) * 8 * (p.pass == 1 ? p.S + p.SP : p.S);
-  hipLaunchKernelGGL((chunk_reduce_kernel<KDA, In, DK, NW>), dim3(grid), dim3(64 * (NW + 1)), 0, st, p);
+  hipLaunchKernelGGL((chunk_reduce_kernel<KDA, In, DK, NW, RAW>), dim3(grid), dim3(SH::THREADS), 0, st,
+                     p);
   return hipGetLastError();
 }
 
 template <bool KDA, typename In, int DK>
 static hipError_t launch_reduce_w(const ReduceParams &p, int W, hipStream_t st) {
+  // raw K / Q staging: 16-bit GDN at 64 columns
+  if (p.raw_kq) {
+    if constexpr (!KDA && sizeof(In) == 2) {
+      if (W == 64) return launch_reduce_t<KDA, In, DK, 4, true>(p, st);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (W) {
     case 32: return launch_reduce_t<KDA, In, DK, 2>(p, st);
     case 64: return launch_reduce_t<KDA, In, DK, 4>(p, st);

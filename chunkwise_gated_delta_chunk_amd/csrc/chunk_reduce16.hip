@@ -82,47 +82,6 @@ struct R16 {
 __device__ __host__ constexpr int fR(int i) { return i < 2 ? i : (i + 2) / 2; }
 __device__ __host__ constexpr int fS(int i) { return i < 2 ? 0 : (i & 1); }
 
-template <int N>
-__device__ __forceinline__ void wait_lgkm() {
-  static_assert(N >= 0 && N <= 15, "lgkmcnt");
-  asm volatile("s_waitcnt lgkmcnt(%0)" ::"n"(N) : "memory");
-}
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N <= 63, "vmcnt");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-// Keeps the vector memory operations issued before it ahead of those issued
-// after it: the copy waves' vmcnt waits count operations in issue order, so
-// neither the compiler nor its scheduler may interleave the groups.
-__device__ __forceinline__ void issue_fence() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
-template <int OFF>
-__device__ __forceinline__ void ds_write_b128_at(uint32_t a, const u32x4 &v) {
-  static_assert(OFF >= 0 && OFF < 65536, "DS immediate offset");
-  asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(a), "v"(v), "n"(OFF) : "memory");
-}
-template <int OFF>
-__device__ __forceinline__ void ds_write_b32_at(uint32_t a, float v) {
-  static_assert(OFF >= 0 && OFF < 65536, "DS immediate offset");
-  asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(a), "v"(v), "n"(OFF) : "memory");
-}
-__device__ __forceinline__ void ds_write_b128(uint32_t a, const u32x4 &v) {
-  asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
-}
-// two bf16 / fp16 input values in one word -> two fp16 (nearest even)
-template <typename In>
-__device__ __forceinline__ uint32_t to_f16x2(uint32_t w) {
-  if constexpr (std::is_same<In, f16>::value) {
-    return w;
-  } else {
-    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
-    const h2 r = {(_Float16)__uint_as_float(w << 16), (_Float16)__uint_as_float(w & 0xffff0000u)};
-    return __builtin_bit_cast(uint32_t, r);
-  }
-}
 __device__ __forceinline__ half8 as_half8(const u32x4 &v) { return __builtin_bit_cast(half8, v); }
 __device__ __forceinline__ u32x4 as_u32x4(const half8 &v) { return __builtin_bit_cast(u32x4, v); }
 

@@ -26,8 +26,10 @@ struct MapParams {
 struct ReduceParams {
   const void *v;
   // 16-bit GDN: the raw q, k rows ([T][Hqk][d_k]), staged by the reduce itself
+  // (always at 32 columns; at 64 columns when raw_kq is set)
   const void *q_raw, *k_raw;
   int Hqk;
+  int raw_kq;
   const void *cu_seqlens;  // int32, or int64 with cu64
   const int32_t *chunk_offsets;
   int cu64;

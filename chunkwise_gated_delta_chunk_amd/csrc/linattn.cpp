@@ -114,8 +114,14 @@ int seg_split(const la_chunk_fwd_args *a) {
 // the d_v slices of the forward's reduce
 int fwd_split(const la_chunk_fwd_args *a) { return seg_for(a) ? seg_split(a) : split_for(a); }
 
-// whether the map stores no K, Q (the reduce stages them from the raw rows)
-bool raw_kq(const la_chunk_fwd_args *a, bool kda) { return !kda && reduce16(a, fwd_split(a)); }
+// whether the map stores no K, Q: GDN with 16-bit inputs in 32- or 64-column
+// slices, whose reduces stage them from the raw q, k rows (128-column slices
+// read them from the image)
+bool raw_kq(const la_chunk_fwd_args *a, bool kda) {
+  if (kda || a->qkv_dtype == LA_F32) return false;
+  const int W = a->d_v / fwd_split(a);
+  return W == 32 || W == 64;
+}
 
 // segment slots: ceil(T_max / (BT L)) + N_max - 1
 int64_t ns_max(const la_chunk_fwd_args *a, int L) {
@@ -210,6 +216,7 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     rp.q_raw = a->q;
     rp.k_raw = a->k;
     rp.Hqk = a->H_qk ? a->H_qk : a->H;
+    rp.raw_kq = raw_kq(a, kda);
     rp.cu_seqlens = a->cu_seqlens;
     rp.cu64 = a->cu_seqlens_i64;
     rp.chunk_offsets = meta.co;
@@ -618,6 +625,7 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
     rp.q_raw = a->q;
     rp.k_raw = a->k;
     rp.Hqk = a->H_qk ? a->H_qk : a->H;
+    rp.raw_kq = raw_kq(&f, kda);
     rp.S = split_for(&f);
     rp.scale = a->scale;
     rp.hsave = reinterpret_cast<float *>(ws + L.hs);

@@ -123,11 +123,11 @@ def test_workspace_size_and_split():
     import torch
     for (T, N, H, d, dt, esz, raw) in [(8192, 8, 16, 128, torch.bfloat16, 2, True),
                                        (256, 1, 2, 64, torch.float32, 4, False),
-                                       (16384, 64, 32, 128, torch.bfloat16, 2, False)]:
+                                       (16384, 64, 32, 128, torch.bfloat16, 2, True)]:
         cells = meta_ref.nt_max(T, N, 64) * H
         # one image per cell: K, Q, [K^T: KDA or fp32], Tn, M, vec padded to
-        # 1 KiB; GDN with 16-bit inputs in 32-column slices (raw) stores no K
-        # and Q (its reduce stages them itself)
+        # 1 KiB; GDN with 16-bit inputs in 32- or 64-column slices (raw)
+        # stores no K and Q (its reduce stages them itself)
         vec = -(-(192 + d) * 4 // 1024) * 1024
         kt = 64 * d * esz
         gdn = (0 if raw else 2 * 64 * d * esz) + (kt if esz == 4 else 0) + \
@@ -135,9 +135,13 @@ def test_workspace_size_and_split():
         assert la.workspace_bytes(T, N, H, d, d, dt) == cells * gdn
         kda = 2 * 64 * d * esz + kt + 2 * 64 * 64 * esz + vec
         assert la.workspace_bytes(T, N, H, d, d, dt, kda=True) == cells * kda
-    # a 64-column split of the first shape stores K and Q again
-    full = (2 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 2048) * meta_ref.nt_max(8192, 8, 64) * 16
-    assert la.workspace_bytes(8192, 8, 16, 128, 128, torch.bfloat16, dv_split=2) == full
+    # a 64-column split of the first shape stages K and Q from the raw rows
+    # too; a 128-column one stores them again
+    cells = meta_ref.nt_max(8192, 8, 64) * 16
+    raw = (2 * 64 * 64 * 2 + 2048) * cells
+    full = (2 * 64 * 128 * 2 + 2 * 64 * 64 * 2 + 2048) * cells
+    assert la.workspace_bytes(8192, 8, 16, 128, 128, torch.bfloat16, dv_split=2) == raw
+    assert la.workspace_bytes(8192, 8, 16, 128, 128, torch.bfloat16, dv_split=1) == full
     assert la.workspace_bytes(0, 1, 1, 64, 64, torch.bfloat16) == 0
     # 64 columns per workgroup, 32 when that leaves at most one workgroup per
     # CU (256 of them)
