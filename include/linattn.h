@@ -145,16 +145,16 @@ typedef struct {
  * multiple of 1 KiB.  With e = 2 (bf16, fp16 inputs: fp16 values) or 4 (fp32
  * inputs), a cell holds in order
  *   K, Q  [BT][d_k]  the chunk's keys and queries (KDA: K*exp(G), Q*exp(G));
- *                    absent for GDN with 16-bit inputs in 32-column slices,
- *                    whose reduce reads the rows of k and q itself
+ *                    absent for GDN with 16-bit inputs in 32- or 64-column
+ *                    slices, whose reduce reads the rows of k and q itself
  *   KT    [d_k][BT]  KDA: (K*exp(G_C - G))^T; fp32 inputs: K^T; absent for
  *                    GDN with 16-bit inputs
  *   Tn    [BT][BT]   T = A^-1 diag(beta) with its diagonal removed
  *   M     [BT][BT]   masked decayed Q K^T (lower triangle incl. diagonal)
- *                    (of the 16x16 tiles above the diagonal of Tn and M only
- *                    (0,1) and (2,3) are written, as zeros; with GDN and
- *                    16-bit inputs the others are left as they were, since
- *                    the reduce never reads them)
+ *                    Above the diagonal of Tn and M the reduce reads only the
+ *                    16x16 tiles (0,1) and (2,3), which are written as zeros;
+ *                    with GDN and 16-bit inputs the other upper tiles are
+ *                    not written, otherwise they are zeros too
  *   vec   [192 + d_k] fp32: exp(G_r), exp(G_C - G_r), beta_r (BT each), then
  *                    the state decay of each key row; padded to 1 KiB
  * where G is the chunk-local cumulative gate and G_C its last row.  Matrices
