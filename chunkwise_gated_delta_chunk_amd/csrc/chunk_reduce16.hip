@@ -358,6 +358,28 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
     const int off_st = (lane / LPR) * rs_o + (cw0 + 4 * (lane % LPR)) * osz;
     char *o_c = static_cast<char *>(p.o) + ((size_t)wk.t0 * H + h) * DV * osz;
     const size_t o_step = (size_t)kBT * H * DV * osz;
+    // rows of chunk jj's O tile -> o (C valid rows)
+    auto store_o = [&](const f32x4 *orow, int jj, int C) {
+      char *o_r = o_c + (size_t)(jj - j0) * o_step;
+#pragma unroll
+      for (int i = 0; i < 4 * CT; ++i) {
+        const auto ro = buffer_rsrc(o_r + (size_t)RPI * i * rs_o, (C - RPI * i) * rs_o);
+        if (p.o_bf16) {
+          const uint32_t w0 = f32_to_bf16_rne(orow[i][0]) | (f32_to_bf16_rne(orow[i][1]) << 16);
+          const uint32_t w1 = f32_to_bf16_rne(orow[i][2]) | (f32_to_bf16_rne(orow[i][3]) << 16);
+          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+          __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, ro, off_st, 0, 0);
+        } else {
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, orow[i]), ro, off_st, 0, 0);
+        }
+      }
+    };
+    // A chunk's O rows are stored during the next chunk, once that chunk's
+    // first LDS reads are issued: the stores then queue behind the copy
+    // waves' loads while this wave waits for its operands anyway, instead of
+    // holding up the barrier that opens the next chunk.
+    f32x4 opend[4 * CT];
+    int jpend = j0, cpend = 0;  // cpend > 0: the O rows of chunk jpend are pending
     auto ochunk = [&](auto bc, int jj) {
       constexpr int B = decltype(bc)::value;
       chunk_barrier();  // B0
@@ -386,6 +408,7 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
         };
         read_q(std::integral_constant<int, 0>{});
         if constexpr (NKD > 1) read_q(std::integral_constant<int, 1>{});
+        if (cpend > 0) store_o(opend, jpend, cpend);
         f32x4 yq[CT][4];
 #pragma unroll
         for (int c = 0; c < CT; ++c)
@@ -471,19 +494,10 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
           wait_lds_tied8<0>(orow[0], orow[1], orow[2], orow[3], orow[4], orow[5], orow[6], orow[7]);
         else
           wait_lds_tied4<0>(orow[0], orow[1], orow[2], orow[3]);
-        char *o_r = o_c + (size_t)(jj - j0) * o_step;
 #pragma unroll
-        for (int i = 0; i < 4 * CT; ++i) {
-          const auto ro = buffer_rsrc(o_r + (size_t)RPI * i * rs_o, (C - RPI * i) * rs_o);
-          if (p.o_bf16) {
-            const uint32_t w0 = f32_to_bf16_rne(orow[i][0]) | (f32_to_bf16_rne(orow[i][1]) << 16);
-            const uint32_t w1 = f32_to_bf16_rne(orow[i][2]) | (f32_to_bf16_rne(orow[i][3]) << 16);
-            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-            __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, ro, off_st, 0, 0);
-          } else {
-            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, orow[i]), ro, off_st, 0, 0);
-          }
-        }
+        for (int i = 0; i < 4 * CT; ++i) opend[i] = orow[i];
+        jpend = jj;
+        cpend = C;
       }
     };
     for (int jj = j0;;) {
@@ -492,6 +506,7 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
       ochunk(std::integral_constant<int, 1>{}, jj);
       if (++jj == j1) break;
     }
+    if (cpend > 0) store_o(opend, jpend, cpend);
     return;
   }
 
