@@ -253,12 +253,14 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
           issue_fence();
           load_raw(std::integral_constant<int, B>{}, jj + 2);
           issue_fence();
-          // the conversion only has to land before B0 of chunk jj + 1: it
-          // runs after B1, off the chain waves' path to it (and its LDS
-          // writes off their K H, X and U phases)
-          chunk_barrier();                         // B1 of chunk jj
+          // the conversion only has to land before B0 of chunk jj + 1: a
+          // quarter of it runs before B1 (where its LDS writes meet the K H,
+          // X and U reads), the rest after
           wait_vm<ND + NR>();                      // raw rows of jj + 1
           put_raw(std::integral_constant<int, 1 - B>{}, 1 - B, std::integral_constant<int, 0>{},
+                  std::integral_constant<int, NU / 4>{});
+          chunk_barrier();                         // B1 of chunk jj
+          put_raw(std::integral_constant<int, 1 - B>{}, 1 - B, std::integral_constant<int, NU / 4>{},
                   std::integral_constant<int, NU>{});
           wait_vm<NR>();                           // direct loads of jj + 1
           wait_lgkm<0>();
