@@ -428,9 +428,14 @@ def bench_bwd(args, torch, la, synth, dev):
     if h0 is not None:
         outs["dh0"] = torch.empty_like(h0)
     fn = la.kda_chunk_bwd if kda else la.gdn_chunk_bwd
+    # the reverse pass runs beside the forward recompute on a second stream
+    # (the caller's stream, fork and join events)
+    aux = torch.cuda.Stream()
+    evs = la.fork_join_events()
 
     def step():
-        fn(q, k, v, g, beta, cu, ci, co, dout, h0=h0, workspace=ws, **outs)
+        fn(q, k, v, g, beta, cu, ci, co, dout, h0=h0, workspace=ws, aux_stream=aux, events=evs,
+           **outs)
 
     for _ in range(max(1, args.warmup)):
         step()
