@@ -743,7 +743,6 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
         });
       });
     }
-    constexpr int NW_U = OUT ? 2 * CT : 0;
     // GDN: K^T of state row tile t, k-step s as two transposed reads
     // (half q of k-step s: rows 32 s + 16 q ..) from the row-major K tile
     s16x4 tr[GDN ? NHT : 1][4];
@@ -762,10 +761,12 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
       }
     };
     constexpr int RPT = GDN ? 4 : 2;                      // reads per state row tile
-    constexpr int PRE = (15 - NW_U) / RPT < NHT ? (15 - NW_U) / RPT : NHT;  // tiles read before B1
+    // tiles read before B1: none.  B1 then comes as soon as U is out, which
+    // starts the output waves' M U and the copy waves' conversion earlier;
+    // the transposed reads' latency moves to the chain's own update
+    constexpr int PRE = 0;
     static_for<PRE>([&](auto tc) { read_kt(tc); });
-    // the exchange writes must land before B1 (LDS operations complete in
-    // order: at most the K^T reads issued after them may be outstanding)
+    // the exchange writes must land before B1
     wait_lgkm<PRE * RPT>();
     chunk_barrier();  // B1
     static_for<NHT - PRE>([&](auto tc) { read_kt(std::integral_constant<int, PRE + decltype(tc)::value>{}); });
