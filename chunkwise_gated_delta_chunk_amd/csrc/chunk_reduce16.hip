@@ -574,21 +574,20 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
     if (lane == 0) *reinterpret_cast<volatile float *>(spare) = ics;
   }
   half8 hb[CT][NKD];
-  auto put_hb = [&]() {
+  // the B operands of k-step s of H (state row tiles 2s, 2s + 1), kept for
+  // this wave's next K H and handed to the output wave
+  auto put_hb_step = [&](auto sc) {
+    constexpr int s = decltype(sc)::value;
 #pragma unroll
-    for (int s = 0; s < NKD; ++s)
-#pragma unroll
-      for (int c = 0; c < CT; ++c) hb[c][s] = b_frag<O>(hacc[c], s);
+    for (int c = 0; c < CT; ++c) hb[c][s] = b_frag<O>(hacc[c], s);
     if constexpr (OUT) {
-      static_for<NKD>([&](auto sc) {
-        constexpr int s = decltype(sc)::value;
-        static_for<CT>([&](auto cc) {
-          constexpr int c = decltype(cc)::value;
-          ds_write_b128_at<(CT * s + c) * 1024>(aHB, as_u32x4(hb[c][s]));
-        });
+      static_for<CT>([&](auto cc) {
+        constexpr int c = decltype(cc)::value;
+        ds_write_b128_at<(CT * s + c) * 1024>(aHB, as_u32x4(hb[c][s]));
       });
     }
   };
+  auto put_hb = [&]() { static_for<NKD>([&](auto sc) { put_hb_step(sc); }); };
   put_hb();
   wait_lgkm<0>();
 
@@ -796,8 +795,11 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
           for (int s = 0; s < 2; ++s) hacc[c][t] = O::mfma(fkt[t][s], ubf[c][s], hacc[c][t]);
         }
       }
+      // the H operands of a pair of row tiles go out while the next pair's
+      // products run (the pair before the one just issued is complete)
+      if constexpr (t % 2 == 1 && t >= 3) put_hb_step(std::integral_constant<int, (t - 3) / 2>{});
     });
-    put_hb();
+    put_hb_step(std::integral_constant<int, NKD - 1>{});
     wait_lgkm<0>();
   };
   for (int jj = j0;;) {
