@@ -65,7 +65,6 @@ struct R16 {
   static constexpr int PK = DK * 2 / 16, PT = kBT * 2 / 16;   // pieces per K / Tn row
   static constexpr int HB = NKD * CT * 1024;                  // H operands of a chain wave
   static constexpr int UB = 2 * CT * 1024;                    // U operands of a chain wave
-  static constexpr int ORS = (16 * CT + 4) * 4;               // O scratch row stride (bytes)
   static constexpr int XCH = 2 * STAGE;                       // exchange area
   static constexpr int XW = HB + UB + 16;                     // per chain wave: HB, UB, 1/cs
   static constexpr int LDS = XCH + NCW * XW;
@@ -75,7 +74,6 @@ struct R16 {
   static_assert(I.BYTES % 1024 == 0 && HBM % 1024 == 0 && V_BYTES % 1024 == 0, "1 KiB pieces");
   static_assert(LDS <= 160 * 1024, "LDS");
   static_assert(IMG + I.TN + 3 * 256 * PT + 16 <= 65536, "immediate offsets");
-  static_assert(NCW * 64 * ORS <= 2 * kBT * kBT * 2, "O scratch inside Tn and M");
 };
 
 // Tn / M fragment i = (row tile, k-step) (0,0) (1,0) (2,0) (2,1) (3,0) (3,1)
@@ -344,35 +342,34 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
     // the chain wave's 1 / cs: in the exchange area from the first B0 on
     float osc = p.scale;
     chunk_barrier();  // P
-    // The chunk's O tile ([64][16 CT] fp32 per output wave) goes out through
-    // LDS: written in the accumulator layout (one column, four rows per
-    // lane), read back row by row (four columns per lane) and stored as
-    // 16-byte pieces of whole row spans -- 4 CT stores per lane instead of
-    // 16 CT of 4 bytes, which the CU's vector memory path issues far faster.
-    // The scratch is the current stage's Tn and M region, free once U is
-    // formed (the chain waves read Tn before B1, this wave has its M
-    // fragments in registers); a row stride of 16 CT + 4 floats keeps the
-    // column writes free of bank conflicts.
-    constexpr int ORS = SH::ORS, LPR = 4 * CT, RPI = 16 / CT;  // lanes per row, rows per store
-    const uint32_t osb = IMG + I.TN + ci * 64 * ORS;          // this wave's scratch
-    const uint32_t aOw = osb + 4 * lg * ORS + 4 * lr;                        // + buffer base
-    const uint32_t aOr = osb + (lane / LPR) * ORS + 16 * (lane % LPR);       // + buffer base
-    const int off_st = (lane / LPR) * rs_o + (cw0 + 4 * (lane % LPR)) * osz;
+    // The output tile is formed transposed, O^T = (Q H)^T diag(gamma) +
+    // U^T M^T: the H and U operands the chain wave hands over serve as A
+    // fragments of H^T and U^T as they are, and the Q and M fragments
+    // (row = token, k = key / chunk column in chained order) as B fragments
+    // of Q^T and M^T.  Lane (g, n) of tile (c, R) then holds output row
+    // 16 R + n at the four columns 16 c + 4 g .. +3: 16 contiguous bytes of
+    // one row, stored straight from the accumulators (no LDS round trip);
+    // one store per tile covers 16 rows x 64 bytes.
+    const int off_st = lr * rs_o + (cw0 + 4 * lg) * osz;
     char *o_c = static_cast<char *>(p.o) + ((size_t)wk.t0 * H + h) * DV * osz;
     const size_t o_step = (size_t)kBT * H * DV * osz;
-    // rows of chunk jj's O tile -> o (C valid rows)
-    auto store_o = [&](const f32x4 *orow, int jj, int C) {
+    // chunk jj's O^T tiles -> o (C valid rows)
+    auto store_o = [&](const f32x4 (*ot)[4], int jj, int C) {
       char *o_r = o_c + (size_t)(jj - j0) * o_step;
 #pragma unroll
-      for (int i = 0; i < 4 * CT; ++i) {
-        const auto ro = buffer_rsrc(o_r + (size_t)RPI * i * rs_o, (C - RPI * i) * rs_o);
-        if (p.o_bf16) {
-          const uint32_t w0 = f32_to_bf16_rne(orow[i][0]) | (f32_to_bf16_rne(orow[i][1]) << 16);
-          const uint32_t w1 = f32_to_bf16_rne(orow[i][2]) | (f32_to_bf16_rne(orow[i][3]) << 16);
-          typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-          __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, ro, off_st, 0, 0);
-        } else {
-          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, orow[i]), ro, off_st, 0, 0);
+      for (int R = 0; R < 4; ++R) {
+        const auto ro = buffer_rsrc(o_r + (size_t)16 * R * rs_o, (C - 16 * R) * rs_o);
+#pragma unroll
+        for (int c = 0; c < CT; ++c) {
+          if (p.o_bf16) {
+            const uint32_t w0 = f32_to_bf16_rne(ot[c][R][0]) | (f32_to_bf16_rne(ot[c][R][1]) << 16);
+            const uint32_t w1 = f32_to_bf16_rne(ot[c][R][2]) | (f32_to_bf16_rne(ot[c][R][3]) << 16);
+            typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+            __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, ro, off_st + 16 * c * osz, 0, 0);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, ot[c][R]), ro,
+                                                   off_st + 16 * c * osz, 0, 0);
+          }
         }
       }
     };
@@ -380,8 +377,10 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
     // first LDS reads are issued: the stores then queue behind the copy
     // waves' loads while this wave waits for its operands anyway, instead of
     // holding up the barrier that opens the next chunk.
-    f32x4 opend[4 * CT];
+    f32x4 opend[CT][4];
     int jpend = j0, cpend = 0;  // cpend > 0: the O rows of chunk jpend are pending
+    // gamma of this lane's token in row tile R: exp(G) at 16 R + lane % 16
+    const uint32_t aG = IMG + I.VEC + 4 * lr;  // + buffer base
     auto ochunk = [&](auto bc, int jj) {
       constexpr int B = decltype(bc)::value;
       chunk_barrier();  // B0
@@ -416,7 +415,7 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
         for (int c = 0; c < CT; ++c)
 #pragma unroll
           for (int R = 0; R < 4; ++R) yq[c][R] = zero4();
-        f32x4 gam[4];
+        float gam[4];
         half8 fm[6];
         static_for<NKD>([&](auto sc) {
           constexpr int s = decltype(sc)::value;
@@ -438,7 +437,7 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
           if constexpr (s == NKD - 1) {
             static_for<4>([&](auto rc) {
               constexpr int R = decltype(rc)::value;
-              ds_read_b128_at<64 * R>(gam[R], aS[B]);
+              ds_read_b32_at<64 * R>(gam[R], base + B * STAGE + aG);
             });
             static_for<6>([&](auto ic) {
               constexpr int i = decltype(ic)::value;
@@ -448,7 +447,7 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
 #pragma unroll
           for (int R = 0; R < 4; ++R)
 #pragma unroll
-            for (int c = 0; c < CT; ++c) yq[c][R] = O::mfma(fq[s][R], hb[c][s], yq[c][R]);
+            for (int c = 0; c < CT; ++c) yq[c][R] = O::mfma(hb[c][s], fq[s][R], yq[c][R]);
         });
         wait_lds_tied4<6>(gam[0], gam[1], gam[2], gam[3]);
         chunk_barrier();  // B1: U of this chunk is in the exchange area
@@ -466,7 +465,7 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
 #pragma unroll
           for (int R = 0; R < 4; ++R)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) oa[c][R][e] = gam[R][e] * yq[c][R][e];
+            for (int e = 0; e < 4; ++e) oa[c][R][e] = gam[R] * yq[c][R][e];
         wait_lds_tied2<4>(fm[0], fm[1]);
         wait_lds_tied4<4>(fm[2], fm[3], fm[4], fm[5]);
         if constexpr (CT == 2) wait_lds_tied4<0>(ub[0][0], ub[1][0], ub[0][1], ub[1][1]);
@@ -474,30 +473,14 @@ __device__ __forceinline__ void reduce16_body(const ReduceParams &p, const Work 
         static_for<6>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
 #pragma unroll
-          for (int c = 0; c < CT; ++c) oa[c][fR(i)] = O::mfma(fm[i], ub[c][fS(i)], oa[c][fR(i)]);
+          for (int c = 0; c < CT; ++c) oa[c][fR(i)] = O::mfma(ub[c][fS(i)], fm[i], oa[c][fR(i)]);
         });
-        const uint32_t bw = base + B * STAGE + aOw, br = base + B * STAGE + aOr;
-        static_for<4>([&](auto rc) {
-          constexpr int R = decltype(rc)::value;
-          static_for<CT>([&](auto cc) {
-            constexpr int c = decltype(cc)::value;
-            static_for<4>([&](auto ec) {
-              constexpr int e = decltype(ec)::value;
-              ds_write_b32_at<(16 * R + e) * ORS + 64 * c>(bw, osc * oa[c][R][e]);
-            });
-          });
-        });
-        f32x4 orow[4 * CT];
-        static_for<4 * CT>([&](auto ic) {
-          constexpr int i = decltype(ic)::value;
-          ds_read_b128_at<RPI * i * ORS>(orow[i], br);
-        });
-        if constexpr (CT == 2)
-          wait_lds_tied8<0>(orow[0], orow[1], orow[2], orow[3], orow[4], orow[5], orow[6], orow[7]);
-        else
-          wait_lds_tied4<0>(orow[0], orow[1], orow[2], orow[3]);
 #pragma unroll
-        for (int i = 0; i < 4 * CT; ++i) opend[i] = orow[i];
+        for (int c = 0; c < CT; ++c)
+#pragma unroll
+          for (int R = 0; R < 4; ++R)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) opend[c][R][e] = osc * oa[c][R][e];
         jpend = jj;
         cpend = C;
       }

@@ -357,6 +357,11 @@ __device__ __forceinline__ void ds_read_b128_at(f32x4 &r, uint32_t a) {
   static_assert(OFF >= 0 && OFF < 65536, "DS immediate offset");
   asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(r) : "v"(a), "n"(OFF));
 }
+template <int OFF>
+__device__ __forceinline__ void ds_read_b32_at(float &r, uint32_t a) {
+  static_assert(OFF >= 0 && OFF < 65536, "DS immediate offset");
+  asm volatile("ds_read_b32 %0, %1 offset:%2" : "=v"(r) : "v"(a), "n"(OFF));
+}
 // waits as wait_lds_tied, for other register counts and types
 template <int N, typename F>
 __device__ __forceinline__ void wait_lds_tied4(F &a, F &b, F &c, F &d) {

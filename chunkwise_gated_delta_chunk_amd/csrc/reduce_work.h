@@ -31,11 +31,6 @@ __device__ __forceinline__ void ds_write_b128_at(uint32_t a, const u32x4 &v) {
   static_assert(OFF >= 0 && OFF < 65536, "DS immediate offset");
   asm volatile("ds_write_b128 %0, %1 offset:%2" ::"v"(a), "v"(v), "n"(OFF) : "memory");
 }
-template <int OFF>
-__device__ __forceinline__ void ds_write_b32_at(uint32_t a, float v) {
-  static_assert(OFF >= 0 && OFF < 65536, "DS immediate offset");
-  asm volatile("ds_write_b32 %0, %1 offset:%2" ::"v"(a), "v"(v), "n"(OFF) : "memory");
-}
 __device__ __forceinline__ void ds_write_b128(uint32_t a, const u32x4 &v) {
   asm volatile("ds_write_b128 %0, %1" ::"v"(a), "v"(v) : "memory");
 }
