@@ -217,6 +217,23 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
   for (int e = 0; e < 4; ++e) off_o[e] = (lg * 4 + e) * rs_o + (cw + lr) * osz;
   char *o_c = static_cast<char *>(p.o) + ((size_t)wk.t0 * H + h) * DV * osz;
   const size_t o_step = (size_t)kBT * H * DV * osz;
+  // 16-bit inputs form the output tile transposed (O^T, see below): lane
+  // (g, n) of row tile R holds row 16 R + n at this wave's columns 4 g ..
+  // 4 g + 3, stored as one 16-byte (fp32) or 8-byte (bf16) piece
+  const int off_ot = lr * rs_o + (cw + 4 * lg) * osz;
+  auto store_ot = [&](int R, int C, const f32x4 &oa) {
+    const auto ro = buffer_rsrc(o_c + (size_t)16 * R * rs_o, (C - 16 * R) * rs_o);
+    if (p.o_bf16) {
+      const uint32_t w0 = f32_to_bf16_rne(osc * oa[0]) | (f32_to_bf16_rne(osc * oa[1]) << 16);
+      const uint32_t w1 = f32_to_bf16_rne(osc * oa[2]) | (f32_to_bf16_rne(osc * oa[3]) << 16);
+      typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{w0, w1}, ro, off_ot, 0, 0);
+    } else {
+      const f32x4 v = {osc * oa[0], osc * oa[1], osc * oa[2], osc * oa[3]};
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), ro, off_ot, 0, 0);
+    }
+  };
+  (void)store_ot;
   // 4 output rows of a row tile: fp32, or bf16 rounded to nearest even
   auto store_o = [&](int R, int C, const f32x4 &oa) {
     const auto ro = buffer_rsrc(o_c + (size_t)16 * R * rs_o, (C - 16 * R) * rs_o);
@@ -317,7 +334,8 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
 #pragma unroll
         for (int R = 0; R < 4; ++R) {
           yk[R] = O::mfma(f[2 * R], hb[s], yk[R]);
-          if constexpr (OUT) yq[R] = O::mfma(f[2 * R + 1], hb[s], yq[R]);
+          // (Q H)^T: the state fragment as A, the Q fragment as B
+          if constexpr (OUT) yq[R] = O::mfma(hb[s], f[2 * R + 1], yq[R]);
         }
       });
     } else {
@@ -436,18 +454,26 @@ __device__ __forceinline__ void reduce_body(const ReduceParams &p, const Work &w
         read_kt(std::integral_constant<int, 0>{});
       }
       if constexpr (OUT) {
+        // O^T = (Q H)^T diag(gamma) + U^T M^T: U's B fragments serve as A
+        // fragments of U^T and M's A fragments as B fragments of M^T.  Lane
+        // (g, n) scales by the gamma of its row 16 R + n, which lane 16 (n /
+        // 4) + n % 4 holds as element n % 4 of gam[R].
+        const int gsrc = 16 * (lr >> 2) + (lr & 3);
         f32x4 oa[4];
 #pragma unroll
-        for (int R = 0; R < 4; ++R)
+        for (int R = 0; R < 4; ++R) {
+          const float pub = (lr & 2) ? ((lr & 1) ? gam[R][3] : gam[R][2]) : ((lr & 1) ? gam[R][1] : gam[R][0]);
+          const float gt = __shfl(pub, gsrc, 64);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) oa[R][e] = gam[R][e] * yq[R][e];
+          for (int e = 0; e < 4; ++e) oa[R][e] = gt * yq[R][e];
+        }
         static_for<6>([&](auto ic) {
           constexpr int i = decltype(ic)::value;
-          oa[fR(i)] = O::mfma(fm[i], ufr[fS(i)], oa[fR(i)]);
+          oa[fR(i)] = O::mfma(ufr[fS(i)], fm[i], oa[fR(i)]);
         });
         if constexpr (!HAS_KT) read_kt(std::integral_constant<int, NHT / 2>{});
 #pragma unroll
-        for (int R = 0; R < 4; ++R) store_o(R, C, oa[R]);
+        for (int R = 0; R < 4; ++R) store_ot(R, C, oa[R]);
       } else {
         if constexpr (!HAS_KT) read_kt(std::integral_constant<int, NHT / 2>{});
       }
