@@ -1,8 +1,9 @@
 """Benchmark of the varlen chunkwise gated-delta-rule prefill forward on one MI355X.
 
-One step = the whole hot path over one batch: device chunk metadata
-(build_chunk_meta), the chunk-parallel map and the sequential reduce + output,
-captured once in a HIP graph and replayed (the fixed-capacity graph-replay mode
+One step = the whole hot path over one batch: device chunk metadata (built
+from cu_seqlens inside the map kernel's prologue for up to 64 sequences, by
+build_chunk_meta's kernel beyond), the chunk-parallel map and the sequential
+reduce + output, captured once in a HIP graph and replayed (the fixed-capacity graph-replay mode
 of the FLA graph-capture RFC, section "Performance evaluation").  Inputs are
 seeded synthetic tensors already resident in HBM.
 
@@ -195,8 +196,8 @@ def bench_bucket(args, torch, la, synth, dev):
         cu.copy_(torch.from_numpy(inp["cu_seqlens"].astype(np.int32)))
 
     def step():
-        la.build_chunk_meta(cu, T_max, chunk_indices=ci, chunk_offsets=co, status=st)
-        la.gdn_chunk_fwd(q, k, v, g, beta, cu, ci, co, **kw)
+        # the call builds the chunk layout of cu into ci / co itself
+        la.gdn_chunk_fwd(q, k, v, g, beta, cu, ci, co, build_meta=True, meta_status=st, **kw)
 
     fill(synth.config(3, replay=0))
     s = torch.cuda.Stream()
@@ -250,7 +251,8 @@ def bench_bucket(args, torch, la, synth, dev):
         "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16 inputs; fp16 MFMA operands, fp32 accumulation and state",
         "data": "synthetic (seeded, resident in HBM)",
-        "config": {"workload": WORKLOADS["c3"][2], "mode": "graph-replay of meta+map+reduce",
+        "config": {"workload": WORKLOADS["c3"][2],
+                   "mode": "graph-replay of map (building the chunk layout) + reduce",
                    "layouts": len(rows), "nt_max": NT},
         "op_hbm_frac": {"median": fr[len(fr) // 2], "min": fr[0], "max": fr[-1]},
         "capture_ms": round(capture_ms, 3), "graph_equals_eager": graph_eq,
@@ -588,8 +590,10 @@ def env_record(torch):
 
 class FwdBucket:
     """Static device buffers of one fixed-capacity bucket (T_max, N_max) of a
-    forward workload, and the step on them: build_chunk_meta, then the chunk
-    forward (the FLA graph-capture RFC, "Static buffer contract")."""
+    forward workload, and the step on them: the chunk forward, which builds
+    the chunk layout of cu_seqlens into ci / co itself (in the map kernel up
+    to 64 sequences, else with the metadata kernel first) (the FLA
+    graph-capture RFC, "Static buffer contract" and "Device-side metadata")."""
 
     def __init__(self, torch, la, inp, T_max, N_max, dev, dv_split=0, seg_len=0):
         self.torch, self.la = torch, la
@@ -632,10 +636,8 @@ class FwdBucket:
         self.cu.copy_(cu_host, non_blocking=True)
 
     def step(self):
-        la = self.la
-        la.build_chunk_meta(self.cu, self.T_max, chunk_indices=self.ci, chunk_offsets=self.co,
-                            status=self.st)
-        self.fwd(self.q, self.k, self.v, self.g, self.beta, self.cu, self.ci, self.co, **self.kw)
+        self.fwd(self.q, self.k, self.v, self.g, self.beta, self.cu, self.ci, self.co,
+                 build_meta=True, meta_status=self.st, **self.kw)
 
     def capture(self):
         torch = self.torch
@@ -821,6 +823,11 @@ def bench_forward(args, torch, la, synth, dev):
     split, seg = b.split, b.seg
     fwd_kw = b.kw
     args_t = (b.q, b.k, b.v, b.g, b.beta, b.cu, b.ci, b.co)
+    stage_kw = dict(fwd_kw, build_meta=True, meta_status=b.st)
+    # the standalone metadata kernel, timed for comparison only (not part of
+    # the step), into arrays of its own
+    ci_alone, co_alone = torch.empty_like(b.ci), torch.empty_like(b.co)
+    st_alone = torch.empty_like(b.st)
 
     # ---- eager warmup + per-kernel HIP-event timing on the launch stream
     for _ in range(max(1, args.warmup)):
@@ -832,11 +839,12 @@ def bench_forward(args, torch, la, synth, dev):
     for i in range(args.steps):
         e = evs[i]
         e[0].record()
-        la.build_chunk_meta(b.cu, T, chunk_indices=b.ci, chunk_offsets=b.co, status=b.st)
+        la.build_chunk_meta(b.cu, T, chunk_indices=ci_alone, chunk_offsets=co_alone,
+                            status=st_alone)
         e[1].record()
-        la.chunk_fwd_stages(is_kda, la.STAGE_MAP, *args_t, **fwd_kw)
+        la.chunk_fwd_stages(is_kda, la.STAGE_MAP, *args_t, **stage_kw)
         e[2].record()
-        la.chunk_fwd_stages(is_kda, la.STAGE_REDUCE, *args_t, **fwd_kw)
+        la.chunk_fwd_stages(is_kda, la.STAGE_REDUCE, *args_t, **stage_kw)
         e[3].record()
     torch.cuda.synchronize()
     per = np.array([[e[j].elapsed_time(e[j + 1]) for j in range(3)] for e in evs])  # ms
@@ -869,12 +877,14 @@ def bench_forward(args, torch, la, synth, dev):
 
     op_bytes = alg_bytes(inp, "op")
     op_flops = alg_flops(inp)
-    kernels = {"meta": t_meta, "map": t_map, "reduce": t_red}
+    kernels = {"map": t_map, "reduce": t_red}
     diag = {}
     for kind, t in kernels.items():
-        ab = alg_bytes(inp, kind) if kind != "meta" else 4 * (N + 1) * 2 + 8 * b.NT
+        ab = alg_bytes(inp, kind)
         diag[kind] = {"ms": round(t, 5), "alg_bytes": ab,
                       "hbm_frac": round(ab / (t * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    fused = N <= 64
+    diag["meta_standalone"] = {"ms": round(t_meta, 5), "in_step": not fused}
     # HBM traffic of one step: the sum of every kernel's counter-measured
     # bytes, when all were taken on the current sources (else null)
     tr = [load_traffic(kind, args.workload, inp) for kind in ("map", "reduce")]
@@ -882,7 +892,9 @@ def bench_forward(args, torch, la, synth, dev):
     achieved = op_bytes / (ev_mean * 1e-3) / 1e9
     roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-            "kernel": ("whole step (graph replay): chunk_meta + chunk_map + chunk_reduce"
+            "kernel": ("whole step (graph replay): chunk_map (building the chunk layout) + "
+                       "chunk_reduce" if fused else
+                       "whole step (graph replay): chunk_meta + chunk_map + chunk_reduce"
                        + ("" if seg == 0 else
                           f" x2 + chunk_combine (segments of {seg} chunks)")
                        + f", d_v split {split}"),
@@ -896,7 +908,9 @@ def bench_forward(args, torch, la, synth, dev):
         "dtype": "bf16 inputs; fp16 MFMA operands, fp32 accumulation and state"
         if inp["dtype"] == "bf16" else "fp32",
         "data": "synthetic (seeded, resident in HBM)",
-        "config": {"workload": desc, "mode": "graph-replay of meta+map+reduce",
+        "config": {"workload": desc,
+                   "mode": "graph-replay of map (building the chunk layout) + reduce" if fused
+                   else "graph-replay of meta+map+reduce",
                    "tokens": tokens, "heads": H, "d": dk, "sequences": N, "nt_max": b.NT,
                    "dv_split": split, "seg_len": seg},
         "roofline": roof,
@@ -907,8 +921,8 @@ def bench_forward(args, torch, la, synth, dev):
         "kernels": diag,
         "eager_live_ms": round(eager_ms, 5), "capture_ms": round(capture_ms, 3),
         "replay_p50_ms": round(p50, 5), "replay_p95_ms": round(p95, 5),
-        "kernels_per_step": 3 if seg == 0 else 5,
-        "host_launches_per_step": {"eager": 3 if seg == 0 else 5, "graph": 1},
+        "kernels_per_step": (2 if seg == 0 else 4) + (not fused),
+        "host_launches_per_step": {"eager": (2 if seg == 0 else 4) + (not fused), "graph": 1},
         "chunk_utilisation": round(nt_actual / b.NT, 4),
         "token_utilisation": round(tokens / T, 4),
         "workspace_bytes": int(b.ws.numel()),

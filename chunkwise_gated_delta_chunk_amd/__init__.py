@@ -62,6 +62,8 @@ class ChunkFwdArgs(ctypes.Structure):
         ("chunk_offsets", ctypes.c_void_p), ("h0", ctypes.c_void_p),
         ("o", ctypes.c_void_p), ("ht", ctypes.c_void_p),
         ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+        ("meta_indices", ctypes.c_void_p), ("meta_offsets", ctypes.c_void_p),
+        ("meta_status", ctypes.c_void_p),
     ]
 
 
@@ -289,7 +291,7 @@ def _out(o, o_dtype, shape, dev):
 
 def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0, o, ht,
              output_final_state, workspace, scale, dv_split, seg_len, o_dtype=None, BT=64,
-             static=False):
+             static=False, build_meta=False, meta_status=None):
     _qkv_dtype(q)
     H, H_qk = _heads(q, v, "T_max")
     T_max, _, d_k = q.shape
@@ -305,6 +307,8 @@ def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0
     NT = nt_max(T_max, N_max, BT)
     _need(chunk_indices, "chunk_indices", torch.int32, (NT, 2), dev)
     _need(chunk_offsets, "chunk_offsets", torch.int32, (N_max + 1,), dev)
+    if build_meta and meta_status is not None:
+        _need(meta_status, "meta_status", torch.int32, (1,), dev)
     st_shape = (N_max, H, d_k, d_v)
     if h0 is not None:
         _need(h0, "h0", torch.float32, st_shape, dev)
@@ -330,6 +334,11 @@ def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0
     a.cu_seqlens = cu_seqlens.data_ptr()
     a.chunk_indices = chunk_indices.data_ptr()
     a.chunk_offsets = chunk_offsets.data_ptr()
+    if build_meta:
+        # the call writes the layout of cu_seqlens into these two (outputs)
+        a.meta_indices = chunk_indices.data_ptr()
+        a.meta_offsets = chunk_offsets.data_ptr()
+        a.meta_status = None if meta_status is None else meta_status.data_ptr()
     a.h0 = None if h0 is None else h0.data_ptr()
     a.o = o.data_ptr()
     a.ht = None if ht is None else ht.data_ptr()
@@ -341,10 +350,12 @@ def _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, h0
 
 def _call(name, kda, stages, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, *,
           h0=None, o=None, ht=None, output_final_state=True, workspace=None, scale=1.0,
-          dv_split=0, seg_len=0, o_dtype=None, BT=64, stream=None):
+          dv_split=0, seg_len=0, o_dtype=None, BT=64, stream=None, build_meta=False,
+          meta_status=None):
     a, o, ht, workspace = _prepare(kda, q, k, v, g, beta, cu_seqlens, chunk_indices,
                                    chunk_offsets, h0, o, ht, output_final_state, workspace,
-                                   scale, dv_split, seg_len, o_dtype, BT)
+                                   scale, dv_split, seg_len, o_dtype, BT,
+                                   build_meta=build_meta, meta_status=meta_status)
     L = lib()
     s = _stream(stream)
     if stages is None:
@@ -358,7 +369,12 @@ def _call(name, kda, stages, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_
 
 
 def gdn_chunk_fwd(q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, **kw):
-    """GDN chunk forward (scalar log-decay g [T_max, H]); returns (o, ht)."""
+    """GDN chunk forward (scalar log-decay g [T_max, H]); returns (o, ht).
+
+    With ``build_meta=True`` (BT 64) chunk_indices and chunk_offsets are
+    outputs: the call writes the layout of cu_seqlens into them (and the
+    status word into ``meta_status`` if given), as build_chunk_meta would,
+    inside its map kernel for up to 64 sequences."""
     return _call("gdn_chunk_fwd", False, None, q, k, v, g, beta, cu_seqlens, chunk_indices,
                  chunk_offsets, **kw)
 
@@ -378,14 +394,16 @@ def chunk_fwd_stages(kda, stages, q, k, v, g, beta, cu_seqlens, chunk_indices, c
 
 def chunk_fwd_static(kda, q, k, v, g, beta, cu_seqlens, chunk_indices, chunk_offsets, *,
                      h0=None, o=None, ht=None, output_final_state=True, scale=1.0, dv_split=0,
-                     seg_len=0, o_dtype=None, BT=64, stream=None):
+                     seg_len=0, o_dtype=None, BT=64, stream=None, build_meta=False,
+                     meta_status=None):
     """The forward with the library's static device scratch as its workspace
     (la_chunk_fwd_static): for callers that cannot allocate device memory
     during the call.  Pass o (and ht) to allocate nothing here either.
     Calls that overlap on one GPU share that scratch and race."""
     a, o, ht, _ = _prepare(bool(kda), q, k, v, g, beta, cu_seqlens, chunk_indices,
                            chunk_offsets, h0, o, ht, output_final_state, None, scale, dv_split,
-                           seg_len, o_dtype, BT, static=True)
+                           seg_len, o_dtype, BT, static=True, build_meta=build_meta,
+                           meta_status=meta_status)
     rc = lib().la_chunk_fwd_static(ctypes.byref(a), int(bool(kda)), _stream(stream))
     if rc != 0:
         raise LinAttnError(rc, "la_chunk_fwd_static")

@@ -54,6 +54,85 @@ namespace la {
 
 namespace {
 
+// ---- the chunk layout built in the map's own prologue (up to 64 sequences)
+// The FLA graph-capture RFC ("[RFC] Add Graph Capture Support for FLA Prefill
+// and Training Paths on Ascend NPUs", "Device-side metadata") builds
+// chunk_offsets and chunk_indices on the device from cu_seqlens.  When the
+// caller asks the forward for that layout, every wave of the map derives it
+// by itself, with the checks and results of build_chunk_meta at BT = 64, so
+// the step needs no launch of its own for it: lane m holds the chunk slots of
+// sequences 0..m (lanes >= N_max: all of them), and a layout that fails a
+// check has no slots.
+struct WaveLayout {
+  int end;    // per lane, see above
+  int total;  // slots in use: 0 for an invalid layout
+  int flags;  // build_chunk_meta's status bits
+};
+template <typename Idx>
+__device__ __forceinline__ WaveLayout wave_layout_t(const Idx *cu, int N_max, int T_max, int NT_max) {
+  const int m = lane_id();
+  const bool live = m < N_max;
+  const Idx a = live ? cu[m] : Idx(0), b = live ? cu[m + 1] : Idx(0);
+  int f = 0;
+  if (__ballot(live && b < a)) f |= LA_META_NOT_MONOTONE;
+  if (cu[0] != 0) f |= LA_META_BAD_START;
+  if (cu[N_max] > (Idx)T_max) f |= LA_META_OVER_CAPACITY;
+  int cnt = (live && !f) ? ((int)(b - a) + kBT - 1) / kBT : 0;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int y = __shfl_up(cnt, off, 64);
+    if (m >= off) cnt += y;
+  }
+  const int total = __shfl(cnt, 63, 64);
+  if (!f && total > NT_max) f = LA_META_OVER_CAPACITY;
+  WaveLayout L;
+  L.flags = f;
+  L.total = f ? 0 : total;
+  L.end = f ? 0 : cnt;
+  return L;
+}
+__device__ __forceinline__ WaveLayout wave_layout(const MapParams &p) {
+  return p.cu64 ? wave_layout_t(static_cast<const int64_t *>(p.cu_seqlens), p.N_max, p.T_max, p.NT_max)
+                : wave_layout_t(static_cast<const int32_t *>(p.cu_seqlens), p.N_max, p.T_max, p.NT_max);
+}
+// slot j (the same in every lane) -> sequence and chunk (i_n = -1: sentinel),
+// from this lane's `end` (lane 63's is the slot total)
+__device__ __forceinline__ void layout_slot(int end, int j, int &i_n, int &i_t) {
+  i_n = -1;
+  i_t = 0;
+  if (j >= __builtin_amdgcn_readlane(end, 63)) return;
+  const int n = __popcll(__ballot(end <= j));
+  i_n = n;
+  i_t = j - (n > 0 ? __builtin_amdgcn_readlane(end, n - 1) : 0);
+}
+// Slots j = first + stride * t (t = 0, 1, ...: lane t of this wave's passes)
+// -> chunk_indices, and with `head` also chunk_offsets and the status word.
+// Every slot below NT_max is written by exactly one (wave, lane) of the grid.
+// The whole wave runs every shuffle (the loop bounds are wave-uniform).
+__device__ __forceinline__ void layout_store(const MapParams &p, const WaveLayout &L, int first,
+                                             int stride, bool head) {
+  const int m = lane_id();
+  for (int base = first; base < p.NT_max; base += 64 * stride) {
+    const int j = base + m * stride;
+    // the owning sequence: how many sequences end at or before slot j
+    int n = 0;
+    for (int i = 0; i < p.N_max; ++i) n += __builtin_amdgcn_readlane(L.end, i) <= j;
+    const int start = __shfl(L.end, (n - 1) & 63, 64);
+    const bool in = j < L.total;
+    if (j < p.NT_max) {
+      p.meta_ci[2 * j] = in ? n : -1;
+      p.meta_ci[2 * j + 1] = in ? j - (n > 0 ? start : 0) : 0;
+    }
+  }
+  if (head) {
+    // chunk_offsets[n] = slots of the sequences before n (all 0 when invalid)
+    const int prev = __shfl_up(L.end, 1, 64);
+    if (m <= p.N_max) p.meta_co[m] = m == 0 ? 0 : prev;
+    if (m == 0 && p.N_max == 64) p.meta_co[64] = L.total;
+    if (p.meta_status && m == 0) *p.meta_status = L.flags;
+  }
+}
+
 // (R, S) of the p-th 16x16 tile of the lower block triangle of a 64x64 matrix,
 // p = 0..9 in row order: R = 0,1,1,2,2,2,3,3,3,3 and S = 0,0,1,0,1,2,0,1,2,3,
 // packed two bits per entry
@@ -97,9 +176,17 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
   // the L2 lines of its token rows (q, k rows of adjacent heads, g, beta)
   const int h = blockIdx.x % p.H;
   const int slot = blockIdx.x / p.H;
-  const int i_n = p.chunk_indices[2 * slot];
+  int i_n, i_t;
+  if (p.fuse_meta) {
+    // the layout from cu_seqlens; the head-0 workgroup of each slot stores it
+    const WaveLayout L = wave_layout(p);
+    if (h == 0 && wave_id() == 0) layout_store(p, L, slot, p.NT_max, slot == 0);
+    layout_slot(L.end, slot, i_n, i_t);
+  } else {
+    i_n = p.chunk_indices[2 * slot];
+    i_t = i_n < 0 ? 0 : p.chunk_indices[2 * slot + 1];
+  }
   if (i_n < 0) return;  // sentinel: nothing to do, nothing written
-  const int i_t = p.chunk_indices[2 * slot + 1];
   const int bos = cu_at(p.cu_seqlens, p.cu64, i_n);
   const int eos = cu_at(p.cu_seqlens, p.cu64, i_n + 1);
   const int r0 = bos + i_t * kBT;
@@ -654,13 +741,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   u32x4 kraw[NU][2], qraw[NU][2];
   float bval, gval;
   // the cell's chunk: first row, valid rows (0: sentinel)
+  // the chunk layout, when this kernel builds it: each wave derives it and
+  // keeps its lanes' slot ends in a row of sEnd of its own (read back by
+  // the same wave only, so no barrier), wave 0 of workgroup b stores slots
+  // b, b + grid, ...
+  __shared__ int sEnd[kThreads / 64][64];
+  if (p.fuse_meta) {
+    const WaveLayout L = wave_layout(p);
+    if (w == 0) layout_store(p, L, blockIdx.x, gridDim.x, blockIdx.x == 0);
+    sEnd[w][lane_id()] = L.end;
+  }
   auto cell_rows = [&](int cell, int &r0, int &C) {
     const int slot = cell / H;
-    const int i_n = p.chunk_indices[2 * slot];
+    int i_n, i_t;
+    if (p.fuse_meta) {
+      layout_slot(sEnd[w][lane_id()], slot, i_n, i_t);
+    } else {
+      i_n = p.chunk_indices[2 * slot];
+      i_t = i_n < 0 ? 0 : p.chunk_indices[2 * slot + 1];
+    }
     C = 0;
     r0 = 0;
     if (i_n < 0) return;
-    const int i_t = p.chunk_indices[2 * slot + 1];
     const int bos = cu_at(p.cu_seqlens, p.cu64, i_n);
     const int eos = cu_at(p.cu_seqlens, p.cu64, i_n + 1);
     r0 = bos + i_t * kBT;

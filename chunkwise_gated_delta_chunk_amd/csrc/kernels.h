@@ -21,6 +21,12 @@ struct MapParams {
   int Hqk;  // q, k heads: value head h reads q, k head h / (H / Hqk)
   int raw_kq;  // GDN, 16-bit: the reduce stages K and Q itself (no K, Q stored)
   void *img;
+  // fuse_meta (N_max <= 64): the kernel derives the chunk layout from
+  // cu_seqlens itself (chunk_indices unread) and stores it as build_chunk_meta
+  // does at BT = 64: meta_ci [NT_max][2], meta_co [N_max+1], meta_status
+  // (optional)
+  int fuse_meta, N_max, T_max;
+  int32_t *meta_ci, *meta_co, *meta_status;
 };
 
 struct ReduceParams {

@@ -153,10 +153,24 @@ size_t ws_bytes(const la_chunk_fwd_args *a, bool kda) {
 
 // the chunk layout the kernels read: the caller's (BT = 64), or one built
 // now at the workspace's end (BT = 32)
-struct Meta { const int32_t *ci, *co; };
-hipError_t kernel_meta(const la_chunk_fwd_args *a, char *meta_base, hipStream_t st, Meta &m) {
+// With meta_indices set the layout goes to the caller's meta_* arrays: built
+// in the map's prologue up to 64 sequences (fuse), otherwise by the metadata
+// kernel before a map stage.
+struct Meta { const int32_t *ci, *co; bool fuse; };
+hipError_t kernel_meta(const la_chunk_fwd_args *a, char *meta_base, hipStream_t st, Meta &m,
+                       bool map_stage = true) {
   m.ci = a->chunk_indices;
   m.co = a->chunk_offsets;
+  m.fuse = false;
+  if (a->meta_indices) {
+    m.ci = a->meta_indices;
+    m.co = a->meta_offsets;
+    m.fuse = a->N_max <= 64;
+    if (m.fuse || !map_stage) return hipSuccess;
+    const int nt = (int)la_nt_max(a->T_max, a->N_max, kBTk);
+    return la::launch_chunk_meta(a->cu_seqlens, a->cu_seqlens_i64, a->N_max, a->T_max, kBTk, nt,
+                                 a->meta_indices, a->meta_offsets, a->meta_status, st);
+  }
   if (a->BT == kBTk) return hipSuccess;
   const int nt = (int)la_nt_max(a->T_max, a->N_max, kBTk);
   int32_t *ci = reinterpret_cast<int32_t *>(meta_base);
@@ -173,9 +187,13 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
   if (stages < 1 || stages > 3) return LA_ERR_UNSUPPORTED;
   const int sc = check_shape(a);
   if (sc != LA_OK) return sc;
-  if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->cu_seqlens || !a->chunk_indices ||
-      !a->chunk_offsets || !a->o)
+  if (!a->q || !a->k || !a->v || !a->g || !a->beta || !a->cu_seqlens || !a->o) return LA_ERR_NULL;
+  if (a->meta_indices) {
+    if (!a->meta_offsets) return LA_ERR_NULL;
+    if (a->BT != kBTk) return LA_ERR_UNSUPPORTED;
+  } else if (!a->chunk_indices || !a->chunk_offsets) {
     return LA_ERR_NULL;
+  }
   if (!a->workspace) return LA_ERR_WORKSPACE;
   if (a->workspace_bytes < ws_bytes(a, kda)) return LA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(a->workspace) % 256 != 0) return LA_ERR_WORKSPACE;
@@ -192,7 +210,8 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
   char *ws = static_cast<char *>(a->workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   Meta meta;
-  if (kernel_meta(a, ws + ws_img_bytes(a, kda) + ws_seg_bytes(a), st, meta) != hipSuccess)
+  if (kernel_meta(a, ws + ws_img_bytes(a, kda) + ws_seg_bytes(a), st, meta,
+                  (stages & LA_STAGE_MAP) != 0) != hipSuccess)
     return LA_ERR_HIP;
   if (stages & LA_STAGE_MAP) {
     la::MapParams mp{};
@@ -208,6 +227,12 @@ int forward(const la_chunk_fwd_args *a, bool kda, int stages, void *stream) {
     mp.NT_max = (int)la_nt_max(a->T_max, a->N_max, kBTk);
     mp.raw_kq = raw_kq(a, kda);
     mp.img = ws;
+    mp.fuse_meta = meta.fuse;
+    mp.N_max = a->N_max;
+    mp.T_max = a->T_max;
+    mp.meta_ci = a->meta_indices;
+    mp.meta_co = a->meta_offsets;
+    mp.meta_status = a->meta_status;
     if (la::launch_chunk_map(mp, kda, dt, a->d_k, st) != hipSuccess) return LA_ERR_HIP;
   }
   if (stages & LA_STAGE_REDUCE) {

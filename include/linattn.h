@@ -135,6 +135,18 @@ typedef struct {
     float *ht;                 /* [N_max][H][d_k][d_v] or NULL; may equal h0     */
     void *workspace;           /* >= la_chunk_fwd_workspace_bytes(...) bytes,    */
     size_t workspace_bytes;    /* 256-byte aligned                               */
+    /* Chunk layout built by the call itself (optional; BT must be 64).  With   */
+    /* meta_indices != NULL the call does not read chunk_indices and          */
+    /* chunk_offsets (they may be NULL): it derives the layout of cu_seqlens  */
+    /* on the device and writes meta_indices [NT_max][2], meta_offsets        */
+    /* [N_max+1] and, if not NULL, meta_status [1], with the values           */
+    /* build_chunk_meta (BT = 64) writes for the same arguments.  Up to 64    */
+    /* sequences the map kernel does this in its prologue (no launch of its   */
+    /* own); beyond, the call runs build_chunk_meta's kernel first.  A        */
+    /* LA_STAGE_REDUCE-only call reads meta_offsets as its earlier            */
+    /* LA_STAGE_MAP call left them.  Later calls on the same layout may pass  */
+    /* the written arrays as chunk_indices / chunk_offsets.                   */
+    int32_t *meta_indices, *meta_offsets, *meta_status;
 } la_chunk_fwd_args;
 
 /*
@@ -182,9 +194,10 @@ size_t la_chunk_fwd_workspace_bytes(const la_chunk_fwd_args *shape, int is_kda);
  * recurrence is linear in them, so o and ht are unchanged up to rounding):
  * v and h0 of any magnitude from about 2^-24 to 2^16 keep fp16 precision.
  * The metadata must come from build_chunk_meta on the same cu_seqlens, T_max,
- * N_max and BT.
- * Host errors: LA_ERR_NULL, LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_UNSUPPORTED,
- * LA_ERR_WORKSPACE, LA_ERR_ALIAS, LA_ERR_HIP.
+ * N_max and BT, unless the call builds it itself (meta_indices set).
+ * Host errors: LA_ERR_NULL (also: meta_indices without meta_offsets),
+ * LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_UNSUPPORTED (also: meta_indices with
+ * BT != 64), LA_ERR_WORKSPACE, LA_ERR_ALIAS, LA_ERR_HIP.
  */
 int gdn_chunk_fwd(const la_chunk_fwd_args *a, void *stream);
 int kda_chunk_fwd(const la_chunk_fwd_args *a, void *stream);

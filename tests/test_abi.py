@@ -86,6 +86,11 @@ BAD = [
     ("fp16 d 96", dict(qkv_dtype=2, d_k=96, d_v=96), -4),
     ("fp16 BT 48", dict(qkv_dtype=2, BT=48), -4),
     ("fp32 segmented", dict(qkv_dtype=1, seg_len=4), -4),
+    ("own layout without offsets", dict(meta_indices=0x300000), -1),
+    ("own layout at BT 32", dict(meta_indices=0x300000, meta_offsets=0x300100, BT=32), -4),
+    ("own layout, still no workspace", dict(meta_indices=0x300000, meta_offsets=0x300100,
+                                            chunk_indices=None, chunk_offsets=None,
+                                            workspace=None), -5),
 ]
 
 
