@@ -916,6 +916,11 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
     }
     if (cb + 1 < NBLK) fetch(cb + 1);
     sync_lds();
+    // The products below are formed transposed (operands swapped): lane
+    // (g, n) holds row xr = 16 w + n at the columns 16 hf + 4 g .. +3, so
+    // its hi / lo halves go to LDS as 8-byte pieces and dV leaves as 16-byte
+    // stores.
+    const int xr = 16 * w + lr;
     // X = V - gam*(K H), dU = M^T dOb + fac*(K dH'): rows 16w, both column tiles
     {
       f32x4 kh[2] = {zero4(), zero4()}, kd[2] = {zero4(), zero4()}, mo[2] = {zero4(), zero4()};
@@ -924,28 +929,33 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
         const bf16x8_t a = frag_row(sK, LDK, 16 * w + lr, 32 * s);
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          kh[hf] = mfma_bf(a, frag_col(sHh, LB, 32 * s, 16 * hf), kh[hf]);
-          kh[hf] = mfma_bf(a, frag_col(sHl, LB, 32 * s, 16 * hf), kh[hf]);
-          kd[hf] = mfma_bf(a, frag_col(sDh, LB, 32 * s, 16 * hf), kd[hf]);
-          kd[hf] = mfma_bf(a, frag_col(sDl, LB, 32 * s, 16 * hf), kd[hf]);
+          kh[hf] = mfma_bf(frag_col(sHh, LB, 32 * s, 16 * hf), a, kh[hf]);
+          kh[hf] = mfma_bf(frag_col(sHl, LB, 32 * s, 16 * hf), a, kh[hf]);
+          kd[hf] = mfma_bf(frag_col(sDh, LB, 32 * s, 16 * hf), a, kd[hf]);
+          kd[hf] = mfma_bf(frag_col(sDl, LB, 32 * s, 16 * hf), a, kd[hf]);
         }
       }
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8_t ah = frag_col(sMh, LT, 32 * s, 16 * w), al = frag_col(sMl, LT, 32 * s, 16 * w);
+        const bf16x8_t bh = frag_col(sMh, LT, 32 * s, 16 * w), bl = frag_col(sMl, LT, 32 * s, 16 * w);
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf)
-          mo[hf] = mfma3(ah, al, frag_col(sOh, LB, 32 * s, 16 * hf), frag_col(sOl, LB, 32 * s, 16 * hf), mo[hf]);
+          mo[hf] = mfma3(frag_col(sOh, LB, 32 * s, 16 * hf), frag_col(sOl, LB, 32 * s, 16 * hf), bh, bl, mo[hf]);
       }
+      const float gx = sGam[xr], fx = sFac[xr];
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
+      for (int hf = 0; hf < 2; ++hf) {
+        const int o = xr * LB + 16 * hf + 4 * lg;
+        const bf16x4_t v4 = *reinterpret_cast<const bf16x4_t *>(sV + o);
+        f32x4 x, y;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + 4 * lg + i, c = 16 * hf + lr;
-          const float x = (float)sV[r * LB + c] - sGam[r] * kh[hf][i];
-          splitb(x, sXh[r * LB + c], sXl[r * LB + c]);
-          splitb(mo[hf][i] + sFac[r] * kd[hf][i], sGh[r * LB + c], sGl[r * LB + c]);
+          x[i] = (float)v4[i] - gx * kh[hf][i];
+          y[i] = mo[hf][i] + fx * kd[hf][i];
         }
+        put4(sXh + o, sXl + o, x);
+        put4(sGh + o, sGl + o, y);
+      }
     }
     sync_lds();
     // U = A~ X, dX = A~^T dU (= dV)
@@ -957,19 +967,19 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
         const bf16x8_t th = frag_col(sAh, LT, 32 * s, 16 * w), tl = frag_col(sAl, LT, 32 * s, 16 * w);
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
-          u[hf] = mfma3(ah, al, frag_col(sXh, LB, 32 * s, 16 * hf), frag_col(sXl, LB, 32 * s, 16 * hf), u[hf]);
-          dx[hf] = mfma3(th, tl, frag_col(sGh, LB, 32 * s, 16 * hf), frag_col(sGl, LB, 32 * s, 16 * hf), dx[hf]);
+          u[hf] = mfma3(frag_col(sXh, LB, 32 * s, 16 * hf), frag_col(sXl, LB, 32 * s, 16 * hf), ah, al, u[hf]);
+          dx[hf] = mfma3(frag_col(sGh, LB, 32 * s, 16 * hf), frag_col(sGl, LB, 32 * s, 16 * hf), th, tl, dx[hf]);
         }
       }
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 16 * w + 4 * lg + i, c = 16 * hf + lr;
-          splitb(u[hf][i], sUh[r * LB + c], sUl[r * LB + c]);
-          splitb(dx[hf][i], sEh[r * LB + c], sEl[r * LB + c]);
-          if (r < C) p.dv[((size_t)(r0 + r) * H + h) * DV + NB * cb + c] = dx[hf][i];
-        }
+      for (int hf = 0; hf < 2; ++hf) {
+        const int o = xr * LB + 16 * hf + 4 * lg;
+        put4(sUh + o, sUl + o, u[hf]);
+        put4(sEh + o, sEl + o, dx[hf]);
+        if (xr < C)
+          *reinterpret_cast<f32x4 *>(p.dv + ((size_t)(r0 + xr) * H + h) * DV + NB * cb + 16 * hf + 4 * lg) =
+              dx[hf];
+      }
     }
     sync_lds();
     // contracted over this block's columns
@@ -983,9 +993,11 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
       for (int t = 0; t < PT; ++t) {
         const int br = 16 * t + lr;
         const bf16x8_t hh = frag_row(sHh, LB, br, 0), hl = frag_row(sHl, LB, br, 0);
-        P1[t] = mfma3(oh, ol, hh, hl, P1[t]);
-        P2[t] = mfma3(eh, el, hh, hl, P2[t]);
-        P3[t] = mfma3(uh, ul, frag_row(sDh, LB, br, 0), frag_row(sDl, LB, br, 0), P3[t]);
+        // transposed (operands swapped): lane (g, n) holds row 16 w + n at
+        // the columns 16 t + 4 g .. +3, as the dq / dk stores want them
+        P1[t] = mfma3(hh, hl, oh, ol, P1[t]);
+        P2[t] = mfma3(hh, hl, eh, el, P2[t]);
+        P3[t] = mfma3(frag_row(sDh, LB, br, 0), frag_row(sDl, LB, br, 0), uh, ul, P3[t]);
       }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -1166,42 +1178,54 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
       aF[s][0] = frag_row(qFh, LT, 16 * w + lr, 32 * s);
       aF[s][1] = frag_row(qFl, LT, 16 * w + lr, 32 * s);
     }
-    float q1[4] = {0.f, 0.f, 0.f, 0.f}, k2[4] = {0.f, 0.f, 0.f, 0.f}, k3[4] = {0.f, 0.f, 0.f, 0.f};
+    // every tile transposed (K^T and Q^T as A operands): lane (g, n) holds
+    // row rr = 16 w + n at the columns 16 t + 4 g .. +3, so the dq / dk rows
+    // go out as 16-byte stores and the gate dots read 8 bytes of q / k
+    const int rr = 16 * w + lr;
+    const float gr = sGam[rr], fr = sFac[rr];
+    float q1 = 0.f, k2 = 0.f, k3 = 0.f;
 #pragma unroll
     for (int t = 0; t < PT; ++t) {
       f32x4 dq = zero4(), dk = zero4();
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
         const bf16x8_t bk = frag_col(sK, LDK, 32 * s, 16 * t), bq = frag_col(sQ, LDK, 32 * s, 16 * t);
-        dq = mfma_bf(aE[s][0], bk, dq);
-        dq = mfma_bf(aE[s][1], bk, dq);
-        dk = mfma_bf(aET[s][0], bq, dk);
-        dk = mfma_bf(aET[s][1], bq, dk);
-        dk = mfma_bf(aF[s][0], bk, dk);
-        dk = mfma_bf(aF[s][1], bk, dk);
+        dq = mfma_bf(bk, aE[s][0], dq);
+        dq = mfma_bf(bk, aE[s][1], dq);
+        dk = mfma_bf(bq, aET[s][0], dk);
+        dk = mfma_bf(bq, aET[s][1], dk);
+        dk = mfma_bf(bk, aF[s][0], dk);
+        dk = mfma_bf(bk, aF[s][1], dk);
       }
+      const int c0 = 16 * t + 4 * lg;
+      const bf16x4_t q4 = *reinterpret_cast<const bf16x4_t *>(sQ + rr * LDK + c0);
+      const bf16x4_t k4 = *reinterpret_cast<const bf16x4_t *>(sK + rr * LDK + c0);
+      f32x4 oq, ok;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * lg + i, c = 16 * t + lr;
-        q1[i] += (float)sQ[r * LDK + c] * P1[t][i];
-        k2[i] += (float)sK[r * LDK + c] * P2[t][i];
-        k3[i] += (float)sK[r * LDK + c] * P3[t][i];
-        if (r < C) {
-          const size_t o = ((size_t)(r0 + r) * H + h) * DK + c;
-          p.dq[o] = sGam[r] * P1[t][i] + dq[i];
-          p.dk[o] = -sGam[r] * P2[t][i] + sFac[r] * P3[t][i] + dk[i];
-        }
+        q1 += (float)q4[i] * P1[t][i];
+        k2 += (float)k4[i] * P2[t][i];
+        k3 += (float)k4[i] * P3[t][i];
+        oq[i] = gr * P1[t][i] + dq[i];
+        ok[i] = -gr * P2[t][i] + fr * P3[t][i] + dk[i];
+      }
+      if (rr < C) {
+        const size_t o = ((size_t)(r0 + rr) * H + h) * DK + c0;
+        *reinterpret_cast<f32x4 *>(p.dq + o) = oq;
+        *reinterpret_cast<f32x4 *>(p.dk + o) = ok;
       }
     }
+    // the row's sums over its four lane groups
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float a = sum16(q1[i]), b = sum16(k2[i]), c = sum16(k3[i]);
-      if (lr == 0) {
-        const int r = 16 * w + 4 * lg + i;
-        rowt[3][r] = a;
-        rowt[4][r] = b;
-        rowt[5][r] = c;
-      }
+    for (int m = 16; m < 64; m <<= 1) {
+      q1 += __shfl_xor(q1, m, 64);
+      k2 += __shfl_xor(k2, m, 64);
+      k3 += __shfl_xor(k3, m, 64);
+    }
+    if (lg == 0) {
+      rowt[3][rr] = q1;
+      rowt[4][rr] = k2;
+      rowt[5][rr] = k3;
     }
   }
   sync_lds();

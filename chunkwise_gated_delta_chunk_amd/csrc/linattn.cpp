@@ -555,8 +555,11 @@ static int chunk_bwd(const la_chunk_bwd_args *a, bool kda, void *stream) {
   const BwdLayout L = bwd_layout(a, kda);
   if (a->workspace_bytes < L.total) return LA_ERR_WORKSPACE;
   if (reinterpret_cast<uintptr_t>(a->workspace) % 256 != 0) return LA_ERR_WORKSPACE;
+  // 16-byte vector loads of q, k, v and dout rows, 16-byte stores of dq, dk, dv
   const uintptr_t mis = reinterpret_cast<uintptr_t>(a->q) | reinterpret_cast<uintptr_t>(a->k) |
-                        reinterpret_cast<uintptr_t>(a->v);
+                        reinterpret_cast<uintptr_t>(a->v) | reinterpret_cast<uintptr_t>(a->dout) |
+                        reinterpret_cast<uintptr_t>(a->dq) | reinterpret_cast<uintptr_t>(a->dk) |
+                        reinterpret_cast<uintptr_t>(a->dv);
   if (mis % 16 != 0) return LA_ERR_SHAPE;
   char *ws = static_cast<char *>(a->workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);

@@ -364,8 +364,9 @@ size_t la_chunk_bwd_workspace_bytes(const la_chunk_bwd_args *shape, int is_kda);
  * every call, it creates no stream or event and allocates nothing (all
  * scratch is the caller's workspace).
  * Host errors: LA_ERR_NULL (also: only some of aux_stream, fork_event,
- * join_event set), LA_ERR_SHAPE, LA_ERR_DTYPE, LA_ERR_UNSUPPORTED,
- * LA_ERR_WORKSPACE, LA_ERR_HIP.
+ * join_event set), LA_ERR_SHAPE (also: q, k, v, dout, dq, dk or dv not
+ * 16-byte aligned), LA_ERR_DTYPE, LA_ERR_UNSUPPORTED, LA_ERR_WORKSPACE,
+ * LA_ERR_HIP.
  */
 int gdn_chunk_bwd(const la_chunk_bwd_args *a, void *stream);
 int kda_chunk_bwd(const la_chunk_bwd_args *a, void *stream);

@@ -308,6 +308,10 @@ BBAD = [
     ("no workspace", dict(workspace=None), -5),
     ("workspace small", dict(workspace_bytes=1000), -5),
     ("q misaligned", dict(q=0x100008), -2),
+    ("dout misaligned", dict(dout=0x100004), -2),
+    ("dq misaligned", dict(dq=0x100008), -2),
+    ("dk misaligned", dict(dk=0x100004), -2),
+    ("dv misaligned", dict(dv=0x100008), -2),
     ("H 0", dict(H=0), -2),
     ("aux stream without events", dict(aux_stream=0x100000), -1),
     ("events without aux stream", dict(fork_event=0x100000, join_event=0x100000), -1),
