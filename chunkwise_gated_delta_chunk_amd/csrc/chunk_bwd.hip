@@ -125,7 +125,10 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_bf16_kernel(BwdParams p) {
   float *img = p.prep + (size_t)blockIdx.x * kPrepFloats;
   __bf16 *imh = reinterpret_cast<__bf16 *>(img + kPrepH);
   const int w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
-  // S = strict_lower(K K^T * E), M = lower_incl(Q K^T * E): wave w, rows 16w
+  // S = strict_lower(K K^T * E), M = lower_incl(Q K^T * E): wave w, rows
+  // 16w, formed transposed (operands swapped) so that lane (g, n) holds row
+  // 16 w + n at the columns 16 s4 + 4 g .. +3: S goes to LDS and M's bf16
+  // halves to the image in 16- and 8-byte pieces
   f32x4 aS[4] = {zero4(), zero4(), zero4(), zero4()};
   f32x4 aM[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
@@ -134,30 +137,52 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_bf16_kernel(BwdParams p) {
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       const bf16x8_t b = frag_row(sK, LDK, 16 * s4 + lr, 32 * s);
-      aS[s4] = mfma_bf(ak, b, aS[s4]);
-      aM[s4] = mfma_bf(aq, b, aM[s4]);
+      aS[s4] = mfma_bf(b, ak, aS[s4]);
+      aM[s4] = mfma_bf(b, aq, aM[s4]);
     }
   }
+  {
+    const int r = 16 * w + lr;
+    const float gr = sG[r];
 #pragma unroll
-  for (int s4 = 0; s4 < 4; ++s4) {
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int s0 = 16 * s4 + 4 * lg;
+      const f32x4 gs = *reinterpret_cast<const f32x4 *>(sG + s0);
+      f32x4 sv;
+      bf16x4_t mh, ml;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * w + 4 * lg + i, s = 16 * s4 + lr;
-      const float e = (r < C && s <= r) ? __expf(sG[r] - sG[s]) : 0.f;
-      const float Sv = s < r ? aS[s4][i] * e : 0.f;
-      const float Mv = aM[s4][i] * e;
-      sS[r * kL + s] = Sv;
-      splitb(Mv, imh[r * 64 + s], imh[4096 + r * 64 + s]);  // (no fp32 S, M: see the fused kernel)
+      for (int i = 0; i < 4; ++i) {
+        const int s = s0 + i;
+        const float e = (r < C && s <= r) ? __expf(gr - gs[i]) : 0.f;
+        sv[i] = s < r ? aS[s4][i] * e : 0.f;
+        const float mv = aM[s4][i] * e;  // (no fp32 S, M: see the fused kernel)
+        mh[i] = (__bf16)mv;
+        ml[i] = (__bf16)(mv - (float)mh[i]);
+      }
+      *reinterpret_cast<f32x4 *>(sS + r * kL + s0) = sv;
+      *reinterpret_cast<bf16x4_t *>(imh + r * 64 + s0) = mh;
+      *reinterpret_cast<bf16x4_t *>(imh + 4096 + r * 64 + s0) = ml;
     }
   }
   __syncthreads();
-  // A^-1 = (I + diag(beta) S)^-1, by 16x16 blocks
+  // A^-1 = (I + diag(beta) S)^-1, by 16x16 blocks; stored with its
+  // A^-1 diag(beta) halves, four consecutive entries per thread
   unit_lower_inverse(sS, sB, sX, C);
-  for (int idx = tid; idx < 64 * 64; idx += 256) {
-    const int r = idx >> 6, c = idx & 63;
-    const float a = sX[r * kL + c];
-    img[kPrepA + idx] = a;
-    splitb(a * sB[c], imh[8192 + idx], imh[12288 + idx]);  // A^-1 diag(beta)
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = 4 * tid + 1024 * it, r = idx >> 6, c = idx & 63;
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(sX + r * kL + c);
+    const f32x4 b = *reinterpret_cast<const f32x4 *>(sB + c);
+    bf16x4_t ah, al;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float x = a[e] * b[e];
+      ah[e] = (__bf16)x;
+      al[e] = (__bf16)(x - (float)ah[e]);
+    }
+    *reinterpret_cast<f32x4 *>(img + kPrepA + idx) = a;
+    *reinterpret_cast<bf16x4_t *>(imh + 8192 + idx) = ah;
+    *reinterpret_cast<bf16x4_t *>(imh + 12288 + idx) = al;
   }
   if (tid < 64) {
     const float Gc = sG[C - 1];
