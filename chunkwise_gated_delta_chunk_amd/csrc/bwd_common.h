@@ -41,6 +41,18 @@ __device__ __forceinline__ void splitb(float x, __bf16 &hi, __bf16 &lo) {
   lo = (__bf16)(x - (float)hi);
 }
 
+// four consecutive values -> their bf16 hi / lo halves (8-byte stores)
+__device__ __forceinline__ void split4(__bf16 *hi, __bf16 *lo, const f32x4 &v) {
+  bf16x4_t a, b;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    a[e] = (__bf16)v[e];
+    b[e] = (__bf16)(v[e] - (float)a[e]);
+  }
+  *reinterpret_cast<bf16x4_t *>(hi) = a;
+  *reinterpret_cast<bf16x4_t *>(lo) = b;
+}
+
 // acc += A B over one 32-wide k-step, A and B both split
 __device__ __forceinline__ f32x4 mfma3(bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl, f32x4 c) {
   c = mfma_bf(ah, bh, c);

@@ -431,24 +431,27 @@ __global__ __launch_bounds__(512) void bwd_dh_bf16_kernel(BwdParams p) {
     }
     if (jj > j0) fetch(jj - 1);
     sync_lds();
+    // Every tile below is formed transposed (operands swapped): lane (g, n)
+    // holds row 16 x + n of its tile at the columns 16 y + 4 g .. +3, so
+    // results go to LDS in 16- and 8-byte pieces.
+    const int ur = 16 * rt + lr, uo = ur * LO + 16 * ct + 4 * lg;
     // dU = M^T dOb + fac * (K dH'): one tile per wave
     {
       f32x4 kd = zero4(), du = zero4();
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
         const bf16x8_t a = frag_row(sK, LDK, 16 * rt + lr, 32 * s);
-        kd = mfma_bf(a, frag_col(sDh, LO, 32 * s, 16 * ct), kd);
-        kd = mfma_bf(a, frag_col(sDl, LO, 32 * s, 16 * ct), kd);
+        kd = mfma_bf(frag_col(sDh, LO, 32 * s, 16 * ct), a, kd);
+        kd = mfma_bf(frag_col(sDl, LO, 32 * s, 16 * ct), a, kd);
       }
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        du = mfma3(frag_col(sMh, LT, 32 * s, 16 * rt), frag_col(sMl, LT, 32 * s, 16 * rt),
-                   frag_col(sOh, LO, 32 * s, 16 * ct), frag_col(sOl, LO, 32 * s, 16 * ct), du);
+        du = mfma3(frag_col(sOh, LO, 32 * s, 16 * ct), frag_col(sOl, LO, 32 * s, 16 * ct),
+                   frag_col(sMh, LT, 32 * s, 16 * rt), frag_col(sMl, LT, 32 * s, 16 * rt), du);
+      const float f = sFac[ur];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i, c = 16 * ct + lr;
-        splitb(du[i] + sFac[r] * kd[i], sUh[r * LO + c], sUl[r * LO + c]);
-      }
+      for (int i = 0; i < 4; ++i) du[i] += f * kd[i];
+      split4(sUh + uo, sUl + uo, du);
     }
     sync_lds();
     // dX = beta * (A^-T dU) = A~^T dU; Y = gam * dX (over dOb, read by now)
@@ -456,13 +459,12 @@ __global__ __launch_bounds__(512) void bwd_dh_bf16_kernel(BwdParams p) {
       f32x4 dx = zero4();
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        dx = mfma3(frag_col(sAh, LT, 32 * s, 16 * rt), frag_col(sAl, LT, 32 * s, 16 * rt),
-                   frag_col(sUh, LO, 32 * s, 16 * ct), frag_col(sUl, LO, 32 * s, 16 * ct), dx);
+        dx = mfma3(frag_col(sUh, LO, 32 * s, 16 * ct), frag_col(sUl, LO, 32 * s, 16 * ct),
+                   frag_col(sAh, LT, 32 * s, 16 * rt), frag_col(sAl, LT, 32 * s, 16 * rt), dx);
+      const float gm = sGam[ur];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i, c = 16 * ct + lr;
-        splitb(sGam[r] * dx[i], sYh[r * LO + c], sYl[r * LO + c]);
-      }
+      for (int i = 0; i < 4; ++i) dx[i] *= gm;
+      split4(sYh + uo, sYl + uo, dx);
     }
     sync_lds();
     // dH = gam_C dH' + Q^T (gam dOb) - K^T Y
@@ -479,25 +481,23 @@ __global__ __launch_bounds__(512) void bwd_dh_bf16_kernel(BwdParams p) {
 #pragma unroll
       for (int tt = 0; tt < DK / 64; ++tt) {
         const int t = (w >> 1) + 4 * tt;
-        f32x4 acc, ky = zero4();
+        const int row = 16 * t + lr, c0 = 16 * ht + 4 * lg;
+        f32x4 acc = *reinterpret_cast<const f32x4 *>(sD + row * LC + c0), ky = zero4();
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] = gamC * sD[(16 * t + 4 * lg + i) * LC + 16 * ht + lr];
+        for (int i = 0; i < 4; ++i) acc[i] *= gamC;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
           const bf16x8_t aq = frag_col(sQ, LDK, 32 * s, 16 * t);
           const bf16x8_t ak = frag_col(sK, LDK, 32 * s, 16 * t);
-          acc = mfma_bf(aq, bgh[s], acc);
-          acc = mfma_bf(aq, bgl[s], acc);
-          ky = mfma_bf(ak, byh[s], ky);
-          ky = mfma_bf(ak, byl[s], ky);
+          acc = mfma_bf(bgh[s], aq, acc);
+          acc = mfma_bf(bgl[s], aq, acc);
+          ky = mfma_bf(byh[s], ak, ky);
+          ky = mfma_bf(byl[s], ak, ky);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * t + 4 * lg + i, c = 16 * ht + lr;
-          const float v = acc[i] - ky[i];
-          sD[row * LC + c] = v;
-          splitb(v, sDh[row * LO + c], sDl[row * LO + c]);
-        }
+        for (int i = 0; i < 4; ++i) acc[i] -= ky[i];
+        *reinterpret_cast<f32x4 *>(sD + row * LC + c0) = acc;
+        split4(sDh + row * LO + c0, sDl + row * LO + c0, acc);
       }
     }
   }
