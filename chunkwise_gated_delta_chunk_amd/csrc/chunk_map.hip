@@ -674,8 +674,12 @@ __global__ __launch_bounds__(kThreads) void chunk_map_kernel(MapParams p) {
 
 // ---------------------------------------------------------------------------
 // 16-bit GDN (bf16 / fp16 inputs on fp16 MFMA): a persistent kernel, one
-// workgroup per resident slot, walking cells (chunk slot, head) with a stride
-// of the grid.  The raw q / k rows of a workgroup's next cell are loaded into
+// workgroup per resident slot, walking cells (chunk slot, head).  Workgroups
+// are dispatched to the 8 XCDs round-robin (b on XCD b % 8), and XCD x takes
+// the slots s = x (mod 8) with all their heads: the g / beta lines of a
+// slot's rows (every head of a token shares one) are then fetched into one
+// XCD's L2 only.  The workgroups of an XCD walk its cells with a stride of
+// their count.  The raw q / k rows of a workgroup's next cell are loaded into
 // registers while it computes the current one, so the HBM reads of one cell
 // overlap the products, the inverse and the stores of the previous.
 //
@@ -725,7 +729,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
   constexpr int PK = DK * 2 / 16;
   constexpr int SKIP = image_skip(false, 2, DK, RAW);
   constexpr int HBM = image_hbm_bytes(false, 2, DK, RAW);
-  const int ncell = p.NT_max * H;
   float *Gw = sGw[w];
 
   // staging unit of a thread: row r, 32-element block b, half g2: input
@@ -798,8 +801,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     else return (T)__uint_as_float(x << 16);
   };
 
-  int cell = blockIdx.x;
-  if (cell >= ncell) return;
+  // this workgroup's k-th cell: index jw + k * per of its XCD's cells, -1
+  // past the last slot (the grid is a multiple of 8)
+  const int xcd = blockIdx.x & 7, per = gridDim.x >> 3, jw = blockIdx.x >> 3;
+  auto cell_at = [&](int k) {
+    const int i = jw + k * per, slot = xcd + 8 * (i / H);
+    return slot < p.NT_max ? slot * H + i % H : -1;
+  };
+  int kc = 0;
+  int cell = cell_at(0);
+  if (cell < 0) return;
   int r0, C;
   cell_rows(cell, r0, C);
   if (C <= 0) return;  // sentinel: this and every later cell (slots fill in order)
@@ -870,9 +881,9 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
       sg[tid] = gval;
     }
     // the next cell's rows (issued once the current ones are consumed)
-    const int next = cell + gridDim.x;
+    const int next = cell_at(kc + 1);
     int nr0 = 0, nC = 0;
-    if (next < ncell) cell_rows(next, nr0, nC);
+    if (next >= 0) cell_rows(next, nr0, nC);
     __syncthreads();  // S1: K, Q, beta, g in LDS
 
     const float Gl = wave_inclusive_scan(sg[lane]);  // lane r holds G_r
@@ -1118,6 +1129,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4, 4))
     }
     if (nC <= 0) break;  // no next cell, or a sentinel (slots fill in order)
     cell = next;
+    ++kc;
     __syncthreads();  // S4: the scratch is free for the next cell's K and Q
   }
 }
@@ -1149,8 +1161,9 @@ static hipError_t launch_map16(const MapParams &p, hipStream_t st) {
     res = cus * per > 0 ? cus * per : 1;
     if (dev < 64) slots[dev] = res;
   }
+  // a multiple of 8 (the kernel's XCD order); workgroups past the cells exit
   const int cells = p.H * p.NT_max;
-  const int grid = cells < res ? cells : res;
+  const int grid = ((cells < res ? cells : res) + 7) / 8 * 8;
   hipLaunchKernelGGL((chunk_map16_kernel<In, DK, RAW>), dim3(grid), dim3(kThreads), 0, st, p);
   return hipGetLastError();
 }
