@@ -1073,24 +1073,32 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
   else if (tid < 128) sBeta[tid - 64] = fvec;
   sync_lds();
   // Z = dM * M (gates), dT * A^-1 (beta); dT' = dT diag(beta), dM * E, split,
-  // over the lower triangle of real rows
+  // over the lower triangle of real rows.  dT' and dM * E are stored
+  // transposed: the lane's four rows r0 .. r0 + 3 of column s are one 8-byte
+  // piece of row s there (their readers take frag_col for frag_row).
   {
     float zr[4] = {0.f, 0.f, 0.f, 0.f};
+    const int r0 = 16 * w + 4 * lg;
+    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sG + r0);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int s = 16 * t + lr;
+      const int s = 16 * t + lr, o = s * LT + r0;
+      const float bs = sBeta[s], gs = sG[s];
       float zc = 0.f, bt = 0.f;
+      f32x4 fv, ev;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * lg + i, o = r * LT + s;
+        const int r = r0 + i;
         const bool lo = s <= r && r < C;
         const float z = lo ? dM[t][i] * fmm[t][i] : 0.f;
         zr[i] += z;
         zc += z;
         bt += lo ? dT[t][i] * fam[t][i] : 0.f;
-        splitb(lo ? dT[t][i] * sBeta[s] : 0.f, qFh[o], qFl[o]);
-        splitb(lo ? dM[t][i] * __expf(sG[r] - sG[s]) : 0.f, qEh[o], qEl[o]);
+        fv[i] = lo ? dT[t][i] * bs : 0.f;
+        ev[i] = lo ? dM[t][i] * __expf(g4[i] - gs) : 0.f;
       }
+      split4(qFh + o, qFl + o, fv);
+      split4(qEh + o, qEl + o, ev);
       zc += __shfl_xor(zc, 16, 64);
       zc += __shfl_xor(zc, 32, 64);
       bt += __shfl_xor(bt, 16, 64);
@@ -1112,7 +1120,7 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
     f32x4 t2[4] = {zero4(), zero4(), zero4(), zero4()};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const bf16x8_t ah = frag_row(qFh, LT, 16 * w + lr, 32 * s), al = frag_row(qFl, LT, 16 * w + lr, 32 * s);
+      const bf16x8_t ah = frag_col(qFh, LT, 32 * s, 16 * w), al = frag_col(qFl, LT, 32 * s, 16 * w);
 #pragma unroll
       for (int t = 0; t < 4; ++t)
         t2[t] = mfma3(ah, al, frag_row(qA1h, LT, 16 * t + lr, 32 * s), frag_row(qA1l, LT, 16 * t + lr, 32 * s),
@@ -1196,10 +1204,10 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
     bf16x8_t aE[2][2], aET[2][2], aF[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      aE[s][0] = frag_row(qEh, LT, 16 * w + lr, 32 * s);
-      aE[s][1] = frag_row(qEl, LT, 16 * w + lr, 32 * s);
-      aET[s][0] = frag_col(qEh, LT, 32 * s, 16 * w);
-      aET[s][1] = frag_col(qEl, LT, 32 * s, 16 * w);
+      aE[s][0] = frag_col(qEh, LT, 32 * s, 16 * w);  // E is stored transposed
+      aE[s][1] = frag_col(qEl, LT, 32 * s, 16 * w);
+      aET[s][0] = frag_row(qEh, LT, 16 * w + lr, 32 * s);
+      aET[s][1] = frag_row(qEl, LT, 16 * w + lr, 32 * s);
       aF[s][0] = frag_row(qFh, LT, 16 * w + lr, 32 * s);
       aF[s][1] = frag_row(qFl, LT, 16 * w + lr, 32 * s);
     }
