@@ -803,7 +803,7 @@ __device__ __forceinline__ float wave_sum(float x) {
 // stage follows in the same block, so nothing of either goes through HBM.
 // Phase 1 is the 32-column loop (X, dU, U, dX = dV, and P1 = dOb H^T,
 // P2 = dX H^T, P3 = U dH'^T, dM = dOb U^T, dT = dU X^T accumulated); phase 2
-// reuses the loop's LDS for A^-1, tmp = dT' A^-T, F + F^T and dM*E.  Wave w
+// reuses the loop's LDS for A^-1, tmp = dT' A^-T, F^T and dM*E.  Wave w
 // owns row tile w throughout, so the P tiles it accumulates are the dq/dk
 // tiles it writes.  One wave per SIMD leaves each wave 512 registers for the
 // accumulators and the prefetched block, so nothing spills to memory (a
@@ -816,7 +816,7 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
   constexpr int PT = DK / 16;            // column tiles of P1..P3, dq and dk
   constexpr int MT = 64 * LT;            // one [64][LT] array
   // pool: [K][phase 1: M, A~ halves | H, dH' halves | 64-row block arrays]
-  //       [K][phase 2: A^-1 (then Q), tmp, dT' (then F + F^T), dM*E, halves]
+  //       [K][phase 2: A^-1 (then Q), tmp, dT'^T (then F^T), dM*E, halves]
   constexpr int P1SZ = 4 * MT + 4 * DK * LB + 11 * 64 * LB, P2SZ = 8 * MT;
   static_assert(P2SZ <= P1SZ && 64 * LDK <= 2 * MT, "phase-2 arrays fit");
   __shared__ __attribute__((aligned(16))) __bf16 pool[64 * LDK + P1SZ];
@@ -1136,7 +1136,7 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
   }
   sync_lds();
   // dA = -A^-T tmp; strict lower part: W = dA S (beta), Y = beta dA S
-  // (gates), F = beta dA E (keys), stored as F + F^T over dT'.  S = K K^T * E
+  // (gates), F = beta dA E (keys), stored as F^T over dT'^T.  S = K K^T * E
   // is recomputed here: K is exact in bf16 and still in LDS.
   {
     f32x4 kk[4] = {zero4(), zero4(), zero4(), zero4()};
@@ -1154,29 +1154,34 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
       for (int t = 0; t < 4; ++t)
         t3[t] = mfma3(ah, al, frag_col(qTh, LT, 32 * s, 16 * t), frag_col(qTl, LT, 32 * s, 16 * t), t3[t]);
     }
+    // F (strict lower) is stored transposed, F[r][s] at [s][r]: the lane's
+    // rows r0 .. r0 + 3 of column s are one 8-byte piece of row s, zero on
+    // and below the diagonal (over dT'^T, which is zero below it already,
+    // so every entry of the array is F^T afterwards)
     float wr[4] = {0.f, 0.f, 0.f, 0.f}, yr[4] = {0.f, 0.f, 0.f, 0.f};
+    const int r0 = 16 * w + 4 * lg;
+    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sG + r0);
+    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(sBeta + r0);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       const int s = 16 * t + lr;
+      const float gs = sG[s];
       float yc = 0.f;
+      f32x4 fv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * w + 4 * lg + i;
+        const int r = r0 + i;
         const bool sl = s < r && r < C;
         const float dA = -t3[t][i];
-        const float Wv = sl ? dA * kk[t][i] * __expf(sG[r] - sG[s]) : 0.f;
-        const float Yv = sBeta[r] * Wv;
-        const float Fv = sl ? sBeta[r] * dA * __expf(sG[r] - sG[s]) : 0.f;
+        const float ex = __expf(g4[i] - gs);
+        const float Wv = sl ? dA * kk[t][i] * ex : 0.f;
+        const float Yv = b4[i] * Wv;
+        fv[i] = sl ? b4[i] * dA * ex : 0.f;
         wr[i] += Wv;
         yr[i] += Yv;
         yc += Yv;
-        if (s < r) {
-          splitb(Fv, qFh[r * LT + s], qFl[r * LT + s]);
-          splitb(Fv, qFh[s * LT + r], qFl[s * LT + r]);
-        } else if (s == r) {
-          qFh[r * LT + r] = qFl[r * LT + r] = (__bf16)0.f;
-        }
       }
+      split4(qFh + s * LT + r0, qFl + s * LT + r0, fv);
       yc += __shfl_xor(yc, 16, 64);
       yc += __shfl_xor(yc, 32, 64);
       if (lg == 0) colt[2][w][s] = yc;
@@ -1198,18 +1203,20 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
     *reinterpret_cast<u32x4 *>(sQ + r * LDK + c) = rq[it];
   }
   sync_lds();
-  // dQ = gam P1 + (dM E) K;  dK = -gam P2 + fac P3 + (dM E)^T Q + (F + F^T) K,
+  // dQ = gam P1 + (dM E) K;  dK = -gam P2 + fac P3 + (dM E)^T Q + F K + F^T K,
   // and the gate dots <q_r, P1_r>, <k_r, P2_r>, <k_r, P3_r>
   {
-    bf16x8_t aE[2][2], aET[2][2], aF[2][2];
+    bf16x8_t aE[2][2], aET[2][2], aF[2][2], aFT[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       aE[s][0] = frag_col(qEh, LT, 32 * s, 16 * w);  // E is stored transposed
       aE[s][1] = frag_col(qEl, LT, 32 * s, 16 * w);
       aET[s][0] = frag_row(qEh, LT, 16 * w + lr, 32 * s);
       aET[s][1] = frag_row(qEl, LT, 16 * w + lr, 32 * s);
-      aF[s][0] = frag_row(qFh, LT, 16 * w + lr, 32 * s);
-      aF[s][1] = frag_row(qFl, LT, 16 * w + lr, 32 * s);
+      aF[s][0] = frag_col(qFh, LT, 32 * s, 16 * w);  // F^T is stored
+      aF[s][1] = frag_col(qFl, LT, 32 * s, 16 * w);
+      aFT[s][0] = frag_row(qFh, LT, 16 * w + lr, 32 * s);
+      aFT[s][1] = frag_row(qFl, LT, 16 * w + lr, 32 * s);
     }
     // every tile transposed (K^T and Q^T as A operands): lane (g, n) holds
     // row rr = 16 w + n at the columns 16 t + 4 g .. +3, so the dq / dk rows
@@ -1229,6 +1236,8 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
         dk = mfma_bf(bq, aET[s][1], dk);
         dk = mfma_bf(bk, aF[s][0], dk);
         dk = mfma_bf(bk, aF[s][1], dk);
+        dk = mfma_bf(bk, aFT[s][0], dk);
+        dk = mfma_bf(bk, aFT[s][1], dk);
       }
       const int c0 = 16 * t + 4 * lg;
       const bf16x4_t q4 = *reinterpret_cast<const bf16x4_t *>(sQ + rr * LDK + c0);
