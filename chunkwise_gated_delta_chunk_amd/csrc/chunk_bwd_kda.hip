@@ -502,22 +502,22 @@ __global__ __launch_bounds__(512) void kda_dh_bf16_kernel(BwdParams p) {
     }
     if (jj > j0) fetch(jj - 1);
     sync_lds();
+    // Every tile below is formed transposed (operands swapped): lane (g, n)
+    // holds row 16 x + n of its tile at the columns 16 y + 4 g .. +3, so
+    // results go to LDS in 16- and 8-byte pieces.
+    const int uo = (16 * rt + lr) * LO + 16 * ct + 4 * lg;
     // dU = M^T dOb + Kh dH': one tile per wave
     {
       f32x4 du = zero4();
 #pragma unroll
       for (int s = 0; s < NKS; ++s)
-        du = mfma3(frag_row(sKh, LDK, 16 * rt + lr, 32 * s), frag_row(sKl, LDK, 16 * rt + lr, 32 * s),
-                   frag_col(sDh, LO, 32 * s, 16 * ct), frag_col(sDl, LO, 32 * s, 16 * ct), du);
+        du = mfma3(frag_col(sDh, LO, 32 * s, 16 * ct), frag_col(sDl, LO, 32 * s, 16 * ct),
+                   frag_row(sKh, LDK, 16 * rt + lr, 32 * s), frag_row(sKl, LDK, 16 * rt + lr, 32 * s), du);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        du = mfma3(frag_col(sMh, LT, 32 * s, 16 * rt), frag_col(sMl, LT, 32 * s, 16 * rt),
-                   frag_col(sOh, LO, 32 * s, 16 * ct), frag_col(sOl, LO, 32 * s, 16 * ct), du);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i, c = 16 * ct + lr;
-        splitb(du[i], sUh[r * LO + c], sUl[r * LO + c]);
-      }
+        du = mfma3(frag_col(sOh, LO, 32 * s, 16 * ct), frag_col(sOl, LO, 32 * s, 16 * ct),
+                   frag_col(sMh, LT, 32 * s, 16 * rt), frag_col(sMl, LT, 32 * s, 16 * rt), du);
+      split4(sUh + uo, sUl + uo, du);
     }
     sync_lds();
     // dX = A~^T dU
@@ -525,13 +525,9 @@ __global__ __launch_bounds__(512) void kda_dh_bf16_kernel(BwdParams p) {
       f32x4 dx = zero4();
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        dx = mfma3(frag_col(sAh, LT, 32 * s, 16 * rt), frag_col(sAl, LT, 32 * s, 16 * rt),
-                   frag_col(sUh, LO, 32 * s, 16 * ct), frag_col(sUl, LO, 32 * s, 16 * ct), dx);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int r = 16 * rt + 4 * lg + i, c = 16 * ct + lr;
-        splitb(dx[i], sXh[r * LO + c], sXl[r * LO + c]);
-      }
+        dx = mfma3(frag_col(sUh, LO, 32 * s, 16 * ct), frag_col(sUl, LO, 32 * s, 16 * ct),
+                   frag_col(sAh, LT, 32 * s, 16 * rt), frag_col(sAl, LT, 32 * s, 16 * rt), dx);
+      split4(sXh + uo, sXl + uo, dx);
     }
     sync_lds();
     // Kt over Kh, Qt over the M and A~ halves
@@ -557,24 +553,20 @@ __global__ __launch_bounds__(512) void kda_dh_bf16_kernel(BwdParams p) {
 #pragma unroll
       for (int tt = 0; tt < DK / 64; ++tt) {
         const int t = (w >> 1) + 4 * tt;
-        f32x4 acc, ky = zero4();
+        const int row = 16 * t + lr, c0 = 16 * ht + 4 * lg;
+        f32x4 acc = *reinterpret_cast<const f32x4 *>(sD + row * LC + c0), ky = zero4();
+        const float gc = sGC[row];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * t + 4 * lg + i;
-          acc[i] = sGC[row] * sD[row * LC + 16 * ht + lr];
-        }
+        for (int i = 0; i < 4; ++i) acc[i] *= gc;
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          acc = mfma3(frag_col(sQh, LDK, 32 * s, 16 * t), frag_col(sQl, LDK, 32 * s, 16 * t), boh[s], bol[s], acc);
-          ky = mfma3(frag_col(sKh, LDK, 32 * s, 16 * t), frag_col(sKl, LDK, 32 * s, 16 * t), bxh[s], bxl[s], ky);
+          acc = mfma3(boh[s], bol[s], frag_col(sQh, LDK, 32 * s, 16 * t), frag_col(sQl, LDK, 32 * s, 16 * t), acc);
+          ky = mfma3(bxh[s], bxl[s], frag_col(sKh, LDK, 32 * s, 16 * t), frag_col(sKl, LDK, 32 * s, 16 * t), ky);
         }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int row = 16 * t + 4 * lg + i, c = 16 * ht + lr;
-          const float v = acc[i] - ky[i];
-          sD[row * LC + c] = v;
-          splitb(v, sDh[row * LO + c], sDl[row * LO + c]);
-        }
+        for (int i = 0; i < 4; ++i) acc[i] -= ky[i];
+        *reinterpret_cast<f32x4 *>(sD + row * LC + c0) = acc;
+        split4(sDh + row * LO + c0, sDl + row * LO + c0, acc);
       }
     }
   }
