@@ -805,23 +805,31 @@ __device__ __forceinline__ float wave_sum(float x) {
 // P2 = dX H^T, P3 = U dH'^T, dM = dOb U^T, dT = dU X^T accumulated); phase 2
 // reuses the loop's LDS for A^-1, tmp = dT' A^-T, F^T and dM*E.  Wave w
 // owns row tile w throughout, so the P tiles it accumulates are the dq/dk
-// tiles it writes.  One wave per SIMD leaves each wave 512 registers for the
-// accumulators and the prefetched block, so nothing spills to memory (a
-// spill reload would wait for every load in flight).
+// tiles it writes.
+// Eight waves, two per SIMD, so that one wave's LDS and MFMA latencies hide
+// behind the other's work (with 256 registers per wave and nothing spilled:
+// a spill reload would wait for every load in flight).  Wave w takes row
+// tile rt = w % 4 and column half hc = w / 4 of every per-wave product: the
+// X / dU / U / dX tile of column half hc, the P1..P3 (and dq / dk) column
+// tiles of half hc, and the dM, dT (Z, dA, tmp) column tiles 2 hc, 2 hc + 1.
+// Row sums of the two halves meet in a [6][2][64] table; column sums stay
+// per row tile.
 template <int DK>
-__global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
+__global__ __launch_bounds__(512) void bwd_cell8_bf16_kernel(BwdParams p) {
   constexpr int DV = DK, LDK = DK + 16, LT = 72, NB = 32, LB = NB + 8, NBLK = DV / NB, NKS = DK / 32;
-  constexpr int KP = 64 * DK / 8 / 256;  // 16-byte K (or Q) pieces per thread
-  constexpr int HP = DK * NB / 4 / 256;  // float4 pieces of an H (or dH') block per thread
+  constexpr int KP = 64 * DK / 8 / 512;  // 16-byte K (or Q) pieces per thread
+  constexpr int HP = DK * NB / 4 / 512;  // float4 pieces of an H (or dH') block per thread
   constexpr int PT = DK / 16;            // column tiles of P1..P3, dq and dk
+  constexpr int PW = PT / 2;             // ... per wave
   constexpr int MT = 64 * LT;            // one [64][LT] array
+  static_assert(KP >= 1 && HP >= 1, "piece split");
   // pool: [K][phase 1: M, A~ halves | H, dH' halves | 64-row block arrays]
   //       [K][phase 2: A^-1 (then Q), tmp, dT'^T (then F^T), dM*E, halves]
   constexpr int P1SZ = 4 * MT + 4 * DK * LB + 11 * 64 * LB, P2SZ = 8 * MT;
   static_assert(P2SZ <= P1SZ && 64 * LDK <= 2 * MT, "phase-2 arrays fit");
   __shared__ __attribute__((aligned(16))) __bf16 pool[64 * LDK + P1SZ];
   __shared__ __attribute__((aligned(16))) float sGam[64], sFac[64], sG[64], sBeta[64];
-  __shared__ __attribute__((aligned(16))) float rowt[6][64], colt[3][4][64], sh4[4];
+  __shared__ __attribute__((aligned(16))) float rowp[6][2][64], colt[3][4][64], sh8[8];
   __bf16 *const sK = pool, *const ph = pool + 64 * LDK;
   __bf16 *const sMh = ph, *const sMl = ph + MT, *const sAh = ph + 2 * MT, *const sAl = ph + 3 * MT;
   __bf16 *const sHh = ph + 4 * MT, *const sHl = sHh + DK * LB, *const sDh = sHl + DK * LB,
@@ -841,6 +849,7 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
   if (!chunk_of(p, slot, ch)) return;
   const int C = ch.C, r0 = ch.r0;
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
+  const int rt = w & 3, hc = w >> 2;  // row tile, column half
   const int Hqk = p.Hqk, hq = h / (H / Hqk);
   const float *img = p.prep + (size_t)blockIdx.x * kPrepFloats;
   const size_t mat = (size_t)DK * DV;
@@ -850,11 +859,11 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
 
   // ---- the cell's K, M and A~ halves, gam and fac
   {
-    u32x4 rk[KP], rimg[8];
+    u32x4 rk[KP], rimg[4];
     float rvec = 0.f;
 #pragma unroll
     for (int it = 0; it < KP; ++it) {
-      const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+      const int pc = tid + 512 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
       rk[it] = u32x4{0u, 0u, 0u, 0u};
       if (r < C)
         rk[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.k) +
@@ -862,198 +871,165 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
     }
     const u32x4 *imh = reinterpret_cast<const u32x4 *>(img + kPrepH);
 #pragma unroll
-    for (int it = 0; it < 8; ++it) rimg[it] = imh[tid + 256 * it];
+    for (int it = 0; it < 4; ++it) rimg[it] = imh[tid + 512 * it];
     if (tid < 128) rvec = img[kPrepGam + tid];
 #pragma unroll
     for (int it = 0; it < KP; ++it) {
-      const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+      const int pc = tid + 512 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
       *reinterpret_cast<u32x4 *>(sK + r * LDK + c) = rk[it];
     }
 #pragma unroll
-    for (int it = 0; it < 8; ++it) {
-      const int pc = tid + 256 * it, a = pc >> 9, r = (pc & 511) / 8, c = (pc % 8) * 8;
-      *reinterpret_cast<u32x4 *>(ph + a * MT + r * LT + c) = rimg[it];
+    for (int it = 0; it < 4; ++it) {
+      const int r = tid / 8, c = (tid % 8) * 8;  // array it, row r, 8 columns
+      *reinterpret_cast<u32x4 *>(ph + it * MT + r * LT + c) = rimg[it];
     }
     if (tid < 64) sGam[tid] = rvec;
     else if (tid < 128) sFac[tid - 64] = rvec;
   }
 
   // ---- phase 1
-  f32x4 rh[HP], rd[HP], ro[2];
-  u32x4 rv;
+  f32x4 rh[HP], rd[HP], ro;
+  u32x4 rv = u32x4{0u, 0u, 0u, 0u};
   auto fetch = [&](int cb) {
     const int cc = NB * cb;
 #pragma unroll
     for (int it = 0; it < HP; ++it) {
-      const int pc = tid + 256 * it, i = pc / (NB / 4), c = (pc % (NB / 4)) * 4;
+      const int pc = tid + 512 * it, i = pc / (NB / 4), c = (pc % (NB / 4)) * 4;
       rh[it] = *reinterpret_cast<const f32x4 *>(Hs + (size_t)i * DV + cc + c);
       rd[it] = *reinterpret_cast<const f32x4 *>(Ds + (size_t)i * DV + cc + c);
     }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int pc = tid + 256 * it, r = pc / (NB / 4), c = (pc % (NB / 4)) * 4;
-      ro[it] = r < C ? *reinterpret_cast<const f32x4 *>(p.dout + ((size_t)(r0 + r) * H + h) * DV + cc + c)
-                     : zero4();
-    }
     {
+      const int r = tid / (NB / 4), c = (tid % (NB / 4)) * 4;
+      ro = r < C ? *reinterpret_cast<const f32x4 *>(p.dout + ((size_t)(r0 + r) * H + h) * DV + cc + c)
+                 : zero4();
+    }
+    if (tid < 64 * NB / 8) {
       const int r = tid / (NB / 8), c = (tid % (NB / 8)) * 8;
       rv = r < C ? *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.v) +
                                                      ((size_t)(r0 + r) * H + h) * DV + cc + c)
                  : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  auto put4 = [](__bf16 *hi, __bf16 *lo, f32x4 v) {
-    bf16x4_t a, b;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      a[e] = (__bf16)v[e];
-      b[e] = (__bf16)(v[e] - (float)a[e]);
-    }
-    *reinterpret_cast<bf16x4_t *>(hi) = a;
-    *reinterpret_cast<bf16x4_t *>(lo) = b;
-  };
 
-  f32x4 P1[PT], P2[PT], P3[PT], dM[4], dT[4];
+  f32x4 P1[PW], P2[PW], P3[PW], dM[2], dT[2];
 #pragma unroll
-  for (int t = 0; t < PT; ++t) P1[t] = P2[t] = P3[t] = zero4();
+  for (int t = 0; t < PW; ++t) P1[t] = P2[t] = P3[t] = zero4();
 #pragma unroll
-  for (int t = 0; t < 4; ++t) dM[t] = dT[t] = zero4();
+  for (int t = 0; t < 2; ++t) dM[t] = dT[t] = zero4();
   float shd = 0.f;
   fetch(0);
   for (int cb = 0; cb < NBLK; ++cb) {
     sync_lds();
 #pragma unroll
     for (int it = 0; it < HP; ++it) {
-      const int pc = tid + 256 * it, i = pc / (NB / 4), c = (pc % (NB / 4)) * 4;
-      put4(sHh + i * LB + c, sHl + i * LB + c, rh[it]);
-      put4(sDh + i * LB + c, sDl + i * LB + c, rd[it]);
+      const int pc = tid + 512 * it, i = pc / (NB / 4), c = (pc % (NB / 4)) * 4;
+      split4(sHh + i * LB + c, sHl + i * LB + c, rh[it]);
+      split4(sDh + i * LB + c, sDl + i * LB + c, rd[it]);
 #pragma unroll
       for (int e = 0; e < 4; ++e) shd += rh[it][e] * rd[it][e];
     }
-#pragma unroll
-    for (int it = 0; it < 2; ++it) {
-      const int pc = tid + 256 * it, r = pc / (NB / 4), c = (pc % (NB / 4)) * 4;
-      put4(sOh + r * LB + c, sOl + r * LB + c, ro[it] * p.scale);
-    }
     {
+      const int r = tid / (NB / 4), c = (tid % (NB / 4)) * 4;
+      split4(sOh + r * LB + c, sOl + r * LB + c, ro * p.scale);
+    }
+    if (tid < 64 * NB / 8) {
       const int r = tid / (NB / 8), c = (tid % (NB / 8)) * 8;
       *reinterpret_cast<u32x4 *>(sV + r * LB + c) = rv;
     }
     if (cb + 1 < NBLK) fetch(cb + 1);
     sync_lds();
-    // The products below are formed transposed (operands swapped): lane
-    // (g, n) holds row xr = 16 w + n at the columns 16 hf + 4 g .. +3, so
-    // its hi / lo halves go to LDS as 8-byte pieces and dV leaves as 16-byte
-    // stores.
-    const int xr = 16 * w + lr;
-    // X = V - gam*(K H), dU = M^T dOb + fac*(K dH'): rows 16w, both column tiles
+    // Transposed products (operands swapped): lane (g, n) holds row
+    // xr = 16 rt + n at the columns 16 hc + 4 g .. +3 of this block.
+    const int xr = 16 * rt + lr, xo = xr * LB + 16 * hc + 4 * lg;
+    // X = V - gam*(K H), dU = M^T dOb + fac*(K dH'): rows 16 rt, column half hc
     {
-      f32x4 kh[2] = {zero4(), zero4()}, kd[2] = {zero4(), zero4()}, mo[2] = {zero4(), zero4()};
+      f32x4 kh = zero4(), kd = zero4(), mo = zero4();
 #pragma unroll
       for (int s = 0; s < NKS; ++s) {
-        const bf16x8_t a = frag_row(sK, LDK, 16 * w + lr, 32 * s);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          kh[hf] = mfma_bf(frag_col(sHh, LB, 32 * s, 16 * hf), a, kh[hf]);
-          kh[hf] = mfma_bf(frag_col(sHl, LB, 32 * s, 16 * hf), a, kh[hf]);
-          kd[hf] = mfma_bf(frag_col(sDh, LB, 32 * s, 16 * hf), a, kd[hf]);
-          kd[hf] = mfma_bf(frag_col(sDl, LB, 32 * s, 16 * hf), a, kd[hf]);
-        }
+        const bf16x8_t a = frag_row(sK, LDK, xr, 32 * s);
+        kh = mfma_bf(frag_col(sHh, LB, 32 * s, 16 * hc), a, kh);
+        kh = mfma_bf(frag_col(sHl, LB, 32 * s, 16 * hc), a, kh);
+        kd = mfma_bf(frag_col(sDh, LB, 32 * s, 16 * hc), a, kd);
+        kd = mfma_bf(frag_col(sDl, LB, 32 * s, 16 * hc), a, kd);
       }
 #pragma unroll
-      for (int s = 0; s < 2; ++s) {
-        const bf16x8_t bh = frag_col(sMh, LT, 32 * s, 16 * w), bl = frag_col(sMl, LT, 32 * s, 16 * w);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf)
-          mo[hf] = mfma3(frag_col(sOh, LB, 32 * s, 16 * hf), frag_col(sOl, LB, 32 * s, 16 * hf), bh, bl, mo[hf]);
-      }
+      for (int s = 0; s < 2; ++s)
+        mo = mfma3(frag_col(sOh, LB, 32 * s, 16 * hc), frag_col(sOl, LB, 32 * s, 16 * hc),
+                   frag_col(sMh, LT, 32 * s, 16 * rt), frag_col(sMl, LT, 32 * s, 16 * rt), mo);
       const float gx = sGam[xr], fx = sFac[xr];
+      const bf16x4_t v4 = *reinterpret_cast<const bf16x4_t *>(sV + xo);
+      f32x4 x, y;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int o = xr * LB + 16 * hf + 4 * lg;
-        const bf16x4_t v4 = *reinterpret_cast<const bf16x4_t *>(sV + o);
-        f32x4 x, y;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          x[i] = (float)v4[i] - gx * kh[hf][i];
-          y[i] = mo[hf][i] + fx * kd[hf][i];
-        }
-        put4(sXh + o, sXl + o, x);
-        put4(sGh + o, sGl + o, y);
+      for (int i = 0; i < 4; ++i) {
+        x[i] = (float)v4[i] - gx * kh[i];
+        y[i] = mo[i] + fx * kd[i];
       }
+      split4(sXh + xo, sXl + xo, x);
+      split4(sGh + xo, sGl + xo, y);
     }
     sync_lds();
     // U = A~ X, dX = A~^T dU (= dV)
     {
-      f32x4 u[2] = {zero4(), zero4()}, dx[2] = {zero4(), zero4()};
+      f32x4 u = zero4(), dx = zero4();
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
-        const bf16x8_t ah = frag_row(sAh, LT, 16 * w + lr, 32 * s), al = frag_row(sAl, LT, 16 * w + lr, 32 * s);
-        const bf16x8_t th = frag_col(sAh, LT, 32 * s, 16 * w), tl = frag_col(sAl, LT, 32 * s, 16 * w);
-#pragma unroll
-        for (int hf = 0; hf < 2; ++hf) {
-          u[hf] = mfma3(frag_col(sXh, LB, 32 * s, 16 * hf), frag_col(sXl, LB, 32 * s, 16 * hf), ah, al, u[hf]);
-          dx[hf] = mfma3(frag_col(sGh, LB, 32 * s, 16 * hf), frag_col(sGl, LB, 32 * s, 16 * hf), th, tl, dx[hf]);
-        }
+        u = mfma3(frag_col(sXh, LB, 32 * s, 16 * hc), frag_col(sXl, LB, 32 * s, 16 * hc),
+                  frag_row(sAh, LT, xr, 32 * s), frag_row(sAl, LT, xr, 32 * s), u);
+        dx = mfma3(frag_col(sGh, LB, 32 * s, 16 * hc), frag_col(sGl, LB, 32 * s, 16 * hc),
+                   frag_col(sAh, LT, 32 * s, 16 * rt), frag_col(sAl, LT, 32 * s, 16 * rt), dx);
       }
-#pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const int o = xr * LB + 16 * hf + 4 * lg;
-        put4(sUh + o, sUl + o, u[hf]);
-        put4(sEh + o, sEl + o, dx[hf]);
-        if (xr < C)
-          *reinterpret_cast<f32x4 *>(p.dv + ((size_t)(r0 + xr) * H + h) * DV + NB * cb + 16 * hf + 4 * lg) =
-              dx[hf];
-      }
+      split4(sUh + xo, sUl + xo, u);
+      split4(sEh + xo, sEl + xo, dx);
+      if (xr < C)
+        *reinterpret_cast<f32x4 *>(p.dv + ((size_t)(r0 + xr) * H + h) * DV + NB * cb + 16 * hc + 4 * lg) = dx;
     }
     sync_lds();
     // contracted over this block's columns
     {
-      const int ar = 16 * w + lr;
-      const bf16x8_t oh = frag_row(sOh, LB, ar, 0), ol = frag_row(sOl, LB, ar, 0);
-      const bf16x8_t eh = frag_row(sEh, LB, ar, 0), el = frag_row(sEl, LB, ar, 0);
-      const bf16x8_t uh = frag_row(sUh, LB, ar, 0), ul = frag_row(sUl, LB, ar, 0);
-      const bf16x8_t gh = frag_row(sGh, LB, ar, 0), gl = frag_row(sGl, LB, ar, 0);
+      const bf16x8_t oh = frag_row(sOh, LB, xr, 0), ol = frag_row(sOl, LB, xr, 0);
+      const bf16x8_t eh = frag_row(sEh, LB, xr, 0), el = frag_row(sEl, LB, xr, 0);
+      const bf16x8_t uh = frag_row(sUh, LB, xr, 0), ul = frag_row(sUl, LB, xr, 0);
+      const bf16x8_t gh = frag_row(sGh, LB, xr, 0), gl = frag_row(sGl, LB, xr, 0);
 #pragma unroll
-      for (int t = 0; t < PT; ++t) {
-        const int br = 16 * t + lr;
+      for (int tp = 0; tp < PW; ++tp) {
+        const int br = 16 * (PW * hc + tp) + lr;
         const bf16x8_t hh = frag_row(sHh, LB, br, 0), hl = frag_row(sHl, LB, br, 0);
-        // transposed (operands swapped): lane (g, n) holds row 16 w + n at
-        // the columns 16 t + 4 g .. +3, as the dq / dk stores want them
-        P1[t] = mfma3(hh, hl, oh, ol, P1[t]);
-        P2[t] = mfma3(hh, hl, eh, el, P2[t]);
-        P3[t] = mfma3(frag_row(sDh, LB, br, 0), frag_row(sDl, LB, br, 0), uh, ul, P3[t]);
+        // transposed: lane (g, n) holds row 16 rt + n at the columns
+        // 16 t + 4 g .. +3, as the dq / dk stores want them
+        P1[tp] = mfma3(hh, hl, oh, ol, P1[tp]);
+        P2[tp] = mfma3(hh, hl, eh, el, P2[tp]);
+        P3[tp] = mfma3(frag_row(sDh, LB, br, 0), frag_row(sDl, LB, br, 0), uh, ul, P3[tp]);
       }
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const int br = 16 * t + lr;
-        dM[t] = mfma3(oh, ol, frag_row(sUh, LB, br, 0), frag_row(sUl, LB, br, 0), dM[t]);
-        dT[t] = mfma3(gh, gl, frag_row(sXh, LB, br, 0), frag_row(sXl, LB, br, 0), dT[t]);
+      for (int tq = 0; tq < 2; ++tq) {
+        const int br = 16 * (2 * hc + tq) + lr;
+        dM[tq] = mfma3(oh, ol, frag_row(sUh, LB, br, 0), frag_row(sUl, LB, br, 0), dM[tq]);
+        dT[tq] = mfma3(gh, gl, frag_row(sXh, LB, br, 0), frag_row(sXl, LB, br, 0), dT[tq]);
       }
     }
   }
 
   // ---- phase 2
-  // M at this lane's tile positions from its halves, still in LDS (the prep
-  // writes no fp32 M or S for bf16 inputs; S is recomputed below)
-  float fa[16], fam[4][4], fmm[4][4], fvec = 0.f;
+  // M at this lane's dM tile positions from its halves, still in LDS
+  float fa[8], fam[2][4], fmm[2][4], fvec = 0.f;
   u32x4 rq[KP];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int tq = 0; tq < 2; ++tq)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int o = (16 * w + 4 * lg + i) * LT + 16 * t + lr;
-      fmm[t][i] = (float)sMh[o] + (float)sMl[o];
+      const int o = (16 * rt + 4 * lg + i) * LT + 16 * (2 * hc + tq) + lr;
+      fmm[tq][i] = (float)sMh[o] + (float)sMl[o];
     }
 #pragma unroll
-  for (int e = 0; e < 16; ++e) fa[e] = img[kPrepA + tid + 256 * e];
+  for (int e = 0; e < 8; ++e) fa[e] = img[kPrepA + tid + 512 * e];
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
+  for (int tq = 0; tq < 2; ++tq)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fam[t][i] = img[kPrepA + (16 * w + 4 * lg + i) * 64 + 16 * t + lr];
+    for (int i = 0; i < 4; ++i)
+      fam[tq][i] = img[kPrepA + (16 * rt + 4 * lg + i) * 64 + 16 * (2 * hc + tq) + lr];
 #pragma unroll
   for (int it = 0; it < KP; ++it) {
-    const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+    const int pc = tid + 512 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
     rq[it] = u32x4{0u, 0u, 0u, 0u};
     if (r < C)
       rq[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.q) +
@@ -1062,40 +1038,38 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
   if (tid < 64) fvec = img[kPrepG + tid];
   else if (tid < 128) fvec = img[kPrepBeta + tid - 64];
   shd = wave_sum(shd);
-  if (l == 0) sh4[w] = shd;
+  if (l == 0) sh8[w] = shd;
   sync_lds();  // every phase-1 LDS read is done
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int r = (tid + 256 * e) >> 6;  // row; the column is the lane
+  for (int e = 0; e < 8; ++e) {
+    const int r = (tid + 512 * e) >> 6;  // row; the column is the lane
     splitb(fa[e], qA1h[r * LT + l], qA1l[r * LT + l]);
   }
   if (tid < 64) sG[tid] = fvec;
   else if (tid < 128) sBeta[tid - 64] = fvec;
   sync_lds();
   // Z = dM * M (gates), dT * A^-1 (beta); dT' = dT diag(beta), dM * E, split,
-  // over the lower triangle of real rows.  dT' and dM * E are stored
-  // transposed: the lane's four rows r0 .. r0 + 3 of column s are one 8-byte
-  // piece of row s there (their readers take frag_col for frag_row).
+  // over the lower triangle of real rows, both stored transposed
   {
     float zr[4] = {0.f, 0.f, 0.f, 0.f};
-    const int r0 = 16 * w + 4 * lg;
-    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sG + r0);
+    const int q0 = 16 * rt + 4 * lg;
+    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sG + q0);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int s = 16 * t + lr, o = s * LT + r0;
+    for (int tq = 0; tq < 2; ++tq) {
+      const int s = 16 * (2 * hc + tq) + lr, o = s * LT + q0;
       const float bs = sBeta[s], gs = sG[s];
       float zc = 0.f, bt = 0.f;
       f32x4 fv, ev;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i;
+        const int r = q0 + i;
         const bool lo = s <= r && r < C;
-        const float z = lo ? dM[t][i] * fmm[t][i] : 0.f;
+        const float z = lo ? dM[tq][i] * fmm[tq][i] : 0.f;
         zr[i] += z;
         zc += z;
-        bt += lo ? dT[t][i] * fam[t][i] : 0.f;
-        fv[i] = lo ? dT[t][i] * bs : 0.f;
-        ev[i] = lo ? dM[t][i] * __expf(g4[i] - gs) : 0.f;
+        bt += lo ? dT[tq][i] * fam[tq][i] : 0.f;
+        fv[i] = lo ? dT[tq][i] * bs : 0.f;
+        ev[i] = lo ? dM[tq][i] * __expf(g4[i] - gs) : 0.f;
       }
       split4(qFh + o, qFl + o, fv);
       split4(qEh + o, qEl + o, ev);
@@ -1104,34 +1078,36 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
       bt += __shfl_xor(bt, 16, 64);
       bt += __shfl_xor(bt, 32, 64);
       if (lg == 0) {
-        colt[0][w][s] = bt;
-        colt[1][w][s] = zc;
+        colt[0][rt][s] = bt;
+        colt[1][rt][s] = zc;
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float v = sum16(zr[i]);
-      if (lr == 0) rowt[0][16 * w + 4 * lg + i] = v;
+      if (lr == 0) rowp[0][hc][q0 + i] = v;
     }
   }
   sync_lds();
   // tmp = dT' A^-T
   {
-    f32x4 t2[4] = {zero4(), zero4(), zero4(), zero4()};
+    f32x4 t2[2] = {zero4(), zero4()};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const bf16x8_t ah = frag_col(qFh, LT, 32 * s, 16 * w), al = frag_col(qFl, LT, 32 * s, 16 * w);
+      const bf16x8_t ah = frag_col(qFh, LT, 32 * s, 16 * rt), al = frag_col(qFl, LT, 32 * s, 16 * rt);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        t2[t] = mfma3(ah, al, frag_row(qA1h, LT, 16 * t + lr, 32 * s), frag_row(qA1l, LT, 16 * t + lr, 32 * s),
-                      t2[t]);
+      for (int tq = 0; tq < 2; ++tq) {
+        const int t = 2 * hc + tq;
+        t2[tq] = mfma3(ah, al, frag_row(qA1h, LT, 16 * t + lr, 32 * s), frag_row(qA1l, LT, 16 * t + lr, 32 * s),
+                       t2[tq]);
+      }
     }
 #pragma unroll
-    for (int t = 0; t < 4; ++t)
+    for (int tq = 0; tq < 2; ++tq)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int o = (16 * w + 4 * lg + i) * LT + 16 * t + lr;
-        splitb(t2[t][i], qTh[o], qTl[o]);
+        const int o = (16 * rt + 4 * lg + i) * LT + 16 * (2 * hc + tq) + lr;
+        splitb(t2[tq][i], qTh[o], qTl[o]);
       }
   }
   sync_lds();
@@ -1139,59 +1115,58 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
   // (gates), F = beta dA E (keys), stored as F^T over dT'^T.  S = K K^T * E
   // is recomputed here: K is exact in bf16 and still in LDS.
   {
-    f32x4 kk[4] = {zero4(), zero4(), zero4(), zero4()};
+    f32x4 kk[2] = {zero4(), zero4()};
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
-      const bf16x8_t a = frag_row(sK, LDK, 16 * w + lr, 32 * s);
+      const bf16x8_t a = frag_row(sK, LDK, 16 * rt + lr, 32 * s);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) kk[t] = mfma_bf(a, frag_row(sK, LDK, 16 * t + lr, 32 * s), kk[t]);
+      for (int tq = 0; tq < 2; ++tq)
+        kk[tq] = mfma_bf(a, frag_row(sK, LDK, 16 * (2 * hc + tq) + lr, 32 * s), kk[tq]);
     }
-    f32x4 t3[4] = {zero4(), zero4(), zero4(), zero4()};
+    f32x4 t3[2] = {zero4(), zero4()};
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const bf16x8_t ah = frag_col(qA1h, LT, 32 * s, 16 * w), al = frag_col(qA1l, LT, 32 * s, 16 * w);
+      const bf16x8_t ah = frag_col(qA1h, LT, 32 * s, 16 * rt), al = frag_col(qA1l, LT, 32 * s, 16 * rt);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        t3[t] = mfma3(ah, al, frag_col(qTh, LT, 32 * s, 16 * t), frag_col(qTl, LT, 32 * s, 16 * t), t3[t]);
+      for (int tq = 0; tq < 2; ++tq) {
+        const int t = 2 * hc + tq;
+        t3[tq] = mfma3(ah, al, frag_col(qTh, LT, 32 * s, 16 * t), frag_col(qTl, LT, 32 * s, 16 * t), t3[tq]);
+      }
     }
-    // F (strict lower) is stored transposed, F[r][s] at [s][r]: the lane's
-    // rows r0 .. r0 + 3 of column s are one 8-byte piece of row s, zero on
-    // and below the diagonal (over dT'^T, which is zero below it already,
-    // so every entry of the array is F^T afterwards)
     float wr[4] = {0.f, 0.f, 0.f, 0.f}, yr[4] = {0.f, 0.f, 0.f, 0.f};
-    const int r0 = 16 * w + 4 * lg;
-    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sG + r0);
-    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(sBeta + r0);
+    const int q0 = 16 * rt + 4 * lg;
+    const f32x4 g4 = *reinterpret_cast<const f32x4 *>(sG + q0);
+    const f32x4 b4 = *reinterpret_cast<const f32x4 *>(sBeta + q0);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int s = 16 * t + lr;
+    for (int tq = 0; tq < 2; ++tq) {
+      const int s = 16 * (2 * hc + tq) + lr;
       const float gs = sG[s];
       float yc = 0.f;
       f32x4 fv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = r0 + i;
+        const int r = q0 + i;
         const bool sl = s < r && r < C;
-        const float dA = -t3[t][i];
+        const float dA = -t3[tq][i];
         const float ex = __expf(g4[i] - gs);
-        const float Wv = sl ? dA * kk[t][i] * ex : 0.f;
+        const float Wv = sl ? dA * kk[tq][i] * ex : 0.f;
         const float Yv = b4[i] * Wv;
         fv[i] = sl ? b4[i] * dA * ex : 0.f;
         wr[i] += Wv;
         yr[i] += Yv;
         yc += Yv;
       }
-      split4(qFh + s * LT + r0, qFl + s * LT + r0, fv);
+      split4(qFh + s * LT + q0, qFl + s * LT + q0, fv);
       yc += __shfl_xor(yc, 16, 64);
       yc += __shfl_xor(yc, 32, 64);
-      if (lg == 0) colt[2][w][s] = yc;
+      if (lg == 0) colt[2][rt][s] = yc;
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const float a = sum16(wr[i]), b = sum16(yr[i]);
       if (lr == 0) {
-        rowt[1][16 * w + 4 * lg + i] = a;
-        rowt[2][16 * w + 4 * lg + i] = b;
+        rowp[1][hc][q0 + i] = a;
+        rowp[2][hc][q0 + i] = b;
       }
     }
   }
@@ -1199,33 +1174,32 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
   // Q over A^-1
 #pragma unroll
   for (int it = 0; it < KP; ++it) {
-    const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+    const int pc = tid + 512 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
     *reinterpret_cast<u32x4 *>(sQ + r * LDK + c) = rq[it];
   }
   sync_lds();
   // dQ = gam P1 + (dM E) K;  dK = -gam P2 + fac P3 + (dM E)^T Q + F K + F^T K,
-  // and the gate dots <q_r, P1_r>, <k_r, P2_r>, <k_r, P3_r>
+  // and the gate dots <q_r, P1_r>, <k_r, P2_r>, <k_r, P3_r>, over this
+  // wave's column half
   {
     bf16x8_t aE[2][2], aET[2][2], aF[2][2], aFT[2][2];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      aE[s][0] = frag_col(qEh, LT, 32 * s, 16 * w);  // E is stored transposed
-      aE[s][1] = frag_col(qEl, LT, 32 * s, 16 * w);
-      aET[s][0] = frag_row(qEh, LT, 16 * w + lr, 32 * s);
-      aET[s][1] = frag_row(qEl, LT, 16 * w + lr, 32 * s);
-      aF[s][0] = frag_col(qFh, LT, 32 * s, 16 * w);  // F^T is stored
-      aF[s][1] = frag_col(qFl, LT, 32 * s, 16 * w);
-      aFT[s][0] = frag_row(qFh, LT, 16 * w + lr, 32 * s);
-      aFT[s][1] = frag_row(qFl, LT, 16 * w + lr, 32 * s);
+      aE[s][0] = frag_col(qEh, LT, 32 * s, 16 * rt);  // E is stored transposed
+      aE[s][1] = frag_col(qEl, LT, 32 * s, 16 * rt);
+      aET[s][0] = frag_row(qEh, LT, 16 * rt + lr, 32 * s);
+      aET[s][1] = frag_row(qEl, LT, 16 * rt + lr, 32 * s);
+      aF[s][0] = frag_col(qFh, LT, 32 * s, 16 * rt);  // F^T is stored
+      aF[s][1] = frag_col(qFl, LT, 32 * s, 16 * rt);
+      aFT[s][0] = frag_row(qFh, LT, 16 * rt + lr, 32 * s);
+      aFT[s][1] = frag_row(qFl, LT, 16 * rt + lr, 32 * s);
     }
-    // every tile transposed (K^T and Q^T as A operands): lane (g, n) holds
-    // row rr = 16 w + n at the columns 16 t + 4 g .. +3, so the dq / dk rows
-    // go out as 16-byte stores and the gate dots read 8 bytes of q / k
-    const int rr = 16 * w + lr;
+    const int rr = 16 * rt + lr;
     const float gr = sGam[rr], fr = sFac[rr];
     float q1 = 0.f, k2 = 0.f, k3 = 0.f;
 #pragma unroll
-    for (int t = 0; t < PT; ++t) {
+    for (int tp = 0; tp < PW; ++tp) {
+      const int t = PW * hc + tp;
       f32x4 dq = zero4(), dk = zero4();
 #pragma unroll
       for (int s = 0; s < 2; ++s) {
@@ -1245,11 +1219,11 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
       f32x4 oq, ok;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        q1 += (float)q4[i] * P1[t][i];
-        k2 += (float)k4[i] * P2[t][i];
-        k3 += (float)k4[i] * P3[t][i];
-        oq[i] = gr * P1[t][i] + dq[i];
-        ok[i] = -gr * P2[t][i] + fr * P3[t][i] + dk[i];
+        q1 += (float)q4[i] * P1[tp][i];
+        k2 += (float)k4[i] * P2[tp][i];
+        k3 += (float)k4[i] * P3[tp][i];
+        oq[i] = gr * P1[tp][i] + dq[i];
+        ok[i] = -gr * P2[tp][i] + fr * P3[tp][i] + dk[i];
       }
       if (rr < C) {
         const size_t o = ((size_t)(r0 + rr) * H + h) * DK + c0;
@@ -1257,7 +1231,6 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
         *reinterpret_cast<f32x4 *>(p.dk + o) = ok;
       }
     }
-    // the row's sums over its four lane groups
 #pragma unroll
     for (int m = 16; m < 64; m <<= 1) {
       q1 += __shfl_xor(q1, m, 64);
@@ -1265,9 +1238,9 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
       k3 += __shfl_xor(k3, m, 64);
     }
     if (lg == 0) {
-      rowt[3][rr] = q1;
-      rowt[4][rr] = k2;
-      rowt[5][rr] = k3;
+      rowp[3][hc][rr] = q1;
+      rowp[4][hc][rr] = k2;
+      rowp[5][hc][rr] = k3;
     }
   }
   sync_lds();
@@ -1276,13 +1249,17 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
     // column sums of Z and Y; dG_{C-1} also takes sum_r fac_r <k_r, P3_r> and
     // gam_{C-1} <dH', H>; dg_t = sum_{r >= t} dG_r; dbeta = the two beta sums
     const int r = l;
+    float rs[6];
+#pragma unroll
+    for (int k = 0; k < 6; ++k) rs[k] = rowp[k][0][r] + rowp[k][1][r];
     float cl[3];
 #pragma unroll
     for (int k = 0; k < 3; ++k) cl[k] = colt[k][0][r] + colt[k][1][r] + colt[k][2][r] + colt[k][3][r];
-    const float t3 = r < C ? sFac[r] * rowt[5][r] : 0.f;
-    const float dGr =
-        r < C ? sGam[r] * (rowt[3][r] - rowt[4][r]) - t3 + rowt[0][r] - cl[1] + rowt[2][r] - cl[2] : 0.f;
-    const float shs = sh4[0] + sh4[1] + sh4[2] + sh4[3];
+    const float t3 = r < C ? sFac[r] * rs[5] : 0.f;
+    const float dGr = r < C ? sGam[r] * (rs[3] - rs[4]) - t3 + rs[0] - cl[1] + rs[2] - cl[2] : 0.f;
+    float shs = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) shs += sh8[k];
     const float extra = wave_sum(t3) + sGam[C - 1] * shs;
     const float x = dGr + (r == C - 1 ? extra : 0.f);
     const float incl = wave_inclusive_scan(x);
@@ -1290,7 +1267,7 @@ __global__ __launch_bounds__(256) void bwd_cell_bf16_kernel(BwdParams p) {
     if (r < C) {
       const size_t o = (size_t)(r0 + r) * H + h;
       p.dg[o] = suffix;
-      p.dbeta[o] = cl[0] + rowt[1][r];
+      p.dbeta[o] = cl[0] + rs[1];
     }
   }
 }
@@ -1314,7 +1291,7 @@ hipError_t launch_all(const BwdParams &p, int stage, hipStream_t st) {
   }
   // the per-chunk stage: needs the recomputed states and the reverse pass
   if constexpr (std::is_same_v<In, bf16>) {
-    hipLaunchKernelGGL((bwd_cell_bf16_kernel<DK>), dim3(cells), dim3(256), 0, st, p);
+    hipLaunchKernelGGL((bwd_cell8_bf16_kernel<DK>), dim3(cells), dim3(512), 0, st, p);
   } else {
     hipLaunchKernelGGL((bwd_part_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
