@@ -208,12 +208,23 @@ __device__ __forceinline__ int seq_by_rank(const int32_t *co, int N_max, int ran
 // forward substitution (wave 0, one lane per column), then the blocks below
 // the diagonal as X_ij = -X_ii sum_{k=j}^{i-1} L_ik X_kj on fp32 MFMA, one
 // block per wave and diagonal distance; the sum waits in the upper block
-// (j, i) of sX, which X never uses.
+// (j, i) of sX, which X never uses.  With `zeroed` the caller has already
+// cleared sX (zero_mat64) before a barrier.
+// sX = 0, four consecutive entries per thread and step (256 threads)
+__device__ __forceinline__ void zero_mat64(float *sX) {
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = 4 * threadIdx.x + 1024 * it;
+    *reinterpret_cast<f32x4 *>(sX + (idx >> 6) * kL + (idx & 63)) = zero4();
+  }
+}
 __device__ __forceinline__ void unit_lower_inverse(const float *sS, const float *sB, float *sX,
-                                                   int C) {
+                                                   int C, bool zeroed = false) {
   const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
-  for (int idx = tid; idx < 4096; idx += 256) sX[(idx >> 6) * kL + (idx & 63)] = 0.f;
-  __syncthreads();
+  if (!zeroed) {
+    zero_mat64(sX);
+    __syncthreads();
+  }
   if (w == 0) {
     const int blk = l >> 4, c = l & 15;
     float xd[16];
@@ -256,10 +267,17 @@ __device__ __forceinline__ void unit_lower_inverse(const float *sS, const float 
     }
     __syncthreads();
   }
-  // clear the scratch blocks and the rows / columns past the chunk
-  for (int idx = tid; idx < 4096; idx += 256) {
-    const int r = idx >> 6, c = idx & 63;
-    if (c > r || r >= C || c >= C) sX[r * kL + c] = 0.f;
+  // clear the scratch blocks and the rows / columns past the chunk, four
+  // consecutive entries per thread and step
+#pragma unroll
+  for (int it = 0; it < 4; ++it) {
+    const int idx = 4 * tid + 1024 * it, r = idx >> 6, c = idx & 63;
+    f32x4 *px = reinterpret_cast<f32x4 *>(sX + r * kL + c);
+    f32x4 v = *px;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (c + e > r || r >= C || c + e >= C) v[e] = 0.f;
+    *px = v;
   }
   __syncthreads();
 }

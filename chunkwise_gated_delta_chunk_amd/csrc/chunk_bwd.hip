@@ -104,17 +104,24 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_bf16_kernel(BwdParams p) {
   if (!chunk_of(p, slot, ch)) return;
   const int C = ch.C;
   const int tid = threadIdx.x, hq = h / (H / p.Hqk);
+  // all K, Q loads first; the inverse's scratch is cleared while they travel
+  u32x4 kv[KP], qv[KP];
 #pragma unroll
   for (int it = 0; it < KP; ++it) {
     const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
-    u32x4 kv = u32x4{0u, 0u, 0u, 0u}, qv = kv;
+    kv[it] = qv[it] = u32x4{0u, 0u, 0u, 0u};
     if (r < C) {
       const size_t off = ((size_t)(ch.r0 + r) * p.Hqk + hq) * DK + c;
-      kv = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.k) + off);
-      qv = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.q) + off);
+      kv[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.k) + off);
+      qv[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.q) + off);
     }
-    *reinterpret_cast<u32x4 *>(sK + r * LDK + c) = kv;
-    *reinterpret_cast<u32x4 *>(sQ + r * LDK + c) = qv;
+  }
+  zero_mat64(sX);
+#pragma unroll
+  for (int it = 0; it < KP; ++it) {
+    const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+    *reinterpret_cast<u32x4 *>(sK + r * LDK + c) = kv[it];
+    *reinterpret_cast<u32x4 *>(sQ + r * LDK + c) = qv[it];
   }
   if (tid < 64) {
     const float gr = tid < C ? p.g[(size_t)(ch.r0 + tid) * H + h] : 0.f;
@@ -167,7 +174,7 @@ __global__ __launch_bounds__(256, 2) void bwd_prep_bf16_kernel(BwdParams p) {
   __syncthreads();
   // A^-1 = (I + diag(beta) S)^-1, by 16x16 blocks; stored with its
   // A^-1 diag(beta) halves, four consecutive entries per thread
-  unit_lower_inverse(sS, sB, sX, C);
+  unit_lower_inverse(sS, sB, sX, C, true);  // sX cleared at the start
 #pragma unroll
   for (int it = 0; it < 4; ++it) {
     const int idx = 4 * tid + 1024 * it, r = idx >> 6, c = idx & 63;
