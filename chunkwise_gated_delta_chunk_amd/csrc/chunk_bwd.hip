@@ -91,112 +91,133 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(BwdParams p) {
 }
 
 // The same for bf16 inputs: K and Q stay bf16 in LDS (exact) and S, M run
-// on bf16 MFMA with fp32 accumulation, one product per k-step.
+// on bf16 MFMA with fp32 accumulation, one product per k-step.  Persistent:
+// a workgroup walks cells with a stride of the grid (two per CU), and the
+// next cell's K, Q, g and beta rows are loaded into registers as soon as
+// the current ones are staged, so their latency passes under this cell's
+// products and inverse.
 template <int DK>
 __global__ __launch_bounds__(256, 2) void bwd_prep_bf16_kernel(BwdParams p) {
   constexpr int LDK = DK + 16, KP = 64 * DK / 8 / 256;
   __shared__ __attribute__((aligned(16))) __bf16 sK[64 * LDK], sQ[64 * LDK];
   __shared__ __attribute__((aligned(16))) float sS[64 * kL], sX[64 * kL];
   __shared__ __attribute__((aligned(16))) float sG[64], sB[64];
-  const int H = p.H;
-  const int slot = blockIdx.x / H, h = blockIdx.x % H;
-  Chunk ch;
-  if (!chunk_of(p, slot, ch)) return;
-  const int C = ch.C;
-  const int tid = threadIdx.x, hq = h / (H / p.Hqk);
-  // all K, Q loads first; the inverse's scratch is cleared while they travel
+  const int H = p.H, ncell = p.NT * H;
+  const int tid = threadIdx.x, w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
   u32x4 kv[KP], qv[KP];
+  float gv = 0.f, bv = 0.f;
+  auto load = [&](int cell, const Chunk &c) {
+    const int h = cell % H, hq = h / (H / p.Hqk);
 #pragma unroll
-  for (int it = 0; it < KP; ++it) {
-    const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
-    kv[it] = qv[it] = u32x4{0u, 0u, 0u, 0u};
-    if (r < C) {
-      const size_t off = ((size_t)(ch.r0 + r) * p.Hqk + hq) * DK + c;
-      kv[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.k) + off);
-      qv[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.q) + off);
-    }
-  }
-  zero_mat64(sX);
-#pragma unroll
-  for (int it = 0; it < KP; ++it) {
-    const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
-    *reinterpret_cast<u32x4 *>(sK + r * LDK + c) = kv[it];
-    *reinterpret_cast<u32x4 *>(sQ + r * LDK + c) = qv[it];
-  }
-  if (tid < 64) {
-    const float gr = tid < C ? p.g[(size_t)(ch.r0 + tid) * H + h] : 0.f;
-    sG[tid] = wave_inclusive_scan(gr);  // rows >= C repeat G_{C-1}
-    sB[tid] = tid < C ? p.beta[(size_t)(ch.r0 + tid) * H + h] : 0.f;
-  }
-  __syncthreads();
-  float *img = p.prep + (size_t)blockIdx.x * kPrepFloats;
-  __bf16 *imh = reinterpret_cast<__bf16 *>(img + kPrepH);
-  const int w = tid >> 6, l = lane_id(), lr = l & 15, lg = l >> 4;
-  // S = strict_lower(K K^T * E), M = lower_incl(Q K^T * E): wave w, rows
-  // 16w, formed transposed (operands swapped) so that lane (g, n) holds row
-  // 16 w + n at the columns 16 s4 + 4 g .. +3: S goes to LDS and M's bf16
-  // halves to the image in 16- and 8-byte pieces
-  f32x4 aS[4] = {zero4(), zero4(), zero4(), zero4()};
-  f32x4 aM[4] = {zero4(), zero4(), zero4(), zero4()};
-#pragma unroll
-  for (int s = 0; s < DK / 32; ++s) {
-    const bf16x8_t ak = frag_row(sK, LDK, 16 * w + lr, 32 * s), aq = frag_row(sQ, LDK, 16 * w + lr, 32 * s);
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const bf16x8_t b = frag_row(sK, LDK, 16 * s4 + lr, 32 * s);
-      aS[s4] = mfma_bf(b, ak, aS[s4]);
-      aM[s4] = mfma_bf(b, aq, aM[s4]);
-    }
-  }
-  {
-    const int r = 16 * w + lr;
-    const float gr = sG[r];
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      const int s0 = 16 * s4 + 4 * lg;
-      const f32x4 gs = *reinterpret_cast<const f32x4 *>(sG + s0);
-      f32x4 sv;
-      bf16x4_t mh, ml;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = s0 + i;
-        const float e = (r < C && s <= r) ? __expf(gr - gs[i]) : 0.f;
-        sv[i] = s < r ? aS[s4][i] * e : 0.f;
-        const float mv = aM[s4][i] * e;  // (no fp32 S, M: see the fused kernel)
-        mh[i] = (__bf16)mv;
-        ml[i] = (__bf16)(mv - (float)mh[i]);
+    for (int it = 0; it < KP; ++it) {
+      const int pc = tid + 256 * it, r = pc / (DK / 8), cc = (pc % (DK / 8)) * 8;
+      kv[it] = qv[it] = u32x4{0u, 0u, 0u, 0u};
+      if (r < c.C) {
+        const size_t off = ((size_t)(c.r0 + r) * p.Hqk + hq) * DK + cc;
+        kv[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.k) + off);
+        qv[it] = *reinterpret_cast<const u32x4 *>(static_cast<const bf16 *>(p.q) + off);
       }
-      *reinterpret_cast<f32x4 *>(sS + r * kL + s0) = sv;
-      *reinterpret_cast<bf16x4_t *>(imh + r * 64 + s0) = mh;
-      *reinterpret_cast<bf16x4_t *>(imh + 4096 + r * 64 + s0) = ml;
     }
-  }
-  __syncthreads();
-  // A^-1 = (I + diag(beta) S)^-1, by 16x16 blocks; stored with its
-  // A^-1 diag(beta) halves, four consecutive entries per thread
-  unit_lower_inverse(sS, sB, sX, C, true);  // sX cleared at the start
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int idx = 4 * tid + 1024 * it, r = idx >> 6, c = idx & 63;
-    const f32x4 a = *reinterpret_cast<const f32x4 *>(sX + r * kL + c);
-    const f32x4 b = *reinterpret_cast<const f32x4 *>(sB + c);
-    bf16x4_t ah, al;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float x = a[e] * b[e];
-      ah[e] = (__bf16)x;
-      al[e] = (__bf16)(x - (float)ah[e]);
+    if (tid < 64) {
+      gv = tid < c.C ? p.g[(size_t)(c.r0 + tid) * H + h] : 0.f;
+      bv = tid < c.C ? p.beta[(size_t)(c.r0 + tid) * H + h] : 0.f;
     }
-    *reinterpret_cast<f32x4 *>(img + kPrepA + idx) = a;
-    *reinterpret_cast<bf16x4_t *>(imh + 8192 + idx) = ah;
-    *reinterpret_cast<bf16x4_t *>(imh + 12288 + idx) = al;
-  }
-  if (tid < 64) {
-    const float Gc = sG[C - 1];
-    img[kPrepG + tid] = sG[tid];
-    img[kPrepGam + tid] = tid < C ? __expf(sG[tid]) : 0.f;
-    img[kPrepFac + tid] = tid < C ? __expf(Gc - sG[tid]) : 0.f;
-    img[kPrepBeta + tid] = sB[tid];
+  };
+  int cell = blockIdx.x;
+  Chunk ch;
+  // sentinel slots come last: the first one ends the walk
+  if (cell >= ncell || !chunk_of(p, cell / H, ch)) return;
+  load(cell, ch);
+  for (;;) {
+    const int h = cell % H, C = ch.C;
+    zero_mat64(sX);  // the inverse's scratch
+#pragma unroll
+    for (int it = 0; it < KP; ++it) {
+      const int pc = tid + 256 * it, r = pc / (DK / 8), c = (pc % (DK / 8)) * 8;
+      *reinterpret_cast<u32x4 *>(sK + r * LDK + c) = kv[it];
+      *reinterpret_cast<u32x4 *>(sQ + r * LDK + c) = qv[it];
+    }
+    if (tid < 64) {
+      sG[tid] = wave_inclusive_scan(gv);  // rows >= C repeat G_{C-1}
+      sB[tid] = bv;
+    }
+    __syncthreads();
+    const int next = cell + gridDim.x;
+    Chunk nch;
+    const bool more = next < ncell && chunk_of(p, next / H, nch);
+    if (more) load(next, nch);
+    float *img = p.prep + (size_t)cell * kPrepFloats;
+    __bf16 *imh = reinterpret_cast<__bf16 *>(img + kPrepH);
+    // S = strict_lower(K K^T * E), M = lower_incl(Q K^T * E): wave w, rows
+    // 16w, formed transposed (operands swapped) so that lane (g, n) holds row
+    // 16 w + n at the columns 16 s4 + 4 g .. +3: S goes to LDS and M's bf16
+    // halves to the image in 16- and 8-byte pieces
+    f32x4 aS[4] = {zero4(), zero4(), zero4(), zero4()};
+    f32x4 aM[4] = {zero4(), zero4(), zero4(), zero4()};
+#pragma unroll
+    for (int s = 0; s < DK / 32; ++s) {
+      const bf16x8_t ak = frag_row(sK, LDK, 16 * w + lr, 32 * s), aq = frag_row(sQ, LDK, 16 * w + lr, 32 * s);
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const bf16x8_t b = frag_row(sK, LDK, 16 * s4 + lr, 32 * s);
+        aS[s4] = mfma_bf(b, ak, aS[s4]);
+        aM[s4] = mfma_bf(b, aq, aM[s4]);
+      }
+    }
+    {
+      const int r = 16 * w + lr;
+      const float gr = sG[r];
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        const int s0 = 16 * s4 + 4 * lg;
+        const f32x4 gs = *reinterpret_cast<const f32x4 *>(sG + s0);
+        f32x4 sv;
+        bf16x4_t mh, ml;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = s0 + i;
+          const float e = (r < C && s <= r) ? __expf(gr - gs[i]) : 0.f;
+          sv[i] = s < r ? aS[s4][i] * e : 0.f;
+          const float mv = aM[s4][i] * e;  // (no fp32 S, M: see the fused kernel)
+          mh[i] = (__bf16)mv;
+          ml[i] = (__bf16)(mv - (float)mh[i]);
+        }
+        *reinterpret_cast<f32x4 *>(sS + r * kL + s0) = sv;
+        *reinterpret_cast<bf16x4_t *>(imh + r * 64 + s0) = mh;
+        *reinterpret_cast<bf16x4_t *>(imh + 4096 + r * 64 + s0) = ml;
+      }
+    }
+    __syncthreads();
+    // A^-1 = (I + diag(beta) S)^-1, by 16x16 blocks; stored with its
+    // A^-1 diag(beta) halves, four consecutive entries per thread
+    unit_lower_inverse(sS, sB, sX, C, true);  // sX cleared at the start
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = 4 * tid + 1024 * it, r = idx >> 6, c = idx & 63;
+      const f32x4 a = *reinterpret_cast<const f32x4 *>(sX + r * kL + c);
+      const f32x4 b = *reinterpret_cast<const f32x4 *>(sB + c);
+      bf16x4_t ah, al;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = a[e] * b[e];
+        ah[e] = (__bf16)x;
+        al[e] = (__bf16)(x - (float)ah[e]);
+      }
+      *reinterpret_cast<f32x4 *>(img + kPrepA + idx) = a;
+      *reinterpret_cast<bf16x4_t *>(imh + 8192 + idx) = ah;
+      *reinterpret_cast<bf16x4_t *>(imh + 12288 + idx) = al;
+    }
+    if (tid < 64) {
+      const float Gc = sG[C - 1];
+      img[kPrepG + tid] = sG[tid];
+      img[kPrepGam + tid] = tid < C ? __expf(sG[tid]) : 0.f;
+      img[kPrepFac + tid] = tid < C ? __expf(Gc - sG[tid]) : 0.f;
+      img[kPrepBeta + tid] = sB[tid];
+    }
+    if (!more) break;
+    __syncthreads();  // this cell's LDS reads are done before the next staging
+    cell = next;
+    ch = nch;
   }
 }
 
@@ -1279,12 +1300,32 @@ __global__ __launch_bounds__(512) void bwd_cell8_bf16_kernel(BwdParams p) {
   }
 }
 
+// the persistent bf16 prep's grid: the workgroups the device holds at once
+// (found once per device), capped by the cells
+template <int DK>
+int prep_grid(int cells) {
+  static int slots[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return cells;
+  int res = dev < 64 ? slots[dev] : 0;
+  if (res == 0) {
+    int cus = 0, per = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, bwd_prep_bf16_kernel<DK>, 256, 0) != hipSuccess ||
+        cus * per <= 0)
+      return cells;
+    res = cus * per;
+    if (dev < 64) slots[dev] = res;
+  }
+  return cells < res ? cells : res;
+}
+
 template <typename In, int DK>
 hipError_t launch_all(const BwdParams &p, int stage, hipStream_t st) {
   const int cells = p.NT * p.H;
   if (stage == 1) {  // prep: needs no forward recompute
     if constexpr (std::is_same_v<In, bf16>)
-      hipLaunchKernelGGL((bwd_prep_bf16_kernel<DK>), dim3(cells), dim3(256), 0, st, p);
+      hipLaunchKernelGGL((bwd_prep_bf16_kernel<DK>), dim3(prep_grid<DK>(cells)), dim3(256), 0, st, p);
     else
       hipLaunchKernelGGL((bwd_prep_kernel<In, DK>), dim3(cells), dim3(256), 0, st, p);
     return hipGetLastError();
