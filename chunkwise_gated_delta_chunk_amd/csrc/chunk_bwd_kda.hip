@@ -121,22 +121,62 @@ __global__ __launch_bounds__(256) void kda_prep_kernel(BwdParams p) {
       imh[4096 + r * 64 + s] = (__bf16)(am - (float)mh);
     }
   };
-  for (int pr = tid; pr < 4096; pr += 256) {  // zero everything above the diagonal blocks
-    const int r = pr >> 6, s = pr & 63;
-    if ((s >> 4) > (r >> 4)) put(r, s, 0.f, 0.f);
-  }
-  for (int pr = tid; pr < 4 * 256; pr += 256) {
-    const int blk = pr >> 8, r = 16 * blk + ((pr >> 4) & 15), s = 16 * blk + (pr & 15);
-    float as = 0.f, am = 0.f;
-    if (r < C && s <= r) {
-#pragma unroll 8
-      for (int i = 0; i < DK; ++i) {
-        const float e = __expf(sG[r * LK + i] - sG[s * LK + i]) * sK[s * LK + i];
-        as += sK[r * LK + i] * e;
-        am += sQ[r * LK + i] * e;
+  // zero everything above the diagonal blocks, four entries per item
+  for (int it = tid; it < 64 * 16; it += 256) {
+    const int r = it >> 4, c0 = (it & 15) * 4;
+    if ((c0 >> 4) > (r >> 4)) {
+      *reinterpret_cast<f32x4 *>(sS + r * kL + c0) = zero4();
+      *reinterpret_cast<f32x4 *>(img + kPrepS + r * 64 + c0) = zero4();
+      *reinterpret_cast<f32x4 *>(img + kPrepM + r * 64 + c0) = zero4();
+      if constexpr (std::is_same_v<In, bf16>) {
+        const bf16x4_t z = {(__bf16)0.f, (__bf16)0.f, (__bf16)0.f, (__bf16)0.f};
+        *reinterpret_cast<bf16x4_t *>(imh + r * 64 + c0) = z;
+        *reinterpret_cast<bf16x4_t *>(imh + 4096 + r * 64 + c0) = z;
       }
     }
-    put(r, s, as, am);
+  }
+  {
+    const int w = tid >> 6, l = lane_id(), j = l & 15, g = l >> 4;
+    // The diagonal block of wave w, factored through its first row b:
+    // e^{G_r - G_s} = e^{G_r - G_b} e^{G_b - G_s}, the first factor <= 1 and
+    // the second >= 1, exact in fp32 while G_b - G_s <= 60 in every channel
+    // (G decreases down the rows, so the block's last row bounds it).
+    // Otherwise the block is summed pair by pair.
+    const int b = 16 * w, ra = b + j;  // this lane's A row and B column
+    bool fits = true;
+    for (int i = l; i < DK; i += 64) fits &= sG[b * LK + i] - sG[(b + 15) * LK + i] <= 60.f;
+    if (__ballot(!fits) == 0) {
+      f32x4 aS = zero4(), aM = zero4();
+#pragma unroll 4
+      for (int i0 = 0; i0 < DK; i0 += 4) {
+        const int i = i0 + g;
+        const float gb = sG[b * LK + i], gr = sG[ra * LK + i];
+        const float kr = sK[ra * LK + i];
+        const float bk = kr * __expf(gb - gr), er = __expf(gr - gb);
+        aS = mfma4(kr * er, bk, aS);
+        aM = mfma4(sQ[ra * LK + i] * er, bk, aM);
+      }
+#pragma unroll
+      for (int ii = 0; ii < 4; ++ii) {
+        const int r = b + 4 * g + ii, s = b + j;
+        const bool ok = r < C && s <= r;
+        put(r, s, ok ? aS[ii] : 0.f, ok ? aM[ii] : 0.f);
+      }
+    } else {
+      for (int pr = l; pr < 256; pr += 64) {
+        const int r = b + (pr >> 4), s = b + (pr & 15);
+        float as = 0.f, am = 0.f;
+        if (r < C && s <= r) {
+#pragma unroll 8
+          for (int i = 0; i < DK; ++i) {
+            const float e = __expf(sG[r * LK + i] - sG[s * LK + i]) * sK[s * LK + i];
+            as += sK[r * LK + i] * e;
+            am += sQ[r * LK + i] * e;
+          }
+        }
+        put(r, s, as, am);
+      }
+    }
   }
   {
     const int w = tid >> 6, l = lane_id(), j = l & 15, g = l >> 4;
