@@ -768,6 +768,7 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
   constexpr int AREA = KQG > 4 * MAT ? KQG : 4 * MAT;
   __shared__ __attribute__((aligned(16))) float smem[AREA + 2 * MAT];
   __shared__ __attribute__((aligned(16))) float sBeta[64], bt[64], ba[64], sEx[256], sTot[256];
+  __shared__ int sFit[4];  // row block X's in-block decays run on MFMA (see below)
   float *sK = smem, *sQ = smem + kBT * LK, *sG = smem + 2 * kBT * LK;
   float *sDM = smem + AREA, *sDS = smem + AREA + MAT;
   float *sA = smem, *sS = smem + MAT, *sTmp = smem + 2 * MAT, *sDAi = smem + 3 * MAT;
@@ -844,6 +845,18 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
   load_rows<In, DK>(sQ, LK, p.q, r0, C, p.Hqk, h / (H / p.Hqk));
   load_block<64, DK>(sG, LK, img + kKdaG, DK);
   __syncthreads();
+  // Row block X's terms inside the block factor through its first row b0
+  // (e^{G_x - G_s} = e^{G_x - G_b0} e^{G_b0 - G_s}, one factor <= 1, the other
+  // >= 1) and run on MFMA with the cross-block terms, when G_b0 - G_s <= 60
+  // in every channel (G decreases down the rows, so the block's last row
+  // bounds it); otherwise the (row, channel) pass sums them pair by pair.
+  {
+    bool fits = true;
+    for (int i = l; i < DK; i += 64) fits &= sG[16 * w * LK + i] - sG[(16 * w + 15) * LK + i] <= 60.f;
+    const bool all = __ballot(!fits) == 0;
+    if (l == 0) sFit[w] = all;
+  }
+  __syncthreads();
   if (tid < C) {
     const size_t o = (size_t)(r0 + tid) * H + h;
     p.dbeta[o] = bt[tid] + ba[tid];
@@ -864,10 +877,12 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
     const float Gx = sG[x * LK + i], qx = sQ[x * LK + i], kx = sK[x * LK + i];
     const float GCi = sG[(C - 1) * LK + i];
     float f1 = 0.f, f2 = 0.f, f3 = 0.f, f4 = 0.f;
-    // the terms inside x's 16-row block (the other blocks follow on MFMA)
-    const int xb = x & ~15, xe = min(C, xb + 16);
+    // the terms inside x's 16-row block, unless they run on MFMA below (the
+    // other blocks follow on MFMA)
+    const bool mf = sFit[x >> 4] != 0;
+    const int xb = x & ~15, xs = mf ? xb - 1 : x, xe = mf ? xb : min(C, xb + 16);
 #pragma unroll 4
-    for (int s = xb; s <= x; ++s) {  // E_xs = exp(G_x - G_s), s <= x
+    for (int s = xb; s <= xs; ++s) {  // E_xs = exp(G_x - G_s), s <= x
       const float e = __expf(Gx - sG[s * LK + i]) * sK[s * LK + i];
       f1 += sDM[x * kL + s] * e;
       f3 += sDS[x * kL + s] * e;
@@ -918,6 +933,41 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
         }
       }
     }
+    // the block's own terms on MFMA (rows and columns inside block X):
+    // F1/F3 += exp(G_x - G_b0) (dM|dS)[X,X] Kb0_X with Kb0 = K exp(G_b0 - G);
+    // F24d = exp(G_b0 - G_x) (dM[X,X]^T Qc + dS[X,X]^T Kc) with
+    // Qc, Kc = (Q, K) exp(G - G_b0)
+    f32x4 F24d[DK / 16];
+    const bool mfx = sFit[X] != 0;
+#pragma unroll
+    for (int t = 0; t < DK / 16; ++t) F24d[t] = zero4();
+    if (mfx) {
+      const int b0 = 16 * X, am = b0 + j;
+#pragma unroll
+      for (int t = 0; t < DK / 16; ++t) {
+        const int i = 16 * t + j;
+        const float gb = sG[b0 * LK + i];
+        f32x4 z1 = zero4(), z3 = zero4(), zd = zero4();
+#pragma unroll
+        for (int k0 = 0; k0 < 16; k0 += 4) {
+          const int s = b0 + k0 + g;  // k index of this lane (a row of block X)
+          const float gs = sG[s * LK + i], ks = sK[s * LK + i];
+          const float bv = ks * __expf(gb - gs), e = __expf(gs - gb);
+          z1 = mfma4(sDM[am * kL + s], bv, z1);
+          z3 = mfma4(sDS[am * kL + s], bv, z3);
+          zd = mfma4(sDM[s * kL + am], sQ[s * LK + i] * e, zd);
+          zd = mfma4(sDS[s * kL + am], ks * e, zd);
+        }
+#pragma unroll
+        for (int ii = 0; ii < 4; ++ii) {
+          const float gx = sG[(b0 + 4 * g + ii) * LK + i];
+          const float sc = __expf(gx - gb);
+          F1[t][ii] += sc * z1[ii];
+          F3[t][ii] += sc * z3[ii];
+          F24d[t][ii] = __expf(gb - gx) * zd[ii];
+        }
+      }
+    }
     const int bx = 16 * X + 15;
     for (int Rb = X + 1; Rb < 4; ++Rb) {
 #pragma unroll
@@ -960,7 +1010,8 @@ __global__ __launch_bounds__(256) void kda_final_kernel(BwdParams p) {
       for (int ii = 0; ii < 4; ++ii) {
         const int x = 16 * X + 4 * g + ii;
         if (x >= C) continue;
-        const float f24 = X < 3 ? __expf(sG[bx * LK + i] - sG[x * LK + i]) * F24[t][ii] : 0.f;
+        const float f24 =
+            (X < 3 ? __expf(sG[bx * LK + i] - sG[x * LK + i]) * F24[t][ii] : 0.f) + F24d[t][ii];
         const float f1 = F1[t][ii], f3 = F3[t][ii];
         const float qx = sQ[x * LK + i], kx = sK[x * LK + i];
         const size_t o = ((size_t)(r0 + x) * H + h) * DK + i;
