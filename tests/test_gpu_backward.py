@@ -214,6 +214,30 @@ def test_backward_kda_strong_decay():
     assert all(v <= TOL["bf16"] for v in errs.values()), errs
 
 
+def test_backward_kda_mixed_block_decay():
+    """KDA gates where only rows 16..31 of every chunk decay steeply in one
+    channel (g = -5 there: the block's last row is e^-75 from its first):
+    that 16-row block takes the pair-by-pair sums in the prep and the final
+    pass, the chunk's other blocks the factored MFMA products, in the same
+    cell.  Every gradient must match the oracle."""
+    inp = make_inputs(SMALL_CU[-1], 2, 64, 64, kda=True, dtype="bf16", seed=790,
+                      cu_seqlens=SMALL_CU, h0_std=0.1)
+    cu = np.asarray(SMALL_CU)
+    for n in range(len(cu) - 1):
+        for t in range(cu[n], cu[n + 1]):
+            if 16 <= (t - cu[n]) % 64 < 32:
+                inp["g"][t, :, 5] = -5.0
+    rng = np.random.default_rng(791)
+    do = rng.standard_normal(inp["v"].shape).astype(np.float32)
+    dht = rng.standard_normal(inp["h0"].shape).astype(np.float32)
+    ref = gated_delta_bwd(inp["q"], inp["k"], inp["v"], inp["g"], inp["beta"], SMALL_CU,
+                          inp["h0"], do, dht, 1.0, kda=True)
+    got = run_bwd(inp, do, dht, 1.0)
+    errs = compare(inp, got, ref)
+    _say("bwd kda mixed block decay: " + " ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    assert all(v <= TOL["bf16"] for v in errs.values()), errs
+
+
 def test_backward_concurrent_streams_match_sequential():
     """Two host threads issue backward calls on two streams at once, each
     forking its reverse pass onto its own second stream with its own events:
