@@ -870,6 +870,16 @@ def bench_forward(args, torch, la, synth, dev):
     # the event-timed mean the headline roofline uses
     p50, p95, ev_mean = event_times(torch, b.graph.replay, args.steps, 0)
     graph_eq = bool(torch.equal(b.o, eager_o) and torch.equal(b.ht, eager_ht))
+    # diagnostic: four steps in one graph, so the runtime's per-launch cost
+    # is paid once per four steps (the headline is one step per replay)
+    g4 = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g4):
+        for _ in range(4):
+            b.step()
+    torch.cuda.synchronize()
+    g4_ms = wall_ms(torch, g4.replay, args.steps, 5) / 4
+    graph_eq = graph_eq and bool(torch.equal(b.o, eager_o) and torch.equal(b.ht, eager_ht))
+    del g4
 
     tokens = int(cu_np[-1])
     value = tokens * args.steps / elapsed
@@ -920,6 +930,7 @@ def bench_forward(args, torch, la, synth, dev):
             "mfma_frac": round(op_flops / (ev_mean * 1e-3) / 1e12 / MFMA_F16_PEAK_TFLOPS, 4)},
         "kernels": diag,
         "eager_live_ms": round(eager_ms, 5), "capture_ms": round(capture_ms, 3),
+        "graph_x4_ms_per_step": round(g4_ms, 5),
         "replay_p50_ms": round(p50, 5), "replay_p95_ms": round(p95, 5),
         "kernels_per_step": (2 if seg == 0 else 4) + (not fused),
         "host_launches_per_step": {"eager": (2 if seg == 0 else 4) + (not fused), "graph": 1},
