@@ -113,3 +113,28 @@ def test_recurrent_grouped_value_heads_and_bf16_output(kda):
     e16 = rel_err_bf16_out(o16.float().cpu().numpy(), o_ref)
     _say(f"decode GVA + bf16 o kda={kda}: o {eo:.2e} ht {eh:.2e} bf16 o {e16:.2e}")
     assert eo <= TOL["bf16"] and eh <= TOL["bf16"] and e16 <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_recurrent_random_shapes(i):
+    """Seeded random decode batches: GDN or KDA, bf16 / fp16 / fp32, d = 64
+    or 128, 1 to 200 sequences, 1 to 16 heads, with or without h0, against
+    the oracle's token recurrence."""
+    rng = np.random.default_rng(60_000 + i)
+    kda = bool(rng.integers(2))
+    dtype = ["bf16", "f16", "f32"][rng.integers(3)]
+    d = int(rng.choice([64, 128]))
+    N, H = int(rng.integers(1, 201)), int(rng.integers(1, 17))
+    h0_std = 0.1 if rng.random() < 0.8 else None
+    scale = float(rng.choice([1.0, d ** -0.5]))
+    inp = _step_inputs(N, H, d, kda, dtype, seed=int(rng.integers(1 << 30)), h0_std=h0_std)
+    dv = _dev(inp)
+    fwd = la.kda_recurrent_fwd if kda else la.gdn_recurrent_fwd
+    o, ht = fwd(dv["q"], dv["k"], dv["v"], dv["g"], dv["beta"], h0=dv["h0"], scale=scale)
+    torch.cuda.synchronize()
+    o_ref, ht_ref = run_oracle(inp, scale=scale)
+    eo = rel_err(o.cpu().numpy(), o_ref)
+    eh = rel_err(ht.cpu().numpy(), ht_ref)
+    _say(f"decode random {i}: kda={kda} {dtype} d={d} N={N} H={H} h0={h0_std is not None}: "
+         f"o {eo:.2e} ht {eh:.2e}")
+    assert eo <= TOL[dtype] and eh <= TOL[dtype]
