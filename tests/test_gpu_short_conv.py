@@ -171,3 +171,31 @@ def test_conv_full_size_sampled_channels():
     assert ey <= GATE
     assert np.array_equal(ht.float().cpu().numpy()[:, :, cols], ht_ref)
     assert bool(torch.isfinite(y.float()).all())
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_conv_random_layouts(i):
+    """Seeded random varlen layouts (empty, one-token and longer sequences),
+    channel counts (multiples of 8 for 16-bit x, of 4 for fp32), widths,
+    BT, bias / residual / state and activation, against the oracle."""
+    rng = np.random.default_rng(70_000 + i)
+    dtype = ["bf16", "f16", "f32"][rng.integers(3)]
+    W = int(rng.integers(1, 5))
+    D = int(rng.integers(1, 200)) * (8 if dtype != "f32" else 4)
+    N = int(rng.integers(1, 40))
+    lens = rng.integers(0, 150, N)
+    lens[rng.random(N) < 0.2] = 0
+    lens[rng.random(N) < 0.15] = 1
+    if lens.sum() == 0:
+        lens[0] = 3
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    act = None if rng.random() < 0.5 else "silu"
+    BT = int(rng.choice([32, 64]))
+    inp = make_conv_inputs(int(cu[-1]), D, W, dtype=dtype, seed=int(rng.integers(1 << 30)),
+                           cu_seqlens=cu, bias=bool(rng.random() < 0.7),
+                           residual=bool(rng.random() < 0.5), h0=bool(rng.random() < 0.6))
+    y, ht = run_conv(inp, BT=BT, activation=act)
+    ey, ok_h = check(inp, y, ht, act)
+    _say(f"conv random {i}: {dtype} W={W} D={D} N={N} T={int(cu[-1])} BT={BT} act={act}: "
+         f"y {ey:.2e} ht exact {ok_h}")
+    assert ey <= GATE and ok_h
